@@ -1,0 +1,183 @@
+"""Cross-entropy oracle: the slow, plain, fp64 CPU definition of what liblce computes.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  It shares no code with
+the HIP library (``vocab_cross_entropy_row_amd``) and imports nothing from it;
+the only code both sides use is the seeded input generator in ``lce_synth``.
+
+Sources (KernelIndex pages; the formula itself is never printed there):
+
+* "Cross-entropy loss" -- description and Semantics block: logits
+  ``float [tokens, vocab]``, target ``int64 [tokens]``, loss ``float [1]``.  Read as
+  the textbook softmax cross-entropy per token, ``ln sum_j exp(z_ij) - z_{i,t_i}``,
+  reduced to the mean over tokens.
+* "Vocab-parallel cross-entropy, Megatron layout" -- description and Semantics
+  block: logits ``[seq, batch, vocab]``, target ``[seq, batch]``, per-token fp32
+  losses ``[seq, batch]`` (no reduction).  At TP=1 this is the same per-row
+  formula on the contiguous ``[seq*batch, vocab]`` view.
+* "Fused linear + CPO loss" -- description and Semantics block: activations
+  ``[batch, seq, hidden]`` projected through a ``[vocab, hidden]`` head,
+  ``z = x W^T``, with the logits never materialised.  The oracle does
+  materialise them (in fp64): it computes ``z`` with a plain fp64 matrix
+  product (a library primitive) and then applies the same per-row formula.
+
+Every function here is pinned by tests that do not reuse its arithmetic:
+closed forms, invariants, brute force in 40-digit decimal arithmetic, and a
+library routine (see ``tests/test_oracle_pins.py``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "xent_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+_DTYPES = {"f32": 0, "bf16": 1, "f64": 2}
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ``liboracle.so`` with gcc (plain -O2, no fast-math, OpenMP over rows)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+               "-fno-fast-math", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.oracle_xent_rows.restype = ctypes.c_int
+        lib.oracle_xent_rows.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                         ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_int]
+        lib.oracle_mean.restype = ctypes.c_double
+        lib.oracle_mean.argtypes = [ctypes.c_void_p, ctypes.c_int64]
+        lib.oracle_default_threads.restype = ctypes.c_int
+        lib.oracle_default_threads.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    """Host threads the oracle uses when none are given."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _dtype_of(logits: np.ndarray, dtype: str | None) -> str:
+    if dtype is not None:
+        return dtype
+    if logits.dtype == np.float32:
+        return "f32"
+    if logits.dtype == np.float64:
+        return "f64"
+    if logits.dtype == np.uint16:
+        return "bf16"
+    raise TypeError(f"oracle: unsupported logits dtype {logits.dtype}")
+
+
+def xent_rows(logits: np.ndarray, target: np.ndarray, dtype: str | None = None,
+              nthreads: int | None = None) -> np.ndarray:
+    """Per-token losses ``ln sum_j exp(z_ij) - z_{i,t_i}`` in fp64.
+
+    ``logits`` is ``[..., vocab]`` (any leading shape, row-major): float32, float64,
+    or uint16 holding bf16 bit patterns.  ``target`` has the leading shape.  The
+    result has the leading shape.  Out-of-range targets give NaN.
+    """
+    dt = _dtype_of(logits, dtype)
+    z = np.ascontiguousarray(logits)
+    t = np.ascontiguousarray(target, dtype=np.int64)
+    vocab = int(z.shape[-1])
+    lead = z.shape[:-1]
+    if t.shape != lead:
+        raise ValueError(f"oracle: target shape {t.shape} != logits leading shape {lead}")
+    rows = int(np.prod(lead, dtype=np.int64)) if lead else 1
+    out = np.empty(rows, dtype=np.float64)
+    rc = _load().oracle_xent_rows(z.ctypes.data, _DTYPES[dt], rows, vocab, t.ctypes.data,
+                                  out.ctypes.data, int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle: bad argument")
+    return out.reshape(lead)
+
+
+def mean(losses: np.ndarray) -> float:
+    """Mean of per-token losses, summed in index order in fp64 (NaN for no tokens)."""
+    l64 = np.ascontiguousarray(losses, dtype=np.float64).reshape(-1)
+    return float(_load().oracle_mean(l64.ctypes.data, l64.size))
+
+
+def xent(logits: np.ndarray, target: np.ndarray, reduction: str = "mean",
+         dtype: str | None = None, nthreads: int | None = None):
+    """Cross-entropy with ``reduction`` in {"mean", "none"}."""
+    per_token = xent_rows(logits, target, dtype=dtype, nthreads=nthreads)
+    if reduction == "none":
+        return per_token
+    if reduction == "mean":
+        return mean(per_token)
+    raise ValueError(f"oracle: unknown reduction {reduction!r}")
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns (uint16) to float64."""
+    u32 = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u32.view(np.float32).astype(np.float64)
+
+
+def fused_logits_f64(x_bits: np.ndarray, w_bits: np.ndarray,
+                     rows: np.ndarray | None = None) -> np.ndarray:
+    """``z = x W^T`` in fp64 for the selected token rows (all rows if ``rows`` is None).
+
+    ``x_bits`` is ``[tokens, hidden]`` and ``w_bits`` ``[vocab, hidden]``, both bf16 bit
+    patterns.  Products of bf16 values are exact in fp64; the sums are fp64.
+    """
+    x64 = bf16_bits_to_f64(x_bits if rows is None else x_bits[rows])
+    w64 = bf16_bits_to_f64(w_bits)
+    return np.matmul(x64, w64.T)
+
+
+def fused_linear_xent_rows(x_bits: np.ndarray, w_bits: np.ndarray, target: np.ndarray,
+                           rows: np.ndarray | None = None, block: int = 128,
+                           nthreads: int | None = None) -> np.ndarray:
+    """Per-token losses of ``x W^T`` against ``target`` (selected rows), in fp64.
+
+    Token rows are processed ``block`` at a time (rows are independent), so only a
+    ``[block, vocab]`` slab of fp64 logits exists at once.
+    """
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    w_bits = np.ascontiguousarray(w_bits, dtype=np.uint16)
+    target = np.ascontiguousarray(target, dtype=np.int64).reshape(-1)
+    if x_bits.ndim != 2 or w_bits.ndim != 2 or x_bits.shape[1] != w_bits.shape[1]:
+        raise ValueError("oracle: x must be [tokens, hidden] and W [vocab, hidden]")
+    sel = np.arange(x_bits.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    w64t = bf16_bits_to_f64(w_bits).T
+    out = np.empty(sel.size, dtype=np.float64)
+    for b0 in range(0, sel.size, block):
+        r = sel[b0:b0 + block]
+        z = np.matmul(bf16_bits_to_f64(x_bits[r]), w64t)
+        out[b0:b0 + block] = xent_rows(z, target[r], dtype="f64", nthreads=nthreads)
+    return out
+
+
+def fused_linear_xent(x_bits: np.ndarray, w_bits: np.ndarray, target: np.ndarray,
+                      reduction: str = "mean", nthreads: int | None = None):
+    """Fused linear + cross-entropy, ``reduction`` in {"mean", "none"}."""
+    per_token = fused_linear_xent_rows(x_bits, w_bits, target, nthreads=nthreads)
+    if reduction == "none":
+        return per_token
+    if reduction == "mean":
+        return mean(per_token)
+    raise ValueError(f"oracle: unknown reduction {reduction!r}")

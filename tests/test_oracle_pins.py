@@ -1,0 +1,265 @@
+"""Pins for the fp64 oracle, none of which reuses the oracle's own arithmetic.
+
+The pages print no loss value for any input, so the oracle is pinned by what the
+mathematics fixes: closed forms, invariants, 40-digit brute force on tiny shapes,
+and an independent library routine.  Each test names the slip it would catch.
+"""
+import math
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import lce_synth
+
+LN = math.log
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f64"])
+@pytest.mark.parametrize("vocab", [1, 2, 3, 7, 4096, 131072])
+@pytest.mark.parametrize("c", [0.0, 37.5, -1000.0])
+def test_uniform_logits_give_ln_vocab(oracle_mod, dtype, vocab, c):
+    """All logits equal to c: loss = ln(vocab) for every target (catches a dropped
+    or sign-flipped -z_t term, a missing max shift at c=-1000, log base slips)."""
+    rows = 3 if vocab > 4096 else 9
+    if dtype == "f32":
+        z = np.full((rows, vocab), c, dtype=np.float32)
+    elif dtype == "f64":
+        z = np.full((rows, vocab), c, dtype=np.float64)
+    else:  # 0.0, 37.5 and -1000.0 are all exact bf16 values
+        z = (np.full((rows, vocab), c, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    t = _rng(vocab).integers(0, vocab, rows)
+    loss = oracle_mod.xent_rows(z, t, dtype=dtype)
+    assert np.allclose(loss, LN(vocab), rtol=0, atol=1e-12)
+    assert oracle_mod.xent(z, t, "mean", dtype=dtype) == pytest.approx(LN(vocab), abs=1e-12)
+
+
+@pytest.mark.parametrize("vocab", [2, 5, 4096])
+@pytest.mark.parametrize("a", [0.0, 1.0, 5.0, 20.0, 50.0, 1000.0])
+def test_dominant_target(oracle_mod, vocab, a):
+    """z_t = a, all other logits 0: loss = ln(1 + (V-1) e^-a), -> 0 as a grows
+    (catches an off-by-one target index and a wrong-sign exponent)."""
+    rows = 4
+    z = np.zeros((rows, vocab))
+    t = np.array([0, vocab - 1, vocab // 2, 1 % vocab])
+    z[np.arange(rows), t] = a
+    want = math.log1p((vocab - 1) * math.exp(-a))
+    got = oracle_mod.xent_rows(z, t)
+    # m + ln(s) - z_t cancels, leaving a few ulp of |a|; the sequential fp64 sum of
+    # V terms adds at most about V * 2^-53 to ln(s)
+    atol = 8 * max(1.0, a) * 2.0 ** -52 + vocab * 2.0 ** -53
+    assert np.allclose(got, want, rtol=1e-12, atol=atol)
+    if a == 1000.0:
+        assert np.all(got == 0.0)
+
+
+@pytest.mark.parametrize("d", [-40.0, -3.5, -1e-3, 0.0, 0.25, 7.0, 40.0])
+def test_two_classes_is_softplus(oracle_mod, d):
+    """V = 2: loss = softplus(z_other - z_t) = ln(1 + e^d)."""
+    z = np.array([[1.5, 1.5 + d], [1.5 + d, 1.5]])
+    t = np.array([0, 1])
+    want = max(d, 0.0) + math.log1p(math.exp(-abs(d)))
+    assert np.allclose(oracle_mod.xent_rows(z, t), want, rtol=1e-13, atol=1e-15)
+
+
+def test_single_class_is_zero(oracle_mod):
+    z = np.array([[3.0], [-7.25], [0.0]])
+    assert np.all(oracle_mod.xent_rows(z, np.zeros(3, dtype=np.int64)) == 0.0)
+
+
+# ---------------------------------------------------------------- invariants
+
+def test_row_shift_invariance(oracle_mod):
+    """Adding a constant to a row leaves its loss unchanged.  Logits on a 2^-8
+    grid with |z| < 8 and integer shifts |c| <= 2^15 stay exact in fp32."""
+    rng = _rng(7)
+    rows, vocab = 16, 513
+    z = np.round(rng.uniform(-8, 8, (rows, vocab)) * 256) / 256
+    c = rng.integers(-2 ** 15, 2 ** 15, rows).astype(np.float64)
+    t = rng.integers(0, vocab, rows)
+    base = oracle_mod.xent_rows(z.astype(np.float32), t)
+    shifted = oracle_mod.xent_rows((z + c[:, None]).astype(np.float32), t)
+    assert np.allclose(base, shifted, rtol=0, atol=1e-10)
+
+
+def test_permutation_invariance(oracle_mod):
+    """Permuting columns together with the target leaves the loss unchanged; permuting
+    rows permutes the losses (catches row/column stride mix-ups)."""
+    rng = _rng(11)
+    rows, vocab = 12, 301
+    z = rng.normal(size=(rows, vocab))
+    t = rng.integers(0, vocab, rows)
+    perm = rng.permutation(vocab)
+    inv = np.argsort(perm)
+    zp = z[:, perm]                      # new column j holds old column perm[j]
+    tp = inv[t]
+    assert np.allclose(oracle_mod.xent_rows(z, t), oracle_mod.xent_rows(zp, tp), rtol=1e-13)
+    rp = rng.permutation(rows)
+    assert np.allclose(oracle_mod.xent_rows(z, t)[rp], oracle_mod.xent_rows(z[rp], t[rp]),
+                       rtol=0, atol=0)
+
+
+def test_megatron_layout_is_row_view(oracle_mod):
+    """[seq, batch, vocab] with row = s*batch + b gives the [seq*batch, vocab] losses."""
+    rng = _rng(3)
+    z = rng.normal(size=(5, 3, 64)).astype(np.float32)
+    t = rng.integers(0, 64, (5, 3))
+    a = oracle_mod.xent_rows(z, t)
+    b = oracle_mod.xent_rows(z.reshape(15, 64), t.reshape(15))
+    assert a.shape == (5, 3)
+    assert np.array_equal(a.reshape(15), b)
+
+
+# ---------------------------------------------------------------- brute force
+
+def _brute(z_row, t):
+    """-ln(e^{z_t} / sum_j e^{z_j}) at 40 digits, no max shift."""
+    getcontext().prec = 40
+    zs = [Decimal(float(v)) for v in z_row]
+    den = sum(v.exp() for v in zs)
+    return float(-((zs[t].exp() / den).ln()))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_brute_force_tiny(oracle_mod, seed):
+    rng = _rng(100 + seed)
+    rows = int(rng.integers(1, 9))
+    vocab = int(rng.integers(1, 17))
+    z = rng.uniform(-20, 20, (rows, vocab))
+    t = rng.integers(0, vocab, rows)
+    want = np.array([_brute(z[i], int(t[i])) for i in range(rows)])
+    assert np.allclose(oracle_mod.xent_rows(z, t), want, rtol=0, atol=1e-13)
+
+
+def test_matches_library_cross_entropy(oracle_mod):
+    """Independent library routine: torch CPU fp64 cross_entropy."""
+    torch = pytest.importorskip("torch")
+    rng = _rng(5)
+    for rows, vocab in [(64, 1000), (7, 4096), (33, 3)]:
+        z = rng.normal(scale=3.0, size=(rows, vocab))
+        t = rng.integers(0, vocab, rows)
+        ref = torch.nn.functional.cross_entropy(torch.from_numpy(z), torch.from_numpy(t),
+                                                reduction="none").numpy()
+        assert np.allclose(oracle_mod.xent_rows(z, t), ref, rtol=1e-12, atol=1e-12)
+        refm = torch.nn.functional.cross_entropy(torch.from_numpy(z), torch.from_numpy(t)).item()
+        assert oracle_mod.xent(z, t, "mean") == pytest.approx(refm, rel=1e-12)
+
+
+# ---------------------------------------------------------------- mean and contract edges
+
+def test_mean_is_average_of_tokens(oracle_mod):
+    rng = _rng(9)
+    z = rng.normal(size=(257, 99))
+    t = rng.integers(0, 99, 257)
+    per = oracle_mod.xent_rows(z, t)
+    assert oracle_mod.mean(per) == pytest.approx(math.fsum(per) / per.size, rel=1e-13)
+
+
+def test_empty_and_invalid(oracle_mod):
+    z = np.zeros((0, 16), dtype=np.float32)
+    assert oracle_mod.xent_rows(z, np.zeros(0, dtype=np.int64)).shape == (0,)
+    assert math.isnan(oracle_mod.xent(z, np.zeros(0, dtype=np.int64), "mean"))
+    z = np.zeros((4, 16), dtype=np.float32)
+    got = oracle_mod.xent_rows(z, np.array([0, -1, 16, 15]))
+    assert not math.isnan(got[0]) and not math.isnan(got[3])
+    assert math.isnan(got[1]) and math.isnan(got[2])
+    zn = np.zeros((2, 8))
+    zn[1, 3] = np.nan
+    got = oracle_mod.xent_rows(zn, np.array([0, 0]))
+    assert got[0] == pytest.approx(LN(8)) and math.isnan(got[1])
+
+
+# ---------------------------------------------------------------- bf16 decode and RNE
+
+def test_bf16_decode_patterns(oracle_mod):
+    """0x3F80 = 1.0, 0xC000 = -2.0, 0x4216 = 37.5 -- through the C decoder (V = 2
+    softplus) and the Python widening used by the fused path."""
+    bits = np.array([[0x3F80, 0xC000], [0xC000, 0x4216]], dtype=np.uint16)
+    got = oracle_mod.xent_rows(bits, np.array([0, 1]))
+    assert got[0] == pytest.approx(math.log1p(math.exp(-3.0)), rel=1e-14)
+    assert got[1] == pytest.approx(math.log1p(math.exp(-39.5)), rel=1e-14)
+    w = oracle_mod.bf16_bits_to_f64(np.array([0x3F80, 0xC000, 0x4216, 0x0001, 0x7F7F], np.uint16))
+    assert list(w[:3]) == [1.0, -2.0, 37.5]
+    assert w[3] == 2.0 ** -133
+    assert w[4] == (2 - 2 ** -7) * 2.0 ** 127
+
+
+def test_generator_rounds_to_nearest_even():
+    vals = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -20, -2.0,
+                     1 - 2 ** -9], dtype=np.float32)
+    got = lce_synth.f32_to_bf16_bits(vals)
+    assert list(got) == [0x3F80, 0x3F80, 0x3F82, 0x3F81, 0xC000, 0x3F80]
+
+
+# ---------------------------------------------------------------- fused path
+
+def test_fused_zero_activations_give_ln_vocab(oracle_mod):
+    rng = _rng(21)
+    V, H = 37, 24
+    x = np.zeros((5, H), dtype=np.uint16)
+    w = lce_synth.f32_to_bf16_bits(rng.normal(size=(V, H)).astype(np.float32))
+    got = oracle_mod.fused_linear_xent_rows(x, w, rng.integers(0, V, 5))
+    assert np.allclose(got, LN(V), rtol=0, atol=1e-13)
+
+
+def test_fused_identity_head_is_plain_ce(oracle_mod):
+    """W = I (vocab = hidden): fused CE of x equals plain CE of x."""
+    rng = _rng(22)
+    H = 40
+    x = lce_synth.f32_to_bf16_bits(rng.normal(size=(6, H)).astype(np.float32))
+    eye = lce_synth.f32_to_bf16_bits(np.eye(H, dtype=np.float32))
+    t = rng.integers(0, H, 6)
+    assert np.allclose(oracle_mod.fused_linear_xent_rows(x, eye, t),
+                       oracle_mod.xent_rows(x, t, dtype="bf16"), rtol=0, atol=1e-14)
+
+
+def test_fused_brute_force_tiny(oracle_mod):
+    """Non-square tiny GEMM by exact rational triple loop, then 40-digit CE
+    (catches a transposed operand or a swapped hidden/vocab axis)."""
+    rng = _rng(23)
+    T, H, V = 3, 5, 7
+    x = lce_synth.f32_to_bf16_bits(rng.normal(size=(T, H)).astype(np.float32))
+    w = lce_synth.f32_to_bf16_bits(rng.normal(size=(V, H)).astype(np.float32))
+    t = rng.integers(0, V, T)
+    xf = [[Fraction(float(v)) for v in r] for r in oracle_mod.bf16_bits_to_f64(x)]
+    wf = [[Fraction(float(v)) for v in r] for r in oracle_mod.bf16_bits_to_f64(w)]
+    want = []
+    for i in range(T):
+        z = [float(sum(xf[i][k] * wf[j][k] for k in range(H))) for j in range(V)]
+        want.append(_brute(z, int(t[i])))
+    got = oracle_mod.fused_linear_xent_rows(x, w, t)
+    assert np.allclose(got, want, rtol=0, atol=1e-12)
+    assert oracle_mod.fused_linear_xent(x, w, t, "mean") == pytest.approx(np.mean(want), abs=1e-12)
+
+
+# ---------------------------------------------------------------- statistical sanity of inputs + oracle
+
+@pytest.mark.parametrize("name,rows,expect", [
+    ("ce_f32_16384x4096_mean", 1024, LN(4096) + 0.5),
+    ("megatron_bf16_2048x4x4096_none", 1024, LN(4096) + 0.5),
+    ("megatron_bf16_2048x4x131072_none", 64, LN(131072) + 2.0),
+])
+def test_mean_loss_near_ln_vocab_plus_half_variance(oracle_mod, name, rows, expect):
+    """For i.i.d. N(0, s^2) logits the mean loss is about ln V + s^2/2 (catches a
+    generator slip such as variance for std, or a wrong target stream)."""
+    w = lce_synth.WORKLOADS[name]
+    got = oracle_mod.xent(w.logits(0, rows), w.target(0, rows), "mean", dtype=w.dtype)
+    assert got == pytest.approx(expect, abs=0.05)
+
+
+def test_fused_workload_statistics(oracle_mod):
+    """The fused workload's logits z = x W^T have variance ~ hidden * 0.02^2; on a
+    vocab slice of 8192 heads the mean loss is about ln 8192 + 4096 * 0.0004 / 2."""
+    w = lce_synth.WORKLOADS["fused_bf16_t2048_h4096_v128256_mean"]
+    x = w.x(0, 16)
+    head = w.weight(0, 8192)
+    t = lce_synth.targets(77, 16, 8192)
+    got = oracle_mod.fused_linear_xent(x, head, t, "mean")
+    assert got == pytest.approx(LN(8192) + 4096 * 0.02 ** 2 / 2, abs=0.1)
