@@ -1,0 +1,332 @@
+"""liblce benchmark: µs per forward cross-entropy on one MI355X, with roofline and CPU oracle.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads all|headline|NAME,...]
+
+A step is one forward call of the hot path on one batch of synthetic input already
+resident in HBM.  The headline workload is bf16 logits [seq 2048, batch 4, vocab 4096]
+with per-token fp32 losses (the Megatron-layout cross-entropy of the pages).  Inputs are
+replicated so that the replicas together exceed the 256 MB Infinity Cache, and step i
+reads replica i mod R: every step streams its logits from HBM.
+
+Timing: W eager warmup steps, then the K timed steps are captured into one HIP graph
+(liblce launches on torch's current stream; nothing in the call allocates or memsets once
+warm) and replayed once between two events on that stream, bracketed by
+torch.cuda.synchronize().  The graph removes host launch overhead, which is longer than
+the kernel itself at this size; the eager per-call time is reported next to it.
+
+Prints ONE JSON line (rank 0, N = 1).  Other workloads are measured the same way and
+reported under "workloads".  The roofline is for the dominant kernel: algorithmic bytes
+(every declared tensor crossing HBM once) per launch over the average launch duration.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "µs per forward CE (and achieved HBM GB/s / % roofline) at tokens×vocab"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, datasheet
+BF16_DENSE_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, datasheet
+INFINITY_CACHE_BYTES = 256 << 20
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+# ------------------------------------------------------------------ work model
+
+def tensor_bytes(tensors) -> int:
+    """Bytes of a list of (numel, itemsize) tensors, each crossing HBM once."""
+    return int(sum(int(n) * int(s) for n, s in tensors))
+
+
+def xent_bytes(tokens: int, vocab: int, esize: int, reduction: str) -> int:
+    """Algorithmic bytes of one row cross-entropy: logits + int64 targets + fp32 output."""
+    out = 1 if reduction == "mean" else tokens
+    return tensor_bytes([(tokens * vocab, esize), (tokens, 8), (out, 4)])
+
+
+def fused_bytes(tokens: int, hidden: int, vocab: int, reduction: str) -> int:
+    """Algorithmic bytes of one fused projection + cross-entropy: x + W + targets + output."""
+    out = 1 if reduction == "mean" else tokens
+    return tensor_bytes([(tokens * hidden, 2), (vocab * hidden, 2), (tokens, 8), (out, 4)])
+
+
+def fused_flops(tokens: int, hidden: int, vocab: int) -> int:
+    """Multiply-adds of z = x W^T, counted as 2 flops each."""
+    return 2 * int(tokens) * int(hidden) * int(vocab)
+
+
+def source_digest() -> str:
+    """sha256 over the kernel sources and build script (ties counter data to a build)."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "vocab_cross_entropy_row_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "vocab_cross_entropy_row_amd", "build.py"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_for(workload: str):
+    """HBM traffic per launch from the committed counter summary, or None if absent or
+    if the kernel sources changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        d = json.load(fh)
+    if d.get("source_sha256") != source_digest():
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+# ------------------------------------------------------------------ device inputs
+
+def _to_dev(arr, torch):
+    import numpy as np
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(arr.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(arr).cuda()
+
+
+def make_inputs(w, torch, replicas: int):
+    """Device replicas of a workload's inputs (generated once on the host, in row blocks)."""
+    if w.kind == "xent":
+        tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+        z = torch.empty(w.shape, dtype=tdt, device="cuda")
+        flat = z.view(w.tokens, w.vocab)
+        blk = max(1, (512 << 20) // (w.vocab * (4 if w.dtype == "f32" else 2)))
+        for r0 in range(0, w.tokens, blk):
+            r1 = min(w.tokens, r0 + blk)
+            flat[r0:r1].copy_(_to_dev(w.logits(r0, r1), torch))
+        t = torch.from_numpy(w.target()).cuda().view(w.target_shape)
+        reps = [(z, t)] + [(z.clone(), t.clone()) for _ in range(replicas - 1)]
+        return reps
+    x = _to_dev(w.x(), torch)
+    W = torch.empty((w.vocab, w.hidden), dtype=torch.bfloat16, device="cuda")
+    blk = 16384
+    for r0 in range(0, w.vocab, blk):
+        r1 = min(w.vocab, r0 + blk)
+        W[r0:r1].copy_(_to_dev(w.weight(r0, r1), torch))
+    t = torch.from_numpy(w.target()).cuda()
+    return [(x, W, t)] + [(x.clone(), W.clone(), t.clone()) for _ in range(replicas - 1)]
+
+
+def replicas_for(w) -> int:
+    """Enough replicas that their logits/weights exceed 4x the Infinity Cache (<= 16)."""
+    per = (w.tokens * w.vocab * (4 if w.dtype == "f32" else 2)) if w.kind == "xent" \
+        else (w.vocab * w.hidden * 2)
+    r = 1
+    while r < 16 and r * per < 4 * INFINITY_CACHE_BYTES:
+        r += 1
+    return r
+
+
+# ------------------------------------------------------------------ timing
+
+def time_workload(w, steps: int, warmup: int, torch, lce):
+    reps = make_inputs(w, torch, replicas_for(w))
+    R = len(reps)
+    outs = [torch.empty((1,) if w.reduction == "mean" else w.target_shape, dtype=torch.float32,
+                        device="cuda") for _ in range(R)]
+
+    def step(i):
+        r = i % R
+        if w.kind == "xent":
+            z, t = reps[r]
+            lce.xent(z, t, w.reduction, out=outs[r])
+        else:
+            x, W, t = reps[r]
+            lce.fused_linear_xent(x, W, t, w.reduction, out=outs[r])
+
+    for i in range(max(1, warmup)):
+        step(i)
+    torch.cuda.synchronize()
+    eager_ref = [o.clone() for o in outs]
+
+    # eager per-call time (host launch overhead included)
+    n_eager = min(steps, 50)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(n_eager):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    eager_us = e0.elapsed_time(e1) * 1000.0 / n_eager
+
+    # capture exactly `steps` steps into one graph; replay once untimed, once timed
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(0)  # scratch for this stream is allocated outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(steps):
+            step(i)
+    g.replay()
+    torch.cuda.synchronize()
+    ok = all(torch.equal(a, b) for a, b in zip(outs, eager_ref))
+
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    with torch.cuda.stream(s):
+        t0.record(s)
+        g.replay()
+        t1.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    us = t0.elapsed_time(t1) * 1000.0 / steps
+    ok = ok and all(torch.equal(a, b) for a, b in zip(outs, eager_ref))
+    del g, reps, outs
+    torch.cuda.empty_cache()
+    return {"us_per_step": us, "eager_us_per_call": eager_us, "replicas": R,
+            "graph_matches_eager": bool(ok), "wall_s": wall}
+
+
+def roofline_entry(w, us: float) -> dict:
+    if w.kind == "xent":
+        esize = 4 if w.dtype == "f32" else 2
+        b = xent_bytes(w.tokens, w.vocab, esize, w.reduction)
+        gbs = b / (us * 1e-6) / 1e9
+        return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_for(w.name),
+                "algorithmic_bytes": b}
+    fl = fused_flops(w.tokens, w.hidden, w.vocab)
+    tf = fl / (us * 1e-6) / 1e12
+    return {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_DENSE_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tf / BF16_DENSE_TFLOPS, 4),
+            "traffic": traffic_for(w.name), "algorithmic_flops": fl,
+            "algorithmic_bytes": fused_bytes(w.tokens, w.hidden, w.vocab, w.reduction)}
+
+
+# ------------------------------------------------------------------ CPU baseline (oracle)
+
+def cpu_baseline(w, budget_s: float = 10.0) -> dict:
+    """Time the fp64 oracle on the host cores over a bounded sample of the workload and
+    scale to µs per full forward call."""
+    import oracle
+    threads = oracle.default_threads()
+    if w.kind == "xent":
+        rows = w.tokens
+        per_row_elems = w.vocab
+        # sample: leading rows, at most ~2^28 elements
+        sample_rows = min(rows, max(1, (1 << 28) // per_row_elems))
+        z = w.logits(0, sample_rows)
+        t = w.target(0, sample_rows)
+        times = []
+        t_end = time.perf_counter() + budget_s
+        while len(times) < 5 and (not times or time.perf_counter() < t_end):
+            t0 = time.perf_counter()
+            oracle.xent_rows(z, t, dtype=w.dtype, nthreads=threads)
+            times.append(time.perf_counter() - t0)
+        per_call = statistics.median(times) * rows / sample_rows
+        sample = (f"rows [0, {sample_rows}) of {rows} ({sample_rows * per_row_elems} logits), "
+                  f"median of {len(times)} runs, scaled to all rows")
+    else:
+        rows = w.tokens
+        sample_rows = min(rows, 16)
+        xb, wb, tg = w.x(0, sample_rows), w.weight(), w.target(0, sample_rows)
+        t0 = time.perf_counter()
+        oracle.fused_linear_xent_rows(xb, wb, tg, nthreads=threads)
+        per_call = (time.perf_counter() - t0) * rows / sample_rows
+        sample = f"{sample_rows} of {rows} token rows (full head), one run, scaled to all rows"
+    return {"value": round(per_call * 1e6, 1), "unit": "µs", "cores": threads, "kind": "oracle",
+            "sample": sample}
+
+
+# ------------------------------------------------------------------ main
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workloads", default="all",
+                    help="'all', 'headline', or a comma list of workload names")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(rows shard across GPUs with one 8-byte all-reduce for the mean; not built). "
+              "Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import lce_synth
+    import vocab_cross_entropy_row_amd as lce
+
+    lce.load()
+    torch.cuda.set_device(0)
+    head = lce_synth.WORKLOADS[lce_synth.HEADLINE]
+    names = list(lce_synth.WORKLOADS) if args.workloads == "all" else (
+        [lce_synth.HEADLINE] if args.workloads == "headline" else args.workloads.split(","))
+    if lce_synth.HEADLINE not in names:
+        names.insert(0, lce_synth.HEADLINE)
+
+    results = {}
+    for name in names:
+        w = lce_synth.WORKLOADS[name]
+        big = w.kind == "fused" or w.tokens * w.vocab >= (1 << 30)
+        k = args.steps if not big else max(5, min(args.steps, 30))
+        print(f"[bench] {name}: {k} steps", file=sys.stderr, flush=True)
+        r = time_workload(w, k, args.warmup, torch, lce)
+        r["steps"] = k
+        r["roofline"] = roofline_entry(w, r["us_per_step"])
+        if not args.no_cpu and name != lce_synth.HEADLINE:
+            r["cpu_oracle"] = cpu_baseline(w, budget_s=5.0)
+        results[name] = r
+        print(f"[bench] {name}: {r['us_per_step']:.2f} µs/step "
+              f"({r['roofline']['achieved']} {r['roofline']['unit']})", file=sys.stderr, flush=True)
+
+    h = results[lce_synth.HEADLINE]
+    line = {
+        "metric": METRIC,
+        "value": round(h["us_per_step"], 3),
+        "unit": "µs",
+        "n_gpus": 1,
+        "steps": h["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": round(h["us_per_step"] / 1000.0, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head.dtype,
+        "data": "synthetic",
+        "config": {"workload": head.name, "seq": head.shape[0], "batch": head.shape[1],
+                   "vocab": head.shape[2], "tokens": head.tokens, "logits_dtype": head.dtype,
+                   "reduction": head.reduction, "timing": "hip graph of K steps, replayed once",
+                   "eager_us_per_call": round(h["eager_us_per_call"], 3),
+                   "replicas": h["replicas"], "graph_matches_eager": h["graph_matches_eager"]},
+        "roofline": {k: v for k, v in h["roofline"].items() if k in
+                     ("bound", "achieved", "peak", "unit", "frac", "traffic")},
+    }
+    line["roofline"]["kernel"] = "xent_wave_rows_kernel<bf16, 8>"
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(head)
+    line["workloads"] = {n: {"us_per_step": round(r["us_per_step"], 3),
+                             "eager_us_per_call": round(r["eager_us_per_call"], 3),
+                             "steps": r["steps"], "replicas": r["replicas"],
+                             "graph_matches_eager": r["graph_matches_eager"],
+                             "roofline": r["roofline"],
+                             **({"cpu_oracle": r["cpu_oracle"]} if "cpu_oracle" in r else {})}
+                         for n, r in results.items()}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

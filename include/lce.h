@@ -1,0 +1,150 @@
+/*
+ * liblce -- cross-entropy over a tokens x vocab logit matrix, for AMD Instinct
+ * MI355X (gfx950).  C ABI: plain pointers, sizes and a HIP stream; no C++ or
+ * framework types cross this boundary.
+ *
+ * Operations (KernelIndex pages; the loss formula itself is not printed there
+ * and is read as textbook softmax cross-entropy in natural log):
+ *
+ *   per token i:   loss_i = ln( sum_j exp(z_ij) ) - z_{i, t_i}
+ *   mean:          (1 / tokens) * sum_i loss_i
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers on the current HIP device,
+ *     row-major and contiguous.  The caller owns every buffer; liblce never
+ *     frees or retains a caller pointer after the call returns.
+ *   - Inputs are never written.  `out` must not overlap any input
+ *     ("No mutation or aliasing" in each page's Semantics block).
+ *   - Calls are asynchronous: work is enqueued on `stream` (0 = the null
+ *     stream) and the call returns without synchronising.  Argument errors are
+ *     reported synchronously, before anything is enqueued; a failed launch is
+ *     reported as LCE_ERR_HIP.  Faults during execution surface at the
+ *     caller's next synchronisation, as for any HIP kernel.
+ *   - Targets are int64 class indices.  A target outside [0, vocab) is a
+ *     contract violation: that token's loss is NaN (so is the mean), and no
+ *     out-of-bounds read happens.  There is no ignore_index: no page
+ *     mentions one.
+ *   - Losses are always fp32; accumulation is fp32.
+ *   - Results are bitwise reproducible run to run for the same inputs, shape
+ *     and device: every reduction has a fixed order and no float atomics are
+ *     used (the pages leave determinism unspecified).
+ *   - liblce keeps a small device scratch buffer per (device, stream), grown
+ *     on demand with hipMalloc and kept until the process ends.  Calls that
+ *     run concurrently on the same stream are ordered by the stream; calls on
+ *     different streams use different scratch buffers.
+ *   - No call throws; every error is a status code plus a thread-local
+ *     message (lce_last_error).
+ */
+#ifndef LCE_H
+#define LCE_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LCE_VERSION_MAJOR 0
+#define LCE_VERSION_MINOR 1
+#define LCE_VERSION_PATCH 0
+
+typedef enum {
+    LCE_F32 = 0,  /* IEEE binary32 logits */
+    LCE_BF16 = 1  /* bfloat16 logits (upper 16 bits of a binary32) */
+} lce_dtype;
+
+typedef enum {
+    LCE_REDUCTION_MEAN = 0, /* out[0] = mean of the per-token losses */
+    LCE_REDUCTION_NONE = 1  /* out[i] = loss of token i */
+} lce_reduction;
+
+typedef enum {
+    LCE_OK = 0,
+    LCE_ERR_INVALID_ARG = 1, /* NULL pointer, negative or zero size, bad enum */
+    LCE_ERR_UNSUPPORTED = 2, /* valid but not handled (see each call) */
+    LCE_ERR_ALIAS = 3,       /* out overlaps an input */
+    LCE_ERR_OOM = 4,         /* scratch allocation failed */
+    LCE_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed */
+} lce_status;
+
+/*
+ * Row-wise softmax cross-entropy over a logit matrix.
+ *
+ * Defines: KernelIndex "Cross-entropy loss" (description; Semantics: logits
+ * float [tokens, vocab], target int64 [tokens], loss float [1]) and
+ * "Vocab-parallel cross-entropy, Megatron layout" (description; Semantics:
+ * logits float [seq, batch, vocab], target int64 [seq, batch], loss fp32
+ * [seq, batch]; only the TP=1 case, where each device holds the whole vocab).
+ *
+ *   logits    device, `tokens * vocab` elements of `dtype`, row-major: row i
+ *             holds token i's vocab logits.  A [seq, batch, vocab] tensor is
+ *             passed as tokens = seq * batch (row = s * batch + b).  Must be
+ *             aligned to its element size; any vocab >= 1 is accepted (rows
+ *             need not be 16-byte aligned).
+ *   dtype     LCE_F32 or LCE_BF16.
+ *   tokens    number of rows, >= 0.
+ *   vocab     number of classes, 1 <= vocab < 2^31.
+ *   target    device, `tokens` int64 class indices (same row order).  May be
+ *             NULL only when tokens == 0.
+ *   reduction LCE_REDUCTION_MEAN: out[0] = mean loss (NaN when tokens == 0).
+ *             LCE_REDUCTION_NONE: out[i] = loss_i, i < tokens (nothing is
+ *             written when tokens == 0).
+ *   out       device fp32, 1 or `tokens` elements; 4-byte aligned; must not
+ *             overlap logits or target.
+ *   stream    HIP stream the work is enqueued on.
+ *
+ * Returns LCE_OK, LCE_ERR_INVALID_ARG (NULL pointer, tokens < 0, vocab < 1,
+ * bad enum, misaligned pointer), LCE_ERR_UNSUPPORTED (vocab >= 2^31),
+ * LCE_ERR_ALIAS, LCE_ERR_OOM or LCE_ERR_HIP.
+ */
+lce_status lce_xent_fwd(const void* logits, lce_dtype dtype, int64_t tokens, int64_t vocab,
+                        const int64_t* target, lce_reduction reduction, float* out,
+                        hipStream_t stream);
+
+/*
+ * Fused LM-head projection + cross-entropy; the logits are never stored.
+ *
+ * Defines: KernelIndex "Fused linear + CPO loss" (description: activations
+ * projected through a vocab x hidden LM head against integer targets,
+ * computed chunked without materialising logits; Semantics: x float
+ * [batch, seq, hidden], weight float [vocab, hidden], target int64
+ * [batch, seq], loss float [1]).  The loss applied to the projected logits
+ * is the same per-token cross-entropy as lce_xent_fwd (the CPO preference
+ * term is not part of this call).
+ *
+ *   x         device bf16 [tokens, hidden], row-major ([batch, seq, hidden]
+ *             passed as tokens = batch * seq, row = b * seq + s).
+ *   weight    device bf16 [vocab, hidden], row-major (one row per class).
+ *   tokens    >= 0;  hidden >= 1 and a multiple of 8;  1 <= vocab < 2^31.
+ *   target    device int64 [tokens].
+ *   reduction LCE_REDUCTION_MEAN or LCE_REDUCTION_NONE, as for lce_xent_fwd.
+ *   out       device fp32, 1 or `tokens` elements; must not overlap inputs.
+ *   stream    HIP stream.
+ *
+ * logits z = x * weight^T are accumulated in fp32 from exact bf16 products
+ * and reduced on the fly into a per-token running (max, sum-exp) and the
+ * target logit.
+ *
+ * Returns as lce_xent_fwd; LCE_ERR_UNSUPPORTED when hidden is not a multiple
+ * of 8 or x / weight are not 16-byte aligned.
+ */
+lce_status lce_fused_linear_xent_fwd(const void* x, const void* weight, int64_t tokens,
+                                     int64_t hidden, int64_t vocab, const int64_t* target,
+                                     lce_reduction reduction, float* out, hipStream_t stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* lce_status_string(lce_status status);
+
+/* Detail message of the last failing call on this thread ("" if none).
+ * The pointer stays valid until the next liblce call on this thread. */
+const char* lce_last_error(void);
+
+/* MAJOR * 10000 + MINOR * 100 + PATCH. */
+int lce_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LCE_H */

@@ -71,11 +71,16 @@ def _load():
 
 
 def default_threads() -> int:
-    """Host threads the oracle uses when none are given."""
+    """Host threads the oracle uses when none are given: the CPUs this process may
+    run on, capped by OMP_NUM_THREADS when that is set."""
     try:
-        return len(os.sched_getaffinity(0))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        return os.cpu_count() or 1
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
 
 
 def _dtype_of(logits: np.ndarray, dtype: str | None) -> str:

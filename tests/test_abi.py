@@ -1,0 +1,123 @@
+"""liblce C ABI on the host: the library loads, exports every declared symbol, and
+rejects bad arguments with the documented status before touching the device.
+
+None of these calls reaches a HIP API: argument validation happens first."""
+import os
+import re
+import subprocess
+
+import pytest
+
+import vocab_cross_entropy_row_amd as lce
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lce.h")
+
+FAKE = 0x7F0000000000  # a plausible, 256-byte aligned device address; never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(lce.LIB_PATH):
+        from vocab_cross_entropy_row_amd import build
+        build.build()
+    return lce.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(lce_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(lce.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", lce.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_version_and_status_strings(lib):
+    assert lce.lce_version() == 100
+    names = [lce.lce_status_string(s) for s in range(6)]
+    assert names == ["LCE_OK", "LCE_ERR_INVALID_ARG", "LCE_ERR_UNSUPPORTED", "LCE_ERR_ALIAS",
+                     "LCE_ERR_OOM", "LCE_ERR_HIP"]
+    assert lce.lce_status_string(99) == "LCE_ERR_UNKNOWN"
+
+
+def _xent(logits=FAKE, dtype=lce.LCE_F32, tokens=16, vocab=32, target=FAKE + (1 << 20),
+          reduction=lce.LCE_REDUCTION_NONE, out=FAKE + (2 << 20)):
+    return lce.lce_xent_fwd(logits, dtype, tokens, vocab, target, reduction, out, 0)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(logits=0), lce.LCE_ERR_INVALID_ARG, "logits is NULL"),
+    (dict(target=0), lce.LCE_ERR_INVALID_ARG, "target is NULL"),
+    (dict(out=0), lce.LCE_ERR_INVALID_ARG, "out is NULL"),
+    (dict(out=0, tokens=0, reduction=lce.LCE_REDUCTION_MEAN), lce.LCE_ERR_INVALID_ARG, "out is NULL"),
+    (dict(dtype=7), lce.LCE_ERR_INVALID_ARG, "dtype"),
+    (dict(reduction=5), lce.LCE_ERR_INVALID_ARG, "reduction"),
+    (dict(tokens=-1), lce.LCE_ERR_INVALID_ARG, "tokens"),
+    (dict(vocab=0), lce.LCE_ERR_INVALID_ARG, "vocab"),
+    (dict(vocab=1 << 31), lce.LCE_ERR_UNSUPPORTED, "vocab"),
+    (dict(tokens=1 << 32), lce.LCE_ERR_UNSUPPORTED, "tokens"),
+    (dict(logits=FAKE + 2), lce.LCE_ERR_INVALID_ARG, "aligned"),
+    (dict(target=FAKE + (1 << 20) + 4), lce.LCE_ERR_INVALID_ARG, "aligned"),
+    (dict(out=FAKE + (2 << 20) + 2), lce.LCE_ERR_INVALID_ARG, "aligned"),
+    (dict(out=FAKE + 64), lce.LCE_ERR_ALIAS, "logits"),
+    (dict(out=FAKE + (1 << 20) + 8), lce.LCE_ERR_ALIAS, "target"),
+    (dict(tokens=1 << 31, vocab=1 << 30, dtype=lce.LCE_F32), lce.LCE_ERR_INVALID_ARG, "overflow"),
+])
+def test_xent_argument_errors(lib, kw, status, needle):
+    assert _xent(**kw) == status
+    assert needle in lce.lce_last_error()
+
+
+def test_xent_bf16_alignment_is_two_bytes(lib):
+    # bf16 logits only need 2-byte alignment; an odd address is rejected.
+    assert _xent(logits=FAKE + 1, dtype=lce.LCE_BF16) == lce.LCE_ERR_INVALID_ARG
+
+
+def test_xent_empty_none_is_a_no_op(lib):
+    # tokens == 0 with no reduction writes nothing and needs no pointers.
+    assert lce.lce_xent_fwd(0, lce.LCE_F32, 0, 32, 0, lce.LCE_REDUCTION_NONE, 0, 0) == lce.LCE_OK
+    assert lce.lce_last_error() == ""
+
+
+def _fused(x=FAKE, w=FAKE + (1 << 24), tokens=8, hidden=64, vocab=100, target=FAKE + (1 << 28),
+           reduction=lce.LCE_REDUCTION_NONE, out=FAKE + (1 << 30)):
+    return lce.lce_fused_linear_xent_fwd(x, w, tokens, hidden, vocab, target, reduction, out, 0)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(x=0), lce.LCE_ERR_INVALID_ARG, "x is NULL"),
+    (dict(w=0), lce.LCE_ERR_INVALID_ARG, "weight is NULL"),
+    (dict(target=0), lce.LCE_ERR_INVALID_ARG, "target is NULL"),
+    (dict(hidden=0), lce.LCE_ERR_INVALID_ARG, "hidden"),
+    (dict(vocab=0), lce.LCE_ERR_INVALID_ARG, "vocab"),
+    (dict(hidden=60), lce.LCE_ERR_UNSUPPORTED, "multiple of 8"),
+    (dict(x=FAKE + 8), lce.LCE_ERR_UNSUPPORTED, "16-byte"),
+    (dict(w=FAKE + (1 << 24) + 8), lce.LCE_ERR_UNSUPPORTED, "16-byte"),
+    (dict(reduction=3), lce.LCE_ERR_INVALID_ARG, "reduction"),
+    (dict(out=FAKE + 16), lce.LCE_ERR_ALIAS, "x"),
+    (dict(out=FAKE + (1 << 24) + 16), lce.LCE_ERR_ALIAS, "weight"),
+    (dict(out=FAKE + (1 << 28)), lce.LCE_ERR_ALIAS, "target"),
+])
+def test_fused_argument_errors(lib, kw, status, needle):
+    assert _fused(**kw) == status
+    assert needle in lce.lce_last_error()
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    torch = pytest.importorskip("torch")
+    z = torch.zeros(4, 8)
+    t = torch.zeros(4, dtype=torch.int64)
+    with pytest.raises(ValueError):
+        lce.xent(z, t)
+    with pytest.raises(ValueError):
+        lce.fused_linear_xent(z.bfloat16(), z.bfloat16(), t)

@@ -1,0 +1,340 @@
+"""GPU parity: liblce (through its C ABI) against the fp64 oracle, element by element.
+
+Tolerances (fixed before any kernel was written):
+  row cross-entropy, fp32 or bf16 logits: per-token |gpu - oracle| <= 1e-4,
+                                          mean relative error <= 1e-5;
+  fused projection + cross-entropy (bf16): per-token |gpu - oracle| <= 2e-2,
+                                          mean relative error <= 1e-3.
+Inputs come from the seeded generator in ``lce_synth``; the oracle sees the very
+same bytes.  Small cases span several tiles, ragged tails, unaligned rows and
+every kernel path; the five full-size workloads run in the launch configuration
+the benchmark times.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import lce_synth
+import oracle
+from lce_synth import WORKLOADS
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import vocab_cross_entropy_row_amd as lce  # noqa: E402
+
+TOK_ABS = 1e-4
+MEAN_REL = 1e-5
+MEAN_ABS_FLOOR = 1e-7
+FUSED_TOK_ABS = 2e-2
+FUSED_MEAN_REL = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lce.load()
+    yield
+    torch.cuda.synchronize()
+
+
+class forced_env:
+    """Temporarily set liblce's path-selection environment variables."""
+
+    def __init__(self, **kv):
+        self.kv = {k: str(v) for k, v in kv.items()}
+        self.old = {}
+
+    def __enter__(self):
+        for k, v in self.kv.items():
+            self.old[k] = os.environ.get(k)
+            os.environ[k] = v
+
+    def __exit__(self, *exc):
+        for k, v in self.old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
+def to_dev(arr):
+    """numpy f32 -> fp32 tensor; numpy uint16 (bf16 bits) -> bf16 tensor."""
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+
+
+def gpu_xent(logits_np, target_np, reduction, dtype):
+    z = to_dev(logits_np)
+    t = torch.from_numpy(np.ascontiguousarray(target_np, dtype=np.int64)).cuda()
+    out = lce.xent(z, t, reduction)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def rand_logits(rng_seed, rows, vocab, dtype, std=1.0, shift=0.0):
+    f = lce_synth.normal_f32(rng_seed, 9, rows, vocab, std)
+    if shift:
+        f = f + np.float32(shift)
+    return f if dtype == "f32" else lce_synth.f32_to_bf16_bits(f)
+
+
+def check_xent(logits_np, target_np, dtype, label=""):
+    want = oracle.xent_rows(logits_np, target_np, dtype=dtype)
+    got = gpu_xent(logits_np, target_np, "none", dtype)
+    assert got.shape == want.shape
+    err = np.abs(got - want)
+    assert np.array_equal(np.isnan(got), np.isnan(want)), label
+    assert np.nanmax(err, initial=0.0) <= TOK_ABS, f"{label} max abs err {np.nanmax(err)}"
+    gm = gpu_xent(logits_np, target_np, "mean", dtype)[0]
+    wm = oracle.mean(want)
+    if math.isnan(wm):
+        assert math.isnan(gm), label
+    else:
+        # relative bound; the absolute floor only matters where the exact mean is 0
+        # (vocab = 1), where a relative bound is undefined
+        assert abs(gm - wm) <= MEAN_REL * abs(wm) + MEAN_ABS_FLOOR, f"{label} mean {gm} vs {wm}"
+    return float(np.nanmax(err, initial=0.0))
+
+
+# ------------------------------------------------------------------ small shapes, every path
+
+SMALL = [(1, 1), (3, 2), (5, 3), (7, 7), (64, 31), (17, 64), (9, 100), (33, 255), (65, 1000),
+         (40, 4096), (13, 4097), (21, 5000), (8, 8191), (5, 8193), (3, 20000)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rows,vocab", SMALL)
+def test_small_auto_path(dtype, rows, vocab):
+    z = rand_logits(rows * 7919 + vocab, rows, vocab, dtype)
+    t = lce_synth.targets(vocab + 5, rows, vocab)
+    check_xent(z, t, dtype, f"{dtype} {rows}x{vocab}")
+
+
+@pytest.mark.parametrize("path,extra", [("wave", {}), ("block", {}), ("split", {}),
+                                        ("split", {"LCE_SPLITS": 3}), ("split", {"LCE_SPLITS": 7})])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rows,vocab", [(6, 3), (11, 777), (9, 4099), (4, 33333), (2, 70001)])
+def test_forced_paths(path, extra, dtype, rows, vocab):
+    z = rand_logits(rows + vocab, rows, vocab, dtype, std=3.0)
+    t = lce_synth.targets(vocab, rows, vocab)
+    with forced_env(LCE_PATH=path, **extra):
+        check_xent(z, t, dtype, f"{path} {extra} {dtype} {rows}x{vocab}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_large_shift_keeps_accuracy(dtype):
+    """Rows shifted by -1000 (exact in both dtypes' grids) lose no accuracy."""
+    z = rand_logits(4, 37, 3001, "f32", std=2.0)
+    z = (np.round(z * 64) / 64 - 1000).astype(np.float32)
+    if dtype == "bf16":
+        z = lce_synth.f32_to_bf16_bits(z)
+    check_xent(z, lce_synth.targets(6, 37, 3001), dtype, "shift -1000")
+
+
+def test_row_shift_invariance_exact_inputs():
+    """Logits on a 2^-8 grid (|z| < 8) plus integer row shifts up to 2^15 are exact in
+    fp32; the GPU loss must not move by more than the tolerance."""
+    rng = np.random.default_rng(1)
+    rows, vocab = 64, 4096
+    z = (np.round(rng.uniform(-8, 8, (rows, vocab)) * 256) / 256).astype(np.float32)
+    c = rng.integers(-2 ** 15, 2 ** 15, rows).astype(np.float32)
+    t = rng.integers(0, vocab, rows)
+    a = gpu_xent(z, t, "none", "f32")
+    b = gpu_xent(z + c[:, None], t, "none", "f32")
+    assert np.max(np.abs(a - b)) <= TOK_ABS
+
+
+def test_uniform_logits_give_ln_vocab():
+    for vocab in (1, 2, 4096, 131072):
+        z = np.full((4, vocab), 37.5, dtype=np.float32)
+        got = gpu_xent(z, np.arange(4) % vocab, "none", "f32")
+        assert np.max(np.abs(got - math.log(vocab))) <= TOK_ABS
+
+
+def test_megatron_layout_matches_flat_view():
+    w = WORKLOADS["megatron_bf16_2048x4x4096_none"]
+    z = to_dev(w.logits(0, 512)).view(128, 4, 4096)
+    t = torch.from_numpy(w.target(0, 512)).cuda().view(128, 4)
+    a = lce.xent(z, t, "none")
+    b = lce.xent(z.reshape(512, 4096), t.reshape(512), "none")
+    torch.cuda.synchronize()
+    assert a.shape == (128, 4)
+    assert torch.equal(a.reshape(512), b)
+
+
+def test_invalid_targets_and_nan_logits():
+    rows, vocab = 8, 1000
+    z = rand_logits(3, rows, vocab, "f32")
+    z[5, 17] = np.nan
+    t = np.array([0, -1, 999, 1000, 5, 3, 1 << 40, 2], dtype=np.int64)
+    check_xent(z, t, "f32", "invalid")
+    got = gpu_xent(z, t, "none", "f32")
+    assert np.isnan(got[[1, 3, 5, 6]]).all() and not np.isnan(got[[0, 2, 4, 7]]).any()
+    assert math.isnan(gpu_xent(z, t, "mean", "f32")[0])
+
+
+def test_zero_tokens():
+    z = torch.empty((0, 16), device="cuda")
+    t = torch.empty((0,), dtype=torch.int64, device="cuda")
+    assert math.isnan(lce.xent(z, t, "mean").item())
+    assert lce.xent(z, t, "none").numel() == 0
+
+
+def test_output_guard_bytes_untouched():
+    rows, vocab = 100, 513
+    z = to_dev(rand_logits(8, rows, vocab, "f32"))
+    t = torch.from_numpy(lce_synth.targets(8, rows, vocab)).cuda()
+    buf = torch.full((rows + 64,), 7.25, device="cuda")
+    out = buf[32:32 + rows]
+    lce.xent(z, t, "none", out=out)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:32] == 7.25) and torch.all(buf[32 + rows:] == 7.25)
+    assert torch.isfinite(out).all()
+
+
+def test_repeated_calls_bitwise_identical():
+    w = WORKLOADS["ce_f32_16384x4096_mean"]
+    z = to_dev(w.logits(0, 4096))
+    t = torch.from_numpy(w.target(0, 4096)).cuda()
+    first_mean = lce.xent(z, t, "mean").clone()
+    first_none = lce.xent(z, t, "none").clone()
+    for _ in range(5):
+        assert torch.equal(lce.xent(z, t, "mean"), first_mean)
+        assert torch.equal(lce.xent(z, t, "none"), first_none)
+
+
+def test_binding_checks_shapes():
+    z = torch.zeros((4, 8), device="cuda")
+    with pytest.raises(ValueError):
+        lce.xent(z, torch.zeros(5, dtype=torch.int64, device="cuda"))
+    with pytest.raises(TypeError):
+        lce.xent(z.half(), torch.zeros(4, dtype=torch.int64, device="cuda"))
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+def load_workload_streaming(w, block_rows=1024):
+    """Generate a row-CE workload block by block into device memory; return the device
+    logits (in the workload's shape), device targets and the oracle's per-token losses."""
+    tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    dev = torch.empty(w.shape, dtype=tdt, device="cuda")
+    flat = dev.view(w.tokens, w.vocab)
+    tgt = w.target()
+    want = np.empty(w.tokens)
+    for r0 in range(0, w.tokens, block_rows):
+        r1 = min(w.tokens, r0 + block_rows)
+        host = w.logits(r0, r1)
+        flat[r0:r1].copy_(to_dev(host))
+        want[r0:r1] = oracle.xent_rows(host, tgt[r0:r1], dtype=w.dtype)
+        del host
+    t_dev = torch.from_numpy(tgt).cuda().view(w.target_shape)
+    return dev, t_dev, want
+
+
+@pytest.mark.parametrize("name", ["ce_f32_16384x4096_mean", "megatron_bf16_2048x4x4096_none",
+                                  "ce_f32_16384x131072_mean", "megatron_bf16_2048x4x131072_none"])
+def test_full_size_row_workloads(name):
+    w = WORKLOADS[name]
+    print(f"\n[parity] workload {name} shape {w.shape}", flush=True)
+    z, t, want = load_workload_streaming(w)
+    per = lce.xent(z, t, "none").cpu().numpy().reshape(-1).astype(np.float64)
+    mean = lce.xent(z, t, "mean").item()
+    err = np.abs(per - want)
+    print(f"[parity] {name}: max abs err {err.max():.3e}; mean {mean:.8f} vs {oracle.mean(want):.8f}",
+          flush=True)
+    assert err.max() <= TOK_ABS
+    wm = oracle.mean(want)
+    assert abs(mean - wm) <= MEAN_REL * abs(wm)
+    del z
+    torch.cuda.empty_cache()
+
+
+def test_fused_full_size_workload():
+    w = WORKLOADS["fused_bf16_t2048_h4096_v128256_mean"]
+    print(f"\n[parity] fused workload {w.shape}", flush=True)
+    xb, wb, tg = w.x(), w.weight(), w.target()
+    x, W, t = to_dev(xb), to_dev(wb), torch.from_numpy(tg).cuda()
+    per = lce.fused_linear_xent(x, W, t, "none").cpu().numpy().astype(np.float64)
+    mean = lce.fused_linear_xent(x, W, t, "mean").item()
+    want = oracle.fused_linear_xent_rows(xb, wb, tg)
+    err = np.abs(per - want)
+    wm = oracle.mean(want)
+    print(f"[parity] fused: max abs err {err.max():.3e}; mean {mean:.8f} vs {wm:.8f}", flush=True)
+    assert err.max() <= FUSED_TOK_ABS
+    assert abs(mean - wm) <= FUSED_MEAN_REL * abs(wm)
+    del x, W
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ fused, small shapes
+
+FUSED_SMALL = [(1, 8, 1), (7, 64, 5), (33, 72, 300), (300, 136, 1000), (257, 64, 4099),
+               (64, 512, 513), (520, 256, 2000)]
+
+
+@pytest.mark.parametrize("tokens,hidden,vocab", FUSED_SMALL)
+def test_fused_small(tokens, hidden, vocab):
+    xb = lce_synth.normal_bf16_bits(11 + tokens, 0, tokens, hidden, 1.0)
+    wb = lce_synth.normal_bf16_bits(12 + vocab, 2, vocab, hidden, 1.0 / math.sqrt(hidden) * 3)
+    tg = lce_synth.targets(13, tokens, vocab)
+    x, W, t = to_dev(xb), to_dev(wb), torch.from_numpy(tg).cuda()
+    want = oracle.fused_linear_xent_rows(xb, wb, tg)
+    per = lce.fused_linear_xent(x, W, t, "none").cpu().numpy().astype(np.float64)
+    mean = lce.fused_linear_xent(x, W, t, "mean").item()
+    err = np.abs(per - want)
+    assert err.max() <= FUSED_TOK_ABS, f"max abs err {err.max()}"
+    # fp32 accumulation of exact bf16 products: far inside the stated tolerance
+    assert err.max() <= 1e-3
+    wm = oracle.mean(want)
+    assert abs(mean - wm) <= FUSED_MEAN_REL * abs(wm) + MEAN_ABS_FLOOR  # floor: vocab = 1
+
+
+@pytest.mark.parametrize("segments", [1, 2, 3, 5])
+def test_fused_segment_counts(segments):
+    tokens, hidden, vocab = 300, 128, 3000
+    xb = lce_synth.normal_bf16_bits(21, 0, tokens, hidden, 1.0)
+    wb = lce_synth.normal_bf16_bits(22, 2, vocab, hidden, 0.2)
+    tg = lce_synth.targets(23, tokens, vocab)
+    want = oracle.fused_linear_xent_rows(xb, wb, tg)
+    with forced_env(LCE_FUSED_SEGMENTS=segments):
+        per = lce.fused_linear_xent(to_dev(xb), to_dev(wb), torch.from_numpy(tg).cuda(), "none")
+        per = per.cpu().numpy().astype(np.float64)
+    assert np.abs(per - want).max() <= 1e-3
+
+
+def test_fused_identity_head_matches_row_path():
+    """W = I: the fused loss equals the row kernel's loss on x."""
+    tokens, hidden = 96, 256
+    xb = lce_synth.normal_bf16_bits(31, 0, tokens, hidden, 2.0)
+    eye = lce_synth.f32_to_bf16_bits(np.eye(hidden, dtype=np.float32))
+    tg = lce_synth.targets(32, tokens, hidden)
+    a = lce.fused_linear_xent(to_dev(xb), to_dev(eye), torch.from_numpy(tg).cuda(), "none")
+    b = lce.xent(to_dev(xb), torch.from_numpy(tg).cuda(), "none")
+    torch.cuda.synchronize()
+    assert torch.max(torch.abs(a - b)).item() <= 1e-5
+
+
+def test_fused_invalid_targets():
+    tokens, hidden, vocab = 10, 64, 500
+    xb = lce_synth.normal_bf16_bits(41, 0, tokens, hidden, 1.0)
+    wb = lce_synth.normal_bf16_bits(42, 2, vocab, hidden, 0.2)
+    tg = np.array([0, -1, 499, 500, 7, 1 << 33, 3, 2, 1, 0], dtype=np.int64)
+    got = lce.fused_linear_xent(to_dev(xb), to_dev(wb), torch.from_numpy(tg).cuda(), "none").cpu().numpy()
+    assert np.isnan(got[[1, 3, 5]]).all() and not np.isnan(got[[0, 2, 4, 6, 7, 8, 9]]).any()
+
+
+def test_fused_repeated_calls_bitwise_identical():
+    tokens, hidden, vocab = 512, 256, 5000
+    x = to_dev(lce_synth.normal_bf16_bits(51, 0, tokens, hidden, 1.0))
+    W = to_dev(lce_synth.normal_bf16_bits(52, 2, vocab, hidden, 0.1))
+    t = torch.from_numpy(lce_synth.targets(53, tokens, vocab)).cuda()
+    first = lce.fused_linear_xent(x, W, t, "none").clone()
+    m0 = lce.fused_linear_xent(x, W, t, "mean").clone()
+    for _ in range(3):
+        assert torch.equal(lce.fused_linear_xent(x, W, t, "none"), first)
+        assert torch.equal(lce.fused_linear_xent(x, W, t, "mean"), m0)

@@ -1,0 +1,180 @@
+"""Python binding for liblce (argument marshalling only; all compute runs in HIP kernels).
+
+The raw C-ABI calls keep their C names and take plain integers (device addresses,
+sizes, enum values, a ``hipStream_t`` as an integer) and return the ``lce_status``
+code:
+
+* :func:`lce_xent_fwd`, :func:`lce_fused_linear_xent_fwd`
+* :func:`lce_status_string`, :func:`lce_last_error`, :func:`lce_version`
+
+:func:`xent` and :func:`fused_linear_xent` are thin conveniences over them for
+torch tensors: they check device/dtype/contiguity, allocate the fp32 output with
+torch, pass ``data_ptr()`` values and torch's current HIP stream, and raise
+:class:`LceError` on a non-zero status.  There is no CPU fallback: if
+``liblce.so`` is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblce.so")
+
+LCE_F32 = 0
+LCE_BF16 = 1
+LCE_REDUCTION_MEAN = 0
+LCE_REDUCTION_NONE = 1
+
+LCE_OK = 0
+LCE_ERR_INVALID_ARG = 1
+LCE_ERR_UNSUPPORTED = 2
+LCE_ERR_ALIAS = 3
+LCE_ERR_OOM = 4
+LCE_ERR_HIP = 5
+
+EXPORTED = ("lce_xent_fwd", "lce_fused_linear_xent_fwd", "lce_status_string",
+            "lce_last_error", "lce_version")
+
+_lib = None
+
+
+class LceError(RuntimeError):
+    """A liblce call returned a non-zero status."""
+
+    def __init__(self, status: int, where: str):
+        self.status = int(status)
+        msg = f"{where}: {lce_status_string(status)}: {lce_last_error()}"
+        super().__init__(msg)
+
+
+def load() -> ctypes.CDLL:
+    """Load the in-tree liblce.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"liblce.so not found at {LIB_PATH}; build it with "
+            "`python -m vocab_cross_entropy_row_amd.build` (there is no CPU fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.lce_xent_fwd.restype = ctypes.c_int
+    lib.lce_xent_fwd.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                 ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.lce_fused_linear_xent_fwd.restype = ctypes.c_int
+    lib.lce_fused_linear_xent_fwd.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                              ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                              ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.lce_status_string.restype = ctypes.c_char_p
+    lib.lce_status_string.argtypes = [ctypes.c_int]
+    lib.lce_last_error.restype = ctypes.c_char_p
+    lib.lce_last_error.argtypes = []
+    lib.lce_version.restype = ctypes.c_int
+    lib.lce_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+# ------------------------------------------------------------------ raw C ABI
+
+def lce_xent_fwd(logits: int, dtype: int, tokens: int, vocab: int, target: int,
+                 reduction: int, out: int, stream: int) -> int:
+    return load().lce_xent_fwd(logits or None, dtype, tokens, vocab, target or None, reduction,
+                               out or None, stream or None)
+
+
+def lce_fused_linear_xent_fwd(x: int, weight: int, tokens: int, hidden: int, vocab: int,
+                              target: int, reduction: int, out: int, stream: int) -> int:
+    return load().lce_fused_linear_xent_fwd(x or None, weight or None, tokens, hidden, vocab,
+                                            target or None, reduction, out or None,
+                                            stream or None)
+
+
+def lce_status_string(status: int) -> str:
+    return load().lce_status_string(int(status)).decode()
+
+
+def lce_last_error() -> str:
+    return load().lce_last_error().decode()
+
+
+def lce_version() -> int:
+    return load().lce_version()
+
+
+# ------------------------------------------------------------------ torch conveniences
+
+_REDUCTIONS = {"mean": LCE_REDUCTION_MEAN, "none": LCE_REDUCTION_NONE}
+
+
+def _stream_of(t) -> int:
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def xent(logits, target, reduction: str = "mean", out=None):
+    """Cross-entropy of ``logits`` ([..., vocab], fp32 or bf16, contiguous, on a HIP device)
+    against int64 ``target`` (the leading shape).  Returns fp32: a 1-element tensor for
+    ``"mean"``, the leading shape for ``"none"``."""
+    import torch
+    if reduction not in _REDUCTIONS:
+        raise ValueError(f"reduction must be 'mean' or 'none', got {reduction!r}")
+    if not logits.is_cuda or not target.is_cuda:
+        raise ValueError("logits and target must be device tensors")
+    if logits.dtype == torch.float32:
+        dt = LCE_F32
+    elif logits.dtype == torch.bfloat16:
+        dt = LCE_BF16
+    else:
+        raise TypeError(f"logits must be float32 or bfloat16, got {logits.dtype}")
+    if target.dtype != torch.int64:
+        raise TypeError(f"target must be int64, got {target.dtype}")
+    if not logits.is_contiguous() or not target.is_contiguous():
+        raise ValueError("logits and target must be contiguous")
+    if logits.dim() < 1 or tuple(target.shape) != tuple(logits.shape[:-1]):
+        raise ValueError(f"target shape {tuple(target.shape)} must be logits shape "
+                         f"{tuple(logits.shape)} without the vocab axis")
+    vocab = logits.shape[-1]
+    tokens = target.numel()
+    if out is None:
+        shape = (1,) if reduction == "mean" else tuple(target.shape)
+        out = torch.empty(shape, dtype=torch.float32, device=logits.device)
+    st = lce_xent_fwd(logits.data_ptr(), dt, tokens, vocab, target.data_ptr(),
+                      _REDUCTIONS[reduction], out.data_ptr(), _stream_of(logits))
+    if st != LCE_OK:
+        raise LceError(st, "lce_xent_fwd")
+    return out
+
+
+def fused_linear_xent(x, weight, target, reduction: str = "mean", out=None):
+    """Cross-entropy of ``x @ weight.T`` against ``target`` without storing the logits.
+
+    ``x``: bf16 [..., hidden]; ``weight``: bf16 [vocab, hidden]; ``target``: int64 with the
+    leading shape of ``x``.  Returns fp32 as :func:`xent`."""
+    import torch
+    if reduction not in _REDUCTIONS:
+        raise ValueError(f"reduction must be 'mean' or 'none', got {reduction!r}")
+    for name, t in (("x", x), ("weight", weight), ("target", target)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if x.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
+        raise TypeError("x and weight must be bfloat16")
+    if target.dtype != torch.int64:
+        raise TypeError("target must be int64")
+    if weight.dim() != 2 or x.shape[-1] != weight.shape[1]:
+        raise ValueError("weight must be [vocab, hidden] with hidden = x.shape[-1]")
+    if tuple(target.shape) != tuple(x.shape[:-1]):
+        raise ValueError("target shape must be x shape without the hidden axis")
+    vocab, hidden = weight.shape
+    tokens = target.numel()
+    if out is None:
+        shape = (1,) if reduction == "mean" else tuple(target.shape)
+        out = torch.empty(shape, dtype=torch.float32, device=x.device)
+    st = lce_fused_linear_xent_fwd(x.data_ptr(), weight.data_ptr(), tokens, hidden, vocab,
+                                   target.data_ptr(), _REDUCTIONS[reduction], out.data_ptr(),
+                                   _stream_of(x))
+    if st != LCE_OK:
+        raise LceError(st, "lce_fused_linear_xent_fwd")
+    return out

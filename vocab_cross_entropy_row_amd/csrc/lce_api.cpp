@@ -1,0 +1,331 @@
+// liblce host API: argument validation, path selection, scratch management
+// and error reporting.  Every entry point validates its arguments on the host
+// before it makes any HIP call, so argument errors never touch the device.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "../../include/lce.h"
+#include "lce_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+lce_status fail(lce_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+lce_status hip_fail(hipError_t e, const char* what) {
+  return fail(LCE_ERR_HIP, "%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
+}
+
+// [a, a + an) and [b, b + bn) overlap (byte ranges).
+bool overlaps(const void* a, uint64_t an, const void* b, uint64_t bn) {
+  if (!a || !b || an == 0 || bn == 0) return false;
+  const uint64_t a0 = (uint64_t)(uintptr_t)a, b0 = (uint64_t)(uintptr_t)b;
+  return a0 < b0 + bn && b0 < a0 + an;
+}
+
+bool aligned(const void* p, uint64_t n) { return ((uintptr_t)p % n) == 0; }
+
+// ------------------------------------------------------------ scratch pool
+// One grow-only device buffer per (device, stream); kept until process exit.
+// Layout: [0, 256) ticket, then 256-byte-aligned regions carved by Carve.
+struct Scratch {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_mu;
+std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
+std::map<int, int> g_num_cus;
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
+
+struct Carve {
+  size_t off = kAlign;  // the ticket lives in the first 256 bytes
+  size_t take(size_t n) {
+    const size_t o = off;
+    off = round_up(off + n, kAlign);
+    return o;
+  }
+};
+
+lce_status get_scratch(hipStream_t stream, size_t need, char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_mu);
+  Scratch& s = g_scratch[{dev, stream}];
+  if (s.bytes < need) {
+    if (getenv("LCE_TEST_FAIL_ALLOC")) return fail(LCE_ERR_OOM, "scratch allocation refused (LCE_TEST_FAIL_ALLOC)");
+    if (s.ptr) {
+      e = hipStreamSynchronize(stream);  // work queued on this stream may still use it
+      if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+      (void)hipFree(s.ptr);
+      s.ptr = nullptr;
+      s.bytes = 0;
+    }
+    const size_t bytes = round_up(need + need / 4, size_t(1) << 20);
+    void* p = nullptr;
+    e = hipMalloc(&p, bytes);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(LCE_ERR_OOM, "hipMalloc of %zu bytes of scratch failed: %s", bytes, hipGetErrorName(e));
+    }
+    // The ticket must start at zero; kernels leave it at zero afterwards.
+    e = lce::launch_zero_u32((unsigned*)p, kAlign / sizeof(unsigned), stream);
+    if (e != hipSuccess) {
+      (void)hipFree(p);
+      return hip_fail(e, "scratch initialisation");
+    }
+    s.ptr = p;
+    s.bytes = bytes;
+  }
+  *out = (char*)s.ptr;
+  return LCE_OK;
+}
+
+lce_status num_cus(int* n) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_mu);
+  auto it = g_num_cus.find(dev);
+  if (it == g_num_cus.end()) {
+    int v = 0;
+    e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    it = g_num_cus.emplace(dev, v > 0 ? v : 1).first;
+  }
+  *n = it->second;
+  return LCE_OK;
+}
+
+int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  return (v && *v) ? atoi(v) : dflt;
+}
+
+// ------------------------------------------------------------ validation (host only)
+lce_status validate_common(int64_t tokens, const int64_t* target, int reduction, const float* out) {
+  if (reduction != LCE_REDUCTION_MEAN && reduction != LCE_REDUCTION_NONE)
+    return fail(LCE_ERR_INVALID_ARG, "reduction must be LCE_REDUCTION_MEAN or LCE_REDUCTION_NONE (got %d)", reduction);
+  if (tokens < 0) return fail(LCE_ERR_INVALID_ARG, "tokens must be >= 0 (got %lld)", (long long)tokens);
+  if (tokens >= (int64_t(1) << 32) - 1)
+    return fail(LCE_ERR_UNSUPPORTED, "tokens must be < 2^32 - 1 (got %lld)", (long long)tokens);
+  const bool writes = reduction == LCE_REDUCTION_MEAN || tokens > 0;
+  if (writes && !out) return fail(LCE_ERR_INVALID_ARG, "out is NULL");
+  if (tokens > 0 && !target) return fail(LCE_ERR_INVALID_ARG, "target is NULL");
+  if (target && !aligned(target, 8)) return fail(LCE_ERR_INVALID_ARG, "target is not 8-byte aligned");
+  if (out && !aligned(out, 4)) return fail(LCE_ERR_INVALID_ARG, "out is not 4-byte aligned");
+  return LCE_OK;
+}
+
+uint64_t out_bytes(int64_t tokens, int reduction) {
+  return reduction == LCE_REDUCTION_MEAN ? 4u : (uint64_t)tokens * 4u;
+}
+
+lce_status validate_xent(const void* logits, int dtype, int64_t tokens, int64_t vocab,
+                         const int64_t* target, int reduction, const float* out) {
+  if (dtype != LCE_F32 && dtype != LCE_BF16)
+    return fail(LCE_ERR_INVALID_ARG, "dtype must be LCE_F32 or LCE_BF16 (got %d)", dtype);
+  lce_status s = validate_common(tokens, target, reduction, out);
+  if (s != LCE_OK) return s;
+  if (vocab < 1) return fail(LCE_ERR_INVALID_ARG, "vocab must be >= 1 (got %lld)", (long long)vocab);
+  if (vocab >= (int64_t(1) << 31))
+    return fail(LCE_ERR_UNSUPPORTED, "vocab must be < 2^31 (got %lld)", (long long)vocab);
+  const int64_t esize = dtype == LCE_F32 ? 4 : 2;
+  if (tokens > 0 && !logits) return fail(LCE_ERR_INVALID_ARG, "logits is NULL");
+  if (tokens > INT64_MAX / (vocab * esize))
+    return fail(LCE_ERR_INVALID_ARG, "tokens * vocab overflows");
+  if (logits && !aligned(logits, (uint64_t)esize))
+    return fail(LCE_ERR_INVALID_ARG, "logits is not aligned to its element size");
+  const uint64_t ob = out_bytes(tokens, reduction);
+  if (overlaps(out, ob, logits, (uint64_t)(tokens * vocab * esize)))
+    return fail(LCE_ERR_ALIAS, "out overlaps logits");
+  if (overlaps(out, ob, target, (uint64_t)tokens * 8u)) return fail(LCE_ERR_ALIAS, "out overlaps target");
+  return LCE_OK;
+}
+
+lce_status validate_fused(const void* x, const void* w, int64_t tokens, int64_t hidden, int64_t vocab,
+                          const int64_t* target, int reduction, const float* out) {
+  lce_status s = validate_common(tokens, target, reduction, out);
+  if (s != LCE_OK) return s;
+  if (hidden < 1) return fail(LCE_ERR_INVALID_ARG, "hidden must be >= 1 (got %lld)", (long long)hidden);
+  if (vocab < 1) return fail(LCE_ERR_INVALID_ARG, "vocab must be >= 1 (got %lld)", (long long)vocab);
+  if (vocab >= (int64_t(1) << 31))
+    return fail(LCE_ERR_UNSUPPORTED, "vocab must be < 2^31 (got %lld)", (long long)vocab);
+  if (hidden >= (int64_t(1) << 31))
+    return fail(LCE_ERR_UNSUPPORTED, "hidden must be < 2^31 (got %lld)", (long long)hidden);
+  if (!w) return fail(LCE_ERR_INVALID_ARG, "weight is NULL");
+  if (tokens > 0 && !x) return fail(LCE_ERR_INVALID_ARG, "x is NULL");
+  if (hidden % 8 != 0)
+    return fail(LCE_ERR_UNSUPPORTED, "hidden must be a multiple of 8 (got %lld)", (long long)hidden);
+  if (!aligned(w, 16) || (x && !aligned(x, 16)))
+    return fail(LCE_ERR_UNSUPPORTED, "x and weight must be 16-byte aligned");
+  if (vocab > INT64_MAX / (hidden * 2) || tokens > INT64_MAX / (hidden * 2))
+    return fail(LCE_ERR_INVALID_ARG, "tensor size overflows");
+  const uint64_t ob = out_bytes(tokens, reduction);
+  if (overlaps(out, ob, x, (uint64_t)(tokens * hidden * 2))) return fail(LCE_ERR_ALIAS, "out overlaps x");
+  if (overlaps(out, ob, w, (uint64_t)(vocab * hidden * 2))) return fail(LCE_ERR_ALIAS, "out overlaps weight");
+  if (overlaps(out, ob, target, (uint64_t)tokens * 8u)) return fail(LCE_ERR_ALIAS, "out overlaps target");
+  return LCE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lce_status_string(lce_status status) {
+  switch (status) {
+    case LCE_OK: return "LCE_OK";
+    case LCE_ERR_INVALID_ARG: return "LCE_ERR_INVALID_ARG";
+    case LCE_ERR_UNSUPPORTED: return "LCE_ERR_UNSUPPORTED";
+    case LCE_ERR_ALIAS: return "LCE_ERR_ALIAS";
+    case LCE_ERR_OOM: return "LCE_ERR_OOM";
+    case LCE_ERR_HIP: return "LCE_ERR_HIP";
+  }
+  return "LCE_ERR_UNKNOWN";
+}
+
+const char* lce_last_error(void) { return g_last_error.c_str(); }
+
+int lce_version(void) { return LCE_VERSION_MAJOR * 10000 + LCE_VERSION_MINOR * 100 + LCE_VERSION_PATCH; }
+
+lce_status lce_xent_fwd(const void* logits, lce_dtype dtype, int64_t tokens, int64_t vocab,
+                        const int64_t* target, lce_reduction reduction, float* out,
+                        hipStream_t stream) {
+  g_last_error.clear();
+  lce_status s = validate_xent(logits, (int)dtype, tokens, vocab, target, (int)reduction, out);
+  if (s != LCE_OK) return s;
+  const bool mean = reduction == LCE_REDUCTION_MEAN;
+  if (tokens == 0) {
+    if (!mean) return LCE_OK;
+    hipError_t e = lce::launch_fill_f32(out, 1, __builtin_nanf(""), stream);
+    return e == hipSuccess ? LCE_OK : hip_fail(e, "launch");
+  }
+  int cus = 0;
+  if ((s = num_cus(&cus)) != LCE_OK) return s;
+
+  lce::XentArgs a{};
+  a.logits = logits;
+  a.bf16 = dtype == LCE_BF16;
+  a.tokens = tokens;
+  a.vocab = vocab;
+  a.target = target;
+  a.out = out;
+  a.reduce_mean = mean ? 1 : 0;
+
+  // Path: short rows -> one wave per row; long rows -> one workgroup per row,
+  // or several workgroups per row when there are too few rows to fill the CUs.
+  const int64_t esize = a.bf16 ? 2 : 4;
+  const int64_t row_bytes = vocab * esize;
+  const int64_t nvec = row_bytes / 16;
+  const char* forced = getenv("LCE_PATH");
+  if (forced && !strcmp(forced, "wave")) a.path = lce::XentPath::WaveRows;
+  else if (forced && !strcmp(forced, "block")) a.path = lce::XentPath::BlockRows;
+  else if (forced && !strcmp(forced, "split")) a.path = lce::XentPath::Split;
+  else if (row_bytes <= 32 * 1024) a.path = lce::XentPath::WaveRows;
+  else if (tokens >= 2 * (int64_t)cus) a.path = lce::XentPath::BlockRows;
+  else a.path = lce::XentPath::Split;
+
+  const int64_t per_lane = (nvec + 63) / 64;
+  a.unroll = per_lane <= 4 ? 4 : per_lane <= 8 ? 8 : 16;
+
+  size_t need_partials = 0, need_split = 0;
+  if (a.path == lce::XentPath::Split) {
+    if (tokens > 65535) return fail(LCE_ERR_UNSUPPORTED, "split path needs tokens <= 65535");
+    // Enough workgroups for ~4 per CU, but at least one 256-thread batch of 8
+    // chunks per workgroup.
+    int64_t S = env_int("LCE_SPLITS", 0);
+    if (S <= 0) S = (4 * (int64_t)cus + tokens - 1) / tokens;
+    const int64_t max_s = (nvec + lce::kRowThreads * 8 - 1) / (lce::kRowThreads * 8);
+    if (S > max_s) S = max_s;
+    if (S < 1) S = 1;
+    if (S > 65535) S = 65535;
+    a.splits = (int)S;
+    a.chunks_per_split = (int)((nvec + S - 1) / S);
+    need_split = (size_t)tokens * (size_t)S * 8u;
+  }
+  const int64_t mean_blocks =
+      (a.path == lce::XentPath::BlockRows) ? tokens : (tokens + lce::kRowThreads / 64 - 1) / (lce::kRowThreads / 64);
+  need_partials = (size_t)mean_blocks * 4u;
+
+  Carve cv;
+  const size_t off_mean = cv.take(need_partials);
+  const size_t off_split = cv.take(need_split);
+  char* base = nullptr;
+  if ((s = get_scratch(stream, cv.off, &base)) != LCE_OK) return s;
+  a.ticket = (unsigned*)base;
+  a.mean_partials = (float*)(base + off_mean);
+  a.split_partials = (float*)(base + off_split);
+
+  hipError_t e = lce::launch_xent(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return LCE_OK;
+}
+
+lce_status lce_fused_linear_xent_fwd(const void* x, const void* weight, int64_t tokens,
+                                     int64_t hidden, int64_t vocab, const int64_t* target,
+                                     lce_reduction reduction, float* out, hipStream_t stream) {
+  g_last_error.clear();
+  lce_status s = validate_fused(x, weight, tokens, hidden, vocab, target, (int)reduction, out);
+  if (s != LCE_OK) return s;
+  const bool mean = reduction == LCE_REDUCTION_MEAN;
+  if (tokens == 0) {
+    if (!mean) return LCE_OK;
+    hipError_t e = lce::launch_fill_f32(out, 1, __builtin_nanf(""), stream);
+    return e == hipSuccess ? LCE_OK : hip_fail(e, "launch");
+  }
+  int cus = 0;
+  if ((s = num_cus(&cus)) != LCE_OK) return s;
+
+  lce::FusedArgs a{};
+  a.x = x;
+  a.w = weight;
+  a.tokens = tokens;
+  a.hidden = hidden;
+  a.vocab = vocab;
+  a.target = target;
+  a.out = out;
+  a.reduce_mean = mean ? 1 : 0;
+  a.segments = lce::fused_segments(tokens, vocab, cus);
+  const int forced = env_int("LCE_FUSED_SEGMENTS", 0);
+  if (forced > 0) {
+    const lce::FusedGeometry g = lce::fused_geometry();
+    const int64_t n_voc = (vocab + g.block_vocab - 1) / g.block_vocab;
+    a.segments = (int)(forced < n_voc ? forced : n_voc);
+  }
+
+  Carve cv;
+  const size_t off_seg = cv.take((size_t)a.segments * (size_t)tokens * 8u);
+  const size_t off_zt = cv.take((size_t)tokens * 4u);
+  const size_t off_mean = cv.take((size_t)((tokens + lce::kRowThreads / 64 - 1) / (lce::kRowThreads / 64)) * 4u);
+  char* base = nullptr;
+  if ((s = get_scratch(stream, cv.off, &base)) != LCE_OK) return s;
+  a.ticket = (unsigned*)base;
+  a.seg_partials = (float*)(base + off_seg);
+  a.target_logit = (float*)(base + off_zt);
+  a.mean_partials = (float*)(base + off_mean);
+
+  hipError_t e = lce::launch_fused(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return LCE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// Internal interface between liblce's host dispatch (lce_api.cpp) and its
+// kernel launchers (xent_kernels.hip, fused_kernel.hip).  Not installed.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace lce {
+
+constexpr int kRowThreads = 256;  // threads per workgroup of the row kernels
+
+enum class XentPath : int { WaveRows = 0, BlockRows = 1, Split = 2 };
+
+struct XentArgs {
+  const void* logits;
+  bool bf16;
+  int64_t tokens;
+  int64_t vocab;
+  const int64_t* target;
+  float* out;
+  int reduce_mean;
+  XentPath path;
+  int unroll;               // chunks per lane per batch (wave_rows: 4, 8 or 16)
+  int splits;               // Split: workgroups per row
+  int chunks_per_split;     // Split: 16-byte chunks per workgroup
+  float* split_partials;    // Split: tokens * splits (max, sum-exp) pairs
+  float* mean_partials;     // one fp32 per workgroup of the last kernel
+  unsigned* ticket;         // zero before the launch; left zero after it
+};
+
+hipError_t launch_xent(const XentArgs& a, hipStream_t stream);
+
+// Fused projection + cross-entropy.
+struct FusedArgs {
+  const void* x;          // bf16 [tokens, hidden]
+  const void* w;          // bf16 [vocab, hidden]
+  int64_t tokens;
+  int64_t hidden;
+  int64_t vocab;
+  const int64_t* target;
+  float* out;
+  int reduce_mean;
+  int segments;           // vocab segments (workgroups per token block)
+  float* seg_partials;    // segments * tokens (max, sum-exp) pairs
+  float* target_logit;    // tokens fp32
+  float* mean_partials;
+  unsigned* ticket;
+};
+
+// Geometry of the fused kernel, needed by the host to size scratch.
+struct FusedGeometry {
+  int block_tokens;   // tokens per workgroup tile
+  int block_vocab;    // vocab rows per workgroup tile
+};
+FusedGeometry fused_geometry();
+int fused_segments(int64_t tokens, int64_t vocab, int num_cus);
+hipError_t launch_fused(const FusedArgs& a, hipStream_t stream);
+
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t stream);
+hipError_t launch_zero_u32(unsigned* p, int64_t n, hipStream_t stream);
+
+}  // namespace lce
