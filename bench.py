@@ -133,7 +133,7 @@ def replicas_for(w) -> int:
 
 # ------------------------------------------------------------------ timing
 
-def time_workload(w, steps: int, warmup: int, torch, lce):
+def time_workload(w, steps: int, warmup: int, torch, lce, eager_only: bool = False):
     reps = make_inputs(w, torch, replicas_for(w))
     R = len(reps)
     outs = [torch.empty((1,) if w.reduction == "mean" else w.target_shape, dtype=torch.float32,
@@ -148,7 +148,7 @@ def time_workload(w, steps: int, warmup: int, torch, lce):
             x, W, t = reps[r]
             lce.fused_linear_xent(x, W, t, w.reduction, out=outs[r])
 
-    for i in range(max(1, warmup)):
+    for i in range(max(warmup, R)):  # every replica's output is written at least once
         step(i)
     torch.cuda.synchronize()
     eager_ref = [o.clone() for o in outs]
@@ -163,6 +163,18 @@ def time_workload(w, steps: int, warmup: int, torch, lce):
     e1.record()
     torch.cuda.synchronize()
     eager_us = e0.elapsed_time(e1) * 1000.0 / n_eager
+    if eager_only:
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(steps):
+            step(i)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1000.0 / steps
+        del reps, outs
+        torch.cuda.empty_cache()
+        return {"us_per_step": us, "eager_us_per_call": eager_us, "replicas": R,
+                "graph_matches_eager": None, "wall_s": None}
 
     # capture exactly `steps` steps into one graph; replay once untimed, once timed
     g = torch.cuda.CUDAGraph()
@@ -247,6 +259,74 @@ def cpu_baseline(w, budget_s: float = 10.0) -> dict:
             "sample": sample}
 
 
+# ------------------------------------------------------------------ HBM counter calibration
+
+COPY_BYTES = 1 << 30
+
+
+def copy_calibration(torch, reps: int = 5) -> None:
+    """A plain device copy of COPY_BYTES (torch's copy kernel): under rocprofv3 --pmc its
+    FETCH_SIZE / WRITE_SIZE per dispatch should read COPY_BYTES; the ratio scales the
+    counters of our kernels to bytes."""
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def _pmc_rows(d: str):
+    import csv
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    for f in files:
+        with open(f) as fh:
+            yield from csv.DictReader(fh)
+
+
+def _per_dispatch(d: str, counter: str):
+    """{kernel name: [counter value per dispatch]} for one rocprofv3 --pmc run."""
+    vals = {}
+    per = {}
+    for r in _pmc_rows(d):
+        if r.get("Counter_Name") != counter:
+            continue
+        key = (r.get("Dispatch_Id") or r.get("Correlation_Id"), r["Kernel_Name"])
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    for (_, name), v in per.items():
+        vals.setdefault(name, []).append(v)
+    return vals
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, kernel_substr: str,
+                  commands: dict) -> dict:
+    """Traffic per launch of the kernel whose name contains `kernel_substr`, from a
+    FETCH_SIZE run and a WRITE_SIZE run (KiB per dispatch), each scaled by the same
+    counter's reading for the COPY_BYTES copy kernel in the same run."""
+    out = {"workload": workload, "kernel_match": kernel_substr, "commands": commands,
+           "copy_bytes": COPY_BYTES, "source_sha256": source_digest()}
+    total = 0.0
+    for label, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        vals = _per_dispatch(d, counter)
+        # the calibration copies are the largest copy dispatches of the run
+        copy = sorted((v for k, vs in vals.items() if "copy" in k.lower() for v in vs),
+                      reverse=True)[:5]
+        mine = [v for k, vs in vals.items() if kernel_substr in k for v in vs]
+        if not copy or not mine:
+            raise SystemExit(f"{counter}: kernels seen: {sorted(vals)}")
+        copy_kib = statistics.median(copy)
+        mine_kib = statistics.median(mine)
+        scale = (COPY_BYTES / 1024.0) / copy_kib
+        bytes_ = mine_kib * 1024.0 * scale
+        out[label] = {"counter": counter, "kernel_kib_per_dispatch_median": round(mine_kib, 1),
+                      "dispatches": len(mine), "copy_kib_per_dispatch_median": round(copy_kib, 1),
+                      "scale": round(scale, 5), "bytes_per_launch": round(bytes_)}
+        total += bytes_
+    out["traffic_bytes_per_launch"] = round(total)
+    return out
+
+
 # ------------------------------------------------------------------ main
 
 def main(argv=None) -> int:
@@ -257,7 +337,29 @@ def main(argv=None) -> int:
     ap.add_argument("--workloads", default="all",
                     help="'all', 'headline', or a comma list of workload names")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--eager", action="store_true",
+                    help="time plain launches instead of a graph replay (for profiler runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc runs")
+    ap.add_argument("--kernel", default="xent_wave_rows_kernel",
+                    help="kernel name substring for --summarize-pmc")
+    ap.add_argument("--pmc-command", action="append", default=[],
+                    help="command lines of the --pmc runs, recorded in the summary")
     args = ap.parse_args(argv)
+
+    if args.summarize_pmc:
+        import lce_synth
+        wl = lce_synth.HEADLINE if args.workloads in ("all", "headline") else args.workloads
+        d = summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], wl, args.kernel,
+                          {"runs": args.pmc_command})
+        os.makedirs(PROFILES, exist_ok=True)
+        path = os.path.join(PROFILES, f"traffic_{wl}.json")
+        with open(path, "w") as fh:
+            json.dump(d, fh, indent=1)
+        print(json.dumps(d))
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -283,7 +385,7 @@ def main(argv=None) -> int:
         big = w.kind == "fused" or w.tokens * w.vocab >= (1 << 30)
         k = args.steps if not big else max(5, min(args.steps, 30))
         print(f"[bench] {name}: {k} steps", file=sys.stderr, flush=True)
-        r = time_workload(w, k, args.warmup, torch, lce)
+        r = time_workload(w, k, args.warmup, torch, lce, eager_only=args.eager)
         r["steps"] = k
         r["roofline"] = roofline_entry(w, r["us_per_step"])
         if not args.no_cpu and name != lce_synth.HEADLINE:
@@ -291,6 +393,9 @@ def main(argv=None) -> int:
         results[name] = r
         print(f"[bench] {name}: {r['us_per_step']:.2f} µs/step "
               f"({r['roofline']['achieved']} {r['roofline']['unit']})", file=sys.stderr, flush=True)
+
+    if args.copy_calibration:
+        copy_calibration(torch)
 
     h = results[lce_synth.HEADLINE]
     line = {
@@ -308,7 +413,8 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": head.name, "seq": head.shape[0], "batch": head.shape[1],
                    "vocab": head.shape[2], "tokens": head.tokens, "logits_dtype": head.dtype,
-                   "reduction": head.reduction, "timing": "hip graph of K steps, replayed once",
+                   "reduction": head.reduction,
+                   "timing": ("eager launches" if args.eager else "hip graph of K steps, replayed once"),
                    "eager_us_per_call": round(h["eager_us_per_call"], 3),
                    "replicas": h["replicas"], "graph_matches_eager": h["graph_matches_eager"]},
         "roofline": {k: v for k, v in h["roofline"].items() if k in

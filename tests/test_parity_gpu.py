@@ -338,3 +338,33 @@ def test_fused_repeated_calls_bitwise_identical():
     for _ in range(3):
         assert torch.equal(lce.fused_linear_xent(x, W, t, "none"), first)
         assert torch.equal(lce.fused_linear_xent(x, W, t, "mean"), m0)
+
+
+@pytest.mark.parametrize("path", ["wave", "block", "split"])
+def test_mean_handoff_many_workgroups(path):
+    """The last-workgroup mean sees every workgroup's partial: 30 back-to-back calls
+    (thousands of workgroups each) agree bitwise, and the mean matches the average of
+    the per-token losses."""
+    rows, vocab = (16384, 2048) if path != "split" else (512, 40000)
+    z = torch.randn((rows, vocab), device="cuda", generator=torch.Generator("cuda").manual_seed(7))
+    t = torch.randint(0, vocab, (rows,), device="cuda", generator=torch.Generator("cuda").manual_seed(8))
+    with forced_env(LCE_PATH=path):
+        per = lce.xent(z, t, "none").double()
+        means = [lce.xent(z, t, "mean").clone() for _ in range(30)]
+    torch.cuda.synchronize()
+    for m in means[1:]:
+        assert torch.equal(m, means[0])
+    ref = per.mean().item()
+    assert abs(means[0].item() - ref) <= 1e-6 * abs(ref)
+
+
+@pytest.mark.parametrize("unroll,waves", [(4, 4), (8, 4), (16, 4), (4, 16), (8, 16)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rows,vocab", [(37, 1000), (70, 4099), (9, 30001)])
+def test_wave_kernel_shapes(unroll, waves, dtype, rows, vocab):
+    """Every instantiated one-wave-per-row kernel shape (chunks per lane per batch,
+    waves per workgroup) on ragged row counts and unaligned rows."""
+    z = rand_logits(rows * 3 + vocab, rows, vocab, dtype, std=2.0)
+    t = lce_synth.targets(rows + 1, rows, vocab)
+    with forced_env(LCE_PATH="wave", LCE_UNROLL=unroll, LCE_WAVES_PER_BLOCK=waves):
+        check_xent(z, t, dtype, f"wave U{unroll} W{waves} {dtype} {rows}x{vocab}")

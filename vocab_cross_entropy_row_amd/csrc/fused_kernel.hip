@@ -36,57 +36,87 @@ namespace lce {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // Tile shape: WV x WT waves; each wave owns BVB x BTB blocks of 32 x 32.
 template <int WV, int WT, int BVB, int BTB>
 struct Tile {
   static constexpr int kWaves = WV * WT;
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kBV = WV * BVB * 32;  // vocab rows per tile
-  static constexpr int kBT = WT * BTB * 32;  // tokens per tile
-  static constexpr int kBK = 64;             // hidden elements per slab
-  static constexpr int kRowsLds = kBV + kBT; // W rows then x rows
-  static constexpr int kChunks = kRowsLds * 8;        // 16-byte chunks per slab
-  static constexpr int kChunksW = kBV * 8;
-  static constexpr int kPerThread = kChunks / kThreads;
-  static constexpr int kPerThreadW = kChunksW / kThreads;
-  static_assert(kChunks % kThreads == 0 && kChunksW % kThreads == 0, "slab split");
+  static constexpr int kBV = WV * BVB * 32;   // vocab rows per tile
+  static constexpr int kBT = WT * BTB * 32;   // tokens per tile
+  static constexpr int kBK = 64;              // hidden elements per slab (128 B per row)
+  static constexpr int kRowsLds = kBV + kBT;  // W rows, then x rows
+  static constexpr int kGroups = kRowsLds / 8;          // 1 KiB (8-row) LDS groups per slab
+  static constexpr int kGroupsW = kBV / 8;
+  static constexpr int kGroupsPerWave = kGroups / kWaves;
+  static_assert(kGroups % kWaves == 0, "slab groups per wave");
+  static_assert(kGroupsW % kWaves == 0, "W groups per wave");
 };
 
-typedef Tile<2, 4, 4, 2> FusedTile;  // 256 vocab x 256 tokens, 8 waves
+typedef Tile<2, 2, 4, 4> FusedTile;  // 256 vocab x 256 tokens, 4 waves of 128 x 128
 
 // Physical 16-byte chunk of logical chunk `c` in LDS row `r`: conflict-free
 // ds_read_b128 for 8 or 16 consecutive rows read at the same logical chunk.
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r & 7) ^ ((r >> 3) & 1)); }
 
-template <class TL>
-__device__ __forceinline__ void load_slab(u32x4_t (&reg)[TL::kPerThread], const uint16_t* __restrict__ x,
-                                          const uint16_t* __restrict__ w, int64_t tokens,
-                                          int64_t hidden, int64_t vocab, int64_t v0, int64_t t0,
-                                          int64_t k0) {
-#pragma unroll
-  for (int i = 0; i < TL::kPerThread; ++i) {
-    const int c = threadIdx.x + i * TL::kThreads;
-    const bool is_w = i < TL::kPerThreadW;
-    const int r = is_w ? (c >> 3) : ((c - TL::kChunksW) >> 3);
-    const int kc = c & 7;
-    const int64_t k = k0 + kc * 8;
-    const int64_t g = is_w ? (v0 + r) : (t0 + r);
-    const bool ok = (g < (is_w ? vocab : tokens)) && (k < hidden);
-    const uint16_t* src = (is_w ? w : x) + g * hidden + k;
-    reg[i] = ok ? *reinterpret_cast<const u32x4_t*>(src) : (u32x4_t)(0u);
-  }
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Buffer resource over `bytes` bytes at `base` (raw, unswizzled; loads past the
+// end return zero).  gfx9 word 3: 32-bit data format, no swizzle.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-template <class TL>
-__device__ __forceinline__ void store_slab(uint16_t* lds, const u32x4_t (&reg)[TL::kPerThread]) {
+// Fold one token column of a finished tile into that token's running state and
+// capture its target logit.  acc[a][v] is the logit of vocab row
+// vbase + a*32 + 8*(v/4) + 4*half + v%4.  RAGGED masks rows >= vocab.
+template <int BVB, bool RAGGED>
+__device__ __forceinline__ void fold_tile_column(Lse& st, const f32x16 (&acc)[BVB], int64_t vbase,
+                                                 int64_t vocab, int half, int tgt, float* zt_dst) {
+  float bm = kNegInf;
 #pragma unroll
-  for (int i = 0; i < TL::kPerThread; ++i) {
-    const int c = threadIdx.x + i * TL::kThreads;
-    const int row = c >> 3;  // W rows first, then x rows, in one array
-    const int kc = c & 7;
-    *reinterpret_cast<u32x4_t*>(lds + row * 64 + swz(row, kc) * 8) = reg[i];
+  for (int a = 0; a < BVB; ++a)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const bool ok = !RAGGED || (vbase + a * 32 + 8 * (v >> 2) + 4 * half + (v & 3) < vocab);
+      bm = fmaxf(bm, ok ? acc[a][v] : kNegInf);
+    }
+  const float mn = fmaxf(st.m, bm);
+  if (mn != kNegInf) {
+    const float Mn = mn * kLog2e;
+    float tsum = 0.0f;
+#pragma unroll
+    for (int a = 0; a < BVB; ++a) {
+      float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+      for (int v = 0; v < 16; v += 2) {
+        const bool ok0 = !RAGGED || (vbase + a * 32 + 8 * (v >> 2) + 4 * half + (v & 3) < vocab);
+        const bool ok1 = !RAGGED || (vbase + a * 32 + 8 * (v >> 2) + 4 * half + ((v + 1) & 3) < vocab);
+        const float e0 = exp2_fast(__builtin_fmaf(acc[a][v], kLog2e, -Mn));
+        const float e1 = exp2_fast(__builtin_fmaf(acc[a][v + 1], kLog2e, -Mn));
+        s0 += ok0 ? e0 : 0.0f;
+        s1 += ok1 ? e1 : 0.0f;
+      }
+      tsum += s0 + s1;
+    }
+    st.s = st.s * lse_rescale(st.m, mn) + tsum;
+    st.m = mn;
+  }
+  // Target logit: only the one lane holding (token, target) writes it.
+  const int64_t rel = (int64_t)tgt - vbase;
+  if (tgt >= 0 && rel >= 0 && rel < BVB * 32) {
+    const int r = (int)rel & 31;
+    if (((r >> 2) & 1) == half) {
+      const int ai = (int)rel >> 5;
+      const int vi = ((r >> 3) << 2) | (r & 3);
+      float z = 0.0f;
+#pragma unroll
+      for (int a = 0; a < BVB; ++a)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (a == ai && v == vi) z = acc[a][v];
+      *zt_dst = z;
+    }
   }
 }
 
@@ -96,7 +126,7 @@ __global__ __launch_bounds__(64 * WV * WT) void fused_xent_partial_kernel(
     int64_t vocab, const int64_t* __restrict__ target, int segments, float2* __restrict__ part,
     float* __restrict__ zt_out) {
   typedef Tile<WV, WT, BVB, BTB> TL;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][TL::kRowsLds * 64];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2][TL::kRowsLds * 64];
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_uniform(threadIdx.x >> 6);
@@ -122,9 +152,29 @@ __global__ __launch_bounds__(64 * WV * WT) void fused_xent_partial_kernel(
 #pragma unroll
   for (int j = 0; j < BTB; ++j) {
     tok[j] = t0 + wt * (BTB * 32) + j * 32 + (lane & 31);
-    int64_t t = (tok[j] < tokens) ? target[tok[j]] : -1;
+    const int64_t t = (tok[j] < tokens) ? target[tok[j]] : -1;
     tgt[j] = (t >= 0 && t < vocab) ? (int)t : -1;
   }
+
+  // Global -> LDS plan.  A slab is kRowsLds rows of 64 bf16 (128 B); one wave
+  // instruction (64 lanes x 16 B) fills LDS group g = rows [8g, 8g + 8).  Wave
+  // `wave` issues groups g = wave + kWaves * i.  Lane l lands on physical chunk
+  // l & 7 of row 8g + (l >> 3), so it loads the logical chunk that the swizzle
+  // maps there.  Offsets are relative to the tile's W or x block; the slab's
+  // hidden offset is the uniform soffset.
+  const uint32_t row_bytes = (uint32_t)hidden * 2u;
+  uint32_t voff[TL::kGroupsPerWave];
+  uint32_t kchunk[TL::kGroupsPerWave];
+#pragma unroll
+  for (int i = 0; i < TL::kGroupsPerWave; ++i) {
+    const int g = wave + TL::kWaves * i;
+    const int r = 8 * g + (lane >> 3);
+    const int c = swz(r, lane & 7);  // swz is an involution in its chunk argument
+    const int rr = (i < TL::kGroupsW / TL::kWaves) ? r : r - TL::kBV;
+    voff[i] = (uint32_t)rr * row_bytes + (uint32_t)c * 16u;
+    kchunk[i] = (uint32_t)c * 8u;
+  }
+  const bool k_ragged = (hidden % TL::kBK) != 0;
 
   Lse st[BTB];
 #pragma unroll
@@ -132,112 +182,99 @@ __global__ __launch_bounds__(64 * WV * WT) void fused_xent_partial_kernel(
 
   const int nk = (int)((hidden + TL::kBK - 1) / TL::kBK);
   const int n_iter = (tile1 - tile0) * nk;
+  const uint32_t x_rows = (uint32_t)((tokens - t0) < TL::kBT ? (tokens - t0) : TL::kBT);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + t0 * hidden, x_rows * row_bytes);
 
-  // Slab pipeline over the flattened (tile, k) sequence: slab it+1 is loaded
-  // from global memory while slab it is multiplied out of LDS.
-  u32x4_t reg[TL::kPerThread];
-  if (n_iter > 0) {
-    load_slab<TL>(reg, x, w, tokens, hidden, vocab, (int64_t)tile0 * TL::kBV, t0, 0);
-    store_slab<TL>(lds[0], reg);
-  }
+  auto issue_slab = [&](int tile, int kk, int buf) {
+    const int64_t v0 = (int64_t)tile * TL::kBV;
+    const uint32_t w_rows = (uint32_t)((vocab - v0) < TL::kBV ? (vocab - v0) : TL::kBV);
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(w + v0 * hidden, w_rows * row_bytes);
+    const uint32_t k0 = (uint32_t)kk * TL::kBK;
+    const uint32_t soff = k0 * 2u;
+#pragma unroll
+    for (int i = 0; i < TL::kGroupsPerWave; ++i) {
+      const int g = wave + TL::kWaves * i;
+      uint32_t vo = voff[i];
+      if (k_ragged && k0 + kchunk[i] >= (uint32_t)hidden) vo = 0x7ffffff0u;  // past the end: zeros
+      lds_ptr_t dst = (lds_ptr_t)(&lds[buf][g * 8 * 64]);
+      if (i < TL::kGroupsW / TL::kWaves)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, vo, soff, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, dst, 16, vo, soff, 0, 0);
+    }
+  };
+
+  if (n_iter > 0) issue_slab(tile0, 0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's slab is in LDS
   __syncthreads();
+
+  // LDS read addresses (bf16 elements) of this lane's fragments at k-step 0;
+  // k-step ks adds the swizzled chunk offset, computed per lane below.
+  int a_row[BVB], b_row[BTB];
+#pragma unroll
+  for (int a = 0; a < BVB; ++a) a_row[a] = wv * (BVB * 32) + a * 32 + (lane & 31);
+#pragma unroll
+  for (int b = 0; b < BTB; ++b) b_row[b] = TL::kBV + wt * (BTB * 32) + b * 32 + (lane & 31);
 
   int it = 0;
   for (int tile = tile0; tile < tile1; ++tile) {
-    f32x16 acc[BVB][BTB];
+    f32x16 acc[BTB][BVB];
 #pragma unroll
-    for (int a = 0; a < BVB; ++a)
+    for (int b = 0; b < BTB; ++b)
 #pragma unroll
-      for (int b = 0; b < BTB; ++b) acc[a][b] = (f32x16)(0.0f);
+      for (int a = 0; a < BVB; ++a) acc[b][a] = (f32x16)(0.0f);
 
     for (int kk = 0; kk < nk; ++kk, ++it) {
       const int cur = it & 1;
-      const bool more = (it + 1) < n_iter;
-      if (more) {
+      if (it + 1 < n_iter) {
         const bool next_tile = (kk + 1 == nk);
-        load_slab<TL>(reg, x, w, tokens, hidden, vocab,
-                      (int64_t)(next_tile ? tile + 1 : tile) * TL::kBV, t0,
-                      (int64_t)(next_tile ? 0 : kk + 1) * TL::kBK);
+        issue_slab(next_tile ? tile + 1 : tile, next_tile ? 0 : kk + 1, cur ^ 1);
       }
-      const uint16_t* Ws = lds[cur];
-      const uint16_t* Xs = lds[cur] + TL::kBV * 64;
+      const uint16_t* S = lds[cur];
+      // Fragments of k-step ks+1 are read while k-step ks is multiplied.
+      bf16x8 af[2][BVB], bfr[2][BTB];
+#pragma unroll
+      for (int a = 0; a < BVB; ++a)
+        af[0][a] = *reinterpret_cast<const bf16x8*>(S + a_row[a] * 64 + swz(a_row[a], half) * 8);
+#pragma unroll
+      for (int b = 0; b < BTB; ++b)
+        bfr[0][b] = *reinterpret_cast<const bf16x8*>(S + b_row[b] * 64 + swz(b_row[b], half) * 8);
 #pragma unroll
       for (int ks = 0; ks < TL::kBK / 16; ++ks) {
-        const int c = 2 * ks + half;
-        bf16x8 af[BVB], bfr[BTB];
+        const int p = ks & 1;
+        if (ks + 1 < TL::kBK / 16) {
+          const int c = 2 * (ks + 1) + half;
 #pragma unroll
-        for (int a = 0; a < BVB; ++a) {
-          const int r = wv * (BVB * 32) + a * 32 + (lane & 31);
-          af[a] = *reinterpret_cast<const bf16x8*>(Ws + r * 64 + swz(r, c) * 8);
-        }
-#pragma unroll
-        for (int b = 0; b < BTB; ++b) {
-          const int r = wt * (BTB * 32) + b * 32 + (lane & 31);
-          bfr[b] = *reinterpret_cast<const bf16x8*>(Xs + r * 64 + swz(TL::kBV + r, c) * 8);
-        }
-#pragma unroll
-        for (int a = 0; a < BVB; ++a)
+          for (int a = 0; a < BVB; ++a)
+            af[p ^ 1][a] = *reinterpret_cast<const bf16x8*>(S + a_row[a] * 64 + swz(a_row[a], c) * 8);
 #pragma unroll
           for (int b = 0; b < BTB; ++b)
-            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
+            bfr[p ^ 1][b] = *reinterpret_cast<const bf16x8*>(S + b_row[b] * 64 + swz(b_row[b], c) * 8);
+        }
+        // Keep the reads above ahead of this k-step's MFMAs (the scheduler would
+        // otherwise sink each read next to its first use and expose LDS latency).
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int b = 0; b < BTB; ++b)
+#pragma unroll
+          for (int a = 0; a < BVB; ++a)
+            acc[b][a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[p][a], bfr[p][b], acc[b][a], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (more) store_slab<TL>(lds[cur ^ 1], reg);
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next slab landed in LDS
       __syncthreads();
     }
 
-    // Epilogue of the finished tile.  acc[a][b][v] is the logit of token
-    // tok[b] and vocab row vbase + a*32 + 8*(v/4) + 4*half + v%4.
+    // Epilogue of the finished tile, one token column at a time.
     const int64_t vbase = (int64_t)tile * TL::kBV + wv * (BVB * 32);
-    const bool ragged = vbase + BVB * 32 > vocab;
+    if (vbase + BVB * 32 > vocab) {
 #pragma unroll
-    for (int b = 0; b < BTB; ++b) {
-      if (ragged) {
+      for (int b = 0; b < BTB; ++b)
+        fold_tile_column<BVB, true>(st[b], acc[b], vbase, vocab, half, tgt[b], zt_out + tok[b]);
+    } else {
 #pragma unroll
-        for (int a = 0; a < BVB; ++a)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int64_t vi = vbase + a * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-            if (vi >= vocab) acc[a][b][v] = kNegInf;
-          }
-      }
-      float bm = kNegInf;
-#pragma unroll
-      for (int a = 0; a < BVB; ++a)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) bm = fmaxf(bm, acc[a][b][v]);
-      const float mn = fmaxf(st[b].m, bm);
-      const float Mn = mn * kLog2e;
-      float tsum = 0.0f;
-#pragma unroll
-      for (int a = 0; a < BVB; ++a) {
-        float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll
-        for (int v = 0; v < 16; v += 2) {
-          s0 += exp2_fast(__builtin_fmaf(acc[a][b][v], kLog2e, -Mn));
-          s1 += exp2_fast(__builtin_fmaf(acc[a][b][v + 1], kLog2e, -Mn));
-        }
-        tsum += s0 + s1;
-      }
-      if (mn != kNegInf) {
-        st[b].s = st[b].s * lse_rescale(st[b].m, mn) + tsum;
-        st[b].m = mn;
-      }
-      // Target logit: only the one lane holding (tok, target) writes it.
-      const int64_t rel = (int64_t)tgt[b] - vbase;
-      if (tgt[b] >= 0 && rel >= 0 && rel < BVB * 32) {
-        const int r = (int)rel & 31;
-        if (((r >> 2) & 1) == half) {
-          const int ai = (int)rel >> 5;
-          const int vi = ((r >> 3) << 2) | (r & 3);
-          float z = 0.0f;
-#pragma unroll
-          for (int a = 0; a < BVB; ++a)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-              if (a == ai && v == vi) z = acc[a][b][v];
-          zt_out[tok[b]] = z;
-        }
-      }
+      for (int b = 0; b < BTB; ++b)
+        fold_tile_column<BVB, false>(st[b], acc[b], vbase, vocab, half, tgt[b], zt_out + tok[b]);
     }
   }
 
@@ -271,35 +308,34 @@ __global__ __launch_bounds__(64 * WV * WT) void fused_xent_partial_kernel(
   }
 }
 
-// One wave per token: merge its `segments` partials, subtract z_target.
+// One thread per token: merge its `segments` partials in segment order
+// (consecutive threads read consecutive tokens of a segment), subtract z_target.
 __global__ __launch_bounds__(kRowThreads) void fused_xent_merge_kernel(
     int64_t tokens, int64_t vocab, int segments, const float2* __restrict__ part,
     const float* __restrict__ zt, const int64_t* __restrict__ target, float* __restrict__ out,
     float* __restrict__ partials, unsigned* __restrict__ ticket, int reduce_mean) {
-  constexpr int kWaves = kRowThreads / 64;
-  const int lane = threadIdx.x & 63;
-  const int wave = wave_uniform(threadIdx.x >> 6);
-  const int64_t row = (int64_t)blockIdx.x * kWaves + wave;
+  const int64_t row = (int64_t)blockIdx.x * kRowThreads + threadIdx.x;
   float loss = 0.0f;
   if (row < tokens) {
     Lse st = lse_empty();
-    for (int s = lane; s < segments; s += 64) {
+    for (int s = 0; s < segments; ++s) {
       const float2 p = part[(int64_t)s * tokens + row];
       st = lse_merge(st, Lse{p.x, p.y});
     }
-    const Lse r = wave_lse(st);
     const int64_t t = target[row];
-    loss = (t >= 0 && t < vocab) ? lse_minus(r, zt[row]) : __builtin_nanf("");
-    if (!reduce_mean && lane == 0) out[row] = loss;
+    loss = (t >= 0 && t < vocab) ? lse_minus(st, zt[row]) : __builtin_nanf("");
+    if (!reduce_mean) out[row] = loss;
   }
   if (reduce_mean) {
-    __shared__ float wl[kWaves];
-    if (lane == 0) wl[wave] = loss;
+    __shared__ float red[kRowThreads];
+    red[threadIdx.x] = loss;
     __syncthreads();
-    float bsum = 0.0f;
-    if (threadIdx.x == 0)
-      for (int i = 0; i < kWaves; ++i) bsum += wl[i];
-    finish_mean<kRowThreads>(bsum, partials, ticket, out, tokens);
+#pragma unroll
+    for (int w = kRowThreads / 2; w > 0; w >>= 1) {
+      if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+      __syncthreads();
+    }
+    finish_mean(red[0], partials, ticket, out, tokens);
   }
 }
 
@@ -317,13 +353,13 @@ int fused_segments(int64_t tokens, int64_t vocab, int num_cus) {
 hipError_t launch_fused(const FusedArgs& a, hipStream_t stream) {
   const int64_t n_tok = (a.tokens + FusedTile::kBT - 1) / FusedTile::kBT;
   const int64_t grid = n_tok * a.segments;
-  hipLaunchKernelGGL((fused_xent_partial_kernel<2, 4, 4, 2>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((fused_xent_partial_kernel<2, 2, 4, 4>), dim3((unsigned)grid),
                      dim3(FusedTile::kThreads), 0, stream, (const uint16_t*)a.x,
                      (const uint16_t*)a.w, a.tokens, a.hidden, a.vocab, a.target, a.segments,
                      (float2*)a.seg_partials, a.target_logit);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t blocks = (a.tokens + kRowThreads / 64 - 1) / (kRowThreads / 64);
+  const int64_t blocks = (a.tokens + kRowThreads - 1) / kRowThreads;
   hipLaunchKernelGGL(fused_xent_merge_kernel, dim3((unsigned)blocks), dim3(kRowThreads), 0, stream,
                      a.tokens, a.vocab, a.segments, (const float2*)a.seg_partials,
                      (const float*)a.target_logit, a.target, a.out, a.mean_partials, a.ticket,

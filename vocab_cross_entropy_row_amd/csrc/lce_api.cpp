@@ -12,7 +12,7 @@
 #include <string>
 #include <utility>
 
-#include "../../include/lce.h"
+#include "lce.h"
 #include "lce_internal.h"
 
 namespace {
@@ -44,7 +44,8 @@ bool aligned(const void* p, uint64_t n) { return ((uintptr_t)p % n) == 0; }
 
 // ------------------------------------------------------------ scratch pool
 // One grow-only device buffer per (device, stream); kept until process exit.
-// Layout: [0, 256) ticket, then 256-byte-aligned regions carved by Carve.
+// Layout: the mean's ticket counters first (kTicketBytes, zero between calls),
+// then 256-byte-aligned regions carved by Carve.
 struct Scratch {
   void* ptr = nullptr;
   size_t bytes = 0;
@@ -57,7 +58,7 @@ constexpr size_t kAlign = 256;
 size_t round_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
 
 struct Carve {
-  size_t off = kAlign;  // the ticket lives in the first 256 bytes
+  size_t off = round_up(lce::kTicketBytes, kAlign);  // the ticket counters come first
   size_t take(size_t n) {
     const size_t o = off;
     off = round_up(off + n, kAlign);
@@ -87,8 +88,8 @@ lce_status get_scratch(hipStream_t stream, size_t need, char** out) {
       (void)hipGetLastError();
       return fail(LCE_ERR_OOM, "hipMalloc of %zu bytes of scratch failed: %s", bytes, hipGetErrorName(e));
     }
-    // The ticket must start at zero; kernels leave it at zero afterwards.
-    e = lce::launch_zero_u32((unsigned*)p, kAlign / sizeof(unsigned), stream);
+    // The ticket counters must start at zero; kernels leave them at zero.
+    e = lce::launch_zero_u32((unsigned*)p, lce::kTicketBytes / sizeof(unsigned), stream);
     if (e != hipSuccess) {
       (void)hipFree(p);
       return hip_fail(e, "scratch initialisation");
@@ -231,21 +232,42 @@ lce_status lce_xent_fwd(const void* logits, lce_dtype dtype, int64_t tokens, int
   a.out = out;
   a.reduce_mean = mean ? 1 : 0;
 
-  // Path: short rows -> one wave per row; long rows -> one workgroup per row,
-  // or several workgroups per row when there are too few rows to fill the CUs.
+  // Path selection (measured on MI355X):
+  //  - rows up to 32 KiB: one wave per row; 4 waves per workgroup without a
+  //    mean, 16 with a mean (a quarter of the ticket hand-offs), then at most
+  //    8 chunks per lane per batch (register budget of 1024-thread groups);
+  //  - longer rows: without a mean, one workgroup per row; with a mean, one
+  //    wave per row in 16-wave workgroups; with few rows, several workgroups
+  //    per row (split).
   const int64_t esize = a.bf16 ? 2 : 4;
   const int64_t row_bytes = vocab * esize;
   const int64_t nvec = row_bytes / 16;
+  const int64_t per_lane = (nvec + 63) / 64;
+  a.unroll = per_lane <= 4 ? 4 : per_lane <= 8 ? 8 : 16;
+  a.waves_per_block = 4;
+  if (row_bytes <= 32 * 1024) {
+    a.path = lce::XentPath::WaveRows;
+    if (mean) a.waves_per_block = 16;
+  } else if (tokens >= 2 * (int64_t)cus) {
+    if (mean) {
+      a.path = lce::XentPath::WaveRows;
+      a.waves_per_block = 16;
+    } else {
+      a.path = lce::XentPath::BlockRows;
+    }
+  } else {
+    a.path = lce::XentPath::Split;
+  }
+  // Overrides for tuning and tests.
   const char* forced = getenv("LCE_PATH");
   if (forced && !strcmp(forced, "wave")) a.path = lce::XentPath::WaveRows;
   else if (forced && !strcmp(forced, "block")) a.path = lce::XentPath::BlockRows;
   else if (forced && !strcmp(forced, "split")) a.path = lce::XentPath::Split;
-  else if (row_bytes <= 32 * 1024) a.path = lce::XentPath::WaveRows;
-  else if (tokens >= 2 * (int64_t)cus) a.path = lce::XentPath::BlockRows;
-  else a.path = lce::XentPath::Split;
-
-  const int64_t per_lane = (nvec + 63) / 64;
-  a.unroll = per_lane <= 4 ? 4 : per_lane <= 8 ? 8 : 16;
+  const int forced_unroll = env_int("LCE_UNROLL", 0);
+  if (forced_unroll == 4 || forced_unroll == 8 || forced_unroll == 16) a.unroll = forced_unroll;
+  const int forced_waves = env_int("LCE_WAVES_PER_BLOCK", 0);
+  if (forced_waves == 4 || forced_waves == 16) a.waves_per_block = forced_waves;
+  if (a.waves_per_block == 16 && a.unroll > 8) a.unroll = 8;
 
   size_t need_partials = 0, need_split = 0;
   if (a.path == lce::XentPath::Split) {
@@ -263,7 +285,9 @@ lce_status lce_xent_fwd(const void* logits, lce_dtype dtype, int64_t tokens, int
     need_split = (size_t)tokens * (size_t)S * 8u;
   }
   const int64_t mean_blocks =
-      (a.path == lce::XentPath::BlockRows) ? tokens : (tokens + lce::kRowThreads / 64 - 1) / (lce::kRowThreads / 64);
+      (a.path == lce::XentPath::BlockRows) ? tokens
+      : (a.path == lce::XentPath::WaveRows) ? (tokens + a.waves_per_block - 1) / a.waves_per_block
+                                              : (tokens + lce::kRowThreads / 64 - 1) / (lce::kRowThreads / 64);
   need_partials = (size_t)mean_blocks * 4u;
 
   Carve cv;
@@ -315,7 +339,7 @@ lce_status lce_fused_linear_xent_fwd(const void* x, const void* weight, int64_t 
   Carve cv;
   const size_t off_seg = cv.take((size_t)a.segments * (size_t)tokens * 8u);
   const size_t off_zt = cv.take((size_t)tokens * 4u);
-  const size_t off_mean = cv.take((size_t)((tokens + lce::kRowThreads / 64 - 1) / (lce::kRowThreads / 64)) * 4u);
+  const size_t off_mean = cv.take((size_t)((tokens + lce::kRowThreads - 1) / lce::kRowThreads) * 4u);
   char* base = nullptr;
   if ((s = get_scratch(stream, cv.off, &base)) != LCE_OK) return s;
   a.ticket = (unsigned*)base;

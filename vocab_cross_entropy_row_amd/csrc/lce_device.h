@@ -125,38 +125,59 @@ __device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_rea
 
 // ------------------------------------------------------------ deterministic mean
 // Every workgroup leaves one fp32 partial; the workgroup that finishes last
-// (found with an integer ticket) adds all partials in a fixed order and writes
-// the mean.  It then resets the ticket to 0, so the next launch on the same
-// scratch starts clean.  Only integer atomics are used.
-template <int NT>
+// adds all partials in a fixed order and writes the mean.  No float atomics
+// are used, so the result is bitwise reproducible.
+//
+// Finding the last workgroup: a two-level integer ticket.  Workgroup b counts
+// itself in group counter b % G (G <= 64 counters, each on its own 256-byte
+// line so they do not serialise on one address); the workgroup that completes
+// a group counts the group in the top counter; the one that completes the top
+// counter is last.  Each completing workgroup resets the counter it completed,
+// so all counters are zero again when the kernel ends.
+//
+// Visibility across the XCDs (each has its own L2): the partials are written
+// and read only with agent-scope atomic stores and loads, which are coherent
+// at agent scope by themselves, and each writer waits for its store to
+// complete (s_waitcnt) before it touches a counter.  A release/acquire fence
+// pair would instead write back (and invalidate) a whole L2 per workgroup.
+//
+// Only wave 0 takes part: the other waves of the workgroup retire at once, so
+// the hand-off's memory round trips do not hold their slots.
+constexpr int kTicketGroups = 64;
+constexpr int kTicketStride = 64;  // unsigned ints (256 bytes) between counters
+
+// `block_sum` must be valid in thread 0; every thread of the workgroup calls
+// this after its last barrier.  Threads of waves other than 0 return at once.
 __device__ __forceinline__ void finish_mean(float block_sum, float* partials, unsigned* ticket,
                                             float* out, int64_t tokens) {
-  __shared__ float red[NT];
-  __shared__ int is_last;
-  const int tid = threadIdx.x;
+  if (threadIdx.x >= 64) return;
+  const unsigned lane = threadIdx.x;
   const unsigned nblocks = gridDim.x * gridDim.y;
   const unsigned bid = blockIdx.y * gridDim.x + blockIdx.x;
-  if (tid == 0) {
-    partials[bid] = block_sum;
-    __threadfence();
-    const unsigned prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    is_last = (prev == nblocks - 1);
+  const unsigned G = nblocks < (unsigned)kTicketGroups ? nblocks : (unsigned)kTicketGroups;
+  const unsigned g = bid % G;
+  const unsigned group_size = nblocks / G + (g < nblocks % G ? 1u : 0u);
+  unsigned* group_ctr = ticket + g * kTicketStride;
+  unsigned* top_ctr = ticket + kTicketGroups * kTicketStride;
+  int last = 0;
+  if (lane == 0) {
+    __hip_atomic_store(&partials[bid], block_sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);  // the partial store has completed
+    if (__hip_atomic_fetch_add(group_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+        group_size - 1) {
+      __hip_atomic_store(group_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(0);
+      last = __hip_atomic_fetch_add(top_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == G - 1;
+    }
   }
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
+  if (!wave_uniform(last)) return;
   float acc = 0.0f;
-  for (unsigned i = tid; i < nblocks; i += NT) acc += partials[i];
-  red[tid] = acc;
-  __syncthreads();
-#pragma unroll
-  for (int w = NT / 2; w > 0; w >>= 1) {
-    if (tid < w) red[tid] += red[tid + w];
-    __syncthreads();
-  }
-  if (tid == 0) {
-    out[0] = red[0] / (float)tokens;
-    __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (unsigned i = lane; i < nblocks; i += 64)
+    acc += __hip_atomic_load(&partials[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const float total = wave_sum(acc);
+  if (lane == 0) {
+    out[0] = total / (float)tokens;
+    __hip_atomic_store(top_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

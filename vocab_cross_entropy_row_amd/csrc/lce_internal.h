@@ -9,6 +9,10 @@ namespace lce {
 
 constexpr int kRowThreads = 256;  // threads per workgroup of the row kernels
 
+// Bytes of mean-ticket counters at the start of the scratch buffer
+// (65 counters, 256 bytes apart; see finish_mean in lce_device.h).
+constexpr size_t kTicketBytes = 65 * 256;
+
 enum class XentPath : int { WaveRows = 0, BlockRows = 1, Split = 2 };
 
 struct XentArgs {
@@ -21,6 +25,7 @@ struct XentArgs {
   int reduce_mean;
   XentPath path;
   int unroll;               // chunks per lane per batch (wave_rows: 4, 8 or 16)
+  int waves_per_block;      // WaveRows: rows (waves) per workgroup, 4 or 16 (then unroll <= 8)
   int splits;               // Split: workgroups per row
   int chunks_per_split;     // Split: 16-byte chunks per workgroup
   float* split_partials;    // Split: tokens * splits (max, sum-exp) pairs

@@ -28,6 +28,9 @@
 
 namespace lce {
 
+static_assert(kTicketBytes == (kTicketGroups + 1) * kTicketStride * sizeof(unsigned),
+              "host scratch layout must match the device ticket layout");
+
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -143,15 +146,16 @@ __device__ __forceinline__ float row_loss(const Lse& st, const T* row, int64_t t
 }
 
 // ------------------------------------------------------------ one wave per row
-template <typename T, int U>
-__global__ __launch_bounds__(kRowThreads) void xent_wave_rows_kernel(
+// WAVES rows (one per wave) per workgroup.  With a mean, larger workgroups
+// mean fewer partials and fewer ticket hand-offs.
+template <typename T, int U, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void xent_wave_rows_kernel(
     const T* __restrict__ logits, int64_t tokens, int vocab, const int64_t* __restrict__ target,
     float* __restrict__ out, float* __restrict__ partials, unsigned* __restrict__ ticket,
     int reduce_mean) {
-  constexpr int kWaves = kRowThreads / 64;
   const int lane = threadIdx.x & 63;
   const int wave = wave_uniform(threadIdx.x >> 6);
-  const int64_t row = (int64_t)blockIdx.x * kWaves + wave;
+  const int64_t row = (int64_t)blockIdx.x * WAVES + wave;
   float loss = 0.0f;
   if (row < tokens) {
     const T* rp = logits + row * (int64_t)vocab;
@@ -167,13 +171,13 @@ __global__ __launch_bounds__(kRowThreads) void xent_wave_rows_kernel(
     if (!reduce_mean && lane == 0) out[row] = loss;
   }
   if (reduce_mean) {
-    __shared__ float wl[kWaves];
+    __shared__ float wl[WAVES];
     if (lane == 0) wl[wave] = loss;
     __syncthreads();
     float bsum = 0.0f;
     if (threadIdx.x == 0)
-      for (int w = 0; w < kWaves; ++w) bsum += wl[w];
-    finish_mean<kRowThreads>(bsum, partials, ticket, out, tokens);
+      for (int w = 0; w < WAVES; ++w) bsum += wl[w];
+    finish_mean(bsum, partials, ticket, out, tokens);
   }
 }
 
@@ -217,7 +221,7 @@ __global__ __launch_bounds__(kRowThreads) void xent_block_rows_kernel(
   if (!reduce_mean) {
     if (threadIdx.x == 0) out[row] = loss;
   } else {
-    finish_mean<kRowThreads>(loss, partials, ticket, out, tokens);
+    finish_mean(loss, partials, ticket, out, tokens);
   }
 }
 
@@ -273,7 +277,7 @@ __global__ __launch_bounds__(kRowThreads) void xent_split_merge_kernel(
     float bsum = 0.0f;
     if (threadIdx.x == 0)
       for (int w = 0; w < kWaves; ++w) bsum += wl[w];
-    finish_mean<kRowThreads>(bsum, partials, ticket, out, tokens);
+    finish_mean(bsum, partials, ticket, out, tokens);
   }
 }
 
@@ -289,13 +293,21 @@ __global__ void zero_u32_kernel(unsigned* p, int64_t n) {
 }
 
 // ------------------------------------------------------------ launchers
-template <typename T, int U>
-static hipError_t launch_wave_rows(const XentArgs& a, hipStream_t st) {
-  const int64_t blocks = (a.tokens + kRowThreads / 64 - 1) / (kRowThreads / 64);
-  hipLaunchKernelGGL((xent_wave_rows_kernel<T, U>), dim3((unsigned)blocks), dim3(kRowThreads), 0,
-                     st, (const T*)a.logits, a.tokens, (int)a.vocab, a.target, a.out,
+template <typename T, int U, int WAVES>
+static hipError_t launch_wave_rows_w(const XentArgs& a, hipStream_t st) {
+  const int64_t blocks = (a.tokens + WAVES - 1) / WAVES;
+  hipLaunchKernelGGL((xent_wave_rows_kernel<T, U, WAVES>), dim3((unsigned)blocks), dim3(64 * WAVES),
+                     0, st, (const T*)a.logits, a.tokens, (int)a.vocab, a.target, a.out,
                      a.mean_partials, a.ticket, a.reduce_mean);
   return hipGetLastError();
+}
+
+// Instantiated shapes: U in {4, 8, 16} with 4 waves; U in {4, 8} with 16 waves
+// (16 waves with U = 16 would need more registers than 1024 threads can have).
+template <typename T, int U>
+static hipError_t launch_wave_rows(const XentArgs& a, hipStream_t st) {
+  if (a.waves_per_block == 16) return launch_wave_rows_w<T, (U > 8 ? 8 : U), 16>(a, st);
+  return launch_wave_rows_w<T, U, 4>(a, st);
 }
 
 template <typename T, int U>
