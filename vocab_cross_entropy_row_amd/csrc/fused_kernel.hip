@@ -37,26 +37,36 @@ namespace lce {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// Tile shape: WV x WT waves; each wave owns BVB x BTB blocks of 32 x 32.
-template <int WV, int WT, int BVB, int BTB>
+// Tile shape: WV x WT waves, each owning BVB x BTB blocks of 32 x 32; K-slabs
+// of 64 hidden elements (one 128-byte LDS row per W row and per token).  W
+// slabs rotate through WST stages, x slabs through XST stages.
+template <int WV, int WT, int BVB, int BTB, int WST, int XST>
 struct Tile {
   static constexpr int kWaves = WV * WT;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kBV = WV * BVB * 32;   // vocab rows per tile
   static constexpr int kBT = WT * BTB * 32;   // tokens per tile
-  static constexpr int kBK = 64;              // hidden elements per slab (128 B per row)
-  static constexpr int kRowsLds = kBV + kBT;  // W rows, then x rows
-  static constexpr int kGroups = kRowsLds / 8;          // 1 KiB (8-row) LDS groups per slab
-  static constexpr int kGroupsW = kBV / 8;
-  static constexpr int kGroupsPerWave = kGroups / kWaves;
-  static_assert(kGroups % kWaves == 0, "slab groups per wave");
-  static_assert(kGroupsW % kWaves == 0, "W groups per wave");
+  static constexpr int kBK = 64;              // hidden elements per slab
+  static constexpr int kKSteps = kBK / 16;    // MFMA k-steps per slab
+  static constexpr int kWStages = WST;
+  static constexpr int kXStages = XST;
+  static constexpr int kWStageElems = kBV * kBK;
+  static constexpr int kXStageElems = kBT * kBK;
+  static constexpr int kLdsElems = WST * kWStageElems + XST * kXStageElems;
+  static constexpr int kWPerWave = kBV / 8 / kWaves;  // 1 KiB W DMAs per wave per slab
+  static constexpr int kXPerWave = kBT / 8 / kWaves;  // 1 KiB x DMAs per wave per slab
+  static_assert((kBV / 8) % kWaves == 0 && (kBT / 8) % kWaves == 0, "slab groups per wave");
+  static_assert(kWPerWave <= 63, "vmcnt range");
 };
 
-typedef Tile<2, 2, 4, 4> FusedTile;  // 256 vocab x 256 tokens, 4 waves of 128 x 128
+// 256 vocab x 256 tokens (4 waves of 128 x 128); 3 W + 2 x stages of 32 KiB
+// fill the 160 KiB of LDS.
+typedef Tile<2, 4, 4, 2, 3, 2> FusedTile;
 
-// Physical 16-byte chunk of logical chunk `c` in LDS row `r`: conflict-free
-// ds_read_b128 for 8 or 16 consecutive rows read at the same logical chunk.
+
+// Physical 16-byte chunk of logical chunk `c` in LDS row `r` (rows of 128 B):
+// a ds_read_b128 of 8 or 16 consecutive rows at one logical chunk touches
+// every bank once.  The map is its own inverse.
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r & 7) ^ ((r >> 3) & 1)); }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -65,6 +75,13 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // end return zero).  gfx9 word 3: 32-bit data format, no swizzle.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// s_waitcnt vmcnt(N) with the other counters left free (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | (0xF << 8) | (0x7 << 4) | (N & 0xF));
 }
 
 // Fold one token column of a finished tile into that token's running state and
@@ -120,13 +137,13 @@ __device__ __forceinline__ void fold_tile_column(Lse& st, const f32x16 (&acc)[BV
   }
 }
 
-template <int WV, int WT, int BVB, int BTB>
-__global__ __launch_bounds__(64 * WV * WT) void fused_xent_partial_kernel(
+template <class TL, int BVB, int BTB, int WV>
+__global__ __launch_bounds__(TL::kThreads) void fused_xent_partial_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int64_t tokens, int64_t hidden,
     int64_t vocab, const int64_t* __restrict__ target, int segments, float2* __restrict__ part,
     float* __restrict__ zt_out) {
-  typedef Tile<WV, WT, BVB, BTB> TL;
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[2][TL::kRowsLds * 64];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[TL::kLdsElems];
+  constexpr int kXBase = TL::kWStages * TL::kWStageElems;  // x stages follow the W stages
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_uniform(threadIdx.x >> 6);
@@ -156,25 +173,29 @@ __global__ __launch_bounds__(64 * WV * WT) void fused_xent_partial_kernel(
     tgt[j] = (t >= 0 && t < vocab) ? (int)t : -1;
   }
 
-  // Global -> LDS plan.  A slab is kRowsLds rows of 64 bf16 (128 B); one wave
-  // instruction (64 lanes x 16 B) fills LDS group g = rows [8g, 8g + 8).  Wave
-  // `wave` issues groups g = wave + kWaves * i.  Lane l lands on physical chunk
-  // l & 7 of row 8g + (l >> 3), so it loads the logical chunk that the swizzle
-  // maps there.  Offsets are relative to the tile's W or x block; the slab's
-  // hidden offset is the uniform soffset.
+  // Global -> LDS plan.  One wave instruction (64 lanes x 16 B) fills 8 LDS
+  // rows; W DMA i of this wave fills W-stage rows 8g .. 8g+7, g = wave + kWaves*i,
+  // and likewise for x.  Lane l lands on physical chunk l & 7 of row
+  // 8g + (l >> 3), so it loads the logical chunk the swizzle maps there.
+  // Offsets are relative to the tile's W or x block; the slab's hidden offset
+  // is the uniform soffset.
   const uint32_t row_bytes = (uint32_t)hidden * 2u;
-  uint32_t voff[TL::kGroupsPerWave];
-  uint32_t kchunk[TL::kGroupsPerWave];
+  uint32_t voff_w[TL::kWPerWave], voff_x[TL::kXPerWave];
+  uint32_t kch_w[TL::kWPerWave], kch_x[TL::kXPerWave];
 #pragma unroll
-  for (int i = 0; i < TL::kGroupsPerWave; ++i) {
-    const int g = wave + TL::kWaves * i;
-    const int r = 8 * g + (lane >> 3);
-    const int c = swz(r, lane & 7);  // swz is an involution in its chunk argument
-    const int rr = (i < TL::kGroupsW / TL::kWaves) ? r : r - TL::kBV;
-    voff[i] = (uint32_t)rr * row_bytes + (uint32_t)c * 16u;
-    kchunk[i] = (uint32_t)c * 8u;
+  for (int i = 0; i < TL::kWPerWave; ++i) {
+    const int r = 8 * (wave + TL::kWaves * i) + (lane >> 3);
+    const int c = swz(r, lane & 7);
+    voff_w[i] = (uint32_t)r * row_bytes + (uint32_t)c * 16u;
+    kch_w[i] = (uint32_t)c * 8u;
   }
-  const bool k_ragged = (hidden % TL::kBK) != 0;
+#pragma unroll
+  for (int i = 0; i < TL::kXPerWave; ++i) {
+    const int r = 8 * (wave + TL::kWaves * i) + (lane >> 3);
+    const int c = swz(r, lane & 7);
+    voff_x[i] = (uint32_t)r * row_bytes + (uint32_t)c * 16u;
+    kch_x[i] = (uint32_t)c * 8u;
+  }
 
   Lse st[BTB];
 #pragma unroll
@@ -185,36 +206,115 @@ __global__ __launch_bounds__(64 * WV * WT) void fused_xent_partial_kernel(
   const uint32_t x_rows = (uint32_t)((tokens - t0) < TL::kBT ? (tokens - t0) : TL::kBT);
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + t0 * hidden, x_rows * row_bytes);
 
-  auto issue_slab = [&](int tile, int kk, int buf) {
+  // W block of vocab tile `tile` as a buffer resource (rows past vocab read 0).
+  auto w_rsrc = [&](int tile) {
     const int64_t v0 = (int64_t)tile * TL::kBV;
-    const uint32_t w_rows = (uint32_t)((vocab - v0) < TL::kBV ? (vocab - v0) : TL::kBV);
-    const __amdgpu_buffer_rsrc_t wr = make_rsrc(w + v0 * hidden, w_rows * row_bytes);
-    const uint32_t k0 = (uint32_t)kk * TL::kBK;
-    const uint32_t soff = k0 * 2u;
-#pragma unroll
-    for (int i = 0; i < TL::kGroupsPerWave; ++i) {
-      const int g = wave + TL::kWaves * i;
-      uint32_t vo = voff[i];
-      if (k_ragged && k0 + kchunk[i] >= (uint32_t)hidden) vo = 0x7ffffff0u;  // past the end: zeros
-      lds_ptr_t dst = (lds_ptr_t)(&lds[buf][g * 8 * 64]);
-      if (i < TL::kGroupsW / TL::kWaves)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, vo, soff, 0, 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, dst, 16, vo, soff, 0, 0);
-    }
+    const int64_t left = vocab - v0;  // <= 0 only for a tile past the end, never loaded
+    const uint32_t w_rows = (uint32_t)(left < 0 ? 0 : (left < TL::kBV ? left : TL::kBV));
+    return make_rsrc(w + (left < 0 ? 0 : v0 * hidden), w_rows * row_bytes);
   };
+  // DMA i of this wave for a slab at hidden offset k0 into a W or x stage.
+  // `tail` marks the last slab of a hidden size that is not a multiple of 64:
+  // chunks past the end read zeros.
+  auto issue_w = [&](int i, __amdgpu_buffer_rsrc_t wr, uint32_t k0, bool tail, uint16_t* stage) {
+    uint32_t vo = voff_w[i];
+    if (tail && k0 + kch_w[i] >= (uint32_t)hidden) vo = 0x7ffffff0u;
+    lds_ptr_t dst = (lds_ptr_t)(stage + (wave + TL::kWaves * i) * 8 * TL::kBK);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, vo, k0 * 2u, 0, 0);
+  };
+  auto issue_x = [&](int i, uint32_t k0, bool tail, uint16_t* stage) {
+    uint32_t vo = voff_x[i];
+    if (tail && k0 + kch_x[i] >= (uint32_t)hidden) vo = 0x7ffffff0u;
+    lds_ptr_t dst = (lds_ptr_t)(stage + (wave + TL::kWaves * i) * 8 * TL::kBK);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, dst, 16, vo, k0 * 2u, 0, 0);
+  };
+  constexpr int kWPerGroup = TL::kWPerWave / BTB;  // spread over one k-step's MFMA groups
+  constexpr int kXPerGroup = TL::kXPerWave / BTB;
+  static_assert(kWPerGroup * BTB == TL::kWPerWave && kXPerGroup * BTB == TL::kXPerWave, "DMA spread");
 
-  if (n_iter > 0) issue_slab(tile0, 0, 0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's slab is in LDS
-  __syncthreads();
-
-  // LDS read addresses (bf16 elements) of this lane's fragments at k-step 0;
-  // k-step ks adds the swizzled chunk offset, computed per lane below.
+  // LDS rows of this lane's fragments.
   int a_row[BVB], b_row[BTB];
 #pragma unroll
   for (int a = 0; a < BVB; ++a) a_row[a] = wv * (BVB * 32) + a * 32 + (lane & 31);
 #pragma unroll
-  for (int b = 0; b < BTB; ++b) b_row[b] = TL::kBV + wt * (BTB * 32) + b * 32 + (lane & 31);
+  for (int b = 0; b < BTB; ++b) b_row[b] = wt * (BTB * 32) + b * 32 + (lane & 31);
+
+  const bool k_ragged = (hidden % TL::kBK) != 0;
+  auto slab_is_tail = [&](int kk) { return k_ragged && kk == nk - 1; };
+
+  // Fragment loads of k-step ks of slab stages (Ws, Xs) into fragment buffer p.
+  bf16x8 af[2][BVB], bfr[2][BTB];
+  auto read_frags = [&](const uint16_t* Ws, const uint16_t* Xs, int ks, int p) {
+    const int c = 2 * ks + half;
+#pragma unroll
+    for (int a = 0; a < BVB; ++a)
+      af[p][a] = *reinterpret_cast<const bf16x8*>(Ws + a_row[a] * TL::kBK + swz(a_row[a], c) * 8);
+#pragma unroll
+    for (int b = 0; b < BTB; ++b)
+      bfr[p][b] = *reinterpret_cast<const bf16x8*>(Xs + b_row[b] * TL::kBK + swz(b_row[b], c) * 8);
+  };
+
+  // Pipeline.  W slabs (the operand that misses to HBM) rotate through
+  // kWStages stages and x slabs through kXStages.  The barrier of slab `it`
+  // sits before its last k-step: by then its last fragments are in registers
+  // and its stages are free.  Right after it, the x slab it+kXStages goes into
+  // the freed x stage (spread over the last k-step's MFMAs), and during the
+  // next slab's first k-step the W slab it+kWStages goes into the freed W
+  // stage.  Every x slab is issued before the newer W slab, so at the next
+  // barrier "all but the newest W slab landed" is exactly what is needed.
+  int wq = 0;                  // it % kWStages
+  int xq = 0;                  // it % kXStages
+  // W cursor (next W slab to issue) and x cursor (next x slab to issue).
+  int w_kk = 0, w_tile = tile0, w_left = n_iter;
+  __amdgpu_buffer_rsrc_t w_cur = w_rsrc(tile0);
+  int x_kk = 0, x_left = n_iter;
+  auto w_issue_part = [&](int stage, int group) {  // this wave's W DMAs for MFMA group `group`
+#pragma unroll
+    for (int d = 0; d < kWPerGroup; ++d) {
+      const int i = group * kWPerGroup + d;
+      issue_w(i, w_cur, (uint32_t)w_kk * TL::kBK, slab_is_tail(w_kk), lds + stage * TL::kWStageElems);
+    }
+  };
+  auto w_advance = [&]() {
+    --w_left;
+    if (++w_kk == nk) {
+      w_kk = 0;
+      ++w_tile;
+      w_cur = w_rsrc(w_tile);
+    }
+  };
+  auto x_issue_part = [&](int stage, int group) {
+#pragma unroll
+    for (int d = 0; d < kXPerGroup; ++d) {
+      const int i = group * kXPerGroup + d;
+      issue_x(i, (uint32_t)x_kk * TL::kBK, slab_is_tail(x_kk), lds + kXBase + stage * TL::kXStageElems);
+    }
+  };
+  auto x_advance = [&]() {
+    --x_left;
+    if (++x_kk == nk) x_kk = 0;
+  };
+
+  // Prologue: x slabs 0 .. kXStages-1 and W slabs 0 .. kWStages-1, in the
+  // order x0 W0 x1 W1 W2: slab 0 landed, then at slab 0's barrier everything
+  // but W2 must have landed.
+  for (int j = 0; j < TL::kWStages; ++j) {
+    if (j < TL::kXStages && x_left > 0) {
+#pragma unroll
+      for (int g = 0; g < BTB; ++g) x_issue_part(j, g);
+      x_advance();
+    }
+    if (w_left > 0) {
+#pragma unroll
+      for (int g = 0; g < BTB; ++g) w_issue_part(j, g);
+      w_advance();
+    }
+    if (j == 0) {
+      wait_vmcnt<0>();  // only the first x and W slabs have been issued
+      __syncthreads();
+    }
+  }
+  if (n_iter > 0) read_frags(lds, lds + kXBase, 0, 0);
 
   int it = 0;
   for (int tile = tile0; tile < tile1; ++tile) {
@@ -225,44 +325,45 @@ __global__ __launch_bounds__(64 * WV * WT) void fused_xent_partial_kernel(
       for (int a = 0; a < BVB; ++a) acc[b][a] = (f32x16)(0.0f);
 
     for (int kk = 0; kk < nk; ++kk, ++it) {
-      const int cur = it & 1;
-      if (it + 1 < n_iter) {
-        const bool next_tile = (kk + 1 == nk);
-        issue_slab(next_tile ? tile + 1 : tile, next_tile ? 0 : kk + 1, cur ^ 1);
-      }
-      const uint16_t* S = lds[cur];
-      // Fragments of k-step ks+1 are read while k-step ks is multiplied.
-      bf16x8 af[2][BVB], bfr[2][BTB];
+      const uint16_t* Ws = lds + wq * TL::kWStageElems;
+      const uint16_t* Xs = lds + kXBase + xq * TL::kXStageElems;
+      // W slab issued in this slab's first k-step (into the stage freed at the
+      // previous barrier), if any is left.
+      const int w_stage_free = (wq + TL::kWStages - 1) % TL::kWStages;
+      const bool w_now = (it > 0) && (w_left > 0);
 #pragma unroll
-      for (int a = 0; a < BVB; ++a)
-        af[0][a] = *reinterpret_cast<const bf16x8*>(S + a_row[a] * 64 + swz(a_row[a], half) * 8);
-#pragma unroll
-      for (int b = 0; b < BTB; ++b)
-        bfr[0][b] = *reinterpret_cast<const bf16x8*>(S + b_row[b] * 64 + swz(b_row[b], half) * 8);
-#pragma unroll
-      for (int ks = 0; ks < TL::kBK / 16; ++ks) {
+      for (int ks = 0; ks < TL::kKSteps - 1; ++ks) {
         const int p = ks & 1;
-        if (ks + 1 < TL::kBK / 16) {
-          const int c = 2 * (ks + 1) + half;
+        read_frags(Ws, Xs, ks + 1, p ^ 1);
 #pragma unroll
-          for (int a = 0; a < BVB; ++a)
-            af[p ^ 1][a] = *reinterpret_cast<const bf16x8*>(S + a_row[a] * 64 + swz(a_row[a], c) * 8);
-#pragma unroll
-          for (int b = 0; b < BTB; ++b)
-            bfr[p ^ 1][b] = *reinterpret_cast<const bf16x8*>(S + b_row[b] * 64 + swz(b_row[b], c) * 8);
-        }
-        // Keep the reads above ahead of this k-step's MFMAs (the scheduler would
-        // otherwise sink each read next to its first use and expose LDS latency).
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int b = 0; b < BTB; ++b)
+        for (int b = 0; b < BTB; ++b) {
 #pragma unroll
           for (int a = 0; a < BVB; ++a)
             acc[b][a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[p][a], bfr[p][b], acc[b][a], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+          if (ks == 0 && w_now) w_issue_part(w_stage_free, b);
+          }
       }
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next slab landed in LDS
+      if (w_now) w_advance();
+      // The next slab's x and W have landed for every wave (only the newest W
+      // slab may still be in flight); every read of this slab is done.
+      if (w_now) wait_vmcnt<TL::kWPerWave>(); else wait_vmcnt<0>();
       __syncthreads();
+      const int wq1 = (wq + 1 == TL::kWStages) ? 0 : wq + 1;
+      const int xq1 = (xq + 1 == TL::kXStages) ? 0 : xq + 1;
+      const bool x_now = x_left > 0;
+      if (it + 1 < n_iter)
+        read_frags(lds + wq1 * TL::kWStageElems, lds + kXBase + xq1 * TL::kXStageElems, 0, 0);
+      constexpr int pl = (TL::kKSteps - 1) & 1;
+#pragma unroll
+      for (int b = 0; b < BTB; ++b) {
+#pragma unroll
+        for (int a = 0; a < BVB; ++a)
+          acc[b][a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[pl][a], bfr[pl][b], acc[b][a], 0, 0, 0);
+        if (x_now) x_issue_part(xq, b);  // x slab it + kXStages into this slab's x stage
+      }
+      if (x_now) x_advance();
+      wq = wq1;
+      xq = xq1;
     }
 
     // Epilogue of the finished tile, one token column at a time.
@@ -284,8 +385,9 @@ __global__ __launch_bounds__(64 * WV * WT) void fused_xent_partial_kernel(
     const Lse o{half_swap(st[b].m), half_swap(st[b].s)};
     st[b] = (half == 0) ? lse_merge(st[b], o) : lse_merge(o, st[b]);
   }
-  // ... then the WV waves that share these tokens, through LDS.
-  float* red = reinterpret_cast<float*>(&lds[0][0]);  // [WV][kBT][2]
+  // ... then the WV waves that share these tokens, through LDS (the slab
+  // stages are free: every wave passed the barrier after its last slab).
+  float* red = reinterpret_cast<float*>(lds);  // [WV][kBT][2]
   if (half == 0) {
 #pragma unroll
     for (int b = 0; b < BTB; ++b) {
@@ -353,7 +455,7 @@ int fused_segments(int64_t tokens, int64_t vocab, int num_cus) {
 hipError_t launch_fused(const FusedArgs& a, hipStream_t stream) {
   const int64_t n_tok = (a.tokens + FusedTile::kBT - 1) / FusedTile::kBT;
   const int64_t grid = n_tok * a.segments;
-  hipLaunchKernelGGL((fused_xent_partial_kernel<2, 2, 4, 4>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((fused_xent_partial_kernel<FusedTile, 4, 2, 2>), dim3((unsigned)grid),
                      dim3(FusedTile::kThreads), 0, stream, (const uint16_t*)a.x,
                      (const uint16_t*)a.w, a.tokens, a.hidden, a.vocab, a.target, a.segments,
                      (float2*)a.seg_partials, a.target_logit);
