@@ -16,7 +16,8 @@ the kernel itself at this size; the eager per-call time is reported next to it.
 
 Prints ONE JSON line (rank 0, N = 1).  Other workloads are measured the same way and
 reported under "workloads".  The roofline is for the dominant kernel: algorithmic bytes
-(every declared tensor crossing HBM once) per launch over the average launch duration.
+(each input and output tensor read or written once) per launch over the average launch
+duration.
 """
 from __future__ import annotations
 
@@ -43,7 +44,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 # ------------------------------------------------------------------ work model
 
 def tensor_bytes(tensors) -> int:
-    """Bytes of a list of (numel, itemsize) tensors, each crossing HBM once."""
+    """Bytes of a list of (numel, itemsize) tensors, each read or written once."""
     return int(sum(int(n) * int(s) for n, s in tensors))
 
 
@@ -64,10 +65,19 @@ def fused_flops(tokens: int, hidden: int, vocab: int) -> int:
     return 2 * int(tokens) * int(hidden) * int(vocab)
 
 
-def source_digest() -> str:
-    """sha256 over the kernel sources and build script (ties counter data to a build)."""
+CSRC = os.path.join(ROOT, "vocab_cross_entropy_row_amd", "csrc")
+# Sources that define each workload's dominant kernel (plus the build flags).
+KERNEL_SOURCES = {
+    "xent": ["xent_kernels.hip", "lce_device.h", "lce_internal.h"],
+    "fused": ["fused_kernel.hip", "lce_device.h", "lce_internal.h"],
+}
+
+
+def source_digest(kind: str) -> str:
+    """sha256 over the sources of a workload kind's kernels and the build script: ties
+    counter data to the kernel build it was taken on."""
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(ROOT, "vocab_cross_entropy_row_amd", "csrc", "*")))
+    files = [os.path.join(CSRC, f) for f in KERNEL_SOURCES[kind]]
     files.append(os.path.join(ROOT, "vocab_cross_entropy_row_amd", "build.py"))
     for f in files:
         h.update(os.path.basename(f).encode())
@@ -76,15 +86,15 @@ def source_digest() -> str:
     return h.hexdigest()
 
 
-def traffic_for(workload: str):
+def traffic_for(workload: str, kind: str):
     """HBM traffic per launch from the committed counter summary, or None if absent or
-    if the kernel sources changed since the counters were taken."""
+    if the kernel's sources changed since the counters were taken."""
     path = os.path.join(PROFILES, f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         d = json.load(fh)
-    if d.get("source_sha256") != source_digest():
+    if d.get("source_sha256") != source_digest(kind):
         return None
     return d.get("traffic_bytes_per_launch")
 
@@ -214,13 +224,13 @@ def roofline_entry(w, us: float) -> dict:
         b = xent_bytes(w.tokens, w.vocab, esize, w.reduction)
         gbs = b / (us * 1e-6) / 1e9
         return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_for(w.name),
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_for(w.name, w.kind),
                 "algorithmic_bytes": b}
     fl = fused_flops(w.tokens, w.hidden, w.vocab)
     tf = fl / (us * 1e-6) / 1e12
     return {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_DENSE_TFLOPS,
             "unit": "TFLOP/s", "frac": round(tf / BF16_DENSE_TFLOPS, 4),
-            "traffic": traffic_for(w.name), "algorithmic_flops": fl,
+            "traffic": traffic_for(w.name, w.kind), "algorithmic_flops": fl,
             "algorithmic_bytes": fused_bytes(w.tokens, w.hidden, w.vocab, w.reduction)}
 
 
@@ -300,12 +310,13 @@ def _per_dispatch(d: str, counter: str):
 
 
 def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, kernel_substr: str,
-                  commands: dict) -> dict:
+                  commands: dict, kind: str) -> dict:
     """Traffic per launch of the kernel whose name contains `kernel_substr`, from a
     FETCH_SIZE run and a WRITE_SIZE run (KiB per dispatch), each scaled by the same
     counter's reading for the COPY_BYTES copy kernel in the same run."""
     out = {"workload": workload, "kernel_match": kernel_substr, "commands": commands,
-           "copy_bytes": COPY_BYTES, "source_sha256": source_digest()}
+           "copy_bytes": COPY_BYTES, "source_files": KERNEL_SOURCES[kind] + ["build.py"],
+           "source_sha256": source_digest(kind)}
     total = 0.0
     for label, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
         vals = _per_dispatch(d, counter)
@@ -353,7 +364,7 @@ def main(argv=None) -> int:
         import lce_synth
         wl = lce_synth.HEADLINE if args.workloads in ("all", "headline") else args.workloads
         d = summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], wl, args.kernel,
-                          {"runs": args.pmc_command})
+                          {"runs": args.pmc_command}, lce_synth.WORKLOADS[wl].kind)
         os.makedirs(PROFILES, exist_ok=True)
         path = os.path.join(PROFILES, f"traffic_{wl}.json")
         with open(path, "w") as fh:

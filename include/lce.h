@@ -14,7 +14,7 @@
  *     row-major and contiguous.  The caller owns every buffer; liblce never
  *     frees or retains a caller pointer after the call returns.
  *   - Inputs are never written.  `out` must not overlap any input
- *     ("No mutation or aliasing" in each page's Semantics block).
+ *     (each page's Semantics block rules out mutating or aliasing inputs).
  *   - Calls are asynchronous: work is enqueued on `stream` (0 = the null
  *     stream) and the call returns without synchronising.  Argument errors are
  *     reported synchronously, before anything is enqueued; a failed launch is
@@ -27,7 +27,7 @@
  *   - Losses are always fp32; accumulation is fp32.
  *   - Results are bitwise reproducible run to run for the same inputs, shape
  *     and device: every reduction has a fixed order and no float atomics are
- *     used (the pages leave determinism unspecified).
+ *     used (the pages do not specify determinism).
  *   - liblce keeps a small device scratch buffer per (device, stream), grown
  *     on demand with hipMalloc and kept until the process ends.  Calls that
  *     run concurrently on the same stream are ordered by the stream; calls on
@@ -107,7 +107,7 @@ lce_status lce_xent_fwd(const void* logits, lce_dtype dtype, int64_t tokens, int
  *
  * Defines: KernelIndex "Fused linear + CPO loss" (description: activations
  * projected through a vocab x hidden LM head against integer targets,
- * computed chunked without materialising logits; Semantics: x float
+ * reduced chunk by chunk so the logits are never stored; Semantics: x float
  * [batch, seq, hidden], weight float [vocab, hidden], target int64
  * [batch, seq], loss float [1]).  The loss applied to the projected logits
  * is the same per-token cross-entropy as lce_xent_fwd (the CPO preference

@@ -5,8 +5,8 @@ the one piece of code that both the HIP path (tests, benchmark) and the fp64
 oracle consume, so both see the very same bytes.
 
 Recipe (the pages give shapes and dtypes but no value distributions; the
-KernelIndex "Cross-entropy loss" description only says the benchmark generates
-fp32 logits):
+KernelIndex "Cross-entropy loss" description states only that its benchmark
+logits are fp32):
 
 * Values are drawn in chunks of ``CHUNK_ROWS`` rows.  Chunk ``c`` of stream ``s``
   under seed ``k`` uses ``numpy.random.Generator(PCG64(SeedSequence([k, s, c])))``,

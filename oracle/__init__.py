@@ -142,18 +142,6 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return u32.view(np.float32).astype(np.float64)
 
 
-def fused_logits_f64(x_bits: np.ndarray, w_bits: np.ndarray,
-                     rows: np.ndarray | None = None) -> np.ndarray:
-    """``z = x W^T`` in fp64 for the selected token rows (all rows if ``rows`` is None).
-
-    ``x_bits`` is ``[tokens, hidden]`` and ``w_bits`` ``[vocab, hidden]``, both bf16 bit
-    patterns.  Products of bf16 values are exact in fp64; the sums are fp64.
-    """
-    x64 = bf16_bits_to_f64(x_bits if rows is None else x_bits[rows])
-    w64 = bf16_bits_to_f64(w_bits)
-    return np.matmul(x64, w64.T)
-
-
 def fused_linear_xent_rows(x_bits: np.ndarray, w_bits: np.ndarray, target: np.ndarray,
                            rows: np.ndarray | None = None, block: int = 128,
                            nthreads: int | None = None) -> np.ndarray:

@@ -1,7 +1,7 @@
 """The benchmark's work model reproduces the bandwidth floors the pages print.
 
-The pages' floor is "every declared tensor crosses HBM exactly once" at a datasheet
-bandwidth; ``bench.tensor_bytes`` / ``xent_bytes`` / ``fused_bytes`` must give exactly
+The pages' floor assumes each declared input and output tensor moves through HBM
+one time, at a datasheet bandwidth; ``bench.tensor_bytes`` / ``xent_bytes`` / ``fused_bytes`` must give exactly
 the bytes behind each printed floor (tests/golden/page_floors.json, cited there)."""
 import json
 import math
