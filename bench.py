@@ -431,7 +431,7 @@ def main(argv=None) -> int:
         "roofline": {k: v for k, v in h["roofline"].items() if k in
                      ("bound", "achieved", "peak", "unit", "frac", "traffic")},
     }
-    line["roofline"]["kernel"] = "xent_wave_rows_kernel<bf16, 8>"
+    line["roofline"]["kernel"] = "xent_wave_rows_kernel<bf16, 8 chunks per lane per batch, 4 waves>"
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(head)
     line["workloads"] = {n: {"us_per_step": round(r["us_per_step"], 3),

@@ -29,9 +29,16 @@
  *     and device: every reduction has a fixed order and no float atomics are
  *     used (the pages do not specify determinism).
  *   - liblce keeps a small device scratch buffer per (device, stream), grown
- *     on demand with hipMalloc and kept until the process ends.  Calls that
- *     run concurrently on the same stream are ordered by the stream; calls on
- *     different streams use different scratch buffers.
+ *     on demand with hipMalloc.  An outgrown buffer is retired, never freed:
+ *     every scratch buffer is kept until the process ends.  Calls on one
+ *     stream are ordered by the stream; calls on different streams use
+ *     different scratch buffers.
+ *   - HIP graph capture: a call may be captured if an earlier, uncaptured
+ *     call on the same stream and device already grew its scratch far enough
+ *     (the largest shape to be captured is enough); otherwise the call fails
+ *     with LCE_ERR_UNSUPPORTED before anything is enqueued.  A captured call
+ *     keeps using the scratch of the stream it was captured on, so replays
+ *     must not run concurrently with other liblce work on that stream.
  *   - No call throws; every error is a status code plus a thread-local
  *     message (lce_last_error).
  */
@@ -95,8 +102,9 @@ typedef enum {
  *   stream    HIP stream the work is enqueued on.
  *
  * Returns LCE_OK, LCE_ERR_INVALID_ARG (NULL pointer, tokens < 0, vocab < 1,
- * bad enum, misaligned pointer), LCE_ERR_UNSUPPORTED (vocab >= 2^31),
- * LCE_ERR_ALIAS, LCE_ERR_OOM or LCE_ERR_HIP.
+ * bad enum, misaligned pointer), LCE_ERR_UNSUPPORTED (vocab >= 2^31, or
+ * scratch that would have to grow under graph capture), LCE_ERR_ALIAS,
+ * LCE_ERR_OOM or LCE_ERR_HIP.
  */
 lce_status lce_xent_fwd(const void* logits, lce_dtype dtype, int64_t tokens, int64_t vocab,
                         const int64_t* target, lce_reduction reduction, float* out,

@@ -11,7 +11,6 @@ every kernel path; the five full-size workloads run in the launch configuration
 the benchmark times.
 """
 import math
-import os
 
 import numpy as np
 import pytest
@@ -24,6 +23,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 import vocab_cross_entropy_row_amd as lce  # noqa: E402
+from gpu_util import forced_env, to_dev  # noqa: E402
 
 TOK_ABS = 1e-4
 MEAN_REL = 1e-5
@@ -39,33 +39,6 @@ def _gpu():
     lce.load()
     yield
     torch.cuda.synchronize()
-
-
-class forced_env:
-    """Temporarily set liblce's path-selection environment variables."""
-
-    def __init__(self, **kv):
-        self.kv = {k: str(v) for k, v in kv.items()}
-        self.old = {}
-
-    def __enter__(self):
-        for k, v in self.kv.items():
-            self.old[k] = os.environ.get(k)
-            os.environ[k] = v
-
-    def __exit__(self, *exc):
-        for k, v in self.old.items():
-            if v is None:
-                os.environ.pop(k, None)
-            else:
-                os.environ[k] = v
-
-
-def to_dev(arr):
-    """numpy f32 -> fp32 tensor; numpy uint16 (bf16 bits) -> bf16 tensor."""
-    if arr.dtype == np.uint16:
-        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).cuda().view(torch.bfloat16)
-    return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
 
 
 def gpu_xent(logits_np, target_np, reduction, dtype):

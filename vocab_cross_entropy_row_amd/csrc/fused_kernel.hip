@@ -71,12 +71,6 @@ __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r & 7) ^ ((r >> 
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// Buffer resource over `bytes` bytes at `base` (raw, unswizzled; loads past the
-// end return zero).  gfx9 word 3: 32-bit data format, no swizzle.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
 // s_waitcnt vmcnt(N) with the other counters left free (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -415,7 +409,7 @@ __global__ __launch_bounds__(TL::kThreads) void fused_xent_partial_kernel(
 __global__ __launch_bounds__(kRowThreads) void fused_xent_merge_kernel(
     int64_t tokens, int64_t vocab, int segments, const float2* __restrict__ part,
     const float* __restrict__ zt, const int64_t* __restrict__ target, float* __restrict__ out,
-    float* __restrict__ partials, unsigned* __restrict__ ticket, int reduce_mean) {
+    uint64_t* __restrict__ slots, unsigned* __restrict__ ticket, int reduce_mean) {
   const int64_t row = (int64_t)blockIdx.x * kRowThreads + threadIdx.x;
   float loss = 0.0f;
   if (row < tokens) {
@@ -437,7 +431,7 @@ __global__ __launch_bounds__(kRowThreads) void fused_xent_merge_kernel(
       if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
       __syncthreads();
     }
-    finish_mean(red[0], partials, ticket, out, tokens);
+    finish_mean(red[0], slots, ticket, out, tokens);
   }
 }
 
@@ -464,7 +458,7 @@ hipError_t launch_fused(const FusedArgs& a, hipStream_t stream) {
   const int64_t blocks = (a.tokens + kRowThreads - 1) / kRowThreads;
   hipLaunchKernelGGL(fused_xent_merge_kernel, dim3((unsigned)blocks), dim3(kRowThreads), 0, stream,
                      a.tokens, a.vocab, a.segments, (const float2*)a.seg_partials,
-                     (const float*)a.target_logit, a.target, a.out, a.mean_partials, a.ticket,
+                     (const float*)a.target_logit, a.target, a.out, a.mean_slots, a.ticket,
                      a.reduce_mean);
   return hipGetLastError();
 }

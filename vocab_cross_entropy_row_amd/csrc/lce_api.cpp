@@ -8,6 +8,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <map>
+#include <vector>
 #include <mutex>
 #include <string>
 #include <utility>
@@ -43,18 +44,24 @@ bool overlaps(const void* a, uint64_t an, const void* b, uint64_t bn) {
 bool aligned(const void* p, uint64_t n) { return ((uintptr_t)p % n) == 0; }
 
 // ------------------------------------------------------------ scratch pool
-// One grow-only device buffer per (device, stream); kept until process exit.
-// Layout: the mean's ticket counters first (kTicketBytes, zero between calls),
-// then 256-byte-aligned regions carved by Carve.
+// One grow-only device buffer per (device, stream).  A buffer that is outgrown
+// is retired, not freed: launches already queued, or recorded into a HIP graph
+// that may be replayed later, keep pointing at it.  Every buffer lives until
+// process exit.  Layout: the mean's ticket counters first (kTicketBytes, zero
+// between calls), then 256-byte-aligned regions carved by Carve.
 struct Scratch {
   void* ptr = nullptr;
   size_t bytes = 0;
 };
 std::mutex g_mu;
 std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
+std::vector<void*> g_retired;
 std::map<int, int> g_num_cus;
 
 constexpr size_t kAlign = 256;
+// Most bytes one kernel streams through a single buffer resource (32-bit
+// offsets, with room for the batch loaded past the end).
+constexpr int64_t kMaxStreamBytes = int64_t(1) << 30;
 size_t round_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
 
 struct Carve {
@@ -73,14 +80,14 @@ lce_status get_scratch(hipStream_t stream, size_t need, char** out) {
   std::lock_guard<std::mutex> lock(g_mu);
   Scratch& s = g_scratch[{dev, stream}];
   if (s.bytes < need) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(stream, &cap);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+    if (cap != hipStreamCaptureStatusNone)
+      return fail(LCE_ERR_UNSUPPORTED,
+                  "stream is being captured and its scratch must grow to %zu bytes: make one call "
+                  "of the largest shape on this stream before capture", need);
     if (getenv("LCE_TEST_FAIL_ALLOC")) return fail(LCE_ERR_OOM, "scratch allocation refused (LCE_TEST_FAIL_ALLOC)");
-    if (s.ptr) {
-      e = hipStreamSynchronize(stream);  // work queued on this stream may still use it
-      if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-      (void)hipFree(s.ptr);
-      s.ptr = nullptr;
-      s.bytes = 0;
-    }
     const size_t bytes = round_up(need + need / 4, size_t(1) << 20);
     void* p = nullptr;
     e = hipMalloc(&p, bytes);
@@ -88,12 +95,14 @@ lce_status get_scratch(hipStream_t stream, size_t need, char** out) {
       (void)hipGetLastError();
       return fail(LCE_ERR_OOM, "hipMalloc of %zu bytes of scratch failed: %s", bytes, hipGetErrorName(e));
     }
-    // The ticket counters must start at zero; kernels leave them at zero.
-    e = lce::launch_zero_u32((unsigned*)p, lce::kTicketBytes / sizeof(unsigned), stream);
+    // Ticket counters, epoch and mean slots must start at zero (kernels leave
+    // the counters at zero; a slot only ever holds tags of earlier launches).
+    e = lce::launch_zero_u32((unsigned*)p, (int64_t)(bytes / sizeof(unsigned)), stream);
     if (e != hipSuccess) {
       (void)hipFree(p);
       return hip_fail(e, "scratch initialisation");
     }
+    if (s.ptr) g_retired.push_back(s.ptr);
     s.ptr = p;
     s.bytes = bytes;
   }
@@ -234,16 +243,16 @@ lce_status lce_xent_fwd(const void* logits, lce_dtype dtype, int64_t tokens, int
 
   // Path selection (measured on MI355X):
   //  - rows up to 32 KiB: one wave per row; 4 waves per workgroup without a
-  //    mean, 16 with a mean (a quarter of the ticket hand-offs), then at most
-  //    8 chunks per lane per batch (register budget of 1024-thread groups);
+  //    mean, 16 with a mean (a quarter of the ticket hand-offs);
   //  - longer rows: without a mean, one workgroup per row; with a mean, one
   //    wave per row in 16-wave workgroups; with few rows, several workgroups
   //    per row (split).
   const int64_t esize = a.bf16 ? 2 : 4;
   const int64_t row_bytes = vocab * esize;
   const int64_t nvec = row_bytes / 16;
+  // Chunks per lane per batch (two batches are in flight at once).
   const int64_t per_lane = (nvec + 63) / 64;
-  a.unroll = per_lane <= 4 ? 4 : per_lane <= 8 ? 8 : 16;
+  a.unroll = per_lane <= 4 ? 4 : 8;
   a.waves_per_block = 4;
   if (row_bytes <= 32 * 1024) {
     a.path = lce::XentPath::WaveRows;
@@ -268,6 +277,8 @@ lce_status lce_xent_fwd(const void* logits, lce_dtype dtype, int64_t tokens, int
   const int forced_waves = env_int("LCE_WAVES_PER_BLOCK", 0);
   if (forced_waves == 4 || forced_waves == 16) a.waves_per_block = forced_waves;
   if (a.waves_per_block == 16 && a.unroll > 8) a.unroll = 8;
+  // The kernels address a row (or a split slice) with 32-bit buffer offsets.
+  if (a.path != lce::XentPath::Split && row_bytes > kMaxStreamBytes) a.path = lce::XentPath::Split;
 
   size_t need_partials = 0, need_split = 0;
   if (a.path == lce::XentPath::Split) {
@@ -280,6 +291,8 @@ lce_status lce_xent_fwd(const void* logits, lce_dtype dtype, int64_t tokens, int
     if (S > max_s) S = max_s;
     if (S < 1) S = 1;
     if (S > 65535) S = 65535;
+    const int64_t min_s = (nvec * 16 + kMaxStreamBytes - 1) / kMaxStreamBytes;
+    if (S < min_s) S = min_s;
     a.splits = (int)S;
     a.chunks_per_split = (int)((nvec + S - 1) / S);
     need_split = (size_t)tokens * (size_t)S * 8u;
@@ -288,7 +301,7 @@ lce_status lce_xent_fwd(const void* logits, lce_dtype dtype, int64_t tokens, int
       (a.path == lce::XentPath::BlockRows) ? tokens
       : (a.path == lce::XentPath::WaveRows) ? (tokens + a.waves_per_block - 1) / a.waves_per_block
                                               : (tokens + lce::kRowThreads / 64 - 1) / (lce::kRowThreads / 64);
-  need_partials = (size_t)mean_blocks * 4u;
+  need_partials = (size_t)mean_blocks * 8u;
 
   Carve cv;
   const size_t off_mean = cv.take(need_partials);
@@ -296,7 +309,7 @@ lce_status lce_xent_fwd(const void* logits, lce_dtype dtype, int64_t tokens, int
   char* base = nullptr;
   if ((s = get_scratch(stream, cv.off, &base)) != LCE_OK) return s;
   a.ticket = (unsigned*)base;
-  a.mean_partials = (float*)(base + off_mean);
+  a.mean_slots = (uint64_t*)(base + off_mean);
   a.split_partials = (float*)(base + off_split);
 
   hipError_t e = lce::launch_xent(a, stream);
@@ -339,13 +352,13 @@ lce_status lce_fused_linear_xent_fwd(const void* x, const void* weight, int64_t 
   Carve cv;
   const size_t off_seg = cv.take((size_t)a.segments * (size_t)tokens * 8u);
   const size_t off_zt = cv.take((size_t)tokens * 4u);
-  const size_t off_mean = cv.take((size_t)((tokens + lce::kRowThreads - 1) / lce::kRowThreads) * 4u);
+  const size_t off_mean = cv.take((size_t)((tokens + lce::kRowThreads - 1) / lce::kRowThreads) * 8u);
   char* base = nullptr;
   if ((s = get_scratch(stream, cv.off, &base)) != LCE_OK) return s;
   a.ticket = (unsigned*)base;
   a.seg_partials = (float*)(base + off_seg);
   a.target_logit = (float*)(base + off_zt);
-  a.mean_partials = (float*)(base + off_mean);
+  a.mean_slots = (uint64_t*)(base + off_mean);
 
   hipError_t e = lce::launch_fused(a, stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");

@@ -123,10 +123,17 @@ __device__ __forceinline__ float half_swap(float v) {
 
 __device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Buffer resource over `bytes` bytes at `base` (raw, unswizzled): a load whose
+// VGPR offset plus immediate offset is at or past `bytes` reads no memory and
+// returns zero.  gfx9 word 3: 32-bit data format, no swizzle.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 // ------------------------------------------------------------ deterministic mean
-// Every workgroup leaves one fp32 partial; the workgroup that finishes last
-// adds all partials in a fixed order and writes the mean.  No float atomics
-// are used, so the result is bitwise reproducible.
+// Every workgroup contributes one fp32 partial; the workgroup that finishes
+// last adds all partials in a fixed order and writes the mean.  No float
+// atomics are used, so the result is bitwise reproducible.
 //
 // Finding the last workgroup: a two-level integer ticket.  Workgroup b counts
 // itself in group counter b % G (G <= 64 counters, each on its own 256-byte
@@ -135,20 +142,33 @@ __device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_rea
 // counter is last.  Each completing workgroup resets the counter it completed,
 // so all counters are zero again when the kernel ends.
 //
-// Visibility across the XCDs (each has its own L2): the partials are written
-// and read only with agent-scope atomic stores and loads, which are coherent
-// at agent scope by themselves, and each writer waits for its store to
-// complete (s_waitcnt) before it touches a counter.  A release/acquire fence
-// pair would instead write back (and invalidate) a whole L2 per workgroup.
+// Handing over the partials: every other workgroup writes its partial after
+// taking its ticket, as one 64-bit agent-scope atomic store of (tag, value),
+// and leaves without waiting for it.  The tag is the launch's epoch + 1: the
+// epoch word is read beside the first ticket, and the last workgroup advances
+// it for the next launch on this scratch buffer.  The last workgroup polls
+// each slot until it carries this launch's tag, so data and flag arrive
+// together and no writer has to wait for its store; slots left by earlier
+// launches carry older tags (a new buffer is zeroed, and tags start at 1).
+// The chain after the last row is then three memory round trips: two ticket
+// atomics and one read of the slots.  Agent-scope atomics are coherent across
+// the XCDs (each has its own L2) without writing back or invalidating an L2.
 //
-// Only wave 0 takes part: the other waves of the workgroup retire at once, so
-// the hand-off's memory round trips do not hold their slots.
+// Only wave 0 takes part: the other waves of the workgroup retire at once.
 constexpr int kTicketGroups = 64;
 constexpr int kTicketStride = 64;  // unsigned ints (256 bytes) between counters
+constexpr int kTopCounter = kTicketGroups * kTicketStride;
+constexpr int kEpochWord = (kTicketGroups + 1) * kTicketStride;
+constexpr unsigned kPollLimit = 1u << 22;  // safety net: never reached by a correct launch
+
+__device__ __forceinline__ uint64_t mean_slot(unsigned tag, float v) {
+  return ((uint64_t)tag << 32) | __float_as_uint(v);
+}
 
 // `block_sum` must be valid in thread 0; every thread of the workgroup calls
 // this after its last barrier.  Threads of waves other than 0 return at once.
-__device__ __forceinline__ void finish_mean(float block_sum, float* partials, unsigned* ticket,
+// `slots` holds one 64-bit slot per workgroup.
+__device__ __forceinline__ void finish_mean(float block_sum, uint64_t* slots, unsigned* ticket,
                                             float* out, int64_t tokens) {
   if (threadIdx.x >= 64) return;
   const unsigned lane = threadIdx.x;
@@ -158,26 +178,54 @@ __device__ __forceinline__ void finish_mean(float block_sum, float* partials, un
   const unsigned g = bid % G;
   const unsigned group_size = nblocks / G + (g < nblocks % G ? 1u : 0u);
   unsigned* group_ctr = ticket + g * kTicketStride;
-  unsigned* top_ctr = ticket + kTicketGroups * kTicketStride;
+  unsigned* top_ctr = ticket + kTopCounter;
+  unsigned* epoch = ticket + kEpochWord;
   int last = 0;
+  unsigned tag = 0;
   if (lane == 0) {
-    __hip_atomic_store(&partials[bid], block_sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0);  // the partial store has completed
-    if (__hip_atomic_fetch_add(group_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-        group_size - 1) {
+    const unsigned e = __hip_atomic_load(epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned tg = __hip_atomic_fetch_add(group_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    tag = e + 1u;
+    if (tg == group_size - 1) {
       __hip_atomic_store(group_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __builtin_amdgcn_s_waitcnt(0);
       last = __hip_atomic_fetch_add(top_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == G - 1;
     }
+    if (!last)
+      __hip_atomic_store(&slots[bid], mean_slot(tag, block_sum), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
   }
   if (!wave_uniform(last)) return;
+  tag = (unsigned)wave_uniform((int)tag);
+  const float own = __int_as_float(wave_uniform(__float_as_int(block_sum)));
+  constexpr int kInFlight = 8;  // slot loads per lane in flight
   float acc = 0.0f;
-  for (unsigned i = lane; i < nblocks; i += 64)
-    acc += __hip_atomic_load(&partials[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  bool ok = true;
+  for (unsigned base = lane; base < nblocks; base += 64u * kInFlight) {
+    uint64_t v[kInFlight];
+#pragma unroll
+    for (int j = 0; j < kInFlight; ++j) {
+      const unsigned i = base + 64u * j;
+      v[j] = (i < nblocks && i != bid)
+                 ? __hip_atomic_load(&slots[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                 : mean_slot(tag, own);
+    }
+#pragma unroll
+    for (int j = 0; j < kInFlight; ++j) {
+      const unsigned i = base + 64u * j;
+      if (i >= nblocks) break;
+      unsigned spins = 0;
+      while ((unsigned)(v[j] >> 32) != tag && spins++ < kPollLimit)
+        v[j] = __hip_atomic_load(&slots[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ok = ok && (unsigned)(v[j] >> 32) == tag;
+      acc += __uint_as_float((unsigned)v[j]);
+    }
+  }
   const float total = wave_sum(acc);
+  const bool all_ok = __builtin_amdgcn_ballot_w64(!ok) == 0;
   if (lane == 0) {
-    out[0] = total / (float)tokens;
+    out[0] = all_ok ? total / (float)tokens : __builtin_nanf("");
     __hip_atomic_store(top_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

@@ -9,9 +9,10 @@ namespace lce {
 
 constexpr int kRowThreads = 256;  // threads per workgroup of the row kernels
 
-// Bytes of mean-ticket counters at the start of the scratch buffer
-// (65 counters, 256 bytes apart; see finish_mean in lce_device.h).
-constexpr size_t kTicketBytes = 65 * 256;
+// Bytes of mean-ticket counters at the start of the scratch buffer: 64 group
+// counters, the top counter and the epoch word, 256 bytes apart (see
+// finish_mean in lce_device.h).
+constexpr size_t kTicketBytes = 66 * 256;
 
 enum class XentPath : int { WaveRows = 0, BlockRows = 1, Split = 2 };
 
@@ -29,8 +30,8 @@ struct XentArgs {
   int splits;               // Split: workgroups per row
   int chunks_per_split;     // Split: 16-byte chunks per workgroup
   float* split_partials;    // Split: tokens * splits (max, sum-exp) pairs
-  float* mean_partials;     // one fp32 per workgroup of the last kernel
-  unsigned* ticket;         // zero before the launch; left zero after it
+  uint64_t* mean_slots;     // one 64-bit (tag, partial) slot per workgroup of the last kernel
+  unsigned* ticket;         // counters zero before the launch and after it; epoch word
 };
 
 hipError_t launch_xent(const XentArgs& a, hipStream_t stream);
@@ -48,7 +49,7 @@ struct FusedArgs {
   int segments;           // vocab segments (workgroups per token block)
   float* seg_partials;    // segments * tokens (max, sum-exp) pairs
   float* target_logit;    // tokens fp32
-  float* mean_partials;
+  uint64_t* mean_slots;
   unsigned* ticket;
 };
 

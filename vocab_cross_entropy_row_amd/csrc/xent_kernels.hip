@@ -8,12 +8,13 @@
 // The work is one pass over HBM: every logit is read once with 16-byte loads
 // (4 fp32 or 8 bf16 per lane per load), consecutive lanes read consecutive
 // 16-byte chunks, and each lane folds what it loaded into a running
-// (max, sum-exp) state in fp32 (see lce_device.h).  Loads are issued in
-// batches of U chunks per lane before any arithmetic, so each wave keeps
-// U * 1 KiB in flight.
+// (max, sum-exp) state in fp32 (see lce_device.h).  Loads are buffer loads
+// issued in batches of U chunks per lane, double-buffered, so each wave keeps
+// up to 2 * U KiB in flight; the row's scalar loads (target logit, unaligned
+// edges) are issued right behind the first batch.
 //
 // Three layouts of work over rows:
-//   wave_rows   one wavefront per row, 4 rows per workgroup (short rows);
+//   wave_rows   one wavefront per row, 4 or 16 rows per workgroup (short rows);
 //   block_rows  one 256-thread workgroup per row; the 4 waves stream the row
 //               together and merge their states through LDS (long rows);
 //   split       S workgroups per row write (max, sum-exp) partials, and a
@@ -28,7 +29,7 @@
 
 namespace lce {
 
-static_assert(kTicketBytes == (kTicketGroups + 1) * kTicketStride * sizeof(unsigned),
+static_assert(kTicketBytes == (kTicketGroups + 2) * kTicketStride * sizeof(unsigned),
               "host scratch layout must match the device ticket layout");
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -42,6 +43,7 @@ struct Vec<float> {
   typedef f32x4 raw;
   __device__ __forceinline__ static raw neg_inf() { return (raw)(kNegInf); }
   __device__ __forceinline__ static float get(const raw& r, int e) { return r[e]; }
+  __device__ __forceinline__ static float get_again(const raw& r, int e) { return r[e]; }
   __device__ __forceinline__ static float scalar(const float* p) { return *p; }
 };
 template <>
@@ -51,6 +53,17 @@ struct Vec<uint16_t> {  // bf16 bit patterns, two per 32-bit word
   __device__ __forceinline__ static raw neg_inf() { return (raw)(0xff80ff80u); }  // bf16 -inf pairs
   __device__ __forceinline__ static float get(const raw& r, int e) {
     return (e & 1) ? bf16_hi(r[e >> 1]) : bf16_lo(r[e >> 1]);
+  }
+  // The same decode, opaque to common-subexpression elimination: the exp pass
+  // decodes again instead of keeping every decoded value of the max pass alive
+  // (one VALU op per element, against 32 VGPRs of a batch of 4 chunks).
+  __device__ __forceinline__ static float get_again(const raw& r, int e) {
+    uint32_t out;
+    if (e & 1)
+      asm volatile("v_and_b32 %0, 0xffff0000, %1" : "=v"(out) : "v"(r[e >> 1]));
+    else
+      asm volatile("v_lshlrev_b32 %0, 16, %1" : "=v"(out) : "v"(r[e >> 1]));
+    return __uint_as_float(out);
   }
   __device__ __forceinline__ static float scalar(const uint16_t* p) { return bf16_to_f32(*p); }
 };
@@ -72,14 +85,26 @@ __device__ __forceinline__ RowSplit row_split(const T* row, int vocab) {
   return {head, body / E, body % E};
 }
 
-// Fold a batch of loaded chunks into the running state.  Padding lanes hold
-// -inf, which contributes 2^-inf = 0.
-template <typename T, int U>
-__device__ __forceinline__ void fold_batch(Lse& st, const typename Vec<T>::raw (&v)[U]) {
+// Pairwise sum of per-chunk sums part[U0..U) (keeps the fp32 error small).
+template <int U, int U0>
+__device__ __forceinline__ float sum_parts(float (&part)[U]) {
+#pragma unroll
+  for (int w = 1; w < U - U0; w <<= 1)
+#pragma unroll
+    for (int u = U0; u + w < U; u += 2 * w) part[u] += part[u + w];
+  return part[U0];
+}
+
+// Two-pass fold of chunks [U0, U1) of a batch into the running state: the
+// batch maximum first, then the sum of exponentials against the new maximum.
+// Padding chunks hold -inf, which contributes 2^-inf = 0.
+template <typename T, int U, int U0, int U1>
+__device__ __forceinline__ void fold_two_pass(Lse& st, const typename Vec<T>::raw (&v)[U]) {
+  static_assert(0 <= U0 && U0 < U1 && U1 <= U, "chunk range");
   constexpr int E = Vec<T>::kElems;
   float bm = kNegInf;
 #pragma unroll
-  for (int u = 0; u < U; ++u)
+  for (int u = U0; u < U1; ++u)
 #pragma unroll
     for (int e = 0; e < E; ++e) bm = fmaxf(bm, Vec<T>::get(v[u], e));
   const float mn = fmaxf(st.m, bm);
@@ -87,19 +112,85 @@ __device__ __forceinline__ void fold_batch(Lse& st, const typename Vec<T>::raw (
   const float Mn = mn * kLog2e;
   float part[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
+  for (int u = U0; u < U1; ++u) {
     float acc = 0.0f;
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc += exp2_fast(__builtin_fmaf(Vec<T>::get(v[u], e), kLog2e, -Mn));
+    for (int e = 0; e < E; ++e) acc += exp2_fast(__builtin_fmaf(Vec<T>::get_again(v[u], e), kLog2e, -Mn));
     part[u] = acc;
   }
   // pairwise sum of the per-chunk sums keeps the fp32 error small
 #pragma unroll
-  for (int w = 1; w < U; w <<= 1)
+  for (int w = 1; w < U1 - U0; w <<= 1)
 #pragma unroll
-    for (int u = 0; u + w < U; u += 2 * w) part[u] += part[u + w];
-  st.s = st.s * lse_rescale(st.m, mn) + part[0];
+    for (int u = U0; u + w < U1; u += 2 * w) part[u] += part[u + w];
+  st.s = st.s * lse_rescale(st.m, mn) + part[U0];
   st.m = mn;
+}
+
+// One-pass fold of chunks [U0, U) against the running maximum, which must be
+// finite: each element is decoded once and feeds both the batch maximum and
+// its exponential 2^(z*L - fp32(m*L)).  If the batch raised the maximum, the
+// sum is rescaled to the new one afterwards, which is exact arithmetic on the
+// same terms; if it raised it so far (more than 64 in log2 units) that a term
+// may have overflowed, the batch's exponentials are taken again against the
+// new maximum.  Per element this is one decode, a third of a 3-input max, one
+// FMA, one exponential and one add: one decode less than the two-pass fold.
+template <typename T, int U, int U0>
+__device__ __forceinline__ void fold_one_pass(Lse& st, const typename Vec<T>::raw (&v)[U]) {
+  static_assert(0 <= U0 && U0 < U, "chunk range");
+  constexpr int E = Vec<T>::kElems;
+  const float M = st.m * kLog2e;
+  float bm = kNegInf;
+  float part[U];
+#pragma unroll
+  for (int u = U0; u < U; ++u) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float z = Vec<T>::get_again(v[u], e);
+      bm = fmaxf(bm, z);
+      acc += exp2_fast(__builtin_fmaf(z, kLog2e, -M));
+    }
+    part[u] = acc;
+  }
+  if (bm > st.m) {
+    if (bm * kLog2e - M > 64.0f) {
+      const float Mn = bm * kLog2e;
+#pragma unroll
+      for (int u = U0; u < U; ++u) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          acc += exp2_fast(__builtin_fmaf(Vec<T>::get_again(v[u], e), kLog2e, -Mn));
+        part[u] = acc;
+      }
+      st.s *= lse_rescale(st.m, bm);
+    } else {
+      st.s = (st.s + sum_parts<U, U0>(part)) * lse_rescale(st.m, bm);
+      st.m = bm;
+      return;
+    }
+    st.m = bm;
+  }
+  st.s += sum_parts<U, U0>(part);
+}
+
+// Fold a batch of loaded chunks into the running state.  A lane that has seen
+// no finite logit yet (always so in the first batch, FIRST) takes its maximum
+// from two passes over the first chunk, then folds the rest in one pass.
+template <typename T, int U, bool FIRST = false>
+__device__ __forceinline__ void fold_batch(Lse& st, const typename Vec<T>::raw (&v)[U]) {
+  if (FIRST || st.m == kNegInf) {
+    fold_two_pass<T, U, 0, 1>(st, v);
+    if constexpr (U > 1) {
+      if (st.m == kNegInf)
+        fold_two_pass<T, U, 1, U>(st, v);  // nothing but -inf so far
+      else
+        fold_one_pass<T, U, 1>(st, v);
+    }
+  } else {
+    fold_one_pass<T, U, 0>(st, v);
+  }
 }
 
 // Fold one scalar (or -inf) into the state.
@@ -110,39 +201,134 @@ __device__ __forceinline__ void fold_one(Lse& st, float z) {
   st.m = mn;
 }
 
-// Stream chunks [c0, c1) of the aligned body with stride `step` starting at
-// chunk `c0 + first`, U chunks per lane per batch.
+// Cache policy of the streaming loads: nt (each logit is read once).
+constexpr int kStreamPolicy = 2;
+
+// Load chunks c + u * step (u < U) through buffer resource `rs`; chunks at or
+// past the resource's end read no memory and come back as zero.
 template <typename T, int U>
-__device__ __forceinline__ void stream_chunks(Lse& st, const typename Vec<T>::raw* body, int c0,
-                                              int c1, int first, int step) {
+__device__ __forceinline__ void load_batch(typename Vec<T>::raw (&v)[U], __amdgpu_buffer_rsrc_t rs,
+                                           int c, int step) {
   typedef typename Vec<T>::raw raw;
-  for (int base = c0 + first; base < c1; base += step * U) {
-    raw v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = base + u * step;
-      v[u] = (c < c1) ? __builtin_nontemporal_load(body + c) : Vec<T>::neg_inf();
-    }
-    fold_batch<T, U>(st, v);
+  for (int u = 0; u < U; ++u)
+    v[u] = (raw)__builtin_amdgcn_raw_buffer_load_b128(rs, (c + u * step) * 16, 0, kStreamPolicy);
+}
+
+// Chunks at or past chunk n become -inf, which folds as nothing.
+template <typename T, int U>
+__device__ __forceinline__ void mask_past(typename Vec<T>::raw (&v)[U], int c, int n, int step) {
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (c + u * step >= n) v[u] = Vec<T>::neg_inf();
+}
+
+// Stream chunks [c0, c1) of the aligned body: lane `first` of a group of
+// `step` lanes takes chunks c0 + first + k * step, U per batch.  c0, c1 and
+// step are uniform over the group.  Two batches live in registers and the
+// next batch's loads are issued before the current one is folded, so up to
+// 2 * U chunks per lane are in flight.  Every load is unconditional: loads
+// past c1 (the lanes beyond a ragged end, and the batch after the last one)
+// read nothing, and only the last batch of a ragged range is masked.
+// `extra()` is called once, right after the first loads are issued (also
+// for an empty range): the row's few scalar loads go there, so that their
+// latency overlaps the stream instead of adding to it.
+// The caller keeps (c1 - c0) * 16 below 2^31.
+template <typename T, int U, typename Extra>
+__device__ __forceinline__ void stream_chunks(Lse& st, const typename Vec<T>::raw* body, int c0,
+                                              int c1, int first, int step, Extra&& extra) {
+  typedef typename Vec<T>::raw raw;
+  const int n = wave_uniform(c1 - c0);
+  if (n <= 0) {
+    extra();
+    return;
+  }
+  const int S = step * U;
+  const int last = wave_uniform((n - 1) / S);  // index of the last batch
+  const bool ragged = (n % S) != 0;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(body + c0, (uint32_t)n * 16u);
+  int c = first;
+  raw a[U], b[U];
+  load_batch<T, U>(a, rs, c, step);
+  __builtin_amdgcn_sched_barrier(0);
+  extra();
+  for (int k = 0;; k += 2) {
+    load_batch<T, U>(b, rs, c + S, step);
+    if (ragged && k == last) mask_past<T, U>(a, c, n, step);
+    fold_batch<T, U>(st, a);
+    if (k == last) break;
+    c += S;
+    load_batch<T, U>(a, rs, c + S, step);
+    if (ragged && k + 1 == last) mask_past<T, U>(b, c, n, step);
+    fold_batch<T, U>(st, b);
+    if (k + 1 == last) break;
+    c += S;
   }
 }
 
-// Scalar head and tail elements of a row, one per lane (at most 2 * (E - 1)).
-template <typename T>
-__device__ __forceinline__ void fold_edges(Lse& st, const T* row, const RowSplit& rs, int vocab,
-                                           int idx) {
-  const int edges = rs.head + rs.tail;
-  if (idx < edges) {
-    const int j = (idx < rs.head) ? idx : (vocab - rs.tail + (idx - rs.head));
-    fold_one(st, Vec<T>::scalar(row + j));
+// The same for ranges of at most MAXB batches, fully unrolled by template
+// recursion (batch K is a compile-time constant, so the two register batches
+// are never indexed at run time): with no loop back edge every fold waits for
+// exactly its own batch (a loop header makes the compiler drain all loads).
+struct ShortRange {
+  __amdgpu_buffer_rsrc_t rs;
+  int first, step, n, last;
+  bool ragged;
+};
+
+template <typename T, int U, int MAXB, int K, typename Extra>
+__device__ __forceinline__ void short_step(Lse& st, typename Vec<T>::raw (&cur)[U],
+                                           typename Vec<T>::raw (&nxt)[U], const ShortRange& r,
+                                           Extra& extra) {
+  const int c = r.first + K * r.step * U;
+  if constexpr (K + 1 < MAXB) load_batch<T, U>(nxt, r.rs, c + r.step * U, r.step);
+  if constexpr (K == 0) {
+    __builtin_amdgcn_sched_barrier(0);
+    extra();
+  }
+  if (r.ragged && K == r.last) mask_past<T, U>(cur, c, r.n, r.step);
+  fold_batch<T, U, K == 0>(st, cur);
+  if constexpr (K + 1 < MAXB) {
+    if (K != r.last) short_step<T, U, MAXB, K + 1>(st, nxt, cur, r, extra);
   }
 }
 
-// loss = ln(sum e^z) - z_t, or NaN when the target is out of range.  `t` is uniform.
-template <typename T>
-__device__ __forceinline__ float row_loss(const Lse& st, const T* row, int64_t t, int vocab) {
-  if (t < 0 || t >= (int64_t)vocab) return __builtin_nanf("");
-  return lse_minus(st, Vec<T>::scalar(row + t));
+template <typename T, int U, int MAXB, typename Extra>
+__device__ __forceinline__ void stream_chunks_short(Lse& st, const typename Vec<T>::raw* body,
+                                                    int c0, int c1, int first, int step,
+                                                    Extra&& extra) {
+  typedef typename Vec<T>::raw raw;
+  const int n = wave_uniform(c1 - c0);
+  if (n <= 0) {
+    extra();
+    return;
+  }
+  const int S = step * U;
+  const ShortRange r{make_rsrc(body + c0, (uint32_t)n * 16u), first, step, n,
+                     wave_uniform((n - 1) / S), (n % S) != 0};
+  raw a[U], b[U];
+  load_batch<T, U>(a, r.rs, first, step);
+  short_step<T, U, MAXB, 0>(st, a, b, r, extra);
+}
+
+// Index of the scalar head or tail element that lane `idx` folds when
+// idx < head + tail; any in-row index (0) otherwise, so the load is always valid.
+__device__ __forceinline__ int edge_index(const RowSplit& rs, int vocab, int idx) {
+  if (idx >= rs.head + rs.tail) return 0;
+  return (idx < rs.head) ? idx : (vocab - rs.tail + (idx - rs.head));
+}
+
+// Target index usable for a load: t itself when valid, else 0 (then the loss is NaN).
+__device__ __forceinline__ int64_t safe_target(int64_t t, int vocab) {
+  return (t >= 0 && t < (int64_t)vocab) ? t : 0;
+}
+
+// The target index, made opaque where this is called: code that uses the
+// result cannot be hoisted above it, so the wait for the target's scalar load
+// lands behind the first batch of logit loads instead of in front of them.
+__device__ __forceinline__ int64_t target_here(int64_t t) {
+  __asm__ volatile("" : "+s"(t));
+  return t;
 }
 
 // ------------------------------------------------------------ one wave per row
@@ -151,7 +337,7 @@ __device__ __forceinline__ float row_loss(const Lse& st, const T* row, int64_t t
 template <typename T, int U, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void xent_wave_rows_kernel(
     const T* __restrict__ logits, int64_t tokens, int vocab, const int64_t* __restrict__ target,
-    float* __restrict__ out, float* __restrict__ partials, unsigned* __restrict__ ticket,
+    float* __restrict__ out, uint64_t* __restrict__ slots, unsigned* __restrict__ ticket,
     int reduce_mean) {
   const int lane = threadIdx.x & 63;
   const int wave = wave_uniform(threadIdx.x >> 6);
@@ -163,11 +349,21 @@ __global__ __launch_bounds__(64 * WAVES) void xent_wave_rows_kernel(
     const RowSplit rs = row_split(rp, vocab);
     const typename Vec<T>::raw* body =
         reinterpret_cast<const typename Vec<T>::raw*>(rp + rs.head);
+    float edge = 0.0f, zt = 0.0f;
+    int64_t tt = -1;
+    auto extra = [&]() {
+      edge = Vec<T>::scalar(rp + edge_index(rs, vocab, lane));
+      tt = target_here(t);
+      zt = Vec<T>::scalar(rp + safe_target(tt, vocab));
+    };
     Lse st = lse_empty();
-    fold_edges(st, rp, rs, vocab, lane);
-    stream_chunks<T, U>(st, body, 0, rs.nvec, lane, 64);
+    if (wave_uniform(rs.nvec) <= 64 * 32)  // at most 32 chunks per lane
+      stream_chunks_short<T, U, 32 / U>(st, body, 0, rs.nvec, lane, 64, extra);
+    else
+      stream_chunks<T, U>(st, body, 0, rs.nvec, lane, 64, extra);
+    if (lane < rs.head + rs.tail) fold_one(st, edge);
     const Lse r = wave_lse(st);
-    loss = row_loss(r, rp, t, vocab);
+    loss = (tt >= 0 && tt < vocab) ? lse_minus(r, zt) : __builtin_nanf("");
     if (!reduce_mean && lane == 0) out[row] = loss;
   }
   if (reduce_mean) {
@@ -177,7 +373,7 @@ __global__ __launch_bounds__(64 * WAVES) void xent_wave_rows_kernel(
     float bsum = 0.0f;
     if (threadIdx.x == 0)
       for (int w = 0; w < WAVES; ++w) bsum += wl[w];
-    finish_mean(bsum, partials, ticket, out, tokens);
+    finish_mean(bsum, slots, ticket, out, tokens);
   }
 }
 
@@ -206,22 +402,29 @@ __device__ __forceinline__ Lse block_lse(Lse st) {
 template <typename T, int U>
 __global__ __launch_bounds__(kRowThreads) void xent_block_rows_kernel(
     const T* __restrict__ logits, int64_t tokens, int vocab, const int64_t* __restrict__ target,
-    float* __restrict__ out, float* __restrict__ partials, unsigned* __restrict__ ticket,
+    float* __restrict__ out, uint64_t* __restrict__ slots, unsigned* __restrict__ ticket,
     int reduce_mean) {
   const int64_t row = blockIdx.x;
   const T* rp = logits + row * (int64_t)vocab;
   const int64_t t = target[row];
   const RowSplit rs = row_split(rp, vocab);
   const typename Vec<T>::raw* body = reinterpret_cast<const typename Vec<T>::raw*>(rp + rs.head);
+  float edge = 0.0f, zt = 0.0f;
+  int64_t tt = -1;
+  auto extra = [&]() {
+    edge = Vec<T>::scalar(rp + edge_index(rs, vocab, threadIdx.x));
+    tt = target_here(t);
+    zt = Vec<T>::scalar(rp + safe_target(tt, vocab));
+  };
   Lse st = lse_empty();
-  fold_edges(st, rp, rs, vocab, threadIdx.x);
-  stream_chunks<T, U>(st, body, 0, rs.nvec, threadIdx.x, kRowThreads);
+  stream_chunks<T, U>(st, body, 0, rs.nvec, threadIdx.x, kRowThreads, extra);
+  if ((int)threadIdx.x < rs.head + rs.tail) fold_one(st, edge);
   const Lse r = block_lse(st);
-  const float loss = row_loss(r, rp, t, vocab);
+  const float loss = (tt >= 0 && tt < vocab) ? lse_minus(r, zt) : __builtin_nanf("");
   if (!reduce_mean) {
     if (threadIdx.x == 0) out[row] = loss;
   } else {
-    finish_mean(loss, partials, ticket, out, tokens);
+    finish_mean(loss, slots, ticket, out, tokens);
   }
 }
 
@@ -237,12 +440,14 @@ __global__ __launch_bounds__(kRowThreads) void xent_split_partial_kernel(
   const T* rp = logits + row * (int64_t)vocab;
   const RowSplit rs = row_split(rp, vocab);
   const typename Vec<T>::raw* body = reinterpret_cast<const typename Vec<T>::raw*>(rp + rs.head);
+  float edge = 0.0f;
+  auto extra = [&]() { edge = Vec<T>::scalar(rp + edge_index(rs, vocab, threadIdx.x)); };
   Lse st = lse_empty();
-  if (s == 0) fold_edges(st, rp, rs, vocab, threadIdx.x);
   const int c0 = s * chunks_per_slice;
   int c1 = c0 + chunks_per_slice;
   c1 = c1 < rs.nvec ? c1 : rs.nvec;
-  stream_chunks<T, U>(st, body, c0, c1, threadIdx.x, kRowThreads);
+  stream_chunks<T, U>(st, body, c0, c1, threadIdx.x, kRowThreads, extra);
+  if (s == 0 && (int)threadIdx.x < rs.head + rs.tail) fold_one(st, edge);
   const Lse r = block_lse(st);
   if (threadIdx.x == 0) part[row * S + s] = make_float2(r.m, r.s);
 }
@@ -253,7 +458,7 @@ template <typename T>
 __global__ __launch_bounds__(kRowThreads) void xent_split_merge_kernel(
     const T* __restrict__ logits, int64_t tokens, int vocab, int S,
     const float2* __restrict__ part, const int64_t* __restrict__ target, float* __restrict__ out,
-    float* __restrict__ partials, unsigned* __restrict__ ticket, int reduce_mean) {
+    uint64_t* __restrict__ slots, unsigned* __restrict__ ticket, int reduce_mean) {
   constexpr int kWaves = kRowThreads / 64;
   const int lane = threadIdx.x & 63;
   const int wave = wave_uniform(threadIdx.x >> 6);
@@ -267,7 +472,8 @@ __global__ __launch_bounds__(kRowThreads) void xent_split_merge_kernel(
     }
     const Lse r = wave_lse(st);
     const T* rp = logits + row * (int64_t)vocab;
-    loss = row_loss(r, rp, target[row], vocab);
+    const int64_t t = target[row];
+    loss = (t >= 0 && t < vocab) ? lse_minus(r, Vec<T>::scalar(rp + t)) : __builtin_nanf("");
     if (!reduce_mean && lane == 0) out[row] = loss;
   }
   if (reduce_mean) {
@@ -277,7 +483,7 @@ __global__ __launch_bounds__(kRowThreads) void xent_split_merge_kernel(
     float bsum = 0.0f;
     if (threadIdx.x == 0)
       for (int w = 0; w < kWaves; ++w) bsum += wl[w];
-    finish_mean(bsum, partials, ticket, out, tokens);
+    finish_mean(bsum, slots, ticket, out, tokens);
   }
 }
 
@@ -298,7 +504,7 @@ static hipError_t launch_wave_rows_w(const XentArgs& a, hipStream_t st) {
   const int64_t blocks = (a.tokens + WAVES - 1) / WAVES;
   hipLaunchKernelGGL((xent_wave_rows_kernel<T, U, WAVES>), dim3((unsigned)blocks), dim3(64 * WAVES),
                      0, st, (const T*)a.logits, a.tokens, (int)a.vocab, a.target, a.out,
-                     a.mean_partials, a.ticket, a.reduce_mean);
+                     a.mean_slots, a.ticket, a.reduce_mean);
   return hipGetLastError();
 }
 
@@ -314,7 +520,7 @@ template <typename T, int U>
 static hipError_t launch_block_rows(const XentArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((xent_block_rows_kernel<T, U>), dim3((unsigned)a.tokens), dim3(kRowThreads), 0,
                      st, (const T*)a.logits, a.tokens, (int)a.vocab, a.target, a.out,
-                     a.mean_partials, a.ticket, a.reduce_mean);
+                     a.mean_slots, a.ticket, a.reduce_mean);
   return hipGetLastError();
 }
 
@@ -328,7 +534,7 @@ static hipError_t launch_split(const XentArgs& a, hipStream_t st) {
   const int64_t blocks = (a.tokens + kRowThreads / 64 - 1) / (kRowThreads / 64);
   hipLaunchKernelGGL((xent_split_merge_kernel<T>), dim3((unsigned)blocks), dim3(kRowThreads), 0, st,
                      (const T*)a.logits, a.tokens, (int)a.vocab, a.splits,
-                     (const float2*)a.split_partials, a.target, a.out, a.mean_partials, a.ticket,
+                     (const float2*)a.split_partials, a.target, a.out, a.mean_slots, a.ticket,
                      a.reduce_mean);
   return hipGetLastError();
 }
