@@ -151,6 +151,66 @@ def test_invalid_targets_and_nan_logits():
     assert math.isnan(gpu_xent(z, t, "mean", "f32")[0])
 
 
+def _spiky_rows(vocab):
+    """Rows that exercise the running maximum: a rising ramp, a falling ramp, single
+    spikes far above the rest (more than 44 nats, past the one-pass fold's overflow
+    guard) and moderately above it (rescale only) at the first, an interior and the last
+    element, -inf entries, and rows that are -inf except at one or two elements."""
+    rows = 14
+    z = rand_logits(11, rows, vocab, "f32")
+    ramp = np.linspace(0.0, 30.0, vocab, dtype=np.float32)
+    z[0] += ramp
+    z[1] -= ramp
+    for r, pos, h in ((2, 0, 200.0), (3, 7, 200.0), (4, vocab // 2, 200.0), (5, vocab - 1, 200.0),
+                      (6, 8 * 64 * 8, 60.0), (7, vocab // 3, 25.0), (8, 5 * vocab // 7, 300.0)):
+        z[r, min(pos, vocab - 1)] += h
+    z[8, vocab // 5] += 150.0
+    z[9, ::3] = -np.inf
+    z[10, :] = -np.inf
+    z[10, vocab // 2] = 3.0
+    z[11, :] = -np.inf
+    z[11, [1, vocab - 2]] = (-5.0, 7.0)
+    z[12, vocab // 4:] -= 100.0
+    z[13] *= 40.0
+    t = lce_synth.targets(12, rows, vocab)
+    t[9] = 1  # a finite entry (every third one is -inf)
+    t[10] = vocab // 2
+    t[11] = vocab - 2
+    return z, t
+
+
+@pytest.mark.parametrize("path", ["auto", "wave", "block", "split"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("vocab", [4099, 9000])
+def test_running_maximum_edge_rows(path, dtype, vocab):
+    z, t = _spiky_rows(vocab)
+    if dtype == "bf16":
+        z = lce_synth.f32_to_bf16_bits(z)
+    env = {} if path == "auto" else {"LCE_PATH": path}
+    with forced_env(**env):
+        check_xent(z, t, dtype, f"{path} {dtype} {vocab}")
+        got = gpu_xent(z, t, "none", dtype)
+    assert abs(got[10]) <= TOK_ABS  # one finite logit, the target: loss 0
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_infinite_logits(dtype):
+    """+inf anywhere in a row makes that row's loss NaN, and a row of -inf only is NaN,
+    as in the oracle (both evaluate the max-shifted form)."""
+    rows, vocab = 6, 3000
+    z = rand_logits(13, rows, vocab, "f32")
+    z[0, 0] = np.inf
+    z[1, 1234] = np.inf
+    z[2, vocab - 1] = np.inf
+    z[3, :] = -np.inf
+    t = lce_synth.targets(14, rows, vocab)
+    if dtype == "bf16":
+        z = lce_synth.f32_to_bf16_bits(z)
+    check_xent(z, t, dtype, "inf")
+    got = gpu_xent(z, t, "none", dtype)
+    assert np.isnan(got[:4]).all() and np.isfinite(got[4:]).all()
+
+
 def test_zero_tokens():
     z = torch.empty((0, 16), device="cuda")
     t = torch.empty((0,), dtype=torch.int64, device="cuda")

@@ -71,6 +71,17 @@ __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r & 7) ^ ((r >> 
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// Workgroup barrier ordering LDS accesses only.  __syncthreads() also orders
+// global memory, which makes the compiler drain every outstanding load
+// (vmcnt(0)) at the barrier, including the slab DMAs meant to stay in flight
+// across it; their completion is waited for explicitly (wait_vmcnt).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
 // s_waitcnt vmcnt(N) with the other counters left free (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -173,24 +184,15 @@ __global__ __launch_bounds__(TL::kThreads) void fused_xent_partial_kernel(
   // 8g + (l >> 3), so it loads the logical chunk the swizzle maps there.
   // Offsets are relative to the tile's W or x block; the slab's hidden offset
   // is the uniform soffset.
+  // With an even number of waves, the swizzled chunk of every row a lane fills
+  // is the same ((r >> 3) & 1 is the wave's parity for all its DMAs), so DMA i
+  // differs from DMA 0 only by 8 * kWaves rows.
+  static_assert(TL::kWaves % 2 == 0, "one swizzled chunk per lane");
   const uint32_t row_bytes = (uint32_t)hidden * 2u;
-  uint32_t voff_w[TL::kWPerWave], voff_x[TL::kXPerWave];
-  uint32_t kch_w[TL::kWPerWave], kch_x[TL::kXPerWave];
-#pragma unroll
-  for (int i = 0; i < TL::kWPerWave; ++i) {
-    const int r = 8 * (wave + TL::kWaves * i) + (lane >> 3);
-    const int c = swz(r, lane & 7);
-    voff_w[i] = (uint32_t)r * row_bytes + (uint32_t)c * 16u;
-    kch_w[i] = (uint32_t)c * 8u;
-  }
-#pragma unroll
-  for (int i = 0; i < TL::kXPerWave; ++i) {
-    const int r = 8 * (wave + TL::kWaves * i) + (lane >> 3);
-    const int c = swz(r, lane & 7);
-    voff_x[i] = (uint32_t)r * row_bytes + (uint32_t)c * 16u;
-    kch_x[i] = (uint32_t)c * 8u;
-  }
-
+  const int r0 = 8 * wave + (lane >> 3);
+  const uint32_t kch = (uint32_t)swz(r0, lane & 7) * 8u;  // hidden offset of the lane's chunk
+  const uint32_t voff0 = (uint32_t)r0 * row_bytes + kch * 2u;
+  const uint32_t voff_step = 8u * TL::kWaves * row_bytes;
   Lse st[BTB];
 #pragma unroll
   for (int j = 0; j < BTB; ++j) st[j] = lse_empty();
@@ -211,14 +213,14 @@ __global__ __launch_bounds__(TL::kThreads) void fused_xent_partial_kernel(
   // `tail` marks the last slab of a hidden size that is not a multiple of 64:
   // chunks past the end read zeros.
   auto issue_w = [&](int i, __amdgpu_buffer_rsrc_t wr, uint32_t k0, bool tail, uint16_t* stage) {
-    uint32_t vo = voff_w[i];
-    if (tail && k0 + kch_w[i] >= (uint32_t)hidden) vo = 0x7ffffff0u;
+    uint32_t vo = voff0 + (uint32_t)i * voff_step;
+    if (tail && k0 + kch >= (uint32_t)hidden) vo = 0x7ffffff0u;
     lds_ptr_t dst = (lds_ptr_t)(stage + (wave + TL::kWaves * i) * 8 * TL::kBK);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, vo, k0 * 2u, 0, 0);
   };
   auto issue_x = [&](int i, uint32_t k0, bool tail, uint16_t* stage) {
-    uint32_t vo = voff_x[i];
-    if (tail && k0 + kch_x[i] >= (uint32_t)hidden) vo = 0x7ffffff0u;
+    uint32_t vo = voff0 + (uint32_t)i * voff_step;
+    if (tail && k0 + kch >= (uint32_t)hidden) vo = 0x7ffffff0u;
     lds_ptr_t dst = (lds_ptr_t)(stage + (wave + TL::kWaves * i) * 8 * TL::kBK);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, dst, 16, vo, k0 * 2u, 0, 0);
   };
@@ -341,7 +343,7 @@ __global__ __launch_bounds__(TL::kThreads) void fused_xent_partial_kernel(
       // The next slab's x and W have landed for every wave (only the newest W
       // slab may still be in flight); every read of this slab is done.
       if (w_now) wait_vmcnt<TL::kWPerWave>(); else wait_vmcnt<0>();
-      __syncthreads();
+      lds_barrier();
       const int wq1 = (wq + 1 == TL::kWStages) ? 0 : wq + 1;
       const int xq1 = (xq + 1 == TL::kXStages) ? 0 : xq + 1;
       const bool x_now = x_left > 0;
@@ -406,6 +408,8 @@ __global__ __launch_bounds__(TL::kThreads) void fused_xent_partial_kernel(
 
 // One thread per token: merge its `segments` partials in segment order
 // (consecutive threads read consecutive tokens of a segment), subtract z_target.
+// The partials are loaded eight segments at a time, so the loads of a group
+// are in flight together instead of one memory latency per segment.
 __global__ __launch_bounds__(kRowThreads) void fused_xent_merge_kernel(
     int64_t tokens, int64_t vocab, int segments, const float2* __restrict__ part,
     const float* __restrict__ zt, const int64_t* __restrict__ target, float* __restrict__ out,
@@ -413,13 +417,19 @@ __global__ __launch_bounds__(kRowThreads) void fused_xent_merge_kernel(
   const int64_t row = (int64_t)blockIdx.x * kRowThreads + threadIdx.x;
   float loss = 0.0f;
   if (row < tokens) {
-    Lse st = lse_empty();
-    for (int s = 0; s < segments; ++s) {
-      const float2 p = part[(int64_t)s * tokens + row];
-      st = lse_merge(st, Lse{p.x, p.y});
-    }
     const int64_t t = target[row];
-    loss = (t >= 0 && t < vocab) ? lse_minus(st, zt[row]) : __builtin_nanf("");
+    const float z = zt[row];
+    constexpr int kGroup = 8;
+    Lse st = lse_empty();
+    for (int s0 = 0; s0 < segments; s0 += kGroup) {
+      float2 p[kGroup];
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j)
+        p[j] = (s0 + j < segments) ? part[(int64_t)(s0 + j) * tokens + row] : make_float2(kNegInf, 0.0f);
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j) st = lse_merge(st, Lse{p[j].x, p[j].y});
+    }
+    loss = (t >= 0 && t < vocab) ? lse_minus(st, z) : __builtin_nanf("");
     if (!reduce_mean) out[row] = loss;
   }
   if (reduce_mean) {
