@@ -64,6 +64,13 @@ def _load():
                                          ctypes.c_int]
         lib.oracle_mean.restype = ctypes.c_double
         lib.oracle_mean.argtypes = [ctypes.c_void_p, ctypes.c_int64]
+        lib.oracle_xent_partial.restype = ctypes.c_int
+        lib.oracle_xent_partial.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                            ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_int]
+        lib.oracle_xent_merge.restype = ctypes.c_int
+        lib.oracle_xent_merge.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         lib.oracle_default_threads.restype = ctypes.c_int
         lib.oracle_default_threads.argtypes = []
         _lib = lib
@@ -117,6 +124,43 @@ def xent_rows(logits: np.ndarray, target: np.ndarray, dtype: str | None = None,
     if rc != 0:
         raise ValueError("oracle: bad argument")
     return out.reshape(lead)
+
+
+def xent_partial(logits: np.ndarray, target: np.ndarray, vocab_start: int,
+                 dtype: str | None = None, nthreads: int | None = None) -> np.ndarray:
+    """Statistics of one vocab shard, ``[rows, 3]`` fp64: (m, s, zt) per row.
+
+    ``logits`` is ``[rows, shard]`` holding full-vocab columns
+    ``[vocab_start, vocab_start + shard)``; ``target`` indexes the full vocab.
+    m = max, s = sum exp(z - m), zt = the target's logit if this shard holds it,
+    else NaN ("Vocab-parallel cross-entropy, Megatron layout": description).
+    """
+    dt = _dtype_of(logits, dtype)
+    z = np.ascontiguousarray(logits)
+    t = np.ascontiguousarray(target, dtype=np.int64).reshape(-1)
+    if z.ndim != 2 or t.size != z.shape[0]:
+        raise ValueError("oracle: logits must be [rows, shard] and target [rows]")
+    out = np.empty((z.shape[0], 3), dtype=np.float64)
+    rc = _load().oracle_xent_partial(z.ctypes.data, _DTYPES[dt], z.shape[0], z.shape[1],
+                                     int(vocab_start), t.ctypes.data, out.ctypes.data,
+                                     int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle: bad argument")
+    return out
+
+
+def xent_merge(partials: np.ndarray, target: np.ndarray, vocab: int) -> np.ndarray:
+    """Per-token losses from ``[shards, rows, 3]`` shard statistics (fp64)."""
+    q = np.ascontiguousarray(partials, dtype=np.float64)
+    t = np.ascontiguousarray(target, dtype=np.int64).reshape(-1)
+    if q.ndim != 3 or q.shape[2] != 3 or q.shape[1] != t.size:
+        raise ValueError("oracle: partials must be [shards, rows, 3]")
+    out = np.empty(t.size, dtype=np.float64)
+    rc = _load().oracle_xent_merge(q.ctypes.data, q.shape[0], q.shape[1], t.ctypes.data,
+                                   int(vocab), out.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle: bad argument")
+    return out
 
 
 def mean(losses: np.ndarray) -> float:

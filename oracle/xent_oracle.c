@@ -112,6 +112,96 @@ int oracle_xent_rows(const void* logits, int dtype, int64_t rows, int64_t vocab,
     return 0;
 }
 
+/*
+ * Shard statistics for the vocab-parallel layout (KernelIndex "Vocab-parallel
+ * cross-entropy, Megatron layout", description: the vocab axis is split across
+ * devices; the page itself measures one device).  `logits` holds, for every
+ * row, the `shard` consecutive vocab columns [v0, v0 + shard) of the full
+ * vocab.  For each row i, written to out[3i .. 3i+2]:
+ *
+ *     m_i  = max_j z_ij
+ *     s_i  = sum_j exp(z_ij - m_i)          (so ln sum_j exp(z_ij) = m_i + ln s_i)
+ *     zt_i = z_{i, t_i - v0}  if v0 <= t_i < v0 + shard, else NaN (not this shard's)
+ *
+ * A shard row of -inf only has sum_j exp(z_ij) = 0, written as (-inf, 0).
+ *
+ * Same two plain passes as oracle_xent_rows.  Returns 0, or -1 on a bad argument.
+ */
+int oracle_xent_partial(const void* logits, int dtype, int64_t rows, int64_t shard, int64_t v0,
+                        const int64_t* target, double* out, int nthreads)
+{
+    if (rows < 0 || shard < 1 || v0 < 0 || (rows > 0 && (!logits || !target || !out)))
+        return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16 && dtype != ORACLE_F64)
+        return -1;
+    if (nthreads < 1)
+        nthreads = 1;
+
+#pragma omp parallel num_threads(nthreads)
+    {
+        double* z = (double*)malloc((size_t)shard * sizeof(double));
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t i = 0; i < rows; ++i) {
+            if (!z) {
+                out[3 * i] = out[3 * i + 1] = out[3 * i + 2] = NAN;
+                continue;
+            }
+            decode_row(logits, dtype, i, shard, z);
+            double m = -INFINITY;
+            for (int64_t j = 0; j < shard; ++j)
+                if (z[j] > m)
+                    m = z[j];
+            double s = 0.0;
+            if (m != -INFINITY)
+                for (int64_t j = 0; j < shard; ++j)
+                    s += exp(z[j] - m);
+            const int64_t t = target[i];
+            out[3 * i] = m;
+            out[3 * i + 1] = s;
+            out[3 * i + 2] = (t >= v0 && t < v0 + shard) ? z[t - v0] : NAN;
+        }
+        free(z);
+    }
+    return 0;
+}
+
+/*
+ * Loss of each row from the statistics of the `shards` vocab shards that
+ * together cover the row (partials[p][i][0..2] = (m, s, zt) as above, shards
+ * in vocab order):
+ *
+ *     ln sum_j exp(z_ij) = M + ln( sum_p s_pi * exp(m_pi - M) ),  M = max_p m_pi
+ *     loss_i = that - zt_i
+ *
+ * where zt_i is the target logit reported by the one shard that holds the
+ * target.  NaN if t_i is outside [0, vocab) or no shard reports it.
+ */
+int oracle_xent_merge(const double* partials, int64_t shards, int64_t rows,
+                      const int64_t* target, int64_t vocab, double* loss)
+{
+    if (shards < 1 || rows < 0 || vocab < 1 || (rows > 0 && (!partials || !target || !loss)))
+        return -1;
+    for (int64_t i = 0; i < rows; ++i) {
+        double M = -INFINITY;
+        for (int64_t p = 0; p < shards; ++p) {
+            const double m = partials[3 * (p * rows + i)];
+            if (m > M)
+                M = m;
+        }
+        double s = 0.0, zt = NAN;
+        for (int64_t p = 0; p < shards; ++p) {
+            const double* q = partials + 3 * (p * rows + i);
+            if (q[0] != -INFINITY) /* a shard of -inf only adds nothing */
+                s += q[1] * exp(q[0] - M);
+            if (!isnan(q[2]))
+                zt = q[2];
+        }
+        const int64_t t = target[i];
+        loss[i] = (t < 0 || t >= vocab) ? NAN : M + log(s) - zt;
+    }
+    return 0;
+}
+
 /* Mean of n per-token losses, summed in index order.  n == 0 gives 0/0 = NaN. */
 double oracle_mean(const double* loss, int64_t n)
 {

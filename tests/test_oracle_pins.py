@@ -263,3 +263,97 @@ def test_fused_workload_statistics(oracle_mod):
     t = lce_synth.targets(77, 16, 8192)
     got = oracle_mod.fused_linear_xent(x, head, t, "mean")
     assert got == pytest.approx(LN(8192) + 4096 * 0.02 ** 2 / 2, abs=0.1)
+
+
+# ---------------------------------------------------------------- vocab shards
+
+def _shard_bounds(vocab, shards, rng):
+    """Uneven split of [0, vocab) into `shards` non-empty consecutive ranges."""
+    cuts = np.sort(rng.choice(np.arange(1, vocab), size=shards - 1, replace=False)) if shards > 1 else []
+    edges = [0, *[int(c) for c in cuts], vocab]
+    return list(zip(edges[:-1], edges[1:]))
+
+
+def test_partial_uniform_shard(oracle_mod):
+    z = np.full((3, 50), 2.5)
+    t = np.array([10, 70, 59])
+    q = oracle_mod.xent_partial(z, t, vocab_start=10)  # columns [10, 60)
+    assert np.all(q[:, 0] == 2.5) and np.allclose(q[:, 1], 50.0, rtol=1e-15)
+    assert q[0, 2] == 2.5 and math.isnan(q[1, 2]) and q[2, 2] == 2.5
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_partial_brute_force_tiny(oracle_mod, seed):
+    """m is the exact shard maximum, m + ln s is the shard's log-sum-exp at 40 digits,
+    and zt is the target's logit exactly when this shard holds the target."""
+    rng = _rng(300 + seed)
+    rows, shard, v0 = int(rng.integers(1, 7)), int(rng.integers(1, 13)), int(rng.integers(0, 20))
+    z = rng.uniform(-30, 30, (rows, shard))
+    t = rng.integers(0, v0 + shard + 5, rows)
+    q = oracle_mod.xent_partial(z, t, vocab_start=v0)
+    getcontext().prec = 40
+    for i in range(rows):
+        lse = float(sum(Decimal(float(v)).exp() for v in z[i]).ln())
+        assert q[i, 0] == z[i].max()
+        assert q[i, 0] + math.log(q[i, 1]) == pytest.approx(lse, abs=1e-13)
+        if v0 <= t[i] < v0 + shard:
+            assert q[i, 2] == z[i, t[i] - v0]
+        else:
+            assert math.isnan(q[i, 2])
+
+
+def test_partial_matches_library_logsumexp(oracle_mod):
+    torch = pytest.importorskip("torch")
+    rng = _rng(11)
+    z = rng.normal(scale=4.0, size=(40, 3000))
+    q = oracle_mod.xent_partial(z, np.zeros(40, dtype=np.int64), vocab_start=5)
+    ref = torch.logsumexp(torch.from_numpy(z), dim=1).numpy()
+    assert np.allclose(q[:, 0] + np.log(q[:, 1]), ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("shards", [1, 2, 3, 7])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f64"])
+def test_shard_merge_equals_whole_row(oracle_mod, shards, dtype):
+    """Statistics of uneven vocab shards, merged, give the whole-row loss (a different
+    computation: per-shard maxima and sums, then one rescaled sum)."""
+    rng = _rng(400 + shards)
+    rows, vocab = 33, 997
+    f = rng.normal(scale=3.0, size=(rows, vocab)).astype(np.float32)
+    z = {"f32": f, "f64": f.astype(np.float64), "bf16": lce_synth.f32_to_bf16_bits(f)}[dtype]
+    t = rng.integers(0, vocab, rows)
+    t[0], t[1] = -1, vocab  # invalid targets: NaN either way
+    parts = np.stack([oracle_mod.xent_partial(np.ascontiguousarray(z[:, a:b]), t, a, dtype=dtype)
+                      for a, b in _shard_bounds(vocab, shards, rng)])
+    got = oracle_mod.xent_merge(parts, t, vocab)
+    want = oracle_mod.xent_rows(z, t, dtype=dtype)
+    assert np.array_equal(np.isnan(got), np.isnan(want)) and np.isnan(got[:2]).all()
+    assert np.allclose(got[2:], want[2:], rtol=0, atol=1e-12)
+    # exactly one shard reports each valid target
+    held = (~np.isnan(parts[:, 2:, 2])).sum(axis=0)
+    assert np.all(held == 1)
+
+
+def test_merge_ignores_shard_order(oracle_mod):
+    rng = _rng(12)
+    rows, vocab = 20, 500
+    z = rng.normal(scale=5.0, size=(rows, vocab))
+    t = rng.integers(0, vocab, rows)
+    parts = np.stack([oracle_mod.xent_partial(np.ascontiguousarray(z[:, a:b]), t, a)
+                      for a, b in _shard_bounds(vocab, 5, rng)])
+    a = oracle_mod.xent_merge(parts, t, vocab)
+    b = oracle_mod.xent_merge(parts[::-1].copy(), t, vocab)
+    assert np.allclose(a, b, rtol=0, atol=1e-12)
+
+
+def test_shard_of_minus_infinity_adds_nothing(oracle_mod):
+    """A shard whose logits are all -inf contributes e^-inf = 0: (-inf, 0), and the
+    merged loss equals that of the row without it."""
+    rng = _rng(13)
+    z = rng.normal(size=(4, 30))
+    z[:, 10:20] = -np.inf
+    t = np.array([0, 5, 25, 29])
+    q = oracle_mod.xent_partial(np.ascontiguousarray(z[:, 10:20]), t, 10)
+    assert np.all(q[:, 0] == -np.inf) and np.all(q[:, 1] == 0.0) and np.isnan(q[:, 2]).all()
+    parts = np.stack([oracle_mod.xent_partial(np.ascontiguousarray(z[:, a:b]), t, a)
+                      for a, b in ((0, 10), (10, 20), (20, 30))])
+    assert np.allclose(oracle_mod.xent_merge(parts, t, 30), oracle_mod.xent_rows(z, t), atol=1e-13)
