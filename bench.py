@@ -234,6 +234,72 @@ def roofline_entry(w, us: float) -> dict:
             "algorithmic_bytes": fused_bytes(w.tokens, w.hidden, w.vocab, w.reduction)}
 
 
+def time_vocab_shard(torch, lce, lce_synth, tp: int, steps: int, warmup: int) -> dict:
+    """The headline workload with its vocab split over `tp` devices, as one device sees it:
+    statistics of its [tokens, vocab/tp] shard (lce_xent_partial_fwd, timed over rotating
+    replicas that exceed the Infinity Cache), and the merge of all `tp` shards' statistics
+    (lce_xent_merge, after the all-gather that one GPU cannot show).  Both are timed as HIP
+    graphs of `steps` calls; the merged losses are checked against the unsplit call."""
+    w = lce_synth.WORKLOADS[lce_synth.HEADLINE]
+    T, V = w.tokens, w.vocab
+    sv = V // tp
+    z = torch.empty((T, V), dtype=torch.bfloat16, device="cuda")
+    blk = 2048
+    for r0 in range(0, T, blk):
+        z[r0:r0 + blk].copy_(_to_dev(w.logits(r0, min(T, r0 + blk)), torch))
+    t = torch.from_numpy(w.target()).cuda()
+    shards = [z[:, p * sv:(p + 1) * sv].contiguous() for p in range(tp)]
+    shard_bytes = T * sv * 2
+    R = max(1, min(128, -(-4 * INFINITY_CACHE_BYTES // shard_bytes)))
+    reps = [shards[0]] + [shards[0].clone() for _ in range(R - 1)]
+    part = torch.empty((T, 3), dtype=torch.float32, device="cuda")
+    stats = torch.stack([lce.xent_partial(sh, t, p * sv) for p, sh in enumerate(shards)])
+    out = torch.empty(T, dtype=torch.float32, device="cuda")
+
+    def graph_us(fn, k):
+        for i in range(max(warmup, R)):
+            fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            fn(0)
+        torch.cuda.current_stream().wait_stream(st)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=st):
+            for i in range(k):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(st):
+            e0.record(st)
+            g.replay()
+            e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1000.0 / k
+
+    p_us = graph_us(lambda i: lce.xent_partial(reps[i % R], t, 0, out=part), steps)
+    m_us = graph_us(lambda i: lce.xent_merge(stats, t, V, "none", out=out), steps)
+    lce.xent_merge(stats, t, V, "none", out=out)
+    whole = lce.xent(z, t.view(-1), "none")
+    torch.cuda.synchronize()
+    diff = float(torch.max(torch.abs(out - whole)).item())
+    p_bytes = shard_bytes + T * 8 + T * 12
+    m_bytes = tp * T * 12 + T * 8 + T * 4
+    del reps, shards, z
+    torch.cuda.empty_cache()
+    return {"shard": f"bf16 [{T}, {sv}] = vocab columns [0, {sv}) of {w.name}, tp={tp}",
+            "partial_us": round(p_us, 3), "merge_us": round(m_us, 3),
+            "partial_roofline": {"bound": "hbm", "achieved": round(p_bytes / (p_us * 1e3), 1),
+                                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": round(p_bytes / (p_us * 1e3) / HBM_PEAK_GBS, 4),
+                                 "algorithmic_bytes": p_bytes, "replicas": R},
+            "merge_algorithmic_bytes": m_bytes,
+            "max_abs_diff_vs_unsplit": diff}
+
+
 # ------------------------------------------------------------------ CPU baseline (oracle)
 
 def cpu_baseline(w, budget_s: float = 10.0) -> dict:
@@ -405,6 +471,13 @@ def main(argv=None) -> int:
         print(f"[bench] {name}: {r['us_per_step']:.2f} µs/step "
               f"({r['roofline']['achieved']} {r['roofline']['unit']})", file=sys.stderr, flush=True)
 
+    shard = None
+    if args.workloads == "all" and not args.eager:
+        shard = time_vocab_shard(torch, lce, lce_synth, 8, min(args.steps, 200), args.warmup)
+        print(f"[bench] vocab shard tp=8: partial {shard['partial_us']:.2f} µs, "
+              f"merge {shard['merge_us']:.2f} µs, max |diff| vs unsplit "
+              f"{shard['max_abs_diff_vs_unsplit']:.2e}", file=sys.stderr, flush=True)
+
     if args.copy_calibration:
         copy_calibration(torch)
 
@@ -441,6 +514,8 @@ def main(argv=None) -> int:
                              "roofline": r["roofline"],
                              **({"cpu_oracle": r["cpu_oracle"]} if "cpu_oracle" in r else {})}
                          for n, r in results.items()}
+    if shard is not None:
+        line["vocab_shard_tp8"] = shard
     print(json.dumps(line), flush=True)
     return 0
 

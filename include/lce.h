@@ -53,7 +53,7 @@ extern "C" {
 #endif
 
 #define LCE_VERSION_MAJOR 0
-#define LCE_VERSION_MINOR 1
+#define LCE_VERSION_MINOR 2
 #define LCE_VERSION_PATCH 0
 
 typedef enum {
@@ -109,6 +109,63 @@ typedef enum {
 lce_status lce_xent_fwd(const void* logits, lce_dtype dtype, int64_t tokens, int64_t vocab,
                         const int64_t* target, lce_reduction reduction, float* out,
                         hipStream_t stream);
+
+/*
+ * Vocab-shard statistics: the per-row quantities one device contributes when
+ * the vocab axis is split across devices.
+ *
+ * Defines: KernelIndex "Vocab-parallel cross-entropy, Megatron layout"
+ * (description: cross-entropy with the vocab axis split across devices; the
+ * page measures only the one-device case).  Each device holds the logits of a
+ * contiguous vocab range [vocab_start, vocab_start + shard_vocab) for every
+ * token and calls this on them; gathering the 12 bytes per token from all
+ * devices and calling lce_xent_merge gives every device the full loss.
+ *
+ *   logits       device, `tokens * shard_vocab` elements of `dtype`,
+ *                row-major: row i holds token i's logits of this vocab range
+ *                (alignment and layout as for lce_xent_fwd).
+ *   shard_vocab  columns held, 1 <= shard_vocab < 2^31.
+ *   vocab_start  full-vocab index of column 0, >= 0.
+ *   target       device int64 [tokens], indices into the FULL vocab.
+ *   partial      device fp32 [tokens][3], 4-byte aligned, must not overlap
+ *                the inputs; row i receives
+ *                  m  = max_j z_ij over this range,
+ *                  s  = sum_j e^(z_ij - m)   (m + ln s is the range's
+ *                       log-sum-exp; a row of -inf only gives (-inf, 0)),
+ *                  zt = z_{i, t_i} if vocab_start <= t_i < vocab_start +
+ *                       shard_vocab, else NaN (another device holds it).
+ *   stream       HIP stream.
+ *
+ * Nothing is written when tokens == 0.  Returns as lce_xent_fwd.
+ */
+lce_status lce_xent_partial_fwd(const void* logits, lce_dtype dtype, int64_t tokens,
+                                int64_t shard_vocab, int64_t vocab_start, const int64_t* target,
+                                float* partial, hipStream_t stream);
+
+/*
+ * Loss from the vocab-shard statistics of all devices (same page and section
+ * as lce_xent_partial_fwd).  For each token the shards' (m, s) are folded in
+ * shard order into M = max m and S = sum s e^(m - M), the target logit is the
+ * one a shard reported, and loss = (M - zt) + ln S.
+ *
+ *   partials  device fp32 [shards][tokens][3]: lce_xent_partial_fwd's output
+ *             of each shard, in a fixed shard order (the result depends on the
+ *             order only through fp32 rounding; one order gives one result).
+ *   shards    >= 1;  tokens >= 0.
+ *   target    device int64 [tokens] (full-vocab indices).
+ *   vocab     full vocab size, >= 1: a target outside [0, vocab), or one no
+ *             shard reported, gives NaN.
+ *   reduction, out, stream: as lce_xent_fwd (out must not overlap partials
+ *             or target).
+ *
+ * Returns LCE_OK, LCE_ERR_INVALID_ARG (NULL pointer, shards < 1, tokens < 0,
+ * vocab < 1, bad enum, misaligned pointer), LCE_ERR_UNSUPPORTED
+ * (shards >= 2^31, or scratch that would have to grow under graph capture),
+ * LCE_ERR_ALIAS, LCE_ERR_OOM or LCE_ERR_HIP.
+ */
+lce_status lce_xent_merge(const float* partials, int64_t shards, int64_t tokens,
+                          const int64_t* target, int64_t vocab, lce_reduction reduction,
+                          float* out, hipStream_t stream);
 
 /*
  * Fused LM-head projection + cross-entropy; the logits are never stored.

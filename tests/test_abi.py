@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lce.lce_version() == 100
+    assert lce.lce_version() == 200
     names = [lce.lce_status_string(s) for s in range(6)]
     assert names == ["LCE_OK", "LCE_ERR_INVALID_ARG", "LCE_ERR_UNSUPPORTED", "LCE_ERR_ALIAS",
                      "LCE_ERR_OOM", "LCE_ERR_HIP"]
@@ -121,3 +121,54 @@ def test_binding_refuses_cpu_tensors(lib):
         lce.xent(z, t)
     with pytest.raises(ValueError):
         lce.fused_linear_xent(z.bfloat16(), z.bfloat16(), t)
+
+
+def _partial(logits=FAKE, dtype=lce.LCE_F32, tokens=16, shard=32, start=64, target=FAKE + (1 << 20),
+             partial=FAKE + (2 << 20)):
+    return lce.lce_xent_partial_fwd(logits, dtype, tokens, shard, start, target, partial, 0)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(logits=0), lce.LCE_ERR_INVALID_ARG, "logits is NULL"),
+    (dict(target=0), lce.LCE_ERR_INVALID_ARG, "target is NULL"),
+    (dict(partial=0), lce.LCE_ERR_INVALID_ARG, "partial is NULL"),
+    (dict(dtype=3), lce.LCE_ERR_INVALID_ARG, "dtype"),
+    (dict(tokens=-2), lce.LCE_ERR_INVALID_ARG, "tokens"),
+    (dict(shard=0), lce.LCE_ERR_INVALID_ARG, "vocab"),
+    (dict(start=-1), lce.LCE_ERR_INVALID_ARG, "vocab_start"),
+    (dict(start=(1 << 63) - 8), lce.LCE_ERR_INVALID_ARG, "overflows"),
+    (dict(partial=FAKE + (2 << 20) + 2), lce.LCE_ERR_INVALID_ARG, "aligned"),
+    (dict(partial=FAKE + 256), lce.LCE_ERR_ALIAS, "partial overlaps logits"),
+    # 16 tokens x 12 bytes reach past the first 64 bytes of partial: overlaps the target
+    (dict(partial=FAKE + (1 << 20) - 100), lce.LCE_ERR_ALIAS, "partial overlaps target"),
+])
+def test_partial_argument_errors(lib, kw, status, needle):
+    assert _partial(**kw) == status
+    assert needle in lce.lce_last_error()
+
+
+def _merge(partials=FAKE, shards=4, tokens=16, target=FAKE + (1 << 20), vocab=1000,
+           reduction=lce.LCE_REDUCTION_NONE, out=FAKE + (2 << 20)):
+    return lce.lce_xent_merge(partials, shards, tokens, target, vocab, reduction, out, 0)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(partials=0), lce.LCE_ERR_INVALID_ARG, "partials is NULL"),
+    (dict(target=0), lce.LCE_ERR_INVALID_ARG, "target is NULL"),
+    (dict(out=0), lce.LCE_ERR_INVALID_ARG, "out is NULL"),
+    (dict(shards=0), lce.LCE_ERR_INVALID_ARG, "shards"),
+    (dict(shards=1 << 31), lce.LCE_ERR_UNSUPPORTED, "shards"),
+    (dict(vocab=0), lce.LCE_ERR_INVALID_ARG, "vocab"),
+    (dict(reduction=9), lce.LCE_ERR_INVALID_ARG, "reduction"),
+    (dict(partials=FAKE + 2), lce.LCE_ERR_INVALID_ARG, "aligned"),
+    (dict(out=FAKE + 4 * 16 * 12 - 4), lce.LCE_ERR_ALIAS, "partials"),
+    (dict(out=FAKE + (1 << 20)), lce.LCE_ERR_ALIAS, "target"),
+])
+def test_merge_argument_errors(lib, kw, status, needle):
+    assert _merge(**kw) == status
+    assert needle in lce.lce_last_error()
+
+
+def test_partial_and_merge_empty_are_no_ops(lib):
+    assert lce.lce_xent_partial_fwd(0, lce.LCE_BF16, 0, 8, 0, 0, 0, 0) == lce.LCE_OK
+    assert lce.lce_xent_merge(0, 3, 0, 0, 10, lce.LCE_REDUCTION_NONE, 0, 0) == lce.LCE_OK

@@ -5,9 +5,11 @@ sizes, enum values, a ``hipStream_t`` as an integer) and return the ``lce_status
 code:
 
 * :func:`lce_xent_fwd`, :func:`lce_fused_linear_xent_fwd`
+* :func:`lce_xent_partial_fwd`, :func:`lce_xent_merge` (vocab split across devices)
 * :func:`lce_status_string`, :func:`lce_last_error`, :func:`lce_version`
 
-:func:`xent` and :func:`fused_linear_xent` are thin conveniences over them for
+:func:`xent`, :func:`fused_linear_xent`, :func:`xent_partial` and :func:`xent_merge`
+are thin conveniences over them for
 torch tensors: they check device/dtype/contiguity, allocate the fp32 output with
 torch, pass ``data_ptr()`` values and torch's current HIP stream, and raise
 :class:`LceError` on a non-zero status.  There is no CPU fallback: if
@@ -33,8 +35,8 @@ LCE_ERR_ALIAS = 3
 LCE_ERR_OOM = 4
 LCE_ERR_HIP = 5
 
-EXPORTED = ("lce_xent_fwd", "lce_fused_linear_xent_fwd", "lce_status_string",
-            "lce_last_error", "lce_version")
+EXPORTED = ("lce_xent_fwd", "lce_fused_linear_xent_fwd", "lce_xent_partial_fwd",
+            "lce_xent_merge", "lce_status_string", "lce_last_error", "lce_version")
 
 _lib = None
 
@@ -65,6 +67,14 @@ def load() -> ctypes.CDLL:
     lib.lce_fused_linear_xent_fwd.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                               ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
                                               ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.lce_xent_partial_fwd.restype = ctypes.c_int
+    lib.lce_xent_partial_fwd.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                         ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p]
+    lib.lce_xent_merge.restype = ctypes.c_int
+    lib.lce_xent_merge.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                   ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                   ctypes.c_void_p, ctypes.c_void_p]
     lib.lce_status_string.restype = ctypes.c_char_p
     lib.lce_status_string.argtypes = [ctypes.c_int]
     lib.lce_last_error.restype = ctypes.c_char_p
@@ -88,6 +98,18 @@ def lce_fused_linear_xent_fwd(x: int, weight: int, tokens: int, hidden: int, voc
     return load().lce_fused_linear_xent_fwd(x or None, weight or None, tokens, hidden, vocab,
                                             target or None, reduction, out or None,
                                             stream or None)
+
+
+def lce_xent_partial_fwd(logits: int, dtype: int, tokens: int, shard_vocab: int,
+                         vocab_start: int, target: int, partial: int, stream: int) -> int:
+    return load().lce_xent_partial_fwd(logits or None, dtype, tokens, shard_vocab, vocab_start,
+                                       target or None, partial or None, stream or None)
+
+
+def lce_xent_merge(partials: int, shards: int, tokens: int, target: int, vocab: int,
+                   reduction: int, out: int, stream: int) -> int:
+    return load().lce_xent_merge(partials or None, shards, tokens, target or None, vocab,
+                                 reduction, out or None, stream or None)
 
 
 def lce_status_string(status: int) -> str:
@@ -177,4 +199,57 @@ def fused_linear_xent(x, weight, target, reduction: str = "mean", out=None):
                                    _stream_of(x))
     if st != LCE_OK:
         raise LceError(st, "lce_fused_linear_xent_fwd")
+    return out
+
+
+def xent_partial(logits, target, vocab_start: int, out=None):
+    """Vocab-shard statistics of ``logits`` ([..., shard_vocab], this device's vocab
+    columns starting at ``vocab_start``) for full-vocab ``target``: fp32
+    ``[..., 3]`` holding (max, sum of e^(z - max), target logit or NaN) per token."""
+    import torch
+    if not logits.is_cuda or not target.is_cuda:
+        raise ValueError("logits and target must be device tensors")
+    if logits.dtype == torch.float32:
+        dt = LCE_F32
+    elif logits.dtype == torch.bfloat16:
+        dt = LCE_BF16
+    else:
+        raise TypeError(f"logits must be float32 or bfloat16, got {logits.dtype}")
+    if target.dtype != torch.int64:
+        raise TypeError(f"target must be int64, got {target.dtype}")
+    if not logits.is_contiguous() or not target.is_contiguous():
+        raise ValueError("logits and target must be contiguous")
+    if logits.dim() < 1 or tuple(target.shape) != tuple(logits.shape[:-1]):
+        raise ValueError("target shape must be logits shape without the vocab axis")
+    if out is None:
+        out = torch.empty(tuple(target.shape) + (3,), dtype=torch.float32, device=logits.device)
+    st = lce_xent_partial_fwd(logits.data_ptr(), dt, target.numel(), logits.shape[-1],
+                              int(vocab_start), target.data_ptr(), out.data_ptr(),
+                              _stream_of(logits))
+    if st != LCE_OK:
+        raise LceError(st, "lce_xent_partial_fwd")
+    return out
+
+
+def xent_merge(partials, target, vocab: int, reduction: str = "mean", out=None):
+    """Cross-entropy from stacked shard statistics ``partials`` (fp32
+    ``[shards, *target.shape, 3]``, shards in a fixed order) against full-vocab ``target``."""
+    import torch
+    if reduction not in _REDUCTIONS:
+        raise ValueError(f"reduction must be 'mean' or 'none', got {reduction!r}")
+    if not partials.is_cuda or not target.is_cuda:
+        raise ValueError("partials and target must be device tensors")
+    if partials.dtype != torch.float32 or target.dtype != torch.int64:
+        raise TypeError("partials must be float32 and target int64")
+    if not partials.is_contiguous() or not target.is_contiguous():
+        raise ValueError("partials and target must be contiguous")
+    if partials.dim() < 2 or partials.shape[-1] != 3 or tuple(partials.shape[1:-1]) != tuple(target.shape):
+        raise ValueError("partials must be [shards, *target.shape, 3]")
+    if out is None:
+        shape = (1,) if reduction == "mean" else tuple(target.shape)
+        out = torch.empty(shape, dtype=torch.float32, device=partials.device)
+    st = lce_xent_merge(partials.data_ptr(), partials.shape[0], target.numel(), target.data_ptr(),
+                        int(vocab), _REDUCTIONS[reduction], out.data_ptr(), _stream_of(partials))
+    if st != LCE_OK:
+        raise LceError(st, "lce_xent_merge")
     return out

@@ -132,17 +132,18 @@ int env_int(const char* name, int dflt) {
 }
 
 // ------------------------------------------------------------ validation (host only)
-lce_status validate_common(int64_t tokens, const int64_t* target, int reduction, const float* out) {
+lce_status validate_common(int64_t tokens, const int64_t* target, int reduction, const float* out,
+                           const char* out_name = "out") {
   if (reduction != LCE_REDUCTION_MEAN && reduction != LCE_REDUCTION_NONE)
     return fail(LCE_ERR_INVALID_ARG, "reduction must be LCE_REDUCTION_MEAN or LCE_REDUCTION_NONE (got %d)", reduction);
   if (tokens < 0) return fail(LCE_ERR_INVALID_ARG, "tokens must be >= 0 (got %lld)", (long long)tokens);
   if (tokens >= (int64_t(1) << 32) - 1)
     return fail(LCE_ERR_UNSUPPORTED, "tokens must be < 2^32 - 1 (got %lld)", (long long)tokens);
   const bool writes = reduction == LCE_REDUCTION_MEAN || tokens > 0;
-  if (writes && !out) return fail(LCE_ERR_INVALID_ARG, "out is NULL");
+  if (writes && !out) return fail(LCE_ERR_INVALID_ARG, "%s is NULL", out_name);
   if (tokens > 0 && !target) return fail(LCE_ERR_INVALID_ARG, "target is NULL");
   if (target && !aligned(target, 8)) return fail(LCE_ERR_INVALID_ARG, "target is not 8-byte aligned");
-  if (out && !aligned(out, 4)) return fail(LCE_ERR_INVALID_ARG, "out is not 4-byte aligned");
+  if (out && !aligned(out, 4)) return fail(LCE_ERR_INVALID_ARG, "%s is not 4-byte aligned", out_name);
   return LCE_OK;
 }
 
@@ -150,11 +151,13 @@ uint64_t out_bytes(int64_t tokens, int reduction) {
   return reduction == LCE_REDUCTION_MEAN ? 4u : (uint64_t)tokens * 4u;
 }
 
+// `out_elems` fp32 outputs per token (1, or 3 for shard statistics).
 lce_status validate_xent(const void* logits, int dtype, int64_t tokens, int64_t vocab,
-                         const int64_t* target, int reduction, const float* out) {
+                         const int64_t* target, int reduction, const float* out,
+                         const char* out_name = "out", int out_elems = 1) {
   if (dtype != LCE_F32 && dtype != LCE_BF16)
     return fail(LCE_ERR_INVALID_ARG, "dtype must be LCE_F32 or LCE_BF16 (got %d)", dtype);
-  lce_status s = validate_common(tokens, target, reduction, out);
+  lce_status s = validate_common(tokens, target, reduction, out, out_name);
   if (s != LCE_OK) return s;
   if (vocab < 1) return fail(LCE_ERR_INVALID_ARG, "vocab must be >= 1 (got %lld)", (long long)vocab);
   if (vocab >= (int64_t(1) << 31))
@@ -165,10 +168,11 @@ lce_status validate_xent(const void* logits, int dtype, int64_t tokens, int64_t 
     return fail(LCE_ERR_INVALID_ARG, "tokens * vocab overflows");
   if (logits && !aligned(logits, (uint64_t)esize))
     return fail(LCE_ERR_INVALID_ARG, "logits is not aligned to its element size");
-  const uint64_t ob = out_bytes(tokens, reduction);
+  const uint64_t ob = out_bytes(tokens, reduction) * (uint64_t)out_elems;
   if (overlaps(out, ob, logits, (uint64_t)(tokens * vocab * esize)))
-    return fail(LCE_ERR_ALIAS, "out overlaps logits");
-  if (overlaps(out, ob, target, (uint64_t)tokens * 8u)) return fail(LCE_ERR_ALIAS, "out overlaps target");
+    return fail(LCE_ERR_ALIAS, "%s overlaps logits", out_name);
+  if (overlaps(out, ob, target, (uint64_t)tokens * 8u))
+    return fail(LCE_ERR_ALIAS, "%s overlaps target", out_name);
   return LCE_OK;
 }
 
@@ -197,44 +201,21 @@ lce_status validate_fused(const void* x, const void* w, int64_t tokens, int64_t 
   return LCE_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* lce_status_string(lce_status status) {
-  switch (status) {
-    case LCE_OK: return "LCE_OK";
-    case LCE_ERR_INVALID_ARG: return "LCE_ERR_INVALID_ARG";
-    case LCE_ERR_UNSUPPORTED: return "LCE_ERR_UNSUPPORTED";
-    case LCE_ERR_ALIAS: return "LCE_ERR_ALIAS";
-    case LCE_ERR_OOM: return "LCE_ERR_OOM";
-    case LCE_ERR_HIP: return "LCE_ERR_HIP";
-  }
-  return "LCE_ERR_UNKNOWN";
-}
-
-const char* lce_last_error(void) { return g_last_error.c_str(); }
-
-int lce_version(void) { return LCE_VERSION_MAJOR * 10000 + LCE_VERSION_MINOR * 100 + LCE_VERSION_PATCH; }
-
-lce_status lce_xent_fwd(const void* logits, lce_dtype dtype, int64_t tokens, int64_t vocab,
-                        const int64_t* target, lce_reduction reduction, float* out,
-                        hipStream_t stream) {
-  g_last_error.clear();
-  lce_status s = validate_xent(logits, (int)dtype, tokens, vocab, target, (int)reduction, out);
-  if (s != LCE_OK) return s;
-  const bool mean = reduction == LCE_REDUCTION_MEAN;
-  if (tokens == 0) {
-    if (!mean) return LCE_OK;
-    hipError_t e = lce::launch_fill_f32(out, 1, __builtin_nanf(""), stream);
-    return e == hipSuccess ? LCE_OK : hip_fail(e, "launch");
-  }
+// Row kernels for `tokens` rows of `vocab` columns: per-token losses or their
+// mean into `out`, or (stats != nullptr) per-row vocab-shard statistics, with
+// targets read relative to `vocab_start`.  Arguments are validated; tokens > 0.
+lce_status run_rows(const void* logits, int dtype, int64_t tokens, int64_t vocab,
+                    const int64_t* target, bool mean, float* out, int64_t vocab_start,
+                    float* stats, hipStream_t stream) {
+  lce_status s = LCE_OK;
   int cus = 0;
   if ((s = num_cus(&cus)) != LCE_OK) return s;
 
   lce::XentArgs a{};
   a.logits = logits;
   a.bf16 = dtype == LCE_BF16;
+  a.vocab_start = vocab_start;
+  a.stats = stats;
   a.tokens = tokens;
   a.vocab = vocab;
   a.target = target;
@@ -313,6 +294,91 @@ lce_status lce_xent_fwd(const void* logits, lce_dtype dtype, int64_t tokens, int
   a.split_partials = (float*)(base + off_split);
 
   hipError_t e = lce::launch_xent(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return LCE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lce_status_string(lce_status status) {
+  switch (status) {
+    case LCE_OK: return "LCE_OK";
+    case LCE_ERR_INVALID_ARG: return "LCE_ERR_INVALID_ARG";
+    case LCE_ERR_UNSUPPORTED: return "LCE_ERR_UNSUPPORTED";
+    case LCE_ERR_ALIAS: return "LCE_ERR_ALIAS";
+    case LCE_ERR_OOM: return "LCE_ERR_OOM";
+    case LCE_ERR_HIP: return "LCE_ERR_HIP";
+  }
+  return "LCE_ERR_UNKNOWN";
+}
+
+const char* lce_last_error(void) { return g_last_error.c_str(); }
+
+int lce_version(void) { return LCE_VERSION_MAJOR * 10000 + LCE_VERSION_MINOR * 100 + LCE_VERSION_PATCH; }
+
+lce_status lce_xent_fwd(const void* logits, lce_dtype dtype, int64_t tokens, int64_t vocab,
+                        const int64_t* target, lce_reduction reduction, float* out,
+                        hipStream_t stream) {
+  g_last_error.clear();
+  lce_status s = validate_xent(logits, (int)dtype, tokens, vocab, target, (int)reduction, out);
+  if (s != LCE_OK) return s;
+  const bool mean = reduction == LCE_REDUCTION_MEAN;
+  if (tokens == 0) {
+    if (!mean) return LCE_OK;
+    hipError_t e = lce::launch_fill_f32(out, 1, __builtin_nanf(""), stream);
+    return e == hipSuccess ? LCE_OK : hip_fail(e, "launch");
+  }
+  return run_rows(logits, (int)dtype, tokens, vocab, target, mean, out, 0, nullptr, stream);
+}
+
+lce_status lce_xent_partial_fwd(const void* logits, lce_dtype dtype, int64_t tokens,
+                                int64_t shard_vocab, int64_t vocab_start, const int64_t* target,
+                                float* partial, hipStream_t stream) {
+  g_last_error.clear();
+  // Same checks as lce_xent_fwd with a per-token output of 3 floats.
+  lce_status s = validate_xent(logits, (int)dtype, tokens, shard_vocab, target,
+                               LCE_REDUCTION_NONE, partial, "partial", 3);
+  if (s != LCE_OK) return s;
+  if (vocab_start < 0)
+    return fail(LCE_ERR_INVALID_ARG, "vocab_start must be >= 0 (got %lld)", (long long)vocab_start);
+  if (vocab_start > INT64_MAX - shard_vocab)
+    return fail(LCE_ERR_INVALID_ARG, "vocab_start + shard_vocab overflows");
+  if (tokens == 0) return LCE_OK;
+  return run_rows(logits, (int)dtype, tokens, shard_vocab, target, false, nullptr, vocab_start,
+                  partial, stream);
+}
+
+lce_status lce_xent_merge(const float* partials, int64_t shards, int64_t tokens,
+                          const int64_t* target, int64_t vocab, lce_reduction reduction,
+                          float* out, hipStream_t stream) {
+  g_last_error.clear();
+  lce_status s = validate_common(tokens, target, (int)reduction, out);
+  if (s != LCE_OK) return s;
+  if (shards < 1) return fail(LCE_ERR_INVALID_ARG, "shards must be >= 1 (got %lld)", (long long)shards);
+  if (shards >= (int64_t(1) << 31))
+    return fail(LCE_ERR_UNSUPPORTED, "shards must be < 2^31 (got %lld)", (long long)shards);
+  if (vocab < 1) return fail(LCE_ERR_INVALID_ARG, "vocab must be >= 1 (got %lld)", (long long)vocab);
+  if (tokens > 0 && !partials) return fail(LCE_ERR_INVALID_ARG, "partials is NULL");
+  if (partials && !aligned(partials, 4)) return fail(LCE_ERR_INVALID_ARG, "partials is not 4-byte aligned");
+  if (tokens > INT64_MAX / 12 / shards) return fail(LCE_ERR_INVALID_ARG, "shards * tokens overflows");
+  const bool mean = reduction == LCE_REDUCTION_MEAN;
+  const uint64_t ob = out_bytes(tokens, (int)reduction);
+  if (overlaps(out, ob, partials, (uint64_t)(shards * tokens * 12)))
+    return fail(LCE_ERR_ALIAS, "out overlaps partials");
+  if (overlaps(out, ob, target, (uint64_t)tokens * 8u)) return fail(LCE_ERR_ALIAS, "out overlaps target");
+  if (tokens == 0) {
+    if (!mean) return LCE_OK;
+    hipError_t e = lce::launch_fill_f32(out, 1, __builtin_nanf(""), stream);
+    return e == hipSuccess ? LCE_OK : hip_fail(e, "launch");
+  }
+  Carve cv;
+  const size_t off_mean = cv.take((size_t)((tokens + lce::kRowThreads - 1) / lce::kRowThreads) * 8u);
+  char* base = nullptr;
+  if ((s = get_scratch(stream, cv.off, &base)) != LCE_OK) return s;
+  hipError_t e = lce::launch_stats_merge(partials, shards, tokens, target, vocab, out, mean ? 1 : 0,
+                                         (uint64_t*)(base + off_mean), (unsigned*)base, stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return LCE_OK;
 }

@@ -24,6 +24,8 @@ struct XentArgs {
   const int64_t* target;
   float* out;
   int reduce_mean;
+  int64_t vocab_start;      // first full-vocab column of these rows (0 for whole rows)
+  float* stats;             // non-null: write (m, s, zt) per row instead of losses
   XentPath path;
   int unroll;               // chunks per lane per batch (wave_rows: 4, 8 or 16)
   int waves_per_block;      // WaveRows: rows (waves) per workgroup, 4 or 16 (then unroll <= 8)
@@ -35,6 +37,11 @@ struct XentArgs {
 };
 
 hipError_t launch_xent(const XentArgs& a, hipStream_t stream);
+
+// Losses (or their mean) from [shards][tokens][3] vocab-shard statistics.
+hipError_t launch_stats_merge(const float* stats, int64_t shards, int64_t tokens,
+                              const int64_t* target, int64_t vocab, float* out, int reduce_mean,
+                              uint64_t* slots, unsigned* ticket, hipStream_t stream);
 
 // Fused projection + cross-entropy.
 struct FusedArgs {

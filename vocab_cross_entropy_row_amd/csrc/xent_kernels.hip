@@ -323,6 +323,23 @@ __device__ __forceinline__ int64_t safe_target(int64_t t, int vocab) {
   return (t >= 0 && t < (int64_t)vocab) ? t : 0;
 }
 
+// Index of the target within this row's columns: t - vocab_start when the row
+// holds it, else -1 (a whole row has vocab_start = 0).
+__device__ __forceinline__ int64_t local_target(int64_t t, int64_t vocab_start, int vocab) {
+  return (t >= vocab_start && t - vocab_start < (int64_t)vocab) ? t - vocab_start : -1;
+}
+
+// Shard statistics of a row state: (m, sum of e^(z - m), target logit or NaN).
+// The state's sum is relative to M = fp32(m*log2e); e^(z - m) = 2^(z*L - M) *
+// 2^(M - m*L), and M - m*L is minus the exact residual fma(m, L, -M).
+__device__ __forceinline__ void write_stats(float* dst, const Lse& r, bool holds_target, float zt) {
+  const float s = (r.m == kNegInf) ? 0.0f
+                                   : r.s * exp2_fast(-__builtin_fmaf(r.m, kLog2e, -(r.m * kLog2e)));
+  dst[0] = r.m;
+  dst[1] = s;
+  dst[2] = holds_target ? zt : __builtin_nanf("");
+}
+
 // The target index, made opaque where this is called: code that uses the
 // result cannot be hoisted above it, so the wait for the target's scalar load
 // lands behind the first batch of logit loads instead of in front of them.
@@ -337,8 +354,8 @@ __device__ __forceinline__ int64_t target_here(int64_t t) {
 template <typename T, int U, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void xent_wave_rows_kernel(
     const T* __restrict__ logits, int64_t tokens, int vocab, const int64_t* __restrict__ target,
-    float* __restrict__ out, uint64_t* __restrict__ slots, unsigned* __restrict__ ticket,
-    int reduce_mean) {
+    int64_t vocab_start, float* __restrict__ stats, float* __restrict__ out,
+    uint64_t* __restrict__ slots, unsigned* __restrict__ ticket, int reduce_mean) {
   const int lane = threadIdx.x & 63;
   const int wave = wave_uniform(threadIdx.x >> 6);
   const int64_t row = (int64_t)blockIdx.x * WAVES + wave;
@@ -353,7 +370,7 @@ __global__ __launch_bounds__(64 * WAVES) void xent_wave_rows_kernel(
     int64_t tt = -1;
     auto extra = [&]() {
       edge = Vec<T>::scalar(rp + edge_index(rs, vocab, lane));
-      tt = target_here(t);
+      tt = local_target(target_here(t), vocab_start, vocab);
       zt = Vec<T>::scalar(rp + safe_target(tt, vocab));
     };
     Lse st = lse_empty();
@@ -363,8 +380,12 @@ __global__ __launch_bounds__(64 * WAVES) void xent_wave_rows_kernel(
       stream_chunks<T, U>(st, body, 0, rs.nvec, lane, 64, extra);
     if (lane < rs.head + rs.tail) fold_one(st, edge);
     const Lse r = wave_lse(st);
-    loss = (tt >= 0 && tt < vocab) ? lse_minus(r, zt) : __builtin_nanf("");
-    if (!reduce_mean && lane == 0) out[row] = loss;
+    if (stats) {
+      if (lane == 0) write_stats(stats + 3 * row, r, tt >= 0, zt);
+    } else {
+      loss = (tt >= 0) ? lse_minus(r, zt) : __builtin_nanf("");
+      if (!reduce_mean && lane == 0) out[row] = loss;
+    }
   }
   if (reduce_mean) {
     __shared__ float wl[WAVES];
@@ -402,8 +423,8 @@ __device__ __forceinline__ Lse block_lse(Lse st) {
 template <typename T, int U>
 __global__ __launch_bounds__(kRowThreads) void xent_block_rows_kernel(
     const T* __restrict__ logits, int64_t tokens, int vocab, const int64_t* __restrict__ target,
-    float* __restrict__ out, uint64_t* __restrict__ slots, unsigned* __restrict__ ticket,
-    int reduce_mean) {
+    int64_t vocab_start, float* __restrict__ stats, float* __restrict__ out,
+    uint64_t* __restrict__ slots, unsigned* __restrict__ ticket, int reduce_mean) {
   const int64_t row = blockIdx.x;
   const T* rp = logits + row * (int64_t)vocab;
   const int64_t t = target[row];
@@ -413,14 +434,18 @@ __global__ __launch_bounds__(kRowThreads) void xent_block_rows_kernel(
   int64_t tt = -1;
   auto extra = [&]() {
     edge = Vec<T>::scalar(rp + edge_index(rs, vocab, threadIdx.x));
-    tt = target_here(t);
+    tt = local_target(target_here(t), vocab_start, vocab);
     zt = Vec<T>::scalar(rp + safe_target(tt, vocab));
   };
   Lse st = lse_empty();
   stream_chunks<T, U>(st, body, 0, rs.nvec, threadIdx.x, kRowThreads, extra);
   if ((int)threadIdx.x < rs.head + rs.tail) fold_one(st, edge);
   const Lse r = block_lse(st);
-  const float loss = (tt >= 0 && tt < vocab) ? lse_minus(r, zt) : __builtin_nanf("");
+  if (stats) {
+    if (threadIdx.x == 0) write_stats(stats + 3 * row, r, tt >= 0, zt);
+    return;
+  }
+  const float loss = (tt >= 0) ? lse_minus(r, zt) : __builtin_nanf("");
   if (!reduce_mean) {
     if (threadIdx.x == 0) out[row] = loss;
   } else {
@@ -457,8 +482,9 @@ __global__ __launch_bounds__(kRowThreads) void xent_split_partial_kernel(
 template <typename T>
 __global__ __launch_bounds__(kRowThreads) void xent_split_merge_kernel(
     const T* __restrict__ logits, int64_t tokens, int vocab, int S,
-    const float2* __restrict__ part, const int64_t* __restrict__ target, float* __restrict__ out,
-    uint64_t* __restrict__ slots, unsigned* __restrict__ ticket, int reduce_mean) {
+    const float2* __restrict__ part, const int64_t* __restrict__ target, int64_t vocab_start,
+    float* __restrict__ stats, float* __restrict__ out, uint64_t* __restrict__ slots,
+    unsigned* __restrict__ ticket, int reduce_mean) {
   constexpr int kWaves = kRowThreads / 64;
   const int lane = threadIdx.x & 63;
   const int wave = wave_uniform(threadIdx.x >> 6);
@@ -472,9 +498,14 @@ __global__ __launch_bounds__(kRowThreads) void xent_split_merge_kernel(
     }
     const Lse r = wave_lse(st);
     const T* rp = logits + row * (int64_t)vocab;
-    const int64_t t = target[row];
-    loss = (t >= 0 && t < vocab) ? lse_minus(r, Vec<T>::scalar(rp + t)) : __builtin_nanf("");
-    if (!reduce_mean && lane == 0) out[row] = loss;
+    const int64_t tt = local_target(target[row], vocab_start, vocab);
+    const float zt = Vec<T>::scalar(rp + safe_target(tt, vocab));
+    if (stats) {
+      if (lane == 0) write_stats(stats + 3 * row, r, tt >= 0, zt);
+    } else {
+      loss = (tt >= 0) ? lse_minus(r, zt) : __builtin_nanf("");
+      if (!reduce_mean && lane == 0) out[row] = loss;
+    }
   }
   if (reduce_mean) {
     __shared__ float wl[kWaves];
@@ -485,6 +516,68 @@ __global__ __launch_bounds__(kRowThreads) void xent_split_merge_kernel(
       for (int w = 0; w < kWaves; ++w) bsum += wl[w];
     finish_mean(bsum, slots, ticket, out, tokens);
   }
+}
+
+// ------------------------------------------------------------ merge of vocab-shard statistics
+// One thread per token: fold the `shards` (m, s, zt) triples of its row in
+// shard order into (M, S) with S relative to e^M (a shard of -inf only adds
+// nothing), take the one target logit a shard reported, and finish the loss
+// as (M - zt) + ln S.  Triples are loaded eight shards at a time.
+__global__ __launch_bounds__(kRowThreads) void xent_stats_merge_kernel(
+    const float* __restrict__ stats, int shards, int64_t tokens, const int64_t* __restrict__ target,
+    int64_t vocab, float* __restrict__ out, uint64_t* __restrict__ slots,
+    unsigned* __restrict__ ticket, int reduce_mean) {
+  const int64_t row = (int64_t)blockIdx.x * kRowThreads + threadIdx.x;
+  float loss = 0.0f;
+  if (row < tokens) {
+    const int64_t t = target[row];
+    constexpr int kGroup = 8;
+    float M = kNegInf, S = 0.0f, zt = __builtin_nanf("");
+    for (int p0 = 0; p0 < shards; p0 += kGroup) {
+      float q[kGroup][3];
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j) {
+        const bool in = p0 + j < shards;
+        const float* src = stats + 3 * ((int64_t)(in ? p0 + j : 0) * tokens + row);
+        q[j][0] = in ? src[0] : kNegInf;
+        q[j][1] = in ? src[1] : 0.0f;
+        q[j][2] = in ? src[2] : __builtin_nanf("");
+      }
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j) {
+        const float m = q[j][0], s = q[j][1];
+        if (m > M) {  // rescale the sum so far to the new maximum
+          S = (M == kNegInf ? 0.0f : S * exp2_fast((M - m) * kLog2e)) + s;
+          M = m;
+        } else if (m != kNegInf) {  // (a NaN maximum lands here and makes S NaN)
+          S += s * exp2_fast((m - M) * kLog2e);
+        }
+        if (q[j][2] == q[j][2]) zt = q[j][2];
+      }
+    }
+    loss = (t >= 0 && t < vocab) ? (M - zt) + kLn2 * log2_fast(S) : __builtin_nanf("");
+    if (!reduce_mean) out[row] = loss;
+  }
+  if (reduce_mean) {
+    __shared__ float red[kRowThreads];
+    red[threadIdx.x] = loss;
+    __syncthreads();
+#pragma unroll
+    for (int w = kRowThreads / 2; w > 0; w >>= 1) {
+      if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+      __syncthreads();
+    }
+    finish_mean(red[0], slots, ticket, out, tokens);
+  }
+}
+
+hipError_t launch_stats_merge(const float* stats, int64_t shards, int64_t tokens,
+                              const int64_t* target, int64_t vocab, float* out, int reduce_mean,
+                              uint64_t* slots, unsigned* ticket, hipStream_t st) {
+  const int64_t blocks = (tokens + kRowThreads - 1) / kRowThreads;
+  hipLaunchKernelGGL(xent_stats_merge_kernel, dim3((unsigned)blocks), dim3(kRowThreads), 0, st, stats,
+                     (int)shards, tokens, target, vocab, out, slots, ticket, reduce_mean);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------ small utilities
@@ -503,8 +596,8 @@ template <typename T, int U, int WAVES>
 static hipError_t launch_wave_rows_w(const XentArgs& a, hipStream_t st) {
   const int64_t blocks = (a.tokens + WAVES - 1) / WAVES;
   hipLaunchKernelGGL((xent_wave_rows_kernel<T, U, WAVES>), dim3((unsigned)blocks), dim3(64 * WAVES),
-                     0, st, (const T*)a.logits, a.tokens, (int)a.vocab, a.target, a.out,
-                     a.mean_slots, a.ticket, a.reduce_mean);
+                     0, st, (const T*)a.logits, a.tokens, (int)a.vocab, a.target, a.vocab_start,
+                     a.stats, a.out, a.mean_slots, a.ticket, a.reduce_mean);
   return hipGetLastError();
 }
 
@@ -519,8 +612,8 @@ static hipError_t launch_wave_rows(const XentArgs& a, hipStream_t st) {
 template <typename T, int U>
 static hipError_t launch_block_rows(const XentArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((xent_block_rows_kernel<T, U>), dim3((unsigned)a.tokens), dim3(kRowThreads), 0,
-                     st, (const T*)a.logits, a.tokens, (int)a.vocab, a.target, a.out,
-                     a.mean_slots, a.ticket, a.reduce_mean);
+                     st, (const T*)a.logits, a.tokens, (int)a.vocab, a.target, a.vocab_start,
+                     a.stats, a.out, a.mean_slots, a.ticket, a.reduce_mean);
   return hipGetLastError();
 }
 
@@ -534,8 +627,8 @@ static hipError_t launch_split(const XentArgs& a, hipStream_t st) {
   const int64_t blocks = (a.tokens + kRowThreads / 64 - 1) / (kRowThreads / 64);
   hipLaunchKernelGGL((xent_split_merge_kernel<T>), dim3((unsigned)blocks), dim3(kRowThreads), 0, st,
                      (const T*)a.logits, a.tokens, (int)a.vocab, a.splits,
-                     (const float2*)a.split_partials, a.target, a.out, a.mean_slots, a.ticket,
-                     a.reduce_mean);
+                     (const float2*)a.split_partials, a.target, a.vocab_start, a.stats, a.out,
+                     a.mean_slots, a.ticket, a.reduce_mean);
   return hipGetLastError();
 }
 
