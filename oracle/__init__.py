@@ -71,6 +71,10 @@ def _load():
         lib.oracle_xent_merge.restype = ctypes.c_int
         lib.oracle_xent_merge.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                           ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        lib.oracle_xent_bwd_rows.restype = ctypes.c_int
+        lib.oracle_xent_bwd_rows.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                             ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         lib.oracle_default_threads.restype = ctypes.c_int
         lib.oracle_default_threads.argtypes = []
         _lib = lib
@@ -161,6 +165,36 @@ def xent_merge(partials: np.ndarray, target: np.ndarray, vocab: int) -> np.ndarr
     if rc != 0:
         raise ValueError("oracle: bad argument")
     return out
+
+
+def xent_bwd(logits: np.ndarray, target: np.ndarray, grad, reduction: str = "mean",
+             dtype: str | None = None, nthreads: int | None = None) -> np.ndarray:
+    """Gradient of the loss with respect to the logits, fp64, the logits' shape.
+
+    ``grad`` is the gradient of the loss output: a scalar for ``"mean"`` (each row
+    then gets grad / tokens), one value per token for ``"none"``.  Rows with an
+    out-of-range target are NaN.  (The pages give the forward only; this is its
+    derivative, softmax minus the one-hot target.)
+    """
+    if reduction not in ("mean", "none"):
+        raise ValueError(f"oracle: unknown reduction {reduction!r}")
+    dt = _dtype_of(logits, dtype)
+    z = np.ascontiguousarray(logits)
+    t = np.ascontiguousarray(target, dtype=np.int64)
+    vocab = int(z.shape[-1])
+    rows = int(np.prod(z.shape[:-1], dtype=np.int64)) if z.ndim > 1 else 1
+    if t.size != rows:
+        raise ValueError("oracle: target must have one entry per row")
+    g = np.ascontiguousarray(np.asarray(grad, dtype=np.float64).reshape(-1))
+    if g.size != (1 if reduction == "mean" else rows):
+        raise ValueError("oracle: grad must be a scalar (mean) or one value per token (none)")
+    out = np.empty((rows, vocab), dtype=np.float64)
+    rc = _load().oracle_xent_bwd_rows(z.ctypes.data, _DTYPES[dt], rows, vocab, t.ctypes.data,
+                                      1 if reduction == "mean" else 0, g.ctypes.data,
+                                      out.ctypes.data, int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle: bad argument")
+    return out.reshape(z.shape)
 
 
 def mean(losses: np.ndarray) -> float:

@@ -202,6 +202,59 @@ int oracle_xent_merge(const double* partials, int64_t shards, int64_t rows,
     return 0;
 }
 
+/*
+ * Gradient of the loss with respect to the logits.  The pages give only the
+ * forward; this is the derivative of the loss above, written out:
+ *
+ *     d loss_i / d z_ij = e^(z_ij - lse_i) - [j == t_i],   lse_i = ln sum_k e^(z_ik)
+ *
+ * scaled by the gradient flowing into the loss output: g_i = grad[i] for the
+ * per-token losses (mean == 0), g_i = grad[0] / rows for their mean (mean != 0).
+ * A row with a target outside [0, vocab) has a NaN loss; its gradient row is NaN.
+ * lse_i comes from the same two plain passes as oracle_xent_rows.
+ * dlogits is [rows, vocab] doubles.  Returns 0, or -1 on a bad argument.
+ */
+int oracle_xent_bwd_rows(const void* logits, int dtype, int64_t rows, int64_t vocab,
+                         const int64_t* target, int mean, const double* grad, double* dlogits,
+                         int nthreads)
+{
+    if (rows < 0 || vocab < 1 || (rows > 0 && (!logits || !target || !grad || !dlogits)))
+        return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16 && dtype != ORACLE_F64)
+        return -1;
+    if (nthreads < 1)
+        nthreads = 1;
+
+#pragma omp parallel num_threads(nthreads)
+    {
+        double* z = (double*)malloc((size_t)vocab * sizeof(double));
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t i = 0; i < rows; ++i) {
+            double* dz = dlogits + i * vocab;
+            const int64_t t = target[i];
+            if (t < 0 || t >= vocab || !z) {
+                for (int64_t j = 0; j < vocab; ++j)
+                    dz[j] = NAN;
+                continue;
+            }
+            decode_row(logits, dtype, i, vocab, z);
+            double m = -INFINITY;
+            for (int64_t j = 0; j < vocab; ++j)
+                if (z[j] > m)
+                    m = z[j];
+            double s = 0.0;
+            for (int64_t j = 0; j < vocab; ++j)
+                s += exp(z[j] - m);
+            const double lse = m + log(s);
+            const double g = mean ? grad[0] / (double)rows : grad[i];
+            for (int64_t j = 0; j < vocab; ++j)
+                dz[j] = g * (exp(z[j] - lse) - (j == t ? 1.0 : 0.0));
+        }
+        free(z);
+    }
+    return 0;
+}
+
 /* Mean of n per-token losses, summed in index order.  n == 0 gives 0/0 = NaN. */
 double oracle_mean(const double* loss, int64_t n)
 {

@@ -357,3 +357,63 @@ def test_shard_of_minus_infinity_adds_nothing(oracle_mod):
     parts = np.stack([oracle_mod.xent_partial(np.ascontiguousarray(z[:, a:b]), t, a)
                       for a, b in ((0, 10), (10, 20), (20, 30))])
     assert np.allclose(oracle_mod.xent_merge(parts, t, 30), oracle_mod.xent_rows(z, t), atol=1e-13)
+
+
+# ---------------------------------------------------------------- gradient
+
+def test_bwd_uniform_logits_closed_form(oracle_mod):
+    """Equal logits: softmax is 1/V, so the gradient is g (1/V - [j == t])."""
+    V = 40
+    z = np.full((3, V), -3.0)
+    t = np.array([0, 17, 39])
+    g = np.array([1.0, -2.5, 0.25])
+    d = oracle_mod.xent_bwd(z, t, g, "none")
+    want = g[:, None] * (np.full((3, V), 1.0 / V) - np.eye(V)[t])
+    assert np.allclose(d, want, rtol=0, atol=1e-15)
+
+
+def test_bwd_rows_sum_to_zero_and_mean_scaling(oracle_mod):
+    rng = _rng(21)
+    z = rng.normal(scale=3.0, size=(50, 777))
+    t = rng.integers(0, 777, 50)
+    d = oracle_mod.xent_bwd(z, t, 2.0, "mean")
+    assert np.allclose(d.sum(axis=1), 0.0, atol=1e-15)
+    d1 = oracle_mod.xent_bwd(z, t, np.full(50, 2.0 / 50), "none")
+    assert np.allclose(d, d1, rtol=1e-15, atol=0)
+
+
+def test_bwd_matches_finite_differences_of_the_loss(oracle_mod):
+    """Central differences of the (separately pinned) forward oracle."""
+    rng = _rng(22)
+    rows, V, h = 3, 12, 1e-6
+    z = rng.normal(scale=2.0, size=(rows, V))
+    t = rng.integers(0, V, rows)
+    g = rng.normal(size=rows)
+    d = oracle_mod.xent_bwd(z, t, g, "none")
+    for i in range(rows):
+        for j in range(V):
+            zp, zm = z.copy(), z.copy()
+            zp[i, j] += h
+            zm[i, j] -= h
+            fd = (oracle_mod.xent_rows(zp, t)[i] - oracle_mod.xent_rows(zm, t)[i]) / (2 * h)
+            assert g[i] * fd == pytest.approx(d[i, j], abs=1e-8)
+
+
+def test_bwd_matches_library_autograd(oracle_mod):
+    torch = pytest.importorskip("torch")
+    rng = _rng(23)
+    for dt, rows, V in (("f64", 30, 2000), ("f32", 9, 4097), ("bf16", 5, 300)):
+        f = rng.normal(scale=4.0, size=(rows, V)).astype(np.float32)
+        z = {"f64": f.astype(np.float64), "f32": f, "bf16": lce_synth.f32_to_bf16_bits(f)}[dt]
+        z64 = oracle_mod.bf16_bits_to_f64(z) if dt == "bf16" else z.astype(np.float64)
+        t = rng.integers(0, V, rows)
+        zt = torch.from_numpy(z64).requires_grad_(True)
+        torch.nn.functional.cross_entropy(zt, torch.from_numpy(t)).mul(3.0).backward()
+        d = oracle_mod.xent_bwd(z, t, 3.0, "mean", dtype=dt)
+        assert np.allclose(d, zt.grad.numpy(), rtol=0, atol=1e-14)
+
+
+def test_bwd_invalid_target_rows_are_nan(oracle_mod):
+    z = np.zeros((3, 5))
+    d = oracle_mod.xent_bwd(z, np.array([0, -1, 5]), 1.0, "mean")
+    assert np.isfinite(d[0]).all() and np.isnan(d[1:]).all()
