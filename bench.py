@@ -68,7 +68,7 @@ def fused_flops(tokens: int, hidden: int, vocab: int) -> int:
 CSRC = os.path.join(ROOT, "vocab_cross_entropy_row_amd", "csrc")
 # Sources that define each workload's dominant kernel (plus the build flags).
 KERNEL_SOURCES = {
-    "xent": ["xent_kernels.hip", "lce_device.h", "lce_internal.h"],
+    "xent": ["xent_kernels.hip", "row_stream.h", "lce_device.h", "lce_internal.h"],
     "fused": ["fused_kernel.hip", "lce_device.h", "lce_internal.h"],
 }
 
@@ -232,6 +232,54 @@ def roofline_entry(w, us: float) -> dict:
             "unit": "TFLOP/s", "frac": round(tf / BF16_DENSE_TFLOPS, 4),
             "traffic": traffic_for(w.name, w.kind), "algorithmic_flops": fl,
             "algorithmic_bytes": fused_bytes(w.tokens, w.hidden, w.vocab, w.reduction)}
+
+
+def time_backward(w, torch, lce, steps: int, warmup: int) -> dict:
+    """Gradient of a row workload's loss with respect to its logits (lce_xent_bwd), timed
+    as a HIP graph of `steps` calls over rotating replicas (logits and gradient buffers)
+    that exceed the Infinity Cache.  Algorithmic bytes: the logits read once, the gradient
+    written once, targets and the output gradient."""
+    reps = make_inputs(w, torch, replicas_for(w))
+    R = len(reps)
+    outs = [torch.empty_like(z) for z, _ in reps]
+    grad = torch.ones((1,) if w.reduction == "mean" else w.target_shape, dtype=torch.float32,
+                      device="cuda")
+
+    def step(i):
+        z, t = reps[i % R]
+        lce.xent_bwd(z, t, grad, w.reduction, out=outs[i % R])
+
+    for i in range(max(warmup, R)):
+        step(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        step(0)
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=st):
+        for i in range(steps):
+            step(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(st):
+        e0.record(st)
+        g.replay()
+        e1.record(st)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / steps
+    esize = 4 if w.dtype == "f32" else 2
+    b = tensor_bytes([(w.tokens * w.vocab, esize), (w.tokens * w.vocab, esize), (w.tokens, 8),
+                      (1 if w.reduction == "mean" else w.tokens, 4)])
+    del reps, outs, g
+    torch.cuda.empty_cache()
+    gbs = b / (us * 1e-6) / 1e9
+    return {"us_per_step": round(us, 3), "replicas": R,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": b}}
 
 
 def time_vocab_shard(torch, lce, lce_synth, tp: int, steps: int, warmup: int) -> dict:
@@ -472,7 +520,13 @@ def main(argv=None) -> int:
               f"({r['roofline']['achieved']} {r['roofline']['unit']})", file=sys.stderr, flush=True)
 
     shard = None
+    backward = {}
     if args.workloads == "all" and not args.eager:
+        for bname in (lce_synth.HEADLINE, "ce_f32_16384x4096_mean"):
+            bw = lce_synth.WORKLOADS[bname]
+            backward[bname] = time_backward(bw, torch, lce, min(args.steps, 200), args.warmup)
+            print(f"[bench] backward {bname}: {backward[bname]['us_per_step']:.2f} µs/step "
+                  f"({backward[bname]['roofline']['achieved']} GB/s)", file=sys.stderr, flush=True)
         shard = time_vocab_shard(torch, lce, lce_synth, 8, min(args.steps, 200), args.warmup)
         print(f"[bench] vocab shard tp=8: partial {shard['partial_us']:.2f} µs, "
               f"merge {shard['merge_us']:.2f} µs, max |diff| vs unsplit "
@@ -516,6 +570,8 @@ def main(argv=None) -> int:
                          for n, r in results.items()}
     if shard is not None:
         line["vocab_shard_tp8"] = shard
+    if backward:
+        line["backward"] = backward
     print(json.dumps(line), flush=True)
     return 0
 

@@ -111,6 +111,32 @@ lce_status lce_xent_fwd(const void* logits, lce_dtype dtype, int64_t tokens, int
                         hipStream_t stream);
 
 /*
+ * Gradient of the cross-entropy with respect to the logits (the backward
+ * step of lce_xent_fwd).  The pages give the forward only; this is its
+ * derivative, softmax minus the one-hot target:
+ *
+ *     dlogits_ij = g_i * (e^(z_ij - lse_i) - [j == t_i]),  lse_i = ln sum_k e^(z_ik)
+ *
+ *   logits, dtype, tokens, vocab, target: as lce_xent_fwd.
+ *   reduction  the reduction of the forward call whose gradient this is.
+ *   grad       device fp32 gradient of the forward's output: 1 element for
+ *              LCE_REDUCTION_MEAN (then g_i = grad[0] / tokens), `tokens`
+ *              elements for LCE_REDUCTION_NONE (g_i = grad[i]).
+ *   dlogits    device, same dtype and layout as logits (bf16 results are
+ *              rounded to nearest even).  May be the logits buffer itself
+ *              (computed in place); must not otherwise overlap logits, and
+ *              must not overlap target or grad.
+ *   stream     HIP stream.
+ *
+ * A row whose target is outside [0, vocab) gets a NaN gradient row.  Rows of
+ * up to 32 KiB are read once and written once; longer rows are read twice.
+ * Nothing is written when tokens == 0.  Returns as lce_xent_fwd.
+ */
+lce_status lce_xent_bwd(const void* logits, lce_dtype dtype, int64_t tokens, int64_t vocab,
+                        const int64_t* target, lce_reduction reduction, const float* grad,
+                        void* dlogits, hipStream_t stream);
+
+/*
  * Vocab-shard statistics: the per-row quantities one device contributes when
  * the vocab axis is split across devices.
  *

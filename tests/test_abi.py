@@ -172,3 +172,30 @@ def test_merge_argument_errors(lib, kw, status, needle):
 def test_partial_and_merge_empty_are_no_ops(lib):
     assert lce.lce_xent_partial_fwd(0, lce.LCE_BF16, 0, 8, 0, 0, 0, 0) == lce.LCE_OK
     assert lce.lce_xent_merge(0, 3, 0, 0, 10, lce.LCE_REDUCTION_NONE, 0, 0) == lce.LCE_OK
+
+
+def _bwd(logits=FAKE, dtype=lce.LCE_F32, tokens=16, vocab=32, target=FAKE + (1 << 20),
+         reduction=lce.LCE_REDUCTION_MEAN, grad=FAKE + (2 << 20), dlogits=FAKE + (3 << 20)):
+    return lce.lce_xent_bwd(logits, dtype, tokens, vocab, target, reduction, grad, dlogits, 0)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(logits=0), lce.LCE_ERR_INVALID_ARG, "logits is NULL"),
+    (dict(target=0), lce.LCE_ERR_INVALID_ARG, "target is NULL"),
+    (dict(grad=0), lce.LCE_ERR_INVALID_ARG, "grad is NULL"),
+    (dict(dlogits=0), lce.LCE_ERR_INVALID_ARG, "dlogits is NULL"),
+    (dict(reduction=4), lce.LCE_ERR_INVALID_ARG, "reduction"),
+    (dict(vocab=0), lce.LCE_ERR_INVALID_ARG, "vocab"),
+    (dict(grad=FAKE + (2 << 20) + 1), lce.LCE_ERR_INVALID_ARG, "aligned"),
+    (dict(dlogits=FAKE + (3 << 20) + 2), lce.LCE_ERR_INVALID_ARG, "aligned"),
+    (dict(dlogits=FAKE + 64), lce.LCE_ERR_ALIAS, "same buffer"),
+    (dict(dlogits=FAKE + (1 << 20) - 256), lce.LCE_ERR_ALIAS, "target"),
+    (dict(dlogits=FAKE + (2 << 20) - 256), lce.LCE_ERR_ALIAS, "grad"),
+])
+def test_bwd_argument_errors(lib, kw, status, needle):
+    assert _bwd(**kw) == status
+    assert needle in lce.lce_last_error()
+
+
+def test_bwd_empty_is_a_no_op(lib):
+    assert lce.lce_xent_bwd(0, lce.LCE_F32, 0, 8, 0, lce.LCE_REDUCTION_NONE, 0, 0, 0) == lce.LCE_OK

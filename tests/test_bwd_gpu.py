@@ -1,0 +1,136 @@
+"""Gradient of the row cross-entropy (lce_xent_bwd, through the C ABI) against the fp64
+oracle's softmax-minus-one-hot.
+
+Tolerances: softmax values are at most 1, and the kernel forms each as
+2^(fma(z, log2e, -M)) times a row constant in fp32, so fp32 gradients must be within
+2e-6 * |g_i| of the oracle (g_i the row's output gradient); bf16 gradients are that fp32
+value rounded to nearest even, so within one bf16 rounding (2^-8 relative) more.
+"""
+import numpy as np
+import pytest
+
+import lce_synth
+import oracle
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import vocab_cross_entropy_row_amd as lce  # noqa: E402
+from gpu_util import forced_env, to_dev  # noqa: E402
+
+ABS_PER_G = 2e-6
+BF16_REL = 2.0 ** -8
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lce.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _logits(seed, rows, vocab, dtype, std=2.0, shift=0.0):
+    f = lce_synth.normal_f32(seed, 9, rows, vocab, std)
+    if shift:
+        f = (np.round(f * 64) / 64 + np.float32(shift)).astype(np.float32)
+    return f if dtype == "f32" else lce_synth.f32_to_bf16_bits(f)
+
+
+def _to_host(d, dtype):
+    if dtype == "f32":
+        return d.cpu().numpy().astype(np.float64)
+    return oracle.bf16_bits_to_f64(d.view(torch.int16).cpu().numpy().view(np.uint16))
+
+
+def _check(got, want, gscale, dtype, label):
+    assert np.array_equal(np.isnan(got), np.isnan(want)), label
+    ok = ~np.isnan(want)
+    tol = ABS_PER_G * np.abs(gscale) + (BF16_REL * np.abs(want) if dtype == "bf16" else 0.0)
+    err = np.where(ok, np.abs(got - want) - tol, 0.0)
+    assert err.max(initial=-1.0) <= 0.0, f"{label}: worst excess {err.max()}"
+
+
+def _run(z, t, dtype, reduction, grad, env=None, in_place=False):
+    zd = to_dev(z)
+    td = torch.from_numpy(np.ascontiguousarray(t, dtype=np.int64)).cuda()
+    gd = torch.from_numpy(np.asarray(grad, dtype=np.float32).reshape(-1)).cuda()
+    with forced_env(**(env or {})):
+        d = lce.xent_bwd(zd, td, gd, reduction, out=zd if in_place else None)
+    torch.cuda.synchronize()
+    return _to_host(d, dtype)
+
+
+SHAPES = [(1, 1), (3, 7), (17, 64), (9, 100), (64, 4096), (13, 4097), (5, 8193), (33, 1000),
+          (7, 16384), (4, 20000), (3, 50001)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rows,vocab", SHAPES)
+@pytest.mark.parametrize("reduction", ["mean", "none"])
+def test_bwd_matches_oracle(dtype, rows, vocab, reduction):
+    z = _logits(rows * 7 + vocab, rows, vocab, dtype)
+    t = lce_synth.targets(rows + 3, rows, vocab)
+    rng = np.random.default_rng(rows + vocab)
+    grad = np.float32(1.7) if reduction == "mean" else rng.normal(size=rows).astype(np.float32)
+    got = _run(z, t, dtype, reduction, grad)
+    want = oracle.xent_bwd(z, t, np.asarray(grad, dtype=np.float64), reduction, dtype=dtype)
+    g = (np.full(rows, float(grad) / rows) if reduction == "mean" else grad.astype(np.float64))
+    _check(got, want, g[:, None], dtype, f"{dtype} {rows}x{vocab} {reduction}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rows,vocab", [(5, 3000), (40, 9000), (3, 70001)])
+def test_bwd_two_pass_path(dtype, rows, vocab):
+    """Rows that would stay in registers, forced through the statistics + apply path."""
+    z = _logits(rows + vocab, rows, vocab, dtype)
+    t = lce_synth.targets(rows, rows, vocab)
+    grad = np.linspace(-1, 1, rows).astype(np.float32)
+    got = _run(z, t, dtype, "none", grad, env={"LCE_BWD_PATH": "apply"})
+    want = oracle.xent_bwd(z, t, grad.astype(np.float64), "none", dtype=dtype)
+    _check(got, want, grad.astype(np.float64)[:, None], dtype, f"apply {dtype} {rows}x{vocab}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("vocab", [4096, 40000])
+def test_bwd_in_place(dtype, vocab):
+    rows = 64
+    z = _logits(3, rows, vocab, dtype)
+    t = lce_synth.targets(4, rows, vocab)
+    a = _run(z, t, dtype, "mean", 1.0)
+    b = _run(z, t, dtype, "mean", 1.0, in_place=True)
+    assert np.array_equal(a, b)
+
+
+def test_bwd_large_shift_and_edge_rows():
+    rows, vocab = 8, 4099
+    z = _logits(5, rows, vocab, "f32", shift=-1000.0)
+    z[1, :] = -np.inf
+    z[1, 7] = 2.0            # one finite logit, the target: gradient 0 everywhere
+    z[2, 3] += 200.0         # dominant non-target logit
+    t = lce_synth.targets(6, rows, vocab)
+    t[1] = 7
+    t[2] = 10
+    t[3] = -1                # invalid: NaN row
+    got = _run(z, t, "f32", "none", np.ones(rows, np.float32))
+    want = oracle.xent_bwd(z, t, np.ones(rows), "none", dtype="f32")
+    _check(got, want, np.ones((rows, 1)), "f32", "edge rows")
+    assert np.isnan(got[3]).all() and np.all(got[1] == 0.0)
+    assert abs(got[2, 3] - 1.0) <= 2e-6 and abs(got[2, t[2]] + 1.0) <= 2e-6
+
+
+@pytest.mark.parametrize("name", ["megatron_bf16_2048x4x4096_none", "ce_f32_16384x4096_mean"])
+def test_bwd_full_size_sampled_rows(name):
+    """Full workloads in the benchmark's launch configuration; the oracle checks a row sample."""
+    w = lce_synth.WORKLOADS[name]
+    z = w.logits()
+    t = w.target()
+    red = w.reduction
+    grad = np.float32(1.0) if red == "mean" else np.linspace(0.5, 1.5, w.tokens).astype(np.float32)
+    got = _run(z, t, w.dtype, red, grad)
+    rows = np.r_[0:64, w.tokens - 64:w.tokens, np.arange(64, w.tokens - 64, 997)]
+    g = (np.full(rows.size, 1.0 / w.tokens) if red == "mean" else grad[rows].astype(np.float64))
+    # the sampled rows' gradients: per-token scale g_i (grad / tokens for the mean)
+    want = oracle.xent_bwd(z[rows], t[rows], g, "none", dtype=w.dtype)
+    _check(got[rows], want, g[:, None], w.dtype, name)

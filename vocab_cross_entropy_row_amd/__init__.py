@@ -5,10 +5,11 @@ sizes, enum values, a ``hipStream_t`` as an integer) and return the ``lce_status
 code:
 
 * :func:`lce_xent_fwd`, :func:`lce_fused_linear_xent_fwd`
+* :func:`lce_xent_bwd` (gradient with respect to the logits)
 * :func:`lce_xent_partial_fwd`, :func:`lce_xent_merge` (vocab split across devices)
 * :func:`lce_status_string`, :func:`lce_last_error`, :func:`lce_version`
 
-:func:`xent`, :func:`fused_linear_xent`, :func:`xent_partial` and :func:`xent_merge`
+:func:`xent`, :func:`xent_bwd`, :func:`fused_linear_xent`, :func:`xent_partial` and :func:`xent_merge`
 are thin conveniences over them for
 torch tensors: they check device/dtype/contiguity, allocate the fp32 output with
 torch, pass ``data_ptr()`` values and torch's current HIP stream, and raise
@@ -35,7 +36,7 @@ LCE_ERR_ALIAS = 3
 LCE_ERR_OOM = 4
 LCE_ERR_HIP = 5
 
-EXPORTED = ("lce_xent_fwd", "lce_fused_linear_xent_fwd", "lce_xent_partial_fwd",
+EXPORTED = ("lce_xent_fwd", "lce_xent_bwd", "lce_fused_linear_xent_fwd", "lce_xent_partial_fwd",
             "lce_xent_merge", "lce_status_string", "lce_last_error", "lce_version")
 
 _lib = None
@@ -67,6 +68,10 @@ def load() -> ctypes.CDLL:
     lib.lce_fused_linear_xent_fwd.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                               ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
                                               ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.lce_xent_bwd.restype = ctypes.c_int
+    lib.lce_xent_bwd.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                 ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_void_p]
     lib.lce_xent_partial_fwd.restype = ctypes.c_int
     lib.lce_xent_partial_fwd.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                          ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
@@ -98,6 +103,12 @@ def lce_fused_linear_xent_fwd(x: int, weight: int, tokens: int, hidden: int, voc
     return load().lce_fused_linear_xent_fwd(x or None, weight or None, tokens, hidden, vocab,
                                             target or None, reduction, out or None,
                                             stream or None)
+
+
+def lce_xent_bwd(logits: int, dtype: int, tokens: int, vocab: int, target: int, reduction: int,
+                 grad: int, dlogits: int, stream: int) -> int:
+    return load().lce_xent_bwd(logits or None, dtype, tokens, vocab, target or None, reduction,
+                               grad or None, dlogits or None, stream or None)
 
 
 def lce_xent_partial_fwd(logits: int, dtype: int, tokens: int, shard_vocab: int,
@@ -252,4 +263,39 @@ def xent_merge(partials, target, vocab: int, reduction: str = "mean", out=None):
                         int(vocab), _REDUCTIONS[reduction], out.data_ptr(), _stream_of(partials))
     if st != LCE_OK:
         raise LceError(st, "lce_xent_merge")
+    return out
+
+
+def xent_bwd(logits, target, grad, reduction: str = "mean", out=None):
+    """Gradient of :func:`xent` with respect to ``logits``: softmax minus the one-hot
+    target, scaled by ``grad`` (the gradient of the forward's output: a 1-element
+    tensor for ``"mean"``, the target's shape for ``"none"``).  Returns a tensor like
+    ``logits``; ``out`` may be ``logits`` itself (in place)."""
+    import torch
+    if reduction not in _REDUCTIONS:
+        raise ValueError(f"reduction must be 'mean' or 'none', got {reduction!r}")
+    if not (logits.is_cuda and target.is_cuda and grad.is_cuda):
+        raise ValueError("logits, target and grad must be device tensors")
+    if logits.dtype == torch.float32:
+        dt = LCE_F32
+    elif logits.dtype == torch.bfloat16:
+        dt = LCE_BF16
+    else:
+        raise TypeError(f"logits must be float32 or bfloat16, got {logits.dtype}")
+    if target.dtype != torch.int64 or grad.dtype != torch.float32:
+        raise TypeError("target must be int64 and grad float32")
+    if not (logits.is_contiguous() and target.is_contiguous() and grad.is_contiguous()):
+        raise ValueError("logits, target and grad must be contiguous")
+    if logits.dim() < 1 or tuple(target.shape) != tuple(logits.shape[:-1]):
+        raise ValueError("target shape must be logits shape without the vocab axis")
+    if grad.numel() != (1 if reduction == "mean" else target.numel()):
+        raise ValueError("grad must have 1 element (mean) or one per token (none)")
+    if out is None:
+        out = torch.empty_like(logits)
+    elif out.shape != logits.shape or out.dtype != logits.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like logits")
+    st = lce_xent_bwd(logits.data_ptr(), dt, target.numel(), logits.shape[-1], target.data_ptr(),
+                      _REDUCTIONS[reduction], grad.data_ptr(), out.data_ptr(), _stream_of(logits))
+    if st != LCE_OK:
+        raise LceError(st, "lce_xent_bwd")
     return out

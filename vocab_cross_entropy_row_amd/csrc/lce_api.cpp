@@ -139,7 +139,8 @@ lce_status validate_common(int64_t tokens, const int64_t* target, int reduction,
   if (tokens < 0) return fail(LCE_ERR_INVALID_ARG, "tokens must be >= 0 (got %lld)", (long long)tokens);
   if (tokens >= (int64_t(1) << 32) - 1)
     return fail(LCE_ERR_UNSUPPORTED, "tokens must be < 2^32 - 1 (got %lld)", (long long)tokens);
-  const bool writes = reduction == LCE_REDUCTION_MEAN || tokens > 0;
+  // out_name == nullptr: the caller checks its own output.
+  const bool writes = out_name && (reduction == LCE_REDUCTION_MEAN || tokens > 0);
   if (writes && !out) return fail(LCE_ERR_INVALID_ARG, "%s is NULL", out_name);
   if (tokens > 0 && !target) return fail(LCE_ERR_INVALID_ARG, "target is NULL");
   if (target && !aligned(target, 8)) return fail(LCE_ERR_INVALID_ARG, "target is not 8-byte aligned");
@@ -168,6 +169,7 @@ lce_status validate_xent(const void* logits, int dtype, int64_t tokens, int64_t 
     return fail(LCE_ERR_INVALID_ARG, "tokens * vocab overflows");
   if (logits && !aligned(logits, (uint64_t)esize))
     return fail(LCE_ERR_INVALID_ARG, "logits is not aligned to its element size");
+  if (!out_name) return LCE_OK;
   const uint64_t ob = out_bytes(tokens, reduction) * (uint64_t)out_elems;
   if (overlaps(out, ob, logits, (uint64_t)(tokens * vocab * esize)))
     return fail(LCE_ERR_ALIAS, "%s overlaps logits", out_name);
@@ -204,9 +206,10 @@ lce_status validate_fused(const void* x, const void* w, int64_t tokens, int64_t 
 // Row kernels for `tokens` rows of `vocab` columns: per-token losses or their
 // mean into `out`, or (stats != nullptr) per-row vocab-shard statistics, with
 // targets read relative to `vocab_start`.  Arguments are validated; tokens > 0.
+// The first `reserved` bytes of scratch regions belong to the caller.
 lce_status run_rows(const void* logits, int dtype, int64_t tokens, int64_t vocab,
                     const int64_t* target, bool mean, float* out, int64_t vocab_start,
-                    float* stats, hipStream_t stream) {
+                    float* stats, hipStream_t stream, size_t reserved = 0) {
   lce_status s = LCE_OK;
   int cus = 0;
   if ((s = num_cus(&cus)) != LCE_OK) return s;
@@ -285,6 +288,7 @@ lce_status run_rows(const void* logits, int dtype, int64_t tokens, int64_t vocab
   need_partials = (size_t)mean_blocks * 8u;
 
   Carve cv;
+  if (reserved) cv.take(reserved);
   const size_t off_mean = cv.take(need_partials);
   const size_t off_split = cv.take(need_split);
   char* base = nullptr;
@@ -379,6 +383,78 @@ lce_status lce_xent_merge(const float* partials, int64_t shards, int64_t tokens,
   if ((s = get_scratch(stream, cv.off, &base)) != LCE_OK) return s;
   hipError_t e = lce::launch_stats_merge(partials, shards, tokens, target, vocab, out, mean ? 1 : 0,
                                          (uint64_t*)(base + off_mean), (unsigned*)base, stream);
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return LCE_OK;
+}
+
+lce_status lce_xent_bwd(const void* logits, lce_dtype dtype, int64_t tokens, int64_t vocab,
+                        const int64_t* target, lce_reduction reduction, const float* grad,
+                        void* dlogits, hipStream_t stream) {
+  g_last_error.clear();
+  lce_status s = validate_xent(logits, (int)dtype, tokens, vocab, target, LCE_REDUCTION_NONE, nullptr,
+                               nullptr);
+  if (s != LCE_OK) return s;
+  if (reduction != LCE_REDUCTION_MEAN && reduction != LCE_REDUCTION_NONE)
+    return fail(LCE_ERR_INVALID_ARG, "reduction must be LCE_REDUCTION_MEAN or LCE_REDUCTION_NONE (got %d)",
+                (int)reduction);
+  if (tokens == 0) return LCE_OK;
+  const int64_t esize = dtype == LCE_F32 ? 4 : 2;
+  if (!grad) return fail(LCE_ERR_INVALID_ARG, "grad is NULL");
+  if (!dlogits) return fail(LCE_ERR_INVALID_ARG, "dlogits is NULL");
+  if (!aligned(grad, 4)) return fail(LCE_ERR_INVALID_ARG, "grad is not 4-byte aligned");
+  if (!aligned(dlogits, (uint64_t)esize))
+    return fail(LCE_ERR_INVALID_ARG, "dlogits is not aligned to its element size");
+  const bool mean = reduction == LCE_REDUCTION_MEAN;
+  const uint64_t zb = (uint64_t)(tokens * vocab * esize);
+  const uint64_t gb = mean ? 4u : (uint64_t)tokens * 4u;
+  // In place (dlogits == logits) is allowed; any other overlap is not.
+  if (dlogits != logits && overlaps(dlogits, zb, logits, zb))
+    return fail(LCE_ERR_ALIAS, "dlogits overlaps logits without being the same buffer");
+  if (overlaps(dlogits, zb, target, (uint64_t)tokens * 8u))
+    return fail(LCE_ERR_ALIAS, "dlogits overlaps target");
+  if (overlaps(dlogits, zb, grad, gb)) return fail(LCE_ERR_ALIAS, "dlogits overlaps grad");
+
+  lce::BwdArgs a{};
+  a.logits = logits;
+  a.bf16 = dtype == LCE_BF16;
+  a.tokens = tokens;
+  a.vocab = vocab;
+  a.target = target;
+  a.grad = grad;
+  a.reduce_mean = mean ? 1 : 0;
+  a.dlogits = dlogits;
+  // Rows of at most 32 chunks per lane stay in one wave's registers (read once,
+  // written once); longer rows take the row states from a statistics pass first.
+  const int64_t nvec = vocab * esize / 16;
+  const int64_t per_lane = (nvec + 63) / 64;
+  a.wave_chunks = per_lane <= 4 ? 4 : per_lane <= 8 ? 8 : per_lane <= 16 ? 16 : per_lane <= 32 ? 32 : 0;
+  const char* forced = getenv("LCE_BWD_PATH");
+  if (forced && !strcmp(forced, "apply")) a.wave_chunks = 0;
+  if (a.wave_chunks == 0) {
+    int cus = 0;
+    if ((s = num_cus(&cus)) != LCE_OK) return s;
+    int64_t S = (4 * (int64_t)cus + tokens - 1) / tokens;
+    const int64_t max_s = (nvec + lce::kRowThreads * 4 - 1) / (lce::kRowThreads * 4);
+    if (S > max_s) S = max_s;
+    const int64_t min_s = (nvec * 16 + kMaxStreamBytes - 1) / kMaxStreamBytes;
+    if (S < min_s) S = min_s;
+    if (S < 1) S = 1;
+    if (S * tokens >= (int64_t(1) << 31))
+      return fail(LCE_ERR_UNSUPPORTED, "tokens * slices must be < 2^31 (got %lld)", (long long)(S * tokens));
+    a.splits = (int)S;
+    a.chunks_per_split = (int)((nvec + S - 1) / S);
+    // Row states (m, sum e^(z - m), .) into scratch, then the gradient pass.
+    Carve cv;
+    const size_t off_stats = cv.take((size_t)tokens * 12u);
+    char* base = nullptr;
+    if ((s = get_scratch(stream, cv.off, &base)) != LCE_OK) return s;
+    float* stats = (float*)(base + off_stats);
+    if ((s = run_rows(logits, (int)dtype, tokens, vocab, target, false, nullptr, 0, stats, stream,
+                      (size_t)tokens * 12u)) != LCE_OK)
+      return s;
+    a.stats = stats;
+  }
+  hipError_t e = lce::launch_bwd(a, stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return LCE_OK;
 }

@@ -38,6 +38,24 @@ struct XentArgs {
 
 hipError_t launch_xent(const XentArgs& a, hipStream_t stream);
 
+// Gradient with respect to the logits.
+struct BwdArgs {
+  const void* logits;
+  bool bf16;
+  int64_t tokens;
+  int64_t vocab;
+  const int64_t* target;
+  const float* grad;        // 1 (mean) or tokens (none) fp32
+  int reduce_mean;
+  void* dlogits;            // same dtype and layout as logits; may be logits itself
+  int wave_chunks;          // > 0: one wave per row holding <= 64 * wave_chunks chunks
+  const float* stats;       // otherwise: (m, s, .) per row from the statistics mode
+  int splits;               //   workgroups per row
+  int chunks_per_split;     //   16-byte chunks per workgroup
+};
+
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+
 // Losses (or their mean) from [shards][tokens][3] vocab-shard statistics.
 hipError_t launch_stats_merge(const float* stats, int64_t shards, int64_t tokens,
                               const int64_t* target, int64_t vocab, float* out, int reduce_mean,
