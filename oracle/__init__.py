@@ -252,3 +252,20 @@ def fused_linear_xent(x_bits: np.ndarray, w_bits: np.ndarray, target: np.ndarray
     if reduction == "mean":
         return mean(per_token)
     raise ValueError(f"oracle: unknown reduction {reduction!r}")
+
+
+def fused_linear_logprob_sums(x_bits: np.ndarray, w_bits: np.ndarray, target: np.ndarray,
+                              batch: int, seq: int, nthreads: int | None = None) -> np.ndarray:
+    """Per-sequence sums of target log-probabilities under ``x W^T``, fp64 ``[batch]``.
+
+    Tokens are ordered row = b * seq + s (the CPO page's ``x [batch, seq, hidden]``,
+    flattened); entry b is sum_s log softmax(z_{b,s})[t_{b,s}] = -sum_s loss_{b,s},
+    summed exactly (``math.fsum``).  These sums are what the "Fused linear + CPO loss"
+    page's preference loss is built from; its formula is not on the page.
+    """
+    import math
+    per = fused_linear_xent_rows(x_bits, w_bits, target, nthreads=nthreads)
+    if per.size != batch * seq:
+        raise ValueError("oracle: tokens must equal batch * seq")
+    per = per.reshape(batch, seq)
+    return np.array([-math.fsum(per[b]) for b in range(batch)], dtype=np.float64)

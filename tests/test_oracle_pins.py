@@ -417,3 +417,42 @@ def test_bwd_invalid_target_rows_are_nan(oracle_mod):
     z = np.zeros((3, 5))
     d = oracle_mod.xent_bwd(z, np.array([0, -1, 5]), 1.0, "mean")
     assert np.isfinite(d[0]).all() and np.isnan(d[1:]).all()
+
+
+# ---------------------------------------------------------------- per-sequence log-prob sums
+
+def test_logprob_sums_brute_force_tiny(oracle_mod):
+    """Sums of 40-digit log-softmax values of an exactly computed tiny GEMM, batch != seq."""
+    rng = _rng(31)
+    batch, seq, hidden, vocab = 3, 4, 8, 5
+    xf = rng.normal(size=(batch * seq, hidden)).astype(np.float32)
+    wf = rng.normal(size=(vocab, hidden)).astype(np.float32)
+    xb, wb = lce_synth.f32_to_bf16_bits(xf), lce_synth.f32_to_bf16_bits(wf)
+    x, w = oracle_mod.bf16_bits_to_f64(xb), oracle_mod.bf16_bits_to_f64(wb)
+    t = rng.integers(0, vocab, batch * seq)
+    getcontext().prec = 40
+    want = []
+    for b in range(batch):
+        acc = Decimal(0)
+        for s in range(seq):
+            r = b * seq + s
+            z = [sum(Fraction(float(x[r, k])) * Fraction(float(w[j, k])) for k in range(hidden))
+                 for j in range(vocab)]
+            zd = [Decimal(v.numerator) / Decimal(v.denominator) for v in z]
+            acc += zd[t[r]] - sum(v.exp() for v in zd).ln()
+        want.append(float(acc))
+    got = oracle_mod.fused_linear_logprob_sums(xb, wb, t, batch, seq)
+    assert np.allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_logprob_sums_closed_forms(oracle_mod):
+    """x = 0: every token's log-prob is -ln V; seq = 1: minus the per-token loss."""
+    rng = _rng(32)
+    wb = lce_synth.f32_to_bf16_bits(rng.normal(size=(50, 16)).astype(np.float32))
+    t = rng.integers(0, 50, 12)
+    zero = np.zeros((12, 16), dtype=np.uint16)
+    assert np.allclose(oracle_mod.fused_linear_logprob_sums(zero, wb, t, 2, 6), -6 * math.log(50),
+                       rtol=0, atol=1e-12)
+    xb = lce_synth.f32_to_bf16_bits(rng.normal(size=(12, 16)).astype(np.float32))
+    assert np.allclose(oracle_mod.fused_linear_logprob_sums(xb, wb, t, 12, 1),
+                       -oracle_mod.fused_linear_xent_rows(xb, wb, t), rtol=0, atol=1e-13)
