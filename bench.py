@@ -282,6 +282,45 @@ def time_backward(w, torch, lce, steps: int, warmup: int) -> dict:
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": b}}
 
 
+def time_logprob_sums(torch, lce, lce_synth, steps: int, warmup: int) -> dict:
+    """Per-sequence target log-probability sums at the fused workload's shape read as the
+    CPO page's [batch 2, seq 1024] (lce_fused_linear_logprob_sums), timed as a HIP graph."""
+    w = lce_synth.WORKLOADS["fused_bf16_t2048_h4096_v128256_mean"]
+    batch, seq = 2, w.tokens // 2
+    (x, W, t), = make_inputs(w, torch, 1)
+    x3, t2 = x.view(batch, seq, w.hidden), t.view(batch, seq)
+    out = torch.empty(batch, dtype=torch.float32, device="cuda")
+    for _ in range(max(1, warmup)):
+        lce.fused_linear_logprob_sums(x3, W, t2, out=out)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        lce.fused_linear_logprob_sums(x3, W, t2, out=out)
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=st):
+        for _ in range(steps):
+            lce.fused_linear_logprob_sums(x3, W, t2, out=out)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(st):
+        e0.record(st)
+        g.replay()
+        e1.record(st)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / steps
+    tf = fused_flops(w.tokens, w.hidden, w.vocab) / (us * 1e-6) / 1e12
+    del x, W, t, g
+    torch.cuda.empty_cache()
+    return {"shape": f"batch {batch} x seq {seq}, hidden {w.hidden}, vocab {w.vocab}",
+            "us_per_step": round(us, 1),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_DENSE_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / BF16_DENSE_TFLOPS, 4)}}
+
+
 def time_vocab_shard(torch, lce, lce_synth, tp: int, steps: int, warmup: int) -> dict:
     """The headline workload with its vocab split over `tp` devices, as one device sees it:
     statistics of its [tokens, vocab/tp] shard (lce_xent_partial_fwd, timed over rotating
@@ -520,6 +559,7 @@ def main(argv=None) -> int:
               f"({r['roofline']['achieved']} {r['roofline']['unit']})", file=sys.stderr, flush=True)
 
     shard = None
+    sums = None
     backward = {}
     if args.workloads == "all" and not args.eager:
         for bname in (lce_synth.HEADLINE, "ce_f32_16384x4096_mean"):
@@ -528,6 +568,9 @@ def main(argv=None) -> int:
             print(f"[bench] backward {bname}: {backward[bname]['us_per_step']:.2f} µs/step "
                   f"({backward[bname]['roofline']['achieved']} GB/s)", file=sys.stderr, flush=True)
         shard = time_vocab_shard(torch, lce, lce_synth, 8, min(args.steps, 200), args.warmup)
+        sums = time_logprob_sums(torch, lce, lce_synth, min(args.steps, 10), 2)
+        print(f"[bench] fused log-prob sums: {sums['us_per_step']:.1f} µs "
+              f"({sums['roofline']['achieved']} TFLOP/s)", file=sys.stderr, flush=True)
         print(f"[bench] vocab shard tp=8: partial {shard['partial_us']:.2f} µs, "
               f"merge {shard['merge_us']:.2f} µs, max |diff| vs unsplit "
               f"{shard['max_abs_diff_vs_unsplit']:.2e}", file=sys.stderr, flush=True)
@@ -572,6 +615,8 @@ def main(argv=None) -> int:
         line["vocab_shard_tp8"] = shard
     if backward:
         line["backward"] = backward
+    if sums is not None:
+        line["fused_logprob_sums"] = sums
     print(json.dumps(line), flush=True)
     return 0
 

@@ -224,6 +224,30 @@ lce_status lce_fused_linear_xent_fwd(const void* x, const void* weight, int64_t 
                                      int64_t hidden, int64_t vocab, const int64_t* target,
                                      lce_reduction reduction, float* out, hipStream_t stream);
 
+/*
+ * Per-sequence sums of target log-probabilities under the fused projection:
+ * the quantity the "Fused linear + CPO loss" page's preference loss is built
+ * from (the page gives the loss only by name; its formula is not on the page,
+ * so the preference term itself is not computed here).
+ *
+ *     out[b] = sum_{s < seq} log softmax(x_{b*seq+s} * weight^T)[t_{b*seq+s}]
+ *            = -(sum of the per-token losses of sequence b)
+ *
+ *   x        device bf16 [batch, seq, hidden] (row b*seq + s), as
+ *            lce_fused_linear_xent_fwd with tokens = batch * seq.
+ *   weight, hidden, vocab: as lce_fused_linear_xent_fwd.
+ *   target   device int64 [batch, seq]; an out-of-range target makes its
+ *            sequence's sum NaN.
+ *   out      device fp32 [batch]; must not overlap the inputs.  seq == 0
+ *            writes zeros; batch == 0 writes nothing.
+ *
+ * The sum over a sequence is a fixed-order reduction (bitwise reproducible).
+ * Returns as lce_fused_linear_xent_fwd.
+ */
+lce_status lce_fused_linear_logprob_sums(const void* x, const void* weight, int64_t batch,
+                                         int64_t seq, int64_t hidden, int64_t vocab,
+                                         const int64_t* target, float* out, hipStream_t stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* lce_status_string(lce_status status);
 

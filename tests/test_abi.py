@@ -199,3 +199,22 @@ def test_bwd_argument_errors(lib, kw, status, needle):
 
 def test_bwd_empty_is_a_no_op(lib):
     assert lce.lce_xent_bwd(0, lce.LCE_F32, 0, 8, 0, lce.LCE_REDUCTION_NONE, 0, 0, 0) == lce.LCE_OK
+
+
+def _sums(x=FAKE, w=FAKE + (1 << 24), batch=2, seq=4, hidden=64, vocab=100, target=FAKE + (1 << 28),
+          out=FAKE + (1 << 30)):
+    return lce.lce_fused_linear_logprob_sums(x, w, batch, seq, hidden, vocab, target, out, 0)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(out=0), lce.LCE_ERR_INVALID_ARG, "out is NULL"),
+    (dict(x=0), lce.LCE_ERR_INVALID_ARG, "x is NULL"),
+    (dict(batch=-1), lce.LCE_ERR_INVALID_ARG, "batch"),
+    (dict(seq=-3), lce.LCE_ERR_INVALID_ARG, "seq"),
+    (dict(batch=1 << 40, seq=1 << 40), lce.LCE_ERR_INVALID_ARG, "overflows"),
+    (dict(hidden=12), lce.LCE_ERR_UNSUPPORTED, "multiple of 8"),
+    (dict(out=FAKE + (1 << 28) + 8), lce.LCE_ERR_ALIAS, "target"),
+])
+def test_logprob_sums_argument_errors(lib, kw, status, needle):
+    assert _sums(**kw) == status
+    assert needle in lce.lce_last_error()

@@ -6,6 +6,7 @@ code:
 
 * :func:`lce_xent_fwd`, :func:`lce_fused_linear_xent_fwd`
 * :func:`lce_xent_bwd` (gradient with respect to the logits)
+* :func:`lce_fused_linear_logprob_sums` (per-sequence target log-probability sums)
 * :func:`lce_xent_partial_fwd`, :func:`lce_xent_merge` (vocab split across devices)
 * :func:`lce_status_string`, :func:`lce_last_error`, :func:`lce_version`
 
@@ -36,7 +37,8 @@ LCE_ERR_ALIAS = 3
 LCE_ERR_OOM = 4
 LCE_ERR_HIP = 5
 
-EXPORTED = ("lce_xent_fwd", "lce_xent_bwd", "lce_fused_linear_xent_fwd", "lce_xent_partial_fwd",
+EXPORTED = ("lce_xent_fwd", "lce_xent_bwd", "lce_fused_linear_xent_fwd",
+            "lce_fused_linear_logprob_sums", "lce_xent_partial_fwd",
             "lce_xent_merge", "lce_status_string", "lce_last_error", "lce_version")
 
 _lib = None
@@ -72,6 +74,10 @@ def load() -> ctypes.CDLL:
     lib.lce_xent_bwd.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
                                  ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                  ctypes.c_void_p]
+    lib.lce_fused_linear_logprob_sums.restype = ctypes.c_int
+    lib.lce_fused_linear_logprob_sums.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.lce_xent_partial_fwd.restype = ctypes.c_int
     lib.lce_xent_partial_fwd.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                          ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
@@ -109,6 +115,12 @@ def lce_xent_bwd(logits: int, dtype: int, tokens: int, vocab: int, target: int, 
                  grad: int, dlogits: int, stream: int) -> int:
     return load().lce_xent_bwd(logits or None, dtype, tokens, vocab, target or None, reduction,
                                grad or None, dlogits or None, stream or None)
+
+
+def lce_fused_linear_logprob_sums(x: int, weight: int, batch: int, seq: int, hidden: int,
+                                  vocab: int, target: int, out: int, stream: int) -> int:
+    return load().lce_fused_linear_logprob_sums(x or None, weight or None, batch, seq, hidden, vocab,
+                                                target or None, out or None, stream or None)
 
 
 def lce_xent_partial_fwd(logits: int, dtype: int, tokens: int, shard_vocab: int,
@@ -298,4 +310,29 @@ def xent_bwd(logits, target, grad, reduction: str = "mean", out=None):
                       _REDUCTIONS[reduction], grad.data_ptr(), out.data_ptr(), _stream_of(logits))
     if st != LCE_OK:
         raise LceError(st, "lce_xent_bwd")
+    return out
+
+
+def fused_linear_logprob_sums(x, weight, target, out=None):
+    """Per-sequence sums of target log-probabilities of ``x @ weight.T``: ``x`` bf16
+    ``[batch, seq, hidden]``, ``weight`` bf16 ``[vocab, hidden]``, ``target`` int64
+    ``[batch, seq]``; returns fp32 ``[batch]``."""
+    import torch
+    for name, t in (("x", x), ("weight", weight), ("target", target)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if x.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16 or target.dtype != torch.int64:
+        raise TypeError("x and weight must be bfloat16, target int64")
+    if x.dim() != 3 or weight.dim() != 2 or x.shape[-1] != weight.shape[1]:
+        raise ValueError("x must be [batch, seq, hidden] and weight [vocab, hidden]")
+    if tuple(target.shape) != tuple(x.shape[:2]):
+        raise ValueError("target must be [batch, seq]")
+    batch, seq, hidden = x.shape
+    if out is None:
+        out = torch.empty(batch, dtype=torch.float32, device=x.device)
+    st = lce_fused_linear_logprob_sums(x.data_ptr(), weight.data_ptr(), batch, seq, hidden,
+                                       weight.shape[0], target.data_ptr(), out.data_ptr(),
+                                       _stream_of(x))
+    if st != LCE_OK:
+        raise LceError(st, "lce_fused_linear_logprob_sums")
     return out

@@ -178,8 +178,10 @@ lce_status validate_xent(const void* logits, int dtype, int64_t tokens, int64_t 
   return LCE_OK;
 }
 
+// `out_floats` >= 0 overrides the output size implied by the reduction.
 lce_status validate_fused(const void* x, const void* w, int64_t tokens, int64_t hidden, int64_t vocab,
-                          const int64_t* target, int reduction, const float* out) {
+                          const int64_t* target, int reduction, const float* out,
+                          int64_t out_floats = -1) {
   lce_status s = validate_common(tokens, target, reduction, out);
   if (s != LCE_OK) return s;
   if (hidden < 1) return fail(LCE_ERR_INVALID_ARG, "hidden must be >= 1 (got %lld)", (long long)hidden);
@@ -196,7 +198,8 @@ lce_status validate_fused(const void* x, const void* w, int64_t tokens, int64_t 
     return fail(LCE_ERR_UNSUPPORTED, "x and weight must be 16-byte aligned");
   if (vocab > INT64_MAX / (hidden * 2) || tokens > INT64_MAX / (hidden * 2))
     return fail(LCE_ERR_INVALID_ARG, "tensor size overflows");
-  const uint64_t ob = out_bytes(tokens, reduction);
+  uint64_t ob = out_bytes(tokens, reduction);
+  if (out_floats >= 0) ob = (uint64_t)out_floats * 4u;
   if (overlaps(out, ob, x, (uint64_t)(tokens * hidden * 2))) return fail(LCE_ERR_ALIAS, "out overlaps x");
   if (overlaps(out, ob, w, (uint64_t)(vocab * hidden * 2))) return fail(LCE_ERR_ALIAS, "out overlaps weight");
   if (overlaps(out, ob, target, (uint64_t)tokens * 8u)) return fail(LCE_ERR_ALIAS, "out overlaps target");
@@ -298,6 +301,49 @@ lce_status run_rows(const void* logits, int dtype, int64_t tokens, int64_t vocab
   a.split_partials = (float*)(base + off_split);
 
   hipError_t e = lce::launch_xent(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return LCE_OK;
+}
+
+// The fused projection + cross-entropy for validated arguments, tokens > 0.
+// The first `reserved` bytes of scratch regions belong to the caller.
+lce_status run_fused(const void* x, const void* weight, int64_t tokens, int64_t hidden, int64_t vocab,
+                     const int64_t* target, bool mean, float* out, hipStream_t stream,
+                     size_t reserved = 0) {
+  lce_status s = LCE_OK;
+  int cus = 0;
+  if ((s = num_cus(&cus)) != LCE_OK) return s;
+
+  lce::FusedArgs a{};
+  a.x = x;
+  a.w = weight;
+  a.tokens = tokens;
+  a.hidden = hidden;
+  a.vocab = vocab;
+  a.target = target;
+  a.out = out;
+  a.reduce_mean = mean ? 1 : 0;
+  a.segments = lce::fused_segments(tokens, vocab, cus);
+  const int forced = env_int("LCE_FUSED_SEGMENTS", 0);
+  if (forced > 0) {
+    const lce::FusedGeometry g = lce::fused_geometry();
+    const int64_t n_voc = (vocab + g.block_vocab - 1) / g.block_vocab;
+    a.segments = (int)(forced < n_voc ? forced : n_voc);
+  }
+
+  Carve cv;
+  if (reserved) cv.take(reserved);
+  const size_t off_seg = cv.take((size_t)a.segments * (size_t)tokens * 8u);
+  const size_t off_zt = cv.take((size_t)tokens * 4u);
+  const size_t off_mean = cv.take((size_t)((tokens + lce::kRowThreads - 1) / lce::kRowThreads) * 8u);
+  char* base = nullptr;
+  if ((s = get_scratch(stream, cv.off, &base)) != LCE_OK) return s;
+  a.ticket = (unsigned*)base;
+  a.seg_partials = (float*)(base + off_seg);
+  a.target_logit = (float*)(base + off_zt);
+  a.mean_slots = (uint64_t*)(base + off_mean);
+
+  hipError_t e = lce::launch_fused(a, stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return LCE_OK;
 }
@@ -471,38 +517,38 @@ lce_status lce_fused_linear_xent_fwd(const void* x, const void* weight, int64_t 
     hipError_t e = lce::launch_fill_f32(out, 1, __builtin_nanf(""), stream);
     return e == hipSuccess ? LCE_OK : hip_fail(e, "launch");
   }
-  int cus = 0;
-  if ((s = num_cus(&cus)) != LCE_OK) return s;
+  return run_fused(x, weight, tokens, hidden, vocab, target, mean, out, stream);
+}
 
-  lce::FusedArgs a{};
-  a.x = x;
-  a.w = weight;
-  a.tokens = tokens;
-  a.hidden = hidden;
-  a.vocab = vocab;
-  a.target = target;
-  a.out = out;
-  a.reduce_mean = mean ? 1 : 0;
-  a.segments = lce::fused_segments(tokens, vocab, cus);
-  const int forced = env_int("LCE_FUSED_SEGMENTS", 0);
-  if (forced > 0) {
-    const lce::FusedGeometry g = lce::fused_geometry();
-    const int64_t n_voc = (vocab + g.block_vocab - 1) / g.block_vocab;
-    a.segments = (int)(forced < n_voc ? forced : n_voc);
+lce_status lce_fused_linear_logprob_sums(const void* x, const void* weight, int64_t batch,
+                                         int64_t seq, int64_t hidden, int64_t vocab,
+                                         const int64_t* target, float* out, hipStream_t stream) {
+  g_last_error.clear();
+  if (batch < 0 || seq < 0)
+    return fail(LCE_ERR_INVALID_ARG, "batch and seq must be >= 0 (got %lld, %lld)", (long long)batch,
+                (long long)seq);
+  if (seq > 0 && batch > INT64_MAX / seq) return fail(LCE_ERR_INVALID_ARG, "batch * seq overflows");
+  const int64_t tokens = batch * seq;
+  // Same checks as the fused call with per-token output; out holds `batch` floats.
+  if (batch > 0 && !out) return fail(LCE_ERR_INVALID_ARG, "out is NULL");
+  lce_status s = validate_fused(x, weight, tokens, hidden, vocab, target, LCE_REDUCTION_NONE,
+                                batch > 0 ? out : nullptr, batch);
+  if (s != LCE_OK) return s;
+  if (batch == 0) return LCE_OK;
+  if (seq == 0) {  // empty sequences: a sum of nothing
+    hipError_t e = lce::launch_fill_f32(out, batch, 0.0f, stream);
+    return e == hipSuccess ? LCE_OK : hip_fail(e, "launch");
   }
-
+  // Per-token losses into the front of scratch, then one wave per sequence.
   Carve cv;
-  const size_t off_seg = cv.take((size_t)a.segments * (size_t)tokens * 8u);
-  const size_t off_zt = cv.take((size_t)tokens * 4u);
-  const size_t off_mean = cv.take((size_t)((tokens + lce::kRowThreads - 1) / lce::kRowThreads) * 8u);
+  const size_t off_loss = cv.take((size_t)tokens * 4u);
   char* base = nullptr;
   if ((s = get_scratch(stream, cv.off, &base)) != LCE_OK) return s;
-  a.ticket = (unsigned*)base;
-  a.seg_partials = (float*)(base + off_seg);
-  a.target_logit = (float*)(base + off_zt);
-  a.mean_slots = (uint64_t*)(base + off_mean);
-
-  hipError_t e = lce::launch_fused(a, stream);
+  float* loss = (float*)(base + off_loss);
+  if ((s = run_fused(x, weight, tokens, hidden, vocab, target, false, loss, stream,
+                     (size_t)tokens * 4u)) != LCE_OK)
+    return s;
+  hipError_t e = lce::launch_seq_logprob_sums(loss, batch, seq, out, stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return LCE_OK;
 }

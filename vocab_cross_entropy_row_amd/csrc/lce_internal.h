@@ -87,6 +87,10 @@ FusedGeometry fused_geometry();
 int fused_segments(int64_t tokens, int64_t vocab, int num_cus);
 hipError_t launch_fused(const FusedArgs& a, hipStream_t stream);
 
+// out[b] = -sum of loss[b * seq .. b * seq + seq - 1] (per-sequence log-prob sums).
+hipError_t launch_seq_logprob_sums(const float* loss, int64_t batch, int64_t seq, float* out,
+                                   hipStream_t stream);
+
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t stream);
 hipError_t launch_zero_u32(unsigned* p, int64_t n, hipStream_t stream);
 
