@@ -269,3 +269,52 @@ def fused_linear_logprob_sums(x_bits: np.ndarray, w_bits: np.ndarray, target: np
         raise ValueError("oracle: tokens must equal batch * seq")
     per = per.reshape(batch, seq)
     return np.array([-math.fsum(per[b]) for b in range(batch)], dtype=np.float64)
+
+
+def _log_softmax_rows(z: np.ndarray) -> np.ndarray:
+    """Row-wise log-softmax in fp64 by the same two plain passes as the C oracle
+    (maximum, then the sum of exp(z - m)); vectorised over the rows of a block."""
+    m = z.max(axis=1, keepdims=True)
+    s = np.exp(z - m).sum(axis=1, keepdims=True)
+    return z - (m + np.log(s))
+
+
+def fused_linear_jsd_rows(xs_bits: np.ndarray, ws_bits: np.ndarray, xt_bits: np.ndarray,
+                          wt_bits: np.ndarray, beta: float = 0.5, block: int = 64) -> np.ndarray:
+    """Per-token generalized Jensen-Shannon divergence between the student and teacher
+    distributions, fp64 ("Fused linear + JSD": description and Semantics block).
+
+    P = softmax(x_s W_s^T) (student), Q = softmax(x_t W_t^T) (teacher), M = beta P +
+    (1 - beta) Q, and per token JSD = beta KL(P || M) + (1 - beta) KL(Q || M) with
+    KL(A || B) = sum_j A_j ln(A_j / B_j) (0 ln 0 = 0).  The page names "generalized JSD
+    (beta 0.5)" without printing it; this is the plain reading, symmetric at beta = 0.5.
+    Logits come from exactly widened bf16 operands and an fp64 matrix product.
+    """
+    xs_bits = np.ascontiguousarray(xs_bits, dtype=np.uint16)
+    xt_bits = np.ascontiguousarray(xt_bits, dtype=np.uint16)
+    ws64 = bf16_bits_to_f64(ws_bits).T
+    wt64 = bf16_bits_to_f64(wt_bits).T
+    rows = xs_bits.shape[0]
+    out = np.empty(rows, dtype=np.float64)
+    for b0 in range(0, rows, block):
+        lp = _log_softmax_rows(np.matmul(bf16_bits_to_f64(xs_bits[b0:b0 + block]), ws64))
+        lq = _log_softmax_rows(np.matmul(bf16_bits_to_f64(xt_bits[b0:b0 + block]), wt64))
+        P, Q = np.exp(lp), np.exp(lq)
+        M = beta * P + (1.0 - beta) * Q
+        with np.errstate(divide="ignore", invalid="ignore"):
+            logM = np.log(M)
+            kp = np.where(P > 0, P * (lp - logM), 0.0).sum(axis=1)
+            kq = np.where(Q > 0, Q * (lq - logM), 0.0).sum(axis=1)
+        out[b0:b0 + block] = beta * kp + (1.0 - beta) * kq
+    return out
+
+
+def fused_linear_jsd(xs_bits, ws_bits, xt_bits, wt_bits, beta: float = 0.5,
+                     reduction: str = "mean"):
+    """Generalized JSD loss: "mean" is the page's batchmean (sum over tokens / tokens)."""
+    per = fused_linear_jsd_rows(xs_bits, ws_bits, xt_bits, wt_bits, beta)
+    if reduction == "none":
+        return per
+    if reduction == "mean":
+        return mean(per)
+    raise ValueError(f"oracle: unknown reduction {reduction!r}")

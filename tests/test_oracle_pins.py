@@ -456,3 +456,87 @@ def test_logprob_sums_closed_forms(oracle_mod):
     xb = lce_synth.f32_to_bf16_bits(rng.normal(size=(12, 16)).astype(np.float32))
     assert np.allclose(oracle_mod.fused_linear_logprob_sums(xb, wb, t, 12, 1),
                        -oracle_mod.fused_linear_xent_rows(xb, wb, t), rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------- fused linear + JSD
+
+def _bf16(rng, shape, scale):
+    return lce_synth.f32_to_bf16_bits((rng.normal(size=shape) * scale).astype(np.float32))
+
+
+def test_jsd_of_identical_distributions_is_zero(oracle_mod):
+    rng = _rng(41)
+    x, w = _bf16(rng, (10, 32), 1.0), _bf16(rng, (300, 32), 0.3)
+    for beta in (0.5, 0.2, 0.9):
+        assert np.all(np.abs(oracle_mod.fused_linear_jsd_rows(x, w, x, w, beta)) <= 1e-14)
+
+
+def test_jsd_of_disjoint_point_masses(oracle_mod):
+    """Student all on class 0, teacher all on class 1: each KL term is -ln(beta) or
+    -ln(1 - beta), so JSD = -beta ln beta - (1 - beta) ln(1 - beta) (ln 2 at 0.5)."""
+    x = lce_synth.f32_to_bf16_bits(np.ones((3, 8), np.float32))
+    ws = np.zeros((4, 8), np.float32)
+    wt = np.zeros((4, 8), np.float32)
+    ws[0], wt[1] = 100.0, 100.0          # logit 800 vs 0: the other classes vanish in fp64
+    ws_b, wt_b = lce_synth.f32_to_bf16_bits(ws), lce_synth.f32_to_bf16_bits(wt)
+    for beta in (0.5, 0.25):
+        want = -beta * math.log(beta) - (1 - beta) * math.log(1 - beta)
+        got = oracle_mod.fused_linear_jsd_rows(x, ws_b, x, wt_b, beta)
+        assert np.allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_jsd_symmetric_and_bounded_at_half(oracle_mod):
+    rng = _rng(42)
+    xs, xt = _bf16(rng, (20, 64), 1.0), _bf16(rng, (20, 64), 1.0)
+    ws, wt = _bf16(rng, (500, 64), 0.4), _bf16(rng, (500, 64), 0.4)
+    a = oracle_mod.fused_linear_jsd_rows(xs, ws, xt, wt, 0.5)
+    b = oracle_mod.fused_linear_jsd_rows(xt, wt, xs, ws, 0.5)
+    assert np.allclose(a, b, rtol=0, atol=1e-14)
+    assert np.all(a >= 0.0) and np.all(a <= math.log(2) + 1e-15)
+
+
+def test_jsd_brute_force_tiny(oracle_mod):
+    """Exact rational GEMMs, 40-digit softmaxes and logarithms, beta = 0.3."""
+    rng = _rng(43)
+    T, H, V, beta = 3, 6, 5, Decimal("0.3")
+    xs, xt = _bf16(rng, (T, H), 1.0), _bf16(rng, (T, H), 1.0)
+    ws, wt = _bf16(rng, (V, H), 1.0), _bf16(rng, (V, H), 1.0)
+    getcontext().prec = 40
+
+    def logits(x, w, i):
+        xf, wf = oracle_mod.bf16_bits_to_f64(x), oracle_mod.bf16_bits_to_f64(w)
+        out = []
+        for j in range(V):
+            f = sum(Fraction(float(xf[i, k])) * Fraction(float(wf[j, k])) for k in range(H))
+            out.append(Decimal(f.numerator) / Decimal(f.denominator))
+        return out
+
+    want = []
+    for i in range(T):
+        zs, zt = logits(xs, ws, i), logits(xt, wt, i)
+        es, et = [v.exp() for v in zs], [v.exp() for v in zt]
+        P = [v / sum(es) for v in es]
+        Q = [v / sum(et) for v in et]
+        M = [beta * p + (1 - beta) * q for p, q in zip(P, Q)]
+        kp = sum(p * (p / m).ln() for p, m in zip(P, M))
+        kq = sum(q * (q / m).ln() for q, m in zip(Q, M))
+        want.append(float(beta * kp + (1 - beta) * kq))
+    got = oracle_mod.fused_linear_jsd_rows(xs, ws, xt, wt, 0.3)
+    assert np.allclose(got, want, rtol=0, atol=1e-13)
+
+
+def test_jsd_matches_library_kl_div(oracle_mod):
+    """torch kl_div (library routine, fp64) on the same fp64 logits."""
+    torch = pytest.importorskip("torch")
+    rng = _rng(44)
+    xs, xt = _bf16(rng, (16, 48), 1.0), _bf16(rng, (16, 48), 1.0)
+    ws, wt = _bf16(rng, (700, 48), 0.5), _bf16(rng, (700, 48), 0.5)
+    f = oracle_mod.bf16_bits_to_f64
+    lp = torch.log_softmax(torch.from_numpy(f(xs) @ f(ws).T), dim=1)
+    lq = torch.log_softmax(torch.from_numpy(f(xt) @ f(wt).T), dim=1)
+    beta = 0.5
+    lm = torch.log(beta * lp.exp() + (1 - beta) * lq.exp())
+    kl = torch.nn.functional.kl_div
+    ref = beta * kl(lm, lp, reduction="batchmean", log_target=True) + \
+        (1 - beta) * kl(lm, lq, reduction="batchmean", log_target=True)
+    assert oracle_mod.fused_linear_jsd(xs, ws, xt, wt, beta, "mean") == pytest.approx(ref.item(), abs=1e-13)
