@@ -53,7 +53,7 @@ extern "C" {
 #endif
 
 #define LCE_VERSION_MAJOR 0
-#define LCE_VERSION_MINOR 2
+#define LCE_VERSION_MINOR 3
 #define LCE_VERSION_PATCH 0
 
 typedef enum {
@@ -207,7 +207,7 @@ lce_status lce_xent_merge(const float* partials, int64_t shards, int64_t tokens,
  *   x         device bf16 [tokens, hidden], row-major ([batch, seq, hidden]
  *             passed as tokens = batch * seq, row = b * seq + s).
  *   weight    device bf16 [vocab, hidden], row-major (one row per class).
- *   tokens    >= 0;  hidden >= 1 and a multiple of 8;  1 <= vocab < 2^31.
+ *   tokens    >= 0;  1 <= hidden < 2^22, a multiple of 8;  1 <= vocab < 2^31.
  *   target    device int64 [tokens].
  *   reduction LCE_REDUCTION_MEAN or LCE_REDUCTION_NONE, as for lce_xent_fwd.
  *   out       device fp32, 1 or `tokens` elements; must not overlap inputs.
@@ -247,6 +247,40 @@ lce_status lce_fused_linear_xent_fwd(const void* x, const void* weight, int64_t 
 lce_status lce_fused_linear_logprob_sums(const void* x, const void* weight, int64_t batch,
                                          int64_t seq, int64_t hidden, int64_t vocab,
                                          const int64_t* target, float* out, hipStream_t stream);
+
+/*
+ * Generalized Jensen-Shannon divergence between a student and a teacher
+ * distribution, each from its own fused projection (KernelIndex "Fused linear +
+ * JSD": description and Semantics block; beta 0.5 and "batchmean" there).
+ * With P = softmax(student_x * student_weight^T), Q = softmax(teacher_x *
+ * teacher_weight^T) and M = beta P + (1 - beta) Q, per token
+ *
+ *     jsd = beta KL(P || M) + (1 - beta) KL(Q || M),   KL(A || B) = sum_j A_j ln(A_j / B_j)
+ *
+ * (the page names the divergence without printing it; this is the usual
+ * generalized form, symmetric at beta = 0.5).  Neither head's logits are
+ * stored: a first pass takes each head's per-token log-sum-exp, a second
+ * recomputes both heads' logits tile by tile and sums the divergence terms.
+ *
+ *   student_x, teacher_x            device bf16 [tokens, hidden], row-major.
+ *   student_weight, teacher_weight  device bf16 [vocab, hidden], row-major.
+ *   tokens >= 0;  1 <= hidden < 2^22, a multiple of 8;  1 <= vocab < 2^31.
+ *   beta       in (0, 1); 0.5 is the page's setting.
+ *   reduction  LCE_REDUCTION_MEAN: out[0] = sum of jsd over tokens / tokens
+ *              ("batchmean"; NaN for tokens == 0), a fixed-order reduction
+ *              (bitwise reproducible).  LCE_REDUCTION_NONE: out[i] = jsd of
+ *              token i (nothing written for tokens == 0).
+ *   out        device fp32, 1 or `tokens` elements; must not overlap inputs.
+ *   stream     HIP stream.
+ *
+ * Returns LCE_ERR_INVALID_ARG for a NULL pointer, a bad size, reduction or
+ * beta; LCE_ERR_UNSUPPORTED as lce_fused_linear_xent_fwd; LCE_ERR_ALIAS when
+ * out overlaps an input; LCE_ERR_HIP / LCE_ERR_OOM as lce_xent_fwd.
+ */
+lce_status lce_fused_linear_jsd_fwd(const void* student_x, const void* student_weight,
+                                    const void* teacher_x, const void* teacher_weight,
+                                    int64_t tokens, int64_t hidden, int64_t vocab, float beta,
+                                    lce_reduction reduction, float* out, hipStream_t stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* lce_status_string(lce_status status);

@@ -203,6 +203,42 @@ WORKLOADS = {
         1005, 2005, w_std=0.02, w_seed=3005),
 }
 
+@dataclasses.dataclass(frozen=True)
+class JsdWorkload:
+    """Student and teacher activations and heads for the fused linear + JSD workload:
+    four independent bf16 draws, activations N(0, x_std^2) and heads N(0, w_std^2)."""
+    name: str
+    tokens: int
+    hidden: int
+    vocab: int
+    x_std: float
+    w_std: float
+    seeds: tuple         # (student x, student head, teacher x, teacher head)
+    reduction: str = "mean"
+
+    def student_x(self, row0: int = 0, row1: int | None = None, threads: int | None = None):
+        return normal_bf16_bits(self.seeds[0], STREAM_LOGITS, self.tokens, self.hidden, self.x_std,
+                                row0, row1, threads)
+
+    def student_weight(self, row0: int = 0, row1: int | None = None, threads: int | None = None):
+        return normal_bf16_bits(self.seeds[1], STREAM_WEIGHT, self.vocab, self.hidden, self.w_std,
+                                row0, row1, threads)
+
+    def teacher_x(self, row0: int = 0, row1: int | None = None, threads: int | None = None):
+        return normal_bf16_bits(self.seeds[2], STREAM_LOGITS, self.tokens, self.hidden, self.x_std,
+                                row0, row1, threads)
+
+    def teacher_weight(self, row0: int = 0, row1: int | None = None, threads: int | None = None):
+        return normal_bf16_bits(self.seeds[3], STREAM_WEIGHT, self.vocab, self.hidden, self.w_std,
+                                row0, row1, threads)
+
+
+# "Fused linear + JSD" (tokens 1024 of the page's 1024..8192 sweep, hidden 4096,
+# vocab 128256, bf16, beta 0.5, batchmean).  Head std 0.02 gives logits of std
+# about 1.3, as for the fused cross-entropy workload.
+JSD = JsdWorkload("jsd_bf16_t1024_h4096_v128256_mean", 1024, 4096, 128256, 1.0, 0.02,
+                  (1006, 3006, 1007, 3007))
+
 # The small case the oracle finishes in seconds, and the headline benchmark workload.
 SMALL = "ce_f32_16384x4096_mean"
 HEADLINE = "megatron_bf16_2048x4x4096_none"

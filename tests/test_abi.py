@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lce.lce_version() == 200
+    assert lce.lce_version() == 300
     names = [lce.lce_status_string(s) for s in range(6)]
     assert names == ["LCE_OK", "LCE_ERR_INVALID_ARG", "LCE_ERR_UNSUPPORTED", "LCE_ERR_ALIAS",
                      "LCE_ERR_OOM", "LCE_ERR_HIP"]
@@ -101,6 +101,7 @@ def _fused(x=FAKE, w=FAKE + (1 << 24), tokens=8, hidden=64, vocab=100, target=FA
     (dict(hidden=0), lce.LCE_ERR_INVALID_ARG, "hidden"),
     (dict(vocab=0), lce.LCE_ERR_INVALID_ARG, "vocab"),
     (dict(hidden=60), lce.LCE_ERR_UNSUPPORTED, "multiple of 8"),
+    (dict(hidden=1 << 22), lce.LCE_ERR_UNSUPPORTED, "2^22"),
     (dict(x=FAKE + 8), lce.LCE_ERR_UNSUPPORTED, "16-byte"),
     (dict(w=FAKE + (1 << 24) + 8), lce.LCE_ERR_UNSUPPORTED, "16-byte"),
     (dict(reduction=3), lce.LCE_ERR_INVALID_ARG, "reduction"),
@@ -218,3 +219,38 @@ def _sums(x=FAKE, w=FAKE + (1 << 24), batch=2, seq=4, hidden=64, vocab=100, targ
 def test_logprob_sums_argument_errors(lib, kw, status, needle):
     assert _sums(**kw) == status
     assert needle in lce.lce_last_error()
+
+
+def _jsd(xs=FAKE, ws=FAKE + (1 << 24), xt=FAKE + (2 << 24), wt=FAKE + (3 << 24), tokens=8,
+         hidden=64, vocab=100, beta=0.5, reduction=lce.LCE_REDUCTION_NONE, out=FAKE + (1 << 30)):
+    return lce.lce_fused_linear_jsd_fwd(xs, ws, xt, wt, tokens, hidden, vocab, beta, reduction,
+                                        out, 0)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(out=0), lce.LCE_ERR_INVALID_ARG, "out is NULL"),
+    (dict(xs=0), lce.LCE_ERR_INVALID_ARG, "student_x is NULL"),
+    (dict(ws=0), lce.LCE_ERR_INVALID_ARG, "student_weight is NULL"),
+    (dict(xt=0), lce.LCE_ERR_INVALID_ARG, "teacher_x is NULL"),
+    (dict(wt=0), lce.LCE_ERR_INVALID_ARG, "teacher_weight is NULL"),
+    (dict(tokens=-1), lce.LCE_ERR_INVALID_ARG, "tokens"),
+    (dict(hidden=0), lce.LCE_ERR_INVALID_ARG, "hidden"),
+    (dict(vocab=0), lce.LCE_ERR_INVALID_ARG, "vocab"),
+    (dict(hidden=20), lce.LCE_ERR_UNSUPPORTED, "multiple of 8"),
+    (dict(hidden=1 << 22), lce.LCE_ERR_UNSUPPORTED, "2^22"),
+    (dict(xt=FAKE + (2 << 24) + 8), lce.LCE_ERR_UNSUPPORTED, "16-byte"),
+    (dict(beta=0.0), lce.LCE_ERR_INVALID_ARG, "beta"),
+    (dict(beta=1.0), lce.LCE_ERR_INVALID_ARG, "beta"),
+    (dict(beta=float("nan")), lce.LCE_ERR_INVALID_ARG, "beta"),
+    (dict(reduction=2), lce.LCE_ERR_INVALID_ARG, "reduction"),
+    (dict(out=FAKE + 16), lce.LCE_ERR_ALIAS, "student_x"),
+    (dict(out=FAKE + (3 << 24) + 64), lce.LCE_ERR_ALIAS, "teacher_weight"),
+])
+def test_jsd_argument_errors(lib, kw, status, needle):
+    assert _jsd(**kw) == status
+    assert needle in lce.lce_last_error()
+
+
+def test_jsd_empty_none_is_a_no_op(lib):
+    assert lce.lce_fused_linear_jsd_fwd(0, FAKE, 0, FAKE, 0, 64, 100, 0.5, lce.LCE_REDUCTION_NONE,
+                                        0, 0) == lce.LCE_OK

@@ -38,7 +38,7 @@ LCE_ERR_OOM = 4
 LCE_ERR_HIP = 5
 
 EXPORTED = ("lce_xent_fwd", "lce_xent_bwd", "lce_fused_linear_xent_fwd",
-            "lce_fused_linear_logprob_sums", "lce_xent_partial_fwd",
+            "lce_fused_linear_logprob_sums", "lce_fused_linear_jsd_fwd", "lce_xent_partial_fwd",
             "lce_xent_merge", "lce_status_string", "lce_last_error", "lce_version")
 
 _lib = None
@@ -78,6 +78,11 @@ def load() -> ctypes.CDLL:
     lib.lce_fused_linear_logprob_sums.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                                   ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.lce_fused_linear_jsd_fwd.restype = ctypes.c_int
+    lib.lce_fused_linear_jsd_fwd.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                             ctypes.c_int64, ctypes.c_float, ctypes.c_int,
+                                             ctypes.c_void_p, ctypes.c_void_p]
     lib.lce_xent_partial_fwd.restype = ctypes.c_int
     lib.lce_xent_partial_fwd.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                          ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
@@ -121,6 +126,15 @@ def lce_fused_linear_logprob_sums(x: int, weight: int, batch: int, seq: int, hid
                                   vocab: int, target: int, out: int, stream: int) -> int:
     return load().lce_fused_linear_logprob_sums(x or None, weight or None, batch, seq, hidden, vocab,
                                                 target or None, out or None, stream or None)
+
+
+def lce_fused_linear_jsd_fwd(student_x: int, student_weight: int, teacher_x: int,
+                             teacher_weight: int, tokens: int, hidden: int, vocab: int,
+                             beta: float, reduction: int, out: int, stream: int) -> int:
+    return load().lce_fused_linear_jsd_fwd(student_x or None, student_weight or None,
+                                           teacher_x or None, teacher_weight or None, tokens,
+                                           hidden, vocab, beta, reduction, out or None,
+                                           stream or None)
 
 
 def lce_xent_partial_fwd(logits: int, dtype: int, tokens: int, shard_vocab: int,
@@ -335,4 +349,45 @@ def fused_linear_logprob_sums(x, weight, target, out=None):
                                        _stream_of(x))
     if st != LCE_OK:
         raise LceError(st, "lce_fused_linear_logprob_sums")
+    return out
+
+
+def fused_linear_jsd(student_x, student_weight, teacher_x, teacher_weight, beta: float = 0.5,
+                     reduction: str = "mean", out=None):
+    """Generalized JSD between softmax(student_x @ student_weight.T) and
+    softmax(teacher_x @ teacher_weight.T) without storing either head's logits.
+
+    Activations bf16 [..., hidden] (same shape for both), heads bf16 [vocab, hidden].
+    ``reduction="mean"`` is the batch mean (one fp32 element), ``"none"`` the
+    per-token divergence with the leading shape of the activations."""
+    import torch
+    if reduction not in _REDUCTIONS:
+        raise ValueError(f"reduction must be 'mean' or 'none', got {reduction!r}")
+    named = (("student_x", student_x), ("student_weight", student_weight),
+             ("teacher_x", teacher_x), ("teacher_weight", teacher_weight))
+    for name, t in named:
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16")
+    if student_weight.dim() != 2 or tuple(teacher_weight.shape) != tuple(student_weight.shape):
+        raise ValueError("student_weight and teacher_weight must both be [vocab, hidden]")
+    if tuple(student_x.shape) != tuple(teacher_x.shape) or student_x.dim() < 1:
+        raise ValueError("student_x and teacher_x must have the same shape [..., hidden]")
+    vocab, hidden = student_weight.shape
+    if student_x.shape[-1] != hidden:
+        raise ValueError("activations' last axis must be the heads' hidden size")
+    lead = tuple(student_x.shape[:-1])
+    tokens = 1
+    for d in lead:
+        tokens *= d
+    if out is None:
+        shape = (1,) if reduction == "mean" else lead
+        out = torch.empty(shape, dtype=torch.float32, device=student_x.device)
+    st = lce_fused_linear_jsd_fwd(student_x.data_ptr(), student_weight.data_ptr(),
+                                  teacher_x.data_ptr(), teacher_weight.data_ptr(), tokens, hidden,
+                                  vocab, float(beta), _REDUCTIONS[reduction], out.data_ptr(),
+                                  _stream_of(student_x))
+    if st != LCE_OK:
+        raise LceError(st, "lce_fused_linear_jsd_fwd")
     return out

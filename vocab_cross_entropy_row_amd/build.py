@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblce.so")
 
-SOURCES = ["lce_api.cpp", "xent_kernels.hip", "fused_kernel.hip", "bwd_kernels.hip", "seq_kernels.hip"]
+SOURCES = ["lce_api.cpp", "xent_kernels.hip", "fused_kernel.hip", "bwd_kernels.hip", "seq_kernels.hip",
+           "jsd_kernel.hip"]
 ARCH = "gfx950"
 
 

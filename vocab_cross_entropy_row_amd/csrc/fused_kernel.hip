@@ -31,11 +31,10 @@
 
 #include "lce_device.h"
 #include "lce_internal.h"
+#include "mfma_common.h"
 
 namespace lce {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // Tile shape: WV x WT waves, each owning BVB x BTB blocks of 32 x 32; K-slabs
 // of 64 hidden elements (one 128-byte LDS row per W row and per token).  W
@@ -63,31 +62,6 @@ struct Tile {
 // fill the 160 KiB of LDS.
 typedef Tile<2, 4, 4, 2, 3, 2> FusedTile;
 
-
-// Physical 16-byte chunk of logical chunk `c` in LDS row `r` (rows of 128 B):
-// a ds_read_b128 of 8 or 16 consecutive rows at one logical chunk touches
-// every bank once.  The map is its own inverse.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r & 7) ^ ((r >> 3) & 1)); }
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// Workgroup barrier ordering LDS accesses only.  __syncthreads() also orders
-// global memory, which makes the compiler drain every outstanding load
-// (vmcnt(0)) at the barrier, including the slab DMAs meant to stay in flight
-// across it; their completion is waited for explicitly (wait_vmcnt).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
-  __asm__ volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  __asm__ volatile("" ::: "memory");
-}
-
-// s_waitcnt vmcnt(N) with the other counters left free (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N <= 63, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | (0xF << 8) | (0x7 << 4) | (N & 0xF));
-}
 
 // Fold one token column of a finished tile into that token's running state and
 // capture its target logit.  acc[a][v] is the logit of vocab row
@@ -174,7 +148,7 @@ __global__ __launch_bounds__(TL::kThreads) void fused_xent_partial_kernel(
 #pragma unroll
   for (int j = 0; j < BTB; ++j) {
     tok[j] = t0 + wt * (BTB * 32) + j * 32 + (lane & 31);
-    const int64_t t = (tok[j] < tokens) ? target[tok[j]] : -1;
+    const int64_t t = (target && tok[j] < tokens) ? target[tok[j]] : -1;
     tgt[j] = (t >= 0 && t < vocab) ? (int)t : -1;
   }
 
@@ -413,12 +387,13 @@ __global__ __launch_bounds__(TL::kThreads) void fused_xent_partial_kernel(
 __global__ __launch_bounds__(kRowThreads) void fused_xent_merge_kernel(
     int64_t tokens, int64_t vocab, int segments, const float2* __restrict__ part,
     const float* __restrict__ zt, const int64_t* __restrict__ target, float* __restrict__ out,
-    uint64_t* __restrict__ slots, unsigned* __restrict__ ticket, int reduce_mean) {
+    float* __restrict__ lse_out, uint64_t* __restrict__ slots, unsigned* __restrict__ ticket,
+    int reduce_mean) {
   const int64_t row = (int64_t)blockIdx.x * kRowThreads + threadIdx.x;
   float loss = 0.0f;
   if (row < tokens) {
-    const int64_t t = target[row];
-    const float z = zt[row];
+    const int64_t t = lse_out ? -1 : target[row];
+    const float z = lse_out ? 0.0f : zt[row];
     constexpr int kGroup = 8;
     Lse st = lse_empty();
     for (int s0 = 0; s0 < segments; s0 += kGroup) {
@@ -428,6 +403,10 @@ __global__ __launch_bounds__(kRowThreads) void fused_xent_merge_kernel(
         p[j] = (s0 + j < segments) ? part[(int64_t)(s0 + j) * tokens + row] : make_float2(kNegInf, 0.0f);
 #pragma unroll
       for (int j = 0; j < kGroup; ++j) st = lse_merge(st, Lse{p[j].x, p[j].y});
+    }
+    if (lse_out) {  // ln sum_j e^z_j = m + ln2 * (log2 s - (m*log2e - fp32(m*log2e)))
+      lse_out[row] = st.m + kLn2 * (log2_fast(st.s) - __builtin_fmaf(st.m, kLog2e, -(st.m * kLog2e)));
+      return;
     }
     loss = (t >= 0 && t < vocab) ? lse_minus(st, z) : __builtin_nanf("");
     if (!reduce_mean) out[row] = loss;
@@ -468,7 +447,7 @@ hipError_t launch_fused(const FusedArgs& a, hipStream_t stream) {
   const int64_t blocks = (a.tokens + kRowThreads - 1) / kRowThreads;
   hipLaunchKernelGGL(fused_xent_merge_kernel, dim3((unsigned)blocks), dim3(kRowThreads), 0, stream,
                      a.tokens, a.vocab, a.segments, (const float2*)a.seg_partials,
-                     (const float*)a.target_logit, a.target, a.out, a.mean_slots, a.ticket,
+                     (const float*)a.target_logit, a.target, a.out, a.lse_out, a.mean_slots, a.ticket,
                      a.reduce_mean);
   return hipGetLastError();
 }

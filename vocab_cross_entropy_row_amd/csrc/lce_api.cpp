@@ -133,7 +133,7 @@ int env_int(const char* name, int dflt) {
 
 // ------------------------------------------------------------ validation (host only)
 lce_status validate_common(int64_t tokens, const int64_t* target, int reduction, const float* out,
-                           const char* out_name = "out") {
+                           const char* out_name = "out", bool has_target = true) {
   if (reduction != LCE_REDUCTION_MEAN && reduction != LCE_REDUCTION_NONE)
     return fail(LCE_ERR_INVALID_ARG, "reduction must be LCE_REDUCTION_MEAN or LCE_REDUCTION_NONE (got %d)", reduction);
   if (tokens < 0) return fail(LCE_ERR_INVALID_ARG, "tokens must be >= 0 (got %lld)", (long long)tokens);
@@ -142,7 +142,7 @@ lce_status validate_common(int64_t tokens, const int64_t* target, int reduction,
   // out_name == nullptr: the caller checks its own output.
   const bool writes = out_name && (reduction == LCE_REDUCTION_MEAN || tokens > 0);
   if (writes && !out) return fail(LCE_ERR_INVALID_ARG, "%s is NULL", out_name);
-  if (tokens > 0 && !target) return fail(LCE_ERR_INVALID_ARG, "target is NULL");
+  if (has_target && tokens > 0 && !target) return fail(LCE_ERR_INVALID_ARG, "target is NULL");
   if (target && !aligned(target, 8)) return fail(LCE_ERR_INVALID_ARG, "target is not 8-byte aligned");
   if (out && !aligned(out, 4)) return fail(LCE_ERR_INVALID_ARG, "%s is not 4-byte aligned", out_name);
   return LCE_OK;
@@ -179,29 +179,41 @@ lce_status validate_xent(const void* logits, int dtype, int64_t tokens, int64_t 
 }
 
 // `out_floats` >= 0 overrides the output size implied by the reduction.
+// One bf16 projection: activations x [tokens, hidden] and head w [vocab, hidden],
+// against an output of `ob` bytes.
+lce_status validate_head(const void* x, const void* w, int64_t tokens, int64_t hidden, int64_t vocab,
+                         const float* out, uint64_t ob, const char* xn = "x",
+                         const char* wn = "weight") {
+  if (hidden < 1) return fail(LCE_ERR_INVALID_ARG, "hidden must be >= 1 (got %lld)", (long long)hidden);
+  if (vocab < 1) return fail(LCE_ERR_INVALID_ARG, "vocab must be >= 1 (got %lld)", (long long)vocab);
+  if (vocab >= (int64_t(1) << 31))
+    return fail(LCE_ERR_UNSUPPORTED, "vocab must be < 2^31 (got %lld)", (long long)vocab);
+  // The kernels address a tile of up to 256 rows through one buffer resource
+  // with 32-bit offsets, and mark a slab past the end of a row with an offset
+  // of 0x7ffffff0: 256 rows * 2 bytes * hidden must stay below it.
+  if (hidden >= (int64_t(1) << 22))
+    return fail(LCE_ERR_UNSUPPORTED, "hidden must be < 2^22 (got %lld)", (long long)hidden);
+  if (!w) return fail(LCE_ERR_INVALID_ARG, "%s is NULL", wn);
+  if (tokens > 0 && !x) return fail(LCE_ERR_INVALID_ARG, "%s is NULL", xn);
+  if (hidden % 8 != 0)
+    return fail(LCE_ERR_UNSUPPORTED, "hidden must be a multiple of 8 (got %lld)", (long long)hidden);
+  if (!aligned(w, 16) || (x && !aligned(x, 16)))
+    return fail(LCE_ERR_UNSUPPORTED, "%s and %s must be 16-byte aligned", xn, wn);
+  if (vocab > INT64_MAX / (hidden * 2) || tokens > INT64_MAX / (hidden * 2))
+    return fail(LCE_ERR_INVALID_ARG, "tensor size overflows");
+  if (overlaps(out, ob, x, (uint64_t)(tokens * hidden * 2))) return fail(LCE_ERR_ALIAS, "out overlaps %s", xn);
+  if (overlaps(out, ob, w, (uint64_t)(vocab * hidden * 2))) return fail(LCE_ERR_ALIAS, "out overlaps %s", wn);
+  return LCE_OK;
+}
+
 lce_status validate_fused(const void* x, const void* w, int64_t tokens, int64_t hidden, int64_t vocab,
                           const int64_t* target, int reduction, const float* out,
                           int64_t out_floats = -1) {
   lce_status s = validate_common(tokens, target, reduction, out);
   if (s != LCE_OK) return s;
-  if (hidden < 1) return fail(LCE_ERR_INVALID_ARG, "hidden must be >= 1 (got %lld)", (long long)hidden);
-  if (vocab < 1) return fail(LCE_ERR_INVALID_ARG, "vocab must be >= 1 (got %lld)", (long long)vocab);
-  if (vocab >= (int64_t(1) << 31))
-    return fail(LCE_ERR_UNSUPPORTED, "vocab must be < 2^31 (got %lld)", (long long)vocab);
-  if (hidden >= (int64_t(1) << 31))
-    return fail(LCE_ERR_UNSUPPORTED, "hidden must be < 2^31 (got %lld)", (long long)hidden);
-  if (!w) return fail(LCE_ERR_INVALID_ARG, "weight is NULL");
-  if (tokens > 0 && !x) return fail(LCE_ERR_INVALID_ARG, "x is NULL");
-  if (hidden % 8 != 0)
-    return fail(LCE_ERR_UNSUPPORTED, "hidden must be a multiple of 8 (got %lld)", (long long)hidden);
-  if (!aligned(w, 16) || (x && !aligned(x, 16)))
-    return fail(LCE_ERR_UNSUPPORTED, "x and weight must be 16-byte aligned");
-  if (vocab > INT64_MAX / (hidden * 2) || tokens > INT64_MAX / (hidden * 2))
-    return fail(LCE_ERR_INVALID_ARG, "tensor size overflows");
   uint64_t ob = out_bytes(tokens, reduction);
   if (out_floats >= 0) ob = (uint64_t)out_floats * 4u;
-  if (overlaps(out, ob, x, (uint64_t)(tokens * hidden * 2))) return fail(LCE_ERR_ALIAS, "out overlaps x");
-  if (overlaps(out, ob, w, (uint64_t)(vocab * hidden * 2))) return fail(LCE_ERR_ALIAS, "out overlaps weight");
+  if ((s = validate_head(x, w, tokens, hidden, vocab, out, ob)) != LCE_OK) return s;
   if (overlaps(out, ob, target, (uint64_t)tokens * 8u)) return fail(LCE_ERR_ALIAS, "out overlaps target");
   return LCE_OK;
 }
@@ -305,14 +317,42 @@ lce_status run_rows(const void* logits, int dtype, int64_t tokens, int64_t vocab
   return LCE_OK;
 }
 
+// Scratch plan of the fused projection + cross-entropy: vocab segments and the
+// offsets of its regions after the caller's `reserved` bytes.
+struct FusedPlan {
+  int segments = 1;
+  size_t off_seg = 0, off_zt = 0, off_mean = 0, end = 0;
+};
+
+FusedPlan plan_fused(int64_t tokens, int64_t vocab, int cus, size_t reserved) {
+  FusedPlan p;
+  p.segments = lce::fused_segments(tokens, vocab, cus);
+  const int forced = env_int("LCE_FUSED_SEGMENTS", 0);
+  if (forced > 0) {
+    const lce::FusedGeometry g = lce::fused_geometry();
+    const int64_t n_voc = (vocab + g.block_vocab - 1) / g.block_vocab;
+    p.segments = (int)(forced < n_voc ? forced : n_voc);
+  }
+  Carve cv;
+  if (reserved) cv.take(reserved);
+  p.off_seg = cv.take((size_t)p.segments * (size_t)tokens * 8u);
+  p.off_zt = cv.take((size_t)tokens * 4u);
+  p.off_mean = cv.take((size_t)((tokens + lce::kRowThreads - 1) / lce::kRowThreads) * 8u);
+  p.end = cv.off;
+  return p;
+}
+
 // The fused projection + cross-entropy for validated arguments, tokens > 0.
-// The first `reserved` bytes of scratch regions belong to the caller.
+// The first `reserved` bytes of scratch regions belong to the caller.  With
+// lse_out set, writes ln sum_j e^(z_j) per token there instead of losses
+// (target and out are then unused).
 lce_status run_fused(const void* x, const void* weight, int64_t tokens, int64_t hidden, int64_t vocab,
                      const int64_t* target, bool mean, float* out, hipStream_t stream,
-                     size_t reserved = 0) {
+                     size_t reserved = 0, float* lse_out = nullptr) {
   lce_status s = LCE_OK;
   int cus = 0;
   if ((s = num_cus(&cus)) != LCE_OK) return s;
+  const FusedPlan p = plan_fused(tokens, vocab, cus, reserved);
 
   lce::FusedArgs a{};
   a.x = x;
@@ -320,28 +360,18 @@ lce_status run_fused(const void* x, const void* weight, int64_t tokens, int64_t 
   a.tokens = tokens;
   a.hidden = hidden;
   a.vocab = vocab;
-  a.target = target;
-  a.out = out;
-  a.reduce_mean = mean ? 1 : 0;
-  a.segments = lce::fused_segments(tokens, vocab, cus);
-  const int forced = env_int("LCE_FUSED_SEGMENTS", 0);
-  if (forced > 0) {
-    const lce::FusedGeometry g = lce::fused_geometry();
-    const int64_t n_voc = (vocab + g.block_vocab - 1) / g.block_vocab;
-    a.segments = (int)(forced < n_voc ? forced : n_voc);
-  }
+  a.target = lse_out ? nullptr : target;
+  a.out = lse_out ? nullptr : out;
+  a.lse_out = lse_out;
+  a.reduce_mean = (mean && !lse_out) ? 1 : 0;
+  a.segments = p.segments;
 
-  Carve cv;
-  if (reserved) cv.take(reserved);
-  const size_t off_seg = cv.take((size_t)a.segments * (size_t)tokens * 8u);
-  const size_t off_zt = cv.take((size_t)tokens * 4u);
-  const size_t off_mean = cv.take((size_t)((tokens + lce::kRowThreads - 1) / lce::kRowThreads) * 8u);
   char* base = nullptr;
-  if ((s = get_scratch(stream, cv.off, &base)) != LCE_OK) return s;
+  if ((s = get_scratch(stream, p.end, &base)) != LCE_OK) return s;
   a.ticket = (unsigned*)base;
-  a.seg_partials = (float*)(base + off_seg);
-  a.target_logit = (float*)(base + off_zt);
-  a.mean_slots = (uint64_t*)(base + off_mean);
+  a.seg_partials = (float*)(base + p.off_seg);
+  a.target_logit = (float*)(base + p.off_zt);
+  a.mean_slots = (uint64_t*)(base + p.off_mean);
 
   hipError_t e = lce::launch_fused(a, stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
@@ -549,6 +579,73 @@ lce_status lce_fused_linear_logprob_sums(const void* x, const void* weight, int6
                      (size_t)tokens * 4u)) != LCE_OK)
     return s;
   hipError_t e = lce::launch_seq_logprob_sums(loss, batch, seq, out, stream);
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return LCE_OK;
+}
+
+lce_status lce_fused_linear_jsd_fwd(const void* student_x, const void* student_weight,
+                                    const void* teacher_x, const void* teacher_weight,
+                                    int64_t tokens, int64_t hidden, int64_t vocab, float beta,
+                                    lce_reduction reduction, float* out, hipStream_t stream) {
+  g_last_error.clear();
+  lce_status s = validate_common(tokens, nullptr, (int)reduction, out, "out", false);
+  if (s != LCE_OK) return s;
+  const uint64_t ob = out_bytes(tokens, (int)reduction);
+  if ((s = validate_head(student_x, student_weight, tokens, hidden, vocab, out, ob, "student_x",
+                         "student_weight")) != LCE_OK)
+    return s;
+  if ((s = validate_head(teacher_x, teacher_weight, tokens, hidden, vocab, out, ob, "teacher_x",
+                         "teacher_weight")) != LCE_OK)
+    return s;
+  if (!(beta > 0.0f && beta < 1.0f))
+    return fail(LCE_ERR_INVALID_ARG, "beta must be in (0, 1) (got %g)", (double)beta);
+  const bool mean = reduction == LCE_REDUCTION_MEAN;
+  if (tokens == 0) {
+    if (!mean) return LCE_OK;
+    hipError_t e = lce::launch_fill_f32(out, 1, __builtin_nanf(""), stream);
+    return e == hipSuccess ? LCE_OK : hip_fail(e, "launch");
+  }
+  int cus = 0;
+  if ((s = num_cus(&cus)) != LCE_OK) return s;
+
+  // Scratch: both heads' log-sum-exp, the divergence kernel's per-segment
+  // sums and mean slots, then the cross-entropy kernel's own regions.
+  lce::JsdArgs a{};
+  a.xs = student_x;
+  a.ws = student_weight;
+  a.xt = teacher_x;
+  a.wt = teacher_weight;
+  a.tokens = tokens;
+  a.hidden = hidden;
+  a.vocab = vocab;
+  a.beta = beta;
+  a.out = out;
+  a.reduce_mean = mean ? 1 : 0;
+  a.segments = lce::jsd_segments(tokens, vocab, cus);
+  Carve cv;
+  const size_t off_ls = cv.take((size_t)tokens * 4u);
+  const size_t off_lt = cv.take((size_t)tokens * 4u);
+  const size_t off_part = cv.take((size_t)a.segments * (size_t)tokens * 4u);
+  const size_t off_mean = cv.take((size_t)((tokens + lce::kRowThreads - 1) / lce::kRowThreads) * 8u);
+  const size_t reserved = cv.off - Carve().off;
+  const FusedPlan fp = plan_fused(tokens, vocab, cus, reserved);
+  char* base = nullptr;
+  if ((s = get_scratch(stream, fp.end > cv.off ? fp.end : cv.off, &base)) != LCE_OK) return s;
+  float* lse_s = (float*)(base + off_ls);
+  float* lse_t = (float*)(base + off_lt);
+  a.lse_s = lse_s;
+  a.lse_t = lse_t;
+  a.partials = (float*)(base + off_part);
+  a.mean_slots = (uint64_t*)(base + off_mean);
+  a.ticket = (unsigned*)base;
+
+  if ((s = run_fused(student_x, student_weight, tokens, hidden, vocab, nullptr, false, nullptr,
+                     stream, reserved, lse_s)) != LCE_OK)
+    return s;
+  if ((s = run_fused(teacher_x, teacher_weight, tokens, hidden, vocab, nullptr, false, nullptr,
+                     stream, reserved, lse_t)) != LCE_OK)
+    return s;
+  hipError_t e = lce::launch_jsd(a, stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return LCE_OK;
 }

@@ -71,6 +71,8 @@ struct FusedArgs {
   const int64_t* target;
   float* out;
   int reduce_mean;
+  float* lse_out;         // non-null: write ln sum_j e^z_j per token instead of losses
+                          // (target may then be null)
   int segments;           // vocab segments (workgroups per token block)
   float* seg_partials;    // segments * tokens (max, sum-exp) pairs
   float* target_logit;    // tokens fp32
@@ -90,6 +92,28 @@ hipError_t launch_fused(const FusedArgs& a, hipStream_t stream);
 // out[b] = -sum of loss[b * seq .. b * seq + seq - 1] (per-sequence log-prob sums).
 hipError_t launch_seq_logprob_sums(const float* loss, int64_t batch, int64_t seq, float* out,
                                    hipStream_t stream);
+
+// Fused projection + generalized JSD between a student and a teacher head.
+struct JsdArgs {
+  const void* xs;           // bf16 [tokens, hidden], student activations
+  const void* ws;           // bf16 [vocab, hidden], student head
+  const void* xt;           // teacher activations
+  const void* wt;           // teacher head
+  int64_t tokens;
+  int64_t hidden;
+  int64_t vocab;
+  float beta;
+  const float* lse_s;       // [tokens] ln sum_j e^(student logits)
+  const float* lse_t;       // [tokens] the same for the teacher
+  float* out;
+  int reduce_mean;
+  int segments;
+  float* partials;          // [segments, tokens]
+  uint64_t* mean_slots;
+  unsigned* ticket;
+};
+int jsd_segments(int64_t tokens, int64_t vocab, int num_cus);
+hipError_t launch_jsd(const JsdArgs& a, hipStream_t stream);
 
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t stream);
 hipError_t launch_zero_u32(unsigned* p, int64_t n, hipStream_t stream);
