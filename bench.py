@@ -69,7 +69,7 @@ CSRC = os.path.join(ROOT, "vocab_cross_entropy_row_amd", "csrc")
 # Sources that define each workload's dominant kernel (plus the build flags).
 KERNEL_SOURCES = {
     "xent": ["xent_kernels.hip", "row_stream.h", "lce_device.h", "lce_internal.h"],
-    "fused": ["fused_kernel.hip", "lce_device.h", "lce_internal.h"],
+    "fused": ["fused_kernel.hip", "mfma_common.h", "lce_device.h", "lce_internal.h"],
 }
 
 
@@ -321,6 +321,63 @@ def time_logprob_sums(torch, lce, lce_synth, steps: int, warmup: int) -> dict:
                          "unit": "TFLOP/s", "frac": round(tf / BF16_DENSE_TFLOPS, 4)}}
 
 
+def time_jsd(torch, lce, lce_synth, steps: int, warmup: int) -> dict:
+    """Fused linear + JSD at the JSD page's shape (tokens 1024, hidden 4096, vocab 128256,
+    beta 0.5, batchmean), timed as a HIP graph of `steps` calls, on the default path
+    (logits stored in scratch) and on the recompute path (LCE_JSD_STORE_BYTES=0).
+    Algorithmic flops: both heads' logits once, 2 * 2*T*H*V."""
+    w = lce_synth.JSD
+    xs, ws, xt, wt = (_to_dev(b, torch) for b in (w.student_x(), w.student_weight(),
+                                                   w.teacher_x(), w.teacher_weight()))
+    out = torch.empty(1, dtype=torch.float32, device="cuda")
+    flops = 2 * fused_flops(w.tokens, w.hidden, w.vocab)
+    res = {"shape": f"tokens {w.tokens}, hidden {w.hidden}, vocab {w.vocab}, beta 0.5, batchmean",
+           "algorithmic_flops": flops}
+    for label, env in (("stored", None), ("recompute", "0")):
+        old = os.environ.get("LCE_JSD_STORE_BYTES")
+        if env is not None:
+            os.environ["LCE_JSD_STORE_BYTES"] = env
+        try:
+            for _ in range(max(1, warmup)):
+                lce.fused_linear_jsd(xs, ws, xt, wt, 0.5, "mean", out=out)
+            torch.cuda.synchronize()
+            val = out.item()
+            g = torch.cuda.CUDAGraph()
+            st = torch.cuda.Stream()
+            st.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(st):
+                lce.fused_linear_jsd(xs, ws, xt, wt, 0.5, "mean", out=out)
+            torch.cuda.current_stream().wait_stream(st)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=st):
+                for _ in range(steps):
+                    lce.fused_linear_jsd(xs, ws, xt, wt, 0.5, "mean", out=out)
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(st):
+                e0.record(st)
+                g.replay()
+                e1.record(st)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1000.0 / steps
+            del g
+        finally:
+            if env is not None:
+                if old is None:
+                    os.environ.pop("LCE_JSD_STORE_BYTES", None)
+                else:
+                    os.environ["LCE_JSD_STORE_BYTES"] = old
+        tf = flops / (us * 1e-6) / 1e12
+        res[label] = {"us_per_step": round(us, 1), "batchmean": val,
+                      "roofline": {"bound": "mfma", "achieved": round(tf, 1),
+                                   "peak": BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
+                                   "frac": round(tf / BF16_DENSE_TFLOPS, 4)}}
+    del xs, ws, xt, wt
+    torch.cuda.empty_cache()
+    return res
+
+
 def time_vocab_shard(torch, lce, lce_synth, tp: int, steps: int, warmup: int) -> dict:
     """The headline workload with its vocab split over `tp` devices, as one device sees it:
     statistics of its [tokens, vocab/tp] shard (lce_xent_partial_fwd, timed over rotating
@@ -560,6 +617,7 @@ def main(argv=None) -> int:
 
     shard = None
     sums = None
+    jsd = None
     backward = {}
     if args.workloads == "all" and not args.eager:
         for bname in (lce_synth.HEADLINE, "ce_f32_16384x4096_mean"):
@@ -569,6 +627,10 @@ def main(argv=None) -> int:
                   f"({backward[bname]['roofline']['achieved']} GB/s)", file=sys.stderr, flush=True)
         shard = time_vocab_shard(torch, lce, lce_synth, 8, min(args.steps, 200), args.warmup)
         sums = time_logprob_sums(torch, lce, lce_synth, min(args.steps, 10), 2)
+        jsd = time_jsd(torch, lce, lce_synth, min(args.steps, 10), 2)
+        print(f"[bench] fused linear + JSD: stored {jsd['stored']['us_per_step']:.1f} µs "
+              f"({jsd['stored']['roofline']['achieved']} TFLOP/s), recompute "
+              f"{jsd['recompute']['us_per_step']:.1f} µs", file=sys.stderr, flush=True)
         print(f"[bench] fused log-prob sums: {sums['us_per_step']:.1f} µs "
               f"({sums['roofline']['achieved']} TFLOP/s)", file=sys.stderr, flush=True)
         print(f"[bench] vocab shard tp=8: partial {shard['partial_us']:.2f} µs, "
@@ -617,6 +679,8 @@ def main(argv=None) -> int:
         line["backward"] = backward
     if sums is not None:
         line["fused_logprob_sums"] = sums
+    if jsd is not None:
+        line["fused_linear_jsd"] = jsd
     print(json.dumps(line), flush=True)
     return 0
 

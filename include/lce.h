@@ -28,11 +28,14 @@
  *   - Results are bitwise reproducible run to run for the same inputs, shape
  *     and device: every reduction has a fixed order and no float atomics are
  *     used (the pages do not specify determinism).
- *   - liblce keeps a small device scratch buffer per (device, stream), grown
- *     on demand with hipMalloc.  An outgrown buffer is retired, never freed:
- *     every scratch buffer is kept until the process ends.  Calls on one
- *     stream are ordered by the stream; calls on different streams use
- *     different scratch buffers.
+ *   - liblce keeps a device scratch buffer per (device, stream), grown on
+ *     demand with hipMalloc to 1.25x the need.  It is small (per-token and
+ *     per-workgroup partials) except for lce_fused_linear_jsd_fwd, which
+ *     keeps up to LCE_JSD_STORE_BYTES (default 2 GiB) of logits there.  An
+ *     outgrown buffer is retired, never freed: every scratch buffer is kept
+ *     until the process ends, so the retired ones add up to at most 4x the
+ *     live one.  Calls on one stream are ordered by the stream; calls on
+ *     different streams use different scratch buffers.
  *   - HIP graph capture: a call may be captured if an earlier, uncaptured
  *     call on the same stream and device already grew its scratch far enough
  *     (the largest shape to be captured is enough); otherwise the call fails
@@ -258,9 +261,15 @@ lce_status lce_fused_linear_logprob_sums(const void* x, const void* weight, int6
  *     jsd = beta KL(P || M) + (1 - beta) KL(Q || M),   KL(A || B) = sum_j A_j ln(A_j / B_j)
  *
  * (the page names the divergence without printing it; this is the usual
- * generalized form, symmetric at beta = 0.5).  Neither head's logits are
- * stored: a first pass takes each head's per-token log-sum-exp, a second
- * recomputes both heads' logits tile by tile and sums the divergence terms.
+ * generalized form, symmetric at beta = 0.5).  Each head's logits are formed
+ * once by the fused projection, which also takes the head's per-token
+ * log-sum-exp and writes the fp32 logits of a chunk of tokens to scratch; a
+ * streaming pass then sums the divergence terms.  The chunk is the largest
+ * multiple of 256 tokens whose two heads' logits (8 * tokens * vocab bytes,
+ * vocab rounded up to 256) fit in LCE_JSD_STORE_BYTES (environment, default
+ * 2 GiB).  With LCE_JSD_STORE_BYTES=0, or too large a vocab, no logits are
+ * stored: a second pass recomputes both heads' logits tile by tile (about
+ * twice the time).
  *
  *   student_x, teacher_x            device bf16 [tokens, hidden], row-major.
  *   student_weight, teacher_weight  device bf16 [vocab, hidden], row-major.

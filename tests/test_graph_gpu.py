@@ -2,7 +2,8 @@
 
 The benchmark times graph replays, so replays must give the eager results bit for
 bit: every kernel path (one wave per row, one workgroup per row, split rows, the
-fused projection) with and without the last-workgroup mean, whose ticket counters
+fused projection, fused linear + JSD with stored logits, in chunks, and recomputed)
+with and without the last-workgroup mean, whose ticket counters
 must be back at zero after each replay.  Between replays the program does eager
 work of its own (other liblce calls on the same stream, torch kernels, host
 synchronisations), and each replay first finds its outputs overwritten with NaN.
@@ -54,8 +55,22 @@ def _fused_case(seed, tokens, hidden, vocab, reduction, env):
     return call, out
 
 
+def _jsd_case(seed, tokens, hidden, vocab, reduction, env):
+    xs, xt = (to_dev(lce_synth.normal_bf16_bits(seed + k, 0, tokens, hidden, 1.0)) for k in (0, 1))
+    ws, wt = (to_dev(lce_synth.normal_bf16_bits(seed + k, 2, vocab, hidden, 0.1)) for k in (2, 3))
+    out = torch.empty((1,) if reduction == "mean" else (tokens,), dtype=torch.float32, device="cuda")
+
+    def call():
+        with forced_env(**env):
+            lce.fused_linear_jsd(xs, ws, xt, wt, 0.5, reduction, out=out)
+    return call, out
+
+
 def _cases():
     return [
+        _jsd_case(109, 300, 128, 2000, "mean", {}),
+        _jsd_case(110, 520, 64, 1001, "none", {"LCE_JSD_STORE_BYTES": 256 * 1024 * 8}),
+        _jsd_case(111, 200, 128, 1500, "mean", {"LCE_JSD_STORE_BYTES": 0}),
         _row_case(101, 1000, 3000, "bf16", "mean", {"LCE_PATH": "wave"}),
         _row_case(102, 777, 4099, "f32", "none", {"LCE_PATH": "wave"}),
         _row_case(103, 600, 20000, "f32", "mean", {"LCE_PATH": "block"}),

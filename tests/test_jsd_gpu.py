@@ -23,7 +23,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 import vocab_cross_entropy_row_amd as lce  # noqa: E402
-from gpu_util import to_dev  # noqa: E402
+from gpu_util import forced_env, to_dev  # noqa: E402
 
 ABS, REL = 1e-4, 1e-3
 
@@ -53,51 +53,80 @@ def _check(got, want):
     assert (err <= bound).all(), f"token {i}: got {got[i]!r}, want {want[i]!r}"
 
 
-def _run(bits, beta=0.5, reduction="none"):
+# Paths: logits stored in scratch for all tokens at once (default), stored in chunks of
+# one 256-token fused tile, and recomputed tile by tile (no logit storage).
+MODES = ("stored", "chunked", "recompute")
+
+
+def _env(mode, vocab):
+    if mode == "recompute":
+        return {"LCE_JSD_STORE_BYTES": 0}
+    if mode == "chunked":
+        ld = -(-vocab // 256) * 256
+        return {"LCE_JSD_STORE_BYTES": 256 * ld * 8}
+    return {}
+
+
+def _run(bits, beta=0.5, reduction="none", mode="stored"):
     xs, ws, xt, wt = (to_dev(b) for b in bits)
-    out = lce.fused_linear_jsd(xs, ws, xt, wt, beta, reduction)
+    with forced_env(**_env(mode, bits[1].shape[0])):
+        out = lce.fused_linear_jsd(xs, ws, xt, wt, beta, reduction)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
 
 # Ragged in every dimension: tokens off the 128-token tile, vocab off the 128-row
 # tile, hidden off the 64-element slab; one token; several tiles per vocab segment.
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("tokens,hidden,vocab", [(1, 64, 100), (5, 128, 1000), (130, 72, 3000),
                                                  (300, 200, 515), (257, 64, 128),
-                                                 (128, 256, 20000)])
-def test_per_token_matches_oracle(tokens, hidden, vocab):
+                                                 (600, 64, 1001), (128, 256, 20000)])
+def test_per_token_matches_oracle(tokens, hidden, vocab, mode):
     bits = _inputs(tokens + vocab, tokens, hidden, vocab)
-    _check(_run(bits), oracle.fused_linear_jsd_rows(*bits))
+    _check(_run(bits, mode=mode), oracle.fused_linear_jsd_rows(*bits))
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("beta", [0.1, 0.5, 0.9])
-def test_batchmean_matches_oracle(beta):
-    bits = _inputs(11, 200, 128, 1500)
-    got = _run(bits, beta, "mean")
+def test_batchmean_matches_oracle(beta, mode):
+    bits = _inputs(11, 520, 128, 1500)
+    got = _run(bits, beta, "mean", mode)
     assert got.shape == (1,)
     _check(got, np.array([oracle.fused_linear_jsd(*bits, beta=beta, reduction="mean")]))
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("beta", [0.2, 0.75])
-def test_other_beta_per_token(beta):
+def test_other_beta_per_token(beta, mode):
     bits = _inputs(21, 70, 64, 700)
-    _check(_run(bits, beta), oracle.fused_linear_jsd_rows(*bits, beta=beta))
+    _check(_run(bits, beta, mode=mode), oracle.fused_linear_jsd_rows(*bits, beta=beta))
 
 
-def test_identical_heads_give_zero():
+@pytest.mark.parametrize("mode", MODES)
+def test_identical_heads_give_zero(mode):
     xs, ws, _, _ = _inputs(31, 150, 128, 2000)
-    got = _run((xs, ws, xs, ws))
+    got = _run((xs, ws, xs, ws), mode=mode)
     assert np.abs(got).max() <= ABS
 
 
-def test_peaked_disjoint_distributions_approach_ln2():
+@pytest.mark.parametrize("mode", MODES)
+def test_peaked_disjoint_distributions_approach_ln2(mode):
     # Logits of std about 16: each distribution sits on a few classes, rarely the
     # same ones, so the divergence at beta 0.5 is close to its ln 2 ceiling.
     bits = _inputs(41, 64, 256, 1000, x_std=1.0, w_std=1.0)
-    got = _run(bits)
+    got = _run(bits, mode=mode)
     want = oracle.fused_linear_jsd_rows(*bits)
     _check(got, want)
     assert np.median(want) > 0.6 and (got <= math.log(2) + ABS).all()
+
+
+def test_paths_agree_on_many_tokens():
+    # Stored in one piece, in 256-token chunks, and recomputed: the same values up
+    # to fp32 summation order.
+    bits = _inputs(71, 1100, 128, 4100)
+    got = {m: _run(bits, mode=m) for m in MODES}
+    assert np.abs(got["stored"] - got["chunked"]).max() <= 1e-6
+    assert np.abs(got["stored"] - got["recompute"]).max() <= 1e-5
 
 
 def test_symmetric_at_half():
@@ -116,14 +145,16 @@ def test_empty_batchmean_is_nan_and_none_writes_nothing():
     assert out.item() == 7.0
 
 
-def test_repeated_calls_bitwise_identical():
+@pytest.mark.parametrize("mode", MODES)
+def test_repeated_calls_bitwise_identical(mode):
     bits = _inputs(61, 400, 128, 5000)
     xs, ws, xt, wt = (to_dev(b) for b in bits)
-    first_none = lce.fused_linear_jsd(xs, ws, xt, wt, 0.5, "none").clone()
-    first_mean = lce.fused_linear_jsd(xs, ws, xt, wt, 0.5, "mean").clone()
-    for _ in range(4):
-        assert torch.equal(lce.fused_linear_jsd(xs, ws, xt, wt, 0.5, "none"), first_none)
-        assert torch.equal(lce.fused_linear_jsd(xs, ws, xt, wt, 0.5, "mean"), first_mean)
+    with forced_env(**_env(mode, 5000)):
+        first_none = lce.fused_linear_jsd(xs, ws, xt, wt, 0.5, "none").clone()
+        first_mean = lce.fused_linear_jsd(xs, ws, xt, wt, 0.5, "mean").clone()
+        for _ in range(4):
+            assert torch.equal(lce.fused_linear_jsd(xs, ws, xt, wt, 0.5, "none"), first_none)
+            assert torch.equal(lce.fused_linear_jsd(xs, ws, xt, wt, 0.5, "mean"), first_mean)
 
 
 def test_page_shape_sampled_against_oracle():
@@ -132,9 +163,13 @@ def test_page_shape_sampled_against_oracle():
     xs, ws, xt, wt = (to_dev(b) for b in (xs_b, ws_b, xt_b, wt_b))
     per = lce.fused_linear_jsd(xs, ws, xt, wt, 0.5, "none").double()
     mean = lce.fused_linear_jsd(xs, ws, xt, wt, 0.5, "mean")
+    with forced_env(LCE_JSD_STORE_BYTES=0):
+        per_rc = lce.fused_linear_jsd(xs, ws, xt, wt, 0.5, "none").double()
     torch.cuda.synchronize()
     ref = per.mean().item()
     assert abs(mean.item() - ref) <= ABS + REL * abs(ref)
+    assert torch.max(torch.abs(per - per_rc)).item() <= 1e-5
     rows = np.r_[0:6, 509:515, 1018:1024]
     want = oracle.fused_linear_jsd_rows(xs_b[rows], ws_b, xt_b[rows], wt_b)
     _check(per.cpu().numpy()[rows], want)
+    _check(per_rc.cpu().numpy()[rows], want)

@@ -116,11 +116,29 @@ __device__ __forceinline__ void fold_tile_column(Lse& st, const f32x16 (&acc)[BV
   }
 }
 
-template <class TL, int BVB, int BTB, int WV>
+// Store the logits of a finished tile into z [tokens, z_ld] fp32 (token
+// rows): for each (a, v/4) the lane's four consecutive vocab rows of its token
+// are one 16-byte store.  `zr` covers the rows of this token tile that exist,
+// so stores for tokens past the end are dropped; z_ld is a multiple of the
+// tile's vocab extent, so columns past vocab land in the row's padding.
+template <int BVB>
+__device__ __forceinline__ void store_tile_column(__amdgpu_buffer_rsrc_t zr, const f32x16 (&acc)[BVB],
+                                                  uint32_t voff) {
+#pragma unroll
+  for (int a = 0; a < BVB; ++a)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 q = {acc[a][4 * g], acc[a][4 * g + 1], acc[a][4 * g + 2], acc[a][4 * g + 3]};
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, q), zr,
+                                             voff + (uint32_t)(a * 32 + 8 * g) * 4u, 0, 0);
+    }
+}
+
+template <class TL, int BVB, int BTB, int WV, bool STORE>
 __global__ __launch_bounds__(TL::kThreads) void fused_xent_partial_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int64_t tokens, int64_t hidden,
     int64_t vocab, const int64_t* __restrict__ target, int segments, float2* __restrict__ part,
-    float* __restrict__ zt_out) {
+    float* __restrict__ zt_out, float* __restrict__ z_out, int64_t z_ld) {
   __shared__ __attribute__((aligned(1024))) uint16_t lds[TL::kLdsElems];
   constexpr int kXBase = TL::kWStages * TL::kWStageElems;  // x stages follow the W stages
 
@@ -175,6 +193,16 @@ __global__ __launch_bounds__(TL::kThreads) void fused_xent_partial_kernel(
   const int n_iter = (tile1 - tile0) * nk;
   const uint32_t x_rows = (uint32_t)((tokens - t0) < TL::kBT ? (tokens - t0) : TL::kBT);
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + t0 * hidden, x_rows * row_bytes);
+  // Logit rows of this token tile (STORE only); byte offset of this lane's
+  // first row and column, relative to vocab tile 0.
+  const __amdgpu_buffer_rsrc_t zr = make_rsrc(z_out + t0 * z_ld, STORE ? x_rows * (uint32_t)z_ld * 4u : 0u);
+  uint32_t z_voff[BTB];
+  if constexpr (STORE) {
+#pragma unroll
+    for (int b = 0; b < BTB; ++b)
+      z_voff[b] = ((uint32_t)(wt * (BTB * 32) + b * 32 + (lane & 31)) * (uint32_t)z_ld +
+                   (uint32_t)(wv * (BVB * 32) + 4 * half)) * 4u;
+  }
 
   // W block of vocab tile `tile` as a buffer resource (rows past vocab read 0).
   auto w_rsrc = [&](int tile) {
@@ -338,6 +366,11 @@ __global__ __launch_bounds__(TL::kThreads) void fused_xent_partial_kernel(
 
     // Epilogue of the finished tile, one token column at a time.
     const int64_t vbase = (int64_t)tile * TL::kBV + wv * (BVB * 32);
+    if constexpr (STORE) {
+#pragma unroll
+      for (int b = 0; b < BTB; ++b)
+        store_tile_column<BVB>(zr, acc[b], z_voff[b] + (uint32_t)tile * (uint32_t)TL::kBV * 4u);
+    }
     if (vbase + BVB * 32 > vocab) {
 #pragma unroll
       for (int b = 0; b < BTB; ++b)
@@ -438,10 +471,16 @@ int fused_segments(int64_t tokens, int64_t vocab, int num_cus) {
 hipError_t launch_fused(const FusedArgs& a, hipStream_t stream) {
   const int64_t n_tok = (a.tokens + FusedTile::kBT - 1) / FusedTile::kBT;
   const int64_t grid = n_tok * a.segments;
-  hipLaunchKernelGGL((fused_xent_partial_kernel<FusedTile, 4, 2, 2>), dim3((unsigned)grid),
-                     dim3(FusedTile::kThreads), 0, stream, (const uint16_t*)a.x,
-                     (const uint16_t*)a.w, a.tokens, a.hidden, a.vocab, a.target, a.segments,
-                     (float2*)a.seg_partials, a.target_logit);
+  if (a.z_out)
+    hipLaunchKernelGGL((fused_xent_partial_kernel<FusedTile, 4, 2, 2, true>), dim3((unsigned)grid),
+                       dim3(FusedTile::kThreads), 0, stream, (const uint16_t*)a.x,
+                       (const uint16_t*)a.w, a.tokens, a.hidden, a.vocab, a.target, a.segments,
+                       (float2*)a.seg_partials, a.target_logit, a.z_out, a.z_ld);
+  else
+    hipLaunchKernelGGL((fused_xent_partial_kernel<FusedTile, 4, 2, 2, false>), dim3((unsigned)grid),
+                       dim3(FusedTile::kThreads), 0, stream, (const uint16_t*)a.x,
+                       (const uint16_t*)a.w, a.tokens, a.hidden, a.vocab, a.target, a.segments,
+                       (float2*)a.seg_partials, a.target_logit, nullptr, (int64_t)0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t blocks = (a.tokens + kRowThreads - 1) / kRowThreads;

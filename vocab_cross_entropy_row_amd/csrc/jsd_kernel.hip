@@ -35,6 +35,21 @@
 
 namespace lce {
 
+// One vocab entry's divergence term  beta P (ln P - ln M) + (1 - beta) Q (ln Q - ln M)
+// from lp = ln P and lq = ln Q.  Relative to mx = max(lp, lq): ln M = mx + ln S
+// with S = beta e^u + (1 - beta) e^w >= min(beta, 1 - beta), u = lp - mx and
+// w = lq - mx (one of them 0), so no underflowing P, Q or M reaches the
+// logarithm, and a term below the fp32 range is 0.
+__device__ __forceinline__ float jsd_term(float lp, float lq, float beta) {
+  const float mx = __builtin_fmaxf(lp, lq);
+  const float u = lp - mx, w = lq - mx;
+  const float e = exp2_fast((u + w) * kLog2e);  // e^(-|lp - lq|)
+  const float eu = lp >= lq ? 1.0f : e;
+  const float ew = lp >= lq ? e : 1.0f;
+  const float ls = kLn2 * log2_fast(beta * eu + (1.0f - beta) * ew);
+  return exp2_fast(mx * kLog2e) * (beta * eu * (u - ls) + (1.0f - beta) * ew * (w - ls));
+}
+
 namespace {
 constexpr int kJV = 128;                  // vocab rows per tile
 constexpr int kJT = 128;                  // tokens per tile
@@ -173,18 +188,7 @@ __global__ __launch_bounds__(kJThreads) void fused_jsd_partial_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int64_t j = vbase + a * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-        const float lp = acc_s[a][v] - As;  // ln P_j
-        const float lq = acc_t[a][v] - At;  // ln Q_j
-        // Relative to mx = max(ln P_j, ln Q_j): ln M_j = mx + ln S with
-        // S = beta e^u + (1 - beta) e^w >= min(beta, 1 - beta), so no
-        // underflowing P, Q or M can reach the logarithm.
-        const float mx = __builtin_fmaxf(lp, lq);
-        const float u = lp - mx, w = lq - mx;         // one of them is 0
-        const float e = exp2_fast((u + w) * kLog2e);  // e^(-|ln P_j - ln Q_j|)
-        const float eu = lp >= lq ? 1.0f : e;
-        const float ew = lp >= lq ? e : 1.0f;
-        const float ls = kLn2 * log2_fast(beta * eu + (1.0f - beta) * ew);
-        const float term = exp2_fast(mx * kLog2e) * (beta * eu * (u - ls) + (1.0f - beta) * ew * (w - ls));
+        const float term = jsd_term(acc_s[a][v] - As, acc_t[a][v] - At, beta);
         jsd += j < vocab ? term : 0.0f;
       }
   }
@@ -203,6 +207,59 @@ __global__ __launch_bounds__(kJThreads) void fused_jsd_partial_kernel(
 #pragma unroll
     for (int q = 1; q < kJWV; ++q) s += red[q * kJT + tl];
     part[(int64_t)seg * tokens + tok] = s;
+  }
+}
+
+// Divergence of token rows whose logits are stored: zs and zt are [rows, z_ld]
+// fp32 (the first vocab columns of each row are the logits), lse_s / lse_t the
+// rows' log-sum-exp.  One workgroup per row streams both rows with 16-byte
+// buffer loads (kJRU chunks of each per lane in flight) and writes the row's
+// sum to dst[row].  Summation order is fixed: per lane in chunk order, then
+// the wave and workgroup reductions.
+namespace {
+constexpr int kJRThreads = 256;
+constexpr int kJRU = 4;
+constexpr int kJRPolicy = 2;  // nontemporal: each stored logit is read once
+}  // namespace
+
+__global__ __launch_bounds__(kJRThreads) void jsd_stored_rows_kernel(
+    const float* __restrict__ zs, const float* __restrict__ zt, int64_t z_ld, int64_t vocab,
+    const float* __restrict__ lse_s, const float* __restrict__ lse_t, float beta,
+    float* __restrict__ dst) {
+  const int64_t row = blockIdx.x;
+  const float As = lse_s[row];
+  const float At = lse_t[row];
+  const uint32_t bytes = (uint32_t)vocab * 4u;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(zs + row * z_ld, bytes);
+  const __amdgpu_buffer_rsrc_t rt = make_rsrc(zt + row * z_ld, bytes);
+  const int nch = (int)((vocab + 3) / 4);
+  float acc = 0.0f;
+  for (int c0 = threadIdx.x; c0 < nch; c0 += kJRThreads * kJRU) {
+    f32x4 a[kJRU], b[kJRU];
+#pragma unroll
+    for (int u = 0; u < kJRU; ++u) {
+      const uint32_t off = (uint32_t)(c0 + u * kJRThreads) * 16u;  // past the row: reads 0
+      a[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kJRPolicy));
+      b[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rt, off, 0, kJRPolicy));
+    }
+#pragma unroll
+    for (int u = 0; u < kJRU; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t j = (int64_t)(c0 + u * kJRThreads) * 4 + e;
+        const float t = jsd_term(a[u][e] - As, b[u][e] - At, beta);
+        acc += j < vocab ? t : 0.0f;
+      }
+  }
+  acc = wave_sum(acc);
+  __shared__ float red[kJRThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float tot = red[0];
+#pragma unroll
+    for (int q = 1; q < kJRThreads / 64; ++q) tot += red[q];
+    dst[row] = tot;
   }
 }
 
@@ -251,6 +308,20 @@ hipError_t launch_jsd(const JsdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(fused_jsd_merge_kernel, dim3((unsigned)blocks), dim3(kRowThreads), 0, stream,
                      a.tokens, a.segments, (const float*)a.partials, a.out, a.mean_slots, a.ticket,
                      a.reduce_mean);
+  return hipGetLastError();
+}
+
+hipError_t launch_jsd_rows(const JsdRowsArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(jsd_stored_rows_kernel, dim3((unsigned)a.rows), dim3(kJRThreads), 0, stream,
+                     a.zs, a.zt, a.z_ld, a.vocab, a.lse_s, a.lse_t, a.beta, a.dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_jsd_mean(int64_t tokens, const float* per_token, float* out, uint64_t* slots,
+                           unsigned* ticket, hipStream_t stream) {
+  const int64_t blocks = (tokens + kRowThreads - 1) / kRowThreads;
+  hipLaunchKernelGGL(fused_jsd_merge_kernel, dim3((unsigned)blocks), dim3(kRowThreads), 0, stream,
+                     tokens, 1, per_token, out, slots, ticket, 1);
   return hipGetLastError();
 }
 

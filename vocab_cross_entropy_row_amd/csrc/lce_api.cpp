@@ -131,6 +131,11 @@ int env_int(const char* name, int dflt) {
   return (v && *v) ? atoi(v) : dflt;
 }
 
+int64_t env_int64(const char* name, int64_t dflt) {
+  const char* v = getenv(name);
+  return (v && *v) ? (int64_t)strtoll(v, nullptr, 10) : dflt;
+}
+
 // ------------------------------------------------------------ validation (host only)
 lce_status validate_common(int64_t tokens, const int64_t* target, int reduction, const float* out,
                            const char* out_name = "out", bool has_target = true) {
@@ -345,10 +350,12 @@ FusedPlan plan_fused(int64_t tokens, int64_t vocab, int cus, size_t reserved) {
 // The fused projection + cross-entropy for validated arguments, tokens > 0.
 // The first `reserved` bytes of scratch regions belong to the caller.  With
 // lse_out set, writes ln sum_j e^(z_j) per token there instead of losses
-// (target and out are then unused).
+// (target and out are then unused).  With z_out set, the logits are also
+// stored there as [tokens, z_ld] fp32 rows.
 lce_status run_fused(const void* x, const void* weight, int64_t tokens, int64_t hidden, int64_t vocab,
                      const int64_t* target, bool mean, float* out, hipStream_t stream,
-                     size_t reserved = 0, float* lse_out = nullptr) {
+                     size_t reserved = 0, float* lse_out = nullptr, float* z_out = nullptr,
+                     int64_t z_ld = 0) {
   lce_status s = LCE_OK;
   int cus = 0;
   if ((s = num_cus(&cus)) != LCE_OK) return s;
@@ -363,6 +370,8 @@ lce_status run_fused(const void* x, const void* weight, int64_t tokens, int64_t 
   a.target = lse_out ? nullptr : target;
   a.out = lse_out ? nullptr : out;
   a.lse_out = lse_out;
+  a.z_out = z_out;
+  a.z_ld = z_ld;
   a.reduce_mean = (mean && !lse_out) ? 1 : 0;
   a.segments = p.segments;
 
@@ -374,6 +383,145 @@ lce_status run_fused(const void* x, const void* weight, int64_t tokens, int64_t 
   a.mean_slots = (uint64_t*)(base + p.off_mean);
 
   hipError_t e = lce::launch_fused(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return LCE_OK;
+}
+
+// Fused linear + JSD.  Both paths first take each head's per-token
+// log-sum-exp with the fused cross-entropy kernel.  The stored path has that
+// kernel also write both heads' fp32 logits for a chunk of tokens into scratch
+// and then streams them once (jsd_stored_rows_kernel); the recompute path
+// multiplies both heads again, tile by tile (fused_jsd_partial_kernel), and
+// needs no logit storage.  The stored path is taken when a chunk of at least
+// one fused token tile fits in LCE_JSD_STORE_BYTES (default 2 GiB) of scratch.
+struct JsdPlan {
+  int64_t chunk = 0;  // tokens per chunk; 0: recompute path
+  int64_t ld = 0;     // stored row length (vocab rounded up to the fused tile)
+};
+
+JsdPlan plan_jsd(int64_t tokens, int64_t vocab) {
+  JsdPlan p;
+  const lce::FusedGeometry g = lce::fused_geometry();
+  const int64_t ld = (vocab + g.block_vocab - 1) / g.block_vocab * g.block_vocab;
+  // Byte offsets within a token tile's rows are 32-bit.
+  if (ld * g.block_tokens * 4 >= (int64_t(1) << 32)) return p;
+  const int64_t cap = env_int64("LCE_JSD_STORE_BYTES", int64_t(2) << 30);
+  const int64_t per_token = ld * 8;  // both heads' rows
+  int64_t max_chunk = cap / per_token / g.block_tokens * g.block_tokens;
+  if (max_chunk < g.block_tokens) return p;
+  if (tokens <= max_chunk) {
+    p.chunk = tokens;
+  } else {
+    const int64_t n = (tokens + max_chunk - 1) / max_chunk;
+    const int64_t even = (tokens + n - 1) / n;
+    p.chunk = (even + g.block_tokens - 1) / g.block_tokens * g.block_tokens;  // <= max_chunk
+  }
+  p.ld = ld;
+  return p;
+}
+
+lce_status run_jsd_stored(const void* xs, const void* ws, const void* xt, const void* wt,
+                          int64_t tokens, int64_t hidden, int64_t vocab, float beta, bool mean,
+                          float* out, hipStream_t stream, int cus, const JsdPlan& plan) {
+  lce_status s = LCE_OK;
+  Carve cv;
+  const size_t off_ls = cv.take((size_t)tokens * 4u);
+  const size_t off_lt = cv.take((size_t)tokens * 4u);
+  const size_t off_per = cv.take(mean ? (size_t)tokens * 4u : 0u);
+  const size_t off_mean = cv.take((size_t)((tokens + lce::kRowThreads - 1) / lce::kRowThreads) * 8u);
+  const size_t zbytes = (size_t)plan.chunk * (size_t)plan.ld * 4u;
+  const size_t off_zs = cv.take(zbytes);
+  const size_t off_zt = cv.take(zbytes);
+  const size_t reserved = cv.off - Carve().off;
+  // The fused kernel's own regions follow; size them for the largest chunk
+  // and for the last (smaller) one, whose plan may differ.
+  const int64_t last = tokens - (tokens - 1) / plan.chunk * plan.chunk;
+  size_t need = cv.off;
+  for (int64_t n : {plan.chunk, last}) {
+    const FusedPlan fp = plan_fused(n, vocab, cus, reserved);
+    if (fp.end > need) need = fp.end;
+  }
+  char* base = nullptr;
+  if ((s = get_scratch(stream, need, &base)) != LCE_OK) return s;
+  float* lse_s = (float*)(base + off_ls);
+  float* lse_t = (float*)(base + off_lt);
+  float* per = mean ? (float*)(base + off_per) : out;
+  float* zs = (float*)(base + off_zs);
+  float* zt = (float*)(base + off_zt);
+
+  const uint16_t* xs16 = (const uint16_t*)xs;
+  const uint16_t* xt16 = (const uint16_t*)xt;
+  for (int64_t c0 = 0; c0 < tokens; c0 += plan.chunk) {
+    const int64_t n = tokens - c0 < plan.chunk ? tokens - c0 : plan.chunk;
+    if ((s = run_fused(xs16 + c0 * hidden, ws, n, hidden, vocab, nullptr, false, nullptr, stream,
+                       reserved, lse_s + c0, zs, plan.ld)) != LCE_OK)
+      return s;
+    if ((s = run_fused(xt16 + c0 * hidden, wt, n, hidden, vocab, nullptr, false, nullptr, stream,
+                       reserved, lse_t + c0, zt, plan.ld)) != LCE_OK)
+      return s;
+    lce::JsdRowsArgs r{};
+    r.zs = zs;
+    r.zt = zt;
+    r.z_ld = plan.ld;
+    r.rows = n;
+    r.vocab = vocab;
+    r.lse_s = lse_s + c0;
+    r.lse_t = lse_t + c0;
+    r.beta = beta;
+    r.dst = per + c0;
+    hipError_t e = lce::launch_jsd_rows(r, stream);
+    if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  }
+  if (mean) {
+    hipError_t e = lce::launch_jsd_mean(tokens, per, out, (uint64_t*)(base + off_mean),
+                                        (unsigned*)base, stream);
+    if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  }
+  return LCE_OK;
+}
+
+lce_status run_jsd_recompute(const void* xs, const void* ws, const void* xt, const void* wt,
+                             int64_t tokens, int64_t hidden, int64_t vocab, float beta, bool mean,
+                             float* out, hipStream_t stream, int cus) {
+  lce_status s = LCE_OK;
+  // Scratch: both heads' log-sum-exp, the divergence kernel's per-segment
+  // sums and mean slots, then the cross-entropy kernel's own regions.
+  lce::JsdArgs a{};
+  a.xs = xs;
+  a.ws = ws;
+  a.xt = xt;
+  a.wt = wt;
+  a.tokens = tokens;
+  a.hidden = hidden;
+  a.vocab = vocab;
+  a.beta = beta;
+  a.out = out;
+  a.reduce_mean = mean ? 1 : 0;
+  a.segments = lce::jsd_segments(tokens, vocab, cus);
+  Carve cv;
+  const size_t off_ls = cv.take((size_t)tokens * 4u);
+  const size_t off_lt = cv.take((size_t)tokens * 4u);
+  const size_t off_part = cv.take((size_t)a.segments * (size_t)tokens * 4u);
+  const size_t off_mean = cv.take((size_t)((tokens + lce::kRowThreads - 1) / lce::kRowThreads) * 8u);
+  const size_t reserved = cv.off - Carve().off;
+  const FusedPlan fp = plan_fused(tokens, vocab, cus, reserved);
+  char* base = nullptr;
+  if ((s = get_scratch(stream, fp.end > cv.off ? fp.end : cv.off, &base)) != LCE_OK) return s;
+  float* lse_s = (float*)(base + off_ls);
+  float* lse_t = (float*)(base + off_lt);
+  a.lse_s = lse_s;
+  a.lse_t = lse_t;
+  a.partials = (float*)(base + off_part);
+  a.mean_slots = (uint64_t*)(base + off_mean);
+  a.ticket = (unsigned*)base;
+
+  if ((s = run_fused(xs, ws, tokens, hidden, vocab, nullptr, false, nullptr, stream, reserved,
+                     lse_s)) != LCE_OK)
+    return s;
+  if ((s = run_fused(xt, wt, tokens, hidden, vocab, nullptr, false, nullptr, stream, reserved,
+                     lse_t)) != LCE_OK)
+    return s;
+  hipError_t e = lce::launch_jsd(a, stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return LCE_OK;
 }
@@ -607,47 +755,12 @@ lce_status lce_fused_linear_jsd_fwd(const void* student_x, const void* student_w
   }
   int cus = 0;
   if ((s = num_cus(&cus)) != LCE_OK) return s;
-
-  // Scratch: both heads' log-sum-exp, the divergence kernel's per-segment
-  // sums and mean slots, then the cross-entropy kernel's own regions.
-  lce::JsdArgs a{};
-  a.xs = student_x;
-  a.ws = student_weight;
-  a.xt = teacher_x;
-  a.wt = teacher_weight;
-  a.tokens = tokens;
-  a.hidden = hidden;
-  a.vocab = vocab;
-  a.beta = beta;
-  a.out = out;
-  a.reduce_mean = mean ? 1 : 0;
-  a.segments = lce::jsd_segments(tokens, vocab, cus);
-  Carve cv;
-  const size_t off_ls = cv.take((size_t)tokens * 4u);
-  const size_t off_lt = cv.take((size_t)tokens * 4u);
-  const size_t off_part = cv.take((size_t)a.segments * (size_t)tokens * 4u);
-  const size_t off_mean = cv.take((size_t)((tokens + lce::kRowThreads - 1) / lce::kRowThreads) * 8u);
-  const size_t reserved = cv.off - Carve().off;
-  const FusedPlan fp = plan_fused(tokens, vocab, cus, reserved);
-  char* base = nullptr;
-  if ((s = get_scratch(stream, fp.end > cv.off ? fp.end : cv.off, &base)) != LCE_OK) return s;
-  float* lse_s = (float*)(base + off_ls);
-  float* lse_t = (float*)(base + off_lt);
-  a.lse_s = lse_s;
-  a.lse_t = lse_t;
-  a.partials = (float*)(base + off_part);
-  a.mean_slots = (uint64_t*)(base + off_mean);
-  a.ticket = (unsigned*)base;
-
-  if ((s = run_fused(student_x, student_weight, tokens, hidden, vocab, nullptr, false, nullptr,
-                     stream, reserved, lse_s)) != LCE_OK)
-    return s;
-  if ((s = run_fused(teacher_x, teacher_weight, tokens, hidden, vocab, nullptr, false, nullptr,
-                     stream, reserved, lse_t)) != LCE_OK)
-    return s;
-  hipError_t e = lce::launch_jsd(a, stream);
-  if (e != hipSuccess) return hip_fail(e, "kernel launch");
-  return LCE_OK;
+  const JsdPlan plan = plan_jsd(tokens, vocab);
+  if (plan.chunk > 0)
+    return run_jsd_stored(student_x, student_weight, teacher_x, teacher_weight, tokens, hidden,
+                          vocab, beta, mean, out, stream, cus, plan);
+  return run_jsd_recompute(student_x, student_weight, teacher_x, teacher_weight, tokens, hidden,
+                           vocab, beta, mean, out, stream, cus);
 }
 
 }  // extern "C"

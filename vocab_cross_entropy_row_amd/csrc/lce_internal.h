@@ -73,6 +73,8 @@ struct FusedArgs {
   int reduce_mean;
   float* lse_out;         // non-null: write ln sum_j e^z_j per token instead of losses
                           // (target may then be null)
+  float* z_out;           // non-null: also store the fp32 logits as [tokens, z_ld] rows
+  int64_t z_ld;           // multiple of block_vocab, >= vocab; z_ld * block_tokens * 4 < 2^32
   int segments;           // vocab segments (workgroups per token block)
   float* seg_partials;    // segments * tokens (max, sum-exp) pairs
   float* target_logit;    // tokens fp32
@@ -114,6 +116,23 @@ struct JsdArgs {
 };
 int jsd_segments(int64_t tokens, int64_t vocab, int num_cus);
 hipError_t launch_jsd(const JsdArgs& a, hipStream_t stream);
+
+// Divergence of rows whose logits were stored by the fused kernel (z_out).
+struct JsdRowsArgs {
+  const float* zs;          // [rows, z_ld] student logits
+  const float* zt;          // [rows, z_ld] teacher logits
+  int64_t z_ld;
+  int64_t rows;
+  int64_t vocab;            // < 2^30
+  const float* lse_s;       // [rows]
+  const float* lse_t;       // [rows]
+  float beta;
+  float* dst;               // [rows] per-token divergence
+};
+hipError_t launch_jsd_rows(const JsdRowsArgs& a, hipStream_t stream);
+// Deterministic mean of `tokens` per-token values into out[0].
+hipError_t launch_jsd_mean(int64_t tokens, const float* per_token, float* out, uint64_t* slots,
+                           unsigned* ticket, hipStream_t stream);
 
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t stream);
 hipError_t launch_zero_u32(unsigned* p, int64_t n, hipStream_t stream);
