@@ -271,6 +271,56 @@ def fused_linear_logprob_sums(x_bits: np.ndarray, w_bits: np.ndarray, target: np
     return np.array([-math.fsum(per[b]) for b in range(batch)], dtype=np.float64)
 
 
+def fused_linear_xent_grads(x_bits: np.ndarray, w_bits: np.ndarray, target: np.ndarray,
+                            row_scale: np.ndarray, block: int = 64, want_dw: bool = True):
+    """Gradients of the fused cross-entropy with respect to the activations and the head,
+    fp64, for per-row output-gradient scales ``row_scale`` (g_i).
+
+    The pages give only the forward; this is its derivative written out.  With
+    z = x W^T (exactly widened bf16 operands, fp64 product), the logit gradient of row i
+    is dZ_i = g_i (softmax(z_i) - onehot(t_i)) (``xent_bwd`` on the fp64 logits), and
+    by the chain rule dx = dZ W and dW = dZ^T x (library matrix products).  Rows with an
+    out-of-range target are NaN, and so is all of dW.  Returns ``(dx, dW)`` (``dW`` is
+    None when ``want_dw`` is false).
+    """
+    x64_all = bf16_bits_to_f64(x_bits)
+    w64 = bf16_bits_to_f64(w_bits)
+    t = np.ascontiguousarray(target, dtype=np.int64).reshape(-1)
+    g = np.ascontiguousarray(row_scale, dtype=np.float64).reshape(-1)
+    rows = x64_all.shape[0]
+    if t.size != rows or g.size != rows:
+        raise ValueError("oracle: target and row_scale must have one entry per row")
+    dx = np.empty((rows, w64.shape[1]), dtype=np.float64)
+    dw = np.zeros_like(w64) if want_dw else None
+    for b0 in range(0, rows, block):
+        x64 = x64_all[b0:b0 + block]
+        z = np.matmul(x64, w64.T)
+        dz = xent_bwd(z, t[b0:b0 + block], g[b0:b0 + block], reduction="none", dtype="f64")
+        dx[b0:b0 + block] = np.matmul(dz, w64)
+        if want_dw:
+            dw += np.matmul(dz.T, x64)
+    return dx, dw
+
+
+def fused_linear_xent_bwd(x_bits: np.ndarray, w_bits: np.ndarray, target: np.ndarray, grad,
+                          reduction: str = "mean"):
+    """``(dx, dW)`` of the fused cross-entropy for the output gradient ``grad``: a scalar
+    for ``"mean"`` (each row then gets grad / tokens), one value per token for ``"none"``."""
+    rows = int(np.asarray(x_bits).shape[0])
+    g = np.asarray(grad, dtype=np.float64).reshape(-1)
+    if reduction == "mean":
+        if g.size != 1:
+            raise ValueError("oracle: grad must be a scalar for mean")
+        scale = np.full(rows, g[0] / rows)
+    elif reduction == "none":
+        if g.size != rows:
+            raise ValueError("oracle: grad must have one value per token for none")
+        scale = g
+    else:
+        raise ValueError(f"oracle: unknown reduction {reduction!r}")
+    return fused_linear_xent_grads(x_bits, w_bits, target, scale)
+
+
 def _log_softmax_rows(z: np.ndarray) -> np.ndarray:
     """Row-wise log-softmax in fp64 by the same two plain passes as the C oracle
     (maximum, then the sum of exp(z - m)); vectorised over the rows of a block."""

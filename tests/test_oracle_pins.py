@@ -540,3 +540,87 @@ def test_jsd_matches_library_kl_div(oracle_mod):
     ref = beta * kl(lm, lp, reduction="batchmean", log_target=True) + \
         (1 - beta) * kl(lm, lq, reduction="batchmean", log_target=True)
     assert oracle_mod.fused_linear_jsd(xs, ws, xt, wt, beta, "mean") == pytest.approx(ref.item(), abs=1e-13)
+
+
+# ---------------------------------------------------------------- fused-linear gradients
+
+def _bf16(a):
+    return lce_synth.f32_to_bf16_bits(np.asarray(a, dtype=np.float32))
+
+
+def test_fused_bwd_zero_activations_closed_form(oracle_mod):
+    """x = 0: softmax is 1/V, so dx_i = g_i (mean_v W_v - W_{t_i}) and dW = 0 (catches a
+    transposed product, a dropped one-hot, a wrong scale)."""
+    rng = _rng(41)
+    T, H, V = 5, 16, 37
+    wb = _bf16(rng.normal(size=(V, H)))
+    w = oracle_mod.bf16_bits_to_f64(wb)
+    xb = np.zeros((T, H), dtype=np.uint16)
+    t = rng.integers(0, V, T)
+    g = rng.normal(size=T)
+    dx, dw = oracle_mod.fused_linear_xent_bwd(xb, wb, t, g, "none")
+    want = g[:, None] * (w.mean(axis=0)[None, :] - w[t])
+    assert np.allclose(dx, want, rtol=0, atol=1e-14)
+    assert np.array_equal(dw, np.zeros_like(dw))
+
+
+def test_fused_bwd_matches_finite_differences(oracle_mod):
+    """Central differences of the separately pinned row oracle on fp64 logits x W^T, for
+    every entry of a small x and W, with a non-square head and mean reduction."""
+    rng = _rng(42)
+    T, H, V, h = 3, 4, 6, 1e-6
+    xb, wb = _bf16(rng.normal(size=(T, H))), _bf16(rng.normal(size=(V, H)))
+    x, w = oracle_mod.bf16_bits_to_f64(xb), oracle_mod.bf16_bits_to_f64(wb)
+    t = rng.integers(0, V, T)
+    dx, dw = oracle_mod.fused_linear_xent_bwd(xb, wb, t, 1.7, "mean")
+
+    def loss(xx, ww):
+        return 1.7 * oracle_mod.xent_rows(xx @ ww.T, t, dtype="f64").mean()
+
+    for i in range(T):
+        for k in range(H):
+            xp, xm = x.copy(), x.copy()
+            xp[i, k] += h
+            xm[i, k] -= h
+            assert (loss(xp, w) - loss(xm, w)) / (2 * h) == pytest.approx(dx[i, k], abs=1e-8)
+    for v in range(V):
+        for k in range(H):
+            wp, wm = w.copy(), w.copy()
+            wp[v, k] += h
+            wm[v, k] -= h
+            assert (loss(x, wp) - loss(x, wm)) / (2 * h) == pytest.approx(dw[v, k], abs=1e-8)
+
+
+def test_fused_bwd_matches_library_autograd(oracle_mod):
+    torch = pytest.importorskip("torch")
+    rng = _rng(43)
+    T, H, V = 70, 24, 301
+    xb, wb = _bf16(rng.normal(size=(T, H))), _bf16(rng.normal(scale=0.3, size=(V, H)))
+    t = rng.integers(0, V, T)
+    g = rng.normal(size=T)
+    xt = torch.from_numpy(oracle_mod.bf16_bits_to_f64(xb)).requires_grad_(True)
+    wt = torch.from_numpy(oracle_mod.bf16_bits_to_f64(wb)).requires_grad_(True)
+    per = torch.nn.functional.cross_entropy(xt @ wt.T, torch.from_numpy(t), reduction="none")
+    (per * torch.from_numpy(g)).sum().backward()
+    dx, dw = oracle_mod.fused_linear_xent_bwd(xb, wb, t, g, "none")
+    assert np.allclose(dx, xt.grad.numpy(), rtol=0, atol=1e-13)
+    assert np.allclose(dw, wt.grad.numpy(), rtol=0, atol=1e-13)
+
+
+def test_fused_bwd_invariants(oracle_mod):
+    """Rows of dZ sum to 0, so the rows of dW sum to 0; mean = none with grad / T; token
+    blocks of any size give the same result; a bad target poisons its dx row and dW."""
+    rng = _rng(44)
+    T, H, V = 130, 8, 50
+    xb, wb = _bf16(rng.normal(size=(T, H))), _bf16(rng.normal(size=(V, H)))
+    t = rng.integers(0, V, T)
+    dx, dw = oracle_mod.fused_linear_xent_bwd(xb, wb, t, 2.0, "mean")
+    assert np.allclose(dw.sum(axis=0), 0.0, atol=1e-13)
+    dx1, dw1 = oracle_mod.fused_linear_xent_bwd(xb, wb, t, np.full(T, 2.0 / T), "none")
+    assert np.allclose(dx, dx1, rtol=1e-14, atol=0) and np.allclose(dw, dw1, rtol=1e-14, atol=0)
+    dx2, dw2 = oracle_mod.fused_linear_xent_grads(xb, wb, t, np.full(T, 2.0 / T), block=7)
+    assert np.allclose(dx, dx2, rtol=1e-13, atol=0) and np.allclose(dw, dw2, rtol=1e-13, atol=1e-16)
+    t[3] = V
+    dx3, dw3 = oracle_mod.fused_linear_xent_bwd(xb, wb, t, 2.0, "mean")
+    assert np.isnan(dx3[3]).all() and np.isfinite(np.delete(dx3, 3, axis=0)).all()
+    assert np.isnan(dw3).all()
