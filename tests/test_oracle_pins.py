@@ -544,7 +544,7 @@ def test_jsd_matches_library_kl_div(oracle_mod):
 
 # ---------------------------------------------------------------- fused-linear gradients
 
-def _bf16(a):
+def _bf16_of(a):
     return lce_synth.f32_to_bf16_bits(np.asarray(a, dtype=np.float32))
 
 
@@ -553,7 +553,7 @@ def test_fused_bwd_zero_activations_closed_form(oracle_mod):
     transposed product, a dropped one-hot, a wrong scale)."""
     rng = _rng(41)
     T, H, V = 5, 16, 37
-    wb = _bf16(rng.normal(size=(V, H)))
+    wb = _bf16_of(rng.normal(size=(V, H)))
     w = oracle_mod.bf16_bits_to_f64(wb)
     xb = np.zeros((T, H), dtype=np.uint16)
     t = rng.integers(0, V, T)
@@ -569,7 +569,7 @@ def test_fused_bwd_matches_finite_differences(oracle_mod):
     every entry of a small x and W, with a non-square head and mean reduction."""
     rng = _rng(42)
     T, H, V, h = 3, 4, 6, 1e-6
-    xb, wb = _bf16(rng.normal(size=(T, H))), _bf16(rng.normal(size=(V, H)))
+    xb, wb = _bf16_of(rng.normal(size=(T, H))), _bf16_of(rng.normal(size=(V, H)))
     x, w = oracle_mod.bf16_bits_to_f64(xb), oracle_mod.bf16_bits_to_f64(wb)
     t = rng.integers(0, V, T)
     dx, dw = oracle_mod.fused_linear_xent_bwd(xb, wb, t, 1.7, "mean")
@@ -595,7 +595,7 @@ def test_fused_bwd_matches_library_autograd(oracle_mod):
     torch = pytest.importorskip("torch")
     rng = _rng(43)
     T, H, V = 70, 24, 301
-    xb, wb = _bf16(rng.normal(size=(T, H))), _bf16(rng.normal(scale=0.3, size=(V, H)))
+    xb, wb = _bf16_of(rng.normal(size=(T, H))), _bf16_of(rng.normal(scale=0.3, size=(V, H)))
     t = rng.integers(0, V, T)
     g = rng.normal(size=T)
     xt = torch.from_numpy(oracle_mod.bf16_bits_to_f64(xb)).requires_grad_(True)
@@ -612,7 +612,7 @@ def test_fused_bwd_invariants(oracle_mod):
     blocks of any size give the same result; a bad target poisons its dx row and dW."""
     rng = _rng(44)
     T, H, V = 130, 8, 50
-    xb, wb = _bf16(rng.normal(size=(T, H))), _bf16(rng.normal(size=(V, H)))
+    xb, wb = _bf16_of(rng.normal(size=(T, H))), _bf16_of(rng.normal(size=(V, H)))
     t = rng.integers(0, V, T)
     dx, dw = oracle_mod.fused_linear_xent_bwd(xb, wb, t, 2.0, "mean")
     assert np.allclose(dw.sum(axis=0), 0.0, atol=1e-13)
