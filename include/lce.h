@@ -56,7 +56,7 @@ extern "C" {
 #endif
 
 #define LCE_VERSION_MAJOR 0
-#define LCE_VERSION_MINOR 3
+#define LCE_VERSION_MINOR 4
 #define LCE_VERSION_PATCH 0
 
 typedef enum {
@@ -250,6 +250,48 @@ lce_status lce_fused_linear_xent_fwd(const void* x, const void* weight, int64_t 
 lce_status lce_fused_linear_logprob_sums(const void* x, const void* weight, int64_t batch,
                                          int64_t seq, int64_t hidden, int64_t vocab,
                                          const int64_t* target, float* out, hipStream_t stream);
+
+/*
+ * Gradients of the fused projection + cross-entropy (lce_fused_linear_xent_fwd)
+ * with respect to the activations and the head.  The pages give only the
+ * forward ("Fused linear + CPO loss": description, Semantics); this is its
+ * derivative written out.  With z = x * weight^T and per-token output
+ * gradient g_i (grad[0] / tokens for a mean, grad[i] per token),
+ *
+ *     dZ_ij  = g_i (softmax(z_i)_j - [j == t_i])
+ *     dx     = dZ * weight        [tokens, hidden]
+ *     dweight = dZ^T * x          [vocab, hidden]
+ *
+ * The full logits are never stored: the forward kernel gives each token's
+ * log-sum-exp, then for chunks of tokens the fused kernel recomputes the
+ * logits and writes dZ as bf16 (round to nearest even) into scratch, and two
+ * hipBLASLt GEMMs (bf16 operands, fp32 accumulation) consume it.  The chunk is
+ * the largest multiple of 256 tokens whose dZ (2 * tokens * vocab bytes, vocab
+ * rounded up to 256) fits in LCE_FUSED_BWD_STORE_BYTES (environment, default
+ * 2 GiB), and at least 256 tokens.
+ *
+ *   x, weight, tokens, hidden, target: as lce_fused_linear_xent_fwd; also
+ *             vocab < 2^23 - 256.
+ *   reduction LCE_REDUCTION_MEAN or LCE_REDUCTION_NONE: the forward's.
+ *   grad      device fp32: 1 element (mean) or `tokens` elements (none).
+ *   dx        device fp32 [tokens, hidden], overwritten; NULL skips it.
+ *   dweight   device fp32 [vocab, hidden], overwritten (zeros for tokens == 0);
+ *             NULL skips it.  At least one of dx, dweight is non-NULL.
+ *   stream    HIP stream.
+ *
+ * A token whose target is outside [0, vocab) gets a NaN row of dx and makes
+ * all of dweight NaN (its loss is NaN).  dweight sums over the tokens of each
+ * chunk inside the GEMM and over chunks in chunk order (deterministic).
+ * Outputs must not overlap the inputs or each other.  The first call of a
+ * shape plans its GEMMs (hipBLASLt handle and heuristic); a call inside a graph
+ * capture whose shape was never planned, or whose scratch would have to grow,
+ * fails with LCE_ERR_UNSUPPORTED.  Returns as lce_fused_linear_xent_fwd,
+ * LCE_ERR_HIP also for a failing hipBLASLt call.
+ */
+lce_status lce_fused_linear_xent_bwd(const void* x, const void* weight, int64_t tokens,
+                                     int64_t hidden, int64_t vocab, const int64_t* target,
+                                     lce_reduction reduction, const float* grad, float* dx,
+                                     float* dweight, hipStream_t stream);
 
 /*
  * Generalized Jensen-Shannon divergence between a student and a teacher

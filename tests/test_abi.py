@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lce.lce_version() == 300
+    assert lce.lce_version() == 400
     names = [lce.lce_status_string(s) for s in range(6)]
     assert names == ["LCE_OK", "LCE_ERR_INVALID_ARG", "LCE_ERR_UNSUPPORTED", "LCE_ERR_ALIAS",
                      "LCE_ERR_OOM", "LCE_ERR_HIP"]
@@ -254,3 +254,32 @@ def test_jsd_argument_errors(lib, kw, status, needle):
 def test_jsd_empty_none_is_a_no_op(lib):
     assert lce.lce_fused_linear_jsd_fwd(0, FAKE, 0, FAKE, 0, 64, 100, 0.5, lce.LCE_REDUCTION_NONE,
                                         0, 0) == lce.LCE_OK
+
+
+def _fbwd(x=FAKE, w=FAKE + (1 << 24), tokens=8, hidden=64, vocab=100, target=FAKE + (1 << 28),
+          reduction=lce.LCE_REDUCTION_MEAN, grad=FAKE + (1 << 29), dx=FAKE + (1 << 30),
+          dw=FAKE + (1 << 31)):
+    return lce.lce_fused_linear_xent_bwd(x, w, tokens, hidden, vocab, target, reduction, grad, dx,
+                                         dw, 0)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(x=0), lce.LCE_ERR_INVALID_ARG, "x is NULL"),
+    (dict(w=0), lce.LCE_ERR_INVALID_ARG, "weight is NULL"),
+    (dict(target=0), lce.LCE_ERR_INVALID_ARG, "target is NULL"),
+    (dict(grad=0), lce.LCE_ERR_INVALID_ARG, "grad is NULL"),
+    (dict(dx=0, dw=0), lce.LCE_ERR_INVALID_ARG, "both NULL"),
+    (dict(grad=FAKE + (1 << 29) + 2), lce.LCE_ERR_INVALID_ARG, "grad is not"),
+    (dict(dx=FAKE + (1 << 30) + 2), lce.LCE_ERR_INVALID_ARG, "aligned"),
+    (dict(hidden=12), lce.LCE_ERR_UNSUPPORTED, "multiple of 8"),
+    (dict(vocab=1 << 23), lce.LCE_ERR_UNSUPPORTED, "fused backward"),
+    (dict(reduction=5), lce.LCE_ERR_INVALID_ARG, "reduction"),
+    (dict(dx=FAKE + 64), lce.LCE_ERR_ALIAS, "dx overlaps x"),
+    (dict(dw=FAKE + (1 << 24) + 64), lce.LCE_ERR_ALIAS, "dweight overlaps weight"),
+    (dict(dx=FAKE + (1 << 28)), lce.LCE_ERR_ALIAS, "dx overlaps target"),
+    (dict(dw=FAKE + (1 << 29)), lce.LCE_ERR_ALIAS, "dweight overlaps grad"),
+    (dict(dw=FAKE + (1 << 30) + 1024), lce.LCE_ERR_ALIAS, "dx overlaps dweight"),
+])
+def test_fused_bwd_argument_errors(lib, kw, status, needle):
+    assert _fbwd(**kw) == status
+    assert needle in lce.lce_last_error()

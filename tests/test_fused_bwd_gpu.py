@@ -1,0 +1,163 @@
+"""Gradients of the fused projection + cross-entropy (lce_fused_linear_xent_bwd, through
+the C ABI) against the fp64 oracle.
+
+Tolerance, derived from the arithmetic: the logit gradient dZ is rounded to bf16 (round
+to nearest even, relative error <= 2^-9) before the two GEMMs, which accumulate exact
+bf16 products in fp32.  So each element of dx = dZ W is within 2^-9 * sum_v |dZ_tv W_vh|
+of the exact value from rounding alone; the tests allow twice that (2^-8), which also
+covers the fp32 accumulation and the fp32 softmax, plus 1e-7 absolute.  dW = dZ^T x gets
+the same bound with sum_t |dZ_tv x_th|.
+
+At the page shape (tokens 2048, hidden 4096, vocab 128256) the oracle checks dx on a
+sample of tokens; dW is checked through properties that hold at any size: its columns
+sum to ~0 (each row of dZ sums to 0), and mean reduction equals per-token reduction with
+gradient 1/tokens.
+"""
+import numpy as np
+import pytest
+
+import lce_synth
+import oracle
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import vocab_cross_entropy_row_amd as lce  # noqa: E402
+from gpu_util import forced_env, to_dev  # noqa: E402
+
+REL, ABS = 2.0 ** -8, 1e-7
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lce.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _inputs(seed, tokens, hidden, vocab, w_std=0.1):
+    xb = lce_synth.normal_bf16_bits(seed, 0, tokens, hidden, 1.0)
+    wb = lce_synth.normal_bf16_bits(seed + 1, 2, vocab, hidden, w_std)
+    t = lce_synth.targets(seed + 2, tokens, vocab)
+    return xb, wb, t
+
+
+def _row_scale(grad, reduction, tokens):
+    g = np.asarray(grad, dtype=np.float64).reshape(-1)
+    return np.full(tokens, g[0] / tokens) if reduction == "mean" else g
+
+
+def _bounds(xb, wb, t, scale, want_dw=True):
+    x64, w64 = oracle.bf16_bits_to_f64(xb), oracle.bf16_bits_to_f64(wb)
+    adz = np.abs(oracle.xent_bwd(x64 @ w64.T, t, scale, "none", dtype="f64"))
+    bw = REL * (adz.T @ np.abs(x64)) + ABS if want_dw else None
+    return REL * (adz @ np.abs(w64)) + ABS, bw
+
+
+def _check(name, got, want, bound):
+    err = np.abs(np.asarray(got, dtype=np.float64) - want)
+    bad = np.argwhere(~(err <= bound))
+    assert bad.size == 0, f"{name}: {len(bad)} elements off, first {tuple(bad[0])}: " \
+        f"got {got[tuple(bad[0])]!r}, want {want[tuple(bad[0])]!r}, bound {bound[tuple(bad[0])]!r}"
+
+
+def _run(xb, wb, t, grad, reduction, want_dx=True, want_dw=True, env=None):
+    x, W = to_dev(xb), to_dev(wb)
+    td = torch.from_numpy(t).cuda()
+    g = torch.tensor(np.asarray(grad, dtype=np.float32).reshape(-1)).cuda()
+    with forced_env(**(env or {})):
+        dx, dw = lce.fused_linear_xent_bwd(x, W, td, g, reduction, want_dx, want_dw)
+    torch.cuda.synchronize()
+    return (None if dx is None else dx.cpu().numpy()), (None if dw is None else dw.cpu().numpy())
+
+
+# Ragged in every dimension (tokens off the 256-token tile, vocab off the 256-row tile,
+# hidden off the 64-element slab), one token, and several token chunks.
+CASES = [(1, 64, 100), (5, 128, 1000), (130, 72, 3000), (300, 200, 515), (600, 64, 1001)]
+
+
+@pytest.mark.parametrize("reduction", ["mean", "none"])
+@pytest.mark.parametrize("tokens,hidden,vocab", CASES)
+def test_grads_match_oracle(tokens, hidden, vocab, reduction):
+    xb, wb, t = _inputs(tokens * 7 + vocab, tokens, hidden, vocab)
+    rng = np.random.default_rng(tokens)
+    grad = np.array([1.7]) if reduction == "mean" else rng.normal(size=tokens)
+    grad = grad.astype(np.float32).astype(np.float64)
+    dx, dw = _run(xb, wb, t, grad, reduction)
+    want_dx, want_dw = oracle.fused_linear_xent_bwd(xb, wb, t, grad, reduction)
+    bx, bw = _bounds(xb, wb, t, _row_scale(grad, reduction, tokens))
+    _check("dx", dx, want_dx, bx)
+    _check("dW", dw, want_dw, bw)
+
+
+def test_token_chunks_give_the_same_grads():
+    """256-token chunks (dW accumulated over chunks in the GEMM's C) against one chunk."""
+    xb, wb, t = _inputs(3, 700, 128, 2000)
+    one = _run(xb, wb, t, [1.0], "mean")
+    ld = 2048
+    chunked = _run(xb, wb, t, [1.0], "mean", env={"LCE_FUSED_BWD_STORE_BYTES": 256 * ld * 2})
+    bx, bw = _bounds(xb, wb, t, np.full(700, 1.0 / 700))
+    _check("dx chunked vs one", chunked[0], one[0], bx)
+    _check("dW chunked vs one", chunked[1], one[1], bw)
+    want_dx, want_dw = oracle.fused_linear_xent_bwd(xb, wb, t, 1.0, "mean")
+    _check("dx chunked", chunked[0], want_dx, bx)
+    _check("dW chunked", chunked[1], want_dw, bw)
+
+
+def test_one_gradient_only():
+    xb, wb, t = _inputs(5, 200, 64, 900)
+    dx, dw = _run(xb, wb, t, [2.0], "mean")
+    dx_only, none_w = _run(xb, wb, t, [2.0], "mean", want_dw=False)
+    none_x, dw_only = _run(xb, wb, t, [2.0], "mean", want_dx=False)
+    assert none_w is None and none_x is None
+    assert np.array_equal(dx, dx_only) and np.array_equal(dw, dw_only)
+
+
+def test_invalid_target_poisons_its_row_and_dweight():
+    xb, wb, t = _inputs(7, 40, 64, 300)
+    t[11] = 300
+    dx, dw = _run(xb, wb, t, [1.0], "mean")
+    assert np.isnan(dx[11]).all() and np.isfinite(np.delete(dx, 11, axis=0)).all()
+    assert np.isnan(dw).all()
+
+
+def test_empty_tokens_give_zero_dweight():
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    W = torch.ones((10, 64), dtype=torch.bfloat16, device="cuda")
+    t = torch.empty((0,), dtype=torch.int64, device="cuda")
+    dw = torch.full((10, 64), 5.0, device="cuda")
+    lce.fused_linear_xent_bwd(x, W, t, torch.ones(1, device="cuda"), "mean", want_dx=False,
+                              dweight=dw)
+    assert torch.equal(dw.cpu(), torch.zeros(10, 64))
+
+
+def test_repeated_calls_bitwise_identical():
+    xb, wb, t = _inputs(9, 520, 128, 3000)
+    first = _run(xb, wb, t, [1.0], "mean")
+    for _ in range(3):
+        again = _run(xb, wb, t, [1.0], "mean")
+        assert np.array_equal(first[0], again[0]) and np.array_equal(first[1], again[1])
+
+
+def test_page_shape_sampled_and_properties():
+    w = lce_synth.WORKLOADS["fused_bf16_t2048_h4096_v128256_mean"]
+    xb, wb, t = w.x(), w.weight(), w.target()
+    x, W = to_dev(xb), to_dev(wb)
+    td = torch.from_numpy(t).cuda()
+    T = w.tokens
+    dx, dw = lce.fused_linear_xent_bwd(x, W, td, torch.ones(1, device="cuda"), "mean")
+    dx_n, dw_n = lce.fused_linear_xent_bwd(x, W, td, torch.full((T,), 1.0 / T, device="cuda"),
+                                           "none")
+    torch.cuda.synchronize()
+    assert torch.equal(dx, dx_n) and torch.equal(dw, dw_n)  # 1/2048 is exact in fp32
+    # Columns of dW sum to ~0: each dZ row sums to 0 up to its bf16 rounding.
+    col = dw.double().sum(dim=0).abs()
+    lim = REL * (x.double().abs().sum(dim=0) * 2.0 / T) + 1e-6
+    assert bool((col <= lim).all())
+    rows = np.r_[0:4, 1021:1025, 2044:2048]
+    scale = np.full(len(rows), 1.0 / T)
+    want_dx, _ = oracle.fused_linear_xent_grads(xb[rows], wb, t[rows], scale, want_dw=False)
+    bx, _ = _bounds(xb[rows], wb, t[rows], scale, want_dw=False)
+    _check("dx rows", dx.cpu().numpy()[rows], want_dx, bx)

@@ -37,7 +37,7 @@ LCE_ERR_ALIAS = 3
 LCE_ERR_OOM = 4
 LCE_ERR_HIP = 5
 
-EXPORTED = ("lce_xent_fwd", "lce_xent_bwd", "lce_fused_linear_xent_fwd",
+EXPORTED = ("lce_xent_fwd", "lce_xent_bwd", "lce_fused_linear_xent_fwd", "lce_fused_linear_xent_bwd",
             "lce_fused_linear_logprob_sums", "lce_fused_linear_jsd_fwd", "lce_xent_partial_fwd",
             "lce_xent_merge", "lce_status_string", "lce_last_error", "lce_version")
 
@@ -83,6 +83,11 @@ def load() -> ctypes.CDLL:
                                              ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                              ctypes.c_int64, ctypes.c_float, ctypes.c_int,
                                              ctypes.c_void_p, ctypes.c_void_p]
+    lib.lce_fused_linear_xent_bwd.restype = ctypes.c_int
+    lib.lce_fused_linear_xent_bwd.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                              ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                              ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_void_p]
     lib.lce_xent_partial_fwd.restype = ctypes.c_int
     lib.lce_xent_partial_fwd.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                          ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
@@ -126,6 +131,14 @@ def lce_fused_linear_logprob_sums(x: int, weight: int, batch: int, seq: int, hid
                                   vocab: int, target: int, out: int, stream: int) -> int:
     return load().lce_fused_linear_logprob_sums(x or None, weight or None, batch, seq, hidden, vocab,
                                                 target or None, out or None, stream or None)
+
+
+def lce_fused_linear_xent_bwd(x: int, weight: int, tokens: int, hidden: int, vocab: int,
+                              target: int, reduction: int, grad: int, dx: int, dweight: int,
+                              stream: int) -> int:
+    return load().lce_fused_linear_xent_bwd(x or None, weight or None, tokens, hidden, vocab,
+                                            target or None, reduction, grad or None, dx or None,
+                                            dweight or None, stream or None)
 
 
 def lce_fused_linear_jsd_fwd(student_x: int, student_weight: int, teacher_x: int,
@@ -391,3 +404,41 @@ def fused_linear_jsd(student_x, student_weight, teacher_x, teacher_weight, beta:
     if st != LCE_OK:
         raise LceError(st, "lce_fused_linear_jsd_fwd")
     return out
+
+
+def fused_linear_xent_bwd(x, weight, target, grad, reduction: str = "mean", want_dx: bool = True,
+                          want_dweight: bool = True, dx=None, dweight=None):
+    """Gradients of :func:`fused_linear_xent` with respect to ``x`` and ``weight`` for the
+    loss-output gradient ``grad`` (one element for "mean", the target's shape for "none").
+    Returns ``(dx, dweight)`` as fp32 tensors (``None`` for one not wanted)."""
+    import torch
+    if reduction not in _REDUCTIONS:
+        raise ValueError(f"reduction must be 'mean' or 'none', got {reduction!r}")
+    for name, t in (("x", x), ("weight", weight), ("target", target), ("grad", grad)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if x.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
+        raise TypeError("x and weight must be bfloat16")
+    if target.dtype != torch.int64 or grad.dtype != torch.float32:
+        raise TypeError("target must be int64 and grad float32")
+    if weight.dim() != 2 or x.shape[-1] != weight.shape[1]:
+        raise ValueError("weight must be [vocab, hidden] with hidden = x.shape[-1]")
+    if tuple(target.shape) != tuple(x.shape[:-1]):
+        raise ValueError("target shape must be x shape without the hidden axis")
+    tokens = target.numel()
+    if grad.numel() != (1 if reduction == "mean" else tokens):
+        raise ValueError("grad must have 1 element (mean) or one per token (none)")
+    if not (want_dx or want_dweight):
+        raise ValueError("nothing to compute")
+    vocab, hidden = weight.shape
+    if want_dx and dx is None:
+        dx = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    if want_dweight and dweight is None:
+        dweight = torch.empty((vocab, hidden), dtype=torch.float32, device=x.device)
+    st = lce_fused_linear_xent_bwd(x.data_ptr(), weight.data_ptr(), tokens, hidden, vocab,
+                                   target.data_ptr(), _REDUCTIONS[reduction], grad.data_ptr(),
+                                   dx.data_ptr() if want_dx else 0,
+                                   dweight.data_ptr() if want_dweight else 0, _stream_of(x))
+    if st != LCE_OK:
+        raise LceError(st, "lce_fused_linear_xent_bwd")
+    return (dx if want_dx else None), (dweight if want_dweight else None)

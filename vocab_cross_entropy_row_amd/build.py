@@ -63,7 +63,8 @@ def build(verbose: bool = False) -> str:
     if failed:
         raise RuntimeError(f"liblce build failed: {', '.join(failed)}")
     tmp = LIB + ".tmp"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp,
+           "-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
     return LIB

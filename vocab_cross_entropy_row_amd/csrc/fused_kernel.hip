@@ -134,11 +134,53 @@ __device__ __forceinline__ void store_tile_column(__amdgpu_buffer_rsrc_t zr, con
     }
 }
 
-template <class TL, int BVB, int BTB, int WV, bool STORE>
+// Store the logit gradient of a finished tile into dz [tokens, dz_ld] bf16
+// (token rows): dz_j = g * e^(z_j - lse) - [j == t] * g for the lane's token,
+// with L = lse * log2e, rounded to nearest even; for each (a, v/4) the lane's
+// four consecutive vocab rows are one 8-byte store.  Same addressing as
+// store_tile_column.
+template <int BVB>
+__device__ __forceinline__ void store_tile_grad(__amdgpu_buffer_rsrc_t dr, const f32x16 (&acc)[BVB],
+                                                uint32_t voff, int64_t vbase, int half, float L,
+                                                float g, int tgt) {
+  // Target row relative to this lane's first row of the tile (-1: not here).
+  const int64_t rel64 = (int64_t)tgt - vbase - 4 * half;
+  const int rel = (tgt >= 0 && rel64 >= 0 && rel64 < BVB * 32) ? (int)rel64 : -1;
+#pragma unroll
+  for (int a = 0; a < BVB; ++a)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float d[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        d[e] = g * exp2_fast(__builtin_fmaf(acc[a][4 * q + e], kLog2e, -L));
+        if (rel == a * 32 + 8 * q + e) d[e] -= g;
+      }
+      const u32x2 packed = {
+          __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{d[0], d[1]}), bf16x2)),
+          __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{d[2], d[3]}), bf16x2))};
+      __builtin_amdgcn_raw_buffer_store_b64(packed, dr, voff + (uint32_t)(a * 32 + 8 * q) * 2u, 0, 0);
+    }
+}
+
+// MODE: kFusedXent (per-token (max, sum-exp) partials and the target logit),
+// kFusedStoreLogits (the same, and the fp32 logits into z_out), kFusedGrad
+// (only the bf16 logit gradient into dz_out, from the log-sum-exp `lse` and
+// the loss-output gradient: grad[0] / grad_tokens with grad_mean, else
+// grad[token]; NaN rows for targets outside [0, vocab)).
+constexpr int kFusedXent = 0;
+constexpr int kFusedStoreLogits = 1;
+constexpr int kFusedGrad = 2;
+
+template <class TL, int BVB, int BTB, int WV, int MODE>
 __global__ __launch_bounds__(TL::kThreads) void fused_xent_partial_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int64_t tokens, int64_t hidden,
     int64_t vocab, const int64_t* __restrict__ target, int segments, float2* __restrict__ part,
-    float* __restrict__ zt_out, float* __restrict__ z_out, int64_t z_ld) {
+    float* __restrict__ zt_out, float* __restrict__ z_out, int64_t z_ld,
+    const float* __restrict__ lse, const float* __restrict__ grad, int grad_mean,
+    int64_t grad_tokens, uint16_t* __restrict__ dz_out) {
+  constexpr bool STORE = MODE == kFusedStoreLogits;
+  constexpr bool GRAD = MODE == kFusedGrad;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[TL::kLdsElems];
   constexpr int kXBase = TL::kWStages * TL::kWStageElems;  // x stages follow the W stages
 
@@ -169,6 +211,18 @@ __global__ __launch_bounds__(TL::kThreads) void fused_xent_partial_kernel(
     const int64_t t = (target && tok[j] < tokens) ? target[tok[j]] : -1;
     tgt[j] = (t >= 0 && t < vocab) ? (int)t : -1;
   }
+  // Gradient mode: L = lse * log2e and the row's output gradient (NaN for an
+  // invalid target) of each of this lane's tokens.
+  float gL[BTB], gg[BTB];
+  if constexpr (GRAD) {
+#pragma unroll
+    for (int j = 0; j < BTB; ++j) {
+      const bool in = tok[j] < tokens;
+      gL[j] = in ? lse[tok[j]] * kLog2e : 0.0f;
+      const float g = grad_mean ? grad[0] / (float)grad_tokens : (in ? grad[tok[j]] : 0.0f);
+      gg[j] = (!in || tgt[j] >= 0) ? g : __builtin_nanf("");
+    }
+  }
 
   // Global -> LDS plan.  One wave instruction (64 lanes x 16 B) fills 8 LDS
   // rows; W DMA i of this wave fills W-stage rows 8g .. 8g+7, g = wave + kWaves*i,
@@ -195,13 +249,17 @@ __global__ __launch_bounds__(TL::kThreads) void fused_xent_partial_kernel(
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + t0 * hidden, x_rows * row_bytes);
   // Logit rows of this token tile (STORE only); byte offset of this lane's
   // first row and column, relative to vocab tile 0.
-  const __amdgpu_buffer_rsrc_t zr = make_rsrc(z_out + t0 * z_ld, STORE ? x_rows * (uint32_t)z_ld * 4u : 0u);
+  // (GRAD: the same for dz_out, bf16 elements, leading dimension z_ld.)
+  constexpr uint32_t kZBytes = GRAD ? 2u : 4u;
+  const __amdgpu_buffer_rsrc_t zr =
+      GRAD ? make_rsrc(dz_out + t0 * z_ld, x_rows * (uint32_t)z_ld * kZBytes)
+           : make_rsrc(z_out + t0 * z_ld, STORE ? x_rows * (uint32_t)z_ld * kZBytes : 0u);
   uint32_t z_voff[BTB];
-  if constexpr (STORE) {
+  if constexpr (STORE || GRAD) {
 #pragma unroll
     for (int b = 0; b < BTB; ++b)
       z_voff[b] = ((uint32_t)(wt * (BTB * 32) + b * 32 + (lane & 31)) * (uint32_t)z_ld +
-                   (uint32_t)(wv * (BVB * 32) + 4 * half)) * 4u;
+                   (uint32_t)(wv * (BVB * 32) + 4 * half)) * kZBytes;
   }
 
   // W block of vocab tile `tile` as a buffer resource (rows past vocab read 0).
@@ -371,6 +429,13 @@ __global__ __launch_bounds__(TL::kThreads) void fused_xent_partial_kernel(
       for (int b = 0; b < BTB; ++b)
         store_tile_column<BVB>(zr, acc[b], z_voff[b] + (uint32_t)tile * (uint32_t)TL::kBV * 4u);
     }
+    if constexpr (GRAD) {
+#pragma unroll
+      for (int b = 0; b < BTB; ++b)
+        store_tile_grad<BVB>(zr, acc[b], z_voff[b] + (uint32_t)tile * (uint32_t)TL::kBV * 2u, vbase,
+                             half, gL[b], gg[b], tgt[b]);
+      continue;  // no (max, sum-exp) state in this mode
+    }
     if (vbase + BVB * 32 > vocab) {
 #pragma unroll
       for (int b = 0; b < BTB; ++b)
@@ -382,6 +447,7 @@ __global__ __launch_bounds__(TL::kThreads) void fused_xent_partial_kernel(
     }
   }
 
+  if constexpr (GRAD) return;
   // Merge the two lane halves (same tokens, different vocab rows) ...
 #pragma unroll
   for (int b = 0; b < BTB; ++b) {
@@ -472,15 +538,17 @@ hipError_t launch_fused(const FusedArgs& a, hipStream_t stream) {
   const int64_t n_tok = (a.tokens + FusedTile::kBT - 1) / FusedTile::kBT;
   const int64_t grid = n_tok * a.segments;
   if (a.z_out)
-    hipLaunchKernelGGL((fused_xent_partial_kernel<FusedTile, 4, 2, 2, true>), dim3((unsigned)grid),
-                       dim3(FusedTile::kThreads), 0, stream, (const uint16_t*)a.x,
-                       (const uint16_t*)a.w, a.tokens, a.hidden, a.vocab, a.target, a.segments,
-                       (float2*)a.seg_partials, a.target_logit, a.z_out, a.z_ld);
+    hipLaunchKernelGGL((fused_xent_partial_kernel<FusedTile, 4, 2, 2, kFusedStoreLogits>),
+                       dim3((unsigned)grid), dim3(FusedTile::kThreads), 0, stream,
+                       (const uint16_t*)a.x, (const uint16_t*)a.w, a.tokens, a.hidden, a.vocab,
+                       a.target, a.segments, (float2*)a.seg_partials, a.target_logit, a.z_out,
+                       a.z_ld, nullptr, nullptr, 0, (int64_t)0, nullptr);
   else
-    hipLaunchKernelGGL((fused_xent_partial_kernel<FusedTile, 4, 2, 2, false>), dim3((unsigned)grid),
-                       dim3(FusedTile::kThreads), 0, stream, (const uint16_t*)a.x,
-                       (const uint16_t*)a.w, a.tokens, a.hidden, a.vocab, a.target, a.segments,
-                       (float2*)a.seg_partials, a.target_logit, nullptr, (int64_t)0);
+    hipLaunchKernelGGL((fused_xent_partial_kernel<FusedTile, 4, 2, 2, kFusedXent>),
+                       dim3((unsigned)grid), dim3(FusedTile::kThreads), 0, stream,
+                       (const uint16_t*)a.x, (const uint16_t*)a.w, a.tokens, a.hidden, a.vocab,
+                       a.target, a.segments, (float2*)a.seg_partials, a.target_logit, nullptr,
+                       (int64_t)0, nullptr, nullptr, 0, (int64_t)0, nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t blocks = (a.tokens + kRowThreads - 1) / kRowThreads;
@@ -488,6 +556,17 @@ hipError_t launch_fused(const FusedArgs& a, hipStream_t stream) {
                      a.tokens, a.vocab, a.segments, (const float2*)a.seg_partials,
                      (const float*)a.target_logit, a.target, a.out, a.lse_out, a.mean_slots, a.ticket,
                      a.reduce_mean);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused_grad(const FusedGradArgs& a, hipStream_t stream) {
+  const int64_t n_tok = (a.tokens + FusedTile::kBT - 1) / FusedTile::kBT;
+  const int64_t grid = n_tok * a.segments;
+  hipLaunchKernelGGL((fused_xent_partial_kernel<FusedTile, 4, 2, 2, kFusedGrad>),
+                     dim3((unsigned)grid), dim3(FusedTile::kThreads), 0, stream,
+                     (const uint16_t*)a.x, (const uint16_t*)a.w, a.tokens, a.hidden, a.vocab,
+                     a.target, a.segments, nullptr, nullptr, nullptr, a.dz_ld, a.lse, a.grad,
+                     a.grad_mean, a.grad_tokens, (uint16_t*)a.dz);
   return hipGetLastError();
 }
 

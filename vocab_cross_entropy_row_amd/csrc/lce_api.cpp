@@ -2,6 +2,7 @@
 // and error reporting.  Every entry point validates its arguments on the host
 // before it makes any HIP call, so argument errors never touch the device.
 #include <hip/hip_runtime.h>
+#include <hipblaslt/hipblaslt.h>
 
 #include <cstdarg>
 #include <cstdio>
@@ -11,6 +12,7 @@
 #include <vector>
 #include <mutex>
 #include <string>
+#include <tuple>
 #include <utility>
 
 #include "lce.h"
@@ -384,6 +386,165 @@ lce_status run_fused(const void* x, const void* weight, int64_t tokens, int64_t 
 
   hipError_t e = lce::launch_fused(a, stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return LCE_OK;
+}
+
+// ------------------------------------------------------------ library GEMMs
+// The two plain products of the fused-projection backward (dx = dZ W and
+// dW = dZ^T x) go to hipBLASLt: bf16 operands, fp32 accumulation and output.
+// One handle per device and one plan (descriptors, layouts and the heuristic's
+// first algorithm) per GEMM shape, created on first use and kept for the
+// process's lifetime.
+struct GemmPlan {
+  hipblasLtMatmulDesc_t desc = nullptr;
+  hipblasLtMatrixLayout_t a = nullptr, b = nullptr, d = nullptr;
+  hipblasLtMatmulAlgo_t algo{};
+  size_t ws = 0;
+};
+typedef std::tuple<int, int, int, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, size_t>
+    GemmKey;
+std::map<int, hipblasLtHandle_t> g_blaslt;
+std::map<GemmKey, GemmPlan> g_gemm_plans;
+
+lce_status blas_fail(hipblasStatus_t st, const char* what) {
+  return fail(LCE_ERR_HIP, "hipBLASLt %s failed (status %d)", what, (int)st);
+}
+
+// D (fp32, column-major m x n, leading dimension ldd) = op(A) op(B) + beta D
+// with bf16 A and B (column-major, op N or T).  `ws` is device workspace.
+lce_status gemm_bf16_f32(hipblasOperation_t ta, hipblasOperation_t tb, int64_t m, int64_t n,
+                         int64_t k, const void* A, int64_t lda, const void* B, int64_t ldb,
+                         float beta, float* D, int64_t ldd, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  hipblasLtHandle_t h = nullptr;
+  GemmPlan plan;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    const GemmKey key{dev, (int)ta, (int)tb, m, n, k, lda, ldb, ldd, ws_bytes};
+    auto hit = g_gemm_plans.find(key);
+    if (hit != g_gemm_plans.end()) {
+      plan = hit->second;
+      h = g_blaslt[dev];
+    } else {
+      // Creating a handle or a plan is not allowed inside a graph capture.
+      hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+      e = hipStreamIsCapturing(stream, &cap);
+      if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+      if (cap != hipStreamCaptureStatusNone)
+        return fail(LCE_ERR_UNSUPPORTED,
+                    "stream is being captured and this GEMM shape has not been planned yet: make "
+                    "one call of the same shape on this device before capture");
+      hipblasStatus_t st = HIPBLAS_STATUS_SUCCESS;
+      auto it = g_blaslt.find(dev);
+      if (it == g_blaslt.end()) {
+        if ((st = hipblasLtCreate(&h)) != HIPBLAS_STATUS_SUCCESS) return blas_fail(st, "handle creation");
+        g_blaslt[dev] = h;
+      } else {
+        h = it->second;
+      }
+      if ((st = hipblasLtMatmulDescCreate(&plan.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F)) != HIPBLAS_STATUS_SUCCESS)
+        return blas_fail(st, "descriptor creation");
+      const int32_t opa = (int32_t)ta, opb = (int32_t)tb;
+      hipblasLtMatmulDescSetAttribute(plan.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &opa, sizeof opa);
+      hipblasLtMatmulDescSetAttribute(plan.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &opb, sizeof opb);
+      const bool an = ta == HIPBLAS_OP_N, bn = tb == HIPBLAS_OP_N;
+      if ((st = hipblasLtMatrixLayoutCreate(&plan.a, HIP_R_16BF, an ? m : k, an ? k : m, lda)) != HIPBLAS_STATUS_SUCCESS ||
+          (st = hipblasLtMatrixLayoutCreate(&plan.b, HIP_R_16BF, bn ? k : n, bn ? n : k, ldb)) != HIPBLAS_STATUS_SUCCESS ||
+          (st = hipblasLtMatrixLayoutCreate(&plan.d, HIP_R_32F, m, n, ldd)) != HIPBLAS_STATUS_SUCCESS)
+        return blas_fail(st, "layout creation");
+      hipblasLtMatmulPreference_t pref = nullptr;
+      if ((st = hipblasLtMatmulPreferenceCreate(&pref)) != HIPBLAS_STATUS_SUCCESS)
+        return blas_fail(st, "preference creation");
+      const uint64_t wsb = ws_bytes;
+      hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsb, sizeof wsb);
+      hipblasLtMatmulHeuristicResult_t res[1];
+      int found = 0;
+      st = hipblasLtMatmulAlgoGetHeuristic(h, plan.desc, plan.a, plan.b, plan.d, plan.d, pref, 1, res, &found);
+      hipblasLtMatmulPreferenceDestroy(pref);
+      if (st != HIPBLAS_STATUS_SUCCESS || found < 1)
+        return fail(LCE_ERR_UNSUPPORTED, "hipBLASLt has no algorithm for a %lld x %lld x %lld GEMM (status %d)",
+                    (long long)m, (long long)n, (long long)k, (int)st);
+      plan.algo = res[0].algo;
+      plan.ws = res[0].workspaceSize;
+      g_gemm_plans[key] = plan;
+    }
+  }
+  const float alpha = 1.0f;
+  hipblasStatus_t st = hipblasLtMatmul(h, plan.desc, &alpha, A, plan.a, B, plan.b, &beta, D, plan.d,
+                                       D, plan.d, &plan.algo, ws, plan.ws, stream);
+  if (st != HIPBLAS_STATUS_SUCCESS) return blas_fail(st, "matmul");
+  return LCE_OK;
+}
+
+// Gradients of the fused projection + cross-entropy.  The per-token
+// log-sum-exp comes from the forward kernel; then, for chunks of tokens, the
+// fused kernel's gradient mode writes the bf16 logit gradient dZ [chunk, ld]
+// into scratch and two library GEMMs consume it: dx[chunk] = dZ W and
+// dW (+)= dZ^T x[chunk].  The chunk is the largest multiple of 256 tokens whose
+// dZ fits in LCE_FUSED_BWD_STORE_BYTES (default 2 GiB), at least 256.
+constexpr size_t kGemmWorkspace = size_t(128) << 20;
+
+lce_status run_fused_bwd(const void* x, const void* weight, int64_t tokens, int64_t hidden,
+                         int64_t vocab, const int64_t* target, bool mean, const float* grad,
+                         float* dx, float* dw, hipStream_t stream) {
+  lce_status s = LCE_OK;
+  int cus = 0;
+  if ((s = num_cus(&cus)) != LCE_OK) return s;
+  const lce::FusedGeometry geo = lce::fused_geometry();
+  const int64_t ld = (vocab + geo.block_vocab - 1) / geo.block_vocab * geo.block_vocab;
+  const int64_t cap = env_int64("LCE_FUSED_BWD_STORE_BYTES", int64_t(2) << 30);
+  int64_t chunk = cap / (ld * 2) / geo.block_tokens * geo.block_tokens;
+  if (chunk < geo.block_tokens) chunk = geo.block_tokens;
+  if (chunk > tokens) chunk = tokens;
+
+  Carve cv;
+  const size_t off_lse = cv.take((size_t)tokens * 4u);
+  const size_t off_ws = cv.take(kGemmWorkspace);
+  const size_t off_dz = cv.take((size_t)chunk * (size_t)ld * 2u);
+  const size_t reserved = cv.off - Carve().off;
+  const FusedPlan fp = plan_fused(tokens, vocab, cus, reserved);
+  char* base = nullptr;
+  if ((s = get_scratch(stream, fp.end > cv.off ? fp.end : cv.off, &base)) != LCE_OK) return s;
+  float* lse = (float*)(base + off_lse);
+  void* ws = base + off_ws;
+  void* dz = base + off_dz;
+
+  if ((s = run_fused(x, weight, tokens, hidden, vocab, nullptr, false, nullptr, stream, reserved,
+                     lse)) != LCE_OK)
+    return s;
+  const uint16_t* x16 = (const uint16_t*)x;
+  for (int64_t c0 = 0; c0 < tokens; c0 += chunk) {
+    const int64_t n = tokens - c0 < chunk ? tokens - c0 : chunk;
+    lce::FusedGradArgs g{};
+    g.x = x16 + c0 * hidden;
+    g.w = weight;
+    g.tokens = n;
+    g.hidden = hidden;
+    g.vocab = vocab;
+    g.target = target + c0;
+    g.lse = lse + c0;
+    g.grad = mean ? grad : grad + c0;
+    g.grad_mean = mean ? 1 : 0;
+    g.grad_tokens = tokens;
+    g.dz = dz;
+    g.dz_ld = ld;
+    g.segments = lce::fused_segments(n, vocab, cus);
+    hipError_t e = lce::launch_fused_grad(g, stream);
+    if (e != hipSuccess) return hip_fail(e, "kernel launch");
+    // Row-major [r, c] is column-major [c, r]: dx^T[H, n] = W^T[H, V] dZ^T[V, n],
+    // dW^T[H, V] (+)= x^T[H, n] dZ[n, V].
+    if (dx && (s = gemm_bf16_f32(HIPBLAS_OP_N, HIPBLAS_OP_N, hidden, n, vocab, weight, hidden, dz,
+                                 ld, 0.0f, dx + c0 * hidden, hidden, ws, kGemmWorkspace,
+                                 stream)) != LCE_OK)
+      return s;
+    if (dw && (s = gemm_bf16_f32(HIPBLAS_OP_N, HIPBLAS_OP_T, hidden, vocab, n, x16 + c0 * hidden,
+                                 hidden, dz, ld, c0 == 0 ? 0.0f : 1.0f, dw, hidden, ws,
+                                 kGemmWorkspace, stream)) != LCE_OK)
+      return s;
+  }
   return LCE_OK;
 }
 
@@ -761,6 +922,44 @@ lce_status lce_fused_linear_jsd_fwd(const void* student_x, const void* student_w
                           vocab, beta, mean, out, stream, cus, plan);
   return run_jsd_recompute(student_x, student_weight, teacher_x, teacher_weight, tokens, hidden,
                            vocab, beta, mean, out, stream, cus);
+}
+
+lce_status lce_fused_linear_xent_bwd(const void* x, const void* weight, int64_t tokens,
+                                     int64_t hidden, int64_t vocab, const int64_t* target,
+                                     lce_reduction reduction, const float* grad, float* dx,
+                                     float* dweight, hipStream_t stream) {
+  g_last_error.clear();
+  lce_status s = validate_common(tokens, target, (int)reduction, nullptr, nullptr);
+  if (s != LCE_OK) return s;
+  if ((s = validate_head(x, weight, tokens, hidden, vocab, nullptr, 0)) != LCE_OK) return s;
+  const bool mean = reduction == LCE_REDUCTION_MEAN;
+  if (!dx && !dweight) return fail(LCE_ERR_INVALID_ARG, "dx and dweight are both NULL");
+  if (tokens > 0 && !grad) return fail(LCE_ERR_INVALID_ARG, "grad is NULL");
+  if (grad && !aligned(grad, 4)) return fail(LCE_ERR_INVALID_ARG, "grad is not 4-byte aligned");
+  if ((dx && !aligned(dx, 4)) || (dweight && !aligned(dweight, 4)))
+    return fail(LCE_ERR_INVALID_ARG, "dx and dweight must be 4-byte aligned");
+  const int64_t ld = (vocab + 255) / 256 * 256;
+  if (ld * 256 * 2 >= (int64_t(1) << 32))
+    return fail(LCE_ERR_UNSUPPORTED, "vocab must be < 2^23 - 256 for the fused backward (got %lld)",
+                (long long)vocab);
+  const uint64_t xb = (uint64_t)(tokens * hidden * 2), wb = (uint64_t)(vocab * hidden * 2);
+  const uint64_t dxb = dx ? (uint64_t)(tokens * hidden * 4) : 0, dwb = dweight ? (uint64_t)(vocab * hidden * 4) : 0;
+  const uint64_t gb = mean ? 4u : (uint64_t)tokens * 4u, tb = (uint64_t)tokens * 8u;
+  const struct { const void* p; uint64_t n; const char* name; } outs[2] = {{dx, dxb, "dx"}, {dweight, dwb, "dweight"}};
+  for (const auto& o : outs) {
+    if (!o.p) continue;
+    if (overlaps(o.p, o.n, x, xb)) return fail(LCE_ERR_ALIAS, "%s overlaps x", o.name);
+    if (overlaps(o.p, o.n, weight, wb)) return fail(LCE_ERR_ALIAS, "%s overlaps weight", o.name);
+    if (overlaps(o.p, o.n, target, tb)) return fail(LCE_ERR_ALIAS, "%s overlaps target", o.name);
+    if (overlaps(o.p, o.n, grad, gb)) return fail(LCE_ERR_ALIAS, "%s overlaps grad", o.name);
+  }
+  if (overlaps(dx, dxb, dweight, dwb)) return fail(LCE_ERR_ALIAS, "dx overlaps dweight");
+  if (tokens == 0) {  // no token contributes: dweight is zero, dx is empty
+    if (!dweight) return LCE_OK;
+    hipError_t e = lce::launch_fill_f32(dweight, vocab * hidden, 0.0f, stream);
+    return e == hipSuccess ? LCE_OK : hip_fail(e, "launch");
+  }
+  return run_fused_bwd(x, weight, tokens, hidden, vocab, target, mean, grad, dx, dweight, stream);
 }
 
 }  // extern "C"

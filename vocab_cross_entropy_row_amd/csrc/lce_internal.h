@@ -82,6 +82,28 @@ struct FusedArgs {
   unsigned* ticket;
 };
 
+// Logit gradient of the fused projection for a block of tokens, written as
+// bf16 rows dz [tokens, dz_ld]: dz_ij = g_i (e^(z_ij - lse_i) - [j == t_i]),
+// g_i = grad[0] / grad_tokens (grad_mean) or grad[i]; NaN rows for targets
+// outside [0, vocab).  Columns in [vocab, dz_ld) receive values for zero
+// logits and are never meaningful.
+struct FusedGradArgs {
+  const void* x;          // bf16 [tokens, hidden]
+  const void* w;          // bf16 [vocab, hidden]
+  int64_t tokens;
+  int64_t hidden;
+  int64_t vocab;
+  const int64_t* target;  // [tokens]
+  const float* lse;       // [tokens] ln sum_j e^z_ij
+  const float* grad;      // [1] or [tokens]
+  int grad_mean;
+  int64_t grad_tokens;    // divisor of grad[0] with grad_mean
+  void* dz;               // bf16 [tokens, dz_ld]
+  int64_t dz_ld;          // multiple of block_vocab, >= vocab; dz_ld * block_tokens * 2 < 2^32
+  int segments;
+};
+hipError_t launch_fused_grad(const FusedGradArgs& a, hipStream_t stream);
+
 // Geometry of the fused kernel, needed by the host to size scratch.
 struct FusedGeometry {
   int block_tokens;   // tokens per workgroup tile
