@@ -321,6 +321,54 @@ def time_logprob_sums(torch, lce, lce_synth, steps: int, warmup: int) -> dict:
                          "unit": "TFLOP/s", "frac": round(tf / BF16_DENSE_TFLOPS, 4)}}
 
 
+def time_fused_bwd(torch, lce, lce_synth, steps: int, warmup: int) -> dict:
+    """Gradients of the fused projection + cross-entropy at the fused workload's shape
+    (lce_fused_linear_xent_bwd, mean reduction, dx and dW in fp32), timed as a HIP graph of
+    `steps` calls.  Algorithmic flops: the logits once plus the two products, 3 * 2*T*H*V
+    (the call executes 4 * 2*T*H*V: a log-sum-exp pass, the logit-gradient pass and the
+    two GEMMs)."""
+    w = lce_synth.WORKLOADS["fused_bf16_t2048_h4096_v128256_mean"]
+    (x, W, t), = make_inputs(w, torch, 1)
+    g = torch.ones(1, dtype=torch.float32, device="cuda")
+    dx = torch.empty(x.shape, dtype=torch.float32, device="cuda")
+    dw = torch.empty(W.shape, dtype=torch.float32, device="cuda")
+
+    def call():
+        lce.fused_linear_xent_bwd(x, W, t, g, "mean", dx=dx, dweight=dw)
+    for _ in range(max(1, warmup)):
+        call()
+    torch.cuda.synchronize()
+    ref = (dx.clone(), dw.clone())
+    gr = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        call()
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(gr, stream=st):
+        for _ in range(steps):
+            call()
+    gr.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(st):
+        e0.record(st)
+        gr.replay()
+        e1.record(st)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / steps
+    same = bool(torch.equal(dx, ref[0]) and torch.equal(dw, ref[1]))
+    flops = 3 * fused_flops(w.tokens, w.hidden, w.vocab)
+    tf = flops / (us * 1e-6) / 1e12
+    del x, W, t, dx, dw, ref, gr
+    torch.cuda.empty_cache()
+    return {"shape": f"tokens {w.tokens}, hidden {w.hidden}, vocab {w.vocab}, mean; dx and dW fp32",
+            "us_per_step": round(us, 1), "graph_matches_eager": same, "algorithmic_flops": flops,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_DENSE_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / BF16_DENSE_TFLOPS, 4)}}
+
+
 def time_jsd(torch, lce, lce_synth, steps: int, warmup: int) -> dict:
     """Fused linear + JSD at the JSD page's shape (tokens 1024, hidden 4096, vocab 128256,
     beta 0.5, batchmean), timed as a HIP graph of `steps` calls, on the default path
@@ -618,6 +666,7 @@ def main(argv=None) -> int:
     shard = None
     sums = None
     jsd = None
+    fbwd = None
     backward = {}
     if args.workloads == "all" and not args.eager:
         for bname in (lce_synth.HEADLINE, "ce_f32_16384x4096_mean"):
@@ -628,6 +677,9 @@ def main(argv=None) -> int:
         shard = time_vocab_shard(torch, lce, lce_synth, 8, min(args.steps, 200), args.warmup)
         sums = time_logprob_sums(torch, lce, lce_synth, min(args.steps, 10), 2)
         jsd = time_jsd(torch, lce, lce_synth, min(args.steps, 10), 2)
+        fbwd = time_fused_bwd(torch, lce, lce_synth, min(args.steps, 5), 2)
+        print(f"[bench] fused backward: {fbwd['us_per_step']:.1f} µs "
+              f"({fbwd['roofline']['achieved']} TFLOP/s over 3*2THV)", file=sys.stderr, flush=True)
         print(f"[bench] fused linear + JSD: stored {jsd['stored']['us_per_step']:.1f} µs "
               f"({jsd['stored']['roofline']['achieved']} TFLOP/s), recompute "
               f"{jsd['recompute']['us_per_step']:.1f} µs", file=sys.stderr, flush=True)
@@ -681,6 +733,8 @@ def main(argv=None) -> int:
         line["fused_logprob_sums"] = sums
     if jsd is not None:
         line["fused_linear_jsd"] = jsd
+    if fbwd is not None:
+        line["fused_backward"] = fbwd
     print(json.dumps(line), flush=True)
     return 0
 

@@ -161,3 +161,36 @@ def test_page_shape_sampled_and_properties():
     want_dx, _ = oracle.fused_linear_xent_grads(xb[rows], wb, t[rows], scale, want_dw=False)
     bx, _ = _bounds(xb[rows], wb, t[rows], scale, want_dw=False)
     _check("dx rows", dx.cpu().numpy()[rows], want_dx, bx)
+
+
+def test_graph_replays_match_eager():
+    """The backward (fused kernels and hipBLASLt GEMMs) recorded into a HIP graph:
+    every replay, with eager work in between, reproduces the eager gradients."""
+    xb, wb, t = _inputs(13, 300, 128, 2000)
+    x, W = to_dev(xb), to_dev(wb)
+    td = torch.from_numpy(t).cuda()
+    g = torch.full((1,), 0.5, device="cuda")
+    dx = torch.empty(x.shape, device="cuda")
+    dw = torch.empty(W.shape, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # eager reference; plans the GEMMs and grows the scratch
+        lce.fused_linear_xent_bwd(x, W, td, g, "mean", dx=dx, dweight=dw)
+    torch.cuda.synchronize()
+    ref = (dx.clone(), dw.clone())
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr, stream=s):
+        lce.fused_linear_xent_bwd(x, W, td, g, "mean", dx=dx, dweight=dw)
+    torch.cuda.synchronize()
+    xo, wo, to_ = _inputs(14, 100, 64, 700)
+    for r in range(3):
+        dx.fill_(float("nan"))
+        dw.fill_(float("nan"))
+        with torch.cuda.stream(s):  # other eager work on the same stream and scratch
+            lce.fused_linear_xent_bwd(to_dev(xo), to_dev(wo), torch.from_numpy(to_).cuda(),
+                                      torch.ones(1, device="cuda"), "mean")
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            gr.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dx, ref[0]) and torch.equal(dw, ref[1]), f"replay {r}"
