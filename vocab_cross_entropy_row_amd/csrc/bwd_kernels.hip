@@ -126,12 +126,16 @@ __global__ __launch_bounds__(64 * WAVES) void xent_bwd_wave_kernel(
   const __amdgpu_buffer_rsrc_t src = make_rsrc(rp + rs.head, (uint32_t)n * 16u);
   const __amdgpu_buffer_rsrc_t dst = make_rsrc(dp + rs.head, (uint32_t)n * 16u);
 
+  // Head and tail elements first, and only when the row has any (a load
+  // issued behind the row's chunks would return behind them all).
+  const int ei = edge_index(rs, vocab, lane);
+  float edge = 0.0f;
+  if (wave_uniform(rs.head + rs.tail) > 0) edge = Vec<T>::scalar(rp + ei);
+  __builtin_amdgcn_sched_barrier(0);
   raw v[NCH];
 #pragma unroll
   for (int k = 0; k < NCH; ++k)
     v[k] = (raw)__builtin_amdgcn_raw_buffer_load_b128(src, (lane + 64 * k) * 16, 0, kStreamPolicy);
-  const int ei = edge_index(rs, vocab, lane);
-  const float edge = Vec<T>::scalar(rp + ei);
   const bool has_edge = lane < rs.head + rs.tail;
 
   // Row state.  Chunks past the body become -inf: they fold as nothing, and
