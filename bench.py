@@ -74,15 +74,15 @@ KERNEL_SOURCES = {
 
 
 def source_digest(kind: str) -> str:
-    """sha256 over the sources of a workload kind's kernels and the build script: ties
-    counter data to the kernel build it was taken on."""
+    """sha256 over the sources of a workload kind's kernels and the device compiler flags:
+    ties counter data to the kernel build it was taken on."""
+    from vocab_cross_entropy_row_amd import build as lce_build
     h = hashlib.sha256()
-    files = [os.path.join(CSRC, f) for f in KERNEL_SOURCES[kind]]
-    files.append(os.path.join(ROOT, "vocab_cross_entropy_row_amd", "build.py"))
-    for f in files:
-        h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
+    for f in KERNEL_SOURCES[kind]:
+        h.update(f.encode())
+        with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
+    h.update(" ".join(lce_build.common_flags()).encode())
     return h.hexdigest()
 
 
@@ -573,7 +573,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, kernel_substr: 
     FETCH_SIZE run and a WRITE_SIZE run (KiB per dispatch), each scaled by the same
     counter's reading for the COPY_BYTES copy kernel in the same run."""
     out = {"workload": workload, "kernel_match": kernel_substr, "commands": commands,
-           "copy_bytes": COPY_BYTES, "source_files": KERNEL_SOURCES[kind] + ["build.py"],
+           "copy_bytes": COPY_BYTES, "source_files": KERNEL_SOURCES[kind] + ["(compile flags)"],
            "source_sha256": source_digest(kind)}
     total = 0.0
     for label, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
