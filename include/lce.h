@@ -262,13 +262,15 @@ lce_status lce_fused_linear_logprob_sums(const void* x, const void* weight, int6
  *     dx     = dZ * weight        [tokens, hidden]
  *     dweight = dZ^T * x          [vocab, hidden]
  *
- * The full logits are never stored: the forward kernel gives each token's
- * log-sum-exp, then for chunks of tokens the fused kernel recomputes the
- * logits and writes dZ as bf16 (round to nearest even) into scratch, and two
- * hipBLASLt GEMMs (bf16 operands, fp32 accumulation) consume it.  The chunk is
- * the largest multiple of 256 tokens whose dZ (2 * tokens * vocab bytes, vocab
- * rounded up to 256) fits in LCE_FUSED_BWD_STORE_BYTES (environment, default
- * 2 GiB), and at least 256 tokens.
+ * Per chunk of tokens, the fused kernel forms the logits with their per-token
+ * log-sum-exp and keeps them in scratch as fp32, a streaming kernel turns them
+ * into dZ as bf16 (round to nearest even), and two hipBLASLt GEMMs (bf16
+ * operands, fp32 accumulation) consume it.  The chunk is the largest multiple
+ * of 256 tokens whose logits and dZ (6 * tokens * vocab bytes, vocab rounded
+ * up to 256) fit in LCE_FUSED_BWD_STORE_BYTES (environment, default 2 GiB).
+ * When not even 256 tokens fit, no fp32 logits are kept: the log-sum-exp of
+ * every token is taken first and the fused kernel recomputes the logits of
+ * each 256-token chunk to write dZ (2 bytes per logit; one more GEMM pass).
  *
  *   x, weight, tokens, hidden, target: as lce_fused_linear_xent_fwd; also
  *             vocab < 2^23 - 256.

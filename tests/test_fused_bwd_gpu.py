@@ -77,27 +77,43 @@ def _run(xb, wb, t, grad, reduction, want_dx=True, want_dw=True, env=None):
 # hidden off the 64-element slab), one token, and several token chunks.
 CASES = [(1, 64, 100), (5, 128, 1000), (130, 72, 3000), (300, 200, 515), (600, 64, 1001)]
 
+# Paths: fp32 logits stored for all tokens at once (default), stored in 256-token chunks,
+# and recomputed by the gradient mode of the fused kernel (no fp32 logits stored).
+MODES = ("stored", "chunked", "recompute")
 
+
+def _env(mode, vocab):
+    ld = -(-vocab // 256) * 256
+    if mode == "chunked":
+        return {"LCE_FUSED_BWD_STORE_BYTES": 256 * ld * 6}
+    if mode == "recompute":
+        return {"LCE_FUSED_BWD_STORE_BYTES": 0}
+    return {}
+
+
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("reduction", ["mean", "none"])
 @pytest.mark.parametrize("tokens,hidden,vocab", CASES)
-def test_grads_match_oracle(tokens, hidden, vocab, reduction):
+def test_grads_match_oracle(tokens, hidden, vocab, reduction, mode):
     xb, wb, t = _inputs(tokens * 7 + vocab, tokens, hidden, vocab)
     rng = np.random.default_rng(tokens)
     grad = np.array([1.7]) if reduction == "mean" else rng.normal(size=tokens)
     grad = grad.astype(np.float32).astype(np.float64)
-    dx, dw = _run(xb, wb, t, grad, reduction)
+    dx, dw = _run(xb, wb, t, grad, reduction, env=_env(mode, vocab))
     want_dx, want_dw = oracle.fused_linear_xent_bwd(xb, wb, t, grad, reduction)
     bx, bw = _bounds(xb, wb, t, _row_scale(grad, reduction, tokens))
     _check("dx", dx, want_dx, bx)
     _check("dW", dw, want_dw, bw)
 
 
-def test_token_chunks_give_the_same_grads():
-    """256-token chunks (dW accumulated over chunks in the GEMM's C) against one chunk."""
+@pytest.mark.parametrize("mode", ["chunked", "recompute"])
+def test_token_chunks_give_the_same_grads(mode):
+    """256-token chunks (dW accumulated over chunks in the GEMM's C) against one chunk;
+    the stored and recomputed logit gradients are the same bf16 values, so only the
+    GEMMs' chunking can differ."""
     xb, wb, t = _inputs(3, 700, 128, 2000)
     one = _run(xb, wb, t, [1.0], "mean")
-    ld = 2048
-    chunked = _run(xb, wb, t, [1.0], "mean", env={"LCE_FUSED_BWD_STORE_BYTES": 256 * ld * 2})
+    chunked = _run(xb, wb, t, [1.0], "mean", env=_env(mode, 2000))
     bx, bw = _bounds(xb, wb, t, np.full(700, 1.0 / 700))
     _check("dx chunked vs one", chunked[0], one[0], bx)
     _check("dW chunked vs one", chunked[1], one[1], bw)
@@ -115,10 +131,11 @@ def test_one_gradient_only():
     assert np.array_equal(dx, dx_only) and np.array_equal(dw, dw_only)
 
 
-def test_invalid_target_poisons_its_row_and_dweight():
+@pytest.mark.parametrize("mode", ["stored", "recompute"])
+def test_invalid_target_poisons_its_row_and_dweight(mode):
     xb, wb, t = _inputs(7, 40, 64, 300)
     t[11] = 300
-    dx, dw = _run(xb, wb, t, [1.0], "mean")
+    dx, dw = _run(xb, wb, t, [1.0], "mean", env=_env(mode, 300))
     assert np.isnan(dx[11]).all() and np.isfinite(np.delete(dx, 11, axis=0)).all()
     assert np.isnan(dw).all()
 
@@ -133,11 +150,12 @@ def test_empty_tokens_give_zero_dweight():
     assert torch.equal(dw.cpu(), torch.zeros(10, 64))
 
 
-def test_repeated_calls_bitwise_identical():
+@pytest.mark.parametrize("mode", MODES)
+def test_repeated_calls_bitwise_identical(mode):
     xb, wb, t = _inputs(9, 520, 128, 3000)
-    first = _run(xb, wb, t, [1.0], "mean")
+    first = _run(xb, wb, t, [1.0], "mean", env=_env(mode, 3000))
     for _ in range(3):
-        again = _run(xb, wb, t, [1.0], "mean")
+        again = _run(xb, wb, t, [1.0], "mean", env=_env(mode, 3000))
         assert np.array_equal(first[0], again[0]) and np.array_equal(first[1], again[1])
 
 
@@ -150,8 +168,13 @@ def test_page_shape_sampled_and_properties():
     dx, dw = lce.fused_linear_xent_bwd(x, W, td, torch.ones(1, device="cuda"), "mean")
     dx_n, dw_n = lce.fused_linear_xent_bwd(x, W, td, torch.full((T,), 1.0 / T, device="cuda"),
                                            "none")
+    with forced_env(LCE_FUSED_BWD_STORE_BYTES=0):
+        dx_r, dw_r = lce.fused_linear_xent_bwd(x, W, td, torch.ones(1, device="cuda"), "mean")
     torch.cuda.synchronize()
     assert torch.equal(dx, dx_n) and torch.equal(dw, dw_n)  # 1/2048 is exact in fp32
+    # Stored and recomputed logits are the same fp32 sums, so dZ is bit-identical; only
+    # the recompute path's 256-token chunks change the GEMMs' shapes.
+    assert torch.allclose(dx_r, dx, rtol=0, atol=1e-6) and torch.allclose(dw_r, dw, rtol=0, atol=1e-6)
     # Columns of dW sum to ~0: each dZ row sums to 0 up to its bf16 rounding.
     col = dw.double().sum(dim=0).abs()
     lim = REL * (x.double().abs().sum(dim=0) * 2.0 / T) + 1e-6

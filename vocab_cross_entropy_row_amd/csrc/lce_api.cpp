@@ -15,6 +15,7 @@
 #include <tuple>
 #include <utility>
 
+#include "fused_grad.h"
 #include "lce.h"
 #include "lce_internal.h"
 
@@ -479,12 +480,17 @@ lce_status gemm_bf16_f32(hipblasOperation_t ta, hipblasOperation_t tb, int64_t m
   return LCE_OK;
 }
 
-// Gradients of the fused projection + cross-entropy.  The per-token
-// log-sum-exp comes from the forward kernel; then, for chunks of tokens, the
-// fused kernel's gradient mode writes the bf16 logit gradient dZ [chunk, ld]
-// into scratch and two library GEMMs consume it: dx[chunk] = dZ W and
-// dW (+)= dZ^T x[chunk].  The chunk is the largest multiple of 256 tokens whose
-// dZ fits in LCE_FUSED_BWD_STORE_BYTES (default 2 GiB), at least 256.
+// Gradients of the fused projection + cross-entropy, for chunks of tokens.
+// Stored path (default): the forward kernel's store mode gives each chunk's
+// log-sum-exp and writes its fp32 logits [chunk, ld] into scratch, then
+// fused_grad_rows_kernel turns them into the bf16 logit gradient dZ [chunk,
+// ld].  Recompute path (when not even 256 tokens of fp32 logits and dZ fit):
+// the forward kernel gives every token's log-sum-exp, then for each chunk
+// the fused kernel's gradient mode recomputes the logits and writes dZ.
+// Either way two library GEMMs consume dZ: dx[chunk] = dZ W and
+// dW (+)= dZ^T x[chunk].  Chunks are the largest multiple of 256 tokens whose
+// buffers (6 or 2 bytes per logit) fit in LCE_FUSED_BWD_STORE_BYTES (default
+// 2 GiB), at least 256.
 constexpr size_t kGemmWorkspace = size_t(128) << 20;
 
 lce_status run_fused_bwd(const void* x, const void* weight, int64_t tokens, int64_t hidden,
@@ -496,7 +502,8 @@ lce_status run_fused_bwd(const void* x, const void* weight, int64_t tokens, int6
   const lce::FusedGeometry geo = lce::fused_geometry();
   const int64_t ld = (vocab + geo.block_vocab - 1) / geo.block_vocab * geo.block_vocab;
   const int64_t cap = env_int64("LCE_FUSED_BWD_STORE_BYTES", int64_t(2) << 30);
-  int64_t chunk = cap / (ld * 2) / geo.block_tokens * geo.block_tokens;
+  const bool stored = cap / (ld * 6) >= geo.block_tokens;
+  int64_t chunk = cap / (ld * (stored ? 6 : 2)) / geo.block_tokens * geo.block_tokens;
   if (chunk < geo.block_tokens) chunk = geo.block_tokens;
   if (chunk > tokens) chunk = tokens;
 
@@ -504,35 +511,61 @@ lce_status run_fused_bwd(const void* x, const void* weight, int64_t tokens, int6
   const size_t off_lse = cv.take((size_t)tokens * 4u);
   const size_t off_ws = cv.take(kGemmWorkspace);
   const size_t off_dz = cv.take((size_t)chunk * (size_t)ld * 2u);
+  const size_t off_z = cv.take(stored ? (size_t)chunk * (size_t)ld * 4u : 0u);
   const size_t reserved = cv.off - Carve().off;
-  const FusedPlan fp = plan_fused(tokens, vocab, cus, reserved);
+  const int64_t last = tokens - (tokens - 1) / chunk * chunk;
+  size_t need = cv.off;
+  for (int64_t n : {stored ? chunk : tokens, last}) {
+    const FusedPlan fp = plan_fused(n, vocab, cus, reserved);
+    if (fp.end > need) need = fp.end;
+  }
   char* base = nullptr;
-  if ((s = get_scratch(stream, fp.end > cv.off ? fp.end : cv.off, &base)) != LCE_OK) return s;
+  if ((s = get_scratch(stream, need, &base)) != LCE_OK) return s;
   float* lse = (float*)(base + off_lse);
   void* ws = base + off_ws;
   void* dz = base + off_dz;
+  float* z = (float*)(base + off_z);
 
-  if ((s = run_fused(x, weight, tokens, hidden, vocab, nullptr, false, nullptr, stream, reserved,
-                     lse)) != LCE_OK)
+  if (!stored && (s = run_fused(x, weight, tokens, hidden, vocab, nullptr, false, nullptr, stream,
+                                reserved, lse)) != LCE_OK)
     return s;
   const uint16_t* x16 = (const uint16_t*)x;
   for (int64_t c0 = 0; c0 < tokens; c0 += chunk) {
     const int64_t n = tokens - c0 < chunk ? tokens - c0 : chunk;
-    lce::FusedGradArgs g{};
-    g.x = x16 + c0 * hidden;
-    g.w = weight;
-    g.tokens = n;
-    g.hidden = hidden;
-    g.vocab = vocab;
-    g.target = target + c0;
-    g.lse = lse + c0;
-    g.grad = mean ? grad : grad + c0;
-    g.grad_mean = mean ? 1 : 0;
-    g.grad_tokens = tokens;
-    g.dz = dz;
-    g.dz_ld = ld;
-    g.segments = lce::fused_segments(n, vocab, cus);
-    hipError_t e = lce::launch_fused_grad(g, stream);
+    hipError_t e = hipSuccess;
+    if (stored) {
+      if ((s = run_fused(x16 + c0 * hidden, weight, n, hidden, vocab, nullptr, false, nullptr,
+                         stream, reserved, lse + c0, z, ld)) != LCE_OK)
+        return s;
+      lce::FusedGradRowsArgs g{};
+      g.z = z;
+      g.lse = lse + c0;
+      g.target = target + c0;
+      g.grad = mean ? grad : grad + c0;
+      g.grad_mean = mean ? 1 : 0;
+      g.grad_tokens = tokens;
+      g.rows = n;
+      g.vocab = vocab;
+      g.ld = ld;
+      g.dz = (uint16_t*)dz;
+      e = lce::launch_fused_grad_rows(g, stream);
+    } else {
+      lce::FusedGradArgs g{};
+      g.x = x16 + c0 * hidden;
+      g.w = weight;
+      g.tokens = n;
+      g.hidden = hidden;
+      g.vocab = vocab;
+      g.target = target + c0;
+      g.lse = lse + c0;
+      g.grad = mean ? grad : grad + c0;
+      g.grad_mean = mean ? 1 : 0;
+      g.grad_tokens = tokens;
+      g.dz = dz;
+      g.dz_ld = ld;
+      g.segments = lce::fused_segments(n, vocab, cus);
+      e = lce::launch_fused_grad(g, stream);
+    }
     if (e != hipSuccess) return hip_fail(e, "kernel launch");
     // Row-major [r, c] is column-major [c, r]: dx^T[H, n] = W^T[H, V] dZ^T[V, n],
     // dW^T[H, V] (+)= x^T[H, n] dZ[n, V].
