@@ -30,8 +30,10 @@
  *     used (the pages do not specify determinism).
  *   - liblce keeps a device scratch buffer per (device, stream), grown on
  *     demand with hipMalloc to 1.25x the need.  It is small (per-token and
- *     per-workgroup partials) except for lce_fused_linear_jsd_fwd, which
- *     keeps up to LCE_JSD_STORE_BYTES (default 2 GiB) of logits there.  An
+ *     per-workgroup partials) except for lce_fused_linear_jsd_fwd and
+ *     lce_fused_linear_xent_bwd, which keep up to LCE_JSD_STORE_BYTES and
+ *     LCE_FUSED_BWD_STORE_BYTES (default 2 GiB each) of logits there (the
+ *     backward also 128 MiB of GEMM workspace).  An
  *     outgrown buffer is retired, never freed: every scratch buffer is kept
  *     until the process ends, so the retired ones add up to at most 4x the
  *     live one.  Calls on one stream are ordered by the stream; calls on
