@@ -9,6 +9,12 @@
  *   per token i:   loss_i = ln( sum_j exp(z_ij) ) - z_{i, t_i}
  *   mean:          (1 / tokens) * sum_i loss_i
  *
+ * on a stored logit matrix or on logits z = x * W^T formed on the fly from
+ * bf16 activations and an LM head; with its gradients, the two local halves
+ * of a vocab split across devices, per-sequence sums of target
+ * log-probabilities, and a generalized Jensen-Shannon divergence between a
+ * student's and a teacher's projections.
+ *
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers on the current HIP device,
  *     row-major and contiguous.  The caller owns every buffer; liblce never
@@ -27,7 +33,8 @@
  *   - Losses are always fp32; accumulation is fp32.
  *   - Results are bitwise reproducible run to run for the same inputs, shape
  *     and device: every reduction has a fixed order and no float atomics are
- *     used (the pages do not specify determinism).
+ *     used (the pages do not specify determinism).  The fused backward's two
+ *     GEMMs run the algorithm hipBLASLt's heuristic picks for the shape.
  *   - liblce keeps a device scratch buffer per (device, stream), grown on
  *     demand with hipMalloc to 1.25x the need.  It is small (per-token and
  *     per-workgroup partials) except for lce_fused_linear_jsd_fwd and
