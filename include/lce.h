@@ -64,6 +64,9 @@
 extern "C" {
 #endif
 
+/* The library is built with hidden visibility; only these entry points are exported. */
+#define LCE_API __attribute__((visibility("default")))
+
 #define LCE_VERSION_MAJOR 0
 #define LCE_VERSION_MINOR 4
 #define LCE_VERSION_PATCH 0
@@ -118,7 +121,7 @@ typedef enum {
  * scratch that would have to grow under graph capture), LCE_ERR_ALIAS,
  * LCE_ERR_OOM or LCE_ERR_HIP.
  */
-lce_status lce_xent_fwd(const void* logits, lce_dtype dtype, int64_t tokens, int64_t vocab,
+LCE_API lce_status lce_xent_fwd(const void* logits, lce_dtype dtype, int64_t tokens, int64_t vocab,
                         const int64_t* target, lce_reduction reduction, float* out,
                         hipStream_t stream);
 
@@ -144,7 +147,7 @@ lce_status lce_xent_fwd(const void* logits, lce_dtype dtype, int64_t tokens, int
  * up to 32 KiB are read once and written once; longer rows are read twice.
  * Nothing is written when tokens == 0.  Returns as lce_xent_fwd.
  */
-lce_status lce_xent_bwd(const void* logits, lce_dtype dtype, int64_t tokens, int64_t vocab,
+LCE_API lce_status lce_xent_bwd(const void* logits, lce_dtype dtype, int64_t tokens, int64_t vocab,
                         const int64_t* target, lce_reduction reduction, const float* grad,
                         void* dlogits, hipStream_t stream);
 
@@ -176,7 +179,7 @@ lce_status lce_xent_bwd(const void* logits, lce_dtype dtype, int64_t tokens, int
  *
  * Nothing is written when tokens == 0.  Returns as lce_xent_fwd.
  */
-lce_status lce_xent_partial_fwd(const void* logits, lce_dtype dtype, int64_t tokens,
+LCE_API lce_status lce_xent_partial_fwd(const void* logits, lce_dtype dtype, int64_t tokens,
                                 int64_t shard_vocab, int64_t vocab_start, const int64_t* target,
                                 float* partial, hipStream_t stream);
 
@@ -201,7 +204,7 @@ lce_status lce_xent_partial_fwd(const void* logits, lce_dtype dtype, int64_t tok
  * (shards >= 2^31, or scratch that would have to grow under graph capture),
  * LCE_ERR_ALIAS, LCE_ERR_OOM or LCE_ERR_HIP.
  */
-lce_status lce_xent_merge(const float* partials, int64_t shards, int64_t tokens,
+LCE_API lce_status lce_xent_merge(const float* partials, int64_t shards, int64_t tokens,
                           const int64_t* target, int64_t vocab, lce_reduction reduction,
                           float* out, hipStream_t stream);
 
@@ -232,7 +235,7 @@ lce_status lce_xent_merge(const float* partials, int64_t shards, int64_t tokens,
  * Returns as lce_xent_fwd; LCE_ERR_UNSUPPORTED when hidden is not a multiple
  * of 8 or x / weight are not 16-byte aligned.
  */
-lce_status lce_fused_linear_xent_fwd(const void* x, const void* weight, int64_t tokens,
+LCE_API lce_status lce_fused_linear_xent_fwd(const void* x, const void* weight, int64_t tokens,
                                      int64_t hidden, int64_t vocab, const int64_t* target,
                                      lce_reduction reduction, float* out, hipStream_t stream);
 
@@ -256,7 +259,7 @@ lce_status lce_fused_linear_xent_fwd(const void* x, const void* weight, int64_t 
  * The sum over a sequence is a fixed-order reduction (bitwise reproducible).
  * Returns as lce_fused_linear_xent_fwd.
  */
-lce_status lce_fused_linear_logprob_sums(const void* x, const void* weight, int64_t batch,
+LCE_API lce_status lce_fused_linear_logprob_sums(const void* x, const void* weight, int64_t batch,
                                          int64_t seq, int64_t hidden, int64_t vocab,
                                          const int64_t* target, float* out, hipStream_t stream);
 
@@ -299,7 +302,7 @@ lce_status lce_fused_linear_logprob_sums(const void* x, const void* weight, int6
  * fails with LCE_ERR_UNSUPPORTED.  Returns as lce_fused_linear_xent_fwd,
  * LCE_ERR_HIP also for a failing hipBLASLt call.
  */
-lce_status lce_fused_linear_xent_bwd(const void* x, const void* weight, int64_t tokens,
+LCE_API lce_status lce_fused_linear_xent_bwd(const void* x, const void* weight, int64_t tokens,
                                      int64_t hidden, int64_t vocab, const int64_t* target,
                                      lce_reduction reduction, const float* grad, float* dx,
                                      float* dweight, hipStream_t stream);
@@ -339,20 +342,20 @@ lce_status lce_fused_linear_xent_bwd(const void* x, const void* weight, int64_t 
  * beta; LCE_ERR_UNSUPPORTED as lce_fused_linear_xent_fwd; LCE_ERR_ALIAS when
  * out overlaps an input; LCE_ERR_HIP / LCE_ERR_OOM as lce_xent_fwd.
  */
-lce_status lce_fused_linear_jsd_fwd(const void* student_x, const void* student_weight,
+LCE_API lce_status lce_fused_linear_jsd_fwd(const void* student_x, const void* student_weight,
                                     const void* teacher_x, const void* teacher_weight,
                                     int64_t tokens, int64_t hidden, int64_t vocab, float beta,
                                     lce_reduction reduction, float* out, hipStream_t stream);
 
 /* Static, human-readable name of a status code (never NULL). */
-const char* lce_status_string(lce_status status);
+LCE_API const char* lce_status_string(lce_status status);
 
 /* Detail message of the last failing call on this thread ("" if none).
  * The pointer stays valid until the next liblce call on this thread. */
-const char* lce_last_error(void);
+LCE_API const char* lce_last_error(void);
 
 /* MAJOR * 10000 + MINOR * 100 + PATCH. */
-int lce_version(void);
+LCE_API int lce_version(void);
 
 #ifdef __cplusplus
 }

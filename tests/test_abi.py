@@ -26,7 +26,8 @@ def lib():
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(lce_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:LCE_API\s+)?(?:const\s+)?\w+\*?\s+\**(lce_\w+)\s*\(",
+                                 text, re.M)))
 
 
 def test_header_declares_the_boundary():
@@ -40,6 +41,8 @@ def test_every_declared_symbol_is_exported(lib):
     for name in declared_functions():
         assert name in exported, name
         assert hasattr(lib, name)
+    # The host code is built with hidden visibility: no internal function leaks.
+    assert not [n for n in exported if "lce" in n and not n.startswith("lce_")]
 
 
 def test_version_and_status_strings(lib):

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblce.so")
 
-SOURCES = ["lce_api.cpp", "xent_kernels.hip", "fused_kernel.hip", "bwd_kernels.hip", "seq_kernels.hip",
+SOURCES = ["lce_api.cpp", "lce_host.cpp", "lce_gemm.cpp", "lce_fused_paths.cpp", "xent_kernels.hip", "fused_kernel.hip", "bwd_kernels.hip", "seq_kernels.hip",
            "jsd_kernel.hip", "fused_grad_kernel.hip"]
 ARCH = "gfx950"
 
@@ -46,7 +46,10 @@ def build(verbose: bool = False) -> str:
         obj = os.path.join(BUILD, src.replace(".", "_") + ".o")
         objs.append(obj)
         lang = ["-x", "hip"]
-        cmd = [cc, *lang, *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+        # Only the C ABI (LCE_API in lce.h) is exported: host code, and the
+        # host side of the kernel sources (launchers, stubs), is hidden.
+        vis = ["-fvisibility=hidden"] if src.endswith(".cpp") else ["-Xarch_host", "-fvisibility=hidden"]
+        cmd = [cc, *lang, *common_flags(), *vis, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
