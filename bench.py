@@ -606,6 +606,9 @@ def main(argv=None) -> int:
     ap.add_argument("--workloads", default="all",
                     help="'all', 'headline', or a comma list of workload names")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--extras", default=None,
+                    help="comma list of extra measurements (backward, shard, sums, jsd, "
+                         "fused_bwd); default: all of them when --workloads is all")
     ap.add_argument("--eager", action="store_true",
                     help="time plain launches instead of a graph replay (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -668,26 +671,38 @@ def main(argv=None) -> int:
     jsd = None
     fbwd = None
     backward = {}
-    if args.workloads == "all" and not args.eager:
+    all_extras = ("backward", "shard", "sums", "jsd", "fused_bwd")
+    if args.extras is not None:
+        extras = [e for e in args.extras.split(",") if e]
+        unknown = [e for e in extras if e not in all_extras]
+        if unknown:
+            raise SystemExit(f"unknown extras {unknown}; choose from {all_extras}")
+    else:
+        extras = list(all_extras) if args.workloads == "all" and not args.eager else []
+    if "backward" in extras:
         for bname in (lce_synth.HEADLINE, "ce_f32_16384x4096_mean"):
             bw = lce_synth.WORKLOADS[bname]
             backward[bname] = time_backward(bw, torch, lce, min(args.steps, 200), args.warmup)
             print(f"[bench] backward {bname}: {backward[bname]['us_per_step']:.2f} µs/step "
                   f"({backward[bname]['roofline']['achieved']} GB/s)", file=sys.stderr, flush=True)
+    if "shard" in extras:
         shard = time_vocab_shard(torch, lce, lce_synth, 8, min(args.steps, 200), args.warmup)
-        sums = time_logprob_sums(torch, lce, lce_synth, min(args.steps, 10), 2)
-        jsd = time_jsd(torch, lce, lce_synth, min(args.steps, 10), 2)
-        fbwd = time_fused_bwd(torch, lce, lce_synth, min(args.steps, 5), 2)
-        print(f"[bench] fused backward: {fbwd['us_per_step']:.1f} µs "
-              f"({fbwd['roofline']['achieved']} TFLOP/s over 3*2THV)", file=sys.stderr, flush=True)
-        print(f"[bench] fused linear + JSD: stored {jsd['stored']['us_per_step']:.1f} µs "
-              f"({jsd['stored']['roofline']['achieved']} TFLOP/s), recompute "
-              f"{jsd['recompute']['us_per_step']:.1f} µs", file=sys.stderr, flush=True)
-        print(f"[bench] fused log-prob sums: {sums['us_per_step']:.1f} µs "
-              f"({sums['roofline']['achieved']} TFLOP/s)", file=sys.stderr, flush=True)
         print(f"[bench] vocab shard tp=8: partial {shard['partial_us']:.2f} µs, "
               f"merge {shard['merge_us']:.2f} µs, max |diff| vs unsplit "
               f"{shard['max_abs_diff_vs_unsplit']:.2e}", file=sys.stderr, flush=True)
+    if "sums" in extras:
+        sums = time_logprob_sums(torch, lce, lce_synth, min(args.steps, 10), 2)
+        print(f"[bench] fused log-prob sums: {sums['us_per_step']:.1f} µs "
+              f"({sums['roofline']['achieved']} TFLOP/s)", file=sys.stderr, flush=True)
+    if "jsd" in extras:
+        jsd = time_jsd(torch, lce, lce_synth, min(args.steps, 10), 2)
+        print(f"[bench] fused linear + JSD: stored {jsd['stored']['us_per_step']:.1f} µs "
+              f"({jsd['stored']['roofline']['achieved']} TFLOP/s), recompute "
+              f"{jsd['recompute']['us_per_step']:.1f} µs", file=sys.stderr, flush=True)
+    if "fused_bwd" in extras:
+        fbwd = time_fused_bwd(torch, lce, lce_synth, min(args.steps, 5), 2)
+        print(f"[bench] fused backward: {fbwd['us_per_step']:.1f} µs "
+              f"({fbwd['roofline']['achieved']} TFLOP/s over 3*2THV)", file=sys.stderr, flush=True)
 
     if args.copy_calibration:
         copy_calibration(torch)
