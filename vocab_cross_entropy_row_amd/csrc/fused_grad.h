@@ -28,4 +28,9 @@ struct FusedGradRowsArgs {
 };
 hipError_t launch_fused_grad_rows(const FusedGradRowsArgs& a, hipStream_t stream);
 
+// out [cols, rows] = transpose of in [rows, cols], 16-bit elements, both
+// row-major and contiguous.
+hipError_t launch_transpose_u16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out,
+                                hipStream_t stream);
+
 }  // namespace lce

@@ -60,6 +60,38 @@ __global__ __launch_bounds__(kGThreads) void fused_grad_rows_kernel(
   }
 }
 
+// Transpose of a [rows, cols] matrix of 16-bit elements through 64 x 64 LDS
+// tiles (the +1 column of padding keeps the transposed reads off one bank).
+// Reads and writes are coalesced along the tile's rows.
+__global__ __launch_bounds__(256) void transpose_u16_kernel(const uint16_t* __restrict__ in,
+                                                            int64_t rows, int64_t cols,
+                                                            uint16_t* __restrict__ out) {
+  __shared__ uint16_t tile[64][65];
+  const int64_t col_tiles = (cols + 63) / 64;  // one-dimensional grid: row tile x col tile
+  const int64_t r0 = (int64_t)blockIdx.x / col_tiles * 64, c0 = (int64_t)blockIdx.x % col_tiles * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;  // 64 x 4 threads
+#pragma unroll
+  for (int i = 0; i < 64; i += 4) {
+    const int64_t r = r0 + ty + i, c = c0 + tx;
+    if (r < rows && c < cols) tile[ty + i][tx] = in[r * cols + c];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 64; i += 4) {
+    const int64_t c = c0 + ty + i, r = r0 + tx;  // output row c, column r
+    if (c < cols && r < rows) out[c * rows + r] = tile[tx][ty + i];
+  }
+}
+
+hipError_t launch_transpose_u16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out,
+                                hipStream_t stream) {
+  const int64_t blocks = ((cols + 63) / 64) * ((rows + 63) / 64);
+  if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(transpose_u16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, in, rows,
+                     cols, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_fused_grad_rows(const FusedGradRowsArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(fused_grad_rows_kernel, dim3((unsigned)a.rows), dim3(kGThreads), 0, stream,
                      a.z, a.lse, a.target, a.grad, a.grad_mean, a.grad_tokens, a.vocab, a.ld,

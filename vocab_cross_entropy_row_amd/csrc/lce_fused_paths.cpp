@@ -46,6 +46,11 @@ lce_status run_fused_bwd(const void* x, const void* weight, int64_t tokens, int6
   const size_t off_ws = cv.take(kGemmWorkspace);
   const size_t off_dz = cv.take((size_t)chunk * (size_t)ld * 2u);
   const size_t off_z = cv.take(stored ? (size_t)chunk * (size_t)ld * 4u : 0u);
+  // dW = x^T dZ as a product of two transposed operands: x^T [hidden, chunk]
+  // is written once per chunk (hipBLASLt's NT kernels for this shape, dZ read
+  // as stored, measured slower).
+  const bool dw_tt = dw && env_int("LCE_FUSED_BWD_DW_NT", 0) == 0;
+  const size_t off_xt = cv.take(dw_tt ? (size_t)chunk * (size_t)hidden * 2u : 0u);
   const size_t reserved = cv.off - Carve().off;
   const int64_t last = tokens - (tokens - 1) / chunk * chunk;
   size_t need = cv.off;
@@ -59,6 +64,7 @@ lce_status run_fused_bwd(const void* x, const void* weight, int64_t tokens, int6
   void* ws = base + off_ws;
   void* dz = base + off_dz;
   float* z = (float*)(base + off_z);
+  uint16_t* xt = (uint16_t*)(base + off_xt);
 
   if (!stored && (s = run_fused(x, weight, tokens, hidden, vocab, nullptr, false, nullptr, stream,
                                 reserved, lse)) != LCE_OK)
@@ -107,10 +113,19 @@ lce_status run_fused_bwd(const void* x, const void* weight, int64_t tokens, int6
                                  ld, 0.0f, dx + c0 * hidden, hidden, ws, kGemmWorkspace,
                                  stream)) != LCE_OK)
       return s;
-    if (dw && (s = gemm_bf16_f32(HIPBLAS_OP_N, HIPBLAS_OP_T, hidden, vocab, n, x16 + c0 * hidden,
-                                 hidden, dz, ld, c0 == 0 ? 0.0f : 1.0f, dw, hidden, ws,
-                                 kGemmWorkspace, stream)) != LCE_OK)
+    if (dw && dw_tt) {
+      // x^T[H, n] as column-major [n, H] (row-major [H, n]) read transposed,
+      // dZ row-major [n, ld] (column-major [ld, n]) read transposed.
+      e = lce::launch_transpose_u16(x16 + c0 * hidden, n, hidden, xt, stream);
+      if (e != hipSuccess) return hip_fail(e, "kernel launch");
+      if ((s = gemm_bf16_f32(HIPBLAS_OP_T, HIPBLAS_OP_T, hidden, vocab, n, xt, n, dz, ld,
+                             c0 == 0 ? 0.0f : 1.0f, dw, hidden, ws, kGemmWorkspace, stream)) != LCE_OK)
+        return s;
+    } else if (dw && (s = gemm_bf16_f32(HIPBLAS_OP_N, HIPBLAS_OP_T, hidden, vocab, n,
+                                        x16 + c0 * hidden, hidden, dz, ld, c0 == 0 ? 0.0f : 1.0f,
+                                        dw, hidden, ws, kGemmWorkspace, stream)) != LCE_OK) {
       return s;
+    }
   }
   return LCE_OK;
 }
