@@ -217,3 +217,15 @@ def test_graph_replays_match_eager():
             gr.replay()
         torch.cuda.synchronize()
         assert torch.equal(dx, ref[0]) and torch.equal(dw, ref[1]), f"replay {r}"
+
+
+def test_dw_gemm_layouts_agree():
+    """dW through transposed operands (default) and through x as stored
+    (LCE_FUSED_BWD_DW_NT=1): the same products in another GEMM kernel."""
+    xb, wb, t = _inputs(15, 600, 136, 1700)
+    a = _run(xb, wb, t, [1.0], "mean", env=_env("chunked", 1700))
+    b = _run(xb, wb, t, [1.0], "mean", env={**_env("chunked", 1700), "LCE_FUSED_BWD_DW_NT": 1})
+    assert np.array_equal(a[0], b[0])
+    _, bw = _bounds(xb, wb, t, np.full(600, 1.0 / 600))
+    _check("dW layouts", a[1], b[1], bw)
+    _check("dW vs oracle", a[1], oracle.fused_linear_xent_bwd(xb, wb, t, 1.0, "mean")[1], bw)
