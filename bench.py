@@ -67,6 +67,8 @@ def fused_flops(tokens: int, hidden: int, vocab: int) -> int:
 
 CSRC = os.path.join(ROOT, "vocab_cross_entropy_row_amd", "csrc")
 # Sources that define each workload's dominant kernel (plus the build flags).
+SPREAD_REPLAYS = 10  # graph replays timed for the median / p10 / p90 per step
+
 KERNEL_SOURCES = {
     "xent": ["xent_kernels.hip", "row_stream.h", "lce_device.h", "lce_internal.h"],
     "fused": ["fused_kernel.hip", "mfma_common.h", "lce_device.h", "lce_internal.h"],
@@ -184,9 +186,10 @@ def time_workload(w, steps: int, warmup: int, torch, lce, eager_only: bool = Fal
         del reps, outs
         torch.cuda.empty_cache()
         return {"us_per_step": us, "eager_us_per_call": eager_us, "replicas": R,
-                "graph_matches_eager": None, "wall_s": None}
+                "graph_matches_eager": None, "wall_s": None, "spread": None}
 
-    # capture exactly `steps` steps into one graph; replay once untimed, once timed
+    # capture exactly `steps` steps into one graph; replay once untimed (its outputs are
+    # checked against the eager ones), then time SPREAD_REPLAYS replays
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -201,21 +204,32 @@ def time_workload(w, steps: int, warmup: int, torch, lce, eager_only: bool = Fal
     torch.cuda.synchronize()
     ok = all(torch.equal(a, b) for a, b in zip(outs, eager_ref))
 
+    # SPREAD_REPLAYS replays, each timed alone; the reported value is the last one
+    # (exactly `steps` steps, after the others have brought the part to steady
+    # state: the first replays after a capture run a few percent slower), and
+    # the spread is over all of them.
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    with torch.cuda.stream(s):
-        t0.record(s)
-        g.replay()
-        t1.record(s)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    us = t0.elapsed_time(t1) * 1000.0 / steps
+    per = []
+    for _ in range(SPREAD_REPLAYS):
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        with torch.cuda.stream(s):
+            t0.record(s)
+            g.replay()
+            t1.record(s)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        per.append(t0.elapsed_time(t1) * 1000.0 / steps)
+    us = per[-1]
     ok = ok and all(torch.equal(a, b) for a, b in zip(outs, eager_ref))
+    per.sort()
+    q = lambda f: per[min(len(per) - 1, int(round(f * (len(per) - 1))))]
+    spread = {"replays": len(per), "median_us": round(statistics.median(per), 3),
+              "p10_us": round(q(0.1), 3), "p90_us": round(q(0.9), 3)}
     del g, reps, outs
     torch.cuda.empty_cache()
     return {"us_per_step": us, "eager_us_per_call": eager_us, "replicas": R,
-            "graph_matches_eager": bool(ok), "wall_s": wall}
+            "graph_matches_eager": bool(ok), "wall_s": wall, "spread": spread}
 
 
 def roofline_entry(w, us: float) -> dict:
@@ -726,7 +740,8 @@ def main(argv=None) -> int:
                    "reduction": head.reduction,
                    "timing": ("eager launches" if args.eager else "hip graph of K steps, replayed once"),
                    "eager_us_per_call": round(h["eager_us_per_call"], 3),
-                   "replicas": h["replicas"], "graph_matches_eager": h["graph_matches_eager"]},
+                   "replicas": h["replicas"], "graph_matches_eager": h["graph_matches_eager"],
+                   "spread": h.get("spread")},
         "roofline": {k: v for k, v in h["roofline"].items() if k in
                      ("bound", "achieved", "peak", "unit", "frac", "traffic")},
     }
@@ -734,6 +749,8 @@ def main(argv=None) -> int:
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(head)
     line["workloads"] = {n: {"us_per_step": round(r["us_per_step"], 3),
+                             "rows_per_s": round(lce_synth.WORKLOADS[n].tokens / (r["us_per_step"] * 1e-6)),
+                             "spread": r.get("spread"),
                              "eager_us_per_call": round(r["eager_us_per_call"], 3),
                              "steps": r["steps"], "replicas": r["replicas"],
                              "graph_matches_eager": r["graph_matches_eager"],
