@@ -84,7 +84,8 @@ def source_digest(kind: str) -> str:
         h.update(f.encode())
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
-    h.update(" ".join(lce_build.common_flags()).encode())
+    # the flags name the repository's include directory: hash it relative to the root
+    h.update(" ".join(lce_build.common_flags()).replace(lce_build.ROOT, "<root>").encode())
     return h.hexdigest()
 
 
