@@ -436,6 +436,29 @@ def time_jsd(torch, lce, lce_synth, steps: int, warmup: int) -> dict:
                       "roofline": {"bound": "mfma", "achieved": round(tf, 1),
                                    "peak": BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
                                    "frac": round(tf / BF16_DENSE_TFLOPS, 4)}}
+    # The page's token sweep (stored path, eager calls between events): the same heads,
+    # activations drawn N(0, 1) on the device (torch generator seeded by the token
+    # count) and rounded to bf16.
+    scaling = {}
+    for tokens in (2048, 4096, 8192):
+        xs2 = torch.randn(tokens, w.hidden, device="cuda", generator=torch.Generator(
+            device="cuda").manual_seed(tokens)).to(torch.bfloat16)
+        xt2 = torch.randn(tokens, w.hidden, device="cuda", generator=torch.Generator(
+            device="cuda").manual_seed(tokens + 1)).to(torch.bfloat16)
+        for _ in range(2):
+            lce.fused_linear_jsd(xs2, ws, xt2, wt, 0.5, "mean", out=out)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            lce.fused_linear_jsd(xs2, ws, xt2, wt, 0.5, "mean", out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1000.0 / 3
+        tf = 2 * fused_flops(tokens, w.hidden, w.vocab) / (us * 1e-6) / 1e12
+        scaling[str(tokens)] = {"us_per_call": round(us, 1), "tflops": round(tf, 1)}
+        del xs2, xt2
+    res["stored_by_tokens"] = scaling
     del xs, ws, xt, wt
     torch.cuda.empty_cache()
     return res
