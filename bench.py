@@ -565,6 +565,82 @@ def cpu_baseline(w, budget_s: float = 10.0) -> dict:
             "sample": sample}
 
 
+# ------------------------------------------------------------------ streaming-read probe
+
+PROBE_SRC = os.path.join(ROOT, "bench_probe.hip")
+PROBE_LIB = os.path.join(ROOT, "bench_probe.so")
+
+
+def build_probe() -> str:
+    """Compile bench_probe.so (gfx950) from bench_probe.hip, the measured-read-peak kernel."""
+    import subprocess
+    from vocab_cross_entropy_row_amd import build as B
+    tmp = PROBE_LIB + ".tmp"
+    subprocess.run([B.hipcc(), "-x", "hip", "-O3", "-std=c++17", "-fPIC", f"--offload-arch={B.ARCH}",
+                    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-shared",
+                    PROBE_SRC, "-o", tmp], check=True, capture_output=True)
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
+def time_stream_read(torch, head_bytes: int, head_replicas: int, steps: int) -> dict:
+    """Measured read peak: bench_probe's streaming read (16-byte nontemporal loads, nothing
+    else) over one 2 GiB buffer, and over the headline's logit bytes with as many rotating
+    replicas as the headline timing uses, each timed as a graph of `steps` reads."""
+    import ctypes
+    if not os.path.exists(PROBE_LIB):
+        raise SystemExit(f"{PROBE_LIB} is missing: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.bench_stream_read.restype = ctypes.c_int
+    lib.bench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def graph_us(bufs, k):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+
+        def call(i):
+            b = bufs[i % len(bufs)]
+            rc = lib.bench_stream_read(b.data_ptr(), b.numel(), sink.data_ptr(), s.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"bench_stream_read failed (hipError {rc})")
+        with torch.cuda.stream(s):
+            for i in range(len(bufs)):
+                call(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(k):
+                call(i)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        per = []
+        for _ in range(SPREAD_REPLAYS):
+            torch.cuda.synchronize()
+            with torch.cuda.stream(s):
+                t0.record(s)
+                g.replay()
+                t1.record(s)
+            torch.cuda.synchronize()
+            per.append(t0.elapsed_time(t1) * 1000.0 / k)
+        del g
+        return per[-1]
+
+    big = [torch.ones(1 << 31, dtype=torch.uint8, device="cuda")]
+    us_big = graph_us(big, max(5, min(steps, 20)))
+    del big
+    small = [torch.ones(head_bytes, dtype=torch.uint8, device="cuda") for _ in range(head_replicas)]
+    us_small = graph_us(small, steps)
+    del small
+    torch.cuda.empty_cache()
+    return {"kernel": "bench_probe.hip stream_read_kernel (16-byte nt buffer loads, 8 per lane "
+                      "in flight, 32 KiB contiguous per workgroup, 2048 x 256 threads)",
+            "bytes_2GiB_us": round(us_big, 2), "gbs_2GiB": round((1 << 31) / (us_big * 1e-6) / 1e9, 1),
+            "headline_bytes": head_bytes, "headline_bytes_replicas": head_replicas,
+            "headline_bytes_us": round(us_small, 3),
+            "gbs_headline_bytes": round(head_bytes / (us_small * 1e-6) / 1e9, 1)}
+
+
 # ------------------------------------------------------------------ HBM counter calibration
 
 COPY_BYTES = 1 << 30
@@ -646,7 +722,7 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--extras", default=None,
                     help="comma list of extra measurements (backward, shard, sums, jsd, "
-                         "fused_bwd); default: all of them when --workloads is all")
+                         "fused_bwd, stream_read); default: all of them when --workloads is all")
     ap.add_argument("--eager", action="store_true",
                     help="time plain launches instead of a graph replay (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -709,7 +785,7 @@ def main(argv=None) -> int:
     jsd = None
     fbwd = None
     backward = {}
-    all_extras = ("backward", "shard", "sums", "jsd", "fused_bwd")
+    all_extras = ("backward", "shard", "sums", "jsd", "fused_bwd", "stream_read")
     if args.extras is not None:
         extras = [e for e in args.extras.split(",") if e]
         unknown = [e for e in extras if e not in all_extras]
@@ -741,6 +817,15 @@ def main(argv=None) -> int:
         fbwd = time_fused_bwd(torch, lce, lce_synth, min(args.steps, 5), 2)
         print(f"[bench] fused backward: {fbwd['us_per_step']:.1f} µs "
               f"({fbwd['roofline']['achieved']} TFLOP/s over 3*2THV)", file=sys.stderr, flush=True)
+
+    probe = None
+    if "stream_read" in extras:
+        hb = head.tokens * head.vocab * (4 if head.dtype == "f32" else 2)
+        probe = time_stream_read(torch, hb, results[lce_synth.HEADLINE]["replicas"],
+                                 min(args.steps, 200))
+        print(f"[bench] streaming read: {probe['gbs_2GiB']} GB/s over 2 GiB, "
+              f"{probe['headline_bytes_us']:.2f} µs for the headline's {hb} logit bytes",
+              file=sys.stderr, flush=True)
 
     if args.copy_calibration:
         copy_calibration(torch)
@@ -791,6 +876,12 @@ def main(argv=None) -> int:
         line["fused_linear_jsd"] = jsd
     if fbwd is not None:
         line["fused_backward"] = fbwd
+    if probe is not None:
+        # the headline against the measured read peak (context beside the datasheet roofline)
+        probe["headline_frac_of_2GiB_read_peak"] = round(
+            line["roofline"]["achieved"] / probe["gbs_2GiB"], 4)
+        probe["headline_us_over_read_only_us"] = round(h["us_per_step"] / probe["headline_bytes_us"], 4)
+        line["stream_read_probe"] = probe
     print(json.dumps(line), flush=True)
     return 0
 

@@ -48,3 +48,12 @@ def test_bench_refuses_several_gpus():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_stream_read_probe_exports():
+    """bench_probe.so (the measured-read-peak kernel bench.py reports) exports its one entry."""
+    import ctypes
+    if not os.path.exists(bench.PROBE_LIB):
+        pytest.skip("bench_probe.so not built (__graft_entry__.build() builds it)")
+    lib = ctypes.CDLL(bench.PROBE_LIB)
+    assert hasattr(lib, "bench_stream_read")
