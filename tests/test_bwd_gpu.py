@@ -134,3 +134,16 @@ def test_bwd_full_size_sampled_rows(name):
     # the sampled rows' gradients: per-token scale g_i (grad / tokens for the mean)
     want = oracle.xent_bwd(z[rows], t[rows], g, "none", dtype=w.dtype)
     _check(got[rows], want, g[:, None], w.dtype, name)
+
+
+def test_bwd_row_longer_than_one_gib():
+    """Maximum row length: a 1 GiB + 12 B fp32 row, whose statistics pass and gradient pass
+    both run in slices below 1 GiB (32-bit buffer offsets); every element is checked."""
+    rows, vocab = 1, (1 << 28) + 3
+    print(f"\n[bwd] row above 1 GiB: f32 {rows}x{vocab}", flush=True)
+    z = _logits(vocab + 21, rows, vocab, "f32")
+    t = lce_synth.targets(vocab + 22, rows, vocab)
+    want = oracle.xent_bwd(z, t, np.float64(1.0), "mean", dtype="f32")
+    got = _run(z, t, "f32", "mean", np.float32(1.0))
+    _check(got, want, np.ones((rows, 1)), "f32", "row above 1 GiB")
+    torch.cuda.empty_cache()

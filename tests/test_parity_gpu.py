@@ -287,6 +287,31 @@ def test_full_size_row_workloads(name):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("dtype,rows,vocab", [("f32", 2, (1 << 28) + 3), ("bf16", 1, (1 << 29) + 5)])
+def test_rows_longer_than_one_gib(dtype, rows, vocab):
+    """Maximum row length: rows of more than 1 GiB, which no kernel addresses in one piece
+    (32-bit buffer offsets).  Whatever path is asked for, the host cuts each row into slices
+    below 1 GiB; asked for one split, it still takes two."""
+    print(f"\n[parity] rows above 1 GiB: {dtype} {rows}x{vocab}", flush=True)
+    z = rand_logits(vocab + 11, rows, vocab, dtype, std=2.0)
+    t = lce_synth.targets(vocab + 12, rows, vocab)
+    want = oracle.xent_rows(z, t, dtype=dtype)
+    wm = oracle.mean(want)
+    zd = to_dev(z)
+    del z
+    td = torch.from_numpy(t).cuda()
+    for env in ({}, {"LCE_PATH": "block"}, {"LCE_PATH": "split", "LCE_SPLITS": 1}):
+        with forced_env(**env):
+            got = lce.xent(zd, td, "none").cpu().numpy().astype(np.float64)
+            gm = lce.xent(zd, td, "mean").item()
+        err = np.max(np.abs(got - want))
+        print(f"[parity] {dtype} {rows}x{vocab} {env}: max abs err {err:.3e}", flush=True)
+        assert err <= TOK_ABS, env
+        assert abs(gm - wm) <= MEAN_REL * abs(wm), env
+    del zd
+    torch.cuda.empty_cache()
+
+
 def test_fused_full_size_workload():
     w = WORKLOADS["fused_bf16_t2048_h4096_v128256_mean"]
     print(f"\n[parity] fused workload {w.shape}", flush=True)
