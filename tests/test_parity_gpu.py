@@ -312,6 +312,33 @@ def test_rows_longer_than_one_gib(dtype, rows, vocab):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("dtype,vocab,paths", [("f32", 5, ({}, {"LCE_PATH": "wave"}, {"LCE_PATH": "block"})),
+                                               ("bf16", 9, ({},))])
+def test_many_short_rows(dtype, vocab, paths):
+    """Row count far above the workloads' at small memory: 2^22 + 7 rows of a few logits
+    each (grids of up to four million workgroups, and as many partials for the mean's last
+    workgroup)."""
+    rows = (1 << 22) + 7
+    print(f"\n[parity] many short rows: {dtype} {rows}x{vocab}", flush=True)
+    z = rand_logits(rows + vocab, rows, vocab, dtype, std=3.0)
+    t = lce_synth.targets(vocab + 40, rows, vocab)
+    want = oracle.xent_rows(z, t, dtype=dtype)
+    wm = oracle.mean(want)
+    zd = to_dev(z)
+    td = torch.from_numpy(t).cuda()
+    for env in paths:
+        with forced_env(**env):
+            got = lce.xent(zd, td, "none").cpu().numpy().astype(np.float64)
+            gm = lce.xent(zd, td, "mean").item()
+        err = np.max(np.abs(got - want))
+        print(f"[parity] {dtype} {rows}x{vocab} {env}: max abs err {err:.3e}, mean {gm:.8f} vs {wm:.8f}",
+              flush=True)
+        assert err <= TOK_ABS, env
+        assert abs(gm - wm) <= MEAN_REL * abs(wm), env
+    del zd
+    torch.cuda.empty_cache()
+
+
 def test_fused_full_size_workload():
     w = WORKLOADS["fused_bf16_t2048_h4096_v128256_mean"]
     print(f"\n[parity] fused workload {w.shape}", flush=True)

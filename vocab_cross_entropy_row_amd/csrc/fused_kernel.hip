@@ -9,8 +9,9 @@
 // kBV vocab rows x kBT tokens.  A workgroup owns one token block and a
 // contiguous segment of vocab tiles; it walks the segment tile by tile, and
 // for each tile runs the K loop over `hidden` in slabs of 64:
-//   global (16-byte loads, W and x tiles) -> registers -> LDS (double
-//   buffered, 16-byte chunks XOR-swizzled per row) -> ds_read_b128 ->
+//   global -> LDS directly (16-byte buffer loads into LDS, no registers;
+//   W slabs rotate through three stages and x slabs through two, 16-byte
+//   chunks XOR-swizzled per row) -> ds_read_b128 ->
 //   v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
 // W is the MFMA "A" operand (rows = vocab) and x the "B" operand
 // (columns = tokens), so each lane's 32x32 accumulator block holds 16 vocab

@@ -198,7 +198,9 @@ __device__ __forceinline__ void finish_mean(float block_sum, uint64_t* slots, un
   tag = (unsigned)wave_uniform((int)tag);
   const float own = __int_as_float(wave_uniform(__float_as_int(block_sum)));
   constexpr int kInFlight = 8;  // slot loads per lane in flight
-  float acc = 0.0f;
+  // Each lane adds its share (nblocks / 64 partials, millions for the largest grids)
+  // in fp64, so the sum's rounding does not grow with the number of workgroups.
+  double acc = 0.0;
   bool ok = true;
   for (unsigned base = lane; base < nblocks; base += 64u * kInFlight) {
     uint64_t v[kInFlight];
@@ -217,10 +219,10 @@ __device__ __forceinline__ void finish_mean(float block_sum, uint64_t* slots, un
       while ((unsigned)(v[j] >> 32) != tag && spins++ < kPollLimit)
         v[j] = __hip_atomic_load(&slots[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       ok = ok && (unsigned)(v[j] >> 32) == tag;
-      acc += __uint_as_float((unsigned)v[j]);
+      acc += (double)__uint_as_float((unsigned)v[j]);
     }
   }
-  const float total = wave_sum(acc);
+  const float total = wave_sum((float)acc);
   const bool all_ok = __builtin_amdgcn_ballot_w64(!ok) == 0;
   if (lane == 0) {
     out[0] = all_ok ? total / (float)tokens : __builtin_nanf("");
