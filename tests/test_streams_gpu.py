@@ -1,8 +1,10 @@
 """liblce calls on several streams and from several host threads at once.
 
 Each (device, stream) pair has its own scratch buffer, and the host side keeps its
-tables under a mutex: calls issued concurrently from different threads onto different
-streams must give the same results as the same calls made one after the other.
+tables (scratch buffers, GEMM plans and the hipBLASLt handle) under a mutex: calls issued
+concurrently from different threads onto different streams (row and fused cross-entropy,
+the fused backward with its library GEMMs, fused linear + JSD) must give the same results
+as the same calls made one after the other.
 """
 import threading
 
@@ -37,6 +39,10 @@ def _cases():
         w = to_dev(lce_synth.normal_bf16_bits(600 + k, 2, 2000 + 111 * k, 128, 0.1))
         tt = torch.from_numpy(lce_synth.targets(700 + k, x.shape[0], w.shape[0])).cuda()
         out.append(("fused", (x, w, tt)))
+        out.append(("fused_bwd", (x, w, tt)))
+        x2 = to_dev(lce_synth.normal_bf16_bits(800 + k, 0, x.shape[0], 128, 1.0))
+        w2 = to_dev(lce_synth.normal_bf16_bits(900 + k, 2, w.shape[0], 128, 0.1))
+        out.append(("jsd", (x, w, x2, w2)))
     return out
 
 
@@ -44,7 +50,15 @@ def _call(kind, args):
     if kind == "xent":
         z, t = args
         return torch.cat([lce.xent(z, t, "mean"), lce.xent(z, t, "none")])
+    if kind == "jsd":
+        x, w, x2, w2 = args
+        return torch.cat([lce.fused_linear_jsd(x, w, x2, w2, 0.3, "mean"),
+                          lce.fused_linear_jsd(x, w, x2, w2, 0.5, "none")])
     x, w, t = args
+    if kind == "fused_bwd":
+        g = torch.full((1,), 0.7, device="cuda")
+        dx, dw = lce.fused_linear_xent_bwd(x, w, t, g, "mean")
+        return torch.cat([dx.reshape(-1), dw.reshape(-1)])
     return torch.cat([lce.fused_linear_xent(x, w, t, "mean"), lce.fused_linear_xent(x, w, t, "none")])
 
 

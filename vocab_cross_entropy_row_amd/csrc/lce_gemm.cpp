@@ -70,8 +70,17 @@ lce_status gemm_bf16_f32(hipblasOperation_t ta, hipblasOperation_t tb, int64_t m
       } else {
         h = it->second;
       }
+      // On any failure below, what was created so far is released (a plan is
+      // kept only once it is complete).
+      auto drop = [&plan](lce_status r) {
+        if (plan.d) hipblasLtMatrixLayoutDestroy(plan.d);
+        if (plan.b) hipblasLtMatrixLayoutDestroy(plan.b);
+        if (plan.a) hipblasLtMatrixLayoutDestroy(plan.a);
+        if (plan.desc) hipblasLtMatmulDescDestroy(plan.desc);
+        return r;
+      };
       if ((st = hipblasLtMatmulDescCreate(&plan.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F)) != HIPBLAS_STATUS_SUCCESS)
-        return blas_fail(st, "descriptor creation");
+        return drop(blas_fail(st, "descriptor creation"));
       const int32_t opa = (int32_t)ta, opb = (int32_t)tb;
       hipblasLtMatmulDescSetAttribute(plan.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &opa, sizeof opa);
       hipblasLtMatmulDescSetAttribute(plan.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &opb, sizeof opb);
@@ -79,10 +88,10 @@ lce_status gemm_bf16_f32(hipblasOperation_t ta, hipblasOperation_t tb, int64_t m
       if ((st = hipblasLtMatrixLayoutCreate(&plan.a, HIP_R_16BF, an ? m : k, an ? k : m, lda)) != HIPBLAS_STATUS_SUCCESS ||
           (st = hipblasLtMatrixLayoutCreate(&plan.b, HIP_R_16BF, bn ? k : n, bn ? n : k, ldb)) != HIPBLAS_STATUS_SUCCESS ||
           (st = hipblasLtMatrixLayoutCreate(&plan.d, HIP_R_32F, m, n, ldd)) != HIPBLAS_STATUS_SUCCESS)
-        return blas_fail(st, "layout creation");
+        return drop(blas_fail(st, "layout creation"));
       hipblasLtMatmulPreference_t pref = nullptr;
       if ((st = hipblasLtMatmulPreferenceCreate(&pref)) != HIPBLAS_STATUS_SUCCESS)
-        return blas_fail(st, "preference creation");
+        return drop(blas_fail(st, "preference creation"));
       const uint64_t wsb = ws_bytes;
       hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsb, sizeof wsb);
       hipblasLtMatmulHeuristicResult_t res[1];
@@ -90,8 +99,8 @@ lce_status gemm_bf16_f32(hipblasOperation_t ta, hipblasOperation_t tb, int64_t m
       st = hipblasLtMatmulAlgoGetHeuristic(h, plan.desc, plan.a, plan.b, plan.d, plan.d, pref, 1, res, &found);
       hipblasLtMatmulPreferenceDestroy(pref);
       if (st != HIPBLAS_STATUS_SUCCESS || found < 1)
-        return fail(LCE_ERR_UNSUPPORTED, "hipBLASLt has no algorithm for a %lld x %lld x %lld GEMM (status %d)",
-                    (long long)m, (long long)n, (long long)k, (int)st);
+        return drop(fail(LCE_ERR_UNSUPPORTED, "hipBLASLt has no algorithm for a %lld x %lld x %lld GEMM (status %d)",
+                         (long long)m, (long long)n, (long long)k, (int)st));
       plan.algo = res[0].algo;
       plan.ws = res[0].workspaceSize;
       g_gemm_plans[key] = plan;
