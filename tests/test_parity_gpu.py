@@ -193,6 +193,39 @@ def test_running_maximum_edge_rows(path, dtype, vocab):
     assert abs(got[10]) <= TOK_ABS  # one finite logit, the target: loss 0
 
 
+@pytest.mark.parametrize("path", ["auto", "wave", "block"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("vocab", [4096, 20000])
+def test_fixed_reference_guard_boundary(path, dtype, vocab):
+    """Loss rows are first folded against each lane's first-chunk maximum, and again with
+    a tracked maximum when a lane's sum reaches 2^64 (a logit about 44.4 above that
+    reference).  Spikes of 40 to 48 above a flat row put lane sums on both sides of that
+    bound, in the first, a middle and the last chunk a lane reads; other rows hold many
+    logits 36 to 41 above the first chunk, so sums of many large terms approach it too.
+    4096-wide rows take the unrolled short loop, 20000-wide the long loop (the block
+    path takes its own loop); every row must match the oracle."""
+    heights = [40.0, 43.0, 44.0, 44.5, 45.0, 48.0]
+    positions = [1024 + 5, vocab // 2 + 3, vocab - 9]
+    rows = len(heights) * len(positions) + 4
+    z = np.round(rand_logits(21, rows, vocab, "f32") * 64) / 64
+    r = 0
+    for h in heights:
+        for pos in positions:
+            z[r, pos] += np.float32(h)
+            r += 1
+    for lift in (36.0, 38.0, 40.0, 41.0):  # every element past the first 1024, lifted
+        z[r, 1024:] += np.float32(lift)
+        r += 1
+    z = z.astype(np.float32)
+    t = lce_synth.targets(22, rows, vocab)
+    t[:len(positions)] = positions  # the spike itself is the target in a few rows
+    if dtype == "bf16":
+        z = lce_synth.f32_to_bf16_bits(z)
+    env = {} if path == "auto" else {"LCE_PATH": path}
+    with forced_env(**env):
+        check_xent(z, t, dtype, f"guard {path} {dtype} {vocab}")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_infinite_logits(dtype):
     """+inf anywhere in a row makes that row's loss NaN, and a row of -inf only is NaN,

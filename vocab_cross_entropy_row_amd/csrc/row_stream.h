@@ -155,21 +155,65 @@ __device__ __forceinline__ void fold_one_pass(Lse& st, const typename Vec<T>::ra
   st.s += sum_parts<U, U0>(part);
 }
 
+// Fixed-reference fold of chunks [U0, U): the sum of 2^(z*L - M) against the
+// state's M, which is left where it is even when a chunk holds a larger
+// logit.  The state stays exact (s is still relative to fp32(m*L)), but s is
+// no longer bounded by the element count: a logit d above the reference adds
+// e^d.  Per element this is one decode, one FMA, one exponential and one add
+// (no maximum).  Callers check the finished lane sums against kRefGuard and
+// fold the row again with the tracked fold when any sum is not below it.
+template <typename T, int U, int U0>
+__device__ __forceinline__ void fold_fixed(Lse& st, const typename Vec<T>::raw (&v)[U]) {
+  static_assert(0 <= U0 && U0 < U, "chunk range");
+  constexpr int E = Vec<T>::kElems;
+  const float M = st.m * kLog2e;
+  float part[U];
+#pragma unroll
+  for (int u = U0; u < U; ++u) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc += exp2_fast(__builtin_fmaf(Vec<T>::get_again(v[u], e), kLog2e, -M));
+    part[u] = acc;
+  }
+  st.s += sum_parts<U, U0>(part);
+}
+
+// Bound on a lane sum built by fold_fixed.  Below it, every later merge stays
+// far from fp32 overflow (64 lanes, the waves of a workgroup and any number of
+// split partials add at most a few powers of two, and rescaling only shrinks a
+// sum); a sum at or above it, or one that is inf or NaN, sends the row to the
+// tracked fold.  Only a logit about 44 above its lane's reference (the
+// maximum of the lane's first finite chunk) can reach it.
+constexpr float kRefGuard = 0x1p64f;
+
+__device__ __forceinline__ bool lane_sum_unsafe(const Lse& st) { return !(st.s < kRefGuard); }
+
+// Tag selecting the tracked (true) or fixed-reference (false) batch fold.
+template <bool B>
+struct TrackMax {
+  static constexpr bool value = B;
+};
+
 // Fold a batch of loaded chunks into the running state.  A lane that has seen
 // no finite logit yet (always so in the first batch, FIRST) takes its maximum
-// from two passes over the first chunk, then folds the rest in one pass.
-template <typename T, int U, bool FIRST = false>
+// from two passes over the first chunk, then folds the rest in one pass:
+// max-tracking (TRACK) or against that fixed reference.
+template <typename T, int U, bool FIRST = false, bool TRACK = true>
 __device__ __forceinline__ void fold_batch(Lse& st, const typename Vec<T>::raw (&v)[U]) {
   if (FIRST || st.m == kNegInf) {
     fold_two_pass<T, U, 0, 1>(st, v);
     if constexpr (U > 1) {
       if (st.m == kNegInf)
         fold_two_pass<T, U, 1, U>(st, v);  // nothing but -inf so far
-      else
+      else if constexpr (TRACK)
         fold_one_pass<T, U, 1>(st, v);
+      else
+        fold_fixed<T, U, 1>(st, v);
     }
-  } else {
+  } else if constexpr (TRACK) {
     fold_one_pass<T, U, 0>(st, v);
+  } else {
+    fold_fixed<T, U, 0>(st, v);
   }
 }
 
@@ -213,8 +257,9 @@ __device__ __forceinline__ void mask_past(typename Vec<T>::raw (&v)[U], int c, i
 // `extra()` is called once, right after the first loads are issued (also
 // for an empty range): the row's few scalar loads go there, so that their
 // latency overlaps the stream instead of adding to it.
-// The caller keeps (c1 - c0) * 16 below 2^31.
-template <typename T, int U, typename Extra>
+// TRACK selects the batch fold (fold_batch).  The caller keeps (c1 - c0) * 16
+// below 2^31.
+template <typename T, int U, bool TRACK = true, typename Extra>
 __device__ __forceinline__ void stream_chunks(Lse& st, const typename Vec<T>::raw* body, int c0,
                                               int c1, int first, int step, Extra&& extra) {
   typedef typename Vec<T>::raw raw;
@@ -235,12 +280,12 @@ __device__ __forceinline__ void stream_chunks(Lse& st, const typename Vec<T>::ra
   for (int k = 0;; k += 2) {
     load_batch<T, U>(b, rs, c + S, step);
     if (ragged && k == last) mask_past<T, U>(a, c, n, step);
-    fold_batch<T, U>(st, a);
+    fold_batch<T, U, false, TRACK>(st, a);
     if (k == last) break;
     c += S;
     load_batch<T, U>(a, rs, c + S, step);
     if (ragged && k + 1 == last) mask_past<T, U>(b, c, n, step);
-    fold_batch<T, U>(st, b);
+    fold_batch<T, U, false, TRACK>(st, b);
     if (k + 1 == last) break;
     c += S;
   }
@@ -256,7 +301,7 @@ struct ShortRange {
   bool ragged;
 };
 
-template <typename T, int U, int MAXB, int K, typename Extra>
+template <typename T, int U, int MAXB, int K, bool TRACK, typename Extra>
 __device__ __forceinline__ void short_step(Lse& st, typename Vec<T>::raw (&cur)[U],
                                            typename Vec<T>::raw (&nxt)[U], const ShortRange& r,
                                            Extra& extra) {
@@ -267,13 +312,13 @@ __device__ __forceinline__ void short_step(Lse& st, typename Vec<T>::raw (&cur)[
     extra();
   }
   if (r.ragged && K == r.last) mask_past<T, U>(cur, c, r.n, r.step);
-  fold_batch<T, U, K == 0>(st, cur);
+  fold_batch<T, U, K == 0, TRACK>(st, cur);
   if constexpr (K + 1 < MAXB) {
-    if (K != r.last) short_step<T, U, MAXB, K + 1>(st, nxt, cur, r, extra);
+    if (K != r.last) short_step<T, U, MAXB, K + 1, TRACK>(st, nxt, cur, r, extra);
   }
 }
 
-template <typename T, int U, int MAXB, typename Extra>
+template <typename T, int U, int MAXB, bool TRACK = true, typename Extra>
 __device__ __forceinline__ void stream_chunks_short(Lse& st, const typename Vec<T>::raw* body,
                                                     int c0, int c1, int first, int step,
                                                     Extra&& extra) {
@@ -288,7 +333,7 @@ __device__ __forceinline__ void stream_chunks_short(Lse& st, const typename Vec<
                      wave_uniform((n - 1) / S), (n % S) != 0};
   raw a[U], b[U];
   load_batch<T, U>(a, r.rs, first, step);
-  short_step<T, U, MAXB, 0>(st, a, b, r, extra);
+  short_step<T, U, MAXB, 0, TRACK>(st, a, b, r, extra);
 }
 
 // Index of the scalar head or tail element that lane `idx` folds when

@@ -64,10 +64,25 @@ __global__ __launch_bounds__(64 * WAVES) void xent_wave_rows_kernel(
       zt = Vec<T>::scalar(rp + safe_target(tt, vocab));
     };
     Lse st = lse_empty();
-    if (wave_uniform(rs.nvec) <= 64 * 32)  // at most 32 chunks per lane
-      stream_chunks_short<T, U, 32 / U>(st, body, 0, rs.nvec, lane, 64, extra);
-    else
-      stream_chunks<T, U>(st, body, 0, rs.nvec, lane, 64, extra);
+    auto stream = [&](auto track, auto&& ex) {
+      constexpr bool kTrack = decltype(track)::value;
+      if (wave_uniform(rs.nvec) <= 64 * 32)  // at most 32 chunks per lane
+        stream_chunks_short<T, U, 32 / U, kTrack>(st, body, 0, rs.nvec, lane, 64, ex);
+      else
+        stream_chunks<T, U, kTrack>(st, body, 0, rs.nvec, lane, 64, ex);
+    };
+    // Shard statistics report the exact maximum, so they take the tracked
+    // fold.  Losses take the fixed-reference fold, and the whole row again
+    // through the tracked one if any lane's sum is not safely bounded.
+    if (stats) {
+      stream(TrackMax<true>{}, extra);
+    } else {
+      stream(TrackMax<false>{}, extra);
+      if (__builtin_amdgcn_ballot_w64(lane_sum_unsafe(st))) {
+        st = lse_empty();
+        stream(TrackMax<true>{}, [] {});
+      }
+    }
     if (lane < rs.head + rs.tail) fold_one(st, edge);
     const Lse r = wave_lse(st);
     if (stats) {
@@ -107,7 +122,17 @@ __global__ __launch_bounds__(kRowThreads) void xent_block_rows_kernel(
     zt = Vec<T>::scalar(rp + safe_target(tt, vocab));
   };
   Lse st = lse_empty();
-  stream_chunks<T, U>(st, body, 0, rs.nvec, threadIdx.x, kRowThreads, extra);
+  // As in the wave kernel: fixed-reference fold for losses, the tracked fold
+  // for shard statistics and for rows where any lane's sum is not bounded.
+  if (stats) {
+    stream_chunks<T, U, true>(st, body, 0, rs.nvec, threadIdx.x, kRowThreads, extra);
+  } else {
+    stream_chunks<T, U, false>(st, body, 0, rs.nvec, threadIdx.x, kRowThreads, extra);
+    if (__syncthreads_or(lane_sum_unsafe(st))) {
+      st = lse_empty();
+      stream_chunks<T, U, true>(st, body, 0, rs.nvec, threadIdx.x, kRowThreads, [] {});
+    }
+  }
   if ((int)threadIdx.x < rs.head + rs.tail) fold_one(st, edge);
   const Lse r = block_lse(st);
   if (stats) {
