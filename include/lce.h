@@ -71,17 +71,28 @@ extern "C" {
 #define LCE_VERSION_MINOR 4
 #define LCE_VERSION_PATCH 0
 
-typedef enum {
+/* The enums are passed as int.  A caller may pass any int value (a bad one is
+ * rejected with LCE_ERR_INVALID_ARG), so C++ gives them int as a fixed
+ * underlying type: every int is then a valid value of the enum type, and the
+ * library reads such an argument without undefined behaviour.  In C an enum
+ * with these constants is int-sized too, so the ABI is the same. */
+#ifdef __cplusplus
+#define LCE_ENUM enum : int
+#else
+#define LCE_ENUM enum
+#endif
+
+typedef LCE_ENUM {
     LCE_F32 = 0,  /* IEEE binary32 logits */
     LCE_BF16 = 1  /* bfloat16 logits (upper 16 bits of a binary32) */
 } lce_dtype;
 
-typedef enum {
+typedef LCE_ENUM {
     LCE_REDUCTION_MEAN = 0, /* out[0] = mean of the per-token losses */
     LCE_REDUCTION_NONE = 1  /* out[i] = loss of token i */
 } lce_reduction;
 
-typedef enum {
+typedef LCE_ENUM {
     LCE_OK = 0,
     LCE_ERR_INVALID_ARG = 1, /* NULL pointer, negative or zero size, bad enum */
     LCE_ERR_UNSUPPORTED = 2, /* valid but not handled (see each call) */

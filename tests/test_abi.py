@@ -58,7 +58,7 @@ def _xent(logits=FAKE, dtype=lce.LCE_F32, tokens=16, vocab=32, target=FAKE + (1 
     return lce.lce_xent_fwd(logits, dtype, tokens, vocab, target, reduction, out, 0)
 
 
-@pytest.mark.parametrize("kw,status,needle", [
+XENT_CASES = [
     (dict(logits=0), lce.LCE_ERR_INVALID_ARG, "logits is NULL"),
     (dict(target=0), lce.LCE_ERR_INVALID_ARG, "target is NULL"),
     (dict(out=0), lce.LCE_ERR_INVALID_ARG, "out is NULL"),
@@ -75,7 +75,10 @@ def _xent(logits=FAKE, dtype=lce.LCE_F32, tokens=16, vocab=32, target=FAKE + (1 
     (dict(out=FAKE + 64), lce.LCE_ERR_ALIAS, "logits"),
     (dict(out=FAKE + (1 << 20) + 8), lce.LCE_ERR_ALIAS, "target"),
     (dict(tokens=1 << 31, vocab=1 << 30, dtype=lce.LCE_F32), lce.LCE_ERR_INVALID_ARG, "overflow"),
-])
+]
+
+
+@pytest.mark.parametrize("kw,status,needle", XENT_CASES)
 def test_xent_argument_errors(lib, kw, status, needle):
     assert _xent(**kw) == status
     assert needle in lce.lce_last_error()
@@ -97,7 +100,7 @@ def _fused(x=FAKE, w=FAKE + (1 << 24), tokens=8, hidden=64, vocab=100, target=FA
     return lce.lce_fused_linear_xent_fwd(x, w, tokens, hidden, vocab, target, reduction, out, 0)
 
 
-@pytest.mark.parametrize("kw,status,needle", [
+FUSED_CASES = [
     (dict(x=0), lce.LCE_ERR_INVALID_ARG, "x is NULL"),
     (dict(w=0), lce.LCE_ERR_INVALID_ARG, "weight is NULL"),
     (dict(target=0), lce.LCE_ERR_INVALID_ARG, "target is NULL"),
@@ -111,7 +114,10 @@ def _fused(x=FAKE, w=FAKE + (1 << 24), tokens=8, hidden=64, vocab=100, target=FA
     (dict(out=FAKE + 16), lce.LCE_ERR_ALIAS, "x"),
     (dict(out=FAKE + (1 << 24) + 16), lce.LCE_ERR_ALIAS, "weight"),
     (dict(out=FAKE + (1 << 28)), lce.LCE_ERR_ALIAS, "target"),
-])
+]
+
+
+@pytest.mark.parametrize("kw,status,needle", FUSED_CASES)
 def test_fused_argument_errors(lib, kw, status, needle):
     assert _fused(**kw) == status
     assert needle in lce.lce_last_error()
@@ -132,7 +138,7 @@ def _partial(logits=FAKE, dtype=lce.LCE_F32, tokens=16, shard=32, start=64, targ
     return lce.lce_xent_partial_fwd(logits, dtype, tokens, shard, start, target, partial, 0)
 
 
-@pytest.mark.parametrize("kw,status,needle", [
+PARTIAL_CASES = [
     (dict(logits=0), lce.LCE_ERR_INVALID_ARG, "logits is NULL"),
     (dict(target=0), lce.LCE_ERR_INVALID_ARG, "target is NULL"),
     (dict(partial=0), lce.LCE_ERR_INVALID_ARG, "partial is NULL"),
@@ -145,7 +151,10 @@ def _partial(logits=FAKE, dtype=lce.LCE_F32, tokens=16, shard=32, start=64, targ
     (dict(partial=FAKE + 256), lce.LCE_ERR_ALIAS, "partial overlaps logits"),
     # 16 tokens x 12 bytes reach past the first 64 bytes of partial: overlaps the target
     (dict(partial=FAKE + (1 << 20) - 100), lce.LCE_ERR_ALIAS, "partial overlaps target"),
-])
+]
+
+
+@pytest.mark.parametrize("kw,status,needle", PARTIAL_CASES)
 def test_partial_argument_errors(lib, kw, status, needle):
     assert _partial(**kw) == status
     assert needle in lce.lce_last_error()
@@ -156,7 +165,7 @@ def _merge(partials=FAKE, shards=4, tokens=16, target=FAKE + (1 << 20), vocab=10
     return lce.lce_xent_merge(partials, shards, tokens, target, vocab, reduction, out, 0)
 
 
-@pytest.mark.parametrize("kw,status,needle", [
+MERGE_CASES = [
     (dict(partials=0), lce.LCE_ERR_INVALID_ARG, "partials is NULL"),
     (dict(target=0), lce.LCE_ERR_INVALID_ARG, "target is NULL"),
     (dict(out=0), lce.LCE_ERR_INVALID_ARG, "out is NULL"),
@@ -167,7 +176,10 @@ def _merge(partials=FAKE, shards=4, tokens=16, target=FAKE + (1 << 20), vocab=10
     (dict(partials=FAKE + 2), lce.LCE_ERR_INVALID_ARG, "aligned"),
     (dict(out=FAKE + 4 * 16 * 12 - 4), lce.LCE_ERR_ALIAS, "partials"),
     (dict(out=FAKE + (1 << 20)), lce.LCE_ERR_ALIAS, "target"),
-])
+]
+
+
+@pytest.mark.parametrize("kw,status,needle", MERGE_CASES)
 def test_merge_argument_errors(lib, kw, status, needle):
     assert _merge(**kw) == status
     assert needle in lce.lce_last_error()
@@ -183,7 +195,7 @@ def _bwd(logits=FAKE, dtype=lce.LCE_F32, tokens=16, vocab=32, target=FAKE + (1 <
     return lce.lce_xent_bwd(logits, dtype, tokens, vocab, target, reduction, grad, dlogits, 0)
 
 
-@pytest.mark.parametrize("kw,status,needle", [
+BWD_CASES = [
     (dict(logits=0), lce.LCE_ERR_INVALID_ARG, "logits is NULL"),
     (dict(target=0), lce.LCE_ERR_INVALID_ARG, "target is NULL"),
     (dict(grad=0), lce.LCE_ERR_INVALID_ARG, "grad is NULL"),
@@ -195,7 +207,10 @@ def _bwd(logits=FAKE, dtype=lce.LCE_F32, tokens=16, vocab=32, target=FAKE + (1 <
     (dict(dlogits=FAKE + 64), lce.LCE_ERR_ALIAS, "same buffer"),
     (dict(dlogits=FAKE + (1 << 20) - 256), lce.LCE_ERR_ALIAS, "target"),
     (dict(dlogits=FAKE + (2 << 20) - 256), lce.LCE_ERR_ALIAS, "grad"),
-])
+]
+
+
+@pytest.mark.parametrize("kw,status,needle", BWD_CASES)
 def test_bwd_argument_errors(lib, kw, status, needle):
     assert _bwd(**kw) == status
     assert needle in lce.lce_last_error()
@@ -210,7 +225,7 @@ def _sums(x=FAKE, w=FAKE + (1 << 24), batch=2, seq=4, hidden=64, vocab=100, targ
     return lce.lce_fused_linear_logprob_sums(x, w, batch, seq, hidden, vocab, target, out, 0)
 
 
-@pytest.mark.parametrize("kw,status,needle", [
+SUMS_CASES = [
     (dict(out=0), lce.LCE_ERR_INVALID_ARG, "out is NULL"),
     (dict(x=0), lce.LCE_ERR_INVALID_ARG, "x is NULL"),
     (dict(batch=-1), lce.LCE_ERR_INVALID_ARG, "batch"),
@@ -218,7 +233,10 @@ def _sums(x=FAKE, w=FAKE + (1 << 24), batch=2, seq=4, hidden=64, vocab=100, targ
     (dict(batch=1 << 40, seq=1 << 40), lce.LCE_ERR_INVALID_ARG, "overflows"),
     (dict(hidden=12), lce.LCE_ERR_UNSUPPORTED, "multiple of 8"),
     (dict(out=FAKE + (1 << 28) + 8), lce.LCE_ERR_ALIAS, "target"),
-])
+]
+
+
+@pytest.mark.parametrize("kw,status,needle", SUMS_CASES)
 def test_logprob_sums_argument_errors(lib, kw, status, needle):
     assert _sums(**kw) == status
     assert needle in lce.lce_last_error()
@@ -230,7 +248,7 @@ def _jsd(xs=FAKE, ws=FAKE + (1 << 24), xt=FAKE + (2 << 24), wt=FAKE + (3 << 24),
                                         out, 0)
 
 
-@pytest.mark.parametrize("kw,status,needle", [
+JSD_CASES = [
     (dict(out=0), lce.LCE_ERR_INVALID_ARG, "out is NULL"),
     (dict(xs=0), lce.LCE_ERR_INVALID_ARG, "student_x is NULL"),
     (dict(ws=0), lce.LCE_ERR_INVALID_ARG, "student_weight is NULL"),
@@ -248,7 +266,10 @@ def _jsd(xs=FAKE, ws=FAKE + (1 << 24), xt=FAKE + (2 << 24), wt=FAKE + (3 << 24),
     (dict(reduction=2), lce.LCE_ERR_INVALID_ARG, "reduction"),
     (dict(out=FAKE + 16), lce.LCE_ERR_ALIAS, "student_x"),
     (dict(out=FAKE + (3 << 24) + 64), lce.LCE_ERR_ALIAS, "teacher_weight"),
-])
+]
+
+
+@pytest.mark.parametrize("kw,status,needle", JSD_CASES)
 def test_jsd_argument_errors(lib, kw, status, needle):
     assert _jsd(**kw) == status
     assert needle in lce.lce_last_error()
@@ -266,7 +287,7 @@ def _fbwd(x=FAKE, w=FAKE + (1 << 24), tokens=8, hidden=64, vocab=100, target=FAK
                                          dw, 0)
 
 
-@pytest.mark.parametrize("kw,status,needle", [
+FBWD_CASES = [
     (dict(x=0), lce.LCE_ERR_INVALID_ARG, "x is NULL"),
     (dict(w=0), lce.LCE_ERR_INVALID_ARG, "weight is NULL"),
     (dict(target=0), lce.LCE_ERR_INVALID_ARG, "target is NULL"),
@@ -282,7 +303,10 @@ def _fbwd(x=FAKE, w=FAKE + (1 << 24), tokens=8, hidden=64, vocab=100, target=FAK
     (dict(dx=FAKE + (1 << 28)), lce.LCE_ERR_ALIAS, "dx overlaps target"),
     (dict(dw=FAKE + (1 << 29)), lce.LCE_ERR_ALIAS, "dweight overlaps grad"),
     (dict(dw=FAKE + (1 << 30) + 1024), lce.LCE_ERR_ALIAS, "dx overlaps dweight"),
-])
+]
+
+
+@pytest.mark.parametrize("kw,status,needle", FBWD_CASES)
 def test_fused_bwd_argument_errors(lib, kw, status, needle):
     assert _fbwd(**kw) == status
     assert needle in lce.lce_last_error()

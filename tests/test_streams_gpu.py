@@ -88,3 +88,57 @@ def test_concurrent_threads_and_streams_match_sequential():
     assert not errors, errors
     for i, (r, g) in enumerate(zip(ref, got)):
         assert torch.equal(r, g), f"case {i} ({cases[i][0]})"
+
+
+
+_OOM_SCRIPT = r"""
+import json, os, sys
+sys.path.insert(0, sys.argv[1])
+import numpy as np, torch
+import lce_synth, oracle
+import vocab_cross_entropy_row_amd as lce
+rows, vocab = 64, 1000
+f = lce_synth.normal_f32(31, 0, rows, vocab, 1.0)
+tn = lce_synth.targets(32, rows, vocab)
+z = torch.from_numpy(f).cuda()
+t = torch.from_numpy(tn).cuda()
+out = torch.full((1,), 123.0, device="cuda")
+s = torch.cuda.current_stream().cuda_stream
+torch.cuda.synchronize()
+os.environ["LCE_TEST_FAIL_ALLOC"] = "1"
+st1 = lce.lce_xent_fwd(z.data_ptr(), lce.LCE_F32, rows, vocab, t.data_ptr(),
+                       lce.LCE_REDUCTION_MEAN, out.data_ptr(), s)
+msg = lce.lce_last_error()
+torch.cuda.synchronize()
+canary = out.item()
+del os.environ["LCE_TEST_FAIL_ALLOC"]
+st2 = lce.lce_xent_fwd(z.data_ptr(), lce.LCE_F32, rows, vocab, t.data_ptr(),
+                       lce.LCE_REDUCTION_MEAN, out.data_ptr(), s)
+torch.cuda.synchronize()
+want = oracle.mean(oracle.xent_rows(f, tn, dtype="f32"))
+print(json.dumps({"st1": st1, "msg": msg, "canary": canary, "st2": st2,
+                  "got": out.item(), "want": want}))
+"""
+
+
+def test_refused_scratch_allocation_reports_oom():
+    """Scratch is kept per (device, stream) and grows on first use.  When that growth is
+    refused (the LCE_TEST_FAIL_ALLOC hook, standing in for a failed hipMalloc) the call
+    returns LCE_ERR_OOM with a message and enqueues nothing (the output keeps its canary);
+    the same call succeeds once allocation is allowed again.  Runs in a child process,
+    where liblce has no scratch yet on any stream."""
+    import json
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = {k: v for k, v in os.environ.items() if k != "LCE_TEST_FAIL_ALLOC"}
+    r = subprocess.run([sys.executable, "-c", _OOM_SCRIPT, root], capture_output=True,
+                       text=True, timeout=180, env=env)
+    assert r.returncode == 0, r.stderr[-2000:]
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    assert d["st1"] == lce.LCE_ERR_OOM, d
+    assert "LCE_TEST_FAIL_ALLOC" in d["msg"], d
+    assert d["canary"] == 123.0, d
+    assert d["st2"] == lce.LCE_OK, d
+    assert abs(d["got"] - d["want"]) <= 1e-5 * abs(d["want"]), d

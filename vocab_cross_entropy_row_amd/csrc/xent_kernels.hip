@@ -7,8 +7,11 @@
 //
 // The work is one pass over HBM: every logit is read once with 16-byte loads
 // (4 fp32 or 8 bf16 per lane per load), consecutive lanes read consecutive
-// 16-byte chunks, and each lane folds what it loaded into a running
-// (max, sum-exp) state in fp32 (see lce_device.h).  Loads are buffer loads
+// 16-byte chunks, and each lane folds what it loaded into a (max, sum-exp)
+// state in fp32 (see lce_device.h).  For losses the sum is taken against a
+// fixed per-lane reference (the maximum of the lane's first chunk) with no
+// per-element maximum; a row whose lane sums are not safely bounded is folded
+// again with a tracked maximum (row_stream.h).  Loads are buffer loads
 // issued in batches of U chunks per lane, double-buffered, so each wave keeps
 // up to 2 * U KiB in flight; the row's scalar loads (target logit, unaligned
 // edges) are issued right behind the first batch.
