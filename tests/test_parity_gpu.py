@@ -226,6 +226,48 @@ def test_fixed_reference_guard_boundary(path, dtype, vocab):
         check_xent(z, t, dtype, f"guard {path} {dtype} {vocab}")
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_randomized_rows(seed):
+    """Seeded random cases, 16 per seed, each checked against the oracle element by
+    element: 1-79 rows, vocab log-uniform in [1, 40000), fp32 or bf16, logit scales from
+    0.05 to 25, whole-matrix shifts of -3000 to +1000, spikes 5 to 120 above the rest (past
+    the fixed-reference guard or not), -inf entries around finite targets, a first row
+    0-7 elements past an aligned address, and every forced path."""
+    rng = np.random.default_rng(7100 + seed)
+    for case in range(16):
+        dtype = str(rng.choice(["f32", "bf16"]))
+        rows = int(rng.integers(1, 80))
+        vocab = max(1, int(np.exp(rng.uniform(0.0, np.log(40000.0)))))
+        std = float(rng.choice([0.05, 1.0, 4.0, 25.0]))
+        z = rng.standard_normal((rows, vocab), dtype=np.float32) * np.float32(std)
+        z += np.float32(rng.choice([0.0, 0.0, 1000.0, -3000.0]))
+        t = rng.integers(0, vocab, rows)
+        if rng.random() < 0.5:
+            for r in rng.integers(0, rows, 1 + rows // 4):
+                z[r, rng.integers(0, vocab)] += np.float32(rng.uniform(5.0, 120.0))
+        if rng.random() < 0.3:
+            keep = z[np.arange(rows), t].copy()
+            z[rng.random((rows, vocab)) < 0.2] = -np.inf
+            z[np.arange(rows), t] = keep
+        host = z if dtype == "f32" else lce_synth.f32_to_bf16_bits(z)
+        off = int(rng.integers(0, 8))
+        buf = np.zeros(off + rows * vocab, dtype=host.dtype)
+        buf[off:] = host.reshape(-1)
+        zd = to_dev(buf)[off:].view(rows, vocab)
+        td = torch.from_numpy(t.astype(np.int64)).cuda()
+        path = str(rng.choice(["auto", "wave", "block", "split"]))
+        label = f"seed {seed} case {case}: {dtype} {rows}x{vocab} std {std} offset {off} {path}"
+        want = oracle.xent_rows(host, t, dtype=dtype)
+        env = {} if path == "auto" else {"LCE_PATH": path}
+        with forced_env(**env):
+            got = lce.xent(zd, td, "none").cpu().numpy().astype(np.float64)
+            gm = lce.xent(zd, td, "mean").item()
+        assert np.array_equal(np.isnan(got), np.isnan(want)), label
+        assert np.nanmax(np.abs(got - want), initial=0.0) <= TOK_ABS, label
+        wm = oracle.mean(want)
+        assert abs(gm - wm) <= MEAN_REL * abs(wm) + MEAN_ABS_FLOOR, f"{label}: mean {gm} vs {wm}"
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_infinite_logits(dtype):
     """+inf anywhere in a row makes that row's loss NaN, and a row of -inf only is NaN,
