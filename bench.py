@@ -69,9 +69,9 @@ CSRC = os.path.join(ROOT, "vocab_cross_entropy_row_amd", "csrc")
 # Sources that define each workload's dominant kernel (plus the build flags).
 SPREAD_REPLAYS = 10  # graph replays timed for the median / p10 / p90 per step
 
-KERNEL_SOURCES = {
-    "xent": ["xent_kernels.hip", "row_stream.h", "lce_device.h", "lce_internal.h"],
-    "fused": ["fused_kernel.hip", "mfma_common.h", "lce_device.h", "lce_internal.h"],
+KERNEL_SOURCES = {  # kernel sources, and lce_api.cpp, which picks the instantiation and launch shape
+    "xent": ["xent_kernels.hip", "row_stream.h", "lce_device.h", "lce_internal.h", "lce_api.cpp"],
+    "fused": ["fused_kernel.hip", "mfma_common.h", "lce_device.h", "lce_internal.h", "lce_api.cpp"],
 }
 
 
@@ -854,7 +854,7 @@ def main(argv=None) -> int:
         "roofline": {k: v for k, v in h["roofline"].items() if k in
                      ("bound", "achieved", "peak", "unit", "frac", "traffic")},
     }
-    line["roofline"]["kernel"] = "xent_wave_rows_kernel<bf16, 8 chunks per lane per batch, 4 waves>"
+    line["roofline"]["kernel"] = "xent_wave_rows_kernel<bf16, 4 chunks per lane per batch, 4 waves>"
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(head)
     line["workloads"] = {n: {"us_per_step": round(r["us_per_step"], 3),

@@ -46,9 +46,18 @@ lce_status run_rows(const void* logits, int dtype, int64_t tokens, int64_t vocab
   const int64_t esize = a.bf16 ? 2 : 4;
   const int64_t row_bytes = vocab * esize;
   const int64_t nvec = row_bytes / 16;
-  // Chunks per lane per batch (two batches are in flight at once).
+  // Chunks per lane per batch (two batches are in flight at once).  Rows of
+  // up to 8 chunks per lane take batches of 4 when there is a mean or the
+  // logits are bf16.  With a mean, the 16-wave workgroups end at a barrier, and
+  // at the register count of 8-chunk batches only one such workgroup fits on a
+  // CU, which then idles until its slowest row is done; with 4-chunk batches
+  // two fit (bf16 [8192, 4096] mean 16.4 -> 14.6 us, fp32 [16384, 2048] mean
+  // 26.7 -> 24.5 us).  Without a mean, bf16 rows gain a little (bf16
+  // [8192, 4096] 12.01-12.07 -> 11.94 us) and fp32 rows lose (fp32
+  // [16384, 2048] 20.83 -> 21.10 us); fp32 rows of 16 chunks per lane with a
+  // mean are slower with 4 as well (45.2 vs 44.3 us).
   const int64_t per_lane = (nvec + 63) / 64;
-  a.unroll = per_lane <= 4 ? 4 : 8;
+  a.unroll = (per_lane <= 4 || (per_lane <= 8 && (mean || a.bf16))) ? 4 : 8;
   a.waves_per_block = 4;
   if (row_bytes <= 32 * 1024) {
     a.path = lce::XentPath::WaveRows;
