@@ -454,6 +454,39 @@ def test_fused_small(tokens, hidden, vocab):
     assert abs(mean - wm) <= FUSED_MEAN_REL * abs(wm) + MEAN_ABS_FLOOR  # floor: vocab = 1
 
 
+@pytest.mark.parametrize("seed", range(3))
+def test_fused_randomized(seed):
+    """Seeded random fused cases, 8 per seed, each against the oracle token by token:
+    1-599 tokens, hidden a multiple of 8 in [8, 1024], vocab log-uniform in [1, 6000),
+    activations N(0, 1) and a head scaled to logit spreads from ~0.3 to ~12, targets
+    anywhere (also the first and last vocab rows), and the vocab split into the default or
+    a forced number of segments (1-9)."""
+    rng = np.random.default_rng(8200 + seed)
+    for case in range(8):
+        tokens = int(rng.integers(1, 600))
+        hidden = 8 * int(rng.integers(1, 129))
+        vocab = max(1, int(np.exp(rng.uniform(0.0, np.log(6000.0)))))
+        spread = float(rng.choice([0.3, 1.0, 3.0, 12.0]))
+        xb = lce_synth.normal_bf16_bits(9000 + 97 * seed + case, 0, tokens, hidden, 1.0)
+        wb = lce_synth.normal_bf16_bits(9500 + 97 * seed + case, 2, vocab, hidden,
+                                        spread / math.sqrt(hidden))
+        tg = rng.integers(0, vocab, tokens)
+        tg[rng.random(tokens) < 0.1] = vocab - 1
+        tg[rng.random(tokens) < 0.1] = 0
+        segments = int(rng.choice([0, 1, 2, 3, 9]))
+        label = f"seed {seed} case {case}: T {tokens} H {hidden} V {vocab} spread {spread} segments {segments}"
+        x, W, t = to_dev(xb), to_dev(wb), torch.from_numpy(tg.astype(np.int64)).cuda()
+        want = oracle.fused_linear_xent_rows(xb, wb, tg)
+        env = {"LCE_FUSED_SEGMENTS": segments} if segments else {}
+        with forced_env(**env):
+            per = lce.fused_linear_xent(x, W, t, "none").cpu().numpy().astype(np.float64)
+            mean = lce.fused_linear_xent(x, W, t, "mean").item()
+        err = np.abs(per - want)
+        assert err.max() <= FUSED_TOK_ABS, f"{label}: max abs err {err.max()}"
+        wm = oracle.mean(want)
+        assert abs(mean - wm) <= FUSED_MEAN_REL * abs(wm) + MEAN_ABS_FLOOR, f"{label}: {mean} vs {wm}"
+
+
 @pytest.mark.parametrize("segments", [1, 2, 3, 5])
 def test_fused_segment_counts(segments):
     tokens, hidden, vocab = 300, 128, 3000
