@@ -551,9 +551,10 @@ def test_mean_handoff_many_workgroups(path):
     assert abs(means[0].item() - ref) <= 1e-6 * abs(ref)
 
 
-@pytest.mark.parametrize("unroll,waves", [(4, 4), (8, 4), (16, 4), (4, 16), (8, 16)])
+@pytest.mark.parametrize("unroll,waves", [(1, 4), (2, 4), (4, 4), (8, 4), (16, 4), (1, 16), (2, 16),
+                                          (4, 16), (8, 16)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("rows,vocab", [(37, 1000), (70, 4099), (9, 30001)])
+@pytest.mark.parametrize("rows,vocab", [(13, 100), (40, 517), (37, 1000), (70, 4099), (9, 30001)])
 def test_wave_kernel_shapes(unroll, waves, dtype, rows, vocab):
     """Every instantiated one-wave-per-row kernel shape (chunks per lane per batch,
     waves per workgroup) on ragged row counts and unaligned rows."""

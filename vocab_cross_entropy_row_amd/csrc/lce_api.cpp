@@ -55,9 +55,13 @@ lce_status run_rows(const void* logits, int dtype, int64_t tokens, int64_t vocab
   // 26.7 -> 24.5 us).  Without a mean, bf16 rows gain a little (bf16
   // [8192, 4096] 12.01-12.07 -> 11.94 us) and fp32 rows lose (fp32
   // [16384, 2048] 20.83 -> 21.10 us); fp32 rows of 16 chunks per lane with a
-  // mean are slower with 4 as well (45.2 vs 44.3 us).
+  // mean are slower with 4 as well (45.2 vs 44.3 us).  Rows of one or two
+  // chunks per lane take batches of exactly that size: larger batches would be
+  // mostly loads past the row (bf16 [65536, 512] 30.8 -> 18.6 us per token,
+  // 46.3 -> 34.2 us with a mean; fp32 [65536, 256] 23.2 -> 16.9 us).
   const int64_t per_lane = (nvec + 63) / 64;
   a.unroll = (per_lane <= 4 || (per_lane <= 8 && (mean || a.bf16))) ? 4 : 8;
+  if (per_lane <= 2) a.unroll = per_lane < 1 ? 1 : (int)per_lane;
   a.waves_per_block = 4;
   if (row_bytes <= 32 * 1024) {
     a.path = lce::XentPath::WaveRows;
@@ -78,7 +82,9 @@ lce_status run_rows(const void* logits, int dtype, int64_t tokens, int64_t vocab
   else if (forced && !strcmp(forced, "block")) a.path = lce::XentPath::BlockRows;
   else if (forced && !strcmp(forced, "split")) a.path = lce::XentPath::Split;
   const int forced_unroll = env_int("LCE_UNROLL", 0);
-  if (forced_unroll == 4 || forced_unroll == 8 || forced_unroll == 16) a.unroll = forced_unroll;
+  if (forced_unroll == 1 || forced_unroll == 2 || forced_unroll == 4 || forced_unroll == 8 ||
+      forced_unroll == 16)
+    a.unroll = forced_unroll;
   const int forced_waves = env_int("LCE_WAVES_PER_BLOCK", 0);
   if (forced_waves == 4 || forced_waves == 16) a.waves_per_block = forced_waves;
   if (a.waves_per_block == 16 && a.unroll > 8) a.unroll = 8;

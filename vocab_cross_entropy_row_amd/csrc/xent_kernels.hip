@@ -67,10 +67,13 @@ __global__ __launch_bounds__(64 * WAVES) void xent_wave_rows_kernel(
       zt = Vec<T>::scalar(rp + safe_target(tt, vocab));
     };
     Lse st = lse_empty();
+    // Rows of at most kMaxB batches take the unrolled loop: 32 chunks per lane
+    // for batches of 4 or more, two batches for batches of 1 or 2.
+    constexpr int kMaxB = U >= 4 ? 32 / U : 2;
     auto stream = [&](auto track, auto&& ex) {
       constexpr bool kTrack = decltype(track)::value;
-      if (wave_uniform(rs.nvec) <= 64 * 32)  // at most 32 chunks per lane
-        stream_chunks_short<T, U, 32 / U, kTrack>(st, body, 0, rs.nvec, lane, 64, ex);
+      if (wave_uniform(rs.nvec) <= 64 * U * kMaxB)
+        stream_chunks_short<T, U, kMaxB, kTrack>(st, body, 0, rs.nvec, lane, 64, ex);
       else
         stream_chunks<T, U, kTrack>(st, body, 0, rs.nvec, lane, 64, ex);
     };
@@ -298,8 +301,9 @@ static hipError_t launch_wave_rows_w(const XentArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Instantiated shapes: U in {4, 8, 16} with 4 waves; U in {4, 8} with 16 waves
-// (16 waves with U = 16 would need more registers than 1024 threads can have).
+// Instantiated shapes: U in {1, 2, 4, 8, 16} with 4 waves; U in {1, 2, 4, 8} with
+// 16 waves (16 waves with U = 16 would need more registers than 1024 threads can
+// have).
 template <typename T, int U>
 static hipError_t launch_wave_rows(const XentArgs& a, hipStream_t st) {
   if (a.waves_per_block == 16) return launch_wave_rows_w<T, (U > 8 ? 8 : U), 16>(a, st);
@@ -334,6 +338,8 @@ static hipError_t launch_xent_t(const XentArgs& a, hipStream_t st) {
   switch (a.path) {
     case XentPath::WaveRows:
       switch (a.unroll) {
+        case 1: return launch_wave_rows<T, 1>(a, st);
+        case 2: return launch_wave_rows<T, 2>(a, st);
         case 4: return launch_wave_rows<T, 4>(a, st);
         case 8: return launch_wave_rows<T, 8>(a, st);
         default: return launch_wave_rows<T, 16>(a, st);
