@@ -482,8 +482,10 @@ __global__ __launch_bounds__(TL::kThreads) void fused_xent_partial_kernel(
 
 // One thread per token: merge its `segments` partials in segment order
 // (consecutive threads read consecutive tokens of a segment), subtract z_target.
-// The partials are loaded eight segments at a time, so the loads of a group
-// are in flight together instead of one memory latency per segment.
+// The partials are loaded 32 segments at a time (the default segment count
+// of the benchmark shapes), so the loads of a group are in flight together
+// instead of one memory latency per segment or per group of eight; padding
+// entries past `segments` merge as exact no-ops.
 __global__ __launch_bounds__(kRowThreads) void fused_xent_merge_kernel(
     int64_t tokens, int64_t vocab, int segments, const float2* __restrict__ part,
     const float* __restrict__ zt, const int64_t* __restrict__ target, float* __restrict__ out,
@@ -494,7 +496,7 @@ __global__ __launch_bounds__(kRowThreads) void fused_xent_merge_kernel(
   if (row < tokens) {
     const int64_t t = lse_out ? -1 : target[row];
     const float z = lse_out ? 0.0f : zt[row];
-    constexpr int kGroup = 8;
+    constexpr int kGroup = 32;
     Lse st = lse_empty();
     for (int s0 = 0; s0 < segments; s0 += kGroup) {
       float2 p[kGroup];
