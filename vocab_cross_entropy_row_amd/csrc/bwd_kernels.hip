@@ -246,6 +246,8 @@ template <typename T>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   if (a.wave_chunks > 0) {
     switch (a.wave_chunks) {
+      case 1: return launch_bwd_wave_t<T, 1>(a, st);
+      case 2: return launch_bwd_wave_t<T, 2>(a, st);
       case 4: return launch_bwd_wave_t<T, 4>(a, st);
       case 8: return launch_bwd_wave_t<T, 8>(a, st);
       case 16: return launch_bwd_wave_t<T, 16>(a, st);
