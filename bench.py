@@ -3,20 +3,25 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads all|headline|NAME,...]
 
 A step is one forward call of the hot path on one batch of synthetic input already
-resident in HBM.  The headline workload is bf16 logits [seq 2048, batch 4, vocab 4096]
-with per-token fp32 losses (the Megatron-layout cross-entropy of the pages).  Inputs are
-replicated so that the replicas together exceed the 256 MB Infinity Cache, and step i
-reads replica i mod R: every step streams its logits from HBM.
+resident in HBM.  The headline workload is the largest configuration that fits one GPU:
+fp32 logits [16384, 131072] (8.6 GB) with the mean loss.  Inputs are replicated so that
+the replicas together exceed the 256 MB Infinity Cache, and step i reads replica i mod R:
+every step streams its logits from HBM.
 
-Timing: W eager warmup steps, then the K timed steps are captured into one HIP graph
-(liblce launches on torch's current stream; nothing in the call allocates or memsets once
-warm) and replayed once between two events on that stream, bracketed by
-torch.cuda.synchronize().  The graph removes host launch overhead, which is longer than
-the kernel itself at this size; the eager per-call time is reported next to it.
+Timing (graph_replays): W eager warmup steps, then the K timed steps are captured into
+one HIP graph (liblce launches on torch's current stream; nothing in the call allocates
+or memsets once warm), replayed once untimed (its outputs are checked against the eager
+ones), then replayed SPREAD_REPLAYS times, each replay timed between two events recorded
+on the capture stream, bracketed by torch.cuda.synchronize().  `value` is the median µs
+per step over those replays, with p10 and p90 beside it.  The graph removes host launch
+overhead, which is longer than the shortest kernels; the eager per-call time is reported
+next to it.
 
 Prints ONE JSON line (rank 0, N = 1).  Other workloads are measured the same way and
-reported under "workloads".  The roofline is for the dominant kernel: algorithmic bytes
-(each input and output tensor read or written once) per launch over the average launch
+reported under "workloads".  The roofline is for the dominant kernel, named from what the
+library reports it launched (lce_last_launch): algorithmic bytes (each input and output
+tensor read or written once) or flops per step over the median step time.  Every
+headline step is one launch of that kernel, so the step time is its average launch
 duration.
 """
 from __future__ import annotations
@@ -111,8 +116,24 @@ def _to_dev(arr, torch):
     return torch.from_numpy(arr).cuda()
 
 
+# Device inputs of the workloads named in KEEP are kept here after their own timing,
+# for the measurements that reuse them (split path, sweeps).
+KEEP = set()
+_KEPT = {}
+
+
 def make_inputs(w, torch, replicas: int):
     """Device replicas of a workload's inputs (generated once on the host, in row blocks)."""
+    if w.name in _KEPT:
+        base = _KEPT[w.name]
+        return [base] + [tuple(a.clone() for a in base) for _ in range(replicas - 1)]
+    reps = _make_inputs(w, torch, replicas)
+    if w.name in KEEP:
+        _KEPT[w.name] = reps[0]
+    return reps
+
+
+def _make_inputs(w, torch, replicas: int):
     if w.kind == "xent":
         tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
         z = torch.empty(w.shape, dtype=tdt, device="cuda")
@@ -146,6 +167,52 @@ def replicas_for(w) -> int:
 
 # ------------------------------------------------------------------ timing
 
+def spread_of(per) -> dict:
+    """Median, p10, p90, min, max and last of per-replay µs per step."""
+    s = sorted(per)
+    q = lambda f: s[min(len(s) - 1, int(round(f * (len(s) - 1))))]
+    return {"replays": len(per), "median_us": round(statistics.median(s), 3),
+            "p10_us": round(q(0.1), 3), "p90_us": round(q(0.9), 3), "min_us": round(s[0], 3),
+            "max_us": round(s[-1], 3), "last_us": round(per[-1], 3)}
+
+
+def graph_replays(step, steps: int, warmup: int, replays: int = None):
+    """The timing protocol of every measurement here: `warmup` eager calls step(i), then
+    `steps` calls captured into one HIP graph on a side stream (after one eager call on
+    that stream, so liblce's per-stream scratch exists before capture), one untimed
+    replay, then `replays` replays each timed between two events recorded on the capture
+    stream.  Returns the µs per step of each timed replay, in order."""
+    import torch
+    replays = SPREAD_REPLAYS if replays is None else replays
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(0)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(steps):
+            step(i)
+    g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    per = []
+    for _ in range(replays):
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            t0.record(s)
+            g.replay()
+            t1.record(s)
+        torch.cuda.synchronize()
+        per.append(t0.elapsed_time(t1) * 1000.0 / steps)
+    del g
+    return per
+
+
 def time_workload(w, steps: int, warmup: int, torch, lce, eager_only: bool = False):
     reps = make_inputs(w, torch, replicas_for(w))
     R = len(reps)
@@ -165,6 +232,8 @@ def time_workload(w, steps: int, warmup: int, torch, lce, eager_only: bool = Fal
         step(i)
     torch.cuda.synchronize()
     eager_ref = [o.clone() for o in outs]
+    step(0)
+    launch = lce.lce_last_launch()  # what the library enqueued for one step
 
     # eager per-call time (host launch overhead included)
     n_eager = min(steps, 50)
@@ -187,50 +256,17 @@ def time_workload(w, steps: int, warmup: int, torch, lce, eager_only: bool = Fal
         del reps, outs
         torch.cuda.empty_cache()
         return {"us_per_step": us, "eager_us_per_call": eager_us, "replicas": R,
-                "graph_matches_eager": None, "wall_s": None, "spread": None}
+                "graph_matches_eager": None, "spread": None, "launch": launch}
 
-    # capture exactly `steps` steps into one graph; replay once untimed (its outputs are
-    # checked against the eager ones), then time SPREAD_REPLAYS replays
-    g = torch.cuda.CUDAGraph()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        step(0)  # scratch for this stream is allocated outside the capture
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(g, stream=s):
-        for i in range(steps):
-            step(i)
-    g.replay()
-    torch.cuda.synchronize()
+    # exactly `steps` steps in one graph; after the replays, every output must equal the
+    # eager one bitwise
+    per = graph_replays(step, steps, 0)
     ok = all(torch.equal(a, b) for a, b in zip(outs, eager_ref))
-
-    # SPREAD_REPLAYS replays, each timed alone; the reported value is the last one
-    # (exactly `steps` steps, after the others have brought the part to steady
-    # state: the first replays after a capture run a few percent slower), and
-    # the spread is over all of them.
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    per = []
-    for _ in range(SPREAD_REPLAYS):
-        torch.cuda.synchronize()
-        wall0 = time.perf_counter()
-        with torch.cuda.stream(s):
-            t0.record(s)
-            g.replay()
-            t1.record(s)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - wall0
-        per.append(t0.elapsed_time(t1) * 1000.0 / steps)
-    us = per[-1]
-    ok = ok and all(torch.equal(a, b) for a, b in zip(outs, eager_ref))
-    per.sort()
-    q = lambda f: per[min(len(per) - 1, int(round(f * (len(per) - 1))))]
-    spread = {"replays": len(per), "median_us": round(statistics.median(per), 3),
-              "p10_us": round(q(0.1), 3), "p90_us": round(q(0.9), 3)}
-    del g, reps, outs
+    spread = spread_of(per)
+    del reps, outs
     torch.cuda.empty_cache()
-    return {"us_per_step": us, "eager_us_per_call": eager_us, "replicas": R,
-            "graph_matches_eager": bool(ok), "wall_s": wall, "spread": spread}
+    return {"us_per_step": spread["median_us"], "eager_us_per_call": eager_us, "replicas": R,
+            "graph_matches_eager": bool(ok), "spread": spread, "launch": launch}
 
 
 def roofline_entry(w, us: float) -> dict:
@@ -264,35 +300,17 @@ def time_backward(w, torch, lce, steps: int, warmup: int) -> dict:
         z, t = reps[i % R]
         lce.xent_bwd(z, t, grad, w.reduction, out=outs[i % R])
 
-    for i in range(max(warmup, R)):
-        step(i)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    st = torch.cuda.Stream()
-    st.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(st):
-        step(0)
-    torch.cuda.current_stream().wait_stream(st)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(g, stream=st):
-        for i in range(steps):
-            step(i)
-    g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(st):
-        e0.record(st)
-        g.replay()
-        e1.record(st)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1000.0 / steps
+    step(0)
+    launch = lce.lce_last_launch()
+    sp = spread_of(graph_replays(step, steps, max(warmup, R)))
+    us = sp["median_us"]
     esize = 4 if w.dtype == "f32" else 2
     b = tensor_bytes([(w.tokens * w.vocab, esize), (w.tokens * w.vocab, esize), (w.tokens, 8),
                       (1 if w.reduction == "mean" else w.tokens, 4)])
-    del reps, outs, g
+    del reps, outs
     torch.cuda.empty_cache()
     gbs = b / (us * 1e-6) / 1e9
-    return {"us_per_step": round(us, 3), "replicas": R,
+    return {"us_per_step": round(us, 3), "replicas": R, "spread": sp, "launch": launch,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": b}}
 
@@ -305,33 +323,14 @@ def time_logprob_sums(torch, lce, lce_synth, steps: int, warmup: int) -> dict:
     (x, W, t), = make_inputs(w, torch, 1)
     x3, t2 = x.view(batch, seq, w.hidden), t.view(batch, seq)
     out = torch.empty(batch, dtype=torch.float32, device="cuda")
-    for _ in range(max(1, warmup)):
-        lce.fused_linear_logprob_sums(x3, W, t2, out=out)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    st = torch.cuda.Stream()
-    st.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(st):
-        lce.fused_linear_logprob_sums(x3, W, t2, out=out)
-    torch.cuda.current_stream().wait_stream(st)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(g, stream=st):
-        for _ in range(steps):
-            lce.fused_linear_logprob_sums(x3, W, t2, out=out)
-    g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(st):
-        e0.record(st)
-        g.replay()
-        e1.record(st)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1000.0 / steps
+    sp = spread_of(graph_replays(lambda i: lce.fused_linear_logprob_sums(x3, W, t2, out=out), steps,
+                                 max(1, warmup), replays=5))
+    us = sp["median_us"]
     tf = fused_flops(w.tokens, w.hidden, w.vocab) / (us * 1e-6) / 1e12
-    del x, W, t, g
+    del x, W, t
     torch.cuda.empty_cache()
     return {"shape": f"batch {batch} x seq {seq}, hidden {w.hidden}, vocab {w.vocab}",
-            "us_per_step": round(us, 1),
+            "us_per_step": round(us, 1), "spread": sp,
             "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_DENSE_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / BF16_DENSE_TFLOPS, 4)}}
 
@@ -348,38 +347,22 @@ def time_fused_bwd(torch, lce, lce_synth, steps: int, warmup: int) -> dict:
     dx = torch.empty(x.shape, dtype=torch.float32, device="cuda")
     dw = torch.empty(W.shape, dtype=torch.float32, device="cuda")
 
-    def call():
+    def call(i=0):
         lce.fused_linear_xent_bwd(x, W, t, g, "mean", dx=dx, dweight=dw)
-    for _ in range(max(1, warmup)):
-        call()
+    call()
+    launch = lce.lce_last_launch()
     torch.cuda.synchronize()
     ref = (dx.clone(), dw.clone())
-    gr = torch.cuda.CUDAGraph()
-    st = torch.cuda.Stream()
-    st.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(st):
-        call()
-    torch.cuda.current_stream().wait_stream(st)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(gr, stream=st):
-        for _ in range(steps):
-            call()
-    gr.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(st):
-        e0.record(st)
-        gr.replay()
-        e1.record(st)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1000.0 / steps
+    sp = spread_of(graph_replays(call, steps, max(1, warmup), replays=5))
+    us = sp["median_us"]
     same = bool(torch.equal(dx, ref[0]) and torch.equal(dw, ref[1]))
     flops = 3 * fused_flops(w.tokens, w.hidden, w.vocab)
     tf = flops / (us * 1e-6) / 1e12
-    del x, W, t, dx, dw, ref, gr
+    del x, W, t, dx, dw, ref
     torch.cuda.empty_cache()
     return {"shape": f"tokens {w.tokens}, hidden {w.hidden}, vocab {w.vocab}, mean; dx and dW fp32",
-            "us_per_step": round(us, 1), "graph_matches_eager": same, "algorithmic_flops": flops,
+            "us_per_step": round(us, 1), "spread": sp, "launch": launch,
+            "graph_matches_eager": same, "algorithmic_flops": flops,
             "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_DENSE_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / BF16_DENSE_TFLOPS, 4)}}
 
@@ -401,30 +384,14 @@ def time_jsd(torch, lce, lce_synth, steps: int, warmup: int) -> dict:
         if env is not None:
             os.environ["LCE_JSD_STORE_BYTES"] = env
         try:
-            for _ in range(max(1, warmup)):
-                lce.fused_linear_jsd(xs, ws, xt, wt, 0.5, "mean", out=out)
+            lce.fused_linear_jsd(xs, ws, xt, wt, 0.5, "mean", out=out)
+            launch = lce.lce_last_launch()
             torch.cuda.synchronize()
             val = out.item()
-            g = torch.cuda.CUDAGraph()
-            st = torch.cuda.Stream()
-            st.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(st):
-                lce.fused_linear_jsd(xs, ws, xt, wt, 0.5, "mean", out=out)
-            torch.cuda.current_stream().wait_stream(st)
-            torch.cuda.synchronize()
-            with torch.cuda.graph(g, stream=st):
-                for _ in range(steps):
-                    lce.fused_linear_jsd(xs, ws, xt, wt, 0.5, "mean", out=out)
-            g.replay()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            with torch.cuda.stream(st):
-                e0.record(st)
-                g.replay()
-                e1.record(st)
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1000.0 / steps
-            del g
+            sp = spread_of(graph_replays(
+                lambda i: lce.fused_linear_jsd(xs, ws, xt, wt, 0.5, "mean", out=out), steps,
+                max(1, warmup), replays=5))
+            us = sp["median_us"]
         finally:
             if env is not None:
                 if old is None:
@@ -432,7 +399,8 @@ def time_jsd(torch, lce, lce_synth, steps: int, warmup: int) -> dict:
                 else:
                     os.environ["LCE_JSD_STORE_BYTES"] = old
         tf = flops / (us * 1e-6) / 1e12
-        res[label] = {"us_per_step": round(us, 1), "batchmean": val,
+        res[label] = {"us_per_step": round(us, 1), "batchmean": val, "spread": sp,
+                      "launch": launch,
                       "roofline": {"bound": "mfma", "achieved": round(tf, 1),
                                    "peak": BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
                                    "frac": round(tf / BF16_DENSE_TFLOPS, 4)}}
@@ -470,7 +438,7 @@ def time_vocab_shard(torch, lce, lce_synth, tp: int, steps: int, warmup: int) ->
     replicas that exceed the Infinity Cache), and the merge of all `tp` shards' statistics
     (lce_xent_merge, after the all-gather that one GPU cannot show).  Both are timed as HIP
     graphs of `steps` calls; the merged losses are checked against the unsplit call."""
-    w = lce_synth.WORKLOADS[lce_synth.HEADLINE]
+    w = lce_synth.WORKLOADS["megatron_bf16_2048x4x4096_none"]
     T, V = w.tokens, w.vocab
     sv = V // tp
     z = torch.empty((T, V), dtype=torch.bfloat16, device="cuda")
@@ -487,28 +455,7 @@ def time_vocab_shard(torch, lce, lce_synth, tp: int, steps: int, warmup: int) ->
     out = torch.empty(T, dtype=torch.float32, device="cuda")
 
     def graph_us(fn, k):
-        for i in range(max(warmup, R)):
-            fn(i)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        st = torch.cuda.Stream()
-        st.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(st):
-            fn(0)
-        torch.cuda.current_stream().wait_stream(st)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g, stream=st):
-            for i in range(k):
-                fn(i)
-        g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(st):
-            e0.record(st)
-            g.replay()
-            e1.record(st)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1000.0 / k
+        return spread_of(graph_replays(fn, k, max(warmup, R)))["median_us"]
 
     p_us = graph_us(lambda i: lce.xent_partial(reps[i % R], t, 0, out=part), steps)
     m_us = graph_us(lambda i: lce.xent_merge(stats, t, V, "none", out=out), steps)
@@ -528,6 +475,104 @@ def time_vocab_shard(torch, lce, lce_synth, tp: int, steps: int, warmup: int) ->
                                  "algorithmic_bytes": p_bytes, "replicas": R},
             "merge_algorithmic_bytes": m_bytes,
             "max_abs_diff_vs_unsplit": diff}
+
+
+# ------------------------------------------------------------------ split path and sweeps
+
+def _xent_point(torch, lce, z_all, t_all, rows: int, vocab: int, reduction: str, steps: int,
+                warmup: int, target_seed: int, lce_synth) -> dict:
+    """One row cross-entropy measurement on [rows, vocab] views cut from a kept workload's
+    logit buffer (seeded synthetic values; disjoint slices serve as the rotating replicas,
+    as many as fit, up to enough to exceed 4x the Infinity Cache) with targets drawn
+    uniform on [0, vocab) from their own seed."""
+    flat = z_all.reshape(-1)
+    esize = flat.element_size()
+    per = rows * vocab
+    R = 1
+    while R < 16 and R * per * esize < 4 * INFINITY_CACHE_BYTES and (R + 1) * per <= flat.numel():
+        R += 1
+    views = [flat[r * per:(r + 1) * per].view(rows, vocab) for r in range(R)]
+    t = torch.from_numpy(lce_synth.targets(target_seed, rows, vocab)).cuda()
+    outs = [torch.empty((1,) if reduction == "mean" else (rows,), dtype=torch.float32,
+                        device="cuda") for _ in range(R)]
+
+    def step(i):
+        lce.xent(views[i % R], t, reduction, out=outs[i % R])
+
+    step(0)
+    launch = lce.lce_last_launch()
+    sp = spread_of(graph_replays(step, steps, max(warmup, R)))
+    b = xent_bytes(rows, vocab, esize, reduction)
+    gbs = b / (sp["median_us"] * 1e-6) / 1e9
+    return {"tokens": rows, "vocab": vocab, "reduction": reduction, "replicas": R,
+            "us_per_step": sp["median_us"], "spread": sp, "launch": launch,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes": b}}
+
+
+def time_split(torch, lce, lce_synth, steps: int, warmup: int) -> dict:
+    """Few rows of 131072 logits, where the split-vocab path is the default (fewer rows
+    than twice the CU count): 256 rows of the fp32 [16384, 131072] workload's logits with
+    the mean, and 256 rows of the bf16 [2048, 4, 131072] workload's logits per token."""
+    res = {}
+    for name, red, tseed in (("ce_f32_16384x131072_mean", "mean", 2101),
+                             ("megatron_bf16_2048x4x131072_none", "none", 2102)):
+        z, _t = _KEPT[name]
+        w = lce_synth.WORKLOADS[name]
+        key = f"split_{w.dtype}_256x{w.vocab}_{red}"
+        res[key] = _xent_point(torch, lce, z, None, 256, w.vocab, red, steps, warmup, tseed,
+                               lce_synth)
+        print(f"[bench] {key}: {res[key]['us_per_step']:.2f} µs/step "
+              f"({res[key]['roofline']['achieved']} GB/s) via {res[key]['launch']}",
+              file=sys.stderr, flush=True)
+    return res
+
+
+SWEEP_VOCABS = (4096, 8192, 16384, 32768, 65536, 131072)
+FUSED_SWEEP_BATCHES = (2, 4, 8, 16)
+
+
+def time_sweeps(torch, lce, lce_synth, steps: int, warmup: int) -> dict:
+    """The pages' own workload axes: vocab 4096..131072 at tokens 16384 fp32 with the mean
+    ("Cross-entropy loss", Current records) and at seq 2048 x batch 4 bf16 per token
+    ("Vocab-parallel cross-entropy, Megatron layout", Current records), each cut from the
+    kept 131072-wide workload's logit buffer; and the fused projection at batch 2/4/8/16 x
+    seq 1024 ("Fused linear + CPO loss", Scaling by batch) with the fused workload's head
+    and activations drawn by its recipe (seed 1005) for the larger token counts."""
+    res = {"ce_f32_tokens16384_mean": {}, "megatron_bf16_2048x4_none": {}, "fused_by_batch": {}}
+    zf, _ = _KEPT["ce_f32_16384x131072_mean"]
+    zb, _ = _KEPT["megatron_bf16_2048x4x131072_none"]
+    for v in SWEEP_VOCABS:
+        k = min(steps, 30) if v >= 65536 else steps
+        res["ce_f32_tokens16384_mean"][str(v)] = _xent_point(
+            torch, lce, zf, None, 16384, v, "mean", k, warmup, 2200 + v % 997, lce_synth)
+        res["megatron_bf16_2048x4_none"][str(v)] = _xent_point(
+            torch, lce, zb, None, 8192, v, "none", k, warmup, 2300 + v % 991, lce_synth)
+        print(f"[bench] sweep vocab {v}: fp32 mean "
+              f"{res['ce_f32_tokens16384_mean'][str(v)]['us_per_step']:.2f} µs, bf16 none "
+              f"{res['megatron_bf16_2048x4_none'][str(v)]['us_per_step']:.2f} µs",
+              file=sys.stderr, flush=True)
+    w = lce_synth.WORKLOADS["fused_bf16_t2048_h4096_v128256_mean"]
+    x0, W, _t = _KEPT[w.name]
+    for b in FUSED_SWEEP_BATCHES:
+        T = b * 1024
+        x = x0 if T == w.tokens else _to_dev(lce_synth.normal_bf16_bits(
+            w.seed, lce_synth.STREAM_LOGITS, T, w.hidden, w.std), torch)
+        t = torch.from_numpy(lce_synth.targets(w.target_seed, T, w.vocab)).cuda()
+        out = torch.empty(1, dtype=torch.float32, device="cuda")
+        sp = spread_of(graph_replays(lambda i: lce.fused_linear_xent(x, W, t, "mean", out=out),
+                                     max(3, min(steps, 30) * 2 // b), 1, replays=5))
+        tf = fused_flops(T, w.hidden, w.vocab) / (sp["median_us"] * 1e-6) / 1e12
+        res["fused_by_batch"][str(b)] = {
+            "tokens": T, "us_per_step": sp["median_us"], "spread": sp,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_DENSE_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / BF16_DENSE_TFLOPS, 4)}}
+        print(f"[bench] sweep fused batch {b}: {sp['median_us']:.1f} µs ({tf:.1f} TFLOP/s)",
+              file=sys.stderr, flush=True)
+        del x, t
+    torch.cuda.empty_cache()
+    return res
 
 
 # ------------------------------------------------------------------ CPU baseline (oracle)
@@ -584,9 +629,11 @@ def build_probe() -> str:
 
 
 def time_stream_read(torch, head_bytes: int, head_replicas: int, steps: int) -> dict:
-    """Measured read peak: bench_probe's streaming read (16-byte nontemporal loads, nothing
-    else) over one 2 GiB buffer, and over the headline's logit bytes with as many rotating
-    replicas as the headline timing uses, each timed as a graph of `steps` reads."""
+    """A plain streaming read for comparison (not a peak: the long row kernels read faster):
+    bench_probe's kernel (16-byte nontemporal loads, nothing else) over one 2 GiB buffer,
+    and over `head_bytes` (the logit bytes of a short-row workload) with as many rotating
+    replicas as that workload's timing uses, each timed as a graph of `steps` reads
+    (median of the replays)."""
     import ctypes
     if not os.path.exists(PROBE_LIB):
         raise SystemExit(f"{PROBE_LIB} is missing: run __graft_entry__.build() first")
@@ -624,7 +671,7 @@ def time_stream_read(torch, head_bytes: int, head_replicas: int, steps: int) -> 
             torch.cuda.synchronize()
             per.append(t0.elapsed_time(t1) * 1000.0 / k)
         del g
-        return per[-1]
+        return statistics.median(per)
 
     big = [torch.ones(1 << 31, dtype=torch.uint8, device="cuda")]
     us_big = graph_us(big, max(5, min(steps, 20)))
@@ -636,9 +683,8 @@ def time_stream_read(torch, head_bytes: int, head_replicas: int, steps: int) -> 
     return {"kernel": "bench_probe.hip stream_read_kernel (16-byte nt buffer loads, 8 per lane "
                       "in flight, 32 KiB contiguous per workgroup, 2048 x 256 threads)",
             "bytes_2GiB_us": round(us_big, 2), "gbs_2GiB": round((1 << 31) / (us_big * 1e-6) / 1e9, 1),
-            "headline_bytes": head_bytes, "headline_bytes_replicas": head_replicas,
-            "headline_bytes_us": round(us_small, 3),
-            "gbs_headline_bytes": round(head_bytes / (us_small * 1e-6) / 1e9, 1)}
+            "bytes": head_bytes, "replicas": head_replicas, "read_us": round(us_small, 3),
+            "gbs": round(head_bytes / (us_small * 1e-6) / 1e9, 1)}
 
 
 # ------------------------------------------------------------------ HBM counter calibration
@@ -710,6 +756,89 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str, kernel_substr: 
     return out
 
 
+def _work_of(w):
+    """(algorithmic bytes, algorithmic flops or None) of one step of a workload."""
+    if w.kind == "xent":
+        return xent_bytes(w.tokens, w.vocab, 4 if w.dtype == "f32" else 2, w.reduction), None
+    return (fused_bytes(w.tokens, w.hidden, w.vocab, w.reduction),
+            fused_flops(w.tokens, w.hidden, w.vocab))
+
+
+def summarize_trace(trace_dir: str, workload: str, kernel_substr: str, command: str) -> str:
+    """profiles/kernel_trace_<workload>.md from one rocprofv3 --kernel-trace --stats run:
+    the busiest kernels, and the duration spread of the dispatches of the kernel whose
+    name contains `kernel_substr`, with its roofline at the median and mean duration."""
+    import csv
+    import lce_synth
+    w = lce_synth.WORKLOADS[workload]
+    tf = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    sf = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not tf or not sf:
+        raise SystemExit(f"no kernel_trace.csv / kernel_stats.csv under {trace_dir}")
+    rows = [r for r in csv.DictReader(open(tf[0])) if kernel_substr in r["Kernel_Name"]]
+    if not rows:
+        raise SystemExit(f"no dispatch of {kernel_substr} in {tf[0]}")
+    d = sorted((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0 for r in rows)
+    q = lambda f: d[min(len(d) - 1, int(round(f * (len(d) - 1))))]
+    med, mean = statistics.median(d), statistics.fmean(d)
+    r0 = rows[0]
+    b, fl = _work_of(w)
+    lines = [f"# Kernel trace: {workload}", "",
+             "Command (run from /tmp on one MI355X, repository at $R):", "", f"    {command}", "",
+             "Busiest kernels (run_kernel_stats.csv; every launch of the process, durations in µs):",
+             "", "| kernel | calls | average | min | max |", "|---|---|---|---|---|"]
+    for s in list(csv.DictReader(open(sf[0])))[:5]:
+        lines.append(f"| `{s['Name'][:90]}` | {s['Calls']} | {float(s['AverageNs']) / 1000:.2f} | "
+                     f"{float(s['MinNs']) / 1000:.2f} | {float(s['MaxNs']) / 1000:.2f} |")
+    lines += ["", f"Dispatches of `{kernel_substr}` (run_kernel_trace.csv: eager warm-up and reference "
+              "calls and graph replays): " + f"{len(d)} dispatches, grid {r0['Grid_Size_X']} x "
+              f"{r0['Grid_Size_Y']} work-items in workgroups of {r0['Workgroup_Size_X']}, "
+              f"{r0['LDS_Block_Size']} bytes of LDS.", "",
+              "| statistic | µs |", "|---|---|"]
+    for k, v in (("median", med), ("mean", mean), ("p10", q(0.1)), ("p90", q(0.9)),
+                 ("min", d[0]), ("max", d[-1])):
+        lines.append(f"| {k} | {v:.2f} |")
+    lines.append("")
+    if fl is None:
+        lines.append(f"Algorithmic bytes per launch: {b:,} (each input and output tensor once). At the "
+                     f"median duration that is {b / (med * 1e3):.1f} GB/s = "
+                     f"{b / (med * 1e3) / HBM_PEAK_GBS:.4f} of 8 TB/s; at the mean, "
+                     f"{b / (mean * 1e3):.1f} GB/s = {b / (mean * 1e3) / HBM_PEAK_GBS:.4f}.")
+    else:
+        lines.append(f"Algorithmic flops per launch: {fl:,} (2·T·H·V). At the median duration that is "
+                     f"{fl / (med * 1e6):.1f} TFLOP/s = {fl / (med * 1e6) / BF16_DENSE_TFLOPS:.4f} of "
+                     f"2.5 PFLOP/s; at the mean, {fl / (mean * 1e6):.1f} TFLOP/s.")
+    os.makedirs(PROFILES, exist_ok=True)
+    path = os.path.join(PROFILES, f"kernel_trace_{workload}.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return path
+
+
+def traffic_markdown(d: dict) -> str:
+    """profiles/traffic_<workload>.md beside the JSON summary of summarize_pmc."""
+    import lce_synth
+    w = lce_synth.WORKLOADS[d["workload"]]
+    b, _ = _work_of(w)
+    lines = [f"# HBM traffic: {d['kernel_match']} on {d['workload']}", "",
+             f"Two counter runs, each with a {COPY_BYTES >> 30} GiB device copy (`--copy-calibration`) "
+             "in the same process (run from /tmp, repository at $R):", ""]
+    lines += [f"    {c}" for c in d["commands"].get("runs", [])]
+    lines += ["", f"Summary (traffic_{d['workload']}.json, written by `python bench.py --summarize-pmc "
+              f"<fetch dir> <write dir> --workloads {d['workload']} --kernel {d['kernel_match']}`; it "
+              "is used by bench.py only while the kernel's sources hash to its `source_sha256`).", "",
+              "| counter | kernel, KiB per dispatch (median) | dispatches | copy, KiB per dispatch | "
+              "scale | bytes per launch |", "|---|---|---|---|---|---|"]
+    for k in ("fetch", "write"):
+        e = d[k]
+        lines.append(f"| {e['counter']} | {e['kernel_kib_per_dispatch_median']} | {e['dispatches']} | "
+                     f"{e['copy_kib_per_dispatch_median']} | {e['scale']} | {e['bytes_per_launch']:,} |")
+    t = d["traffic_bytes_per_launch"]
+    lines += ["", f"Traffic per launch: {t:,} B against {b:,} algorithmic bytes: "
+              f"{t / b:.4f}x.", ""]
+    return "\n".join(lines)
+
+
 # ------------------------------------------------------------------ main
 
 def main(argv=None) -> int:
@@ -729,10 +858,12 @@ def main(argv=None) -> int:
                     help="also run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc runs")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="write profiles/kernel_trace_<workload>.md from a rocprofv3 --kernel-trace run")
     ap.add_argument("--kernel", default="xent_wave_rows_kernel",
-                    help="kernel name substring for --summarize-pmc")
+                    help="kernel name substring for --summarize-pmc / --summarize-trace")
     ap.add_argument("--pmc-command", action="append", default=[],
-                    help="command lines of the --pmc runs, recorded in the summary")
+                    help="command lines of the profiler runs, recorded in the summary")
     args = ap.parse_args(argv)
 
     if args.summarize_pmc:
@@ -744,7 +875,14 @@ def main(argv=None) -> int:
         path = os.path.join(PROFILES, f"traffic_{wl}.json")
         with open(path, "w") as fh:
             json.dump(d, fh, indent=1)
+        with open(os.path.join(PROFILES, f"traffic_{wl}.md"), "w") as fh:
+            fh.write(traffic_markdown(d))
         print(json.dumps(d))
+        return 0
+    if args.summarize_trace:
+        import lce_synth
+        wl = lce_synth.HEADLINE if args.workloads in ("all", "headline") else args.workloads
+        print(summarize_trace(args.summarize_trace, wl, args.kernel, " ".join(args.pmc_command)))
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -759,11 +897,34 @@ def main(argv=None) -> int:
 
     lce.load()
     torch.cuda.set_device(0)
-    head = lce_synth.WORKLOADS[lce_synth.HEADLINE]
-    names = list(lce_synth.WORKLOADS) if args.workloads == "all" else (
-        [lce_synth.HEADLINE] if args.workloads == "headline" else args.workloads.split(","))
-    if lce_synth.HEADLINE not in names:
-        names.insert(0, lce_synth.HEADLINE)
+    if args.workloads == "all":
+        names = list(lce_synth.WORKLOADS)
+    elif args.workloads == "headline":
+        names = [lce_synth.HEADLINE]
+    else:
+        names = args.workloads.split(",")
+        unknown = [n for n in names if n not in lce_synth.WORKLOADS]
+        if unknown:
+            raise SystemExit(f"unknown workloads {unknown}; choose from {list(lce_synth.WORKLOADS)}")
+    # The line's head: the headline workload when it is measured, else the first named.
+    head_name = lce_synth.HEADLINE if lce_synth.HEADLINE in names else names[0]
+    head = lce_synth.WORKLOADS[head_name]
+
+    all_extras = ("backward", "shard", "sums", "jsd", "fused_bwd", "split", "sweep", "stream_read")
+    if args.extras is not None:
+        extras = [e for e in args.extras.split(",") if e]
+        unknown = [e for e in extras if e not in all_extras]
+        if unknown:
+            raise SystemExit(f"unknown extras {unknown}; choose from {all_extras}")
+    else:
+        extras = list(all_extras) if args.workloads == "all" and not args.eager else []
+    if "split" in extras or "sweep" in extras:
+        KEEP.update({"ce_f32_16384x131072_mean", "megatron_bf16_2048x4x131072_none"})
+        names += [n for n in sorted(KEEP) if n not in names]
+    if "sweep" in extras:
+        KEEP.add("fused_bf16_t2048_h4096_v128256_mean")
+        if "fused_bf16_t2048_h4096_v128256_mean" not in names:
+            names.append("fused_bf16_t2048_h4096_v128256_mean")
 
     results = {}
     for name in names:
@@ -774,27 +935,17 @@ def main(argv=None) -> int:
         r = time_workload(w, k, args.warmup, torch, lce, eager_only=args.eager)
         r["steps"] = k
         r["roofline"] = roofline_entry(w, r["us_per_step"])
-        if not args.no_cpu and name != lce_synth.HEADLINE:
+        if not args.no_cpu and name != head_name:
             r["cpu_oracle"] = cpu_baseline(w, budget_s=5.0)
         results[name] = r
-        print(f"[bench] {name}: {r['us_per_step']:.2f} µs/step "
-              f"({r['roofline']['achieved']} {r['roofline']['unit']})", file=sys.stderr, flush=True)
+        print(f"[bench] {name}: {r['us_per_step']:.2f} µs/step (median; "
+              f"{r['roofline']['achieved']} {r['roofline']['unit']}) via {r['launch']}",
+              file=sys.stderr, flush=True)
 
-    shard = None
-    sums = None
-    jsd = None
-    fbwd = None
+    shard = sums = jsd = fbwd = split = sweeps = None
     backward = {}
-    all_extras = ("backward", "shard", "sums", "jsd", "fused_bwd", "stream_read")
-    if args.extras is not None:
-        extras = [e for e in args.extras.split(",") if e]
-        unknown = [e for e in extras if e not in all_extras]
-        if unknown:
-            raise SystemExit(f"unknown extras {unknown}; choose from {all_extras}")
-    else:
-        extras = list(all_extras) if args.workloads == "all" and not args.eager else []
     if "backward" in extras:
-        for bname in (lce_synth.HEADLINE, "ce_f32_16384x4096_mean"):
+        for bname in ("megatron_bf16_2048x4x4096_none", "ce_f32_16384x4096_mean"):
             bw = lce_synth.WORKLOADS[bname]
             backward[bname] = time_backward(bw, torch, lce, min(args.steps, 200), args.warmup)
             print(f"[bench] backward {bname}: {backward[bname]['us_per_step']:.2f} µs/step "
@@ -804,6 +955,12 @@ def main(argv=None) -> int:
         print(f"[bench] vocab shard tp=8: partial {shard['partial_us']:.2f} µs, "
               f"merge {shard['merge_us']:.2f} µs, max |diff| vs unsplit "
               f"{shard['max_abs_diff_vs_unsplit']:.2e}", file=sys.stderr, flush=True)
+    if "split" in extras:
+        split = time_split(torch, lce, lce_synth, min(args.steps, 200), args.warmup)
+    if "sweep" in extras:
+        sweeps = time_sweeps(torch, lce, lce_synth, min(args.steps, 100), args.warmup)
+    _KEPT.clear()
+    torch.cuda.empty_cache()
     if "sums" in extras:
         sums = time_logprob_sums(torch, lce, lce_synth, min(args.steps, 10), 2)
         print(f"[bench] fused log-prob sums: {sums['us_per_step']:.1f} µs "
@@ -819,18 +976,40 @@ def main(argv=None) -> int:
               f"({fbwd['roofline']['achieved']} TFLOP/s over 3*2THV)", file=sys.stderr, flush=True)
 
     probe = None
-    if "stream_read" in extras:
-        hb = head.tokens * head.vocab * (4 if head.dtype == "f32" else 2)
-        probe = time_stream_read(torch, hb, results[lce_synth.HEADLINE]["replicas"],
-                                 min(args.steps, 200))
+    if "stream_read" in extras and "megatron_bf16_2048x4x4096_none" in results:
+        pw = lce_synth.WORKLOADS["megatron_bf16_2048x4x4096_none"]
+        hb = pw.tokens * pw.vocab * 2
+        probe = time_stream_read(torch, hb, results[pw.name]["replicas"], min(args.steps, 200))
+        probe["workload"] = pw.name
+        probe["kernel_us_over_read_only_us"] = round(results[pw.name]["us_per_step"] / probe["read_us"], 4)
         print(f"[bench] streaming read: {probe['gbs_2GiB']} GB/s over 2 GiB, "
-              f"{probe['headline_bytes_us']:.2f} µs for the headline's {hb} logit bytes",
+              f"{probe['read_us']:.2f} µs for {pw.name}'s {hb} logit bytes",
               file=sys.stderr, flush=True)
 
     if args.copy_calibration:
         copy_calibration(torch)
 
-    h = results[lce_synth.HEADLINE]
+    h = results[head_name]
+    cfg = {"workload": head.name}
+    if head.kind == "xent":
+        cfg.update({"tokens": head.tokens, "vocab": head.vocab, "logits_dtype": head.dtype,
+                    "logits_shape": list(head.shape)})
+    else:
+        cfg.update({"tokens": head.tokens, "hidden": head.hidden, "vocab": head.vocab})
+    cfg.update({"reduction": head.reduction,
+                "timing": ("eager launches" if args.eager else
+                           f"hip graph of K steps; median over {SPREAD_REPLAYS} timed replays"),
+                "eager_us_per_call": round(h["eager_us_per_call"], 3),
+                "replicas": h["replicas"], "graph_matches_eager": h["graph_matches_eager"],
+                "spread": h.get("spread")})
+    roof = {k: v for k, v in h["roofline"].items() if k in
+            ("bound", "achieved", "peak", "unit", "frac", "traffic")}
+    roof["kernel"] = h["launch"].split(" + ")[0]
+    roof["launch"] = h["launch"]
+    roof["duration_us"] = h["us_per_step"]
+    roof["algorithmic_bytes"] = h["roofline"].get("algorithmic_bytes")
+    if "algorithmic_flops" in h["roofline"]:
+        roof["algorithmic_flops"] = h["roofline"]["algorithmic_flops"]
     line = {
         "metric": METRIC,
         "value": round(h["us_per_step"], 3),
@@ -844,28 +1023,24 @@ def main(argv=None) -> int:
         "vs_baseline": None,
         "dtype": head.dtype,
         "data": "synthetic",
-        "config": {"workload": head.name, "seq": head.shape[0], "batch": head.shape[1],
-                   "vocab": head.shape[2], "tokens": head.tokens, "logits_dtype": head.dtype,
-                   "reduction": head.reduction,
-                   "timing": ("eager launches" if args.eager else "hip graph of K steps, replayed once"),
-                   "eager_us_per_call": round(h["eager_us_per_call"], 3),
-                   "replicas": h["replicas"], "graph_matches_eager": h["graph_matches_eager"],
-                   "spread": h.get("spread")},
-        "roofline": {k: v for k, v in h["roofline"].items() if k in
-                     ("bound", "achieved", "peak", "unit", "frac", "traffic")},
+        "config": cfg,
+        "roofline": roof,
     }
-    line["roofline"]["kernel"] = "xent_wave_rows_kernel<bf16, 4 chunks per lane per batch, 4 waves>"
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(head)
     line["workloads"] = {n: {"us_per_step": round(r["us_per_step"], 3),
                              "rows_per_s": round(lce_synth.WORKLOADS[n].tokens / (r["us_per_step"] * 1e-6)),
-                             "spread": r.get("spread"),
+                             "spread": r.get("spread"), "launch": r["launch"],
                              "eager_us_per_call": round(r["eager_us_per_call"], 3),
                              "steps": r["steps"], "replicas": r["replicas"],
                              "graph_matches_eager": r["graph_matches_eager"],
                              "roofline": r["roofline"],
                              **({"cpu_oracle": r["cpu_oracle"]} if "cpu_oracle" in r else {})}
                          for n, r in results.items()}
+    if split is not None:
+        line["split_path"] = split
+    if sweeps is not None:
+        line["sweeps"] = sweeps
     if shard is not None:
         line["vocab_shard_tp8"] = shard
     if backward:
@@ -877,10 +1052,6 @@ def main(argv=None) -> int:
     if fbwd is not None:
         line["fused_backward"] = fbwd
     if probe is not None:
-        # the headline against the measured read peak (context beside the datasheet roofline)
-        probe["headline_frac_of_2GiB_read_peak"] = round(
-            line["roofline"]["achieved"] / probe["gbs_2GiB"], 4)
-        probe["headline_us_over_read_only_us"] = round(h["us_per_step"] / probe["headline_bytes_us"], 4)
         line["stream_read_probe"] = probe
     print(json.dumps(line), flush=True)
     return 0

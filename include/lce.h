@@ -68,7 +68,7 @@ extern "C" {
 #define LCE_API __attribute__((visibility("default")))
 
 #define LCE_VERSION_MAJOR 0
-#define LCE_VERSION_MINOR 4
+#define LCE_VERSION_MINOR 5
 #define LCE_VERSION_PATCH 0
 
 /* The enums are passed as int.  A caller may pass any int value (a bad one is
@@ -367,6 +367,16 @@ LCE_API const char* lce_last_error(void);
 
 /* MAJOR * 10000 + MINOR * 100 + PATCH. */
 LCE_API int lce_version(void);
+
+/* What the last call on this thread enqueued, for profilers and benchmarks:
+ * the kernels in launch order, joined by " + ", each as its name with the
+ * template arguments that select it (as a demangler prints them) and its grid,
+ * e.g. "xent_wave_rows_kernel<float, 8, 16> grid 1024 x 1024", and
+ * "hipBLASLt GEMM m .. n .. k .." for a library product.  "" after a call that
+ * failed before launching anything or had nothing to do.  Not an operation of
+ * the pages; it describes this library's own dispatch.  The pointer stays
+ * valid until the next liblce call on this thread. */
+LCE_API const char* lce_last_launch(void);
 
 #ifdef __cplusplus
 }

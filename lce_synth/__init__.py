@@ -239,6 +239,7 @@ class JsdWorkload:
 JSD = JsdWorkload("jsd_bf16_t1024_h4096_v128256_mean", 1024, 4096, 128256, 1.0, 0.02,
                   (1006, 3006, 1007, 3007))
 
-# The small case the oracle finishes in seconds, and the headline benchmark workload.
+# The small case the oracle finishes in seconds, and the headline benchmark workload:
+# the largest configuration that fits one GPU (fp32 logits [16384, 131072], 8.6 GB).
 SMALL = "ce_f32_16384x4096_mean"
-HEADLINE = "megatron_bf16_2048x4x4096_none"
+HEADLINE = "ce_f32_16384x131072_mean"

@@ -12,6 +12,10 @@
 //
 // Then two threads make different failing calls at the same time and check
 // that each one sees its own detail message (the message is per thread).
+//
+// The pseudo-call `plan_fused_bwd <tokens> <vocab> <cap>` runs the fused
+// backward's chunk planner (host only) and returns 2 * chunk + stored as its
+// "status", so the planner's choices are checked the same way.
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -22,6 +26,7 @@
 #include <vector>
 
 #include "lce.h"
+#include "lce_host.h"
 
 namespace {
 
@@ -57,6 +62,11 @@ int call(const std::string& fn, const Args& a) {
   if (fn == "lce_fused_linear_jsd_fwd" && k == 10)
     return lce_fused_linear_jsd_fwd(a.p(0), a.p(1), a.p(2), a.p(3), a.n(4), a.n(5), a.n(6), a.f(7),
                                     (lce_reduction)a.e(8), (float*)a.p(9), nullptr);
+  if (fn == "plan_fused_bwd" && k == 3) {
+    lce::host::last_error().clear();
+    const lce::host::FusedBwdPlan p = lce::host::plan_fused_bwd(a.n(0), a.n(1), a.n(2));
+    return (int)(2 * p.chunk + (p.stored ? 1 : 0));
+  }
   if (fn == "lce_fused_linear_xent_bwd" && k == 10)
     return lce_fused_linear_xent_bwd(a.p(0), a.p(1), a.n(2), a.n(3), a.n(4), (const int64_t*)a.p(5),
                                      (lce_reduction)a.e(6), (const float*)a.p(7), (float*)a.p(8),

@@ -46,7 +46,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lce.lce_version() == 400
+    assert lce.lce_version() == 500
     names = [lce.lce_status_string(s) for s in range(6)]
     assert names == ["LCE_OK", "LCE_ERR_INVALID_ARG", "LCE_ERR_UNSUPPORTED", "LCE_ERR_ALIAS",
                      "LCE_ERR_OOM", "LCE_ERR_HIP"]
@@ -75,6 +75,12 @@ XENT_CASES = [
     (dict(out=FAKE + 64), lce.LCE_ERR_ALIAS, "logits"),
     (dict(out=FAKE + (1 << 20) + 8), lce.LCE_ERR_ALIAS, "target"),
     (dict(tokens=1 << 31, vocab=1 << 30, dtype=lce.LCE_F32), lce.LCE_ERR_INVALID_ARG, "overflow"),
+    # one wave (64 work-items) per row: 2^26 rows would need 2^32 work-items in one dispatch
+    (dict(tokens=1 << 26, vocab=32, out=FAKE + (1 << 40), target=FAKE + (1 << 41)),
+     lce.LCE_ERR_UNSUPPORTED, "work-items"),
+    # rows over 32 KiB take a 256-thread workgroup each
+    (dict(tokens=1 << 24, vocab=16384, out=FAKE + (1 << 42), target=FAKE + (1 << 43)),
+     lce.LCE_ERR_UNSUPPORTED, "work-items"),
 ]
 
 
@@ -93,6 +99,12 @@ def test_xent_empty_none_is_a_no_op(lib):
     # tokens == 0 with no reduction writes nothing and needs no pointers.
     assert lce.lce_xent_fwd(0, lce.LCE_F32, 0, 32, 0, lce.LCE_REDUCTION_NONE, 0, 0) == lce.LCE_OK
     assert lce.lce_last_error() == ""
+    assert lce.lce_last_launch() == ""  # nothing was enqueued
+
+
+def test_failed_call_records_no_launch(lib):
+    assert _xent(logits=0) == lce.LCE_ERR_INVALID_ARG
+    assert lce.lce_last_launch() == ""
 
 
 def _fused(x=FAKE, w=FAKE + (1 << 24), tokens=8, hidden=64, vocab=100, target=FAKE + (1 << 28),
@@ -114,6 +126,8 @@ FUSED_CASES = [
     (dict(out=FAKE + 16), lce.LCE_ERR_ALIAS, "x"),
     (dict(out=FAKE + (1 << 24) + 16), lce.LCE_ERR_ALIAS, "weight"),
     (dict(out=FAKE + (1 << 28)), lce.LCE_ERR_ALIAS, "target"),
+    (dict(tokens=1 << 30, target=FAKE + (1 << 41), out=FAKE + (1 << 42)), lce.LCE_ERR_UNSUPPORTED,
+     "2^30"),
 ]
 
 
@@ -148,6 +162,8 @@ PARTIAL_CASES = [
     (dict(start=-1), lce.LCE_ERR_INVALID_ARG, "vocab_start"),
     (dict(start=(1 << 63) - 8), lce.LCE_ERR_INVALID_ARG, "overflows"),
     (dict(partial=FAKE + (2 << 20) + 2), lce.LCE_ERR_INVALID_ARG, "aligned"),
+    (dict(tokens=1 << 26, partial=FAKE + (1 << 40), target=FAKE + (1 << 41)),
+     lce.LCE_ERR_UNSUPPORTED, "work-items"),
     (dict(partial=FAKE + 256), lce.LCE_ERR_ALIAS, "partial overlaps logits"),
     # 16 tokens x 12 bytes reach past the first 64 bytes of partial: overlaps the target
     (dict(partial=FAKE + (1 << 20) - 100), lce.LCE_ERR_ALIAS, "partial overlaps target"),
@@ -207,6 +223,8 @@ BWD_CASES = [
     (dict(dlogits=FAKE + 64), lce.LCE_ERR_ALIAS, "same buffer"),
     (dict(dlogits=FAKE + (1 << 20) - 256), lce.LCE_ERR_ALIAS, "target"),
     (dict(dlogits=FAKE + (2 << 20) - 256), lce.LCE_ERR_ALIAS, "grad"),
+    (dict(tokens=1 << 26, target=FAKE + (1 << 40), grad=FAKE + (1 << 41), dlogits=FAKE + (1 << 42)),
+     lce.LCE_ERR_UNSUPPORTED, "work-items"),
 ]
 
 
@@ -303,6 +321,8 @@ FBWD_CASES = [
     (dict(dx=FAKE + (1 << 28)), lce.LCE_ERR_ALIAS, "dx overlaps target"),
     (dict(dw=FAKE + (1 << 29)), lce.LCE_ERR_ALIAS, "dweight overlaps grad"),
     (dict(dw=FAKE + (1 << 30) + 1024), lce.LCE_ERR_ALIAS, "dx overlaps dweight"),
+    (dict(tokens=1 << 30, target=FAKE + (1 << 40), grad=FAKE + (1 << 41), dx=FAKE + (1 << 42),
+          dw=FAKE + (1 << 44)), lce.LCE_ERR_UNSUPPORTED, "2^30"),
 ]
 
 

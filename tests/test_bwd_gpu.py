@@ -62,8 +62,12 @@ def _run(z, t, dtype, reduction, grad, env=None, in_place=False):
     return _to_host(d, dtype)
 
 
-SHAPES = [(1, 1), (3, 7), (17, 64), (9, 100), (64, 4096), (13, 4097), (5, 8193), (33, 1000),
-          (7, 16384), (4, 20000), (3, 50001)]
+# Rows of every per-lane chunk count the one-wave kernel is instantiated for (1, 2, 4, 8,
+# 16, 32 chunks of 16 bytes per lane) in both dtypes, and longer rows (two-pass path):
+# fp32 vocab 100, 500, 1000, 2000, 4096, 8193 and bf16 vocab 100, 1000, 2000, 4096, 8193,
+# 16384 take 1, 2, 4, 8, 16, 32 chunks per lane.
+SHAPES = [(1, 1), (3, 7), (17, 64), (9, 100), (11, 500), (6, 2000), (64, 4096), (13, 4097),
+          (5, 8193), (33, 1000), (7, 16384), (4, 20000), (3, 50001)]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

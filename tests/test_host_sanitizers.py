@@ -23,6 +23,22 @@ KERNEL_SOURCES = [s for s in lce_build.SOURCES if s.endswith(".hip")]
 OUT = os.path.join(ROOT, "_build", "host_sanitize")
 
 
+# The fused backward's chunk planner, (tokens, vocab, cap) -> (chunk, stored).  The
+# stored path writes a token tile's fp32 logits (256 * ld * 4 bytes) through one
+# buffer resource with 32-bit offsets, so it is never chosen once ld reaches 2^22,
+# however large the cap.
+PLANS = [
+    ((2048, 128256, 2 << 30), (2048, True)),        # the page shape: one stored chunk
+    ((8192, 128256, 2 << 30), (2560, True)),        # chunks of 2560 tokens
+    ((4096, (1 << 22) - 256, 16 << 30), (512, True)),   # ld = 2^22 - 256: still addressable
+    ((4096, (1 << 22) - 255, 16 << 30), (2048, False)),  # ld = 2^22: recompute, 2 B per logit
+    ((8192, (1 << 23) - 512, 64 << 30), (4096, False)),
+    ((4096, (1 << 23) - 512, 2 << 30), (256, False)),   # not even 256 tokens: one tile
+    ((300, 1000, 0), (256, False)),                      # no cap: recompute
+    ((100, 1000, 2 << 30), (100, True)),                 # fewer tokens than a chunk
+]
+
+
 def _flags():
     san = []
     for kind in ("address", "undefined"):  # host only: the device code is not instrumented
@@ -43,7 +59,7 @@ def _build_driver() -> str:
     for src in srcs:
         obj = os.path.join(OUT, os.path.basename(src) + ".o")
         objs.append(obj)
-        cmd = [cc, "-x", "hip", "--cuda-host-only", *_flags(), "-c", src, "-o", obj]
+        cmd = [cc, "-x", "hip", "--cuda-host-only", *_flags(), "-I", lce_build.CSRC, "-c", src, "-o", obj]
         jobs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
     for src, p in jobs:
         out, _ = p.communicate()
@@ -89,6 +105,8 @@ def test_host_code_is_clean_under_sanitizers():
     lines = [_line(fn, helper, kw, st, needle)
              for fn, helper, table in CASE_TABLES for kw, st, needle in table]
     lines += EMPTY
+    lines += [f"plan_fused_bwd {2 * chunk + int(stored)} 3 {t} {v} {cap} "
+              for (t, v, cap), (chunk, stored) in PLANS]
     env = dict(os.environ)
     # the HIP runtime's own allocations outlive main: leak reports would be about it
     env["ASAN_OPTIONS"] = "detect_leaks=0:halt_on_error=1:abort_on_error=0"

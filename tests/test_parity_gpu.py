@@ -347,19 +347,55 @@ def load_workload_streaming(w, block_rows=1024):
 @pytest.mark.parametrize("name", ["ce_f32_16384x4096_mean", "megatron_bf16_2048x4x4096_none",
                                   "ce_f32_16384x131072_mean", "megatron_bf16_2048x4x131072_none"])
 def test_full_size_row_workloads(name):
+    """Every logit of the four row workloads against the oracle, per token and the mean, on
+    the default path; the two 131072-wide workloads also on the split-vocab path forced
+    with 8 and 32 slices per row (the path the large-vocab configuration names, which the
+    default selection keeps for fewer rows than twice the CU count)."""
     w = WORKLOADS[name]
     print(f"\n[parity] workload {name} shape {w.shape}", flush=True)
     z, t, want = load_workload_streaming(w)
-    per = lce.xent(z, t, "none").cpu().numpy().reshape(-1).astype(np.float64)
-    mean = lce.xent(z, t, "mean").item()
-    err = np.abs(per - want)
-    print(f"[parity] {name}: max abs err {err.max():.3e}; mean {mean:.8f} vs {oracle.mean(want):.8f}",
-          flush=True)
-    assert err.max() <= TOK_ABS
     wm = oracle.mean(want)
-    assert abs(mean - wm) <= MEAN_REL * abs(wm)
+    envs = [{}]
+    if w.vocab == 131072:
+        envs += [{"LCE_PATH": "split", "LCE_SPLITS": 8}, {"LCE_PATH": "split", "LCE_SPLITS": 32}]
+    for env in envs:
+        with forced_env(**env):
+            per = lce.xent(z, t, "none").cpu().numpy().reshape(-1).astype(np.float64)
+            launch_none = lce.lce_last_launch()
+            mean = lce.xent(z, t, "mean").item()
+            launch_mean = lce.lce_last_launch()
+        err = np.abs(per - want)
+        print(f"[parity] {name} {env}: max abs err {err.max():.3e}; mean {mean:.8f} vs {wm:.8f}; "
+              f"{launch_none} | {launch_mean}", flush=True)
+        if env:
+            s = env["LCE_SPLITS"]
+            assert launch_none.startswith("xent_split_partial_kernel") and f"grid ({s}, " in launch_none
+            assert launch_mean.startswith("xent_split_partial_kernel") and f"grid ({s}, " in launch_mean
+        assert err.max() <= TOK_ABS, env
+        assert abs(mean - wm) <= MEAN_REL * abs(wm), env
     del z
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["ce_f32_16384x131072_mean", "megatron_bf16_2048x4x131072_none"])
+def test_few_long_rows_take_the_split_path(name):
+    """256 rows of a 131072-wide workload (fewer rows than twice the CU count): the default
+    selection is the split-vocab path; every row against the oracle, per token and mean."""
+    w = WORKLOADS[name]
+    rows = 256
+    host = w.logits(0, rows)
+    tg = w.target(0, rows)
+    want = oracle.xent_rows(host, tg, dtype=w.dtype)
+    wm = oracle.mean(want)
+    z, t = to_dev(host), torch.from_numpy(tg).cuda()
+    per = lce.xent(z, t, "none").cpu().numpy().astype(np.float64)
+    launch = lce.lce_last_launch()
+    mean = lce.xent(z, t, "mean").item()
+    print(f"\n[parity] {name} rows [0, {rows}): {launch}; max abs err "
+          f"{np.max(np.abs(per - want)):.3e}", flush=True)
+    assert launch.startswith("xent_split_partial_kernel"), launch
+    assert np.max(np.abs(per - want)) <= TOK_ABS
+    assert abs(mean - wm) <= MEAN_REL * abs(wm)
 
 
 @pytest.mark.parametrize("dtype,rows,vocab", [("f32", 2, (1 << 28) + 3), ("bf16", 1, (1 << 29) + 5)])

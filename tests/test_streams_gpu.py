@@ -142,3 +142,34 @@ def test_refused_scratch_allocation_reports_oom():
     assert d["canary"] == 123.0, d
     assert d["st2"] == lce.LCE_OK, d
     assert abs(d["got"] - d["want"]) <= 1e-5 * abs(d["want"]), d
+
+
+def test_mean_after_fused_backward_on_one_stream():
+    """The deterministic mean hands each workgroup's partial to the last workgroup through
+    tagged 64-bit slots, which must never hold another call's data.  They live in a buffer
+    that only the mean reductions write: a fused backward (which fills this stream's scratch
+    with fp32 logits, the bf16 logit gradient and GEMM workspace) followed, on the same
+    stream, by large-grid means of every mean-reducing entry point must give the mean of the
+    same call's per-token values, on every repetition."""
+    s = torch.cuda.Stream()
+    x = to_dev(lce_synth.normal_bf16_bits(41, 0, 777, 256, 1.0))
+    w = to_dev(lce_synth.normal_bf16_bits(42, 2, 9000, 256, 0.1))
+    t = torch.from_numpy(lce_synth.targets(43, 777, 9000)).cuda()
+    rows, vocab = 300_001, 64  # 18751 workgroups of 16 rows: the mean reads 18751 slots
+    z = to_dev(lce_synth.f32_to_bf16_bits(lce_synth.normal_f32(44, 0, rows, vocab, 2.0)))
+    tz = torch.from_numpy(lce_synth.targets(45, rows, vocab)).cuda()
+    x2 = to_dev(lce_synth.normal_bf16_bits(46, 0, 777, 256, 1.0))
+    w2 = to_dev(lce_synth.normal_bf16_bits(47, 2, 9000, 256, 0.1))
+    with torch.cuda.stream(s):
+        per_row = lce.xent(z, tz, "none").double()
+        per_fused = lce.fused_linear_xent(x, w, t, "none").double()
+        per_jsd = lce.fused_linear_jsd(x, w, x2, w2, 0.5, "none").double()
+        for rep in range(4):
+            g = torch.full((1,), 1.0 + rep, device="cuda")
+            lce.fused_linear_xent_bwd(x, w, t, g, "mean")
+            means = [lce.xent(z, tz, "mean"), lce.fused_linear_xent(x, w, t, "mean"),
+                     lce.fused_linear_jsd(x, w, x2, w2, 0.5, "mean")]
+            s.synchronize()
+            for name, m, per in zip(("row", "fused", "jsd"), means, (per_row, per_fused, per_jsd)):
+                want = per.mean().item()
+                assert abs(m.item() - want) <= 1e-5 * abs(want), (rep, name, m.item(), want)

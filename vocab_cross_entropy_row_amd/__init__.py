@@ -8,7 +8,7 @@ code:
 * :func:`lce_xent_bwd` (gradient with respect to the logits)
 * :func:`lce_fused_linear_logprob_sums` (per-sequence target log-probability sums)
 * :func:`lce_xent_partial_fwd`, :func:`lce_xent_merge` (vocab split across devices)
-* :func:`lce_status_string`, :func:`lce_last_error`, :func:`lce_version`
+* :func:`lce_status_string`, :func:`lce_last_error`, :func:`lce_last_launch`, :func:`lce_version`
 
 :func:`xent`, :func:`xent_bwd`, :func:`fused_linear_xent`, :func:`xent_partial` and :func:`xent_merge`
 are thin conveniences over them for
@@ -39,7 +39,8 @@ LCE_ERR_HIP = 5
 
 EXPORTED = ("lce_xent_fwd", "lce_xent_bwd", "lce_fused_linear_xent_fwd", "lce_fused_linear_xent_bwd",
             "lce_fused_linear_logprob_sums", "lce_fused_linear_jsd_fwd", "lce_xent_partial_fwd",
-            "lce_xent_merge", "lce_status_string", "lce_last_error", "lce_version")
+            "lce_xent_merge", "lce_status_string", "lce_last_error", "lce_last_launch",
+            "lce_version")
 
 _lib = None
 
@@ -100,6 +101,8 @@ def load() -> ctypes.CDLL:
     lib.lce_status_string.argtypes = [ctypes.c_int]
     lib.lce_last_error.restype = ctypes.c_char_p
     lib.lce_last_error.argtypes = []
+    lib.lce_last_launch.restype = ctypes.c_char_p
+    lib.lce_last_launch.argtypes = []
     lib.lce_version.restype = ctypes.c_int
     lib.lce_version.argtypes = []
     _lib = lib
@@ -172,6 +175,11 @@ def lce_last_error() -> str:
 
 def lce_version() -> int:
     return load().lce_version()
+
+
+def lce_last_launch() -> str:
+    """Kernels (with template arguments and grids) the last call on this thread enqueued."""
+    return load().lce_last_launch().decode()
 
 
 # ------------------------------------------------------------------ torch conveniences

@@ -236,6 +236,7 @@ template <typename T, int NCH>
 hipError_t launch_bwd_wave_t(const BwdArgs& a, hipStream_t st) {
   constexpr int W = 4;
   const int64_t blocks = (a.tokens + W - 1) / W;
+  if (!grid_fits(blocks, 64 * W)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((xent_bwd_wave_kernel<T, NCH, W>), dim3((unsigned)blocks), dim3(64 * W), 0, st,
                      (const T*)a.logits, a.tokens, (int)a.vocab, a.target, a.grad, a.reduce_mean,
                      (T*)a.dlogits);
@@ -255,6 +256,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
       default: return hipErrorInvalidValue;
     }
   }
+  if (!grid_fits((int64_t)a.splits * a.tokens, kRowThreads)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((xent_bwd_apply_kernel<T, 4>), dim3((unsigned)(a.splits * a.tokens)),
                      dim3(kRowThreads), 0, st, (const T*)a.logits, a.tokens, (int)a.vocab, a.target,
                      a.grad, a.reduce_mean, a.stats, a.splits, a.chunks_per_split, (T*)a.dlogits);

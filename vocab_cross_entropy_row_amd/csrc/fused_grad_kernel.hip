@@ -12,6 +12,7 @@
 #include <stdint.h>
 
 #include "fused_grad.h"
+#include "lce_internal.h"
 #include "lce_device.h"
 #include "mfma_common.h"
 
@@ -86,13 +87,14 @@ __global__ __launch_bounds__(256) void transpose_u16_kernel(const uint16_t* __re
 hipError_t launch_transpose_u16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out,
                                 hipStream_t stream) {
   const int64_t blocks = ((cols + 63) / 64) * ((rows + 63) / 64);
-  if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  if (!grid_fits(blocks, 256)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(transpose_u16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, in, rows,
                      cols, out);
   return hipGetLastError();
 }
 
 hipError_t launch_fused_grad_rows(const FusedGradRowsArgs& a, hipStream_t stream) {
+  if (!grid_fits(a.rows, kGThreads)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(fused_grad_rows_kernel, dim3((unsigned)a.rows), dim3(kGThreads), 0, stream,
                      a.z, a.lse, a.target, a.grad, a.grad_mean, a.grad_tokens, a.vocab, a.ld,
                      (uint16_t*)a.dz);

@@ -540,6 +540,9 @@ int fused_segments(int64_t tokens, int64_t vocab, int num_cus) {
 hipError_t launch_fused(const FusedArgs& a, hipStream_t stream) {
   const int64_t n_tok = (a.tokens + FusedTile::kBT - 1) / FusedTile::kBT;
   const int64_t grid = n_tok * a.segments;
+  if (!grid_fits(grid, FusedTile::kThreads) ||
+      !grid_fits((a.tokens + kRowThreads - 1) / kRowThreads, kRowThreads))
+    return hipErrorInvalidConfiguration;
   if (a.z_out)
     hipLaunchKernelGGL((fused_xent_partial_kernel<FusedTile, 4, 2, 2, kFusedStoreLogits>),
                        dim3((unsigned)grid), dim3(FusedTile::kThreads), 0, stream,
@@ -565,6 +568,7 @@ hipError_t launch_fused(const FusedArgs& a, hipStream_t stream) {
 hipError_t launch_fused_grad(const FusedGradArgs& a, hipStream_t stream) {
   const int64_t n_tok = (a.tokens + FusedTile::kBT - 1) / FusedTile::kBT;
   const int64_t grid = n_tok * a.segments;
+  if (!grid_fits(grid, FusedTile::kThreads)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((fused_xent_partial_kernel<FusedTile, 4, 2, 2, kFusedGrad>),
                      dim3((unsigned)grid), dim3(FusedTile::kThreads), 0, stream,
                      (const uint16_t*)a.x, (const uint16_t*)a.w, a.tokens, a.hidden, a.vocab,

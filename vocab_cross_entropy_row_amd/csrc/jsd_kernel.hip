@@ -298,6 +298,9 @@ int jsd_segments(int64_t tokens, int64_t vocab, int num_cus) {
 
 hipError_t launch_jsd(const JsdArgs& a, hipStream_t stream) {
   const int64_t n_tok = (a.tokens + kJT - 1) / kJT;
+  if (!grid_fits(n_tok * a.segments, kJThreads) ||
+      !grid_fits((a.tokens + kRowThreads - 1) / kRowThreads, kRowThreads))
+    return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(fused_jsd_partial_kernel, dim3((unsigned)(n_tok * a.segments)), dim3(kJThreads),
                      0, stream, (const uint16_t*)a.xs, (const uint16_t*)a.ws, (const uint16_t*)a.xt,
                      (const uint16_t*)a.wt, a.tokens, a.hidden, a.vocab, a.lse_s, a.lse_t, a.beta,
@@ -312,6 +315,7 @@ hipError_t launch_jsd(const JsdArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_jsd_rows(const JsdRowsArgs& a, hipStream_t stream) {
+  if (!grid_fits(a.rows, kJRThreads)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(jsd_stored_rows_kernel, dim3((unsigned)a.rows), dim3(kJRThreads), 0, stream,
                      a.zs, a.zt, a.z_ld, a.vocab, a.lse_s, a.lse_t, a.beta, a.dst);
   return hipGetLastError();
@@ -320,6 +324,7 @@ hipError_t launch_jsd_rows(const JsdRowsArgs& a, hipStream_t stream) {
 hipError_t launch_jsd_mean(int64_t tokens, const float* per_token, float* out, uint64_t* slots,
                            unsigned* ticket, hipStream_t stream) {
   const int64_t blocks = (tokens + kRowThreads - 1) / kRowThreads;
+  if (!grid_fits(blocks, kRowThreads)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(fused_jsd_merge_kernel, dim3((unsigned)blocks), dim3(kRowThreads), 0, stream,
                      tokens, 1, per_token, out, slots, ticket, 1);
   return hipGetLastError();

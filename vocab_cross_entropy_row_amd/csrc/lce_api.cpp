@@ -21,7 +21,7 @@ namespace host {
 // The first `reserved` bytes of scratch regions belong to the caller.
 lce_status run_rows(const void* logits, int dtype, int64_t tokens, int64_t vocab,
                     const int64_t* target, bool mean, float* out, int64_t vocab_start,
-                    float* stats, hipStream_t stream, size_t reserved) {
+                    float* stats, hipStream_t stream, size_t reserved, const RowWorkspace* ws) {
   lce_status s = LCE_OK;
   int cus = 0;
   if ((s = num_cus(&cus)) != LCE_OK) return s;
@@ -91,14 +91,16 @@ lce_status run_rows(const void* logits, int dtype, int64_t tokens, int64_t vocab
   // The kernels address a row (or a split slice) with 32-bit buffer offsets.
   if (a.path != lce::XentPath::Split && row_bytes > kMaxStreamBytes) a.path = lce::XentPath::Split;
 
-  size_t need_partials = 0, need_split = 0;
+  size_t need_split = 0;
   if (a.path == lce::XentPath::Split) {
     if (tokens > 65535) return fail(LCE_ERR_UNSUPPORTED, "split path needs tokens <= 65535");
     // Enough workgroups for ~4 per CU, but at least one 256-thread batch of 8
     // chunks per workgroup.
-    int64_t S = env_int("LCE_SPLITS", 0);
-    if (S <= 0) S = (4 * (int64_t)cus + tokens - 1) / tokens;
-    const int64_t max_s = (nvec + lce::kRowThreads * 8 - 1) / (lce::kRowThreads * 8);
+    // A forced count (LCE_SPLITS) may go down to one chunk per thread.
+    const int64_t forced_s = env_int("LCE_SPLITS", 0);
+    int64_t S = forced_s > 0 ? forced_s : (4 * (int64_t)cus + tokens - 1) / tokens;
+    const int64_t per_split = forced_s > 0 ? lce::kRowThreads : lce::kRowThreads * 8;
+    const int64_t max_s = (nvec + per_split - 1) / per_split;
     if (S > max_s) S = max_s;
     if (S < 1) S = 1;
     if (S > 65535) S = 65535;
@@ -112,20 +114,46 @@ lce_status run_rows(const void* logits, int dtype, int64_t tokens, int64_t vocab
       (a.path == lce::XentPath::BlockRows) ? tokens
       : (a.path == lce::XentPath::WaveRows) ? (tokens + a.waves_per_block - 1) / a.waves_per_block
                                               : (tokens + lce::kRowThreads / 64 - 1) / (lce::kRowThreads / 64);
-  need_partials = (size_t)mean_blocks * 8u;
 
-  Carve cv;
-  if (reserved) cv.take(reserved);
-  const size_t off_mean = cv.take(need_partials);
-  const size_t off_split = cv.take(need_split);
-  char* base = nullptr;
-  if ((s = get_scratch(stream, cv.off, &base)) != LCE_OK) return s;
-  a.ticket = (unsigned*)base;
-  a.mean_slots = (uint64_t*)(base + off_mean);
-  a.split_partials = (float*)(base + off_split);
+  if (ws) {  // the caller's memory: nothing is allocated
+    if (need_split > ws->general_bytes)
+      return fail(LCE_ERR_UNSUPPORTED,
+                  "the split path needs %zu bytes of partials; the workspace holds %zu", need_split,
+                  ws->general_bytes);
+    if (mean && mean_blocks > ws->max_slots)
+      return fail(LCE_ERR_UNSUPPORTED, "the mean needs %lld workgroup slots; the workspace holds %lld",
+                  (long long)mean_blocks, (long long)ws->max_slots);
+    a.split_partials = (float*)ws->general;
+    a.ticket = ws->ticket;
+    a.mean_slots = ws->slots;
+  } else {
+    Carve cv;
+    if (reserved) cv.take(reserved);
+    const size_t off_split = cv.take(need_split);
+    char* base = nullptr;
+    if ((s = get_scratch(stream, cv.off, &base)) != LCE_OK) return s;
+    a.split_partials = (float*)(base + off_split);
+    if (mean) {
+      MeanState ms;
+      if ((s = get_mean_state(stream, mean_blocks, &ms)) != LCE_OK) return s;
+      a.ticket = ms.ticket;
+      a.mean_slots = ms.slots;
+    }
+  }
 
   hipError_t e = lce::launch_xent(a, stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  // Template arguments as a demangler prints them (T is float or unsigned short).
+  const char* tn = a.bf16 ? "unsigned short" : "float";
+  if (a.path == lce::XentPath::WaveRows)
+    note_launch("xent_wave_rows_kernel<%s, %d, %d> grid %lld x %d", tn, a.unroll, a.waves_per_block,
+                (long long)((tokens + a.waves_per_block - 1) / a.waves_per_block), 64 * a.waves_per_block);
+  else if (a.path == lce::XentPath::BlockRows)
+    note_launch("xent_block_rows_kernel<%s, 8> grid %lld x %d", tn, (long long)tokens, lce::kRowThreads);
+  else
+    note_launch("xent_split_partial_kernel<%s, 8> grid (%d, %lld) x %d + xent_split_merge_kernel<%s> "
+                "grid %lld x %d", tn, a.splits, (long long)tokens, lce::kRowThreads, tn,
+                (long long)((tokens + 3) / 4), lce::kRowThreads);
   return LCE_OK;
 }
 
@@ -142,7 +170,6 @@ FusedPlan plan_fused(int64_t tokens, int64_t vocab, int cus, size_t reserved) {
   if (reserved) cv.take(reserved);
   p.off_seg = cv.take((size_t)p.segments * (size_t)tokens * 8u);
   p.off_zt = cv.take((size_t)tokens * 4u);
-  p.off_mean = cv.take((size_t)((tokens + lce::kRowThreads - 1) / lce::kRowThreads) * 8u);
   p.end = cv.off;
   return p;
 }
@@ -176,13 +203,23 @@ lce_status run_fused(const void* x, const void* weight, int64_t tokens, int64_t 
 
   char* base = nullptr;
   if ((s = get_scratch(stream, p.end, &base)) != LCE_OK) return s;
-  a.ticket = (unsigned*)base;
   a.seg_partials = (float*)(base + p.off_seg);
   a.target_logit = (float*)(base + p.off_zt);
-  a.mean_slots = (uint64_t*)(base + p.off_mean);
+  if (a.reduce_mean) {
+    MeanState ms;
+    if ((s = get_mean_state(stream, (tokens + lce::kRowThreads - 1) / lce::kRowThreads, &ms)) != LCE_OK)
+      return s;
+    a.ticket = ms.ticket;
+    a.mean_slots = ms.slots;
+  }
 
   hipError_t e = lce::launch_fused(a, stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  const lce::FusedGeometry g = lce::fused_geometry();
+  note_launch("fused_xent_partial_kernel (%s) grid %lld x 512 + fused_xent_merge_kernel grid %lld x %d",
+              z_out ? "log-sum-exp, logits stored" : lse_out ? "log-sum-exp" : "loss",
+              (long long)((tokens + g.block_tokens - 1) / g.block_tokens * p.segments),
+              (long long)((tokens + lce::kRowThreads - 1) / lce::kRowThreads), lce::kRowThreads);
   return LCE_OK;
 }
 
@@ -207,12 +244,14 @@ const char* lce_status_string(lce_status status) {
 
 const char* lce_last_error(void) { return last_error().c_str(); }
 
+const char* lce_last_launch(void) { return last_launch().c_str(); }
+
 int lce_version(void) { return LCE_VERSION_MAJOR * 10000 + LCE_VERSION_MINOR * 100 + LCE_VERSION_PATCH; }
 
 lce_status lce_xent_fwd(const void* logits, lce_dtype dtype, int64_t tokens, int64_t vocab,
                         const int64_t* target, lce_reduction reduction, float* out,
                         hipStream_t stream) {
-  last_error().clear();
+  begin_call();
   lce_status s = validate_xent(logits, (int)dtype, tokens, vocab, target, (int)reduction, out);
   if (s != LCE_OK) return s;
   const bool mean = reduction == LCE_REDUCTION_MEAN;
@@ -227,7 +266,7 @@ lce_status lce_xent_fwd(const void* logits, lce_dtype dtype, int64_t tokens, int
 lce_status lce_xent_partial_fwd(const void* logits, lce_dtype dtype, int64_t tokens,
                                 int64_t shard_vocab, int64_t vocab_start, const int64_t* target,
                                 float* partial, hipStream_t stream) {
-  last_error().clear();
+  begin_call();
   // Same checks as lce_xent_fwd with a per-token output of 3 floats.
   lce_status s = validate_xent(logits, (int)dtype, tokens, shard_vocab, target,
                                LCE_REDUCTION_NONE, partial, "partial", 3);
@@ -244,7 +283,7 @@ lce_status lce_xent_partial_fwd(const void* logits, lce_dtype dtype, int64_t tok
 lce_status lce_xent_merge(const float* partials, int64_t shards, int64_t tokens,
                           const int64_t* target, int64_t vocab, lce_reduction reduction,
                           float* out, hipStream_t stream) {
-  last_error().clear();
+  begin_call();
   lce_status s = validate_common(tokens, target, (int)reduction, out);
   if (s != LCE_OK) return s;
   if (shards < 1) return fail(LCE_ERR_INVALID_ARG, "shards must be >= 1 (got %lld)", (long long)shards);
@@ -264,20 +303,21 @@ lce_status lce_xent_merge(const float* partials, int64_t shards, int64_t tokens,
     hipError_t e = lce::launch_fill_f32(out, 1, __builtin_nanf(""), stream);
     return e == hipSuccess ? LCE_OK : hip_fail(e, "launch");
   }
-  Carve cv;
-  const size_t off_mean = cv.take((size_t)((tokens + lce::kRowThreads - 1) / lce::kRowThreads) * 8u);
-  char* base = nullptr;
-  if ((s = get_scratch(stream, cv.off, &base)) != LCE_OK) return s;
+  MeanState ms;
+  if (mean && (s = get_mean_state(stream, (tokens + lce::kRowThreads - 1) / lce::kRowThreads, &ms)) != LCE_OK)
+    return s;
   hipError_t e = lce::launch_stats_merge(partials, shards, tokens, target, vocab, out, mean ? 1 : 0,
-                                         (uint64_t*)(base + off_mean), (unsigned*)base, stream);
+                                         ms.slots, ms.ticket, stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  note_launch("xent_stats_merge_kernel grid %lld x %d",
+              (long long)((tokens + lce::kRowThreads - 1) / lce::kRowThreads), lce::kRowThreads);
   return LCE_OK;
 }
 
 lce_status lce_xent_bwd(const void* logits, lce_dtype dtype, int64_t tokens, int64_t vocab,
                         const int64_t* target, lce_reduction reduction, const float* grad,
                         void* dlogits, hipStream_t stream) {
-  last_error().clear();
+  begin_call();
   lce_status s = validate_xent(logits, (int)dtype, tokens, vocab, target, LCE_REDUCTION_NONE, nullptr,
                                nullptr);
   if (s != LCE_OK) return s;
@@ -335,8 +375,9 @@ lce_status lce_xent_bwd(const void* logits, lce_dtype dtype, int64_t tokens, int
     const int64_t min_s = (nvec * 16 + kMaxStreamBytes - 1) / kMaxStreamBytes;
     if (S < min_s) S = min_s;
     if (S < 1) S = 1;
-    if (S * tokens >= (int64_t(1) << 31))
-      return fail(LCE_ERR_UNSUPPORTED, "tokens * slices must be < 2^31 (got %lld)", (long long)(S * tokens));
+    if (!lce::grid_fits(S * tokens, lce::kRowThreads))
+      return fail(LCE_ERR_UNSUPPORTED, "tokens * slices * 256 work-items must be < 2^32 (got %lld slices)",
+                  (long long)(S * tokens));
     a.splits = (int)S;
     a.chunks_per_split = (int)((nvec + S - 1) / S);
     // Row states (m, sum e^(z - m), .) into scratch, then the gradient pass.
@@ -352,13 +393,20 @@ lce_status lce_xent_bwd(const void* logits, lce_dtype dtype, int64_t tokens, int
   }
   hipError_t e = lce::launch_bwd(a, stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  const char* tn = a.bf16 ? "unsigned short" : "float";
+  if (a.wave_chunks > 0)
+    note_launch("xent_bwd_wave_kernel<%s, %d, 4> grid %lld x 256", tn, a.wave_chunks,
+                (long long)((tokens + 3) / 4));
+  else
+    note_launch("xent_bwd_apply_kernel<%s, 4> grid %lld x %d", tn, (long long)(a.splits * tokens),
+                lce::kRowThreads);
   return LCE_OK;
 }
 
 lce_status lce_fused_linear_xent_fwd(const void* x, const void* weight, int64_t tokens,
                                      int64_t hidden, int64_t vocab, const int64_t* target,
                                      lce_reduction reduction, float* out, hipStream_t stream) {
-  last_error().clear();
+  begin_call();
   lce_status s = validate_fused(x, weight, tokens, hidden, vocab, target, (int)reduction, out);
   if (s != LCE_OK) return s;
   const bool mean = reduction == LCE_REDUCTION_MEAN;
@@ -373,7 +421,7 @@ lce_status lce_fused_linear_xent_fwd(const void* x, const void* weight, int64_t 
 lce_status lce_fused_linear_logprob_sums(const void* x, const void* weight, int64_t batch,
                                          int64_t seq, int64_t hidden, int64_t vocab,
                                          const int64_t* target, float* out, hipStream_t stream) {
-  last_error().clear();
+  begin_call();
   if (batch < 0 || seq < 0)
     return fail(LCE_ERR_INVALID_ARG, "batch and seq must be >= 0 (got %lld, %lld)", (long long)batch,
                 (long long)seq);
@@ -400,6 +448,7 @@ lce_status lce_fused_linear_logprob_sums(const void* x, const void* weight, int6
     return s;
   hipError_t e = lce::launch_seq_logprob_sums(loss, batch, seq, out, stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  note_launch("seq_logprob_sum_kernel grid %lld x %d", (long long)((batch + 3) / 4), lce::kRowThreads);
   return LCE_OK;
 }
 }  // extern "C"

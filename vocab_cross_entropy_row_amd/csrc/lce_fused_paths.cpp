@@ -26,6 +26,28 @@ namespace host {
 // buffers (6 or 2 bytes per logit) fit in LCE_FUSED_BWD_STORE_BYTES (default
 // 2 GiB), at least 256.
 constexpr size_t kGemmWorkspace = size_t(128) << 20;
+// Most tokens per chunk: the per-token streaming kernels launch 256 work-items
+// per token, and a dispatch counts its work-items in 32 bits.
+constexpr int64_t kMaxChunk = (int64_t(1) << 24) - 256;
+
+// The stored path also needs the store mode's 32-bit addressing: a token
+// tile's fp32 rows (block_tokens * ld * 4 bytes) go through one buffer
+// resource.  Beyond that (vocab >= 2^22 - 256 with the tile of 256 tokens)
+// the recompute path is taken whatever the cap, since its bf16 dZ rows need
+// half the bytes (the entry point refuses vocab >= 2^23 - 256).
+FusedBwdPlan plan_fused_bwd(int64_t tokens, int64_t vocab, int64_t cap) {
+  FusedBwdPlan p;
+  const lce::FusedGeometry geo = lce::fused_geometry();
+  p.ld = (vocab + geo.block_vocab - 1) / geo.block_vocab * geo.block_vocab;
+  const bool addressable = p.ld * geo.block_tokens * 4 < (int64_t(1) << 32);
+  p.stored = addressable && cap / (p.ld * 6) >= geo.block_tokens;
+  int64_t chunk = cap / (p.ld * (p.stored ? 6 : 2)) / geo.block_tokens * geo.block_tokens;
+  if (chunk < geo.block_tokens) chunk = geo.block_tokens;
+  if (chunk > kMaxChunk) chunk = kMaxChunk;
+  if (chunk > tokens) chunk = tokens;
+  p.chunk = chunk;
+  return p;
+}
 
 lce_status run_fused_bwd(const void* x, const void* weight, int64_t tokens, int64_t hidden,
                          int64_t vocab, const int64_t* target, bool mean, const float* grad,
@@ -33,13 +55,10 @@ lce_status run_fused_bwd(const void* x, const void* weight, int64_t tokens, int6
   lce_status s = LCE_OK;
   int cus = 0;
   if ((s = num_cus(&cus)) != LCE_OK) return s;
-  const lce::FusedGeometry geo = lce::fused_geometry();
-  const int64_t ld = (vocab + geo.block_vocab - 1) / geo.block_vocab * geo.block_vocab;
-  const int64_t cap = env_int64("LCE_FUSED_BWD_STORE_BYTES", int64_t(2) << 30);
-  const bool stored = cap / (ld * 6) >= geo.block_tokens;
-  int64_t chunk = cap / (ld * (stored ? 6 : 2)) / geo.block_tokens * geo.block_tokens;
-  if (chunk < geo.block_tokens) chunk = geo.block_tokens;
-  if (chunk > tokens) chunk = tokens;
+  const FusedBwdPlan plan =
+      plan_fused_bwd(tokens, vocab, env_int64("LCE_FUSED_BWD_STORE_BYTES", int64_t(2) << 30));
+  const int64_t ld = plan.ld, chunk = plan.chunk;
+  const bool stored = plan.stored;
 
   Carve cv;
   const size_t off_lse = cv.take((size_t)tokens * 4u);
@@ -89,6 +108,7 @@ lce_status run_fused_bwd(const void* x, const void* weight, int64_t tokens, int6
       g.ld = ld;
       g.dz = (uint16_t*)dz;
       e = lce::launch_fused_grad_rows(g, stream);
+      if (e == hipSuccess) note_launch("fused_grad_rows_kernel grid %lld x 256", (long long)n);
     } else {
       lce::FusedGradArgs g{};
       g.x = x16 + c0 * hidden;
@@ -105,6 +125,7 @@ lce_status run_fused_bwd(const void* x, const void* weight, int64_t tokens, int6
       g.dz_ld = ld;
       g.segments = lce::fused_segments(n, vocab, cus);
       e = lce::launch_fused_grad(g, stream);
+      if (e == hipSuccess) note_launch("fused_xent_partial_kernel (logit gradient)");
     }
     if (e != hipSuccess) return hip_fail(e, "kernel launch");
     // Row-major [r, c] is column-major [c, r]: dx^T[H, n] = W^T[H, V] dZ^T[V, n],
@@ -118,6 +139,7 @@ lce_status run_fused_bwd(const void* x, const void* weight, int64_t tokens, int6
       // dZ row-major [n, ld] (column-major [ld, n]) read transposed.
       e = lce::launch_transpose_u16(x16 + c0 * hidden, n, hidden, xt, stream);
       if (e != hipSuccess) return hip_fail(e, "kernel launch");
+      note_launch("transpose_u16_kernel");
       if ((s = gemm_bf16_f32(HIPBLAS_OP_T, HIPBLAS_OP_T, hidden, vocab, n, xt, n, dz, ld,
                              c0 == 0 ? 0.0f : 1.0f, dw, hidden, ws, kGemmWorkspace, stream)) != LCE_OK)
         return s;
@@ -152,6 +174,7 @@ JsdPlan plan_jsd(int64_t tokens, int64_t vocab) {
   const int64_t per_token = ld * 8;  // both heads' rows
   int64_t max_chunk = cap / per_token / g.block_tokens * g.block_tokens;
   if (max_chunk < g.block_tokens) return p;
+  if (max_chunk > kMaxChunk) max_chunk = kMaxChunk;
   if (tokens <= max_chunk) {
     p.chunk = tokens;
   } else {
@@ -171,7 +194,6 @@ lce_status run_jsd_stored(const void* xs, const void* ws, const void* xt, const 
   const size_t off_ls = cv.take((size_t)tokens * 4u);
   const size_t off_lt = cv.take((size_t)tokens * 4u);
   const size_t off_per = cv.take(mean ? (size_t)tokens * 4u : 0u);
-  const size_t off_mean = cv.take((size_t)((tokens + lce::kRowThreads - 1) / lce::kRowThreads) * 8u);
   const size_t zbytes = (size_t)plan.chunk * (size_t)plan.ld * 4u;
   const size_t off_zs = cv.take(zbytes);
   const size_t off_zt = cv.take(zbytes);
@@ -186,6 +208,9 @@ lce_status run_jsd_stored(const void* xs, const void* ws, const void* xt, const 
   }
   char* base = nullptr;
   if ((s = get_scratch(stream, need, &base)) != LCE_OK) return s;
+  MeanState ms;
+  if (mean && (s = get_mean_state(stream, (tokens + lce::kRowThreads - 1) / lce::kRowThreads, &ms)) != LCE_OK)
+    return s;
   float* lse_s = (float*)(base + off_ls);
   float* lse_t = (float*)(base + off_lt);
   float* per = mean ? (float*)(base + off_per) : out;
@@ -214,11 +239,12 @@ lce_status run_jsd_stored(const void* xs, const void* ws, const void* xt, const 
     r.dst = per + c0;
     hipError_t e = lce::launch_jsd_rows(r, stream);
     if (e != hipSuccess) return hip_fail(e, "kernel launch");
+    note_launch("jsd_stored_rows_kernel grid %lld x 256", (long long)n);
   }
   if (mean) {
-    hipError_t e = lce::launch_jsd_mean(tokens, per, out, (uint64_t*)(base + off_mean),
-                                        (unsigned*)base, stream);
+    hipError_t e = lce::launch_jsd_mean(tokens, per, out, ms.slots, ms.ticket, stream);
     if (e != hipSuccess) return hip_fail(e, "kernel launch");
+    note_launch("fused_jsd_merge_kernel (mean)");
   }
   return LCE_OK;
 }
@@ -245,7 +271,6 @@ lce_status run_jsd_recompute(const void* xs, const void* ws, const void* xt, con
   const size_t off_ls = cv.take((size_t)tokens * 4u);
   const size_t off_lt = cv.take((size_t)tokens * 4u);
   const size_t off_part = cv.take((size_t)a.segments * (size_t)tokens * 4u);
-  const size_t off_mean = cv.take((size_t)((tokens + lce::kRowThreads - 1) / lce::kRowThreads) * 8u);
   const size_t reserved = cv.off - Carve().off;
   const FusedPlan fp = plan_fused(tokens, vocab, cus, reserved);
   char* base = nullptr;
@@ -255,8 +280,13 @@ lce_status run_jsd_recompute(const void* xs, const void* ws, const void* xt, con
   a.lse_s = lse_s;
   a.lse_t = lse_t;
   a.partials = (float*)(base + off_part);
-  a.mean_slots = (uint64_t*)(base + off_mean);
-  a.ticket = (unsigned*)base;
+  if (mean) {
+    MeanState ms;
+    if ((s = get_mean_state(stream, (tokens + lce::kRowThreads - 1) / lce::kRowThreads, &ms)) != LCE_OK)
+      return s;
+    a.mean_slots = ms.slots;
+    a.ticket = ms.ticket;
+  }
 
   if ((s = run_fused(xs, ws, tokens, hidden, vocab, nullptr, false, nullptr, stream, reserved,
                      lse_s)) != LCE_OK)
@@ -266,6 +296,8 @@ lce_status run_jsd_recompute(const void* xs, const void* ws, const void* xt, con
     return s;
   hipError_t e = lce::launch_jsd(a, stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  note_launch("fused_jsd_partial_kernel grid %lld x 512 + fused_jsd_merge_kernel",
+              (long long)((tokens + 127) / 128 * a.segments));
   return LCE_OK;
 }
 
@@ -280,7 +312,7 @@ lce_status lce_fused_linear_jsd_fwd(const void* student_x, const void* student_w
                                     const void* teacher_x, const void* teacher_weight,
                                     int64_t tokens, int64_t hidden, int64_t vocab, float beta,
                                     lce_reduction reduction, float* out, hipStream_t stream) {
-  last_error().clear();
+  begin_call();
   lce_status s = validate_common(tokens, nullptr, (int)reduction, out, "out", false);
   if (s != LCE_OK) return s;
   const uint64_t ob = out_bytes(tokens, (int)reduction);
@@ -312,7 +344,7 @@ lce_status lce_fused_linear_xent_bwd(const void* x, const void* weight, int64_t 
                                      int64_t hidden, int64_t vocab, const int64_t* target,
                                      lce_reduction reduction, const float* grad, float* dx,
                                      float* dweight, hipStream_t stream) {
-  last_error().clear();
+  begin_call();
   lce_status s = validate_common(tokens, target, (int)reduction, nullptr, nullptr);
   if (s != LCE_OK) return s;
   if ((s = validate_head(x, weight, tokens, hidden, vocab, nullptr, 0)) != LCE_OK) return s;

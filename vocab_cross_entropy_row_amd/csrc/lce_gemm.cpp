@@ -110,6 +110,7 @@ lce_status gemm_bf16_f32(hipblasOperation_t ta, hipblasOperation_t tb, int64_t m
   hipblasStatus_t st = hipblasLtMatmul(h, plan.desc, &alpha, A, plan.a, B, plan.b, &beta, D, plan.d,
                                        D, plan.d, &plan.algo, ws, plan.ws, stream);
   if (st != HIPBLAS_STATUS_SUCCESS) return blas_fail(st, "matmul");
+  note_launch("hipBLASLt GEMM m %lld n %lld k %lld", (long long)m, (long long)n, (long long)k);
   return LCE_OK;
 }
 

@@ -34,6 +34,25 @@ lce_status fail(lce_status s, const char* fmt, ...) {
   return s;
 }
 
+thread_local std::string g_last_launch;
+
+std::string& last_launch() { return g_last_launch; }
+
+void note_launch(const char* fmt, ...) {
+  char buf[256];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  if (!g_last_launch.empty()) g_last_launch += " + ";
+  g_last_launch += buf;
+}
+
+void begin_call() {
+  g_last_error.clear();
+  g_last_launch.clear();
+}
+
 lce_status hip_fail(hipError_t e, const char* what) {
   return fail(LCE_ERR_HIP, "%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
 }
@@ -48,28 +67,26 @@ bool overlaps(const void* a, uint64_t an, const void* b, uint64_t bn) {
 bool aligned(const void* p, uint64_t n) { return ((uintptr_t)p % n) == 0; }
 
 // ------------------------------------------------------------ scratch pool
-// One grow-only device buffer per (device, stream).  A buffer that is outgrown
-// is retired, not freed: launches already queued, or recorded into a HIP graph
-// that may be replayed later, keep pointing at it.  Every buffer lives until
-// process exit.  Layout: the mean's ticket counters first (kTicketBytes, zero
-// between calls), then 256-byte-aligned regions carved by Carve.
+// Grow-only device buffers per (device, stream): general scratch, carved into
+// regions by Carve, and the deterministic mean's state (tickets, epoch and
+// slots), which nothing else writes.  A buffer that is outgrown is retired,
+// not freed: launches already queued, or recorded into a HIP graph that may be
+// replayed later, keep pointing at it.  Every buffer lives until process exit.
+// A new buffer is zeroed whole.
 struct Scratch {
   void* ptr = nullptr;
   size_t bytes = 0;
 };
 std::mutex g_mu;
 std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
+std::map<std::pair<int, hipStream_t>, Scratch> g_mean;
 std::vector<void*> g_retired;
 std::map<int, int> g_num_cus;
 
-
-lce_status get_scratch(hipStream_t stream, size_t need, char** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  std::lock_guard<std::mutex> lock(g_mu);
-  Scratch& s = g_scratch[{dev, stream}];
+// Grows `s` (the buffer of `stream`) to at least `need` bytes; call with g_mu held.
+static lce_status grow(Scratch& s, hipStream_t stream, size_t need) {
   if (s.bytes < need) {
+    hipError_t e = hipSuccess;
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     e = hipStreamIsCapturing(stream, &cap);
     if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
@@ -86,7 +103,8 @@ lce_status get_scratch(hipStream_t stream, size_t need, char** out) {
       return fail(LCE_ERR_OOM, "hipMalloc of %zu bytes of scratch failed: %s", bytes, hipGetErrorName(e));
     }
     // Ticket counters, epoch and mean slots must start at zero (kernels leave
-    // the counters at zero; a slot only ever holds tags of earlier launches).
+    // the counters at zero; a slot then only ever holds tags of earlier
+    // launches on this buffer).
     e = lce::launch_zero_u32((unsigned*)p, (int64_t)(bytes / sizeof(unsigned)), stream);
     if (e != hipSuccess) {
       (void)hipFree(p);
@@ -96,7 +114,32 @@ lce_status get_scratch(hipStream_t stream, size_t need, char** out) {
     s.ptr = p;
     s.bytes = bytes;
   }
+  return LCE_OK;
+}
+
+lce_status get_scratch(hipStream_t stream, size_t need, char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_mu);
+  Scratch& s = g_scratch[{dev, stream}];
+  lce_status st = grow(s, stream, need);
+  if (st != LCE_OK) return st;
   *out = (char*)s.ptr;
+  return LCE_OK;
+}
+
+lce_status get_mean_state(hipStream_t stream, int64_t nslots, MeanState* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_mu);
+  Scratch& s = g_mean[{dev, stream}];
+  const size_t off_slots = round_up(lce::kTicketBytes, kAlign);
+  lce_status st = grow(s, stream, off_slots + (size_t)(nslots > 0 ? nslots : 1) * 8u);
+  if (st != LCE_OK) return st;
+  out->ticket = (unsigned*)s.ptr;
+  out->slots = (uint64_t*)((char*)s.ptr + off_slots);
   return LCE_OK;
 }
 
@@ -164,6 +207,14 @@ lce_status validate_xent(const void* logits, int dtype, int64_t tokens, int64_t 
     return fail(LCE_ERR_INVALID_ARG, "tokens * vocab overflows");
   if (logits && !aligned(logits, (uint64_t)esize))
     return fail(LCE_ERR_INVALID_ARG, "logits is not aligned to its element size");
+  // The row kernels launch one wave (64 work-items) per row, or a 256-thread
+  // workgroup per row for rows longer than 32 KiB; a dispatch counts its
+  // work-items in 32 bits.
+  const int64_t per_row = vocab * esize > 32 * 1024 ? lce::kRowThreads : 64;
+  if (tokens > lce::kMaxGridItems / per_row)
+    return fail(LCE_ERR_UNSUPPORTED,
+                "tokens * %lld work-items per row must be < 2^32 (got %lld tokens)",
+                (long long)per_row, (long long)tokens);
   if (!out_name) return LCE_OK;
   const uint64_t ob = out_bytes(tokens, reduction) * (uint64_t)out_elems;
   if (overlaps(out, ob, logits, (uint64_t)(tokens * vocab * esize)))
@@ -196,6 +247,11 @@ lce_status validate_head(const void* x, const void* w, int64_t tokens, int64_t h
     return fail(LCE_ERR_UNSUPPORTED, "%s and %s must be 16-byte aligned", xn, wn);
   if (vocab > INT64_MAX / (hidden * 2) || tokens > INT64_MAX / (hidden * 2))
     return fail(LCE_ERR_INVALID_ARG, "tensor size overflows");
+  // The projection kernels launch up to 4 work-items per token per vocab
+  // segment (a dispatch counts its work-items in 32 bits).
+  if (tokens >= (int64_t(1) << 30))
+    return fail(LCE_ERR_UNSUPPORTED, "tokens must be < 2^30 for the fused projection (got %lld)",
+                (long long)tokens);
   if (overlaps(out, ob, x, (uint64_t)(tokens * hidden * 2))) return fail(LCE_ERR_ALIAS, "out overlaps %s", xn);
   if (overlaps(out, ob, w, (uint64_t)(vocab * hidden * 2))) return fail(LCE_ERR_ALIAS, "out overlaps %s", wn);
   return LCE_OK;

@@ -14,6 +14,14 @@ constexpr int kRowThreads = 256;  // threads per workgroup of the row kernels
 // finish_mean in lce_device.h).
 constexpr size_t kTicketBytes = 66 * 256;
 
+// A dispatch counts its work-items in 32 bits, so blocks * threads must stay
+// below 2^32.  Launchers check it (hipErrorInvalidConfiguration); the entry
+// points refuse such sizes first, with LCE_ERR_UNSUPPORTED.
+constexpr int64_t kMaxGridItems = (int64_t(1) << 32) - 1;
+inline bool grid_fits(int64_t blocks, int64_t threads) {
+  return blocks >= 0 && blocks <= kMaxGridItems / threads;
+}
+
 enum class XentPath : int { WaveRows = 0, BlockRows = 1, Split = 2 };
 
 struct XentArgs {

@@ -28,6 +28,7 @@ hipError_t launch_seq_logprob_sums(const float* loss, int64_t batch, int64_t seq
                                    hipStream_t st) {
   constexpr int kWaves = kRowThreads / 64;
   const int64_t blocks = (batch + kWaves - 1) / kWaves;
+  if (!grid_fits(blocks, kRowThreads)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(seq_logprob_sum_kernel, dim3((unsigned)blocks), dim3(kRowThreads), 0, st, loss,
                      batch, seq, out);
   return hipGetLastError();

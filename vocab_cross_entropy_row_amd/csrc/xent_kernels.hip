@@ -275,26 +275,34 @@ hipError_t launch_stats_merge(const float* stats, int64_t shards, int64_t tokens
                               const int64_t* target, int64_t vocab, float* out, int reduce_mean,
                               uint64_t* slots, unsigned* ticket, hipStream_t st) {
   const int64_t blocks = (tokens + kRowThreads - 1) / kRowThreads;
+  if (!grid_fits(blocks, kRowThreads)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(xent_stats_merge_kernel, dim3((unsigned)blocks), dim3(kRowThreads), 0, st, stats,
                      (int)shards, tokens, target, vocab, out, slots, ticket, reduce_mean);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------ small utilities
+// Grid-stride fills: any n (a zero-filled dweight can exceed 2^32 elements).
 __global__ void fill_f32_kernel(float* p, int64_t n, float v) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = v;
+  const int64_t step = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += step) p[i] = v;
 }
 
 __global__ void zero_u32_kernel(unsigned* p, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0u;
+  const int64_t step = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += step) p[i] = 0u;
+}
+
+static unsigned fill_blocks(int64_t n) {
+  const int64_t b = (n + 255) / 256;
+  return (unsigned)(b < 65536 ? b : 65536);
 }
 
 // ------------------------------------------------------------ launchers
 template <typename T, int U, int WAVES>
 static hipError_t launch_wave_rows_w(const XentArgs& a, hipStream_t st) {
   const int64_t blocks = (a.tokens + WAVES - 1) / WAVES;
+  if (!grid_fits(blocks, 64 * WAVES)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((xent_wave_rows_kernel<T, U, WAVES>), dim3((unsigned)blocks), dim3(64 * WAVES),
                      0, st, (const T*)a.logits, a.tokens, (int)a.vocab, a.target, a.vocab_start,
                      a.stats, a.out, a.mean_slots, a.ticket, a.reduce_mean);
@@ -312,6 +320,7 @@ static hipError_t launch_wave_rows(const XentArgs& a, hipStream_t st) {
 
 template <typename T, int U>
 static hipError_t launch_block_rows(const XentArgs& a, hipStream_t st) {
+  if (!grid_fits(a.tokens, kRowThreads)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((xent_block_rows_kernel<T, U>), dim3((unsigned)a.tokens), dim3(kRowThreads), 0,
                      st, (const T*)a.logits, a.tokens, (int)a.vocab, a.target, a.vocab_start,
                      a.stats, a.out, a.mean_slots, a.ticket, a.reduce_mean);
@@ -320,6 +329,9 @@ static hipError_t launch_block_rows(const XentArgs& a, hipStream_t st) {
 
 template <typename T, int U>
 static hipError_t launch_split(const XentArgs& a, hipStream_t st) {
+  if (a.tokens > 65535 || !grid_fits(a.splits, kRowThreads) ||
+      !grid_fits((a.tokens + kRowThreads / 64 - 1) / (kRowThreads / 64), kRowThreads))
+    return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((xent_split_partial_kernel<T, U>), dim3((unsigned)a.splits, (unsigned)a.tokens),
                      dim3(kRowThreads), 0, st, (const T*)a.logits, (int)a.vocab,
                      a.chunks_per_split, (float2*)a.split_partials);
@@ -358,13 +370,13 @@ hipError_t launch_xent(const XentArgs& a, hipStream_t st) {
 
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t st) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fill_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n, v);
+  hipLaunchKernelGGL(fill_f32_kernel, dim3(fill_blocks(n)), dim3(256), 0, st, p, n, v);
   return hipGetLastError();
 }
 
 hipError_t launch_zero_u32(unsigned* p, int64_t n, hipStream_t st) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n);
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(fill_blocks(n)), dim3(256), 0, st, p, n);
   return hipGetLastError();
 }
 
