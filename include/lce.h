@@ -137,6 +137,31 @@ LCE_API lce_status lce_xent_fwd(const void* logits, lce_dtype dtype, int64_t tok
                         hipStream_t stream);
 
 /*
+ * lce_xent_fwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, kernels, path selection, results (bitwise) and errors as
+ * lce_xent_fwd, but the call makes no hipMalloc or hipFree and uses no
+ * allocating library routine: its scratch (the mean's ticket counters and
+ * per-workgroup slots, the split path's partials) lives in one static 8 MiB
+ * device array per GPU, held until the process ends.
+ *
+ * Limits: with LCE_REDUCTION_MEAN at most 2^19 workgroup slots (a mean over
+ * at most 2^23 rows), and the split path's partials (8 bytes per row and
+ * slice) within 4 MiB; a call beyond them returns LCE_ERR_UNSUPPORTED before
+ * anything but the first call's clear is enqueued.
+ *
+ * Every call on a GPU shares that GPU's array, and the array keeps the last
+ * call's contents between calls: calls that overlap on one GPU (concurrent
+ * streams, threads or graph replays) race and must be serialised by the
+ * caller.  The first call on a GPU also clears the array's counters with a
+ * kernel on `stream` (when that call is being captured into a HIP graph, the
+ * clear is captured too and the next uncaptured call clears again).
+ */
+LCE_API lce_status lce_xent_fwd_noalloc(const void* logits, lce_dtype dtype, int64_t tokens,
+                                        int64_t vocab, const int64_t* target,
+                                        lce_reduction reduction, float* out, hipStream_t stream);
+
+/*
  * Gradient of the cross-entropy with respect to the logits (the backward
  * step of lce_xent_fwd).  The pages give the forward only; this is its
  * derivative, softmax minus the one-hot target:

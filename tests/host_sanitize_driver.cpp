@@ -44,6 +44,9 @@ int call(const std::string& fn, const Args& a) {
   if (fn == "lce_xent_fwd" && k == 7)
     return lce_xent_fwd(a.p(0), (lce_dtype)a.e(1), a.n(2), a.n(3), (const int64_t*)a.p(4),
                         (lce_reduction)a.e(5), (float*)a.p(6), nullptr);
+  if (fn == "lce_xent_fwd_noalloc" && k == 7)
+    return lce_xent_fwd_noalloc(a.p(0), (lce_dtype)a.e(1), a.n(2), a.n(3), (const int64_t*)a.p(4),
+                                (lce_reduction)a.e(5), (float*)a.p(6), nullptr);
   if (fn == "lce_fused_linear_xent_fwd" && k == 8)
     return lce_fused_linear_xent_fwd(a.p(0), a.p(1), a.n(2), a.n(3), a.n(4), (const int64_t*)a.p(5),
                                      (lce_reduction)a.e(6), (float*)a.p(7), nullptr);

@@ -90,6 +90,24 @@ def test_xent_argument_errors(lib, kw, status, needle):
     assert needle in lce.lce_last_error()
 
 
+def _xent_noalloc(logits=FAKE, dtype=lce.LCE_F32, tokens=16, vocab=32, target=FAKE + (1 << 20),
+                  reduction=lce.LCE_REDUCTION_NONE, out=FAKE + (2 << 20)):
+    return lce.lce_xent_fwd_noalloc(logits, dtype, tokens, vocab, target, reduction, out, 0)
+
+
+@pytest.mark.parametrize("kw,status,needle", XENT_CASES)
+def test_xent_noalloc_argument_errors(lib, kw, status, needle):
+    # the allocation-free variant validates exactly as lce_xent_fwd
+    assert _xent_noalloc(**kw) == status
+    assert needle in lce.lce_last_error()
+    assert lce.lce_last_launch() == ""
+
+
+def test_xent_noalloc_empty_none_is_a_no_op(lib):
+    assert lce.lce_xent_fwd_noalloc(0, lce.LCE_BF16, 0, 32, 0, lce.LCE_REDUCTION_NONE, 0, 0) == lce.LCE_OK
+    assert lce.lce_last_error() == ""
+
+
 def test_xent_bf16_alignment_is_two_bytes(lib):
     # bf16 logits only need 2-byte alignment; an odd address is rejected.
     assert _xent(logits=FAKE + 1, dtype=lce.LCE_BF16) == lce.LCE_ERR_INVALID_ARG

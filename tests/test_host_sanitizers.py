@@ -19,6 +19,7 @@ from vocab_cross_entropy_row_amd import build as lce_build
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HOST_SOURCES = ["lce_api.cpp", "lce_host.cpp", "lce_gemm.cpp", "lce_fused_paths.cpp"]
+# noalloc.hip holds a device array and its entry point in one file: it is linked as built
 KERNEL_SOURCES = [s for s in lce_build.SOURCES if s.endswith(".hip")]
 OUT = os.path.join(ROOT, "_build", "host_sanitize")
 
@@ -81,6 +82,7 @@ def _line(fn_name, helper, kw, status, needle):
 
 CASE_TABLES = [
     ("lce_xent_fwd", abi._xent, abi.XENT_CASES),
+    ("lce_xent_fwd_noalloc", abi._xent_noalloc, abi.XENT_CASES),
     ("lce_fused_linear_xent_fwd", abi._fused, abi.FUSED_CASES),
     ("lce_xent_partial_fwd", abi._partial, abi.PARTIAL_CASES),
     ("lce_xent_merge", abi._merge, abi.MERGE_CASES),
@@ -93,6 +95,7 @@ CASE_TABLES = [
 # Empty calls that are no-ops: status LCE_OK and an empty detail message.
 EMPTY = [
     "lce_xent_fwd 0 7 0 0 0 32 0 1 0 ",
+    "lce_xent_fwd_noalloc 0 7 0 1 0 32 0 1 0 ",
     "lce_xent_partial_fwd 0 7 0 1 0 8 0 0 0 ",
     "lce_xent_merge 0 7 0 3 0 0 10 1 0 ",
     "lce_xent_bwd 0 8 0 0 0 8 0 1 0 0 ",

@@ -5,6 +5,7 @@ sizes, enum values, a ``hipStream_t`` as an integer) and return the ``lce_status
 code:
 
 * :func:`lce_xent_fwd`, :func:`lce_fused_linear_xent_fwd`
+* :func:`lce_xent_fwd_noalloc` (lce_xent_fwd with static scratch: allocates nothing)
 * :func:`lce_xent_bwd` (gradient with respect to the logits)
 * :func:`lce_fused_linear_logprob_sums` (per-sequence target log-probability sums)
 * :func:`lce_xent_partial_fwd`, :func:`lce_xent_merge` (vocab split across devices)
@@ -37,7 +38,7 @@ LCE_ERR_ALIAS = 3
 LCE_ERR_OOM = 4
 LCE_ERR_HIP = 5
 
-EXPORTED = ("lce_xent_fwd", "lce_xent_bwd", "lce_fused_linear_xent_fwd", "lce_fused_linear_xent_bwd",
+EXPORTED = ("lce_xent_fwd", "lce_xent_fwd_noalloc", "lce_xent_bwd", "lce_fused_linear_xent_fwd", "lce_fused_linear_xent_bwd",
             "lce_fused_linear_logprob_sums", "lce_fused_linear_jsd_fwd", "lce_xent_partial_fwd",
             "lce_xent_merge", "lce_status_string", "lce_last_error", "lce_last_launch",
             "lce_version")
@@ -67,6 +68,8 @@ def load() -> ctypes.CDLL:
     lib.lce_xent_fwd.restype = ctypes.c_int
     lib.lce_xent_fwd.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
                                  ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.lce_xent_fwd_noalloc.restype = ctypes.c_int
+    lib.lce_xent_fwd_noalloc.argtypes = lib.lce_xent_fwd.argtypes
     lib.lce_fused_linear_xent_fwd.restype = ctypes.c_int
     lib.lce_fused_linear_xent_fwd.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                               ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
@@ -115,6 +118,12 @@ def lce_xent_fwd(logits: int, dtype: int, tokens: int, vocab: int, target: int,
                  reduction: int, out: int, stream: int) -> int:
     return load().lce_xent_fwd(logits or None, dtype, tokens, vocab, target or None, reduction,
                                out or None, stream or None)
+
+
+def lce_xent_fwd_noalloc(logits: int, dtype: int, tokens: int, vocab: int, target: int,
+                         reduction: int, out: int, stream: int) -> int:
+    return load().lce_xent_fwd_noalloc(logits or None, dtype, tokens, vocab, target or None,
+                                       reduction, out or None, stream or None)
 
 
 def lce_fused_linear_xent_fwd(x: int, weight: int, tokens: int, hidden: int, vocab: int,

@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblce.so")
 
 SOURCES = ["lce_api.cpp", "lce_host.cpp", "lce_gemm.cpp", "lce_fused_paths.cpp", "xent_kernels.hip", "fused_kernel.hip", "bwd_kernels.hip", "seq_kernels.hip",
-           "jsd_kernel.hip", "fused_grad_kernel.hip"]
+           "jsd_kernel.hip", "fused_grad_kernel.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 
