@@ -77,6 +77,8 @@ def _cases():
         _row_case(104, 300, 9001, "bf16", "none", {"LCE_PATH": "block"}),
         _row_case(105, 40, 70001, "f32", "mean", {"LCE_PATH": "split"}),
         _row_case(106, 23, 50000, "bf16", "none", {"LCE_PATH": "split"}),
+        _row_case(112, 300, 70001, "f32", "mean", {"LCE_PATH": "split", "LCE_SPLITS": 9}),
+        _row_case(113, 256, 131072, "f32", "mean", {}),
         _fused_case(107, 300, 128, 3000, "mean", {}),
         _fused_case(108, 130, 256, 1500, "none", {"LCE_FUSED_SEGMENTS": 3}),
     ]

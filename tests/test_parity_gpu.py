@@ -89,7 +89,8 @@ def test_small_auto_path(dtype, rows, vocab):
 
 
 @pytest.mark.parametrize("path,extra", [("wave", {}), ("block", {}), ("split", {}),
-                                        ("split", {"LCE_SPLITS": 3}), ("split", {"LCE_SPLITS": 7})])
+                                        ("split", {"LCE_SPLITS": 3}), ("split", {"LCE_SPLITS": 7}),
+                                        ("split", {"LCE_SPLITS": 41})])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("rows,vocab", [(6, 3), (11, 777), (9, 4099), (4, 33333), (2, 70001)])
 def test_forced_paths(path, extra, dtype, rows, vocab):

@@ -59,7 +59,7 @@ def _check_stats(got, want, label):
     assert np.all(got[~finite, 1] == 0.0)
 
 
-@pytest.mark.parametrize("path", ["auto", "wave", "block", "split"])
+@pytest.mark.parametrize("path", ["auto", "wave", "block", "split", "split_many"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("rows,shard,start", [(37, 1000, 0), (64, 4099, 12345), (5, 20001, 7),
                                               (130, 129, 999)])
@@ -68,6 +68,8 @@ def test_partial_matches_oracle(path, dtype, rows, shard, start):
     t = lce_synth.targets(rows, rows, start + shard + 50)  # some targets past this shard
     t[:3] = (start, start + shard - 1, -5)                 # both ends, and an invalid one
     env = {} if path == "auto" else {"LCE_PATH": path}
+    if path == "split_many":  # many slices per row: more partials per merged row
+        env = {"LCE_PATH": "split", "LCE_SPLITS": 37}
     with forced_env(**env):
         got = lce.xent_partial(to_dev(z), torch.from_numpy(t).cuda(), start)
     torch.cuda.synchronize()

@@ -110,10 +110,13 @@ lce_status run_rows(const void* logits, int dtype, int64_t tokens, int64_t vocab
     a.chunks_per_split = (int)((nvec + S - 1) / S);
     need_split = (size_t)tokens * (size_t)S * 8u;
   }
+  // The split path's target logits follow its partials.
+  const size_t off_zt_rel = round_up(need_split, kAlign);
+  if (need_split) need_split = off_zt_rel + (size_t)tokens * 4u;
   const int64_t mean_blocks =
       (a.path == lce::XentPath::BlockRows) ? tokens
       : (a.path == lce::XentPath::WaveRows) ? (tokens + a.waves_per_block - 1) / a.waves_per_block
-                                              : (tokens + lce::kRowThreads / 64 - 1) / (lce::kRowThreads / 64);
+                                              : (tokens + lce::kRowThreads - 1) / lce::kRowThreads;
 
   if (ws) {  // the caller's memory: nothing is allocated
     if (need_split > ws->general_bytes)
@@ -124,6 +127,7 @@ lce_status run_rows(const void* logits, int dtype, int64_t tokens, int64_t vocab
       return fail(LCE_ERR_UNSUPPORTED, "the mean needs %lld workgroup slots; the workspace holds %lld",
                   (long long)mean_blocks, (long long)ws->max_slots);
     a.split_partials = (float*)ws->general;
+    a.split_zt = (float*)(ws->general + off_zt_rel);
     a.ticket = ws->ticket;
     a.mean_slots = ws->slots;
   } else {
@@ -133,6 +137,7 @@ lce_status run_rows(const void* logits, int dtype, int64_t tokens, int64_t vocab
     char* base = nullptr;
     if ((s = get_scratch(stream, cv.off, &base)) != LCE_OK) return s;
     a.split_partials = (float*)(base + off_split);
+    a.split_zt = (float*)(base + off_split + off_zt_rel);
     if (mean) {
       MeanState ms;
       if ((s = get_mean_state(stream, mean_blocks, &ms)) != LCE_OK) return s;
@@ -151,9 +156,9 @@ lce_status run_rows(const void* logits, int dtype, int64_t tokens, int64_t vocab
   else if (a.path == lce::XentPath::BlockRows)
     note_launch("xent_block_rows_kernel<%s, 8> grid %lld x %d", tn, (long long)tokens, lce::kRowThreads);
   else
-    note_launch("xent_split_partial_kernel<%s, 8> grid (%d, %lld) x %d + xent_split_merge_kernel<%s> "
-                "grid %lld x %d", tn, a.splits, (long long)tokens, lce::kRowThreads, tn,
-                (long long)((tokens + 3) / 4), lce::kRowThreads);
+    note_launch("xent_split_partial_kernel<%s, 8> grid (%d, %lld) x %d + xent_split_merge_kernel "
+                "grid %lld x %d", tn, a.splits, (long long)tokens, lce::kRowThreads,
+                (long long)((tokens + lce::kRowThreads - 1) / lce::kRowThreads), lce::kRowThreads);
   return LCE_OK;
 }
 

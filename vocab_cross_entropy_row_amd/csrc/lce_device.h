@@ -173,6 +173,10 @@ __device__ __forceinline__ void finish_mean(float block_sum, uint64_t* slots, un
   if (threadIdx.x >= 64) return;
   const unsigned lane = threadIdx.x;
   const unsigned nblocks = gridDim.x * gridDim.y;
+  if (nblocks == 1) {  // the only workgroup: no hand-off (same result as the general path)
+    if (lane == 0) out[0] = block_sum / (float)tokens;
+    return;
+  }
   const unsigned bid = blockIdx.y * gridDim.x + blockIdx.x;
   const unsigned G = nblocks < (unsigned)kTicketGroups ? nblocks : (unsigned)kTicketGroups;
   const unsigned g = bid % G;

@@ -39,7 +39,8 @@ struct XentArgs {
   int waves_per_block;      // WaveRows: rows (waves) per workgroup, 4 or 16 (then unroll <= 8)
   int splits;               // Split: workgroups per row
   int chunks_per_split;     // Split: 16-byte chunks per workgroup
-  float* split_partials;    // Split: tokens * splits (max, sum-exp) pairs
+  float* split_partials;    // Split: splits * tokens (max, sum-exp) pairs, slice-major
+  float* split_zt;          // Split: tokens target logits (NaN where not held)
   uint64_t* mean_slots;     // one 64-bit (tag, partial) slot per workgroup of the last kernel
   unsigned* ticket;         // counters zero before the launch and after it; epoch word
 };

@@ -155,18 +155,30 @@ __global__ __launch_bounds__(kRowThreads) void xent_block_rows_kernel(
 
 // ------------------------------------------------------------ split rows
 // grid = (S, tokens).  Workgroup (s, row) streams chunk slice s of the row and
-// writes its state to part[row * S + s]; slice 0 also folds the scalar edges.
+// writes its state to part[s * tokens + row]; slice 0 also folds the scalar
+// edges, and loads the target logit right behind its first batch (its latency
+// hides under the stream) and writes it to zt[row], NaN when these columns do
+// not hold the target.  The merge then needs no dependent load.
 template <typename T, int U>
 __global__ __launch_bounds__(kRowThreads) void xent_split_partial_kernel(
-    const T* __restrict__ logits, int vocab, int chunks_per_slice, float2* __restrict__ part) {
-  const int S = gridDim.x;
+    const T* __restrict__ logits, int vocab, int chunks_per_slice, const int64_t* __restrict__ target,
+    int64_t vocab_start, float2* __restrict__ part, float* __restrict__ zt_out) {
   const int s = blockIdx.x;
+  const int64_t tokens = gridDim.y;
   const int64_t row = blockIdx.y;
   const T* rp = logits + row * (int64_t)vocab;
+  const int64_t t = (s == 0) ? target[row] : -1;
   const RowSplit rs = row_split(rp, vocab);
   const typename Vec<T>::raw* body = reinterpret_cast<const typename Vec<T>::raw*>(rp + rs.head);
-  float edge = 0.0f;
-  auto extra = [&]() { edge = Vec<T>::scalar(rp + edge_index(rs, vocab, threadIdx.x)); };
+  float edge = 0.0f, zt = 0.0f;
+  int64_t tt = -1;
+  auto extra = [&]() {
+    edge = Vec<T>::scalar(rp + edge_index(rs, vocab, threadIdx.x));
+    if (s == 0) {
+      tt = local_target(target_here(t), vocab_start, vocab);
+      zt = Vec<T>::scalar(rp + safe_target(tt, vocab));
+    }
+  };
   Lse st = lse_empty();
   const int c0 = s * chunks_per_slice;
   int c1 = c0 + chunks_per_slice;
@@ -174,47 +186,53 @@ __global__ __launch_bounds__(kRowThreads) void xent_split_partial_kernel(
   stream_chunks<T, U>(st, body, c0, c1, threadIdx.x, kRowThreads, extra);
   if (s == 0 && (int)threadIdx.x < rs.head + rs.tail) fold_one(st, edge);
   const Lse r = block_lse(st);
-  if (threadIdx.x == 0) part[row * S + s] = make_float2(r.m, r.s);
+  if (threadIdx.x == 0) {
+    part[s * tokens + row] = make_float2(r.m, r.s);
+    if (s == 0) zt_out[row] = tt >= 0 ? zt : __builtin_nanf("");
+  }
 }
 
-// One wave per row merges that row's S partials (lanes read them in order,
-// then the wave reduction), then finishes the loss.
-template <typename T>
+// One thread per row: merge its S partials in slice order (consecutive
+// threads read consecutive rows of a slice; eight slices' loads in flight at
+// once, padding entries merging as exact no-ops), then finish the loss (NaN
+// for a NaN target logit: the target was invalid or outside these columns),
+// the shard statistics, or the mean.  Every load is independent of the
+// others, so the merge is one memory round trip before its stores.
 __global__ __launch_bounds__(kRowThreads) void xent_split_merge_kernel(
-    const T* __restrict__ logits, int64_t tokens, int vocab, int S,
-    const float2* __restrict__ part, const int64_t* __restrict__ target, int64_t vocab_start,
+    int64_t tokens, int S, const float2* __restrict__ part, const float* __restrict__ zt_in,
     float* __restrict__ stats, float* __restrict__ out, uint64_t* __restrict__ slots,
     unsigned* __restrict__ ticket, int reduce_mean) {
-  constexpr int kWaves = kRowThreads / 64;
-  const int lane = threadIdx.x & 63;
-  const int wave = wave_uniform(threadIdx.x >> 6);
-  const int64_t row = (int64_t)blockIdx.x * kWaves + wave;
+  const int64_t row = (int64_t)blockIdx.x * kRowThreads + threadIdx.x;
   float loss = 0.0f;
   if (row < tokens) {
+    constexpr int kGroup = 8;
     Lse st = lse_empty();
-    for (int i = lane; i < S; i += 64) {
-      const float2 p = part[row * S + i];
-      st = lse_merge(st, Lse{p.x, p.y});
+    const float zt = zt_in[row];
+    for (int s0 = 0; s0 < S; s0 += kGroup) {
+      float2 p[kGroup];
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j)
+        p[j] = (s0 + j < S) ? part[(int64_t)(s0 + j) * tokens + row] : make_float2(kNegInf, 0.0f);
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j) st = lse_merge(st, Lse{p[j].x, p[j].y});
     }
-    const Lse r = wave_lse(st);
-    const T* rp = logits + row * (int64_t)vocab;
-    const int64_t tt = local_target(target[row], vocab_start, vocab);
-    const float zt = Vec<T>::scalar(rp + safe_target(tt, vocab));
     if (stats) {
-      if (lane == 0) write_stats(stats + 3 * row, r, tt >= 0, zt);
+      write_stats(stats + 3 * row, st, true, zt);  // zt is NaN when these columns lack the target
     } else {
-      loss = (tt >= 0) ? lse_minus(r, zt) : __builtin_nanf("");
-      if (!reduce_mean && lane == 0) out[row] = loss;
+      loss = lse_minus(st, zt);
+      if (!reduce_mean) out[row] = loss;
     }
   }
   if (reduce_mean) {
-    __shared__ float wl[kWaves];
-    if (lane == 0) wl[wave] = loss;
+    __shared__ float red[kRowThreads];
+    red[threadIdx.x] = loss;
     __syncthreads();
-    float bsum = 0.0f;
-    if (threadIdx.x == 0)
-      for (int w = 0; w < kWaves; ++w) bsum += wl[w];
-    finish_mean(bsum, slots, ticket, out, tokens);
+#pragma unroll
+    for (int w = kRowThreads / 2; w > 0; w >>= 1) {
+      if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+      __syncthreads();
+    }
+    finish_mean(red[0], slots, ticket, out, tokens);
   }
 }
 
@@ -329,19 +347,17 @@ static hipError_t launch_block_rows(const XentArgs& a, hipStream_t st) {
 
 template <typename T, int U>
 static hipError_t launch_split(const XentArgs& a, hipStream_t st) {
-  if (a.tokens > 65535 || !grid_fits(a.splits, kRowThreads) ||
-      !grid_fits((a.tokens + kRowThreads / 64 - 1) / (kRowThreads / 64), kRowThreads))
-    return hipErrorInvalidConfiguration;
+  if (a.tokens > 65535 || !grid_fits(a.splits, kRowThreads)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((xent_split_partial_kernel<T, U>), dim3((unsigned)a.splits, (unsigned)a.tokens),
                      dim3(kRowThreads), 0, st, (const T*)a.logits, (int)a.vocab,
-                     a.chunks_per_split, (float2*)a.split_partials);
+                     a.chunks_per_split, a.target, a.vocab_start, (float2*)a.split_partials,
+                     a.split_zt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t blocks = (a.tokens + kRowThreads / 64 - 1) / (kRowThreads / 64);
-  hipLaunchKernelGGL((xent_split_merge_kernel<T>), dim3((unsigned)blocks), dim3(kRowThreads), 0, st,
-                     (const T*)a.logits, a.tokens, (int)a.vocab, a.splits,
-                     (const float2*)a.split_partials, a.target, a.vocab_start, a.stats, a.out,
-                     a.mean_slots, a.ticket, a.reduce_mean);
+  const int64_t blocks = (a.tokens + kRowThreads - 1) / kRowThreads;
+  hipLaunchKernelGGL(xent_split_merge_kernel, dim3((unsigned)blocks), dim3(kRowThreads), 0, st,
+                     a.tokens, a.splits, (const float2*)a.split_partials, (const float*)a.split_zt,
+                     a.stats, a.out, a.mean_slots, a.ticket, a.reduce_mean);
   return hipGetLastError();
 }
 
