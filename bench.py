@@ -617,7 +617,7 @@ PROBE_LIB = os.path.join(ROOT, "bench_probe.so")
 
 
 def build_probe() -> str:
-    """Compile bench_probe.so (gfx950) from bench_probe.hip, the measured-read-peak kernel."""
+    """Compile bench_probe.so (gfx950) from bench_probe.hip: the plain-read and VALU-rate probes."""
     import subprocess
     from vocab_cross_entropy_row_amd import build as B
     tmp = PROBE_LIB + ".tmp"
@@ -685,6 +685,39 @@ def time_stream_read(torch, head_bytes: int, head_replicas: int, steps: int) -> 
             "bytes_2GiB_us": round(us_big, 2), "gbs_2GiB": round((1 << 31) / (us_big * 1e-6) / 1e9, 1),
             "bytes": head_bytes, "replicas": head_replicas, "read_us": round(us_small, 3),
             "gbs": round(head_bytes / (us_small * 1e-6) / 1e9, 1)}
+
+
+def time_valu_rate(torch) -> dict:
+    """bench_probe's vector-arithmetic rates: 8 independent chains per lane of v_exp_f32,
+    of v_fma_f32 and of the bf16 row-fold step (decode, FMA, exponential, add) in 2048
+    workgroups of 256 threads (every wave slot of 256 CUs), each timed with events (median of
+    three launches after one untimed), as SIMD cycles per wave instruction (per element for
+    the fold step) at the 2.4 GHz datasheet clock."""
+    import ctypes
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.bench_valu_rate.restype = ctypes.c_int
+    lib.bench_valu_rate.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_void_p]
+    blocks, iters = 2048, 4096
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    steps_per_simd = blocks * 4 / 1024 * iters * 8  # 4 waves per workgroup, 1024 SIMDs
+    res = {}
+    for mode, name in ((0, "exp_f32"), (1, "fma_f32"), (2, "bf16_fold_step")):
+        s = torch.cuda.current_stream()
+        per = []
+        for _ in range(4):
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record(s)
+            rc = lib.bench_valu_rate(mode, out.data_ptr(), blocks, iters, s.cuda_stream)
+            t1.record(s)
+            if rc != 0:
+                raise RuntimeError(f"bench_valu_rate failed (hipError {rc})")
+            torch.cuda.synchronize()
+            per.append(t0.elapsed_time(t1) * 1e3)
+        us = statistics.median(per[1:])
+        res[name] = {"us": round(us, 1),
+                     "cycles_per_wave_instruction_at_2_4_GHz": round(us * 1e-6 * 2.4e9 / steps_per_simd, 2)}
+    return res
 
 
 # ------------------------------------------------------------------ HBM counter calibration
@@ -982,6 +1015,7 @@ def main(argv=None) -> int:
         probe = time_stream_read(torch, hb, results[pw.name]["replicas"], min(args.steps, 200))
         probe["workload"] = pw.name
         probe["kernel_us_over_read_only_us"] = round(results[pw.name]["us_per_step"] / probe["read_us"], 4)
+        probe["valu_rate"] = time_valu_rate(torch)
         print(f"[bench] streaming read: {probe['gbs_2GiB']} GB/s over 2 GiB, "
               f"{probe['read_us']:.2f} µs for {pw.name}'s {hb} logit bytes",
               file=sys.stderr, flush=True)

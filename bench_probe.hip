@@ -1,10 +1,15 @@
-// Streaming-read probe for bench.py (measurement only, not part of liblce).
+// Measurement probes for bench.py (not part of liblce).
 //
-// Reads a device buffer once with 16-byte nontemporal buffer loads, the loads
-// the row kernels stream logits with, and does nothing else with the data but
-// fold it into one register per lane.  Its rate is the measured read peak of
-// the part for that transfer size, which the row kernels' achieved bandwidth
-// is quoted against beside the 8 TB/s datasheet figure.
+// stream_read_kernel reads a device buffer once with 16-byte nontemporal buffer
+// loads, the loads the row kernels stream logits with, and does nothing else
+// with the data but fold it into one register per lane: what a plain read of a
+// workload's bytes costs, for comparison with the kernel that reads them (not
+// a peak: the long-row kernels read faster than it does).
+//
+// valu_rate_kernel times the vector arithmetic of the row fold: 8 independent
+// chains per lane of v_exp_f32, of v_fma_f32, or of the whole bf16 fold step
+// (decode one half of a 32-bit word, FMA, exponential, add), in a grid that
+// fills every wave slot.
 //
 // Build (done by __graft_entry__.build()):
 //   hipcc -O3 --offload-arch=gfx950 -Xclang -target-feature -Xclang -packed-fp32-ops
@@ -49,7 +54,56 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const void* src, 
   if (acc == 0x9e3779b9u) sink[0] = acc;  // keeps the loads live; a store almost never happens
 }
 
+// MODE 0: a = 2^a; 1: a = a * 0.999 + 1e-7; 2: a += 2^(z * log2(e) - 3) with z the high or
+// low bf16 half of a word that changes every step.  Each thread writes one value, so no
+// chain is dead code.
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void valu_rate_kernel(float* out, int iters, float seed) {
+  float a[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a[j] = seed * (float)(threadIdx.x + j) * 1e-6f;
+  uint32_t r = __float_as_uint(seed) ^ threadIdx.x;
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if constexpr (MODE == 0) {
+        a[j] = __builtin_amdgcn_exp2f(a[j]);
+      } else if constexpr (MODE == 1) {
+        a[j] = __builtin_fmaf(a[j], 0.999f, 1e-7f);
+      } else {
+        const uint32_t w = r + (uint32_t)j * 0x9e3779b9u;
+        const float z = (j & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+        a[j] += __builtin_amdgcn_exp2f(__builtin_fmaf(z, 1.442695f, -3.0f));
+      }
+    }
+    r += 0x7f4a7c15u;
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += a[j];
+  out[blockIdx.x * kThreads + threadIdx.x] = s;
+}
+
 }  // namespace
+
+// Enqueue one valu_rate_kernel<mode> launch of `blocks` workgroups of 256 threads, each
+// thread taking `iters` steps of its 8 chains; `out` holds blocks * 256 floats.  Returns a
+// hipError_t value: hipErrorInvalidValue for mode outside 0..2, blocks outside 1..65535 or
+// iters outside 1..2^20.
+extern "C" __attribute__((visibility("default"))) int bench_valu_rate(int mode, float* out,
+                                                                       int blocks, int iters,
+                                                                       hipStream_t stream) {
+  if (!out || mode < 0 || mode > 2 || blocks < 1 || blocks > 65535 || iters < 1 ||
+      iters > (1 << 20))
+    return (int)hipErrorInvalidValue;
+  if (mode == 0)
+    hipLaunchKernelGGL(valu_rate_kernel<0>, dim3(blocks), dim3(kThreads), 0, stream, out, iters, 0.5f);
+  else if (mode == 1)
+    hipLaunchKernelGGL(valu_rate_kernel<1>, dim3(blocks), dim3(kThreads), 0, stream, out, iters, 0.5f);
+  else
+    hipLaunchKernelGGL(valu_rate_kernel<2>, dim3(blocks), dim3(kThreads), 0, stream, out, iters, 0.5f);
+  return (int)hipGetLastError();
+}
 
 // Enqueue one read of `bytes` bytes at `src` (16-byte aligned, bytes a multiple of 16 and
 // at most 2^31) on `stream`.  `sink` is a 4-byte device buffer the kernel may write.

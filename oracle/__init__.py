@@ -302,6 +302,34 @@ def fused_linear_xent_grads(x_bits: np.ndarray, w_bits: np.ndarray, target: np.n
     return dx, dw
 
 
+def fused_linear_xent_dw_rows(x_bits: np.ndarray, w_bits: np.ndarray, target: np.ndarray,
+                              row_scale: np.ndarray, head_rows: np.ndarray, block: int = 128):
+    """Selected rows of the head gradient dW = dZ^T x, fp64, for per-token scales g_i.
+
+    The same derivative as ``fused_linear_xent_grads``, for a head too large to hold
+    all of dW or dZ in fp64: each block of tokens gets its full fp64 logits and their
+    logit gradient (``xent_bwd``, which needs every logit of the row for the softmax),
+    and only the columns of dZ for ``head_rows`` are kept.  Row r of the result is
+    sum_i dZ[i, head_rows[r]] x_i.  Returns ``(dw_rows [k, hidden], dz_cols [tokens, k])``.
+    """
+    x64_all = bf16_bits_to_f64(x_bits)
+    w64 = bf16_bits_to_f64(w_bits)
+    t = np.ascontiguousarray(target, dtype=np.int64).reshape(-1)
+    g = np.ascontiguousarray(row_scale, dtype=np.float64).reshape(-1)
+    sel = np.asarray(head_rows, dtype=np.int64).reshape(-1)
+    rows = x64_all.shape[0]
+    if t.size != rows or g.size != rows:
+        raise ValueError("oracle: target and row_scale must have one entry per row")
+    if sel.size and (sel.min() < 0 or sel.max() >= w64.shape[0]):
+        raise ValueError("oracle: head_rows outside the head")
+    dz_cols = np.empty((rows, sel.size), dtype=np.float64)
+    for b0 in range(0, rows, block):
+        z = np.matmul(x64_all[b0:b0 + block], w64.T)
+        dz = xent_bwd(z, t[b0:b0 + block], g[b0:b0 + block], reduction="none", dtype="f64")
+        dz_cols[b0:b0 + block] = dz[:, sel]
+    return np.matmul(dz_cols.T, x64_all), dz_cols
+
+
 def fused_linear_xent_bwd(x_bits: np.ndarray, w_bits: np.ndarray, target: np.ndarray, grad,
                           reduction: str = "mean"):
     """``(dx, dW)`` of the fused cross-entropy for the output gradient ``grad``: a scalar

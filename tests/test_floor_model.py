@@ -51,9 +51,10 @@ def test_bench_refuses_several_gpus():
 
 
 def test_stream_read_probe_exports():
-    """bench_probe.so (the measured-read-peak kernel bench.py reports) exports its one entry."""
+    """bench_probe.so (the plain-read and VALU-rate probes bench.py reports) exports both entries."""
     import ctypes
     if not os.path.exists(bench.PROBE_LIB):
         pytest.skip("bench_probe.so not built (__graft_entry__.build() builds it)")
     lib = ctypes.CDLL(bench.PROBE_LIB)
     assert hasattr(lib, "bench_stream_read")
+    assert hasattr(lib, "bench_valu_rate")

@@ -9,9 +9,10 @@ covers the fp32 accumulation and the fp32 softmax, plus 1e-7 absolute.  dW = dZ^
 the same bound with sum_t |dZ_tv x_th|.
 
 At the page shape (tokens 2048, hidden 4096, vocab 128256) the oracle checks dx on a
-sample of tokens; dW is checked through properties that hold at any size: its columns
-sum to ~0 (each row of dZ sums to 0), and mean reduction equals per-token reduction with
-gradient 1/tokens.
+sample of tokens and dW on a sample of head rows (each row needs every token's softmax,
+so the oracle takes all 2048 tokens' fp64 logits block by block); properties that hold
+at any size check the rest: the columns of dW sum to ~0 (each row of dZ sums to 0), and
+mean reduction equals per-token reduction with gradient 1/tokens.
 """
 import numpy as np
 import pytest
@@ -184,6 +185,12 @@ def test_page_shape_sampled_and_properties():
     want_dx, _ = oracle.fused_linear_xent_grads(xb[rows], wb, t[rows], scale, want_dw=False)
     bx, _ = _bounds(xb[rows], wb, t[rows], scale, want_dw=False)
     _check("dx rows", dx.cpu().numpy()[rows], want_dx, bx)
+    # Rows of dW against the oracle: the first and last head rows, two in the middle, and
+    # the rows of three tokens' targets (where the one-hot term enters the sum).
+    head = np.unique(np.r_[0:2, 64127:64129, w.vocab - 2:w.vocab, t[[0, 1023, 2047]]])
+    want_dw, dz_cols = oracle.fused_linear_xent_dw_rows(xb, wb, t, np.full(T, 1.0 / T), head)
+    bw = REL * (np.abs(dz_cols).T @ np.abs(oracle.bf16_bits_to_f64(xb))) + ABS
+    _check("dW rows", dw[torch.from_numpy(head).cuda()].cpu().numpy(), want_dw, bw)
 
 
 def test_graph_replays_match_eager():

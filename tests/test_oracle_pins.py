@@ -624,3 +624,50 @@ def test_fused_bwd_invariants(oracle_mod):
     dx3, dw3 = oracle_mod.fused_linear_xent_bwd(xb, wb, t, 2.0, "mean")
     assert np.isnan(dx3[3]).all() and np.isfinite(np.delete(dx3, 3, axis=0)).all()
     assert np.isnan(dw3).all()
+
+
+def test_fused_dw_rows_match_full_gradient_and_autograd(oracle_mod):
+    """Selected head rows of dW (any order, repeats, the targets' rows among them) equal the
+    rows of the full fp64 dW, and torch autograd's, for several token block sizes; their dZ
+    columns sum over the head rows to the full dZ's (catches a dropped one-hot, a column
+    taken from the wrong row, a block boundary lost)."""
+    torch = pytest.importorskip("torch")
+    rng = _rng(45)
+    T, H, V = 67, 12, 211
+    xb, wb = _bf16_of(rng.normal(size=(T, H))), _bf16_of(rng.normal(scale=0.4, size=(V, H)))
+    t = rng.integers(0, V, T)
+    g = rng.normal(size=T)
+    sel = np.array([t[5], 0, V - 1, 17, t[5], t[60], 100])
+    _, dw = oracle_mod.fused_linear_xent_grads(xb, wb, t, g)
+    xt = torch.from_numpy(oracle_mod.bf16_bits_to_f64(xb))
+    wt = torch.from_numpy(oracle_mod.bf16_bits_to_f64(wb)).requires_grad_(True)
+    per = torch.nn.functional.cross_entropy(xt @ wt.T, torch.from_numpy(t), reduction="none")
+    (per * torch.from_numpy(g)).sum().backward()
+    for block in (1, 16, 128):
+        rows, dz = oracle_mod.fused_linear_xent_dw_rows(xb, wb, t, g, sel, block=block)
+        assert rows.shape == (sel.size, H) and dz.shape == (T, sel.size)
+        assert np.allclose(rows, dw[sel], rtol=0, atol=1e-13)
+        assert np.allclose(rows, wt.grad.numpy()[sel], rtol=0, atol=1e-13)
+    _, dz_all = oracle_mod.fused_linear_xent_dw_rows(xb, wb, t, g, np.arange(V))
+    assert np.allclose(dz_all.sum(axis=1), 0.0, atol=1e-13)
+
+
+def test_fused_dw_rows_edge_cases(oracle_mod):
+    """x = 0 gives dW = 0; an invalid target makes every selected row NaN; an empty
+    selection is an empty result; a row outside the head is refused."""
+    rng = _rng(46)
+    T, H, V = 9, 5, 13
+    wb = _bf16_of(rng.normal(size=(V, H)))
+    t = rng.integers(0, V, T)
+    g = np.ones(T)
+    rows, _ = oracle_mod.fused_linear_xent_dw_rows(np.zeros((T, H), np.uint16), wb, t, g, [0, 4, 12])
+    assert np.array_equal(rows, np.zeros((3, H)))
+    xb = _bf16_of(rng.normal(size=(T, H)))
+    bad = t.copy()
+    bad[2] = -1
+    rows, _ = oracle_mod.fused_linear_xent_dw_rows(xb, wb, bad, g, [1, 7])
+    assert np.isnan(rows).all()
+    rows, dz = oracle_mod.fused_linear_xent_dw_rows(xb, wb, t, g, np.array([], dtype=np.int64))
+    assert rows.shape == (0, H) and dz.shape == (T, 0)
+    with pytest.raises(ValueError):
+        oracle_mod.fused_linear_xent_dw_rows(xb, wb, t, g, [V])
