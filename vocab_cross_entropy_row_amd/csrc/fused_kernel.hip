@@ -21,7 +21,11 @@
 // segment the states of the two lane halves and of the waves that share a
 // token are merged, and one (max, sum-exp) pair per (segment, token) is
 // written.  A small merge kernel combines the segments and finishes the loss
-// and, optionally, the deterministic mean.
+// and, optionally, the deterministic mean.  The same pipeline serves the
+// kernel's other modes (stored logits, the logit gradient, and the
+// generalized JSD of two projections: KernelIndex "Fused linear + JSD",
+// description), which differ only in the epilogue and, for the JSD, in
+// running each tile's K loop once per head.
 //
 // Placement.  Consecutive workgroup ids are dealt round-robin to the 8 XCDs
 // (each with its own L2).  Workgroup ids are remapped so that the token
@@ -59,9 +63,14 @@ struct Tile {
   static_assert(kWPerWave <= 63, "vmcnt range");
 };
 
-// 256 vocab x 256 tokens (4 waves of 128 x 128); 3 W + 2 x stages of 32 KiB
-// fill the 160 KiB of LDS.
+// 256 vocab x 256 tokens (8 waves of 128 vocab x 64 tokens); 3 W + 2 x stages
+// of 32 KiB fill the 160 KiB of LDS.
 typedef Tile<2, 4, 4, 2, 3, 2> FusedTile;
+
+// JSD mode: 256 vocab x 128 tokens (8 waves of 64 x 64) per head, so that both
+// heads' accumulators fit (2 x 64 per lane); 3 W stages of 32 KiB and 2 x
+// stages of 16 KiB.
+typedef Tile<4, 2, 2, 2, 3, 2> JsdTile;
 
 
 // Fold one token column of a finished tile into that token's running state and
@@ -168,10 +177,15 @@ __device__ __forceinline__ void store_tile_grad(__amdgpu_buffer_rsrc_t dr, const
 // kFusedStoreLogits (the same, and the fp32 logits into z_out), kFusedGrad
 // (only the bf16 logit gradient into dz_out, from the log-sum-exp `lse` and
 // the loss-output gradient: grad[0] / grad_tokens with grad_mean, else
-// grad[token]; NaN rows for targets outside [0, vocab)).
+// grad[token]; NaN rows for targets outside [0, vocab)), kFusedJsd (two
+// projections, x W^T and x2 W2^T, each tile's K loop run once per head into
+// its own accumulators, then per element the generalized JSD term from the
+// heads' log-sum-exps `lse` and `lse2`; per (segment, token) sums into
+// jsd_part).
 constexpr int kFusedXent = 0;
 constexpr int kFusedStoreLogits = 1;
 constexpr int kFusedGrad = 2;
+constexpr int kFusedJsd = 3;
 
 template <class TL, int BVB, int BTB, int WV, int MODE>
 __global__ __launch_bounds__(TL::kThreads) void fused_xent_partial_kernel(
@@ -179,9 +193,13 @@ __global__ __launch_bounds__(TL::kThreads) void fused_xent_partial_kernel(
     int64_t vocab, const int64_t* __restrict__ target, int segments, float2* __restrict__ part,
     float* __restrict__ zt_out, float* __restrict__ z_out, int64_t z_ld,
     const float* __restrict__ lse, const float* __restrict__ grad, int grad_mean,
-    int64_t grad_tokens, uint16_t* __restrict__ dz_out) {
+    int64_t grad_tokens, uint16_t* __restrict__ dz_out, const uint16_t* __restrict__ x2,
+    const uint16_t* __restrict__ w2, const float* __restrict__ lse2, float beta,
+    float* __restrict__ jsd_part) {
   constexpr bool STORE = MODE == kFusedStoreLogits;
   constexpr bool GRAD = MODE == kFusedGrad;
+  constexpr bool JSD = MODE == kFusedJsd;
+  constexpr int kHeads = JSD ? 2 : 1;
   __shared__ __attribute__((aligned(1024))) uint16_t lds[TL::kLdsElems];
   constexpr int kXBase = TL::kWStages * TL::kWStageElems;  // x stages follow the W stages
 
@@ -225,6 +243,17 @@ __global__ __launch_bounds__(TL::kThreads) void fused_xent_partial_kernel(
     }
   }
 
+  // JSD mode: both heads' log-sum-exps of each of this lane's tokens.
+  float lA[BTB], lB[BTB];
+  if constexpr (JSD) {
+#pragma unroll
+    for (int j = 0; j < BTB; ++j) {
+      const bool in = tok[j] < tokens;
+      lA[j] = in ? lse[tok[j]] : 0.0f;
+      lB[j] = in ? lse2[tok[j]] : 0.0f;
+    }
+  }
+
   // Global -> LDS plan.  One wave instruction (64 lanes x 16 B) fills 8 LDS
   // rows; W DMA i of this wave fills W-stage rows 8g .. 8g+7, g = wave + kWaves*i,
   // and likewise for x.  Lane l lands on physical chunk l & 7 of row
@@ -245,9 +274,10 @@ __global__ __launch_bounds__(TL::kThreads) void fused_xent_partial_kernel(
   for (int j = 0; j < BTB; ++j) st[j] = lse_empty();
 
   const int nk = (int)((hidden + TL::kBK - 1) / TL::kBK);
-  const int n_iter = (tile1 - tile0) * nk;
+  const int n_iter = (tile1 - tile0) * nk * kHeads;
   const uint32_t x_rows = (uint32_t)((tokens - t0) < TL::kBT ? (tokens - t0) : TL::kBT);
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + t0 * hidden, x_rows * row_bytes);
+  const __amdgpu_buffer_rsrc_t xr2 = make_rsrc(JSD ? x2 + t0 * hidden : x, JSD ? x_rows * row_bytes : 0u);
   // Logit rows of this token tile (STORE only); byte offset of this lane's
   // first row and column, relative to vocab tile 0.
   // (GRAD: the same for dz_out, bf16 elements, leading dimension z_ld.)
@@ -263,12 +293,14 @@ __global__ __launch_bounds__(TL::kThreads) void fused_xent_partial_kernel(
                    (uint32_t)(wv * (BVB * 32) + 4 * half)) * kZBytes;
   }
 
-  // W block of vocab tile `tile` as a buffer resource (rows past vocab read 0).
-  auto w_rsrc = [&](int tile) {
+  // W block of vocab tile `tile` of head `head` (W2 for head 1, JSD mode) as a
+  // buffer resource (rows past vocab read 0).
+  auto w_rsrc = [&](int tile, int head) {
     const int64_t v0 = (int64_t)tile * TL::kBV;
     const int64_t left = vocab - v0;  // <= 0 only for a tile past the end, never loaded
     const uint32_t w_rows = (uint32_t)(left < 0 ? 0 : (left < TL::kBV ? left : TL::kBV));
-    return make_rsrc(w + (left < 0 ? 0 : v0 * hidden), w_rows * row_bytes);
+    const uint16_t* wh = (JSD && head) ? w2 : w;
+    return make_rsrc(wh + (left < 0 ? 0 : v0 * hidden), w_rows * row_bytes);
   };
   // DMA i of this wave for a slab at hidden offset k0 into a W or x stage.
   // `tail` marks the last slab of a hidden size that is not a multiple of 64:
@@ -279,11 +311,11 @@ __global__ __launch_bounds__(TL::kThreads) void fused_xent_partial_kernel(
     lds_ptr_t dst = (lds_ptr_t)(stage + (wave + TL::kWaves * i) * 8 * TL::kBK);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, vo, k0 * 2u, 0, 0);
   };
-  auto issue_x = [&](int i, uint32_t k0, bool tail, uint16_t* stage) {
+  auto issue_x = [&](int i, __amdgpu_buffer_rsrc_t xres, uint32_t k0, bool tail, uint16_t* stage) {
     uint32_t vo = voff0 + (uint32_t)i * voff_step;
     if (tail && k0 + kch >= (uint32_t)hidden) vo = 0x7ffffff0u;
     lds_ptr_t dst = (lds_ptr_t)(stage + (wave + TL::kWaves * i) * 8 * TL::kBK);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, dst, 16, vo, k0 * 2u, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, dst, 16, vo, k0 * 2u, 0, 0);
   };
   constexpr int kWPerGroup = TL::kWPerWave / BTB;  // spread over one k-step's MFMA groups
   constexpr int kXPerGroup = TL::kXPerWave / BTB;
@@ -322,9 +354,10 @@ __global__ __launch_bounds__(TL::kThreads) void fused_xent_partial_kernel(
   int wq = 0;                  // it % kWStages
   int xq = 0;                  // it % kXStages
   // W cursor (next W slab to issue) and x cursor (next x slab to issue).
-  int w_kk = 0, w_tile = tile0, w_left = n_iter;
-  __amdgpu_buffer_rsrc_t w_cur = w_rsrc(tile0);
-  int x_kk = 0, x_left = n_iter;
+  // In JSD mode each tile's slabs run head 0 (x, W) then head 1 (x2, W2).
+  int w_kk = 0, w_tile = tile0, w_head = 0, w_left = n_iter;
+  __amdgpu_buffer_rsrc_t w_cur = w_rsrc(tile0, 0);
+  int x_kk = 0, x_head = 0, x_left = n_iter;
   auto w_issue_part = [&](int stage, int group) {  // this wave's W DMAs for MFMA group `group`
 #pragma unroll
     for (int d = 0; d < kWPerGroup; ++d) {
@@ -336,20 +369,30 @@ __global__ __launch_bounds__(TL::kThreads) void fused_xent_partial_kernel(
     --w_left;
     if (++w_kk == nk) {
       w_kk = 0;
-      ++w_tile;
-      w_cur = w_rsrc(w_tile);
+      if (JSD && w_head == 0) {
+        w_head = 1;
+      } else {
+        w_head = 0;
+        ++w_tile;
+      }
+      w_cur = w_rsrc(w_tile, w_head);
     }
   };
   auto x_issue_part = [&](int stage, int group) {
+    const __amdgpu_buffer_rsrc_t xres = (JSD && x_head) ? xr2 : xr;
 #pragma unroll
     for (int d = 0; d < kXPerGroup; ++d) {
       const int i = group * kXPerGroup + d;
-      issue_x(i, (uint32_t)x_kk * TL::kBK, slab_is_tail(x_kk), lds + kXBase + stage * TL::kXStageElems);
+      issue_x(i, xres, (uint32_t)x_kk * TL::kBK, slab_is_tail(x_kk),
+              lds + kXBase + stage * TL::kXStageElems);
     }
   };
   auto x_advance = [&]() {
     --x_left;
-    if (++x_kk == nk) x_kk = 0;
+    if (++x_kk == nk) {
+      x_kk = 0;
+      if constexpr (JSD) x_head ^= 1;
+    }
   };
 
   // Prologue: x slabs 0 .. kXStages-1 and W slabs 0 .. kWStages-1, in the
@@ -374,53 +417,78 @@ __global__ __launch_bounds__(TL::kThreads) void fused_xent_partial_kernel(
   if (n_iter > 0) read_frags(lds, lds + kXBase, 0, 0);
 
   int it = 0;
+  float jsd[BTB];  // JSD mode: this lane's share of each token's divergence
+#pragma unroll
+  for (int b = 0; b < BTB; ++b) jsd[b] = 0.0f;
   for (int tile = tile0; tile < tile1; ++tile) {
-    f32x16 acc[BTB][BVB];
+    // Each head's K loop (one head except in JSD mode) into its accumulators:
+    // nk slabs per head.  The head loop is unrolled, so `A` names a fixed array.
+    f32x16 acc[BTB][BVB], acc2[BTB][BVB];
 #pragma unroll
-    for (int b = 0; b < BTB; ++b)
+    for (int h = 0; h < kHeads; ++h) {
+      f32x16 (&A)[BTB][BVB] = h == 0 ? acc : acc2;
 #pragma unroll
-      for (int a = 0; a < BVB; ++a) acc[b][a] = (f32x16)(0.0f);
+      for (int b = 0; b < BTB; ++b)
+#pragma unroll
+        for (int a = 0; a < BVB; ++a) A[b][a] = (f32x16)(0.0f);
 
-    for (int kk = 0; kk < nk; ++kk, ++it) {
-      const uint16_t* Ws = lds + wq * TL::kWStageElems;
-      const uint16_t* Xs = lds + kXBase + xq * TL::kXStageElems;
-      // W slab issued in this slab's first k-step (into the stage freed at the
-      // previous barrier), if any is left.
-      const int w_stage_free = (wq + TL::kWStages - 1) % TL::kWStages;
-      const bool w_now = (it > 0) && (w_left > 0);
+      for (int kk = 0; kk < nk; ++kk, ++it) {
+        const uint16_t* Ws = lds + wq * TL::kWStageElems;
+        const uint16_t* Xs = lds + kXBase + xq * TL::kXStageElems;
+        // W slab issued in this slab's first k-step (into the stage freed at the
+        // previous barrier), if any is left.
+        const int w_stage_free = (wq + TL::kWStages - 1) % TL::kWStages;
+        const bool w_now = (it > 0) && (w_left > 0);
 #pragma unroll
-      for (int ks = 0; ks < TL::kKSteps - 1; ++ks) {
-        const int p = ks & 1;
-        read_frags(Ws, Xs, ks + 1, p ^ 1);
+        for (int ks = 0; ks < TL::kKSteps - 1; ++ks) {
+          const int p = ks & 1;
+          read_frags(Ws, Xs, ks + 1, p ^ 1);
+#pragma unroll
+          for (int b = 0; b < BTB; ++b) {
+#pragma unroll
+            for (int a = 0; a < BVB; ++a)
+              A[b][a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[p][a], bfr[p][b], A[b][a], 0, 0, 0);
+            if (ks == 0 && w_now) w_issue_part(w_stage_free, b);
+          }
+        }
+        if (w_now) w_advance();
+        // The next slab's x and W have landed for every wave (only the newest W
+        // slab may still be in flight); every read of this slab is done.
+        if (w_now) wait_vmcnt<TL::kWPerWave>(); else wait_vmcnt<0>();
+        lds_barrier();
+        const int wq1 = (wq + 1 == TL::kWStages) ? 0 : wq + 1;
+        const int xq1 = (xq + 1 == TL::kXStages) ? 0 : xq + 1;
+        const bool x_now = x_left > 0;
+        if (it + 1 < n_iter)
+          read_frags(lds + wq1 * TL::kWStageElems, lds + kXBase + xq1 * TL::kXStageElems, 0, 0);
+        constexpr int pl = (TL::kKSteps - 1) & 1;
 #pragma unroll
         for (int b = 0; b < BTB; ++b) {
 #pragma unroll
           for (int a = 0; a < BVB; ++a)
-            acc[b][a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[p][a], bfr[p][b], acc[b][a], 0, 0, 0);
-          if (ks == 0 && w_now) w_issue_part(w_stage_free, b);
-          }
+            A[b][a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[pl][a], bfr[pl][b], A[b][a], 0, 0, 0);
+          if (x_now) x_issue_part(xq, b);  // x slab it + kXStages into this slab's x stage
+        }
+        if (x_now) x_advance();
+        wq = wq1;
+        xq = xq1;
       }
-      if (w_now) w_advance();
-      // The next slab's x and W have landed for every wave (only the newest W
-      // slab may still be in flight); every read of this slab is done.
-      if (w_now) wait_vmcnt<TL::kWPerWave>(); else wait_vmcnt<0>();
-      lds_barrier();
-      const int wq1 = (wq + 1 == TL::kWStages) ? 0 : wq + 1;
-      const int xq1 = (xq + 1 == TL::kXStages) ? 0 : xq + 1;
-      const bool x_now = x_left > 0;
-      if (it + 1 < n_iter)
-        read_frags(lds + wq1 * TL::kWStageElems, lds + kXBase + xq1 * TL::kXStageElems, 0, 0);
-      constexpr int pl = (TL::kKSteps - 1) & 1;
+    }
+    if constexpr (JSD) {
+      // Head 1's logits of the same tile, then the divergence terms:
+      // acc[b][a][v] is vocab row vbase + a*32 + 8*(v/4) + 4*half + v%4 of token tok[b].
+      const int64_t vbase = (int64_t)tile * TL::kBV + wv * (BVB * 32);
 #pragma unroll
-      for (int b = 0; b < BTB; ++b) {
+      for (int b = 0; b < BTB; ++b)
 #pragma unroll
         for (int a = 0; a < BVB; ++a)
-          acc[b][a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[pl][a], bfr[pl][b], acc[b][a], 0, 0, 0);
-        if (x_now) x_issue_part(xq, b);  // x slab it + kXStages into this slab's x stage
-      }
-      if (x_now) x_advance();
-      wq = wq1;
-      xq = xq1;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int64_t j = vbase + a * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+            const float term = jsd_term(acc[b][a][v] - lA[b], acc2[b][a][v] - lB[b], beta);
+            jsd[b] += j < vocab ? term : 0.0f;
+          }
+      continue;
     }
 
     // Epilogue of the finished tile, one token column at a time.
@@ -449,6 +517,29 @@ __global__ __launch_bounds__(TL::kThreads) void fused_xent_partial_kernel(
   }
 
   if constexpr (GRAD) return;
+  if constexpr (JSD) {
+    // Sum the two lane halves (same tokens, different vocab rows), then the WV
+    // waves that share these tokens, in wave order, through LDS (free: every
+    // wave passed the barrier after its last slab).
+    float* red = reinterpret_cast<float*>(lds);  // [WV][kBT]
+#pragma unroll
+    for (int b = 0; b < BTB; ++b) {
+      const float v = jsd[b] + half_swap(jsd[b]);
+      if (half == 0) red[wv * TL::kBT + wt * (BTB * 32) + b * 32 + (lane & 31)] = v;
+    }
+    __syncthreads();
+    if (wv == 0 && half == 0) {
+#pragma unroll
+      for (int b = 0; b < BTB; ++b) {
+        const int tl = wt * (BTB * 32) + b * 32 + (lane & 31);
+        float sum = red[tl];
+#pragma unroll
+        for (int q = 1; q < WV; ++q) sum += red[q * TL::kBT + tl];
+        if (tok[b] < tokens) jsd_part[(int64_t)seg * tokens + tok[b]] = sum;
+      }
+    }
+    return;
+  }
   // Merge the two lane halves (same tokens, different vocab rows) ...
 #pragma unroll
   for (int b = 0; b < BTB; ++b) {
@@ -527,6 +618,7 @@ __global__ __launch_bounds__(kRowThreads) void fused_xent_merge_kernel(
 }
 
 FusedGeometry fused_geometry() { return {FusedTile::kBT, FusedTile::kBV}; }
+FusedGeometry jsd_geometry() { return {JsdTile::kBT, JsdTile::kBV}; }
 
 int fused_segments(int64_t tokens, int64_t vocab, int num_cus) {
   const int64_t n_tok = (tokens + FusedTile::kBT - 1) / FusedTile::kBT;
@@ -548,13 +640,15 @@ hipError_t launch_fused(const FusedArgs& a, hipStream_t stream) {
                        dim3((unsigned)grid), dim3(FusedTile::kThreads), 0, stream,
                        (const uint16_t*)a.x, (const uint16_t*)a.w, a.tokens, a.hidden, a.vocab,
                        a.target, a.segments, (float2*)a.seg_partials, a.target_logit, a.z_out,
-                       a.z_ld, nullptr, nullptr, 0, (int64_t)0, nullptr);
+                       a.z_ld, nullptr, nullptr, 0, (int64_t)0, nullptr, nullptr, nullptr, nullptr,
+                       0.0f, nullptr);
   else
     hipLaunchKernelGGL((fused_xent_partial_kernel<FusedTile, 4, 2, 2, kFusedXent>),
                        dim3((unsigned)grid), dim3(FusedTile::kThreads), 0, stream,
                        (const uint16_t*)a.x, (const uint16_t*)a.w, a.tokens, a.hidden, a.vocab,
                        a.target, a.segments, (float2*)a.seg_partials, a.target_logit, nullptr,
-                       (int64_t)0, nullptr, nullptr, 0, (int64_t)0, nullptr);
+                       (int64_t)0, nullptr, nullptr, 0, (int64_t)0, nullptr, nullptr, nullptr,
+                       nullptr, 0.0f, nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t blocks = (a.tokens + kRowThreads - 1) / kRowThreads;
@@ -573,7 +667,29 @@ hipError_t launch_fused_grad(const FusedGradArgs& a, hipStream_t stream) {
                      dim3((unsigned)grid), dim3(FusedTile::kThreads), 0, stream,
                      (const uint16_t*)a.x, (const uint16_t*)a.w, a.tokens, a.hidden, a.vocab,
                      a.target, a.segments, nullptr, nullptr, nullptr, a.dz_ld, a.lse, a.grad,
-                     a.grad_mean, a.grad_tokens, (uint16_t*)a.dz);
+                     a.grad_mean, a.grad_tokens, (uint16_t*)a.dz, nullptr, nullptr, nullptr, 0.0f,
+                     nullptr);
+  return hipGetLastError();
+}
+
+int jsd_segments(int64_t tokens, int64_t vocab, int num_cus) {
+  const int64_t n_tok = (tokens + JsdTile::kBT - 1) / JsdTile::kBT;
+  const int64_t n_voc = (vocab + JsdTile::kBV - 1) / JsdTile::kBV;
+  int64_t s = num_cus / (n_tok > 0 ? n_tok : 1);
+  if (s < 1) s = 1;
+  if (s > n_voc) s = n_voc;
+  return (int)s;
+}
+
+hipError_t launch_fused_jsd_partial(const JsdArgs& a, hipStream_t stream) {
+  const int64_t n_tok = (a.tokens + JsdTile::kBT - 1) / JsdTile::kBT;
+  const int64_t grid = n_tok * a.segments;
+  if (!grid_fits(grid, JsdTile::kThreads)) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fused_xent_partial_kernel<JsdTile, 2, 2, 4, kFusedJsd>), dim3((unsigned)grid),
+                     dim3(JsdTile::kThreads), 0, stream, (const uint16_t*)a.xs, (const uint16_t*)a.ws,
+                     a.tokens, a.hidden, a.vocab, nullptr, a.segments, nullptr, nullptr, nullptr,
+                     (int64_t)0, a.lse_s, nullptr, 0, (int64_t)0, nullptr, (const uint16_t*)a.xt,
+                     (const uint16_t*)a.wt, a.lse_t, a.beta, a.partials);
   return hipGetLastError();
 }
 

@@ -235,4 +235,20 @@ __device__ __forceinline__ void finish_mean(float block_sum, uint64_t* slots, un
   }
 }
 
+// ------------------------------------------------------------ generalized JSD
+// One vocab entry's divergence term  beta P (ln P - ln M) + (1 - beta) Q (ln Q - ln M)
+// from lp = ln P and lq = ln Q.  Relative to mx = max(lp, lq): ln M = mx + ln S
+// with S = beta e^u + (1 - beta) e^w >= min(beta, 1 - beta), u = lp - mx and
+// w = lq - mx (one of them 0), so no underflowing P, Q or M reaches the
+// logarithm, and a term below the fp32 range is 0.
+__device__ __forceinline__ float jsd_term(float lp, float lq, float beta) {
+  const float mx = __builtin_fmaxf(lp, lq);
+  const float u = lp - mx, w = lq - mx;
+  const float e = exp2_fast((u + w) * kLog2e);  // e^(-|lp - lq|)
+  const float eu = lp >= lq ? 1.0f : e;
+  const float ew = lp >= lq ? e : 1.0f;
+  const float ls = kLn2 * log2_fast(beta * eu + (1.0f - beta) * ew);
+  return exp2_fast(mx * kLog2e) * (beta * eu * (u - ls) + (1.0f - beta) * ew * (w - ls));
+}
+
 }  // namespace lce

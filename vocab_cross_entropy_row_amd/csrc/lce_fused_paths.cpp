@@ -156,7 +156,7 @@ lce_status run_fused_bwd(const void* x, const void* weight, int64_t tokens, int6
 // log-sum-exp with the fused cross-entropy kernel.  The stored path has that
 // kernel also write both heads' fp32 logits for a chunk of tokens into scratch
 // and then streams them once (jsd_stored_rows_kernel); the recompute path
-// multiplies both heads again, tile by tile (fused_jsd_partial_kernel), and
+// multiplies both heads again, tile by tile (the fused kernel's JSD mode), and
 // needs no logit storage.  The stored path is taken when a chunk of at least
 // one fused token tile fits in LCE_JSD_STORE_BYTES (default 2 GiB) of scratch.
 struct JsdPlan {
@@ -296,8 +296,9 @@ lce_status run_jsd_recompute(const void* xs, const void* ws, const void* xt, con
     return s;
   hipError_t e = lce::launch_jsd(a, stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
-  note_launch("fused_jsd_partial_kernel grid %lld x 512 + fused_jsd_merge_kernel",
-              (long long)((tokens + 127) / 128 * a.segments));
+  const lce::FusedGeometry jg = lce::jsd_geometry();
+  note_launch("fused_xent_partial_kernel<JSD mode> grid %lld x 512 + fused_jsd_merge_kernel",
+              (long long)((tokens + jg.block_tokens - 1) / jg.block_tokens * a.segments));
   return LCE_OK;
 }
 

@@ -119,6 +119,8 @@ struct FusedGeometry {
   int block_vocab;    // vocab rows per workgroup tile
 };
 FusedGeometry fused_geometry();
+// The JSD mode's tile (its token tiles size the recompute path's grid).
+FusedGeometry jsd_geometry();
 int fused_segments(int64_t tokens, int64_t vocab, int num_cus);
 hipError_t launch_fused(const FusedArgs& a, hipStream_t stream);
 
@@ -146,6 +148,9 @@ struct JsdArgs {
   unsigned* ticket;
 };
 int jsd_segments(int64_t tokens, int64_t vocab, int num_cus);
+// The fused kernel's JSD mode alone (per-segment sums into partials).
+hipError_t launch_fused_jsd_partial(const JsdArgs& a, hipStream_t stream);
+// That, then the merge into per-token divergences or their mean.
 hipError_t launch_jsd(const JsdArgs& a, hipStream_t stream);
 
 // Divergence of rows whose logits were stored by the fused kernel (z_out).
