@@ -459,6 +459,9 @@ def time_vocab_shard(torch, lce, lce_synth, tp: int, steps: int, warmup: int) ->
 
     p_us = graph_us(lambda i: lce.xent_partial(reps[i % R], t, 0, out=part), steps)
     m_us = graph_us(lambda i: lce.xent_merge(stats, t, V, "none", out=out), steps)
+    # The same shard bytes read by bench_probe's plain read (nothing else): the floor a
+    # read of this size has on this part (launch and memory latency included).
+    read_us = probe_read_us(torch, reps, steps) if os.path.exists(PROBE_LIB) else None
     lce.xent_merge(stats, t, V, "none", out=out)
     whole = lce.xent(z, t.view(-1), "none")
     torch.cuda.synchronize()
@@ -473,6 +476,8 @@ def time_vocab_shard(torch, lce, lce_synth, tp: int, steps: int, warmup: int) ->
                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                  "frac": round(p_bytes / (p_us * 1e3) / HBM_PEAK_GBS, 4),
                                  "algorithmic_bytes": p_bytes, "replicas": R},
+            "shard_read_only_us": round(read_us, 3) if read_us else None,
+            "partial_us_over_read_only_us": round(p_us / read_us, 4) if read_us else None,
             "merge_algorithmic_bytes": m_bytes,
             "max_abs_diff_vs_unsplit": diff}
 
@@ -628,12 +633,7 @@ def build_probe() -> str:
     return PROBE_LIB
 
 
-def time_stream_read(torch, head_bytes: int, head_replicas: int, steps: int) -> dict:
-    """A plain streaming read for comparison (not a peak: the long row kernels read faster):
-    bench_probe's kernel (16-byte nontemporal loads, nothing else) over one 2 GiB buffer,
-    and over `head_bytes` (the logit bytes of a short-row workload) with as many rotating
-    replicas as that workload's timing uses, each timed as a graph of `steps` reads
-    (median of the replays)."""
+def _probe_lib():
     import ctypes
     if not os.path.exists(PROBE_LIB):
         raise SystemExit(f"{PROBE_LIB} is missing: run __graft_entry__.build() first")
@@ -641,43 +641,56 @@ def time_stream_read(torch, head_bytes: int, head_replicas: int, steps: int) -> 
     lib.bench_stream_read.restype = ctypes.c_int
     lib.bench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
                                       ctypes.c_void_p]
+    return lib
+
+
+def probe_read_us(torch, bufs, k: int) -> float:
+    """bench_probe's plain read of each device buffer in `bufs` in turn (rotating), timed as
+    a graph of `k` reads on a side stream: median µs per read over the timed replays."""
+    lib = _probe_lib()
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
 
-    def graph_us(bufs, k):
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-
-        def call(i):
-            b = bufs[i % len(bufs)]
-            rc = lib.bench_stream_read(b.data_ptr(), b.numel(), sink.data_ptr(), s.cuda_stream)
-            if rc != 0:
-                raise RuntimeError(f"bench_stream_read failed (hipError {rc})")
-        with torch.cuda.stream(s):
-            for i in range(len(bufs)):
-                call(i)
+    def call(i):
+        b = bufs[i % len(bufs)]
+        rc = lib.bench_stream_read(b.data_ptr(), b.numel() * b.element_size(), sink.data_ptr(),
+                                   s.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"bench_stream_read failed (hipError {rc})")
+    with torch.cuda.stream(s):
+        for i in range(len(bufs)):
+            call(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(k):
+            call(i)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    per = []
+    for _ in range(SPREAD_REPLAYS):
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=s):
-            for i in range(k):
-                call(i)
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        per = []
-        for _ in range(SPREAD_REPLAYS):
-            torch.cuda.synchronize()
-            with torch.cuda.stream(s):
-                t0.record(s)
-                g.replay()
-                t1.record(s)
-            torch.cuda.synchronize()
-            per.append(t0.elapsed_time(t1) * 1000.0 / k)
-        del g
-        return statistics.median(per)
+        with torch.cuda.stream(s):
+            t0.record(s)
+            g.replay()
+            t1.record(s)
+        torch.cuda.synchronize()
+        per.append(t0.elapsed_time(t1) * 1000.0 / k)
+    del g
+    return statistics.median(per)
 
+
+def time_stream_read(torch, head_bytes: int, head_replicas: int, steps: int) -> dict:
+    """A plain streaming read for comparison (not a peak: the long row kernels read faster):
+    bench_probe's kernel (16-byte nontemporal loads, nothing else) over one 2 GiB buffer,
+    and over `head_bytes` (the logit bytes of a short-row workload) with as many rotating
+    replicas as that workload's timing uses, each timed as a graph of `steps` reads
+    (median of the replays)."""
     big = [torch.ones(1 << 31, dtype=torch.uint8, device="cuda")]
-    us_big = graph_us(big, max(5, min(steps, 20)))
+    us_big = probe_read_us(torch, big, max(5, min(steps, 20)))
     del big
     small = [torch.ones(head_bytes, dtype=torch.uint8, device="cuda") for _ in range(head_replicas)]
-    us_small = graph_us(small, steps)
+    us_small = probe_read_us(torch, small, steps)
     del small
     torch.cuda.empty_cache()
     return {"kernel": "bench_probe.hip stream_read_kernel (16-byte nt buffer loads, 8 per lane "
@@ -985,9 +998,10 @@ def main(argv=None) -> int:
                   f"({backward[bname]['roofline']['achieved']} GB/s)", file=sys.stderr, flush=True)
     if "shard" in extras:
         shard = time_vocab_shard(torch, lce, lce_synth, 8, min(args.steps, 200), args.warmup)
-        print(f"[bench] vocab shard tp=8: partial {shard['partial_us']:.2f} µs, "
-              f"merge {shard['merge_us']:.2f} µs, max |diff| vs unsplit "
-              f"{shard['max_abs_diff_vs_unsplit']:.2e}", file=sys.stderr, flush=True)
+        print(f"[bench] vocab shard tp=8: partial {shard['partial_us']:.2f} µs (plain read of "
+              f"its bytes {shard['shard_read_only_us']} µs), merge {shard['merge_us']:.2f} µs, "
+              f"max |diff| vs unsplit {shard['max_abs_diff_vs_unsplit']:.2e}",
+              file=sys.stderr, flush=True)
     if "split" in extras:
         split = time_split(torch, lce, lce_synth, min(args.steps, 200), args.warmup)
     if "sweep" in extras:
