@@ -612,7 +612,19 @@ def cpu_baseline(w, budget_s: float = 10.0) -> dict:
         per_call = (time.perf_counter() - t0) * rows / sample_rows
         sample = f"{sample_rows} of {rows} token rows (full head), one run, scaled to all rows"
     return {"value": round(per_call * 1e6, 1), "unit": "µs", "cores": threads, "kind": "oracle",
-            "sample": sample}
+            "sample": sample, "cpu_model": _cpu_model()}
+
+
+def _cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo ("unknown" if not readable)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 # ------------------------------------------------------------------ streaming-read probe
