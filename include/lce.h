@@ -141,7 +141,7 @@ LCE_API lce_status lce_xent_fwd(const void* logits, lce_dtype dtype, int64_t tok
  * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
  * arguments, kernels, path selection, results (bitwise) and errors as
  * lce_xent_fwd, but the call makes no hipMalloc or hipFree and uses no
- * allocating library routine: its scratch (the mean's ticket counters and
+ * allocating library routine: its scratch (the mean's epoch word and
  * per-workgroup slots, the split path's partials) lives in one static 8 MiB
  * device array per GPU, held until the process ends.
  *
@@ -153,7 +153,7 @@ LCE_API lce_status lce_xent_fwd(const void* logits, lce_dtype dtype, int64_t tok
  * Every call on a GPU shares that GPU's array, and the array keeps the last
  * call's contents between calls: calls that overlap on one GPU (concurrent
  * streams, threads or graph replays) race and must be serialised by the
- * caller.  The first call on a GPU also clears the array's counters with a
+ * caller.  The first call on a GPU also clears the array's mean state with a
  * kernel on `stream` (when that call is being captured into a HIP graph, the
  * clear is captured too and the next uncaptured call clears again).
  */

@@ -3,8 +3,8 @@
 The benchmark times graph replays, so replays must give the eager results bit for
 bit: every kernel path (one wave per row, one workgroup per row, split rows, the
 fused projection, fused linear + JSD with stored logits, in chunks, and recomputed)
-with and without the last-workgroup mean, whose ticket counters
-must be back at zero after each replay.  Between replays the program does eager
+with and without the deterministic mean, whose epoch word each replay must advance so
+that the next one tells its partials from those left by earlier launches.  Between replays the program does eager
 work of its own (other liblce calls on the same stream, torch kernels, host
 synchronisations), and each replay first finds its outputs overwritten with NaN.
 """
@@ -118,7 +118,7 @@ def test_graph_replays_match_eager():
     other, other_out = _row_case(109, 5000, 1024, "f32", "mean", {"LCE_PATH": "wave"})
 
     def between(r):
-        # eager liblce work on the capture stream (shares its scratch and tickets) and
+        # eager liblce work on the capture stream (shares its scratch and mean state) and
         # on the default stream, plus torch kernels
         with torch.cuda.stream(s):
             other()

@@ -572,7 +572,7 @@ def test_fused_repeated_calls_bitwise_identical():
 
 @pytest.mark.parametrize("path", ["wave", "block", "split"])
 def test_mean_handoff_many_workgroups(path):
-    """The last-workgroup mean sees every workgroup's partial: 30 back-to-back calls
+    """The deterministic mean's finisher sees every workgroup's partial: 30 back-to-back calls
     (thousands of workgroups each) agree bitwise, and the mean matches the average of
     the per-token losses."""
     rows, vocab = (16384, 2048) if path != "split" else (512, 40000)

@@ -145,7 +145,7 @@ def test_refused_scratch_allocation_reports_oom():
 
 
 def test_mean_after_fused_backward_on_one_stream():
-    """The deterministic mean hands each workgroup's partial to the last workgroup through
+    """The deterministic mean hands each workgroup's partial to the finishing workgroup through
     tagged 64-bit slots, which must never hold another call's data.  They live in a buffer
     that only the mean reductions write: a fused backward (which fills this stream's scratch
     with fp32 logits, the bf16 logit gradient and GEMM workspace) followed, on the same

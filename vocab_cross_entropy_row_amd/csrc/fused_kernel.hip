@@ -580,8 +580,9 @@ __global__ __launch_bounds__(TL::kThreads) void fused_xent_partial_kernel(
 __global__ __launch_bounds__(kRowThreads) void fused_xent_merge_kernel(
     int64_t tokens, int64_t vocab, int segments, const float2* __restrict__ part,
     const float* __restrict__ zt, const int64_t* __restrict__ target, float* __restrict__ out,
-    float* __restrict__ lse_out, uint64_t* __restrict__ slots, unsigned* __restrict__ ticket,
+    float* __restrict__ lse_out, uint64_t* __restrict__ slots, unsigned* __restrict__ epoch,
     int reduce_mean) {
+  const unsigned mean_tag = mean_begin(epoch, reduce_mean);
   const int64_t row = (int64_t)blockIdx.x * kRowThreads + threadIdx.x;
   float loss = 0.0f;
   if (row < tokens) {
@@ -613,7 +614,7 @@ __global__ __launch_bounds__(kRowThreads) void fused_xent_merge_kernel(
       if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
       __syncthreads();
     }
-    finish_mean(red[0], slots, ticket, out, tokens);
+    finish_mean(red[0], slots, epoch, mean_tag, out, tokens);
   }
 }
 
@@ -654,7 +655,7 @@ hipError_t launch_fused(const FusedArgs& a, hipStream_t stream) {
   const int64_t blocks = (a.tokens + kRowThreads - 1) / kRowThreads;
   hipLaunchKernelGGL(fused_xent_merge_kernel, dim3((unsigned)blocks), dim3(kRowThreads), 0, stream,
                      a.tokens, a.vocab, a.segments, (const float2*)a.seg_partials,
-                     (const float*)a.target_logit, a.target, a.out, a.lse_out, a.mean_slots, a.ticket,
+                     (const float*)a.target_logit, a.target, a.out, a.lse_out, a.mean_slots, a.epoch,
                      a.reduce_mean);
   return hipGetLastError();
 }

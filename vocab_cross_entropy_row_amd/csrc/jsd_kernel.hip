@@ -89,7 +89,8 @@ __global__ __launch_bounds__(kJRThreads) void jsd_stored_rows_kernel(
 // per-token divergence or the deterministic batch mean.
 __global__ __launch_bounds__(kRowThreads) void fused_jsd_merge_kernel(
     int64_t tokens, int segments, const float* __restrict__ part, float* __restrict__ out,
-    uint64_t* __restrict__ slots, unsigned* __restrict__ ticket, int reduce_mean) {
+    uint64_t* __restrict__ slots, unsigned* __restrict__ epoch, int reduce_mean) {
+  const unsigned mean_tag = mean_begin(epoch, reduce_mean);
   const int64_t row = (int64_t)blockIdx.x * kRowThreads + threadIdx.x;
   float v = 0.0f;
   if (row < tokens) {
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(kRowThreads) void fused_jsd_merge_kernel(
       if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
       __syncthreads();
     }
-    finish_mean(red[0], slots, ticket, out, tokens);
+    finish_mean(red[0], slots, epoch, mean_tag, out, tokens);
   }
 }
 
@@ -116,7 +117,7 @@ hipError_t launch_jsd(const JsdArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const int64_t blocks = (a.tokens + kRowThreads - 1) / kRowThreads;
   hipLaunchKernelGGL(fused_jsd_merge_kernel, dim3((unsigned)blocks), dim3(kRowThreads), 0, stream,
-                     a.tokens, a.segments, (const float*)a.partials, a.out, a.mean_slots, a.ticket,
+                     a.tokens, a.segments, (const float*)a.partials, a.out, a.mean_slots, a.epoch,
                      a.reduce_mean);
   return hipGetLastError();
 }
@@ -129,11 +130,11 @@ hipError_t launch_jsd_rows(const JsdRowsArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_jsd_mean(int64_t tokens, const float* per_token, float* out, uint64_t* slots,
-                           unsigned* ticket, hipStream_t stream) {
+                           unsigned* epoch, hipStream_t stream) {
   const int64_t blocks = (tokens + kRowThreads - 1) / kRowThreads;
   if (!grid_fits(blocks, kRowThreads)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(fused_jsd_merge_kernel, dim3((unsigned)blocks), dim3(kRowThreads), 0, stream,
-                     tokens, 1, per_token, out, slots, ticket, 1);
+                     tokens, 1, per_token, out, slots, epoch, 1);
   return hipGetLastError();
 }
 

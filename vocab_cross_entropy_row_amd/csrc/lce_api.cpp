@@ -39,7 +39,7 @@ lce_status run_rows(const void* logits, int dtype, int64_t tokens, int64_t vocab
 
   // Path selection (measured on MI355X):
   //  - rows up to 32 KiB: one wave per row; 4 waves per workgroup without a
-  //    mean, 16 with a mean (a quarter of the ticket hand-offs);
+  //    mean, 16 with a mean (a quarter of the partials to hand off);
   //  - longer rows: without a mean, one workgroup per row; with a mean, one
   //    wave per row in 16-wave workgroups; with few rows, several workgroups
   //    per row (split).
@@ -133,7 +133,7 @@ lce_status run_rows(const void* logits, int dtype, int64_t tokens, int64_t vocab
                   (long long)mean_blocks, (long long)ws->max_slots);
     a.split_partials = (float*)ws->general;
     a.split_zt = (float*)(ws->general + off_zt_rel);
-    a.ticket = ws->ticket;
+    a.epoch = ws->epoch;
     a.mean_slots = ws->slots;
   } else {
     Carve cv;
@@ -146,7 +146,7 @@ lce_status run_rows(const void* logits, int dtype, int64_t tokens, int64_t vocab
     if (mean) {
       MeanState ms;
       if ((s = get_mean_state(stream, mean_blocks, &ms)) != LCE_OK) return s;
-      a.ticket = ms.ticket;
+      a.epoch = ms.epoch;
       a.mean_slots = ms.slots;
     }
   }
@@ -219,7 +219,7 @@ lce_status run_fused(const void* x, const void* weight, int64_t tokens, int64_t 
     MeanState ms;
     if ((s = get_mean_state(stream, (tokens + lce::kRowThreads - 1) / lce::kRowThreads, &ms)) != LCE_OK)
       return s;
-    a.ticket = ms.ticket;
+    a.epoch = ms.epoch;
     a.mean_slots = ms.slots;
   }
 
@@ -317,7 +317,7 @@ lce_status lce_xent_merge(const float* partials, int64_t shards, int64_t tokens,
   if (mean && (s = get_mean_state(stream, (tokens + lce::kRowThreads - 1) / lce::kRowThreads, &ms)) != LCE_OK)
     return s;
   hipError_t e = lce::launch_stats_merge(partials, shards, tokens, target, vocab, out, mean ? 1 : 0,
-                                         ms.slots, ms.ticket, stream);
+                                         ms.slots, ms.epoch, stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   note_launch("xent_stats_merge_kernel grid %lld x %d",
               (long long)((tokens + lce::kRowThreads - 1) / lce::kRowThreads), lce::kRowThreads);

@@ -131,45 +131,50 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 
 // ------------------------------------------------------------ deterministic mean
-// Every workgroup contributes one fp32 partial; the workgroup that finishes
-// last adds all partials in a fixed order and writes the mean.  No float
-// atomics are used, so the result is bitwise reproducible.
+// Every workgroup contributes one fp32 partial; one workgroup adds all
+// partials in a fixed order and writes the mean.  No float atomics are used,
+// so the result is bitwise reproducible.
 //
-// Finding the last workgroup: a two-level integer ticket.  Workgroup b counts
-// itself in group counter b % G (G <= 64 counters, each on its own 256-byte
-// line so they do not serialise on one address); the workgroup that completes
-// a group counts the group in the top counter; the one that completes the top
-// counter is last.  Each completing workgroup resets the counter it completed,
-// so all counters are zero again when the kernel ends.
-//
-// Handing over the partials: every other workgroup writes its partial after
-// taking its ticket, as one 64-bit agent-scope atomic store of (tag, value),
-// and leaves without waiting for it.  The tag is the launch's epoch + 1: the
-// epoch word is read beside the first ticket, and the last workgroup advances
-// it for the next launch on this scratch buffer.  The last workgroup polls
-// each slot until it carries this launch's tag, so data and flag arrive
-// together and no writer has to wait for its store; slots left by earlier
+// The finisher is the workgroup with the highest index.  Workgroups are
+// dispatched in index order, so when the finisher starts every other
+// workgroup has started and none waits on anything: the finisher's wait for
+// the partials always ends.  Every other workgroup writes its partial as one
+// 64-bit agent-scope atomic store of (tag, value) and retires at once,
+// without any returning atomic.  The tag is the launch's epoch + 1: each
+// workgroup reads the epoch word when it starts (mean_begin, so the load's
+// latency hides under its rows) and the finisher advances it for the next
+// launch on this buffer.  The finisher polls each slot until it carries this
+// launch's tag, so data and flag arrive together; slots left by earlier
 // launches carry older tags (a new buffer is zeroed, and tags start at 1).
-// The chain after the last row is then three memory round trips: two ticket
-// atomics and one read of the slots.  Agent-scope atomics are coherent across
-// the XCDs (each has its own L2) without writing back or invalidating an L2.
+// After the last row the chain is the last partial's store and one read of
+// it.  Agent-scope atomics are coherent across the XCDs (each has its own L2)
+// without writing back or invalidating an L2.  The finisher's polling is
+// bounded (kPollBudget re-reads in all, a short sleep between them): a launch
+// that runs out of it writes NaN instead of hanging.
 //
 // Only wave 0 takes part: the other waves of the workgroup retire at once.
-constexpr int kTicketGroups = 64;
-constexpr int kTicketStride = 64;  // unsigned ints (256 bytes) between counters
-constexpr int kTopCounter = kTicketGroups * kTicketStride;
-constexpr int kEpochWord = (kTicketGroups + 1) * kTicketStride;
-constexpr unsigned kPollLimit = 1u << 22;  // safety net: never reached by a correct launch
+constexpr int kEpochWord = 0;                  // the mean state's header: the epoch word
+constexpr unsigned kPollBudget = 1u << 24;     // safety net: never reached by a correct launch
 
 __device__ __forceinline__ uint64_t mean_slot(unsigned tag, float v) {
   return ((uint64_t)tag << 32) | __float_as_uint(v);
 }
 
-// `block_sum` must be valid in thread 0; every thread of the workgroup calls
-// this after its last barrier.  Threads of waves other than 0 return at once.
-// `slots` holds one 64-bit slot per workgroup.
-__device__ __forceinline__ void finish_mean(float block_sum, uint64_t* slots, unsigned* ticket,
-                                            float* out, int64_t tokens) {
+// The launch's tag (epoch + 1), read by thread 0 of a workgroup when it
+// starts; 0 (unused) without a mean or in the only workgroup.  Pass the result
+// to finish_mean.
+__device__ __forceinline__ unsigned mean_begin(const unsigned* epoch, int reduce_mean) {
+  unsigned tag = 0;
+  if (reduce_mean && threadIdx.x == 0 && gridDim.x * gridDim.y > 1)
+    tag = __hip_atomic_load(epoch + kEpochWord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  return tag;
+}
+
+// `block_sum` and `tag` (from mean_begin) must be valid in thread 0; every
+// thread of the workgroup calls this after its last barrier.  Threads of waves
+// other than 0 return at once.  `slots` holds one 64-bit slot per workgroup.
+__device__ __forceinline__ void finish_mean(float block_sum, uint64_t* slots, unsigned* epoch,
+                                            unsigned tag, float* out, int64_t tokens) {
   if (threadIdx.x >= 64) return;
   const unsigned lane = threadIdx.x;
   const unsigned nblocks = gridDim.x * gridDim.y;
@@ -178,27 +183,12 @@ __device__ __forceinline__ void finish_mean(float block_sum, uint64_t* slots, un
     return;
   }
   const unsigned bid = blockIdx.y * gridDim.x + blockIdx.x;
-  const unsigned G = nblocks < (unsigned)kTicketGroups ? nblocks : (unsigned)kTicketGroups;
-  const unsigned g = bid % G;
-  const unsigned group_size = nblocks / G + (g < nblocks % G ? 1u : 0u);
-  unsigned* group_ctr = ticket + g * kTicketStride;
-  unsigned* top_ctr = ticket + kTopCounter;
-  unsigned* epoch = ticket + kEpochWord;
-  int last = 0;
-  unsigned tag = 0;
-  if (lane == 0) {
-    const unsigned e = __hip_atomic_load(epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned tg = __hip_atomic_fetch_add(group_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    tag = e + 1u;
-    if (tg == group_size - 1) {
-      __hip_atomic_store(group_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      last = __hip_atomic_fetch_add(top_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == G - 1;
-    }
-    if (!last)
+  if (bid != nblocks - 1) {
+    if (lane == 0)
       __hip_atomic_store(&slots[bid], mean_slot(tag, block_sum), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
+    return;
   }
-  if (!wave_uniform(last)) return;
   tag = (unsigned)wave_uniform((int)tag);
   const float own = __int_as_float(wave_uniform(__float_as_int(block_sum)));
   constexpr int kInFlight = 8;  // slot loads per lane in flight
@@ -206,6 +196,7 @@ __device__ __forceinline__ void finish_mean(float block_sum, uint64_t* slots, un
   // in fp64, so the sum's rounding does not grow with the number of workgroups.
   double acc = 0.0;
   bool ok = true;
+  unsigned budget = kPollBudget;
   for (unsigned base = lane; base < nblocks; base += 64u * kInFlight) {
     uint64_t v[kInFlight];
 #pragma unroll
@@ -219,9 +210,11 @@ __device__ __forceinline__ void finish_mean(float block_sum, uint64_t* slots, un
     for (int j = 0; j < kInFlight; ++j) {
       const unsigned i = base + 64u * j;
       if (i >= nblocks) break;
-      unsigned spins = 0;
-      while ((unsigned)(v[j] >> 32) != tag && spins++ < kPollLimit)
+      while ((unsigned)(v[j] >> 32) != tag && budget > 0) {
+        --budget;
+        __builtin_amdgcn_s_sleep(2);
         v[j] = __hip_atomic_load(&slots[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
       ok = ok && (unsigned)(v[j] >> 32) == tag;
       acc += (double)__uint_as_float((unsigned)v[j]);
     }
@@ -230,8 +223,7 @@ __device__ __forceinline__ void finish_mean(float block_sum, uint64_t* slots, un
   const bool all_ok = __builtin_amdgcn_ballot_w64(!ok) == 0;
   if (lane == 0) {
     out[0] = all_ok ? total / (float)tokens : __builtin_nanf("");
-    __hip_atomic_store(top_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(epoch + kEpochWord, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

@@ -242,7 +242,7 @@ lce_status run_jsd_stored(const void* xs, const void* ws, const void* xt, const 
     note_launch("jsd_stored_rows_kernel grid %lld x 256", (long long)n);
   }
   if (mean) {
-    hipError_t e = lce::launch_jsd_mean(tokens, per, out, ms.slots, ms.ticket, stream);
+    hipError_t e = lce::launch_jsd_mean(tokens, per, out, ms.slots, ms.epoch, stream);
     if (e != hipSuccess) return hip_fail(e, "kernel launch");
     note_launch("fused_jsd_merge_kernel (mean)");
   }
@@ -285,7 +285,7 @@ lce_status run_jsd_recompute(const void* xs, const void* ws, const void* xt, con
     if ((s = get_mean_state(stream, (tokens + lce::kRowThreads - 1) / lce::kRowThreads, &ms)) != LCE_OK)
       return s;
     a.mean_slots = ms.slots;
-    a.ticket = ms.ticket;
+    a.epoch = ms.epoch;
   }
 
   if ((s = run_fused(xs, ws, tokens, hidden, vocab, nullptr, false, nullptr, stream, reserved,

@@ -68,7 +68,7 @@ bool aligned(const void* p, uint64_t n) { return ((uintptr_t)p % n) == 0; }
 
 // ------------------------------------------------------------ scratch pool
 // Grow-only device buffers per (device, stream): general scratch, carved into
-// regions by Carve, and the deterministic mean's state (tickets, epoch and
+// regions by Carve, and the deterministic mean's state (epoch word and
 // slots), which nothing else writes.  A buffer that is outgrown is retired,
 // not freed: launches already queued, or recorded into a HIP graph that may be
 // replayed later, keep pointing at it.  Every buffer lives until process exit.
@@ -102,9 +102,8 @@ static lce_status grow(Scratch& s, hipStream_t stream, size_t need) {
       (void)hipGetLastError();
       return fail(LCE_ERR_OOM, "hipMalloc of %zu bytes of scratch failed: %s", bytes, hipGetErrorName(e));
     }
-    // Ticket counters, epoch and mean slots must start at zero (kernels leave
-    // the counters at zero; a slot then only ever holds tags of earlier
-    // launches on this buffer).
+    // The epoch word and the mean slots must start at zero (a slot then only
+    // ever holds tags of earlier launches on this buffer).
     e = lce::launch_zero_u32((unsigned*)p, (int64_t)(bytes / sizeof(unsigned)), stream);
     if (e != hipSuccess) {
       (void)hipFree(p);
@@ -135,10 +134,10 @@ lce_status get_mean_state(hipStream_t stream, int64_t nslots, MeanState* out) {
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   std::lock_guard<std::mutex> lock(g_mu);
   Scratch& s = g_mean[{dev, stream}];
-  const size_t off_slots = round_up(lce::kTicketBytes, kAlign);
+  const size_t off_slots = round_up(lce::kMeanHeaderBytes, kAlign);
   lce_status st = grow(s, stream, off_slots + (size_t)(nslots > 0 ? nslots : 1) * 8u);
   if (st != LCE_OK) return st;
-  out->ticket = (unsigned*)s.ptr;
+  out->epoch = (unsigned*)s.ptr;
   out->slots = (uint64_t*)((char*)s.ptr + off_slots);
   return LCE_OK;
 }

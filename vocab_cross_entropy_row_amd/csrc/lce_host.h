@@ -53,15 +53,15 @@ struct Carve {
 // This stream's scratch, grown (outside graph capture only) to `need` bytes.
 lce_status get_scratch(hipStream_t stream, size_t need, char** out);
 
-// The deterministic mean's state for one launch: the ticket counters and the
-// epoch word (kTicketBytes), then one 64-bit (tag, partial) slot per
+// The deterministic mean's state for one launch: the epoch word (on its own
+// line of kMeanHeaderBytes), then one 64-bit (tag, partial) slot per
 // workgroup.  It lives in a buffer that only the mean reductions write, so a
 // slot can hold nothing but a tag of an earlier launch on the same buffer
 // (or zero, for a new buffer); general scratch, which other calls fill with
 // arbitrary data, never overlaps it.  One per (device, stream), grown
 // (outside graph capture only) and zeroed whole when it grows.
 struct MeanState {
-  unsigned* ticket = nullptr;
+  unsigned* epoch = nullptr;
   uint64_t* slots = nullptr;
 };
 lce_status get_mean_state(hipStream_t stream, int64_t nslots, MeanState* out);
@@ -91,10 +91,10 @@ lce_status validate_fused(const void* x, const void* w, int64_t tokens, int64_t 
 // bytes of scratch regions belong to the caller.
 //
 // Device memory a caller brings for the row kernels instead of the pool: the
-// mean's ticket counters and epoch (kTicketBytes, zero between launches),
+// mean's epoch word (kMeanHeaderBytes, zero before the first launch),
 // `max_slots` mean slots, and `general_bytes` for the split path's partials.
 struct RowWorkspace {
-  unsigned* ticket = nullptr;
+  unsigned* epoch = nullptr;
   uint64_t* slots = nullptr;
   int64_t max_slots = 0;
   char* general = nullptr;

@@ -9,10 +9,9 @@ namespace lce {
 
 constexpr int kRowThreads = 256;  // threads per workgroup of the row kernels
 
-// Bytes of mean-ticket counters at the start of the scratch buffer: 64 group
-// counters, the top counter and the epoch word, 256 bytes apart (see
-// finish_mean in lce_device.h).
-constexpr size_t kTicketBytes = 66 * 256;
+// Bytes of the mean state's header at the start of its buffer: the epoch
+// word on a 256-byte line of its own (see finish_mean in lce_device.h).
+constexpr size_t kMeanHeaderBytes = 256;
 
 // A dispatch counts its work-items in 32 bits, so blocks * threads must stay
 // below 2^32.  Launchers check it (hipErrorInvalidConfiguration); the entry
@@ -42,7 +41,7 @@ struct XentArgs {
   float* split_partials;    // Split: splits * tokens (max, sum-exp) pairs, slice-major
   float* split_zt;          // Split: tokens target logits (NaN where not held)
   uint64_t* mean_slots;     // one 64-bit (tag, partial) slot per workgroup of the last kernel
-  unsigned* ticket;         // counters zero before the launch and after it; epoch word
+  unsigned* epoch;          // the mean state's epoch word (advanced by every launch with a mean)
 };
 
 hipError_t launch_xent(const XentArgs& a, hipStream_t stream);
@@ -68,7 +67,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 // Losses (or their mean) from [shards][tokens][3] vocab-shard statistics.
 hipError_t launch_stats_merge(const float* stats, int64_t shards, int64_t tokens,
                               const int64_t* target, int64_t vocab, float* out, int reduce_mean,
-                              uint64_t* slots, unsigned* ticket, hipStream_t stream);
+                              uint64_t* slots, unsigned* epoch, hipStream_t stream);
 
 // Fused projection + cross-entropy.
 struct FusedArgs {
@@ -88,7 +87,7 @@ struct FusedArgs {
   float* seg_partials;    // segments * tokens (max, sum-exp) pairs
   float* target_logit;    // tokens fp32
   uint64_t* mean_slots;
-  unsigned* ticket;
+  unsigned* epoch;
 };
 
 // Logit gradient of the fused projection for a block of tokens, written as
@@ -145,7 +144,7 @@ struct JsdArgs {
   int segments;
   float* partials;          // [segments, tokens]
   uint64_t* mean_slots;
-  unsigned* ticket;
+  unsigned* epoch;
 };
 int jsd_segments(int64_t tokens, int64_t vocab, int num_cus);
 // The fused kernel's JSD mode alone (per-segment sums into partials).
@@ -168,7 +167,7 @@ struct JsdRowsArgs {
 hipError_t launch_jsd_rows(const JsdRowsArgs& a, hipStream_t stream);
 // Deterministic mean of `tokens` per-token values into out[0].
 hipError_t launch_jsd_mean(int64_t tokens, const float* per_token, float* out, uint64_t* slots,
-                           unsigned* ticket, hipStream_t stream);
+                           unsigned* epoch, hipStream_t stream);
 
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t stream);
 hipError_t launch_zero_u32(unsigned* p, int64_t n, hipStream_t stream);

@@ -1,6 +1,6 @@
 // Row cross-entropy for callers that cannot allocate (lce_xent_fwd_noalloc):
 // the same kernels and path selection as lce_xent_fwd, with the scratch they
-// need -- the mean's ticket counters, epoch word and per-workgroup slots, and
+// need -- the mean's epoch word and per-workgroup slots, and
 // the split path's per-slice partials -- in one file-scope device array
 // instead of the library's grow-only pool.  The call makes no hipMalloc or
 // hipFree and uses no allocating library routine.
@@ -16,12 +16,12 @@
 
 namespace lce {
 
-// Layout of the array: ticket counters and epoch (kTicketBytes), then 2^19
+// Layout of the array: the mean's epoch word (kMeanHeaderBytes), then 2^19
 // 64-bit mean slots (4 MiB: a mean over up to 2^23 rows of <= 32 KiB on the
 // one-wave-per-row path, 16 rows per workgroup), then the split path's
 // (max, sum-exp) partials in the rest (8 bytes per row and slice).
 constexpr size_t kStaticBytes = size_t(8) << 20;
-constexpr size_t kSlotsOff = kTicketBytes;
+constexpr size_t kSlotsOff = kMeanHeaderBytes;
 constexpr int64_t kMaxSlots = int64_t(1) << 19;
 constexpr size_t kGeneralOff = kSlotsOff + (size_t)kMaxSlots * 8u;
 constexpr size_t kGeneralBytes = kStaticBytes - kGeneralOff;
@@ -36,7 +36,7 @@ namespace {
 
 struct DeviceArray {
   unsigned char* ptr = nullptr;  // device address of `scratch` on this GPU
-  bool cleared = false;          // counters, epoch and slots zeroed by an uncaptured call
+  bool cleared = false;          // epoch word and slots zeroed by an uncaptured call
 };
 std::mutex g_mu;
 std::map<int, DeviceArray> g_arrays;
@@ -77,7 +77,7 @@ lce_status lce_xent_fwd_noalloc(const void* logits, lce_dtype dtype, int64_t tok
     }
     base = d.ptr;
     if (!d.cleared) {
-      // The first call on a GPU zeroes the counters, epoch and slots with a
+      // The first call on a GPU zeroes the epoch word and slots with a
       // kernel on the caller's stream, ahead of its own kernels.  Under graph
       // capture the clear is recorded into the graph (each replay repeats it)
       // and the next uncaptured call clears again.
@@ -94,7 +94,7 @@ lce_status lce_xent_fwd_noalloc(const void* logits, lce_dtype dtype, int64_t tok
     }
   }
   RowWorkspace ws;
-  ws.ticket = (unsigned*)base;
+  ws.epoch = (unsigned*)base;
   ws.slots = (uint64_t*)(base + lce::kSlotsOff);
   ws.max_slots = lce::kMaxSlots;
   ws.general = (char*)(base + lce::kGeneralOff);

@@ -33,17 +33,18 @@
 
 namespace lce {
 
-static_assert(kTicketBytes == (kTicketGroups + 2) * kTicketStride * sizeof(unsigned),
-              "host scratch layout must match the device ticket layout");
+static_assert(kMeanHeaderBytes >= (kEpochWord + 1) * sizeof(unsigned),
+              "host mean-state layout must hold the device's epoch word");
 
 // ------------------------------------------------------------ one wave per row
 // WAVES rows (one per wave) per workgroup.  With a mean, larger workgroups
-// mean fewer partials and fewer ticket hand-offs.
+// mean fewer partials to hand off.
 template <typename T, int U, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void xent_wave_rows_kernel(
     const T* __restrict__ logits, int64_t tokens, int vocab, const int64_t* __restrict__ target,
     int64_t vocab_start, float* __restrict__ stats, float* __restrict__ out,
-    uint64_t* __restrict__ slots, unsigned* __restrict__ ticket, int reduce_mean) {
+    uint64_t* __restrict__ slots, unsigned* __restrict__ epoch, int reduce_mean) {
+  const unsigned mean_tag = mean_begin(epoch, reduce_mean);
   const int lane = threadIdx.x & 63;
   const int wave = wave_uniform(threadIdx.x >> 6);
   const int64_t row = (int64_t)blockIdx.x * WAVES + wave;
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(64 * WAVES) void xent_wave_rows_kernel(
     float bsum = 0.0f;
     if (threadIdx.x == 0)
       for (int w = 0; w < WAVES; ++w) bsum += wl[w];
-    finish_mean(bsum, slots, ticket, out, tokens);
+    finish_mean(bsum, slots, epoch, mean_tag, out, tokens);
   }
 }
 
@@ -114,7 +115,8 @@ template <typename T, int U>
 __global__ __launch_bounds__(kRowThreads) void xent_block_rows_kernel(
     const T* __restrict__ logits, int64_t tokens, int vocab, const int64_t* __restrict__ target,
     int64_t vocab_start, float* __restrict__ stats, float* __restrict__ out,
-    uint64_t* __restrict__ slots, unsigned* __restrict__ ticket, int reduce_mean) {
+    uint64_t* __restrict__ slots, unsigned* __restrict__ epoch, int reduce_mean) {
+  const unsigned mean_tag = mean_begin(epoch, reduce_mean);
   const int64_t row = blockIdx.x;
   const T* rp = logits + row * (int64_t)vocab;
   const int64_t t = target[row];
@@ -149,7 +151,7 @@ __global__ __launch_bounds__(kRowThreads) void xent_block_rows_kernel(
   if (!reduce_mean) {
     if (threadIdx.x == 0) out[row] = loss;
   } else {
-    finish_mean(loss, slots, ticket, out, tokens);
+    finish_mean(loss, slots, epoch, mean_tag, out, tokens);
   }
 }
 
@@ -201,7 +203,8 @@ __global__ __launch_bounds__(kRowThreads) void xent_split_partial_kernel(
 __global__ __launch_bounds__(kRowThreads) void xent_split_merge_kernel(
     int64_t tokens, int S, const float2* __restrict__ part, const float* __restrict__ zt_in,
     float* __restrict__ stats, float* __restrict__ out, uint64_t* __restrict__ slots,
-    unsigned* __restrict__ ticket, int reduce_mean) {
+    unsigned* __restrict__ epoch, int reduce_mean) {
+  const unsigned mean_tag = mean_begin(epoch, reduce_mean);
   const int64_t row = (int64_t)blockIdx.x * kRowThreads + threadIdx.x;
   float loss = 0.0f;
   if (row < tokens) {
@@ -232,7 +235,7 @@ __global__ __launch_bounds__(kRowThreads) void xent_split_merge_kernel(
       if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
       __syncthreads();
     }
-    finish_mean(red[0], slots, ticket, out, tokens);
+    finish_mean(red[0], slots, epoch, mean_tag, out, tokens);
   }
 }
 
@@ -244,7 +247,8 @@ __global__ __launch_bounds__(kRowThreads) void xent_split_merge_kernel(
 __global__ __launch_bounds__(kRowThreads) void xent_stats_merge_kernel(
     const float* __restrict__ stats, int shards, int64_t tokens, const int64_t* __restrict__ target,
     int64_t vocab, float* __restrict__ out, uint64_t* __restrict__ slots,
-    unsigned* __restrict__ ticket, int reduce_mean) {
+    unsigned* __restrict__ epoch, int reduce_mean) {
+  const unsigned mean_tag = mean_begin(epoch, reduce_mean);
   const int64_t row = (int64_t)blockIdx.x * kRowThreads + threadIdx.x;
   float loss = 0.0f;
   if (row < tokens) {
@@ -285,17 +289,17 @@ __global__ __launch_bounds__(kRowThreads) void xent_stats_merge_kernel(
       if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
       __syncthreads();
     }
-    finish_mean(red[0], slots, ticket, out, tokens);
+    finish_mean(red[0], slots, epoch, mean_tag, out, tokens);
   }
 }
 
 hipError_t launch_stats_merge(const float* stats, int64_t shards, int64_t tokens,
                               const int64_t* target, int64_t vocab, float* out, int reduce_mean,
-                              uint64_t* slots, unsigned* ticket, hipStream_t st) {
+                              uint64_t* slots, unsigned* epoch, hipStream_t st) {
   const int64_t blocks = (tokens + kRowThreads - 1) / kRowThreads;
   if (!grid_fits(blocks, kRowThreads)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(xent_stats_merge_kernel, dim3((unsigned)blocks), dim3(kRowThreads), 0, st, stats,
-                     (int)shards, tokens, target, vocab, out, slots, ticket, reduce_mean);
+                     (int)shards, tokens, target, vocab, out, slots, epoch, reduce_mean);
   return hipGetLastError();
 }
 
@@ -323,7 +327,7 @@ static hipError_t launch_wave_rows_w(const XentArgs& a, hipStream_t st) {
   if (!grid_fits(blocks, 64 * WAVES)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((xent_wave_rows_kernel<T, U, WAVES>), dim3((unsigned)blocks), dim3(64 * WAVES),
                      0, st, (const T*)a.logits, a.tokens, (int)a.vocab, a.target, a.vocab_start,
-                     a.stats, a.out, a.mean_slots, a.ticket, a.reduce_mean);
+                     a.stats, a.out, a.mean_slots, a.epoch, a.reduce_mean);
   return hipGetLastError();
 }
 
@@ -341,7 +345,7 @@ static hipError_t launch_block_rows(const XentArgs& a, hipStream_t st) {
   if (!grid_fits(a.tokens, kRowThreads)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((xent_block_rows_kernel<T, U>), dim3((unsigned)a.tokens), dim3(kRowThreads), 0,
                      st, (const T*)a.logits, a.tokens, (int)a.vocab, a.target, a.vocab_start,
-                     a.stats, a.out, a.mean_slots, a.ticket, a.reduce_mean);
+                     a.stats, a.out, a.mean_slots, a.epoch, a.reduce_mean);
   return hipGetLastError();
 }
 
@@ -357,7 +361,7 @@ static hipError_t launch_split(const XentArgs& a, hipStream_t st) {
   const int64_t blocks = (a.tokens + kRowThreads - 1) / kRowThreads;
   hipLaunchKernelGGL(xent_split_merge_kernel, dim3((unsigned)blocks), dim3(kRowThreads), 0, st,
                      a.tokens, a.splits, (const float2*)a.split_partials, (const float*)a.split_zt,
-                     a.stats, a.out, a.mean_slots, a.ticket, a.reduce_mean);
+                     a.stats, a.out, a.mean_slots, a.epoch, a.reduce_mean);
   return hipGetLastError();
 }
 
