@@ -149,10 +149,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // After the last row the chain is the last partial's store and one read of
 // it.  Agent-scope atomics are coherent across the XCDs (each has its own L2)
 // without writing back or invalidating an L2.  The finisher's polling is
-// bounded (kPollBudget re-reads in all, a short sleep between them): a launch
-// that runs out of it writes NaN instead of hanging.
+// bounded (kPollBudget re-reads per lane, a short sleep between them): a
+// launch that runs out of it writes NaN instead of hanging.
 //
-// Only wave 0 takes part: the other waves of the workgroup retire at once.
+// In the other workgroups only thread 0 stores; the finisher's waves all read.
 constexpr int kEpochWord = 0;                  // the mean state's header: the epoch word
 constexpr unsigned kPollBudget = 1u << 24;     // safety net: never reached by a correct launch
 
@@ -171,44 +171,59 @@ __device__ __forceinline__ unsigned mean_begin(const unsigned* epoch, int reduce
 }
 
 // `block_sum` and `tag` (from mean_begin) must be valid in thread 0; every
-// thread of the workgroup calls this after its last barrier.  Threads of waves
-// other than 0 return at once.  `slots` holds one 64-bit slot per workgroup.
+// thread of the workgroup calls this after its last barrier.  `slots` holds
+// one 64-bit slot per workgroup.  In the finisher every wave reads a share of
+// the slots (slot i goes to wave (i / 64) mod W and lane i mod 64), each lane
+// adding its share in fp64 in slot order; the waves' sums are then added in
+// wave order.
 __device__ __forceinline__ void finish_mean(float block_sum, uint64_t* slots, unsigned* epoch,
                                             unsigned tag, float* out, int64_t tokens) {
-  if (threadIdx.x >= 64) return;
-  const unsigned lane = threadIdx.x;
   const unsigned nblocks = gridDim.x * gridDim.y;
   if (nblocks == 1) {  // the only workgroup: no hand-off (same result as the general path)
-    if (lane == 0) out[0] = block_sum / (float)tokens;
+    if (threadIdx.x == 0) out[0] = block_sum / (float)tokens;
     return;
   }
   const unsigned bid = blockIdx.y * gridDim.x + blockIdx.x;
   if (bid != nblocks - 1) {
-    if (lane == 0)
+    if (threadIdx.x == 0)
       __hip_atomic_store(&slots[bid], mean_slot(tag, block_sum), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
-  tag = (unsigned)wave_uniform((int)tag);
-  const float own = __int_as_float(wave_uniform(__float_as_int(block_sum)));
+  constexpr int kMaxWaves = 16;
+  __shared__ unsigned fin_tag;
+  __shared__ float fin_own, fin_sum[kMaxWaves];
+  __shared__ int fin_bad[kMaxWaves];
+  const unsigned lane = threadIdx.x & 63u;
+  const unsigned wave = threadIdx.x >> 6;
+  const unsigned W = (blockDim.x + 63u) >> 6;  // at most kMaxWaves
+  if (threadIdx.x == 0) {
+    fin_tag = tag;
+    fin_own = block_sum;
+  }
+  __syncthreads();
+  tag = fin_tag;
+  const float own = fin_own;
   constexpr int kInFlight = 8;  // slot loads per lane in flight
-  // Each lane adds its share (nblocks / 64 partials, millions for the largest grids)
-  // in fp64, so the sum's rounding does not grow with the number of workgroups.
+  const unsigned stride = 64u * W;
+  // Each lane adds its share (nblocks / (64 W) partials, up to hundreds of
+  // thousands for the largest grids) in fp64, so the sum's rounding does not
+  // grow with the number of workgroups.
   double acc = 0.0;
   bool ok = true;
   unsigned budget = kPollBudget;
-  for (unsigned base = lane; base < nblocks; base += 64u * kInFlight) {
+  for (unsigned base = lane + 64u * wave; base < nblocks; base += stride * kInFlight) {
     uint64_t v[kInFlight];
 #pragma unroll
     for (int j = 0; j < kInFlight; ++j) {
-      const unsigned i = base + 64u * j;
+      const unsigned i = base + stride * j;
       v[j] = (i < nblocks && i != bid)
                  ? __hip_atomic_load(&slots[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                  : mean_slot(tag, own);
     }
 #pragma unroll
     for (int j = 0; j < kInFlight; ++j) {
-      const unsigned i = base + 64u * j;
+      const unsigned i = base + stride * j;
       if (i >= nblocks) break;
       while ((unsigned)(v[j] >> 32) != tag && budget > 0) {
         --budget;
@@ -219,9 +234,20 @@ __device__ __forceinline__ void finish_mean(float block_sum, uint64_t* slots, un
       acc += (double)__uint_as_float((unsigned)v[j]);
     }
   }
-  const float total = wave_sum((float)acc);
-  const bool all_ok = __builtin_amdgcn_ballot_w64(!ok) == 0;
+  const float wsum = wave_sum((float)acc);
+  const bool wave_ok = __builtin_amdgcn_ballot_w64(!ok) == 0;
   if (lane == 0) {
+    fin_sum[wave] = wsum;
+    fin_bad[wave] = wave_ok ? 0 : 1;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float total = 0.0f;
+    bool all_ok = true;
+    for (unsigned w = 0; w < W; ++w) {
+      total += fin_sum[w];
+      all_ok = all_ok && fin_bad[w] == 0;
+    }
     out[0] = all_ok ? total / (float)tokens : __builtin_nanf("");
     __hip_atomic_store(epoch + kEpochWord, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
