@@ -307,12 +307,36 @@ def time_backward(w, torch, lce, steps: int, warmup: int) -> dict:
     esize = 4 if w.dtype == "f32" else 2
     b = tensor_bytes([(w.tokens * w.vocab, esize), (w.tokens * w.vocab, esize), (w.tokens, 8),
                       (1 if w.reduction == "mean" else w.tokens, 4)])
-    del reps, outs
+    # A training step's two halves: the forward then the backward (two calls), against
+    # both in one call (lce_xent_fwd_bwd), on the same replicas.
+    losses = [torch.empty((1,) if w.reduction == "mean" else w.target_shape, dtype=torch.float32,
+                          device="cuda") for _ in range(R)]
+
+    def fwd(i):
+        z, t = reps[i % R]
+        lce.xent(z, t, w.reduction, out=losses[i % R])
+
+    def fwd_bwd(i):
+        z, t = reps[i % R]
+        lce.xent_fwd_bwd(z, t, grad, w.reduction, out=losses[i % R], dlogits=outs[i % R])
+    fwd_bwd(0)
+    fb_launch = lce.lce_last_launch()
+    fwd_us = spread_of(graph_replays(fwd, steps, max(warmup, R)))["median_us"]
+    fb = spread_of(graph_replays(fwd_bwd, steps, max(warmup, R)))
+    del reps, outs, losses
     torch.cuda.empty_cache()
     gbs = b / (us * 1e-6) / 1e9
+    fb_gbs = b / (fb["median_us"] * 1e-6) / 1e9
     return {"us_per_step": round(us, 3), "replicas": R, "spread": sp, "launch": launch,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": b}}
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": b},
+            "training_step": {"forward_us": round(fwd_us, 3),
+                              "forward_then_backward_us": round(fwd_us + us, 3),
+                              "fwd_bwd_us": round(fb["median_us"], 3), "fwd_bwd_spread": fb,
+                              "fwd_bwd_launch": fb_launch,
+                              "fwd_bwd_roofline": {"bound": "hbm", "achieved": round(fb_gbs, 1),
+                                                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                                   "frac": round(fb_gbs / HBM_PEAK_GBS, 4)}}}
 
 
 def time_logprob_sums(torch, lce, lce_synth, steps: int, warmup: int) -> dict:
@@ -358,13 +382,33 @@ def time_fused_bwd(torch, lce, lce_synth, steps: int, warmup: int) -> dict:
     same = bool(torch.equal(dx, ref[0]) and torch.equal(dw, ref[1]))
     flops = 3 * fused_flops(w.tokens, w.hidden, w.vocab)
     tf = flops / (us * 1e-6) / 1e12
+    # A training step: the forward call then this one, against the loss and both
+    # gradients from one call (lce_fused_linear_xent_fwd_bwd).
+    loss = torch.empty(1, dtype=torch.float32, device="cuda")
+    fwd_us = spread_of(graph_replays(lambda i: lce.fused_linear_xent(x, W, t, "mean", out=loss),
+                                     steps, max(1, warmup), replays=5))["median_us"]
+
+    def fwd_bwd(i=0):
+        lce.fused_linear_xent_fwd_bwd(x, W, t, g, "mean", out=loss, dx=dx, dweight=dw)
+    fwd_bwd()
+    fb_launch = lce.lce_last_launch()
+    fb = spread_of(graph_replays(fwd_bwd, steps, max(1, warmup), replays=5))
+    fb_same = bool(torch.equal(dx, ref[0]) and torch.equal(dw, ref[1]))
+    fb_tf = flops / (fb["median_us"] * 1e-6) / 1e12
     del x, W, t, dx, dw, ref
     torch.cuda.empty_cache()
     return {"shape": f"tokens {w.tokens}, hidden {w.hidden}, vocab {w.vocab}, mean; dx and dW fp32",
             "us_per_step": round(us, 1), "spread": sp, "launch": launch,
             "graph_matches_eager": same, "algorithmic_flops": flops,
             "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_DENSE_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tf / BF16_DENSE_TFLOPS, 4)}}
+                         "unit": "TFLOP/s", "frac": round(tf / BF16_DENSE_TFLOPS, 4)},
+            "training_step": {"forward_us": round(fwd_us, 1),
+                              "forward_then_backward_us": round(fwd_us + us, 1),
+                              "fwd_bwd_us": round(fb["median_us"], 1), "fwd_bwd_spread": fb,
+                              "fwd_bwd_launch": fb_launch, "fwd_bwd_gradients_match": fb_same,
+                              "fwd_bwd_roofline": {"bound": "mfma", "achieved": round(fb_tf, 1),
+                                                   "peak": BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
+                                                   "frac": round(fb_tf / BF16_DENSE_TFLOPS, 4)}}}
 
 
 def time_jsd(torch, lce, lce_synth, steps: int, warmup: int) -> dict:
@@ -1006,8 +1050,11 @@ def main(argv=None) -> int:
         for bname in ("megatron_bf16_2048x4x4096_none", "ce_f32_16384x4096_mean"):
             bw = lce_synth.WORKLOADS[bname]
             backward[bname] = time_backward(bw, torch, lce, min(args.steps, 200), args.warmup)
+            ts = backward[bname]["training_step"]
             print(f"[bench] backward {bname}: {backward[bname]['us_per_step']:.2f} µs/step "
-                  f"({backward[bname]['roofline']['achieved']} GB/s)", file=sys.stderr, flush=True)
+                  f"({backward[bname]['roofline']['achieved']} GB/s); forward + backward "
+                  f"{ts['forward_then_backward_us']:.2f} µs in two calls, {ts['fwd_bwd_us']:.2f} µs "
+                  f"in one", file=sys.stderr, flush=True)
     if "shard" in extras:
         shard = time_vocab_shard(torch, lce, lce_synth, 8, min(args.steps, 200), args.warmup)
         print(f"[bench] vocab shard tp=8: partial {shard['partial_us']:.2f} µs (plain read of "
@@ -1032,7 +1079,9 @@ def main(argv=None) -> int:
     if "fused_bwd" in extras:
         fbwd = time_fused_bwd(torch, lce, lce_synth, min(args.steps, 5), 2)
         print(f"[bench] fused backward: {fbwd['us_per_step']:.1f} µs "
-              f"({fbwd['roofline']['achieved']} TFLOP/s over 3*2THV)", file=sys.stderr, flush=True)
+              f"({fbwd['roofline']['achieved']} TFLOP/s over 3*2THV); forward + backward "
+              f"{fbwd['training_step']['forward_then_backward_us']:.1f} µs in two calls, "
+              f"{fbwd['training_step']['fwd_bwd_us']:.1f} µs in one", file=sys.stderr, flush=True)
 
     probe = None
     if "stream_read" in extras and "megatron_bf16_2048x4x4096_none" in results:

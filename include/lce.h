@@ -68,7 +68,7 @@ extern "C" {
 #define LCE_API __attribute__((visibility("default")))
 
 #define LCE_VERSION_MAJOR 0
-#define LCE_VERSION_MINOR 5
+#define LCE_VERSION_MINOR 6
 #define LCE_VERSION_PATCH 0
 
 /* The enums are passed as int.  A caller may pass any int value (a bad one is
@@ -174,9 +174,10 @@ LCE_API lce_status lce_xent_fwd_noalloc(const void* logits, lce_dtype dtype, int
  *              LCE_REDUCTION_MEAN (then g_i = grad[0] / tokens), `tokens`
  *              elements for LCE_REDUCTION_NONE (g_i = grad[i]).
  *   dlogits    device, same dtype and layout as logits (bf16 results are
- *              rounded to nearest even).  May be the logits buffer itself
- *              (computed in place); must not otherwise overlap logits, and
- *              must not overlap target or grad.
+ *              rounded to nearest even), starting at the same byte offset
+ *              modulo 16 as logits (else LCE_ERR_UNSUPPORTED).  May be the
+ *              logits buffer itself (computed in place); must not otherwise
+ *              overlap logits, and must not overlap target or grad.
  *   stream     HIP stream.
  *
  * A row whose target is outside [0, vocab) gets a NaN gradient row.  Rows of
@@ -186,6 +187,33 @@ LCE_API lce_status lce_xent_fwd_noalloc(const void* logits, lce_dtype dtype, int
 LCE_API lce_status lce_xent_bwd(const void* logits, lce_dtype dtype, int64_t tokens, int64_t vocab,
                         const int64_t* target, lce_reduction reduction, const float* grad,
                         void* dlogits, hipStream_t stream);
+
+/*
+ * The forward and the backward of the row cross-entropy in one call: the
+ * losses (or their mean) of lce_xent_fwd and the logit gradient of
+ * lce_xent_bwd, for a training step whose output gradient `grad` is known
+ * before the loss (for a mean loss, usually 1).  Rows of up to 32 KiB are read
+ * once and the gradient written once, against one read for lce_xent_fwd and
+ * a read and a write for lce_xent_bwd; the loss comes from the same row state
+ * as the gradient.
+ *
+ *   logits, dtype, tokens, vocab, target, reduction: as lce_xent_fwd.
+ *   grad, dlogits: as lce_xent_bwd (dlogits may be the logits buffer).
+ *   out        device fp32, as lce_xent_fwd's; must not overlap logits,
+ *              target, grad or dlogits.
+ *   stream     HIP stream.
+ *
+ * dlogits is bitwise what lce_xent_bwd writes.  The losses agree with
+ * lce_xent_fwd's within the forward's tolerance but not always bitwise: for
+ * rows of up to 32 KiB they come from the gradient kernel's own fold of the
+ * row (the running-maximum fold rather than the forward kernels' fixed
+ * reference).  A row whose target is outside [0, vocab) has a NaN loss (and
+ * a NaN mean) and a NaN gradient row.  tokens == 0 writes NaN for a mean and
+ * nothing else.  Returns as lce_xent_fwd.
+ */
+LCE_API lce_status lce_xent_fwd_bwd(const void* logits, lce_dtype dtype, int64_t tokens, int64_t vocab,
+                                    const int64_t* target, lce_reduction reduction, const float* grad,
+                                    float* out, void* dlogits, hipStream_t stream);
 
 /*
  * Vocab-shard statistics: the per-row quantities one device contributes when
@@ -342,6 +370,33 @@ LCE_API lce_status lce_fused_linear_xent_bwd(const void* x, const void* weight, 
                                      int64_t hidden, int64_t vocab, const int64_t* target,
                                      lce_reduction reduction, const float* grad, float* dx,
                                      float* dweight, hipStream_t stream);
+
+/*
+ * The forward and the backward of the fused projection + cross-entropy in
+ * one call: the losses (or their mean) of lce_fused_linear_xent_fwd together
+ * with dx and dweight of lce_fused_linear_xent_bwd, for a training step whose
+ * output gradient `grad` is known before the loss.  The backward's first
+ * pass over the head already forms every token's log-sum-exp; it also
+ * finishes the losses, so the separate forward pass is not needed.
+ *
+ *   x, weight, tokens, hidden, vocab, target, reduction, grad, dx, dweight,
+ *             stream: as lce_fused_linear_xent_bwd.
+ *   out       device fp32, as lce_fused_linear_xent_fwd's; must not overlap
+ *             x, weight, target, grad, dx or dweight.
+ *
+ * dx and dweight are bitwise what lce_fused_linear_xent_bwd writes.  The
+ * losses are bitwise those of lce_fused_linear_xent_fwd when one chunk of
+ * the backward's plan holds every token or the logits are recomputed.  With
+ * several chunks of stored logits, each chunk's losses come from its own
+ * vocab segmentation and a mean is the fixed-order mean of the per-token
+ * losses: both agree with the forward's within its tolerance, and are
+ * deterministic.  tokens == 0 writes NaN for a mean and zeros into dweight.
+ * Returns as lce_fused_linear_xent_bwd.
+ */
+LCE_API lce_status lce_fused_linear_xent_fwd_bwd(const void* x, const void* weight, int64_t tokens,
+                                                 int64_t hidden, int64_t vocab, const int64_t* target,
+                                                 lce_reduction reduction, const float* grad, float* out,
+                                                 float* dx, float* dweight, hipStream_t stream);
 
 /*
  * Generalized Jensen-Shannon divergence between a student and a teacher

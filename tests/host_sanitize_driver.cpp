@@ -59,6 +59,15 @@ int call(const std::string& fn, const Args& a) {
   if (fn == "lce_xent_bwd" && k == 8)
     return lce_xent_bwd(a.p(0), (lce_dtype)a.e(1), a.n(2), a.n(3), (const int64_t*)a.p(4),
                         (lce_reduction)a.e(5), (const float*)a.p(6), (void*)a.p(7), nullptr);
+  if (fn == "lce_xent_fwd_bwd" && k == 9)
+    return lce_xent_fwd_bwd(a.p(0), (lce_dtype)a.e(1), a.n(2), a.n(3), (const int64_t*)a.p(4),
+                            (lce_reduction)a.e(5), (const float*)a.p(6), (float*)a.p(7),
+                            (void*)a.p(8), nullptr);
+  if (fn == "lce_fused_linear_xent_fwd_bwd" && k == 11)
+    return lce_fused_linear_xent_fwd_bwd(a.p(0), a.p(1), a.n(2), a.n(3), a.n(4),
+                                         (const int64_t*)a.p(5), (lce_reduction)a.e(6),
+                                         (const float*)a.p(7), (float*)a.p(8), (float*)a.p(9),
+                                         (float*)a.p(10), nullptr);
   if (fn == "lce_fused_linear_logprob_sums" && k == 8)
     return lce_fused_linear_logprob_sums(a.p(0), a.p(1), a.n(2), a.n(3), a.n(4), a.n(5),
                                          (const int64_t*)a.p(6), (float*)a.p(7), nullptr);

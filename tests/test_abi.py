@@ -46,7 +46,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lce.lce_version() == 500
+    assert lce.lce_version() == 600
     names = [lce.lce_status_string(s) for s in range(6)]
     assert names == ["LCE_OK", "LCE_ERR_INVALID_ARG", "LCE_ERR_UNSUPPORTED", "LCE_ERR_ALIAS",
                      "LCE_ERR_OOM", "LCE_ERR_HIP"]
@@ -238,6 +238,7 @@ BWD_CASES = [
     (dict(vocab=0), lce.LCE_ERR_INVALID_ARG, "vocab"),
     (dict(grad=FAKE + (2 << 20) + 1), lce.LCE_ERR_INVALID_ARG, "aligned"),
     (dict(dlogits=FAKE + (3 << 20) + 2), lce.LCE_ERR_INVALID_ARG, "aligned"),
+    (dict(dlogits=FAKE + (3 << 20) + 4), lce.LCE_ERR_UNSUPPORTED, "modulo 16"),
     (dict(dlogits=FAKE + 64), lce.LCE_ERR_ALIAS, "same buffer"),
     (dict(dlogits=FAKE + (1 << 20) - 256), lce.LCE_ERR_ALIAS, "target"),
     (dict(dlogits=FAKE + (2 << 20) - 256), lce.LCE_ERR_ALIAS, "grad"),
@@ -254,6 +255,41 @@ def test_bwd_argument_errors(lib, kw, status, needle):
 
 def test_bwd_empty_is_a_no_op(lib):
     assert lce.lce_xent_bwd(0, lce.LCE_F32, 0, 8, 0, lce.LCE_REDUCTION_NONE, 0, 0, 0) == lce.LCE_OK
+
+
+def _fwd_bwd(logits=FAKE, dtype=lce.LCE_F32, tokens=16, vocab=32, target=FAKE + (1 << 20),
+             reduction=lce.LCE_REDUCTION_MEAN, grad=FAKE + (2 << 20), out=FAKE + (4 << 20),
+             dlogits=FAKE + (3 << 20)):
+    return lce.lce_xent_fwd_bwd(logits, dtype, tokens, vocab, target, reduction, grad, out, dlogits, 0)
+
+
+# The forward's checks on out, then the backward's on grad and dlogits, then out
+# against the gradient's buffers.
+FWD_BWD_CASES = [
+    (dict(out=0), lce.LCE_ERR_INVALID_ARG, "out is NULL"),
+    (dict(out=FAKE + (4 << 20) + 2), lce.LCE_ERR_INVALID_ARG, "out is not"),
+    (dict(out=FAKE + 128), lce.LCE_ERR_ALIAS, "out overlaps logits"),
+    (dict(out=FAKE + (1 << 20) + 8), lce.LCE_ERR_ALIAS, "out overlaps target"),
+    (dict(out=FAKE + (3 << 20) + 4), lce.LCE_ERR_ALIAS, "out overlaps dlogits"),
+    (dict(out=FAKE + (2 << 20)), lce.LCE_ERR_ALIAS, "out overlaps grad"),
+    (dict(grad=0), lce.LCE_ERR_INVALID_ARG, "grad is NULL"),
+    (dict(dlogits=0), lce.LCE_ERR_INVALID_ARG, "dlogits is NULL"),
+    (dict(dlogits=FAKE + 64), lce.LCE_ERR_ALIAS, "same buffer"),
+    (dict(reduction=3), lce.LCE_ERR_INVALID_ARG, "reduction"),
+    (dict(logits=0), lce.LCE_ERR_INVALID_ARG, "logits is NULL"),
+    (dict(tokens=1 << 26, target=FAKE + (1 << 40), grad=FAKE + (1 << 41), dlogits=FAKE + (1 << 42),
+          out=FAKE + (1 << 43)), lce.LCE_ERR_UNSUPPORTED, "work-items"),
+]
+
+
+@pytest.mark.parametrize("kw,status,needle", FWD_BWD_CASES)
+def test_fwd_bwd_argument_errors(lib, kw, status, needle):
+    assert _fwd_bwd(**kw) == status
+    assert needle in lce.lce_last_error()
+
+
+def test_fwd_bwd_empty_none_is_a_no_op(lib):
+    assert lce.lce_xent_fwd_bwd(0, lce.LCE_F32, 0, 8, 0, lce.LCE_REDUCTION_NONE, 0, 0, 0, 0) == lce.LCE_OK
 
 
 def _sums(x=FAKE, w=FAKE + (1 << 24), batch=2, seq=4, hidden=64, vocab=100, target=FAKE + (1 << 28),
@@ -347,4 +383,32 @@ FBWD_CASES = [
 @pytest.mark.parametrize("kw,status,needle", FBWD_CASES)
 def test_fused_bwd_argument_errors(lib, kw, status, needle):
     assert _fbwd(**kw) == status
+    assert needle in lce.lce_last_error()
+
+
+def _ffb(x=FAKE, w=FAKE + (1 << 24), tokens=8, hidden=64, vocab=100, target=FAKE + (1 << 28),
+         reduction=lce.LCE_REDUCTION_MEAN, grad=FAKE + (1 << 29), out=FAKE + (1 << 32),
+         dx=FAKE + (1 << 30), dw=FAKE + (1 << 31)):
+    return lce.lce_fused_linear_xent_fwd_bwd(x, w, tokens, hidden, vocab, target, reduction, grad,
+                                             out, dx, dw, 0)
+
+
+FUSED_FWD_BWD_CASES = [
+    (dict(out=0), lce.LCE_ERR_INVALID_ARG, "out is NULL"),
+    (dict(out=FAKE + 32), lce.LCE_ERR_ALIAS, "x"),
+    (dict(out=FAKE + (1 << 28) + 16), lce.LCE_ERR_ALIAS, "target"),
+    (dict(out=FAKE + (1 << 29)), lce.LCE_ERR_ALIAS, "out overlaps grad"),
+    (dict(out=FAKE + (1 << 30) + 64), lce.LCE_ERR_ALIAS, "out overlaps dx"),
+    (dict(out=FAKE + (1 << 31) + 64), lce.LCE_ERR_ALIAS, "out overlaps dweight"),
+    (dict(grad=0), lce.LCE_ERR_INVALID_ARG, "grad is NULL"),
+    (dict(dx=0, dw=0), lce.LCE_ERR_INVALID_ARG, "both NULL"),
+    (dict(hidden=12), lce.LCE_ERR_UNSUPPORTED, "multiple of 8"),
+    (dict(vocab=1 << 23), lce.LCE_ERR_UNSUPPORTED, "fused backward"),
+    (dict(reduction=5), lce.LCE_ERR_INVALID_ARG, "reduction"),
+]
+
+
+@pytest.mark.parametrize("kw,status,needle", FUSED_FWD_BWD_CASES)
+def test_fused_fwd_bwd_argument_errors(lib, kw, status, needle):
+    assert _ffb(**kw) == status
     assert needle in lce.lce_last_error()

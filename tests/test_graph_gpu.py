@@ -2,7 +2,8 @@
 
 The benchmark times graph replays, so replays must give the eager results bit for
 bit: every kernel path (one wave per row, one workgroup per row, split rows, the
-fused projection, fused linear + JSD with stored logits, in chunks, and recomputed)
+fused projection, fused linear + JSD with stored logits, in chunks, and recomputed,
+and the forward and backward in one call, row and fused, in chunks and not)
 with and without the deterministic mean, whose epoch word each replay must advance so
 that the next one tells its partials from those left by earlier launches.  Between replays the program does eager
 work of its own (other liblce calls on the same stream, torch kernels, host
@@ -66,8 +67,42 @@ def _jsd_case(seed, tokens, hidden, vocab, reduction, env):
     return call, out
 
 
+def _row_fwd_bwd_case(seed, rows, vocab, dtype, reduction, env):
+    f = lce_synth.normal_f32(seed, 9, rows, vocab, 1.5)
+    z = to_dev(f if dtype == "f32" else lce_synth.f32_to_bf16_bits(f))
+    t = torch.from_numpy(lce_synth.targets(seed + 1, rows, vocab)).cuda()
+    g = torch.full((1,) if reduction == "mean" else (rows,), 0.75, device="cuda")
+    out = torch.empty((1,) if reduction == "mean" else (rows,), dtype=torch.float32, device="cuda")
+    d = torch.empty_like(z)
+
+    def call():
+        with forced_env(**env):
+            lce.xent_fwd_bwd(z, t, g, reduction, out=out, dlogits=d)
+    return call, (out, d)
+
+
+def _fused_fwd_bwd_case(seed, tokens, hidden, vocab, reduction, env):
+    x = to_dev(lce_synth.normal_bf16_bits(seed, 0, tokens, hidden, 1.0))
+    W = to_dev(lce_synth.normal_bf16_bits(seed + 1, 2, vocab, hidden, 0.1))
+    t = torch.from_numpy(lce_synth.targets(seed + 2, tokens, vocab)).cuda()
+    g = torch.ones((1,) if reduction == "mean" else (tokens,), device="cuda")
+    out = torch.empty((1,) if reduction == "mean" else (tokens,), dtype=torch.float32, device="cuda")
+    dx = torch.empty((tokens, hidden), dtype=torch.float32, device="cuda")
+    dw = torch.empty((vocab, hidden), dtype=torch.float32, device="cuda")
+
+    def call():
+        with forced_env(**env):
+            lce.fused_linear_xent_fwd_bwd(x, W, t, g, reduction, out=out, dx=dx, dweight=dw)
+    return call, (out, dx, dw)
+
+
 def _cases():
     return [
+        _row_fwd_bwd_case(114, 1000, 4096, "bf16", "mean", {}),
+        _row_fwd_bwd_case(115, 333, 1001, "f32", "none", {}),
+        _row_fwd_bwd_case(116, 200, 9000, "f32", "mean", {"LCE_BWD_PATH": "apply"}),
+        _fused_fwd_bwd_case(117, 300, 64, 1000, "mean", {}),
+        _fused_fwd_bwd_case(118, 600, 64, 1000, "mean", {"LCE_FUSED_BWD_STORE_BYTES": 256 * 1024 * 6}),
         _jsd_case(109, 300, 128, 2000, "mean", {}),
         _jsd_case(110, 520, 64, 1001, "none", {"LCE_JSD_STORE_BYTES": 256 * 1024 * 8}),
         _jsd_case(111, 200, 128, 1500, "mean", {"LCE_JSD_STORE_BYTES": 0}),
@@ -100,7 +135,7 @@ def _replay_and_check(g, s, outs, refs, between):
 def test_graph_replays_match_eager():
     cases = _cases()
     calls = [c for c, _ in cases]
-    outs = [o for _, o in cases]
+    outs = [o for _, os_ in cases for o in (os_ if isinstance(os_, tuple) else (os_,))]
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):

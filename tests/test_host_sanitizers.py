@@ -90,6 +90,8 @@ CASE_TABLES = [
     ("lce_fused_linear_logprob_sums", abi._sums, abi.SUMS_CASES),
     ("lce_fused_linear_jsd_fwd", abi._jsd, abi.JSD_CASES),
     ("lce_fused_linear_xent_bwd", abi._fbwd, abi.FBWD_CASES),
+    ("lce_xent_fwd_bwd", abi._fwd_bwd, abi.FWD_BWD_CASES),
+    ("lce_fused_linear_xent_fwd_bwd", abi._ffb, abi.FUSED_FWD_BWD_CASES),
 ]
 
 # Empty calls that are no-ops: status LCE_OK and an empty detail message.
@@ -99,6 +101,7 @@ EMPTY = [
     "lce_xent_partial_fwd 0 7 0 1 0 8 0 0 0 ",
     "lce_xent_merge 0 7 0 3 0 0 10 1 0 ",
     "lce_xent_bwd 0 8 0 0 0 8 0 1 0 0 ",
+    "lce_xent_fwd_bwd 0 9 0 0 0 8 0 1 0 0 0 ",
     f"lce_fused_linear_jsd_fwd 0 10 0 {abi.FAKE} 0 {abi.FAKE} 0 64 100 0.5 1 0 ",
 ]
 

@@ -38,7 +38,8 @@ LCE_ERR_ALIAS = 3
 LCE_ERR_OOM = 4
 LCE_ERR_HIP = 5
 
-EXPORTED = ("lce_xent_fwd", "lce_xent_fwd_noalloc", "lce_xent_bwd", "lce_fused_linear_xent_fwd", "lce_fused_linear_xent_bwd",
+EXPORTED = ("lce_xent_fwd", "lce_xent_fwd_noalloc", "lce_xent_bwd", "lce_xent_fwd_bwd",
+            "lce_fused_linear_xent_fwd", "lce_fused_linear_xent_bwd", "lce_fused_linear_xent_fwd_bwd",
             "lce_fused_linear_logprob_sums", "lce_fused_linear_jsd_fwd", "lce_xent_partial_fwd",
             "lce_xent_merge", "lce_status_string", "lce_last_error", "lce_last_launch",
             "lce_version")
@@ -78,6 +79,10 @@ def load() -> ctypes.CDLL:
     lib.lce_xent_bwd.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
                                  ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                  ctypes.c_void_p]
+    lib.lce_xent_fwd_bwd.restype = ctypes.c_int
+    lib.lce_xent_fwd_bwd.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                     ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_void_p]
     lib.lce_fused_linear_logprob_sums.restype = ctypes.c_int
     lib.lce_fused_linear_logprob_sums.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                                   ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
@@ -92,6 +97,11 @@ def load() -> ctypes.CDLL:
                                               ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
                                               ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                               ctypes.c_void_p, ctypes.c_void_p]
+    lib.lce_fused_linear_xent_fwd_bwd.restype = ctypes.c_int
+    lib.lce_fused_linear_xent_fwd_bwd.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                                  ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.lce_xent_partial_fwd.restype = ctypes.c_int
     lib.lce_xent_partial_fwd.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                          ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
@@ -139,6 +149,12 @@ def lce_xent_bwd(logits: int, dtype: int, tokens: int, vocab: int, target: int, 
                                grad or None, dlogits or None, stream or None)
 
 
+def lce_xent_fwd_bwd(logits: int, dtype: int, tokens: int, vocab: int, target: int,
+                     reduction: int, grad: int, out: int, dlogits: int, stream: int) -> int:
+    return load().lce_xent_fwd_bwd(logits or None, dtype, tokens, vocab, target or None, reduction,
+                                   grad or None, out or None, dlogits or None, stream or None)
+
+
 def lce_fused_linear_logprob_sums(x: int, weight: int, batch: int, seq: int, hidden: int,
                                   vocab: int, target: int, out: int, stream: int) -> int:
     return load().lce_fused_linear_logprob_sums(x or None, weight or None, batch, seq, hidden, vocab,
@@ -151,6 +167,14 @@ def lce_fused_linear_xent_bwd(x: int, weight: int, tokens: int, hidden: int, voc
     return load().lce_fused_linear_xent_bwd(x or None, weight or None, tokens, hidden, vocab,
                                             target or None, reduction, grad or None, dx or None,
                                             dweight or None, stream or None)
+
+
+def lce_fused_linear_xent_fwd_bwd(x: int, weight: int, tokens: int, hidden: int, vocab: int,
+                                  target: int, reduction: int, grad: int, out: int, dx: int,
+                                  dweight: int, stream: int) -> int:
+    return load().lce_fused_linear_xent_fwd_bwd(x or None, weight or None, tokens, hidden, vocab,
+                                                target or None, reduction, grad or None, out or None,
+                                                dx or None, dweight or None, stream or None)
 
 
 def lce_fused_linear_jsd_fwd(student_x: int, student_weight: int, teacher_x: int,
@@ -322,11 +346,8 @@ def xent_merge(partials, target, vocab: int, reduction: str = "mean", out=None):
     return out
 
 
-def xent_bwd(logits, target, grad, reduction: str = "mean", out=None):
-    """Gradient of :func:`xent` with respect to ``logits``: softmax minus the one-hot
-    target, scaled by ``grad`` (the gradient of the forward's output: a 1-element
-    tensor for ``"mean"``, the target's shape for ``"none"``).  Returns a tensor like
-    ``logits``; ``out`` may be ``logits`` itself (in place)."""
+def _xent_bwd_args(logits, target, grad, reduction: str) -> int:
+    """Checks shared by the row gradient calls; returns the logits' dtype code."""
     import torch
     if reduction not in _REDUCTIONS:
         raise ValueError(f"reduction must be 'mean' or 'none', got {reduction!r}")
@@ -346,15 +367,49 @@ def xent_bwd(logits, target, grad, reduction: str = "mean", out=None):
         raise ValueError("target shape must be logits shape without the vocab axis")
     if grad.numel() != (1 if reduction == "mean" else target.numel()):
         raise ValueError("grad must have 1 element (mean) or one per token (none)")
+    return dt
+
+
+def _grad_out(logits, out):
+    import torch
     if out is None:
-        out = torch.empty_like(logits)
-    elif out.shape != logits.shape or out.dtype != logits.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor like logits")
+        return torch.empty_like(logits)
+    if out.shape != logits.shape or out.dtype != logits.dtype or not out.is_contiguous():
+        raise ValueError("dlogits must be a contiguous tensor like logits")
+    return out
+
+
+def xent_bwd(logits, target, grad, reduction: str = "mean", out=None):
+    """Gradient of :func:`xent` with respect to ``logits``: softmax minus the one-hot
+    target, scaled by ``grad`` (the gradient of the forward's output: a 1-element
+    tensor for ``"mean"``, the target's shape for ``"none"``).  Returns a tensor like
+    ``logits``; ``out`` may be ``logits`` itself (in place)."""
+    dt = _xent_bwd_args(logits, target, grad, reduction)
+    out = _grad_out(logits, out)
     st = lce_xent_bwd(logits.data_ptr(), dt, target.numel(), logits.shape[-1], target.data_ptr(),
                       _REDUCTIONS[reduction], grad.data_ptr(), out.data_ptr(), _stream_of(logits))
     if st != LCE_OK:
         raise LceError(st, "lce_xent_bwd")
     return out
+
+
+def xent_fwd_bwd(logits, target, grad, reduction: str = "mean", out=None, dlogits=None):
+    """:func:`xent` and :func:`xent_bwd` in one call (``grad`` known before the loss).
+    Returns ``(loss, dlogits)``; ``dlogits`` may be ``logits`` itself (in place)."""
+    import torch
+    dt = _xent_bwd_args(logits, target, grad, reduction)
+    dlogits = _grad_out(logits, dlogits)
+    shape = (1,) if reduction == "mean" else tuple(target.shape)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=logits.device)
+    elif tuple(out.shape) != shape or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous float32 tensor of shape {shape}")
+    st = lce_xent_fwd_bwd(logits.data_ptr(), dt, target.numel(), logits.shape[-1],
+                          target.data_ptr(), _REDUCTIONS[reduction], grad.data_ptr(),
+                          out.data_ptr(), dlogits.data_ptr(), _stream_of(logits))
+    if st != LCE_OK:
+        raise LceError(st, "lce_xent_fwd_bwd")
+    return out, dlogits
 
 
 def fused_linear_logprob_sums(x, weight, target, out=None):
@@ -423,11 +478,8 @@ def fused_linear_jsd(student_x, student_weight, teacher_x, teacher_weight, beta:
     return out
 
 
-def fused_linear_xent_bwd(x, weight, target, grad, reduction: str = "mean", want_dx: bool = True,
-                          want_dweight: bool = True, dx=None, dweight=None):
-    """Gradients of :func:`fused_linear_xent` with respect to ``x`` and ``weight`` for the
-    loss-output gradient ``grad`` (one element for "mean", the target's shape for "none").
-    Returns ``(dx, dweight)`` as fp32 tensors (``None`` for one not wanted)."""
+def _fused_bwd_args(x, weight, target, grad, reduction: str, want_dx: bool, want_dweight: bool):
+    """Checks shared by the fused gradient calls; returns (tokens, hidden, vocab)."""
     import torch
     if reduction not in _REDUCTIONS:
         raise ValueError(f"reduction must be 'mean' or 'none', got {reduction!r}")
@@ -448,6 +500,16 @@ def fused_linear_xent_bwd(x, weight, target, grad, reduction: str = "mean", want
     if not (want_dx or want_dweight):
         raise ValueError("nothing to compute")
     vocab, hidden = weight.shape
+    return tokens, hidden, vocab
+
+
+def fused_linear_xent_bwd(x, weight, target, grad, reduction: str = "mean", want_dx: bool = True,
+                          want_dweight: bool = True, dx=None, dweight=None):
+    """Gradients of :func:`fused_linear_xent` with respect to ``x`` and ``weight`` for the
+    loss-output gradient ``grad`` (one element for "mean", the target's shape for "none").
+    Returns ``(dx, dweight)`` as fp32 tensors (``None`` for one not wanted)."""
+    import torch
+    tokens, hidden, vocab = _fused_bwd_args(x, weight, target, grad, reduction, want_dx, want_dweight)
     if want_dx and dx is None:
         dx = torch.empty(x.shape, dtype=torch.float32, device=x.device)
     if want_dweight and dweight is None:
@@ -459,3 +521,29 @@ def fused_linear_xent_bwd(x, weight, target, grad, reduction: str = "mean", want
     if st != LCE_OK:
         raise LceError(st, "lce_fused_linear_xent_bwd")
     return (dx if want_dx else None), (dweight if want_dweight else None)
+
+
+def fused_linear_xent_fwd_bwd(x, weight, target, grad, reduction: str = "mean",
+                              want_dx: bool = True, want_dweight: bool = True, out=None, dx=None,
+                              dweight=None):
+    """:func:`fused_linear_xent` and :func:`fused_linear_xent_bwd` in one call (``grad``
+    known before the loss).  Returns ``(loss, dx, dweight)`` (``None`` for a gradient not
+    wanted)."""
+    import torch
+    tokens, hidden, vocab = _fused_bwd_args(x, weight, target, grad, reduction, want_dx, want_dweight)
+    shape = (1,) if reduction == "mean" else tuple(target.shape)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=x.device)
+    elif tuple(out.shape) != shape or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous float32 tensor of shape {shape}")
+    if want_dx and dx is None:
+        dx = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    if want_dweight and dweight is None:
+        dweight = torch.empty((vocab, hidden), dtype=torch.float32, device=x.device)
+    st = lce_fused_linear_xent_fwd_bwd(x.data_ptr(), weight.data_ptr(), tokens, hidden, vocab,
+                                       target.data_ptr(), _REDUCTIONS[reduction], grad.data_ptr(),
+                                       out.data_ptr(), dx.data_ptr() if want_dx else 0,
+                                       dweight.data_ptr() if want_dweight else 0, _stream_of(x))
+    if st != LCE_OK:
+        raise LceError(st, "lce_fused_linear_xent_fwd_bwd")
+    return out, (dx if want_dx else None), (dweight if want_dweight else None)

@@ -25,6 +25,11 @@
 //                          its gradient.
 // dlogits may be the logits buffer itself (so neither pointer is restrict):
 // every element is read before the same thread writes it.
+//
+// With a loss output (the forward and the backward in one call), the wave
+// kernel also finishes each row's loss from the state it built, with the
+// target logit read out of the row's registers: per-token losses, or their
+// deterministic mean (finish_mean).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -104,65 +109,115 @@ __device__ __forceinline__ float row_grad_scale(const float* grad, int64_t row, 
   return reduce_mean ? grad[0] / (float)tokens : grad[row];
 }
 
+// Element `te` of chunk `k` in lane `ln` of a row held in registers (all three
+// wave-uniform): one 32-bit word selected, read with one readlane, decoded.
+template <typename T, int NCH>
+__device__ __forceinline__ float row_element(const typename Vec<T>::raw (&v)[NCH], int k, int ln,
+                                             int te) {
+  constexpr int EW = Vec<T>::kElems / 4;  // elements per 32-bit word
+  const int wi = te / EW;
+  uint32_t w = 0;
+#pragma unroll
+  for (int kk = 0; kk < NCH; ++kk) {
+    const u32x4 q = __builtin_bit_cast(u32x4, v[kk]);
+    if (kk == k) w = wi == 0 ? q[0] : wi == 1 ? q[1] : wi == 2 ? q[2] : q[3];
+  }
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)w, ln);
+  if constexpr (EW == 1) return __uint_as_float(b);
+  return __uint_as_float((te & 1) ? (b & 0xffff0000u) : (b << 16));
+}
+
 // ------------------------------------------------------------ one wave per row, row in registers
 // Lane l holds chunks l + 64k (k < NCH) of the aligned body; loads past the
 // body read nothing and stores past it are dropped (buffer resources).
-template <typename T, int NCH, int WAVES>
+// LOSS: also the row's loss into loss_out (per token, or their mean with
+// reduce_mean; `slots` and `epoch` are then the mean state).
+template <typename T, int NCH, int WAVES, bool LOSS>
 __global__ __launch_bounds__(64 * WAVES) void xent_bwd_wave_kernel(
     const T* logits, int64_t tokens, int vocab, const int64_t* __restrict__ target,
-    const float* __restrict__ grad, int reduce_mean, T* dlogits) {
+    const float* __restrict__ grad, int reduce_mean, T* dlogits, float* __restrict__ loss_out,
+    uint64_t* __restrict__ slots, unsigned* __restrict__ epoch) {
   typedef typename Vec<T>::raw raw;
   constexpr int E = Vec<T>::kElems;
+  const unsigned mean_tag = LOSS ? mean_begin(epoch, reduce_mean) : 0u;
   const int lane = threadIdx.x & 63;
   const int wave = wave_uniform(threadIdx.x >> 6);
   const int64_t row = (int64_t)blockIdx.x * WAVES + wave;
-  if (row >= tokens) return;
-  const T* rp = logits + row * (int64_t)vocab;
-  T* dp = dlogits + row * (int64_t)vocab;
-  const int64_t t = target[row];
-  const float g = row_grad_scale(grad, row, tokens, reduce_mean);
-  const RowSplit rs = row_split(rp, vocab);
-  const int n = wave_uniform(rs.nvec);
-  const __amdgpu_buffer_rsrc_t src = make_rsrc(rp + rs.head, (uint32_t)n * 16u);
-  const __amdgpu_buffer_rsrc_t dst = make_rsrc(dp + rs.head, (uint32_t)n * 16u);
+  float loss = 0.0f;
+  if (row < tokens) {
+    const T* rp = logits + row * (int64_t)vocab;
+    T* dp = dlogits + row * (int64_t)vocab;
+    const int64_t t = target[row];
+    const float g = row_grad_scale(grad, row, tokens, reduce_mean);
+    const RowSplit rs = row_split(rp, vocab);
+    const int n = wave_uniform(rs.nvec);
+    const __amdgpu_buffer_rsrc_t src = make_rsrc(rp + rs.head, (uint32_t)n * 16u);
+    const __amdgpu_buffer_rsrc_t dst = make_rsrc(dp + rs.head, (uint32_t)n * 16u);
 
-  // Head and tail elements first, and only when the row has any (a load
-  // issued behind the row's chunks would return behind them all).
-  const int ei = edge_index(rs, vocab, lane);
-  float edge = 0.0f;
-  if (wave_uniform(rs.head + rs.tail) > 0) edge = Vec<T>::scalar(rp + ei);
-  __builtin_amdgcn_sched_barrier(0);
-  raw v[NCH];
+    // Head and tail elements first, and only when the row has any (a load
+    // issued behind the row's chunks would return behind them all).
+    const int ei = edge_index(rs, vocab, lane);
+    float edge = 0.0f;
+    if (wave_uniform(rs.head + rs.tail) > 0) edge = Vec<T>::scalar(rp + ei);
+    __builtin_amdgcn_sched_barrier(0);
+    raw v[NCH];
 #pragma unroll
-  for (int k = 0; k < NCH; ++k)
-    v[k] = (raw)__builtin_amdgcn_raw_buffer_load_b128(src, (lane + 64 * k) * 16, 0, kStreamPolicy);
-  const bool has_edge = lane < rs.head + rs.tail;
+    for (int k = 0; k < NCH; ++k)
+      v[k] = (raw)__builtin_amdgcn_raw_buffer_load_b128(src, (lane + 64 * k) * 16, 0, kStreamPolicy);
+    const bool has_edge = lane < rs.head + rs.tail;
 
-  // Row state.  Chunks past the body become -inf: they fold as nothing, and
-  // their (zero) gradient is never stored.
+    // Row state.  Chunks past the body become -inf: they fold as nothing, and
+    // their (zero) gradient is never stored.
 #pragma unroll
-  for (int k = 0; k < NCH; ++k)
-    if (lane + 64 * k >= n) v[k] = Vec<T>::neg_inf();
-  Lse st = lse_empty();
-  fold_batch<T, NCH, true>(st, v);
-  if (has_edge) fold_one(st, edge);
-  const Lse r = wave_lse(st);
-  const bool valid = t >= 0 && t < (int64_t)vocab;
-  const GradRow gr = grad_row(r, g, valid);
+    for (int k = 0; k < NCH; ++k)
+      if (lane + 64 * k >= n) v[k] = Vec<T>::neg_inf();
+    Lse st = lse_empty();
+    fold_batch<T, NCH, true>(st, v);
+    if (has_edge) fold_one(st, edge);
+    const Lse r = wave_lse(st);
+    const bool valid = t >= 0 && t < (int64_t)vocab;
+    const GradRow gr = grad_row(r, g, valid);
 
-  // Target position: aligned-body chunk and element, or an edge element.
-  const int64_t tb = valid ? t - rs.head : -1;
-  const int tc = (tb >= 0 && tb < (int64_t)n * E) ? (int)(tb / E) : -1;
-  const int te = (tc >= 0) ? (int)(tb % E) : -1;
+    // Target position: aligned-body chunk and element, or an edge element.
+    const int64_t tb = valid ? t - rs.head : -1;
+    const int tc = (tb >= 0 && tb < (int64_t)n * E) ? (int)(tb / E) : -1;
+    const int te = (tc >= 0) ? (int)(tb % E) : -1;
+    if constexpr (LOSS) {
+      // The target logit: from its chunk's lane, or from the edge lane that
+      // holds it (head element t is lane t, tail element t lane head + t -
+      // (vocab - tail)).
+      float zt = 0.0f;
+      if (tc >= 0) {
+        zt = row_element<T, NCH>(v, tc >> 6, tc & 63, te);
+      } else if (valid) {
+        const int el = t < rs.head ? (int)t : rs.head + (int)(t - (vocab - rs.tail));
+        zt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(edge), el));
+      }
+      loss = valid ? lse_minus(r, zt) : __builtin_nanf("");
+    }
 #pragma unroll
-  for (int k = 0; k < NCH; ++k) {
-    const int c = lane + 64 * k;
-    store_chunk<T>(dst, c, grad_chunk<T>(v[k], gr, c == tc ? te : -1));
+    for (int k = 0; k < NCH; ++k) {
+      const int c = lane + 64 * k;
+      store_chunk<T>(dst, c, grad_chunk<T>(v[k], gr, c == tc ? te : -1));
+    }
+    if (has_edge) {
+      float d = exp2_fast(__builtin_fmaf(edge, kLog2e, -gr.M)) * gr.c;
+      if ((int64_t)ei == t) d -= gr.g;
+      Out<T>::store(dp + ei, d);
+    }
   }
-  if (has_edge) {
-    float d = exp2_fast(__builtin_fmaf(edge, kLog2e, -gr.M)) * gr.c;
-    if ((int64_t)ei == t) d -= gr.g;
-    Out<T>::store(dp + ei, d);
+  if constexpr (LOSS) {
+    if (!reduce_mean) {
+      if (row < tokens && lane == 0) loss_out[row] = loss;
+    } else {
+      __shared__ float wl[WAVES];
+      if (lane == 0) wl[wave] = loss;
+      __syncthreads();
+      float bsum = 0.0f;
+      if (threadIdx.x == 0)
+        for (int w = 0; w < WAVES; ++w) bsum += wl[w];
+      finish_mean(bsum, slots, epoch, mean_tag, loss_out, tokens);
+    }
   }
 }
 
@@ -232,15 +287,32 @@ __global__ __launch_bounds__(kRowThreads) void xent_bwd_apply_kernel(
 }
 
 // ------------------------------------------------------------ launchers
-template <typename T, int NCH>
-hipError_t launch_bwd_wave_t(const BwdArgs& a, hipStream_t st) {
-  constexpr int W = 4;
+template <typename T, int NCH, int W, bool LOSS>
+hipError_t launch_bwd_wave_w(const BwdArgs& a, hipStream_t st) {
   const int64_t blocks = (a.tokens + W - 1) / W;
   if (!grid_fits(blocks, 64 * W)) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((xent_bwd_wave_kernel<T, NCH, W>), dim3((unsigned)blocks), dim3(64 * W), 0, st,
+  hipLaunchKernelGGL((xent_bwd_wave_kernel<T, NCH, W, LOSS>), dim3((unsigned)blocks), dim3(64 * W), 0, st,
                      (const T*)a.logits, a.tokens, (int)a.vocab, a.target, a.grad, a.reduce_mean,
-                     (T*)a.dlogits);
+                     (T*)a.dlogits, a.loss_out, a.mean_slots, a.epoch);
   return hipGetLastError();
+}
+
+// Rows per workgroup: 4, and for a mean of the losses 16 (a quarter of the
+// workgroups hand a partial to the mean's finisher), or 8 for rows of 32 chunks
+// per lane (about 176 VGPRs: a 1024-thread workgroup would allow 128).
+int bwd_wave_rows(const BwdArgs& a) {
+  if (!(a.loss_out && a.reduce_mean)) return 4;
+  return a.wave_chunks >= 32 ? 8 : 16;
+}
+
+template <typename T, int NCH>
+hipError_t launch_bwd_wave_t(const BwdArgs& a, hipStream_t st) {
+  if (!a.loss_out) return launch_bwd_wave_w<T, NCH, 4, false>(a, st);
+  if (!a.reduce_mean) return launch_bwd_wave_w<T, NCH, 4, true>(a, st);
+  if constexpr (NCH >= 32)
+    return launch_bwd_wave_w<T, NCH, 8, true>(a, st);
+  else
+    return launch_bwd_wave_w<T, NCH, 16, true>(a, st);
 }
 
 template <typename T>

@@ -573,6 +573,8 @@ __global__ __launch_bounds__(TL::kThreads) void fused_xent_partial_kernel(
 
 // One thread per token: merge its `segments` partials in segment order
 // (consecutive threads read consecutive tokens of a segment), subtract z_target.
+// Writes ln sum_j e^z_j per token into lse_out when it is set, and the loss
+// (or the mean) into out when that is set; at least one of them is.
 // The partials are loaded 32 segments at a time (the default segment count
 // of the benchmark shapes), so the loads of a group are in flight together
 // instead of one memory latency per segment or per group of eight; padding
@@ -586,8 +588,8 @@ __global__ __launch_bounds__(kRowThreads) void fused_xent_merge_kernel(
   const int64_t row = (int64_t)blockIdx.x * kRowThreads + threadIdx.x;
   float loss = 0.0f;
   if (row < tokens) {
-    const int64_t t = lse_out ? -1 : target[row];
-    const float z = lse_out ? 0.0f : zt[row];
+    const int64_t t = out ? target[row] : -1;
+    const float z = out ? zt[row] : 0.0f;
     constexpr int kGroup = 32;
     Lse st = lse_empty();
     for (int s0 = 0; s0 < segments; s0 += kGroup) {
@@ -598,10 +600,9 @@ __global__ __launch_bounds__(kRowThreads) void fused_xent_merge_kernel(
 #pragma unroll
       for (int j = 0; j < kGroup; ++j) st = lse_merge(st, Lse{p[j].x, p[j].y});
     }
-    if (lse_out) {  // ln sum_j e^z_j = m + ln2 * (log2 s - (m*log2e - fp32(m*log2e)))
+    if (lse_out)  // ln sum_j e^z_j = m + ln2 * (log2 s - (m*log2e - fp32(m*log2e)))
       lse_out[row] = st.m + kLn2 * (log2_fast(st.s) - __builtin_fmaf(st.m, kLog2e, -(st.m * kLog2e)));
-      return;
-    }
+    if (!out) return;  // (no mean without out)
     loss = (t >= 0 && t < vocab) ? lse_minus(st, z) : __builtin_nanf("");
     if (!reduce_mean) out[row] = loss;
   }

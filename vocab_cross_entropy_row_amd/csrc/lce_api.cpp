@@ -186,9 +186,9 @@ FusedPlan plan_fused(int64_t tokens, int64_t vocab, int cus, size_t reserved) {
 
 // The fused projection + cross-entropy for validated arguments, tokens > 0.
 // The first `reserved` bytes of scratch regions belong to the caller.  With
-// lse_out set, writes ln sum_j e^(z_j) per token there instead of losses
-// (target and out are then unused).  With z_out set, the logits are also
-// stored there as [tokens, z_ld] fp32 rows.
+// lse_out set, writes ln sum_j e^(z_j) per token there; with out set (and
+// target), the losses or their mean; at least one of the two.  With z_out
+// set, the logits are also stored there as [tokens, z_ld] fp32 rows.
 lce_status run_fused(const void* x, const void* weight, int64_t tokens, int64_t hidden, int64_t vocab,
                      const int64_t* target, bool mean, float* out, hipStream_t stream,
                      size_t reserved, float* lse_out, float* z_out, int64_t z_ld) {
@@ -203,12 +203,12 @@ lce_status run_fused(const void* x, const void* weight, int64_t tokens, int64_t 
   a.tokens = tokens;
   a.hidden = hidden;
   a.vocab = vocab;
-  a.target = lse_out ? nullptr : target;
-  a.out = lse_out ? nullptr : out;
+  a.target = out ? target : nullptr;
+  a.out = out;
   a.lse_out = lse_out;
   a.z_out = z_out;
   a.z_ld = z_ld;
-  a.reduce_mean = (mean && !lse_out) ? 1 : 0;
+  a.reduce_mean = (mean && out) ? 1 : 0;
   a.segments = p.segments;
 
   char* base = nullptr;
@@ -227,7 +227,8 @@ lce_status run_fused(const void* x, const void* weight, int64_t tokens, int64_t 
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   const lce::FusedGeometry g = lce::fused_geometry();
   note_launch("fused_xent_partial_kernel (%s) grid %lld x 512 + fused_xent_merge_kernel grid %lld x %d",
-              z_out ? "log-sum-exp, logits stored" : lse_out ? "log-sum-exp" : "loss",
+              z_out ? (out ? "loss and log-sum-exp, logits stored" : "log-sum-exp, logits stored")
+                    : lse_out ? (out ? "loss and log-sum-exp" : "log-sum-exp") : "loss",
               (long long)((tokens + g.block_tokens - 1) / g.block_tokens * p.segments),
               (long long)((tokens + lce::kRowThreads - 1) / lce::kRowThreads), lce::kRowThreads);
   return LCE_OK;
@@ -324,24 +325,22 @@ lce_status lce_xent_merge(const float* partials, int64_t shards, int64_t tokens,
   return LCE_OK;
 }
 
-lce_status lce_xent_bwd(const void* logits, lce_dtype dtype, int64_t tokens, int64_t vocab,
-                        const int64_t* target, lce_reduction reduction, const float* grad,
-                        void* dlogits, hipStream_t stream) {
-  begin_call();
-  lce_status s = validate_xent(logits, (int)dtype, tokens, vocab, target, LCE_REDUCTION_NONE, nullptr,
-                               nullptr);
-  if (s != LCE_OK) return s;
-  if (reduction != LCE_REDUCTION_MEAN && reduction != LCE_REDUCTION_NONE)
-    return fail(LCE_ERR_INVALID_ARG, "reduction must be LCE_REDUCTION_MEAN or LCE_REDUCTION_NONE (got %d)",
-                (int)reduction);
-  if (tokens == 0) return LCE_OK;
+// The row gradient for a call whose logits, target and reduction are already
+// validated (tokens > 0); with `out` also the forward's losses (or their mean).
+static lce_status run_xent_bwd(const void* logits, lce_dtype dtype, int64_t tokens, int64_t vocab,
+                               const int64_t* target, bool mean, const float* grad, void* dlogits,
+                               float* out, hipStream_t stream) {
+  lce_status s = LCE_OK;
   const int64_t esize = dtype == LCE_F32 ? 4 : 2;
   if (!grad) return fail(LCE_ERR_INVALID_ARG, "grad is NULL");
   if (!dlogits) return fail(LCE_ERR_INVALID_ARG, "dlogits is NULL");
   if (!aligned(grad, 4)) return fail(LCE_ERR_INVALID_ARG, "grad is not 4-byte aligned");
   if (!aligned(dlogits, (uint64_t)esize))
     return fail(LCE_ERR_INVALID_ARG, "dlogits is not aligned to its element size");
-  const bool mean = reduction == LCE_REDUCTION_MEAN;
+  // Each row is cut into scalar edges and 16-byte chunks by the logits' address;
+  // the gradient rows are written with the same cut.
+  if (((uintptr_t)dlogits - (uintptr_t)logits) % 16u != 0)
+    return fail(LCE_ERR_UNSUPPORTED, "dlogits must start at the same offset modulo 16 bytes as logits");
   const uint64_t zb = (uint64_t)(tokens * vocab * esize);
   const uint64_t gb = mean ? 4u : (uint64_t)tokens * 4u;
   // In place (dlogits == logits) is allowed; any other overlap is not.
@@ -350,6 +349,11 @@ lce_status lce_xent_bwd(const void* logits, lce_dtype dtype, int64_t tokens, int
   if (overlaps(dlogits, zb, target, (uint64_t)tokens * 8u))
     return fail(LCE_ERR_ALIAS, "dlogits overlaps target");
   if (overlaps(dlogits, zb, grad, gb)) return fail(LCE_ERR_ALIAS, "dlogits overlaps grad");
+  if (out) {
+    const uint64_t ob = out_bytes(tokens, mean ? LCE_REDUCTION_MEAN : LCE_REDUCTION_NONE);
+    if (overlaps(out, ob, dlogits, zb)) return fail(LCE_ERR_ALIAS, "out overlaps dlogits");
+    if (overlaps(out, ob, grad, gb)) return fail(LCE_ERR_ALIAS, "out overlaps grad");
+  }
 
   lce::BwdArgs a{};
   a.logits = logits;
@@ -376,6 +380,7 @@ lce_status lce_xent_bwd(const void* logits, lce_dtype dtype, int64_t tokens, int
                                    : 0;
   const char* forced = getenv("LCE_BWD_PATH");
   if (forced && !strcmp(forced, "apply")) a.wave_chunks = 0;
+  MeanState ms;
   if (a.wave_chunks == 0) {
     int cus = 0;
     if ((s = num_cus(&cus)) != LCE_OK) return s;
@@ -390,7 +395,8 @@ lce_status lce_xent_bwd(const void* logits, lce_dtype dtype, int64_t tokens, int
                   (long long)(S * tokens));
     a.splits = (int)S;
     a.chunks_per_split = (int)((nvec + S - 1) / S);
-    // Row states (m, sum e^(z - m), .) into scratch, then the gradient pass.
+    // Row states (m, sum e^(z - m), z_target) into scratch, then the gradient
+    // pass; the losses (with `out`) come from the same states.
     Carve cv;
     const size_t off_stats = cv.take((size_t)tokens * 12u);
     char* base = nullptr;
@@ -400,17 +406,64 @@ lce_status lce_xent_bwd(const void* logits, lce_dtype dtype, int64_t tokens, int
                       (size_t)tokens * 12u)) != LCE_OK)
       return s;
     a.stats = stats;
+    if (out) {
+      if (mean && (s = get_mean_state(stream, (tokens + lce::kRowThreads - 1) / lce::kRowThreads, &ms)) != LCE_OK)
+        return s;
+      hipError_t e = lce::launch_stats_merge(stats, 1, tokens, target, vocab, out, mean ? 1 : 0, ms.slots,
+                                             ms.epoch, stream);
+      if (e != hipSuccess) return hip_fail(e, "kernel launch");
+      note_launch("xent_stats_merge_kernel grid %lld x %d",
+                  (long long)((tokens + lce::kRowThreads - 1) / lce::kRowThreads), lce::kRowThreads);
+    }
+  } else if (out) {
+    a.loss_out = out;
+    const int rows = lce::bwd_wave_rows(a);
+    if (mean && (s = get_mean_state(stream, (tokens + rows - 1) / rows, &ms)) != LCE_OK) return s;
+    a.mean_slots = ms.slots;
+    a.epoch = ms.epoch;
   }
   hipError_t e = lce::launch_bwd(a, stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   const char* tn = a.bf16 ? "unsigned short" : "float";
-  if (a.wave_chunks > 0)
-    note_launch("xent_bwd_wave_kernel<%s, %d, 4> grid %lld x 256", tn, a.wave_chunks,
-                (long long)((tokens + 3) / 4));
+  if (a.wave_chunks > 0) {
+    const int rows = lce::bwd_wave_rows(a);
+    note_launch("xent_bwd_wave_kernel<%s, %d, %d, %s> grid %lld x %d", tn, a.wave_chunks, rows,
+                out ? "true" : "false", (long long)((tokens + rows - 1) / rows), 64 * rows);
+  }
   else
     note_launch("xent_bwd_apply_kernel<%s, 4> grid %lld x %d", tn, (long long)(a.splits * tokens),
                 lce::kRowThreads);
   return LCE_OK;
+}
+
+lce_status lce_xent_bwd(const void* logits, lce_dtype dtype, int64_t tokens, int64_t vocab,
+                        const int64_t* target, lce_reduction reduction, const float* grad,
+                        void* dlogits, hipStream_t stream) {
+  begin_call();
+  lce_status s = validate_xent(logits, (int)dtype, tokens, vocab, target, LCE_REDUCTION_NONE, nullptr,
+                               nullptr);
+  if (s != LCE_OK) return s;
+  if (reduction != LCE_REDUCTION_MEAN && reduction != LCE_REDUCTION_NONE)
+    return fail(LCE_ERR_INVALID_ARG, "reduction must be LCE_REDUCTION_MEAN or LCE_REDUCTION_NONE (got %d)",
+                (int)reduction);
+  if (tokens == 0) return LCE_OK;
+  return run_xent_bwd(logits, dtype, tokens, vocab, target, reduction == LCE_REDUCTION_MEAN, grad,
+                      dlogits, nullptr, stream);
+}
+
+lce_status lce_xent_fwd_bwd(const void* logits, lce_dtype dtype, int64_t tokens, int64_t vocab,
+                            const int64_t* target, lce_reduction reduction, const float* grad,
+                            float* out, void* dlogits, hipStream_t stream) {
+  begin_call();
+  lce_status s = validate_xent(logits, (int)dtype, tokens, vocab, target, (int)reduction, out);
+  if (s != LCE_OK) return s;
+  const bool mean = reduction == LCE_REDUCTION_MEAN;
+  if (tokens == 0) {
+    if (!mean) return LCE_OK;
+    hipError_t e = lce::launch_fill_f32(out, 1, __builtin_nanf(""), stream);
+    return e == hipSuccess ? LCE_OK : hip_fail(e, "launch");
+  }
+  return run_xent_bwd(logits, dtype, tokens, vocab, target, mean, grad, dlogits, out, stream);
 }
 
 lce_status lce_fused_linear_xent_fwd(const void* x, const void* weight, int64_t tokens,

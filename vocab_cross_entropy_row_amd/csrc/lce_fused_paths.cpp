@@ -22,7 +22,10 @@ namespace host {
 // the forward kernel gives every token's log-sum-exp, then for each chunk
 // the fused kernel's gradient mode recomputes the logits and writes dZ.
 // Either way two library GEMMs consume dZ: dx[chunk] = dZ W and
-// dW (+)= dZ^T x[chunk].  Chunks are the largest multiple of 256 tokens whose
+// dW (+)= dZ^T x[chunk].  With `out`, the pass that gives the log-sum-exps
+// also gives the forward's losses: per token into out, or their mean (the
+// merge's own mean when one pass covers every token, else a mean kernel over
+// per-token losses kept in scratch).  Chunks are the largest multiple of 256 tokens whose
 // buffers (6 or 2 bytes per logit) fit in LCE_FUSED_BWD_STORE_BYTES (default
 // 2 GiB), at least 256.
 constexpr size_t kGemmWorkspace = size_t(128) << 20;
@@ -51,7 +54,7 @@ FusedBwdPlan plan_fused_bwd(int64_t tokens, int64_t vocab, int64_t cap) {
 
 lce_status run_fused_bwd(const void* x, const void* weight, int64_t tokens, int64_t hidden,
                          int64_t vocab, const int64_t* target, bool mean, const float* grad,
-                         float* dx, float* dw, hipStream_t stream) {
+                         float* dx, float* dw, float* out, hipStream_t stream) {
   lce_status s = LCE_OK;
   int cus = 0;
   if ((s = num_cus(&cus)) != LCE_OK) return s;
@@ -70,6 +73,9 @@ lce_status run_fused_bwd(const void* x, const void* weight, int64_t tokens, int6
   // as stored, measured slower).
   const bool dw_tt = dw && env_int("LCE_FUSED_BWD_DW_NT", 0) == 0;
   const size_t off_xt = cv.take(dw_tt ? (size_t)chunk * (size_t)hidden * 2u : 0u);
+  // A mean over several stored chunks: their per-token losses first.
+  const bool chunk_losses = out && mean && stored && chunk < tokens;
+  const size_t off_loss = cv.take(chunk_losses ? (size_t)tokens * 4u : 0u);
   const size_t reserved = cv.off - Carve().off;
   const int64_t last = tokens - (tokens - 1) / chunk * chunk;
   size_t need = cv.off;
@@ -84,8 +90,9 @@ lce_status run_fused_bwd(const void* x, const void* weight, int64_t tokens, int6
   void* dz = base + off_dz;
   float* z = (float*)(base + off_z);
   uint16_t* xt = (uint16_t*)(base + off_xt);
+  float* losses = (float*)(base + off_loss);
 
-  if (!stored && (s = run_fused(x, weight, tokens, hidden, vocab, nullptr, false, nullptr, stream,
+  if (!stored && (s = run_fused(x, weight, tokens, hidden, vocab, target, mean, out, stream,
                                 reserved, lse)) != LCE_OK)
     return s;
   const uint16_t* x16 = (const uint16_t*)x;
@@ -93,8 +100,9 @@ lce_status run_fused_bwd(const void* x, const void* weight, int64_t tokens, int6
     const int64_t n = tokens - c0 < chunk ? tokens - c0 : chunk;
     hipError_t e = hipSuccess;
     if (stored) {
-      if ((s = run_fused(x16 + c0 * hidden, weight, n, hidden, vocab, nullptr, false, nullptr,
-                         stream, reserved, lse + c0, z, ld)) != LCE_OK)
+      float* chunk_out = !out ? nullptr : chunk_losses ? losses + c0 : mean ? out : out + c0;
+      if ((s = run_fused(x16 + c0 * hidden, weight, n, hidden, vocab, target + c0,
+                         mean && !chunk_losses, chunk_out, stream, reserved, lse + c0, z, ld)) != LCE_OK)
         return s;
       lce::FusedGradRowsArgs g{};
       g.z = z;
@@ -148,6 +156,14 @@ lce_status run_fused_bwd(const void* x, const void* weight, int64_t tokens, int6
                                         dw, hidden, ws, kGemmWorkspace, stream)) != LCE_OK) {
       return s;
     }
+  }
+  if (chunk_losses) {
+    MeanState ms;
+    if ((s = get_mean_state(stream, (tokens + lce::kRowThreads - 1) / lce::kRowThreads, &ms)) != LCE_OK)
+      return s;
+    hipError_t e = lce::launch_jsd_mean(tokens, losses, out, ms.slots, ms.epoch, stream);
+    if (e != hipSuccess) return hip_fail(e, "kernel launch");
+    note_launch("fused_jsd_merge_kernel (mean of the chunks' losses)");
   }
   return LCE_OK;
 }
@@ -341,12 +357,14 @@ lce_status lce_fused_linear_jsd_fwd(const void* student_x, const void* student_w
                            vocab, beta, mean, out, stream, cus);
 }
 
-lce_status lce_fused_linear_xent_bwd(const void* x, const void* weight, int64_t tokens,
-                                     int64_t hidden, int64_t vocab, const int64_t* target,
-                                     lce_reduction reduction, const float* grad, float* dx,
-                                     float* dweight, hipStream_t stream) {
-  begin_call();
-  lce_status s = validate_common(tokens, target, (int)reduction, nullptr, nullptr);
+// Both fused gradient entry points: arguments checked here, `out` (the
+// forward's output) only when non-null.
+static lce_status fused_bwd_call(const void* x, const void* weight, int64_t tokens, int64_t hidden,
+                                 int64_t vocab, const int64_t* target, lce_reduction reduction,
+                                 const float* grad, float* out, float* dx, float* dweight,
+                                 hipStream_t stream) {
+  lce_status s = out ? validate_fused(x, weight, tokens, hidden, vocab, target, (int)reduction, out)
+                     : validate_common(tokens, target, (int)reduction, nullptr, nullptr);
   if (s != LCE_OK) return s;
   if ((s = validate_head(x, weight, tokens, hidden, vocab, nullptr, 0)) != LCE_OK) return s;
   const bool mean = reduction == LCE_REDUCTION_MEAN;
@@ -371,12 +389,41 @@ lce_status lce_fused_linear_xent_bwd(const void* x, const void* weight, int64_t 
     if (overlaps(o.p, o.n, grad, gb)) return fail(LCE_ERR_ALIAS, "%s overlaps grad", o.name);
   }
   if (overlaps(dx, dxb, dweight, dwb)) return fail(LCE_ERR_ALIAS, "dx overlaps dweight");
-  if (tokens == 0) {  // no token contributes: dweight is zero, dx is empty
+  if (out) {
+    const uint64_t ob = out_bytes(tokens, (int)reduction);
+    if (overlaps(out, ob, grad, gb)) return fail(LCE_ERR_ALIAS, "out overlaps grad");
+    if (overlaps(out, ob, dx, dxb)) return fail(LCE_ERR_ALIAS, "out overlaps dx");
+    if (overlaps(out, ob, dweight, dwb)) return fail(LCE_ERR_ALIAS, "out overlaps dweight");
+  }
+  if (tokens == 0) {  // no token contributes: dweight is zero, dx is empty, a mean is NaN
+    if (out && mean) {
+      hipError_t e = lce::launch_fill_f32(out, 1, __builtin_nanf(""), stream);
+      if (e != hipSuccess) return hip_fail(e, "launch");
+    }
     if (!dweight) return LCE_OK;
     hipError_t e = lce::launch_fill_f32(dweight, vocab * hidden, 0.0f, stream);
     return e == hipSuccess ? LCE_OK : hip_fail(e, "launch");
   }
-  return run_fused_bwd(x, weight, tokens, hidden, vocab, target, mean, grad, dx, dweight, stream);
+  return run_fused_bwd(x, weight, tokens, hidden, vocab, target, mean, grad, dx, dweight, out, stream);
+}
+
+lce_status lce_fused_linear_xent_bwd(const void* x, const void* weight, int64_t tokens,
+                                     int64_t hidden, int64_t vocab, const int64_t* target,
+                                     lce_reduction reduction, const float* grad, float* dx,
+                                     float* dweight, hipStream_t stream) {
+  begin_call();
+  return fused_bwd_call(x, weight, tokens, hidden, vocab, target, reduction, grad, nullptr, dx,
+                        dweight, stream);
+}
+
+lce_status lce_fused_linear_xent_fwd_bwd(const void* x, const void* weight, int64_t tokens,
+                                         int64_t hidden, int64_t vocab, const int64_t* target,
+                                         lce_reduction reduction, const float* grad, float* out,
+                                         float* dx, float* dweight, hipStream_t stream) {
+  begin_call();
+  if (!out) return fail(LCE_ERR_INVALID_ARG, "out is NULL");
+  return fused_bwd_call(x, weight, tokens, hidden, vocab, target, reduction, grad, out, dx, dweight,
+                        stream);
 }
 
 }  // extern "C"

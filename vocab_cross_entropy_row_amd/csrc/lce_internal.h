@@ -60,9 +60,14 @@ struct BwdArgs {
   const float* stats;       // otherwise: (m, s, .) per row from the statistics mode
   int splits;               //   workgroups per row
   int chunks_per_split;     //   16-byte chunks per workgroup
+  float* loss_out;          // wave_chunks > 0: also the losses (or their mean) here; else null
+  uint64_t* mean_slots;     //   with reduce_mean: the mean state
+  unsigned* epoch;
 };
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+// Rows per workgroup of the one-wave-per-row gradient kernel for these arguments.
+int bwd_wave_rows(const BwdArgs& a);
 
 // Losses (or their mean) from [shards][tokens][3] vocab-shard statistics.
 hipError_t launch_stats_merge(const float* stats, int64_t shards, int64_t tokens,
@@ -79,8 +84,8 @@ struct FusedArgs {
   const int64_t* target;
   float* out;
   int reduce_mean;
-  float* lse_out;         // non-null: write ln sum_j e^z_j per token instead of losses
-                          // (target may then be null)
+  float* lse_out;         // non-null: write ln sum_j e^z_j per token; losses (or the mean)
+                          // go to out only when out is non-null (target may then be null)
   float* z_out;           // non-null: also store the fp32 logits as [tokens, z_ld] rows
   int64_t z_ld;           // multiple of block_vocab, >= vocab; z_ld * block_tokens * 4 < 2^32
   int segments;           // vocab segments (workgroups per token block)
