@@ -151,3 +151,24 @@ def test_bwd_row_longer_than_one_gib():
     got = _run(z, t, "f32", "mean", np.float32(1.0))
     _check(got, want, np.ones((rows, 1)), "f32", "row above 1 GiB")
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bwd_unaligned_base(dtype):
+    """Logits that start off a 16-byte boundary: the binding allocates the gradient at the
+    same offset modulo 16 bytes, and a gradient buffer at another offset is refused."""
+    rows, vocab = 12, 1000
+    z = _logits(31, rows * vocab + 3, 1, dtype).reshape(-1)
+    zd = to_dev(z)[3:].view(rows, vocab)
+    t = lce_synth.targets(32, rows, vocab)
+    td = torch.from_numpy(t).cuda()
+    gd = torch.ones(1, device="cuda")
+    d = lce.xent_bwd(zd, td, gd, "mean")
+    torch.cuda.synchronize()
+    assert (d.data_ptr() - zd.data_ptr()) % 16 == 0
+    want = oracle.xent_bwd(np.ascontiguousarray(z[3:].reshape(rows, vocab)), t, np.float64(1.0), "mean",
+                           dtype=dtype)
+    _check(_to_host(d, dtype), want, np.full((rows, 1), 1.0 / rows), dtype, f"unaligned base {dtype}")
+    with pytest.raises(lce.LceError) as e:
+        lce.xent_bwd(zd, td, gd, "mean", out=torch.empty_like(zd))
+    assert e.value.status == lce.LCE_ERR_UNSUPPORTED

@@ -371,9 +371,16 @@ def _xent_bwd_args(logits, target, grad, reduction: str) -> int:
 
 
 def _grad_out(logits, out):
+    """The gradient buffer: ``out``, or a new tensor like ``logits`` whose data starts at
+    the same offset modulo 16 bytes (the library writes gradient rows with the logits'
+    16-byte cut)."""
     import torch
     if out is None:
-        return torch.empty_like(logits)
+        off = (logits.data_ptr() % 16) // logits.element_size()
+        if off == 0:
+            return torch.empty_like(logits)
+        buf = torch.empty(logits.numel() + off, dtype=logits.dtype, device=logits.device)
+        return buf[off:].view(logits.shape)
     if out.shape != logits.shape or out.dtype != logits.dtype or not out.is_contiguous():
         raise ValueError("dlogits must be a contiguous tensor like logits")
     return out
