@@ -100,6 +100,48 @@ def test_forced_paths(path, extra, dtype, rows, vocab):
         check_xent(z, t, dtype, f"{path} {extra} {dtype} {rows}x{vocab}")
 
 
+# Rows of at most 128 16-byte chunks with no scalar edges take several rows per wave
+# (8, 4 or 2 rows for up to 32, 64 or 128 chunks): chunk counts at and around each
+# boundary, ragged row counts (a last wave with fewer rows than it holds).
+GROUP = [(1, 8), (7, 64), (33, 124), (100, 128), (257, 132), (31, 256), (1001, 260), (65, 512)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rows,vocab", GROUP)
+def test_several_rows_per_wave(dtype, rows, vocab):
+    v = vocab if dtype == "f32" else 2 * vocab  # the same chunk counts in both dtypes
+    z = rand_logits(rows * 31 + v, rows, v, dtype, std=2.5)
+    t = lce_synth.targets(rows + v, rows, v)
+    t[0] = v - 1
+    if rows > 2:
+        t[1], t[2] = 0, -1
+    check_xent(z, t, dtype, f"{dtype} {rows}x{v}")
+    lce.xent(to_dev(z), torch.from_numpy(t).cuda(), "none")
+    nvec = v * (4 if dtype == "f32" else 2) // 16
+    g = 8 if nvec <= 32 else 4 if nvec <= 64 else 2
+    assert f"xent_group_rows_kernel<{'float' if dtype == 'f32' else 'unsigned short'}, {g}, 4, 4>" \
+        in lce.lce_last_launch()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_several_rows_per_wave_edge_rows(dtype):
+    """Rows held several to a wave: an all -inf row but its target, a spike far above the
+    fixed reference (refolded with the running maximum), -inf entries, a row with no finite
+    logit (NaN loss)."""
+    rows, vocab = 24, 512 if dtype == "f32" else 1024
+    z = rand_logits(77, rows, vocab, "f32", std=2.0)
+    z[1, :] = -np.inf
+    z[1, 5] = 3.0
+    z[2, 300] = 90.0
+    z[3, ::3] = -np.inf
+    z[4, :] = -np.inf
+    if dtype == "bf16":
+        z = lce_synth.f32_to_bf16_bits(z)
+    t = lce_synth.targets(78, rows, vocab)
+    t[1], t[2] = 5, 300
+    check_xent(z, t, dtype, f"edge rows {dtype}")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_large_shift_keeps_accuracy(dtype):
     """Rows shifted by -1000 (exact in both dtypes' grids) lose no accuracy."""

@@ -62,7 +62,7 @@ def _check_stats(got, want, label):
 @pytest.mark.parametrize("path", ["auto", "wave", "block", "split", "split_many"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("rows,shard,start", [(37, 1000, 0), (64, 4099, 12345), (5, 20001, 7),
-                                              (130, 129, 999)])
+                                              (130, 129, 999), (130, 128, 999), (1000, 512, 3584)])
 def test_partial_matches_oracle(path, dtype, rows, shard, start):
     z = _logits(rows + shard, rows, shard, dtype)
     t = lce_synth.targets(rows, rows, start + shard + 50)  # some targets past this shard

@@ -106,11 +106,35 @@ struct AddOp {
 __device__ __forceinline__ float wave_max(float v) { return wave_allreduce(v, MaxOp{}); }
 __device__ __forceinline__ float wave_sum(float v) { return wave_allreduce(v, AddOp{}); }
 
+// The same butterfly over groups of N consecutive lanes (N = 8, 16 or 32: its
+// first 3, 4 or 5 steps); every lane ends with its group's value.
+template <int N, typename Op>
+__device__ __forceinline__ float group_allreduce(float v, Op op) {
+  static_assert(N == 8 || N == 16 || N == 32, "group of 8, 16 or 32 lanes");
+  v = op(v, dpp_f<kDppQuadXor1>(v));
+  v = op(v, dpp_f<kDppQuadXor2>(v));
+  v = op(v, dpp_f<kDppRowHalfMirror>(v));
+  if constexpr (N >= 16) v = op(v, dpp_f<kDppRowMirror>(v));
+  if constexpr (N >= 32) {
+    auto p = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+    v = op(__int_as_float(p[0]), __int_as_float(p[1]));
+  }
+  return v;
+}
+
 // Combine the 64 lanes' states: global max first, then each lane rescales its
 // own sum to it, then one sum reduction.  All lanes return the row state.
 __device__ __forceinline__ Lse wave_lse(Lse st) {
   const float m = wave_max(st.m);
   const float s = wave_sum(st.s * lse_rescale(st.m, m));
+  return {m, s};
+}
+
+// The same over groups of N consecutive lanes (one row per group).
+template <int N>
+__device__ __forceinline__ Lse group_lse(Lse st) {
+  const float m = group_allreduce<N>(st.m, MaxOp{});
+  const float s = group_allreduce<N>(st.s * lse_rescale(st.m, m), AddOp{});
   return {m, s};
 }
 

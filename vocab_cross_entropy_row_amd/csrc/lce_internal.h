@@ -21,7 +21,7 @@ inline bool grid_fits(int64_t blocks, int64_t threads) {
   return blocks >= 0 && blocks <= kMaxGridItems / threads;
 }
 
-enum class XentPath : int { WaveRows = 0, BlockRows = 1, Split = 2 };
+enum class XentPath : int { WaveRows = 0, BlockRows = 1, Split = 2, GroupRows = 3 };
 
 struct XentArgs {
   const void* logits;
@@ -36,6 +36,7 @@ struct XentArgs {
   XentPath path;
   int unroll;               // chunks per lane per batch (wave_rows: 4, 8 or 16)
   int waves_per_block;      // WaveRows: rows (waves) per workgroup, 4 or 16 (then unroll <= 8)
+  int rows_per_wave;        // GroupRows: 2, 4 or 8 rows per wave (4 waves per workgroup)
   int splits;               // Split: workgroups per row
   int chunks_per_split;     // Split: 16-byte chunks per workgroup
   float* split_partials;    // Split: splits * tokens (max, sum-exp) pairs, slice-major

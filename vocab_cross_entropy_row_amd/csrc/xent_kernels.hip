@@ -110,6 +110,85 @@ __global__ __launch_bounds__(64 * WAVES) void xent_wave_rows_kernel(
   }
 }
 
+// ------------------------------------------------------------ several rows per wave
+// Short rows (at most 4 * N 16-byte chunks, the rows' bytes a multiple of 16
+// and the logits 16-byte aligned, so a row has no scalar edges): G rows per
+// wave and N = 64 / G lanes per row, lane j of a row's group holding chunks
+// j + N * u (u < U).  A wave's G rows are consecutive in memory, so one buffer
+// resource covers them; a chunk past its row's end is loaded at an offset past
+// the resource (no memory is read) and folds as -inf.  The group's lanes then
+// merge their states (group_lse) and its first lane finishes the row.  Per row
+// this is one group of lanes' worth of fixed work (target, target logit,
+// reduction, store) instead of one wave's.
+template <typename T, int G, int U, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void xent_group_rows_kernel(
+    const T* __restrict__ logits, int64_t tokens, int vocab, const int64_t* __restrict__ target,
+    int64_t vocab_start, float* __restrict__ stats, float* __restrict__ out,
+    uint64_t* __restrict__ slots, unsigned* __restrict__ epoch, int reduce_mean) {
+  constexpr int N = 64 / G;
+  typedef typename Vec<T>::raw raw;
+  const unsigned mean_tag = mean_begin(epoch, reduce_mean);
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_uniform(threadIdx.x >> 6);
+  const int g = lane / N, j = lane % N;
+  const int64_t r0 = ((int64_t)blockIdx.x * WAVES + wave) * G;  // this wave's first row
+  const int64_t row = r0 + g;
+  const bool have = row < tokens;
+  float loss = 0.0f;
+  if (r0 < tokens) {
+    const int64_t left = tokens - r0;
+    const uint32_t rows_here = (uint32_t)(left < G ? left : G);
+    const uint32_t row_bytes = (uint32_t)vocab * (uint32_t)sizeof(T);
+    const int nvec = (int)(row_bytes / 16u);
+    // The target first: its wait then leaves the chunk loads in flight.
+    const int64_t t = have ? target[row] : -1;
+    __builtin_amdgcn_sched_barrier(0);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(logits + r0 * (int64_t)vocab, rows_here * row_bytes);
+    raw v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = j + N * u;
+      const uint32_t off = c < nvec ? (uint32_t)g * row_bytes + (uint32_t)c * 16u : 0x7ffffff0u;
+      v[u] = (raw)__builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kStreamPolicy);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t tt = have ? local_target(t, vocab_start, vocab) : -1;
+    const float zt = have ? Vec<T>::scalar(logits + row * (int64_t)vocab + safe_target(tt, vocab)) : 0.0f;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (j + N * u >= nvec) v[u] = Vec<T>::neg_inf();
+    // Shard statistics take the tracked fold (exact maximum); losses the
+    // fixed-reference fold, and the tracked one if any lane's sum is not bounded.
+    Lse st = lse_empty();
+    if (stats) {
+      fold_batch<T, U, true, true>(st, v);
+    } else {
+      fold_batch<T, U, true, false>(st, v);
+      if (__builtin_amdgcn_ballot_w64(lane_sum_unsafe(st))) {
+        st = lse_empty();
+        fold_batch<T, U, true, true>(st, v);
+      }
+    }
+    const Lse r = group_lse<N>(st);
+    if (stats) {
+      if (j == 0 && have) write_stats(stats + 3 * row, r, tt >= 0, zt);
+    } else {
+      loss = (tt >= 0) ? lse_minus(r, zt) : __builtin_nanf("");
+      if (!reduce_mean && j == 0 && have) out[row] = loss;
+    }
+  }
+  if (reduce_mean) {
+    // The workgroup's rows in order (rows past the end add 0).
+    __shared__ float wl[WAVES * G];
+    if (j == 0) wl[wave * G + g] = have ? loss : 0.0f;
+    __syncthreads();
+    float bsum = 0.0f;
+    if (threadIdx.x == 0)
+      for (int i = 0; i < WAVES * G; ++i) bsum += wl[i];
+    finish_mean(bsum, slots, epoch, mean_tag, out, tokens);
+  }
+}
+
 // ------------------------------------------------------------ one workgroup per row
 template <typename T, int U>
 __global__ __launch_bounds__(kRowThreads) void xent_block_rows_kernel(
@@ -340,6 +419,17 @@ static hipError_t launch_wave_rows(const XentArgs& a, hipStream_t st) {
   return launch_wave_rows_w<T, U, 4>(a, st);
 }
 
+template <typename T, int G>
+static hipError_t launch_group_rows(const XentArgs& a, hipStream_t st) {
+  constexpr int W = 4;
+  const int64_t blocks = (a.tokens + W * G - 1) / (W * G);
+  if (!grid_fits(blocks, 64 * W)) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((xent_group_rows_kernel<T, G, 4, W>), dim3((unsigned)blocks), dim3(64 * W), 0, st,
+                     (const T*)a.logits, a.tokens, (int)a.vocab, a.target, a.vocab_start, a.stats,
+                     a.out, a.mean_slots, a.epoch, a.reduce_mean);
+  return hipGetLastError();
+}
+
 template <typename T, int U>
 static hipError_t launch_block_rows(const XentArgs& a, hipStream_t st) {
   if (!grid_fits(a.tokens, kRowThreads)) return hipErrorInvalidConfiguration;
@@ -375,6 +465,13 @@ static hipError_t launch_xent_t(const XentArgs& a, hipStream_t st) {
         case 4: return launch_wave_rows<T, 4>(a, st);
         case 8: return launch_wave_rows<T, 8>(a, st);
         default: return launch_wave_rows<T, 16>(a, st);
+      }
+    case XentPath::GroupRows:
+      switch (a.rows_per_wave) {
+        case 2: return launch_group_rows<T, 2>(a, st);
+        case 4: return launch_group_rows<T, 4>(a, st);
+        case 8: return launch_group_rows<T, 8>(a, st);
+        default: return hipErrorInvalidValue;
       }
     case XentPath::BlockRows:
       return launch_block_rows<T, 8>(a, st);
