@@ -988,8 +988,8 @@ def main(argv=None) -> int:
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(rows shard across GPUs with one 8-byte all-reduce for the mean; not built). "
+        print("bench.py measures one GPU only: liblce has no multi-GPU path "
+              "(rows would shard across GPUs with one 8-byte all-reduce for the mean). "
               "Run with --gpus 1.", file=sys.stderr)
         return 2
 
