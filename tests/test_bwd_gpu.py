@@ -172,3 +172,29 @@ def test_bwd_unaligned_base(dtype):
     with pytest.raises(lce.LceError) as e:
         lce.xent_bwd(zd, td, gd, "mean", out=torch.empty_like(zd))
     assert e.value.status == lce.LCE_ERR_UNSUPPORTED
+
+
+# Rows of at most 128 16-byte chunks with no scalar edges: several rows per wave (8, 4
+# or 2 rows for up to 32, 64 or 128 chunks), at and around each boundary, ragged row counts.
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rows,vocab", [(1, 8), (7, 64), (33, 124), (100, 128), (257, 132),
+                                        (31, 256), (1001, 260), (65, 512)])
+@pytest.mark.parametrize("reduction", ["mean", "none"])
+def test_bwd_several_rows_per_wave(dtype, rows, vocab, reduction):
+    v = vocab if dtype == "f32" else 2 * vocab  # the same chunk counts in both dtypes
+    z = _logits(rows * 13 + v, rows, v, dtype)
+    t = lce_synth.targets(rows + 2 * v, rows, v)
+    t[0] = v - 1
+    if rows > 2:
+        t[1], t[2] = 0, -1
+    grad = np.float32(0.9) if reduction == "mean" else np.linspace(-1, 1, rows).astype(np.float32)
+    got = _run(z, t, dtype, reduction, grad)
+    nvec = v * (4 if dtype == "f32" else 2) // 16
+    g = 8 if nvec <= 32 else 4 if nvec <= 64 else 2
+    assert f"xent_bwd_group_kernel<{'float' if dtype == 'f32' else 'unsigned short'}, {g}, 4, 4, false>" \
+        in lce.lce_last_launch()
+    want = oracle.xent_bwd(z, t, np.asarray(grad, dtype=np.float64), reduction, dtype=dtype)
+    gs = (np.full(rows, float(grad) / rows) if reduction == "mean" else grad.astype(np.float64))
+    _check(got, want, gs[:, None], dtype, f"grouped {dtype} {rows}x{v} {reduction}")
+    one_wave = _run(z, t, dtype, reduction, grad, env={"LCE_BWD_PATH": "wave"})
+    _check(one_wave, want, gs[:, None], dtype, f"one wave {dtype} {rows}x{v} {reduction}")

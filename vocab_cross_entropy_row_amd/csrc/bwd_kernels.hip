@@ -221,6 +221,95 @@ __global__ __launch_bounds__(64 * WAVES) void xent_bwd_wave_kernel(
   }
 }
 
+// ------------------------------------------------------------ several short rows per wave
+// Rows of at most 4 * N chunks with no scalar edges (as the forward's
+// several-rows-per-wave kernel): G rows per wave, N = 64 / G lanes per row, lane
+// j of a row's group holding chunks j + N * u (u < U) of the row, all in
+// registers; one buffer resource covers the wave's G consecutive rows for the
+// loads and one for the stores (chunks past a row's end are loaded and stored
+// past the resource: no memory is touched).  The row state is merged over the
+// group's lanes (group_lse).  With LOSS the group also finishes the row's loss
+// (the target logit taken by the lane that holds it and spread over the group
+// with a max), per token or into the deterministic mean.
+template <typename T, int G, int U, int WAVES, bool LOSS>
+__global__ __launch_bounds__(64 * WAVES) void xent_bwd_group_kernel(
+    const T* logits, int64_t tokens, int vocab, const int64_t* __restrict__ target,
+    const float* __restrict__ grad, int reduce_mean, T* dlogits, float* __restrict__ loss_out,
+    uint64_t* __restrict__ slots, unsigned* __restrict__ epoch) {
+  typedef typename Vec<T>::raw raw;
+  constexpr int E = Vec<T>::kElems;
+  constexpr int N = 64 / G;
+  const unsigned mean_tag = LOSS ? mean_begin(epoch, reduce_mean) : 0u;
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_uniform(threadIdx.x >> 6);
+  const int g = lane / N, j = lane % N;
+  const int64_t r0 = ((int64_t)blockIdx.x * WAVES + wave) * G;
+  const int64_t row = r0 + g;
+  const bool have = row < tokens;
+  float loss = 0.0f;
+  if (r0 < tokens) {
+    const int64_t left = tokens - r0;
+    const uint32_t rows_here = (uint32_t)(left < G ? left : G);
+    const uint32_t row_bytes = (uint32_t)vocab * (uint32_t)sizeof(T);
+    const int nvec = (int)(row_bytes / 16u);
+    const int64_t t = have ? target[row] : -1;
+    const float gs = have ? row_grad_scale(grad, row, tokens, reduce_mean) : 0.0f;
+    __builtin_amdgcn_sched_barrier(0);
+    const __amdgpu_buffer_rsrc_t src = make_rsrc(logits + r0 * (int64_t)vocab, rows_here * row_bytes);
+    const __amdgpu_buffer_rsrc_t dst = make_rsrc(dlogits + r0 * (int64_t)vocab, rows_here * row_bytes);
+    uint32_t off[U];
+    raw v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = j + N * u;
+      off[u] = c < nvec ? (uint32_t)g * row_bytes + (uint32_t)c * 16u : 0x7ffffff0u;
+      v[u] = (raw)__builtin_amdgcn_raw_buffer_load_b128(src, off[u], 0, kStreamPolicy);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (j + N * u >= nvec) v[u] = Vec<T>::neg_inf();
+    Lse st = lse_empty();
+    fold_batch<T, U, true>(st, v);
+    const Lse r = group_lse<N>(st);
+    const bool valid = t >= 0 && t < (int64_t)vocab;
+    const GradRow gr = grad_row(r, gs, valid);
+    // The target's chunk and element within the row (all lanes of the group agree).
+    const int tc = valid ? (int)(t / E) : -1;
+    const int te = valid ? (int)(t % E) : -1;
+    if constexpr (LOSS) {
+      float zt = kNegInf;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (tc == j + N * u) {
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+            if (e == te) zt = Vec<T>::get(v[u], e);
+        }
+      zt = group_allreduce<N>(zt, MaxOp{});
+      loss = valid ? lse_minus(r, zt) : __builtin_nanf("");
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = j + N * u;
+      const raw d = grad_chunk<T>(v[u], gr, c == tc ? te : -1);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, d), dst, off[u], 0, 0);
+    }
+  }
+  if constexpr (LOSS) {
+    if (!reduce_mean) {
+      if (have && j == 0) loss_out[row] = loss;
+    } else {
+      __shared__ float wl[WAVES * G];
+      if (j == 0) wl[wave * G + g] = have ? loss : 0.0f;
+      __syncthreads();
+      float bsum = 0.0f;
+      if (threadIdx.x == 0)
+        for (int i = 0; i < WAVES * G; ++i) bsum += wl[i];
+      finish_mean(bsum, slots, epoch, mean_tag, loss_out, tokens);
+    }
+  }
+}
+
 // ------------------------------------------------------------ long rows: apply from row states
 // grid = S * tokens workgroups; workgroup b rewrites chunk slice s = b % S of
 // row b / S, and slice 0 also the row's scalar edges.  stats[3*row ..] = (m, sum e^(z - m), .) from
@@ -315,8 +404,30 @@ hipError_t launch_bwd_wave_t(const BwdArgs& a, hipStream_t st) {
     return launch_bwd_wave_w<T, NCH, 16, true>(a, st);
 }
 
+template <typename T, int G>
+hipError_t launch_bwd_group_t(const BwdArgs& a, hipStream_t st) {
+  constexpr int W = 4;
+  const int64_t blocks = (a.tokens + W * G - 1) / (W * G);
+  if (!grid_fits(blocks, 64 * W)) return hipErrorInvalidConfiguration;
+  if (a.loss_out)
+    hipLaunchKernelGGL((xent_bwd_group_kernel<T, G, 4, W, true>), dim3((unsigned)blocks), dim3(64 * W), 0, st,
+                       (const T*)a.logits, a.tokens, (int)a.vocab, a.target, a.grad, a.reduce_mean,
+                       (T*)a.dlogits, a.loss_out, a.mean_slots, a.epoch);
+  else
+    hipLaunchKernelGGL((xent_bwd_group_kernel<T, G, 4, W, false>), dim3((unsigned)blocks), dim3(64 * W), 0, st,
+                       (const T*)a.logits, a.tokens, (int)a.vocab, a.target, a.grad, a.reduce_mean,
+                       (T*)a.dlogits, nullptr, nullptr, nullptr);
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
+  switch (a.rows_per_wave) {
+    case 2: return launch_bwd_group_t<T, 2>(a, st);
+    case 4: return launch_bwd_group_t<T, 4>(a, st);
+    case 8: return launch_bwd_group_t<T, 8>(a, st);
+    default: break;
+  }
   if (a.wave_chunks > 0) {
     switch (a.wave_chunks) {
       case 1: return launch_bwd_wave_t<T, 1>(a, st);

@@ -395,6 +395,11 @@ static lce_status run_xent_bwd(const void* logits, lce_dtype dtype, int64_t toke
                                    : 0;
   const char* forced = getenv("LCE_BWD_PATH");
   if (forced && !strcmp(forced, "apply")) a.wave_chunks = 0;
+  // Rows of at most 128 chunks with no scalar edges: several rows per wave, as
+  // in the forward (LCE_BWD_PATH=wave keeps one wave per row).
+  const bool edgeless = (vocab * esize) % 16 == 0 && ((uintptr_t)logits % 16) == 0;
+  if (a.wave_chunks > 0 && a.wave_chunks <= 2 && edgeless && !(forced && !strcmp(forced, "wave")))
+    a.rows_per_wave = nvec <= 32 ? 8 : nvec <= 64 ? 4 : 2;
   MeanState ms;
   if (a.wave_chunks == 0) {
     int cus = 0;
@@ -432,7 +437,7 @@ static lce_status run_xent_bwd(const void* logits, lce_dtype dtype, int64_t toke
     }
   } else if (out) {
     a.loss_out = out;
-    const int rows = lce::bwd_wave_rows(a);
+    const int rows = a.rows_per_wave ? 4 * a.rows_per_wave : lce::bwd_wave_rows(a);
     if (mean && (s = get_mean_state(stream, (tokens + rows - 1) / rows, &ms)) != LCE_OK) return s;
     a.mean_slots = ms.slots;
     a.epoch = ms.epoch;
@@ -440,7 +445,10 @@ static lce_status run_xent_bwd(const void* logits, lce_dtype dtype, int64_t toke
   hipError_t e = lce::launch_bwd(a, stream);
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   const char* tn = a.bf16 ? "unsigned short" : "float";
-  if (a.wave_chunks > 0) {
+  if (a.rows_per_wave) {
+    note_launch("xent_bwd_group_kernel<%s, %d, 4, 4, %s> grid %lld x 256", tn, a.rows_per_wave,
+                out ? "true" : "false", (long long)((tokens + 4 * a.rows_per_wave - 1) / (4 * a.rows_per_wave)));
+  } else if (a.wave_chunks > 0) {
     const int rows = lce::bwd_wave_rows(a);
     note_launch("xent_bwd_wave_kernel<%s, %d, %d, %s> grid %lld x %d", tn, a.wave_chunks, rows,
                 out ? "true" : "false", (long long)((tokens + rows - 1) / rows), 64 * rows);

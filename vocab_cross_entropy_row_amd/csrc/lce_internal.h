@@ -57,6 +57,7 @@ struct BwdArgs {
   const float* grad;        // 1 (mean) or tokens (none) fp32
   int reduce_mean;
   void* dlogits;            // same dtype and layout as logits; may be logits itself
+  int rows_per_wave;        // 2, 4 or 8: several short rows per wave (no scalar edges); else 0
   int wave_chunks;          // > 0: one wave per row holding <= 64 * wave_chunks chunks
   const float* stats;       // otherwise: (m, s, .) per row from the statistics mode
   int splits;               //   workgroups per row
