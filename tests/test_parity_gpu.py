@@ -236,7 +236,7 @@ def test_running_maximum_edge_rows(path, dtype, vocab):
     assert abs(got[10]) <= TOK_ABS  # one finite logit, the target: loss 0
 
 
-@pytest.mark.parametrize("path", ["auto", "wave", "block"])
+@pytest.mark.parametrize("path", ["auto", "wave", "block", "split", "split_many"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("vocab", [4096, 20000])
 def test_fixed_reference_guard_boundary(path, dtype, vocab):
@@ -246,7 +246,8 @@ def test_fixed_reference_guard_boundary(path, dtype, vocab):
     bound, in the first, a middle and the last chunk a lane reads; other rows hold many
     logits 36 to 41 above the first chunk, so sums of many large terms approach it too.
     4096-wide rows take the unrolled short loop, 20000-wide the long loop (the block
-    path takes its own loop); every row must match the oracle."""
+    path takes its own loop, the split path its slices, with its default slice count and
+    with 5 slices); every row must match the oracle."""
     heights = [40.0, 43.0, 44.0, 44.5, 45.0, 48.0]
     positions = [1024 + 5, vocab // 2 + 3, vocab - 9]
     rows = len(heights) * len(positions) + 4
@@ -265,6 +266,8 @@ def test_fixed_reference_guard_boundary(path, dtype, vocab):
     if dtype == "bf16":
         z = lce_synth.f32_to_bf16_bits(z)
     env = {} if path == "auto" else {"LCE_PATH": path}
+    if path == "split_many":
+        env = {"LCE_PATH": "split", "LCE_SPLITS": 5}
     with forced_env(**env):
         check_xent(z, t, dtype, f"guard {path} {dtype} {vocab}")
 

@@ -176,8 +176,8 @@ lce_status run_rows(const void* logits, int dtype, int64_t tokens, int64_t vocab
   else if (a.path == lce::XentPath::BlockRows)
     note_launch("xent_block_rows_kernel<%s, 8> grid %lld x %d", tn, (long long)tokens, lce::kRowThreads);
   else
-    note_launch("xent_split_partial_kernel<%s, 8> grid (%d, %lld) x %d + xent_split_merge_kernel "
-                "grid %lld x %d", tn, a.splits, (long long)tokens, lce::kRowThreads,
+    note_launch("xent_split_partial_kernel<%s, %d> grid (%d, %lld) x %d + xent_split_merge_kernel "
+                "grid %lld x %d", tn, a.bf16 ? 4 : 8, a.splits, (long long)tokens, lce::kRowThreads,
                 (long long)((tokens + lce::kRowThreads - 1) / lce::kRowThreads), lce::kRowThreads);
   return LCE_OK;
 }
