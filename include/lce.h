@@ -146,8 +146,11 @@ LCE_API lce_status lce_xent_fwd(const void* logits, lce_dtype dtype, int64_t tok
  * device array per GPU, held until the process ends.
  *
  * Limits: with LCE_REDUCTION_MEAN at most 2^19 workgroup slots (a mean over
- * at most 2^23 rows), and the split path's partials (8 bytes per row and
- * slice) within 4 MiB; a call beyond them returns LCE_ERR_UNSUPPORTED before
+ * at most 2^23 rows of 2 to 32 KiB, 16 rows per workgroup, or of rows with
+ * scalar edges; rows of at most 2 KiB without edges take 32, 16 or 8 rows per
+ * workgroup for rows of at most 512 B, 1 KiB or 2 KiB, so at most 2^24, 2^23
+ * or 2^22 rows), and the split path's partials (8 bytes per row and slice)
+ * within 4 MiB; a call beyond them returns LCE_ERR_UNSUPPORTED before
  * anything but the first call's clear is enqueued.
  *
  * Every call on a GPU shares that GPU's array, and the array keeps the last

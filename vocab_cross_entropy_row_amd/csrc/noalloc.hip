@@ -18,8 +18,10 @@ namespace lce {
 
 // Layout of the array: the mean's epoch word (kMeanHeaderBytes), then 2^19
 // 64-bit mean slots (4 MiB: a mean over up to 2^23 rows of <= 32 KiB on the
-// one-wave-per-row path, 16 rows per workgroup), then the split path's
-// (max, sum-exp) partials in the rest (8 bytes per row and slice).
+// one-wave-per-row path, 16 rows per workgroup, and 2^22 to 2^24 rows of
+// <= 2 KiB on the several-rows-per-wave path, 8 to 32 rows per workgroup),
+// then the split path's (max, sum-exp) partials in the rest (8 bytes per row
+// and slice).
 constexpr size_t kStaticBytes = size_t(8) << 20;
 constexpr size_t kSlotsOff = kMeanHeaderBytes;
 constexpr int64_t kMaxSlots = int64_t(1) << 19;
