@@ -15,7 +15,10 @@
 // so each element costs one decode, one FMA, one exponential and one multiply
 // by the row constant g / s, and the target element subtracts g.
 //
-// Two layouts:
+// Three layouts:
+//   xent_bwd_group_kernel  rows of at most 2 KiB without unaligned edges: 2, 4
+//                          or 8 rows per wave, each row in a group of lanes'
+//                          registers;
 //   xent_bwd_wave_kernel   rows of at most 64 * NCH 16-byte chunks: one wave
 //                          per row holds the whole row in registers, so the
 //                          logits are read once and the gradient written once;
@@ -26,8 +29,8 @@
 // dlogits may be the logits buffer itself (so neither pointer is restrict):
 // every element is read before the same thread writes it.
 //
-// With a loss output (the forward and the backward in one call), the wave
-// kernel also finishes each row's loss from the state it built, with the
+// With a loss output (the forward and the backward in one call), the group and
+// wave kernels also finish each row's loss from the state they built, with the
 // target logit read out of the row's registers: per-token losses, or their
 // deterministic mean (finish_mean).
 #include <hip/hip_runtime.h>

@@ -16,8 +16,11 @@
 // up to 2 * U KiB in flight; the row's scalar loads (target logit, unaligned
 // edges) are issued right behind the first batch.
 //
-// Three layouts of work over rows:
-//   wave_rows   one wavefront per row, 4 or 16 rows per workgroup (short rows);
+// Four layouts of work over rows:
+//   group_rows  2, 4 or 8 rows per wavefront, a group of lanes per row (rows
+//               of at most 2 KiB without unaligned edges);
+//   wave_rows   one wavefront per row, 4 or 16 rows per workgroup (rows of at
+//               most 32 KiB);
 //   block_rows  one 256-thread workgroup per row; the 4 waves stream the row
 //               together and merge their states through LDS (long rows);
 //   split       S workgroups per row write (max, sum-exp) partials, and a
