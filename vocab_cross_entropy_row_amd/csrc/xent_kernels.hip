@@ -121,8 +121,8 @@ __global__ __launch_bounds__(64 * WAVES) void xent_wave_rows_kernel(
 // resource covers them; a chunk past its row's end is loaded at an offset past
 // the resource (no memory is read) and folds as -inf.  The group's lanes then
 // merge their states (group_lse) and its first lane finishes the row.  Per row
-// this is one group of lanes' worth of fixed work (target, target logit,
-// reduction, store) instead of one wave's.
+// this is one group of lanes' worth of fixed work (target, reduction, store)
+// instead of one wave's, and the target logit comes out of the registers.
 template <typename T, int G, int U, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void xent_group_rows_kernel(
     const T* __restrict__ logits, int64_t tokens, int vocab, const int64_t* __restrict__ target,
@@ -156,7 +156,21 @@ __global__ __launch_bounds__(64 * WAVES) void xent_group_rows_kernel(
     }
     __builtin_amdgcn_sched_barrier(0);
     const int64_t tt = have ? local_target(t, vocab_start, vocab) : -1;
-    const float zt = have ? Vec<T>::scalar(logits + row * (int64_t)vocab + safe_target(tt, vocab)) : 0.0f;
+    // The target logit from the registers of the lane that holds it, spread over
+    // the group with a max: no load that waits for the target index (bf16
+    // [65536, 512] 13.31 -> 12.78 us, fp32 [65536, 256] 12.64 -> 12.01 us).
+    constexpr int E = Vec<T>::kElems;
+    const int tcg = tt >= 0 ? (int)(tt / E) : -1;
+    const int teg = tt >= 0 ? (int)(tt % E) : -1;
+    float zr = kNegInf;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (tcg == j + N * u) {
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if (e == teg) zr = Vec<T>::get(v[u], e);
+      }
+    const float zt = group_allreduce<N>(zr, MaxOp{});
 #pragma unroll
     for (int u = 0; u < U; ++u)
       if (j + N * u >= nvec) v[u] = Vec<T>::neg_inf();
