@@ -3,8 +3,8 @@
 Each (device, stream) pair has its own scratch buffer, and the host side keeps its
 tables (scratch buffers, GEMM plans and the hipBLASLt handle) under a mutex: calls issued
 concurrently from different threads onto different streams (row and fused cross-entropy,
-the fused backward with its library GEMMs, fused linear + JSD) must give the same results
-as the same calls made one after the other.
+the fused backward with its library GEMMs, the forward and backward in one call, fused
+linear + JSD) must give the same results as the same calls made one after the other.
 """
 import threading
 
@@ -35,11 +35,16 @@ def _cases():
         z = to_dev(lce_synth.f32_to_bf16_bits(lce_synth.normal_f32(300 + k, 0, 700 + 97 * k, 3001, 1.5)))
         t = torch.from_numpy(lce_synth.targets(400 + k, z.shape[0], 3001)).cuda()
         out.append(("xent", (z, t)))
+        out.append(("xent_fwd_bwd", (z, t)))
+        zs = to_dev(lce_synth.f32_to_bf16_bits(lce_synth.normal_f32(350 + k, 0, 1500 + 77 * k, 512, 1.5)))
+        ts = torch.from_numpy(lce_synth.targets(450 + k, zs.shape[0], 512)).cuda()
+        out.append(("xent_fwd_bwd", (zs, ts)))  # short rows: several per wave
         x = to_dev(lce_synth.normal_bf16_bits(500 + k, 0, 300 + 31 * k, 128, 1.0))
         w = to_dev(lce_synth.normal_bf16_bits(600 + k, 2, 2000 + 111 * k, 128, 0.1))
         tt = torch.from_numpy(lce_synth.targets(700 + k, x.shape[0], w.shape[0])).cuda()
         out.append(("fused", (x, w, tt)))
         out.append(("fused_bwd", (x, w, tt)))
+        out.append(("fused_fwd_bwd", (x, w, tt)))
         x2 = to_dev(lce_synth.normal_bf16_bits(800 + k, 0, x.shape[0], 128, 1.0))
         w2 = to_dev(lce_synth.normal_bf16_bits(900 + k, 2, w.shape[0], 128, 0.1))
         out.append(("jsd", (x, w, x2, w2)))
@@ -50,6 +55,12 @@ def _call(kind, args):
     if kind == "xent":
         z, t = args
         return torch.cat([lce.xent(z, t, "mean"), lce.xent(z, t, "none")])
+    if kind == "xent_fwd_bwd":
+        z, t = args
+        g = torch.full((1,), 0.5, device="cuda")
+        loss, d = lce.xent_fwd_bwd(z, t, g, "mean")
+        lt, _ = lce.xent_fwd_bwd(z, t, torch.ones(t.shape, device="cuda"), "none")
+        return torch.cat([loss, lt, d.float().reshape(-1)])
     if kind == "jsd":
         x, w, x2, w2 = args
         return torch.cat([lce.fused_linear_jsd(x, w, x2, w2, 0.3, "mean"),
@@ -59,6 +70,10 @@ def _call(kind, args):
         g = torch.full((1,), 0.7, device="cuda")
         dx, dw = lce.fused_linear_xent_bwd(x, w, t, g, "mean")
         return torch.cat([dx.reshape(-1), dw.reshape(-1)])
+    if kind == "fused_fwd_bwd":
+        g = torch.full((1,), 0.7, device="cuda")
+        loss, dx, dw = lce.fused_linear_xent_fwd_bwd(x, w, t, g, "mean")
+        return torch.cat([loss, dx.reshape(-1), dw.reshape(-1)])
     return torch.cat([lce.fused_linear_xent(x, w, t, "mean"), lce.fused_linear_xent(x, w, t, "none")])
 
 
