@@ -789,6 +789,50 @@ def time_valu_rate(torch) -> dict:
     return res
 
 
+def time_fused_skeleton(torch) -> dict:
+    """bench_probe's skeleton of the fused kernel's inner loop (mfma_lds_kernel): per wave and
+    k-step 8 MFMAs 32x32x16 bf16 on a 128 x 64 tile with its 6 fragment reads from LDS, a
+    barrier every 4 k-steps and 8 direct-to-LDS 1 KiB loads per wave every 4 k-steps, in 256
+    workgroups of 8 waves (one per CU), the parts added one at a time.  Cycles are s_memtime
+    cycles per wave, the per-workgroup maximum, median over workgroups; MFMA busy is 32
+    cycles (the datasheet rate of one 32x32x16 bf16 MFMA per SIMD) over the measured cycles
+    per MFMA per SIMD (two waves per SIMD)."""
+    import ctypes
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.bench_mfma_lds.restype = ctypes.c_int
+    lib.bench_mfma_lds.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_int, ctypes.c_void_p]
+    iters = 8192
+    cycles = torch.zeros(2048, dtype=torch.int64, device="cuda")
+    sink = torch.empty(256 * 512, dtype=torch.float32, device="cuda")
+    src = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda")
+    names = ("mfma_only", "fragment_reads_only", "mfma_and_fragment_reads",
+             "plus_barrier_every_4_ksteps", "plus_lds_dmas")
+    lds_bytes = (0, 6 * 1024, 6 * 1024, 6 * 1024, 8 * 1024)  # per wave per k-step
+    res = {}
+    s = torch.cuda.current_stream()
+    for v, name in enumerate(names):
+        med = []
+        for _ in range(3):
+            rc = lib.bench_mfma_lds(v, cycles.data_ptr(), sink.data_ptr(), src.data_ptr(), iters,
+                                    s.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"bench_mfma_lds failed (hipError {rc})")
+            torch.cuda.synchronize()
+            per_wg = cycles.view(256, 8).max(dim=1).values.double()
+            med.append(float(per_wg.median()))
+        c = statistics.median(med)
+        entry = {"cycles_per_wave": round(c)}
+        if v != 1:
+            per_mfma = c / (2 * 8 * iters)
+            entry["cycles_per_mfma_per_simd"] = round(per_mfma, 2)
+            entry["mfma_busy"] = round(32.0 / per_mfma, 4)
+        entry["lds_bytes_per_clk_per_cu"] = round(8 * iters * lds_bytes[v] / c, 1)
+        res[name] = entry
+    return {"kernel": "bench_probe.hip mfma_lds_kernel (256 x 8 waves, 8192 k-steps per wave)",
+            "variants": res}
+
+
 # ------------------------------------------------------------------ HBM counter calibration
 
 COPY_BYTES = 1 << 30
@@ -953,7 +997,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--extras", default=None,
                     help="comma list of extra measurements (backward, shard, sums, jsd, "
-                         "fused_bwd, stream_read); default: all of them when --workloads is all")
+                         "fused_bwd, split, sweep, stream_read, skeleton); default: all of them "
+                         "when --workloads is all")
     ap.add_argument("--eager", action="store_true",
                     help="time plain launches instead of a graph replay (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -1012,7 +1057,8 @@ def main(argv=None) -> int:
     head_name = lce_synth.HEADLINE if lce_synth.HEADLINE in names else names[0]
     head = lce_synth.WORKLOADS[head_name]
 
-    all_extras = ("backward", "shard", "sums", "jsd", "fused_bwd", "split", "sweep", "stream_read")
+    all_extras = ("backward", "shard", "sums", "jsd", "fused_bwd", "split", "sweep", "stream_read",
+                  "skeleton")
     if args.extras is not None:
         extras = [e for e in args.extras.split(",") if e]
         unknown = [e for e in extras if e not in all_extras]
@@ -1095,6 +1141,15 @@ def main(argv=None) -> int:
               f"{probe['read_us']:.2f} µs for {pw.name}'s {hb} logit bytes",
               file=sys.stderr, flush=True)
 
+    skeleton = None
+    if "skeleton" in extras:
+        skeleton = time_fused_skeleton(torch)
+        sv = skeleton["variants"]
+        print("[bench] fused-loop skeleton, MFMA busy: " + ", ".join(
+            f"{k} {v['mfma_busy']:.3f}" for k, v in sv.items() if "mfma_busy" in v) +
+            f"; LDS reads alone {sv['fragment_reads_only']['lds_bytes_per_clk_per_cu']} B/clk/CU",
+            file=sys.stderr, flush=True)
+
     if args.copy_calibration:
         copy_calibration(torch)
 
@@ -1162,6 +1217,8 @@ def main(argv=None) -> int:
         line["fused_backward"] = fbwd
     if probe is not None:
         line["stream_read_probe"] = probe
+    if skeleton is not None:
+        line["fused_skeleton_probe"] = skeleton
     print(json.dumps(line), flush=True)
     return 0
 

@@ -177,7 +177,7 @@ def test_bwd_unaligned_base(dtype):
 # Rows of at most 128 16-byte chunks with no scalar edges: several rows per wave (8, 4
 # or 2 rows for up to 32, 64 or 128 chunks), at and around each boundary, ragged row counts.
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("rows,vocab", [(1, 8), (7, 64), (33, 124), (100, 128), (257, 132),
+@pytest.mark.parametrize("rows,vocab", [(5, 4), (1, 8), (7, 64), (33, 124), (100, 128), (257, 132),
                                         (31, 256), (1001, 260), (65, 512)])
 @pytest.mark.parametrize("reduction", ["mean", "none"])
 def test_bwd_several_rows_per_wave(dtype, rows, vocab, reduction):
@@ -198,3 +198,49 @@ def test_bwd_several_rows_per_wave(dtype, rows, vocab, reduction):
     _check(got, want, gs[:, None], dtype, f"grouped {dtype} {rows}x{v} {reduction}")
     one_wave = _run(z, t, dtype, reduction, grad, env={"LCE_BWD_PATH": "wave"})
     _check(one_wave, want, gs[:, None], dtype, f"one wave {dtype} {rows}x{v} {reduction}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("chunks", [16, 48, 125])
+@pytest.mark.parametrize("reduction", ["mean", "none"])
+def test_bwd_several_rows_per_wave_special_values(dtype, chunks, reduction):
+    """Special values on the several-rows-per-wave backward: rows with +inf, a NaN logit, a
+    row of -inf only and invalid targets get NaN gradients, as in the oracle, and the
+    finite rows that share their wave keep theirs; the one-call forward and backward gives
+    the same gradient and the forward's losses."""
+    vocab = chunks * (4 if dtype == "f32" else 8)
+    rows = 37
+    z = _logits(chunks * 11 + vocab, rows, vocab, "f32")
+    z[0, 0] = np.inf
+    z[1, vocab // 2] = np.inf
+    z[2, vocab - 1] = np.inf
+    z[3, 5] = np.nan
+    z[4, :] = -np.inf
+    t = lce_synth.targets(chunks + vocab, rows, vocab)
+    t[5], t[6], t[7], t[8] = -1, vocab, 1 << 40, -(1 << 40)
+    if dtype == "bf16":
+        z = lce_synth.f32_to_bf16_bits(z)
+    grad = np.float32(1.25) if reduction == "mean" else np.linspace(-1, 1, rows).astype(np.float32)
+    got = _run(z, t, dtype, reduction, grad)
+    g = 8 if chunks <= 32 else 4 if chunks <= 64 else 2
+    assert f"xent_bwd_group_kernel<{'float' if dtype == 'f32' else 'unsigned short'}, {g}, 4, 4, false>" \
+        in lce.lce_last_launch()
+    want = oracle.xent_bwd(z, t, np.asarray(grad, dtype=np.float64), reduction, dtype=dtype)
+    gs = (np.full(rows, float(grad) / rows) if reduction == "mean" else grad.astype(np.float64))
+    _check(got, want, gs[:, None], dtype, f"special values {dtype} {vocab} {reduction}")
+    assert np.isnan(got[:9]).all() and np.isfinite(got[9:]).all()
+    zd = to_dev(z)
+    td = torch.from_numpy(t).cuda()
+    gd = torch.from_numpy(np.asarray(grad, dtype=np.float32).reshape(-1)).cuda()
+    loss, d = lce.xent_fwd_bwd(zd, td, gd, reduction)
+    fwd = lce.xent(zd, td, reduction)
+    torch.cuda.synchronize()
+    assert np.array_equal(_to_host(d, dtype), got, equal_nan=True)
+    lw = oracle.xent_rows(z, t, dtype=dtype)
+    lg = loss.cpu().numpy().astype(np.float64)
+    if reduction == "mean":
+        assert np.isnan(lg).all() and np.isnan(fwd.cpu().numpy()).all()
+    else:
+        assert np.array_equal(np.isnan(lg), np.isnan(lw))
+        ok = ~np.isnan(lw)
+        assert np.abs(lg[ok] - lw[ok]).max() <= 1e-4

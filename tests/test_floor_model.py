@@ -51,10 +51,12 @@ def test_bench_refuses_several_gpus():
 
 
 def test_stream_read_probe_exports():
-    """bench_probe.so (the plain-read and VALU-rate probes bench.py reports) exports both entries."""
+    """bench_probe.so (the plain-read, VALU-rate and fused-loop skeleton probes bench.py reports)
+    exports their entries."""
     import ctypes
     if not os.path.exists(bench.PROBE_LIB):
         pytest.skip("bench_probe.so not built (__graft_entry__.build() builds it)")
     lib = ctypes.CDLL(bench.PROBE_LIB)
     assert hasattr(lib, "bench_stream_read")
     assert hasattr(lib, "bench_valu_rate")
+    assert hasattr(lib, "bench_mfma_lds")

@@ -103,7 +103,7 @@ def test_forced_paths(path, extra, dtype, rows, vocab):
 # Rows of at most 128 16-byte chunks with no scalar edges take several rows per wave
 # (8, 4 or 2 rows for up to 32, 64 or 128 chunks): chunk counts at and around each
 # boundary, ragged row counts (a last wave with fewer rows than it holds).
-GROUP = [(1, 8), (7, 64), (33, 124), (100, 128), (257, 132), (31, 256), (1001, 260), (65, 512)]
+GROUP = [(5, 4), (1, 8), (7, 64), (33, 124), (100, 128), (257, 132), (31, 256), (1001, 260), (65, 512)]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -140,6 +140,39 @@ def test_several_rows_per_wave_edge_rows(dtype):
     t = lce_synth.targets(78, rows, vocab)
     t[1], t[2] = 5, 300
     check_xent(z, t, dtype, f"edge rows {dtype}")
+
+
+def special_rows(seed, rows, vocab):
+    """fp32 rows with the special values of the one-row tests, at the top of the batch:
+    +inf at the first, an interior and the last element (NaN loss), a NaN logit, a row of
+    -inf only (NaN loss), then targets at -1, at vocab, far past it and far below 0 (NaN
+    loss), then finite rows.  Returns the logits, the targets and how many rows are NaN."""
+    z = rand_logits(seed, rows, vocab, "f32", std=2.0)
+    z[0, 0] = np.inf
+    z[1, vocab // 2] = np.inf
+    z[2, vocab - 1] = np.inf
+    z[3, min(5, vocab - 1)] = np.nan
+    z[4, :] = -np.inf
+    t = lce_synth.targets(seed + 1, rows, vocab)
+    t[5], t[6], t[7], t[8] = -1, vocab, 1 << 40, -(1 << 40)
+    return z, t, 9
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("chunks", [16, 48, 125])
+def test_several_rows_per_wave_special_values(dtype, chunks):
+    """Special values on the several-rows-per-wave kernel (8, 4 and 2 rows per wave):
+    the NaN rows must not leak into the finite rows that share their wave."""
+    vocab = chunks * (4 if dtype == "f32" else 8)
+    z, t, n_nan = special_rows(chunks * 7 + vocab, 37, vocab)
+    if dtype == "bf16":
+        z = lce_synth.f32_to_bf16_bits(z)
+    check_xent(z, t, dtype, f"special values {dtype} {vocab}")
+    got = gpu_xent(z, t, "none", dtype)
+    assert np.isnan(got[:n_nan]).all() and np.isfinite(got[n_nan:]).all()
+    g = 8 if chunks <= 32 else 4 if chunks <= 64 else 2
+    assert f"xent_group_rows_kernel<{'float' if dtype == 'f32' else 'unsigned short'}, {g}, 4, 4>" \
+        in lce.lce_last_launch()
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
