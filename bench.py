@@ -829,8 +829,11 @@ def time_fused_skeleton(torch) -> dict:
             entry["mfma_busy"] = round(32.0 / per_mfma, 4)
         entry["lds_bytes_per_clk_per_cu"] = round(8 * iters * lds_bytes[v] / c, 1)
         res[name] = entry
+    # the datasheet's 2.5 PFLOP/s is 256 CUs x 4096 flop per clock x 2.4 GHz: the MFMA-only
+    # variant measures the flop per clock a CU's four SIMDs issue
+    per_clk = 4 * 32 * 32 * 16 * 2 / res["mfma_only"]["cycles_per_mfma_per_simd"]
     return {"kernel": "bench_probe.hip mfma_lds_kernel (256 x 8 waves, 8192 k-steps per wave)",
-            "variants": res}
+            "bf16_flop_per_clk_per_cu": round(per_clk, 1), "variants": res}
 
 
 # ------------------------------------------------------------------ HBM counter calibration
