@@ -796,14 +796,15 @@ def time_fused_skeleton(torch) -> dict:
     workgroups of 8 waves (one per CU), the parts added one at a time.  Cycles are s_memtime
     cycles per wave, the per-workgroup maximum, median over workgroups; MFMA busy is 32
     cycles (the datasheet rate of one 32x32x16 bf16 MFMA per SIMD) over the measured cycles
-    per MFMA per SIMD (two waves per SIMD)."""
+    per MFMA per SIMD (two waves per SIMD).  Beside it, bench_probe's lds_read_kernel: LDS
+    read throughput alone (ds_read_b128, nothing else) at 4, 8 and 16 waves per CU."""
     import ctypes
     lib = ctypes.CDLL(PROBE_LIB)
     lib.bench_mfma_lds.restype = ctypes.c_int
     lib.bench_mfma_lds.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                    ctypes.c_int, ctypes.c_void_p]
     iters = 8192
-    cycles = torch.zeros(2048, dtype=torch.int64, device="cuda")
+    cycles = torch.zeros(256 * 16, dtype=torch.int64, device="cuda")  # 2048 waves; 4096 for the LDS probe
     sink = torch.empty(256 * 512, dtype=torch.float32, device="cuda")
     src = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda")
     names = ("mfma_only", "fragment_reads_only", "mfma_and_fragment_reads",
@@ -819,7 +820,7 @@ def time_fused_skeleton(torch) -> dict:
             if rc != 0:
                 raise RuntimeError(f"bench_mfma_lds failed (hipError {rc})")
             torch.cuda.synchronize()
-            per_wg = cycles.view(256, 8).max(dim=1).values.double()
+            per_wg = cycles[:2048].view(256, 8).max(dim=1).values.double()
             med.append(float(per_wg.median()))
         c = statistics.median(med)
         entry = {"cycles_per_wave": round(c)}
@@ -829,11 +830,27 @@ def time_fused_skeleton(torch) -> dict:
             entry["mfma_busy"] = round(32.0 / per_mfma, 4)
         entry["lds_bytes_per_clk_per_cu"] = round(8 * iters * lds_bytes[v] / c, 1)
         res[name] = entry
+    # LDS read throughput alone at 1, 2 and 4 waves per SIMD (bench_probe's lds_read_kernel)
+    lib.bench_lds_read.restype = ctypes.c_int
+    lib.bench_lds_read.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                   ctypes.c_void_p]
+    lds_read = {}
+    rsink = torch.empty(256 * 64 * 16, dtype=torch.int32, device="cuda")
+    for w in (4, 8, 16):
+        med = []
+        for _ in range(3):
+            rc = lib.bench_lds_read(w, cycles.data_ptr(), rsink.data_ptr(), 4096, s.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"bench_lds_read failed (hipError {rc})")
+            torch.cuda.synchronize()
+            med.append(float(cycles[:256 * w].view(256, w).max(dim=1).values.double().median()))
+        lds_read[f"{w}_waves_per_cu"] = round(w * 4096 * 8 * 1024 / statistics.median(med), 1)
     # the datasheet's 2.5 PFLOP/s is 256 CUs x 4096 flop per clock x 2.4 GHz: the MFMA-only
     # variant measures the flop per clock a CU's four SIMDs issue
     per_clk = 4 * 32 * 32 * 16 * 2 / res["mfma_only"]["cycles_per_mfma_per_simd"]
     return {"kernel": "bench_probe.hip mfma_lds_kernel (256 x 8 waves, 8192 k-steps per wave)",
-            "bf16_flop_per_clk_per_cu": round(per_clk, 1), "variants": res}
+            "bf16_flop_per_clk_per_cu": round(per_clk, 1), "variants": res,
+            "lds_read_bytes_per_clk_per_cu": lds_read}
 
 
 # ------------------------------------------------------------------ HBM counter calibration
@@ -1150,7 +1167,8 @@ def main(argv=None) -> int:
         sv = skeleton["variants"]
         print("[bench] fused-loop skeleton, MFMA busy: " + ", ".join(
             f"{k} {v['mfma_busy']:.3f}" for k, v in sv.items() if "mfma_busy" in v) +
-            f"; LDS reads alone {sv['fragment_reads_only']['lds_bytes_per_clk_per_cu']} B/clk/CU",
+            "; LDS reads alone (B/clk/CU) at 4, 8, 16 waves per CU: " +
+            ", ".join(str(v) for v in skeleton["lds_read_bytes_per_clk_per_cu"].values()),
             file=sys.stderr, flush=True)
 
     if args.copy_calibration:

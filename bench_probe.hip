@@ -18,6 +18,9 @@
 // 8-wave workgroups, one per CU.  Variants add these parts one at a time, so the cycles each
 // costs the matrix cores can be read off (s_memtime cycles per wave).
 //
+// lds_read_kernel measures LDS read throughput alone: W waves per workgroup, one workgroup
+// per CU, each wave reading 1 KiB blocks with ds_read_b128, 8 per step, folded with xor.
+//
 // Build (done by __graft_entry__.build()):
 //   hipcc -O3 --offload-arch=gfx950 -Xclang -target-feature -Xclang -packed-fp32-ops
 //         -shared -fPIC bench_probe.hip -o bench_probe.so
@@ -184,6 +187,26 @@ __global__ __launch_bounds__(kSkThreads) void mfma_lds_kernel(int iters, unsigne
   if (lane == 0) cycles[blockIdx.x * kSkWaves + wave] = t1 - t0;
 }
 
+// W waves; reads cover LDS bytes [0, 64 KiB) (64 blocks of 1 KiB), 96 KiB requested so that
+// one workgroup runs per CU.
+template <int W>
+__global__ __launch_bounds__(64 * W) void lds_read_kernel(int iters, unsigned long long* cycles,
+                                                          uint32_t* sink) {
+  extern __shared__ u32x4 lds[];
+  for (int i = threadIdx.x; i < 4096; i += 64 * W) lds[i] = (u32x4){(uint32_t)i, 1u, 2u, 3u};
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  u32x4 x = (u32x4){0u, 0u, 0u, 0u};
+  const unsigned long long t0 = clock64();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x ^= lds[((it * 8 + k + wave * 5) & 63) * 64 + lane];
+  }
+  const unsigned long long t1 = clock64();
+  sink[blockIdx.x * 64 * W + threadIdx.x] = x.x ^ x.y ^ x.z ^ x.w;
+  if (lane == 0) cycles[blockIdx.x * W + wave] = t1 - t0;
+}
+
 }  // namespace
 
 // Enqueue one valu_rate_kernel<mode> launch of `blocks` workgroups of 256 threads, each
@@ -250,5 +273,32 @@ extern "C" __attribute__((visibility("default"))) int bench_mfma_lds(int variant
     default: SK_LAUNCH(4) break;
   }
 #undef SK_LAUNCH
+  return (int)hipGetLastError();
+}
+
+// Enqueue one lds_read_kernel<waves> launch (waves 4, 8 or 16): 256 workgroups, `iters`
+// steps of 8 reads per wave.  `cycles` holds 256 * waves uint64, `sink` 256 * 64 * waves
+// uint32.  Returns a hipError_t value: hipErrorInvalidValue for other wave counts, iters
+// outside 1..2^20 or a null pointer.
+extern "C" __attribute__((visibility("default"))) int bench_lds_read(int waves, unsigned long long* cycles,
+                                                                      uint32_t* sink, int iters,
+                                                                      hipStream_t stream) {
+  if (!cycles || !sink || iters < 1 || iters > (1 << 20) || (waves != 4 && waves != 8 && waves != 16))
+    return (int)hipErrorInvalidValue;
+  hipError_t e = hipSuccess;
+#define LR_LAUNCH(W)                                                                                \
+  e = hipFuncSetAttribute((const void*)lds_read_kernel<W>, hipFuncAttributeMaxDynamicSharedMemorySize, \
+                          kSkLdsBytes);                                                             \
+  if (e != hipSuccess) return (int)e;                                                               \
+  hipLaunchKernelGGL(lds_read_kernel<W>, dim3(kSkBlocks), dim3(64 * W), kSkLdsBytes, stream, iters,   \
+                     cycles, sink);
+  if (waves == 4) {
+    LR_LAUNCH(4)
+  } else if (waves == 8) {
+    LR_LAUNCH(8)
+  } else {
+    LR_LAUNCH(16)
+  }
+#undef LR_LAUNCH
   return (int)hipGetLastError();
 }

@@ -60,3 +60,4 @@ def test_stream_read_probe_exports():
     assert hasattr(lib, "bench_stream_read")
     assert hasattr(lib, "bench_valu_rate")
     assert hasattr(lib, "bench_mfma_lds")
+    assert hasattr(lib, "bench_lds_read")
