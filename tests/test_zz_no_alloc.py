@@ -42,10 +42,13 @@ def _call(fn, z, t, reduction):
 
 
 # (dtype, (rows, vocab) of the first call, (rows, vocab) of the second, smaller call, the
-# kernel the default selection launches).  One wave per row; one workgroup per row (rows
-# over 32 KiB, no mean: the mean takes one wave per row there); split vocab (fewer rows
-# than twice the CU count).
+# kernel the default selection launches).  Several rows per wave (rows of at most 2 KiB
+# with no scalar edges); one wave per row; one workgroup per row (rows over 32 KiB, no
+# mean: the mean takes one wave per row there); split vocab (fewer rows than twice the CU
+# count).
 CASES = [
+    ("bf16", (65536, 512), (1001, 256), "xent_group_rows_kernel"),
+    ("f32", (20000, 64), (33, 32), "xent_group_rows_kernel"),
     ("f32", (4099, 3001), (1000, 500), "xent_wave_rows_kernel"),
     ("bf16", (8192, 4096), (777, 4096), "xent_wave_rows_kernel"),
     ("f32", (600, 40000), (513, 20000), "xent_block_rows_kernel"),
@@ -87,3 +90,33 @@ def test_noalloc_refuses_sizes_beyond_its_array():
     got, _ = _call(lce.lce_xent_fwd_noalloc, z, t, "none")
     torch.cuda.synchronize()
     assert torch.all(got == 0)
+
+
+def test_noalloc_refuses_grouped_means_beyond_its_array():
+    """Rows of 16 bytes take 8 rows per wave, 32 per workgroup: a mean over 2^24 + 1 such
+    rows needs 2^19 + 1 workgroup slots and is refused before anything is enqueued; the
+    same rows per token are computed (ln 4 for four equal logits)."""
+    rows = (1 << 24) + 1
+    z = torch.zeros((rows, 4), device="cuda")
+    t = torch.zeros(rows, dtype=torch.int64, device="cuda")
+    out = torch.full((1,), 5.0, device="cuda")
+    st = lce.lce_xent_fwd_noalloc(z.data_ptr(), lce.LCE_F32, rows, 4, t.data_ptr(),
+                                  lce.LCE_REDUCTION_MEAN, out.data_ptr(),
+                                  torch.cuda.current_stream().cuda_stream)
+    assert st == lce.LCE_ERR_UNSUPPORTED
+    assert "slots" in lce.lce_last_error()
+    torch.cuda.synchronize()
+    assert out.item() == 5.0
+    got, launch = _call(lce.lce_xent_fwd_noalloc, z, t, "none")
+    torch.cuda.synchronize()
+    assert launch.startswith("xent_group_rows_kernel"), launch
+    assert torch.all((got - float(np.log(4.0))).abs() <= 1e-6)
+    # 2^24 rows fill the 2^19 slots exactly
+    st = lce.lce_xent_fwd_noalloc(z.data_ptr(), lce.LCE_F32, rows - 1, 4, t.data_ptr(),
+                                  lce.LCE_REDUCTION_MEAN, out.data_ptr(),
+                                  torch.cuda.current_stream().cuda_stream)
+    assert st == lce.LCE_OK, lce.lce_last_error()
+    torch.cuda.synchronize()
+    assert abs(out.item() - float(np.log(4.0))) <= 1e-6
+    del z, t, got
+    torch.cuda.empty_cache()
