@@ -244,3 +244,39 @@ def test_bwd_several_rows_per_wave_special_values(dtype, chunks, reduction):
         assert np.array_equal(np.isnan(lg), np.isnan(lw))
         ok = ~np.isnan(lw)
         assert np.abs(lg[ok] - lw[ok]).max() <= 1e-4
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_bwd_randomized_several_rows_per_wave(seed):
+    """Seeded random cases on the several-rows-per-wave backward, 8 per seed: 1-2000 rows of
+    1-128 16-byte chunks, fp32 or bf16, scales 0.05 to 25, spikes, -inf entries, some invalid
+    targets, either reduction; gradients against the oracle's softmax minus one-hot."""
+    rng = np.random.default_rng(7500 + seed)
+    for case in range(8):
+        dtype = str(rng.choice(["f32", "bf16"]))
+        per = 4 if dtype == "f32" else 8
+        rows = int(np.exp(rng.uniform(0.0, np.log(2000.0))))
+        vocab = int(rng.integers(1, 129)) * per
+        std = float(rng.choice([0.05, 1.0, 4.0, 25.0]))
+        z = rng.standard_normal((rows, vocab), dtype=np.float32) * np.float32(std)
+        t = rng.integers(0, vocab, rows)
+        if rng.random() < 0.5:
+            for r in rng.integers(0, rows, 1 + rows // 4):
+                z[r, rng.integers(0, vocab)] += np.float32(rng.uniform(5.0, 120.0))
+        if rng.random() < 0.3:
+            keep = z[np.arange(rows), t].copy()
+            z[rng.random((rows, vocab)) < 0.2] = -np.inf
+            z[np.arange(rows), t] = keep
+        if rng.random() < 0.3:
+            bad = rng.integers(0, rows, 1 + rows // 16)
+            t[bad] = rng.choice([-1, vocab, 1 << 40], bad.size)
+        host = z if dtype == "f32" else lce_synth.f32_to_bf16_bits(z)
+        reduction = str(rng.choice(["mean", "none"]))
+        grad = (np.float32(rng.uniform(0.5, 2.0)) if reduction == "mean"
+                else rng.uniform(-1.0, 1.0, rows).astype(np.float32))
+        label = f"seed {seed} case {case}: {dtype} {rows}x{vocab} std {std} {reduction}"
+        got = _run(host, t, dtype, reduction, grad)
+        assert "xent_bwd_group_kernel" in lce.lce_last_launch(), label
+        want = oracle.xent_bwd(host, t, np.asarray(grad, dtype=np.float64), reduction, dtype=dtype)
+        gs = (np.full(rows, float(grad) / rows) if reduction == "mean" else grad.astype(np.float64))
+        _check(got, want, gs[:, None], dtype, label)

@@ -347,6 +347,49 @@ def test_randomized_rows(seed):
         assert abs(gm - wm) <= MEAN_REL * abs(wm) + MEAN_ABS_FLOOR, f"{label}: mean {gm} vs {wm}"
 
 
+@pytest.mark.parametrize("seed", range(3))
+def test_randomized_several_rows_per_wave(seed):
+    """Seeded random cases on the several-rows-per-wave kernel, 16 per seed: 1-3000 rows of
+    1-128 16-byte chunks (aligned, no scalar edges), fp32 or bf16, logit scales 0.05 to 25,
+    shifts of -3000 to +1000, spikes 5 to 120 above the rest, -inf entries around finite
+    targets, some invalid targets; per-token losses and the mean against the oracle."""
+    rng = np.random.default_rng(7300 + seed)
+    for case in range(16):
+        dtype = str(rng.choice(["f32", "bf16"]))
+        per = 4 if dtype == "f32" else 8
+        rows = int(np.exp(rng.uniform(0.0, np.log(3000.0))))
+        nvec = int(rng.integers(1, 129))
+        vocab = nvec * per
+        std = float(rng.choice([0.05, 1.0, 4.0, 25.0]))
+        z = rng.standard_normal((rows, vocab), dtype=np.float32) * np.float32(std)
+        z += np.float32(rng.choice([0.0, 0.0, 1000.0, -3000.0]))
+        t = rng.integers(0, vocab, rows)
+        if rng.random() < 0.5:
+            for r in rng.integers(0, rows, 1 + rows // 4):
+                z[r, rng.integers(0, vocab)] += np.float32(rng.uniform(5.0, 120.0))
+        if rng.random() < 0.3:
+            keep = z[np.arange(rows), t].copy()
+            z[rng.random((rows, vocab)) < 0.2] = -np.inf
+            z[np.arange(rows), t] = keep
+        if rng.random() < 0.3:
+            bad = rng.integers(0, rows, 1 + rows // 16)
+            t[bad] = rng.choice([-1, vocab, 1 << 40], bad.size)
+        host = z if dtype == "f32" else lce_synth.f32_to_bf16_bits(z)
+        label = f"seed {seed} case {case}: {dtype} {rows}x{vocab} std {std}"
+        want = oracle.xent_rows(host, t, dtype=dtype)
+        zd, td = to_dev(host), torch.from_numpy(t.astype(np.int64)).cuda()
+        got = lce.xent(zd, td, "none").cpu().numpy().astype(np.float64)
+        assert "xent_group_rows_kernel" in lce.lce_last_launch(), label
+        gm = lce.xent(zd, td, "mean").item()
+        assert np.array_equal(np.isnan(got), np.isnan(want)), label
+        assert np.nanmax(np.abs(got - want), initial=0.0) <= TOK_ABS, label
+        wm = oracle.mean(want)
+        if math.isnan(wm):
+            assert math.isnan(gm), label
+        else:
+            assert abs(gm - wm) <= MEAN_REL * abs(wm) + MEAN_ABS_FLOOR, f"{label}: mean {gm} vs {wm}"
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_infinite_logits(dtype):
     """+inf anywhere in a row makes that row's loss NaN, and a row of -inf only is NaN,

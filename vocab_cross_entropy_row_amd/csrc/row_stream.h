@@ -107,14 +107,23 @@ __device__ __forceinline__ void fold_two_pass(Lse& st, const typename Vec<T>::ra
   st.m = mn;
 }
 
+// Rise of the running maximum (log2 units) up to which a batch's terms, taken
+// against the old reference, are rescaled to the new one instead of taken
+// again.  Rescaling carries two roundings of each term's exponent (the FMA's
+// result and the difference of the references), each at most half an ulp of
+// the rise: below 8 that is 2^-22, so the batch's largest term, which becomes
+// the row's largest, is off by at most 2^-21 * ln 2 = 3.3e-7 relative.  Past
+// the cut-off (and always before a term could overflow fp32) the exponentials
+// are taken again against the new maximum.
+constexpr float kRescaleRise = 8.0f;
+
 // One-pass fold of chunks [U0, U) against the running maximum, which must be
 // finite: each element is decoded once and feeds both the batch maximum and
-// its exponential 2^(z*L - fp32(m*L)).  If the batch raised the maximum, the
-// sum is rescaled to the new one afterwards, which is exact arithmetic on the
-// same terms; if it raised it so far (more than 64 in log2 units) that a term
-// may have overflowed, the batch's exponentials are taken again against the
-// new maximum.  Per element this is one decode, a third of a 3-input max, one
-// FMA, one exponential and one add: one decode less than the two-pass fold.
+// its exponential 2^(z*L - fp32(m*L)).  If the batch raised the maximum by at
+// most kRescaleRise, the sum is rescaled to the new one afterwards; if it
+// raised it further, the batch's exponentials are taken again against the new
+// maximum.  Per element this is one decode, a third of a 3-input max, one FMA,
+// one exponential and one add: one decode less than the two-pass fold.
 template <typename T, int U, int U0>
 __device__ __forceinline__ void fold_one_pass(Lse& st, const typename Vec<T>::raw (&v)[U]) {
   static_assert(0 <= U0 && U0 < U, "chunk range");
@@ -134,7 +143,7 @@ __device__ __forceinline__ void fold_one_pass(Lse& st, const typename Vec<T>::ra
     part[u] = acc;
   }
   if (bm > st.m) {
-    if (bm * kLog2e - M > 64.0f) {
+    if (bm * kLog2e - M > kRescaleRise) {
       const float Mn = bm * kLog2e;
 #pragma unroll
       for (int u = U0; u < U; ++u) {
