@@ -280,3 +280,54 @@ def test_bwd_randomized_several_rows_per_wave(seed):
         want = oracle.xent_bwd(host, t, np.asarray(grad, dtype=np.float64), reduction, dtype=dtype)
         gs = (np.full(rows, float(grad) / rows) if reduction == "mean" else grad.astype(np.float64))
         _check(got, want, gs[:, None], dtype, label)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_bwd_randomized_rows(seed):
+    """Seeded random cases on every backward path, 10 per seed: 1-300 rows, vocab
+    log-uniform in [1, 40000), fp32 or bf16, scales 0.05 to 25, shifts of -3000 to +1000,
+    spikes 5 to 120 above the rest, -inf entries around finite targets, some invalid
+    targets, the first row 0-7 elements past an aligned address, either reduction, the
+    default path or one wave per row or the statistics-then-apply path; gradients against
+    the oracle, and the one-call forward and backward's gradient bitwise the same."""
+    rng = np.random.default_rng(7700 + seed)
+    for case in range(10):
+        dtype = str(rng.choice(["f32", "bf16"]))
+        rows = int(rng.integers(1, 301))
+        vocab = max(1, int(np.exp(rng.uniform(0.0, np.log(40000.0)))))
+        std = float(rng.choice([0.05, 1.0, 4.0, 25.0]))
+        z = rng.standard_normal((rows, vocab), dtype=np.float32) * np.float32(std)
+        z += np.float32(rng.choice([0.0, 0.0, 1000.0, -3000.0]))
+        t = rng.integers(0, vocab, rows)
+        if rng.random() < 0.5:
+            for r in rng.integers(0, rows, 1 + rows // 4):
+                z[r, rng.integers(0, vocab)] += np.float32(rng.uniform(5.0, 120.0))
+        if rng.random() < 0.3:
+            keep = z[np.arange(rows), t].copy()
+            z[rng.random((rows, vocab)) < 0.2] = -np.inf
+            z[np.arange(rows), t] = keep
+        if rng.random() < 0.3:
+            bad = rng.integers(0, rows, 1 + rows // 16)
+            t[bad] = rng.choice([-1, vocab, 1 << 40], bad.size)
+        host = z if dtype == "f32" else lce_synth.f32_to_bf16_bits(z)
+        reduction = str(rng.choice(["mean", "none"]))
+        grad = (np.float32(rng.uniform(0.5, 2.0)) if reduction == "mean"
+                else rng.uniform(-1.0, 1.0, rows).astype(np.float32))
+        path = str(rng.choice(["auto", "wave", "apply"]))
+        off = int(rng.integers(0, 8))
+        buf = np.zeros(off + rows * vocab, dtype=host.dtype)
+        buf[off:] = host.reshape(-1)
+        zd = to_dev(buf)[off:].view(rows, vocab)
+        td = torch.from_numpy(t.astype(np.int64)).cuda()
+        gd = torch.from_numpy(np.asarray(grad, dtype=np.float32).reshape(-1)).cuda()
+        label = f"seed {seed} case {case}: {dtype} {rows}x{vocab} std {std} offset {off} {path} {reduction}"
+        env = {} if path == "auto" else {"LCE_BWD_PATH": path}
+        with forced_env(**env):
+            d = lce.xent_bwd(zd, td, gd, reduction)
+            _, d2 = lce.xent_fwd_bwd(zd, td, gd, reduction)
+        torch.cuda.synchronize()
+        got = _to_host(d, dtype)
+        assert np.array_equal(got, _to_host(d2, dtype), equal_nan=True), label
+        want = oracle.xent_bwd(host, t, np.asarray(grad, dtype=np.float64), reduction, dtype=dtype)
+        gs = (np.full(rows, float(grad) / rows) if reduction == "mean" else grad.astype(np.float64))
+        _check(got, want, gs[:, None], dtype, label)
