@@ -146,3 +146,49 @@ def test_repeated_merge_bitwise_identical():
     first = lce.xent_merge(parts, td, vocab, "mean").clone()
     for _ in range(10):
         assert torch.equal(lce.xent_merge(parts, td, vocab, "mean"), first)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_randomized_shards(seed):
+    """Seeded random cases, 8 per seed: 1-400 rows, vocab log-uniform in [2, 60000) split at
+    random into 1-7 shards, fp32 or bf16, scales 0.05 to 25, spikes 5 to 120 above the rest,
+    -inf entries around finite targets, some invalid targets, any row path; each shard's
+    statistics against the oracle's, and the merged losses against the whole-row oracle."""
+    rng = np.random.default_rng(7900 + seed)
+    for case in range(8):
+        dtype = str(rng.choice(["f32", "bf16"]))
+        rows = int(rng.integers(1, 401))
+        vocab = max(2, int(np.exp(rng.uniform(np.log(2.0), np.log(60000.0)))))
+        std = float(rng.choice([0.05, 1.0, 4.0, 25.0]))
+        z = rng.standard_normal((rows, vocab), dtype=np.float32) * np.float32(std)
+        t = rng.integers(0, vocab, rows)
+        if rng.random() < 0.5:
+            for r in rng.integers(0, rows, 1 + rows // 4):
+                z[r, rng.integers(0, vocab)] += np.float32(rng.uniform(5.0, 120.0))
+        if rng.random() < 0.3:
+            keep = z[np.arange(rows), t].copy()
+            z[rng.random((rows, vocab)) < 0.2] = -np.inf
+            z[np.arange(rows), t] = keep
+        if rng.random() < 0.3:
+            bad = rng.integers(0, rows, 1 + rows // 16)
+            t[bad] = rng.choice([-1, vocab, 1 << 40], bad.size)
+        host = z if dtype == "f32" else lce_synth.f32_to_bf16_bits(z)
+        shards = int(rng.integers(1, min(7, vocab) + 1))
+        path = str(rng.choice(["auto", "wave", "block", "split"]))
+        env = {} if path == "auto" else {"LCE_PATH": path}
+        label = f"seed {seed} case {case}: {dtype} {rows}x{vocab} std {std} {shards} shards {path}"
+        td = torch.from_numpy(t.astype(np.int64)).cuda()
+        parts = []
+        for a, b in _bounds(vocab, shards, 31 * seed + case):
+            zs = np.ascontiguousarray(host[:, a:b])
+            with forced_env(**env):
+                p = lce.xent_partial(to_dev(zs), td, a)
+            torch.cuda.synchronize()
+            _check_stats(p.cpu().numpy(), oracle.xent_partial(zs, t, a, dtype=dtype), f"{label} shard {a}:{b}")
+            parts.append(p)
+        per = lce.xent_merge(torch.stack(parts), td, vocab, "none")
+        torch.cuda.synchronize()
+        got = per.cpu().numpy().astype(np.float64)
+        want = oracle.xent_rows(host, t, dtype=dtype)
+        assert np.array_equal(np.isnan(got), np.isnan(want)), label
+        assert np.nanmax(np.abs(got - want), initial=0.0) <= TOK_ABS, label
