@@ -1,12 +1,14 @@
 """Gradients of the fused projection + cross-entropy (lce_fused_linear_xent_bwd, through
 the C ABI) against the fp64 oracle.
 
-Tolerance, derived from the arithmetic: the logit gradient dZ is rounded to bf16 (round
-to nearest even, relative error <= 2^-9) before the two GEMMs, which accumulate exact
-bf16 products in fp32.  So each element of dx = dZ W is within 2^-9 * sum_v |dZ_tv W_vh|
-of the exact value from rounding alone; the tests allow twice that (2^-8), which also
-covers the fp32 accumulation and the fp32 softmax, plus 1e-7 absolute.  dW = dZ^T x gets
-the same bound with sum_t |dZ_tv x_th|.
+Tolerance, derived from the arithmetic: the logit gradient dZ_tv = g_t (p_tv - [v = t_t])
+is formed in fp32 from the softmax p, within a few ulps of g_t p_tv (not of dZ, which is
+near 0 where p_tv is near 1 at the target: with one vocab row it is exactly 0), then
+rounded to bf16 (round to nearest even, relative error <= 2^-9) before the two GEMMs,
+which accumulate exact bf16 products in fp32.  So each element of dx = dZ W is within
+sum_v (2^-9 |dZ_tv| + 2^-21 |g_t| (p_tv + [v = t_t])) |W_vh| of the exact value from
+rounding alone; the tests allow twice that (2^-8 and 2^-20), which also covers the fp32
+accumulation, plus 1e-7 absolute.  dW = dZ^T x gets the same bound with x in place of W.
 
 At the page shape (tokens 2048, hidden 4096, vocab 128256) the oracle checks dx on a
 sample of tokens and dW on a sample of head rows (each row needs every token's softmax,
@@ -26,7 +28,7 @@ pytestmark = pytest.mark.gpu
 import vocab_cross_entropy_row_amd as lce  # noqa: E402
 from gpu_util import forced_env, to_dev  # noqa: E402
 
-REL, ABS = 2.0 ** -8, 1e-7
+REL, SOFTMAX, ABS = 2.0 ** -8, 2.0 ** -20, 1e-7
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -52,9 +54,16 @@ def _row_scale(grad, reduction, tokens):
 
 def _bounds(xb, wb, t, scale, want_dw=True):
     x64, w64 = oracle.bf16_bits_to_f64(xb), oracle.bf16_bits_to_f64(wb)
-    adz = np.abs(oracle.xent_bwd(x64 @ w64.T, t, scale, "none", dtype="f64"))
-    bw = REL * (adz.T @ np.abs(x64)) + ABS if want_dw else None
-    return REL * (adz @ np.abs(w64)) + ABS, bw
+    dz = oracle.xent_bwd(x64 @ w64.T, t, scale, "none", dtype="f64")
+    g = np.asarray(scale, dtype=np.float64).reshape(-1, 1)
+    onehot = np.zeros_like(dz)
+    ok = (t >= 0) & (t < dz.shape[1])
+    onehot[np.nonzero(ok)[0], t[ok]] = 1.0
+    # |g| p + |g| [v = t]: the size the fp32 softmax's rounding is relative to
+    gp = np.abs(dz + g * onehot) + np.abs(g) * onehot
+    e = REL * np.abs(dz) + SOFTMAX * gp
+    bw = e.T @ np.abs(x64) + ABS if want_dw else None
+    return e @ np.abs(w64) + ABS, bw
 
 
 def _check(name, got, want, bound):
@@ -189,7 +198,9 @@ def test_page_shape_sampled_and_properties():
     # the rows of three tokens' targets (where the one-hot term enters the sum).
     head = np.unique(np.r_[0:2, 64127:64129, w.vocab - 2:w.vocab, t[[0, 1023, 2047]]])
     want_dw, dz_cols = oracle.fused_linear_xent_dw_rows(xb, wb, t, np.full(T, 1.0 / T), head)
-    bw = REL * (np.abs(dz_cols).T @ np.abs(oracle.bf16_bits_to_f64(xb))) + ABS
+    onehot = (t[:, None] == head[None, :]).astype(np.float64)
+    gp = np.abs(dz_cols + onehot / T) + onehot / T  # |g| p + |g| [v = t], g = 1/T
+    bw = (REL * np.abs(dz_cols) + SOFTMAX * gp).T @ np.abs(oracle.bf16_bits_to_f64(xb)) + ABS
     _check("dW rows", dw[torch.from_numpy(head).cuda()].cpu().numpy(), want_dw, bw)
 
 
@@ -236,3 +247,33 @@ def test_dw_gemm_layouts_agree():
     _, bw = _bounds(xb, wb, t, np.full(600, 1.0 / 600))
     _check("dW layouts", a[1], b[1], bw)
     _check("dW vs oracle", a[1], oracle.fused_linear_xent_bwd(xb, wb, t, 1.0, "mean")[1], bw)
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_randomized_grads(seed):
+    """Seeded random cases, 6 per seed: 1-400 tokens, hidden a multiple of 8 in [8, 512],
+    vocab log-uniform in [1, 4000), heads scaled to logit spreads from ~0.3 to ~12, targets
+    anywhere (also the first and last vocab rows), either reduction, any of the three paths;
+    dx and dW against the oracle within the bound derived above."""
+    rng = np.random.default_rng(8400 + seed)
+    for case in range(6):
+        tokens = int(rng.integers(1, 401))
+        hidden = 8 * int(rng.integers(1, 65))
+        vocab = max(1, int(np.exp(rng.uniform(0.0, np.log(4000.0)))))
+        spread = float(rng.choice([0.3, 1.0, 3.0, 12.0]))
+        xb = lce_synth.normal_bf16_bits(9100 + 31 * seed + case, 0, tokens, hidden, 1.0)
+        wb = lce_synth.normal_bf16_bits(9600 + 31 * seed + case, 2, vocab, hidden,
+                                        spread / np.sqrt(hidden))
+        t = rng.integers(0, vocab, tokens).astype(np.int64)
+        t[rng.random(tokens) < 0.1] = vocab - 1
+        t[rng.random(tokens) < 0.1] = 0
+        reduction = str(rng.choice(["mean", "none"]))
+        grad = (np.array([rng.uniform(0.5, 2.0)]) if reduction == "mean"
+                else rng.normal(size=tokens)).astype(np.float32).astype(np.float64)
+        mode = str(rng.choice(MODES))
+        label = f"seed {seed} case {case}: T {tokens} H {hidden} V {vocab} spread {spread} {reduction} {mode}"
+        dx, dw = _run(xb, wb, t, grad, reduction, env=_env(mode, vocab))
+        want_dx, want_dw = oracle.fused_linear_xent_bwd(xb, wb, t, grad, reduction)
+        bx, bw = _bounds(xb, wb, t, _row_scale(grad, reduction, tokens))
+        _check(f"dx {label}", dx, want_dx, bx)
+        _check(f"dW {label}", dw, want_dw, bw)
