@@ -173,3 +173,26 @@ def test_page_shape_sampled_against_oracle():
     want = oracle.fused_linear_jsd_rows(xs_b[rows], ws_b, xt_b[rows], wt_b)
     _check(per.cpu().numpy()[rows], want)
     _check(per_rc.cpu().numpy()[rows], want)
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_randomized_cases(seed):
+    """Seeded random cases, 6 per seed: 1-400 tokens, hidden a multiple of 8 in [8, 512],
+    vocab log-uniform in [2, 5000), each head scaled to its own logit spread (~0.3 to ~12),
+    beta in (0, 1), either reduction, any of the three paths; against the oracle."""
+    rng = np.random.default_rng(8600 + seed)
+    for case in range(6):
+        tokens = int(rng.integers(1, 401))
+        hidden = 8 * int(rng.integers(1, 65))
+        vocab = max(2, int(np.exp(rng.uniform(np.log(2.0), np.log(5000.0)))))
+        ss, st = (float(rng.choice([0.3, 1.0, 3.0, 12.0])) for _ in range(2))
+        bits = (lce_synth.normal_bf16_bits(9700 + 31 * seed + case, 0, tokens, hidden, 1.0),
+                lce_synth.normal_bf16_bits(9800 + 31 * seed + case, 2, vocab, hidden, ss / math.sqrt(hidden)),
+                lce_synth.normal_bf16_bits(9900 + 31 * seed + case, 0, tokens, hidden, 1.0),
+                lce_synth.normal_bf16_bits(9950 + 31 * seed + case, 2, vocab, hidden, st / math.sqrt(hidden)))
+        beta = float(rng.uniform(0.05, 0.95))
+        reduction = str(rng.choice(["none", "mean"]))
+        mode = str(rng.choice(MODES))
+        got = _run(bits, beta, reduction, mode)
+        want = oracle.fused_linear_jsd(*bits, beta=beta, reduction=reduction)
+        _check(np.atleast_1d(got), np.atleast_1d(np.asarray(want, dtype=np.float64)))
