@@ -289,7 +289,8 @@ def test_bwd_randomized_rows(seed):
     spikes 5 to 120 above the rest, -inf entries around finite targets, some invalid
     targets, the first row 0-7 elements past an aligned address, either reduction, the
     default path or one wave per row or the statistics-then-apply path; gradients against
-    the oracle, and the one-call forward and backward's gradient bitwise the same."""
+    the oracle, the one-call forward and backward's gradient bitwise the same and its losses
+    against the oracle's."""
     rng = np.random.default_rng(7700 + seed)
     for case in range(10):
         dtype = str(rng.choice(["f32", "bf16"]))
@@ -324,10 +325,18 @@ def test_bwd_randomized_rows(seed):
         env = {} if path == "auto" else {"LCE_BWD_PATH": path}
         with forced_env(**env):
             d = lce.xent_bwd(zd, td, gd, reduction)
-            _, d2 = lce.xent_fwd_bwd(zd, td, gd, reduction)
+            loss, d2 = lce.xent_fwd_bwd(zd, td, gd, reduction)
         torch.cuda.synchronize()
         got = _to_host(d, dtype)
         assert np.array_equal(got, _to_host(d2, dtype), equal_nan=True), label
+        lw = oracle.xent_rows(host, t, dtype=dtype)
+        lg = loss.cpu().numpy().astype(np.float64)
+        if reduction == "none":
+            assert np.array_equal(np.isnan(lg), np.isnan(lw)), label
+            assert np.nanmax(np.abs(lg - lw), initial=0.0) <= 1e-4, label
+        else:
+            wm = oracle.mean(lw)
+            assert (np.isnan(lg[0]) and np.isnan(wm)) or abs(lg[0] - wm) <= 1e-5 * abs(wm) + 1e-7, label
         want = oracle.xent_bwd(host, t, np.asarray(grad, dtype=np.float64), reduction, dtype=dtype)
         gs = (np.full(rows, float(grad) / rows) if reduction == "mean" else grad.astype(np.float64))
         _check(got, want, gs[:, None], dtype, label)
