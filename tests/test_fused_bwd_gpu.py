@@ -1,14 +1,18 @@
 """Gradients of the fused projection + cross-entropy (lce_fused_linear_xent_bwd, through
 the C ABI) against the fp64 oracle.
 
-Tolerance, derived from the arithmetic: the logit gradient dZ_tv = g_t (p_tv - [v = t_t])
-is formed in fp32 from the softmax p, within a few ulps of g_t p_tv (not of dZ, which is
-near 0 where p_tv is near 1 at the target: with one vocab row it is exactly 0), then
-rounded to bf16 (round to nearest even, relative error <= 2^-9) before the two GEMMs,
-which accumulate exact bf16 products in fp32.  So each element of dx = dZ W is within
-sum_v (2^-9 |dZ_tv| + 2^-21 |g_t| (p_tv + [v = t_t])) |W_vh| of the exact value from
-rounding alone; the tests allow twice that (2^-8 and 2^-20), which also covers the fp32
-accumulation, plus 1e-7 absolute.  dW = dZ^T x gets the same bound with x in place of W.
+Tolerance, derived from the arithmetic.  The kernel's logits are fp32 sums of exact bf16
+products: one rounding per 16-product MFMA step, so |z - z_exact| <= (H/16 + 2) 2^-24 S
+with S = sum_k |x_k W_k|, and z and the row's log-sum-exp are held in fp32 (half an ulp
+each, <= 2^-24 (|z| + |lse|)).  The softmax p = e^(z - lse) then carries a relative error
+e_p of those two plus a few ulps (2^-21) of its own fp32 arithmetic.  The logit gradient
+dZ_tv = g_t (p_tv - [v = t_t]) is formed in fp32, so its error is relative to g p and
+not to dZ, which is near 0 where p is near 1 at the target (exactly 0 with one vocab
+row); it is then rounded to bf16 (relative error <= 2^-9) before the two GEMMs, which
+accumulate exact bf16 products in fp32.  So each element of dx = dZ W is within
+sum_v (2^-9 |dZ_tv| + |g_t| p_tv e_p,tv + 2^-21 |g_t| [v = t_t]) |W_vh|; the tests allow
+twice each term (2^-8 for the bf16 rounding, which also covers the GEMMs' fp32
+accumulation), plus 1e-7 absolute.  dW = dZ^T x gets the same bound with x for W.
 
 At the page shape (tokens 2048, hidden 4096, vocab 128256) the oracle checks dx on a
 sample of tokens and dW on a sample of head rows (each row needs every token's softmax,
@@ -29,6 +33,14 @@ import vocab_cross_entropy_row_amd as lce  # noqa: E402
 from gpu_util import forced_env, to_dev  # noqa: E402
 
 REL, SOFTMAX, ABS = 2.0 ** -8, 2.0 ** -20, 1e-7
+
+
+def _grad_error(dz, z, lse, S, g, onehot, hidden):
+    """Per-logit bound on the kernel's dZ error (twice each term of the derivation above).
+    dz, z, S: [tokens, cols]; lse, g: [tokens, 1]; onehot: [tokens, cols]."""
+    p = np.exp(z - lse)
+    e_p = 2.0 ** -24 * (np.abs(z) + np.abs(lse)) + (hidden / 16 + 2) * 2.0 ** -24 * S + 2.0 ** -21
+    return REL * np.abs(dz) + 2.0 * np.abs(g) * p * e_p + SOFTMAX * np.abs(g) * onehot
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -54,14 +66,15 @@ def _row_scale(grad, reduction, tokens):
 
 def _bounds(xb, wb, t, scale, want_dw=True):
     x64, w64 = oracle.bf16_bits_to_f64(xb), oracle.bf16_bits_to_f64(wb)
-    dz = oracle.xent_bwd(x64 @ w64.T, t, scale, "none", dtype="f64")
-    g = np.asarray(scale, dtype=np.float64).reshape(-1, 1)
-    onehot = np.zeros_like(dz)
-    ok = (t >= 0) & (t < dz.shape[1])
+    z = x64 @ w64.T
+    dz = oracle.xent_bwd(z, t, scale, "none", dtype="f64")
+    m = z.max(axis=1, keepdims=True)
+    lse = m + np.log(np.exp(z - m).sum(axis=1, keepdims=True))
+    onehot = np.zeros_like(z)
+    ok = (t >= 0) & (t < z.shape[1])
     onehot[np.nonzero(ok)[0], t[ok]] = 1.0
-    # |g| p + |g| [v = t]: the size the fp32 softmax's rounding is relative to
-    gp = np.abs(dz + g * onehot) + np.abs(g) * onehot
-    e = REL * np.abs(dz) + SOFTMAX * gp
+    g = np.asarray(scale, dtype=np.float64).reshape(-1, 1)
+    e = _grad_error(dz, z, lse, np.abs(x64) @ np.abs(w64).T, g, onehot, x64.shape[1])
     bw = e.T @ np.abs(x64) + ABS if want_dw else None
     return e @ np.abs(w64) + ABS, bw
 
@@ -198,9 +211,17 @@ def test_page_shape_sampled_and_properties():
     # the rows of three tokens' targets (where the one-hot term enters the sum).
     head = np.unique(np.r_[0:2, 64127:64129, w.vocab - 2:w.vocab, t[[0, 1023, 2047]]])
     want_dw, dz_cols = oracle.fused_linear_xent_dw_rows(xb, wb, t, np.full(T, 1.0 / T), head)
+    x64 = oracle.bf16_bits_to_f64(xb)
+    w_head = oracle.bf16_bits_to_f64(wb[head])
+    z_cols = x64 @ w_head.T
     onehot = (t[:, None] == head[None, :]).astype(np.float64)
-    gp = np.abs(dz_cols + onehot / T) + onehot / T  # |g| p + |g| [v = t], g = 1/T
-    bw = (REL * np.abs(dz_cols) + SOFTMAX * gp).T @ np.abs(oracle.bf16_bits_to_f64(xb)) + ABS
+    p_cols = dz_cols * T + onehot                    # g = 1/T
+    j = np.argmax(p_cols, axis=1)                    # each token's lse from its largest p here
+    r = np.arange(T)
+    lse = (z_cols[r, j] - np.log(p_cols[r, j]))[:, None]
+    e = _grad_error(dz_cols, z_cols, lse, np.abs(x64) @ np.abs(w_head).T, np.full((T, 1), 1.0 / T),
+                    onehot, x64.shape[1])
+    bw = e.T @ np.abs(x64) + ABS
     _check("dW rows", dw[torch.from_numpy(head).cuda()].cpu().numpy(), want_dw, bw)
 
 
