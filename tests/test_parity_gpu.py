@@ -645,6 +645,39 @@ def test_fused_randomized(seed):
         assert abs(mean - wm) <= FUSED_MEAN_REL * abs(wm) + MEAN_ABS_FLOOR, f"{label}: {mean} vs {wm}"
 
 
+@pytest.mark.parametrize("seed", range(2))
+def test_fused_spiky_heads(seed):
+    """Seeded random fused cases with a few head rows scaled 10-40x (logits up to a few
+    hundred, so the tiles and segments holding them dominate their tokens' sums), 8 per
+    seed; the per-token losses, the mean and the one-call forward and backward's mean
+    against the oracle."""
+    rng = np.random.default_rng(8800 + seed)
+    for case in range(8):
+        tokens = int(rng.integers(1, 400))
+        hidden = 8 * int(rng.integers(1, 65))
+        vocab = max(1, int(np.exp(rng.uniform(0.0, np.log(6000.0)))))
+        xb = lce_synth.normal_bf16_bits(9300 + 17 * seed + case, 0, tokens, hidden, 1.0)
+        w = lce_synth.normal_f32(9400 + 17 * seed + case, 2, vocab, hidden, 1.0 / math.sqrt(hidden))
+        for r in rng.integers(0, vocab, 1 + vocab // 50):
+            w[r] *= np.float32(rng.uniform(10.0, 40.0))
+        wb = lce_synth.f32_to_bf16_bits(w)
+        tg = rng.integers(0, vocab, tokens)
+        segments = int(rng.choice([0, 1, 2, 3, 9]))
+        label = f"seed {seed} case {case}: T {tokens} H {hidden} V {vocab} segments {segments}"
+        x, W, t = to_dev(xb), to_dev(wb), torch.from_numpy(tg.astype(np.int64)).cuda()
+        want = oracle.fused_linear_xent_rows(xb, wb, tg)
+        env = {"LCE_FUSED_SEGMENTS": segments} if segments else {}
+        with forced_env(**env):
+            per = lce.fused_linear_xent(x, W, t, "none").cpu().numpy().astype(np.float64)
+            mean = lce.fused_linear_xent(x, W, t, "mean").item()
+            loss, _, _ = lce.fused_linear_xent_fwd_bwd(x, W, t, torch.ones(1, device="cuda"), "mean")
+        err = np.abs(per - want)
+        assert err.max() <= FUSED_TOK_ABS, f"{label}: max abs err {err.max()}"
+        wm = oracle.mean(want)
+        for name, m in (("mean", mean), ("one-call mean", loss.item())):
+            assert abs(m - wm) <= FUSED_MEAN_REL * abs(wm) + MEAN_ABS_FLOOR, f"{label}: {name} {m} vs {wm}"
+
+
 @pytest.mark.parametrize("segments", [1, 2, 3, 5])
 def test_fused_segment_counts(segments):
     tokens, hidden, vocab = 300, 128, 3000
